@@ -1,0 +1,180 @@
+"""fp64 CPU oracle for direct all-pairs softened gravity (ctypes wrapper of oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by ``__graft_entry__.smoke()``
+and by the cpu_baseline leg of ``bench.py``. The product library never imports
+or links it, and it shares no code with the HIP path.
+
+Inputs are the float32 body records the GPU receives, widened exactly to
+float64; eps2 and dt are taken as their float32 values, widened, unless the
+``*_exact`` entry points are used. See oracle.c for the formulas, their
+sources on the pages and the readings taken.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+_HERE = Path(__file__).resolve().parent
+SRC = _HERE / "oracle.c"
+LIB = _HERE / "liboracle.so"
+
+_c_double_p = ctypes.POINTER(ctypes.c_double)
+_c_int64_p = ctypes.POINTER(ctypes.c_int64)
+
+GCC_FLAGS = ["-O2", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off"]
+
+
+def compile_oracle(src: Path, out: Path) -> Path:
+    """gcc -O2 -fopenmp, no fast-math, no FMA contraction."""
+    tmp = out.with_suffix(".so.tmp")
+    subprocess.run(["gcc", *GCC_FLAGS, "-o", str(tmp), str(src), "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> Path:
+    if force or not LIB.exists():
+        compile_oracle(SRC, LIB)
+    return LIB
+
+
+def _ptr(a, ctype=_c_double_p):
+    if a is None:
+        return ctypes.cast(None, ctype)
+    return a.ctypes.data_as(ctype)
+
+
+def _bodies64(arr) -> np.ndarray:
+    a = np.asarray(arr)
+    if a.ndim != 2 or a.shape[1] != 4:
+        raise ValueError("bodies must have shape (N, 4)")
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def as_f32(x) -> float:
+    """A scalar parameter as the float32 value the GPU path receives, widened."""
+    return float(np.float32(x))
+
+
+class Oracle:
+    """One loaded build of oracle.c (the tests also load deliberately broken copies)."""
+
+    def __init__(self, libpath: Path | str):
+        lib = ctypes.CDLL(str(libpath))
+        lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_accel.argtypes = [_c_double_p, ctypes.c_int64, ctypes.c_double, _c_int64_p,
+                                     ctypes.c_int64, _c_double_p, _c_double_p, _c_double_p,
+                                     _c_double_p]
+        lib.oracle_accel.restype = ctypes.c_int
+        lib.oracle_euler.argtypes = [_c_double_p, _c_double_p, ctypes.c_int64, ctypes.c_double,
+                                     ctypes.c_double, ctypes.c_int64]
+        lib.oracle_euler.restype = ctypes.c_int
+        lib.oracle_energy.argtypes = [_c_double_p, _c_double_p, ctypes.c_int64, ctypes.c_double,
+                                      _c_double_p, _c_double_p]
+        lib.oracle_energy.restype = ctypes.c_double
+        self._lib = lib
+
+    def num_threads(self) -> int:
+        return int(self._lib.oracle_num_threads())
+
+    def accel_exact(self, pos, eps2: float, targets=None) -> dict:
+        """Accelerations, potentials and error scales; float64 bodies and eps2 used as given.
+
+        Returns float64 arrays acc (nt, 3), pot (nt,), bound_a (nt,), bound_p (nt,)
+        for the listed target indices (default: every body, in order).
+        """
+        p = _bodies64(pos)
+        n = p.shape[0]
+        if targets is None:
+            t, nt = None, n
+        else:
+            t = np.ascontiguousarray(targets, dtype=np.int64)
+            nt = t.shape[0]
+        acc = np.zeros((nt, 3))
+        pot = np.zeros(nt)
+        ba = np.zeros(nt)
+        bp = np.zeros(nt)
+        rc = self._lib.oracle_accel(_ptr(p), n, float(eps2), _ptr(t, _c_int64_p), nt, _ptr(acc),
+                                    _ptr(pot), _ptr(ba), _ptr(bp))
+        if rc != 0:
+            raise ValueError("oracle_accel rejected its arguments")
+        return {"acc": acc, "pot": pot, "bound_a": ba, "bound_p": bp}
+
+    def accel(self, pos, eps2, targets=None) -> dict:
+        """As accel_exact, with eps2 rounded to float32 first (the GPU path's value)."""
+        return self.accel_exact(pos, as_f32(eps2), targets)
+
+    def euler_exact(self, pos, vel, dt: float, eps2: float, nsteps: int = 1):
+        """nsteps explicit Euler steps in float64; returns new (pos64, vel64) arrays."""
+        p = _bodies64(pos).copy()
+        v = _bodies64(vel).copy()
+        if p.shape != v.shape:
+            raise ValueError("pos and vel shapes differ")
+        rc = self._lib.oracle_euler(_ptr(p), _ptr(v), p.shape[0], float(dt), float(eps2),
+                                    int(nsteps))
+        if rc != 0:
+            raise ValueError("oracle_euler rejected its arguments")
+        return p, v
+
+    def euler(self, pos, vel, dt, eps2, nsteps: int = 1):
+        """As euler_exact, with dt and eps2 rounded to float32 first."""
+        return self.euler_exact(pos, vel, as_f32(dt), as_f32(eps2), nsteps)
+
+    def energy_exact(self, pos, vel, eps2: float):
+        """(E, K, W): total, kinetic and softened pair potential energy (pairs counted once)."""
+        p = _bodies64(pos)
+        v = _bodies64(vel)
+        k = ctypes.c_double()
+        w = ctypes.c_double()
+        e = self._lib.oracle_energy(_ptr(p), _ptr(v), p.shape[0], float(eps2), ctypes.byref(k),
+                                    ctypes.byref(w))
+        return float(e), float(k.value), float(w.value)
+
+    def energy(self, pos, vel, eps2):
+        return self.energy_exact(pos, vel, as_f32(eps2))
+
+
+_default: Oracle | None = None
+
+
+def get() -> Oracle:
+    """The oracle built from oracle.c (compiled on first use if nothing is built)."""
+    global _default
+    if _default is None:
+        if not LIB.exists():
+            build()
+        _default = Oracle(LIB)
+    return _default
+
+
+def num_threads() -> int:
+    return get().num_threads()
+
+
+def accel(pos, eps2, targets=None) -> dict:
+    return get().accel(pos, eps2, targets)
+
+
+def accel_exact(pos, eps2, targets=None) -> dict:
+    return get().accel_exact(pos, eps2, targets)
+
+
+def euler(pos, vel, dt, eps2, nsteps: int = 1):
+    return get().euler(pos, vel, dt, eps2, nsteps)
+
+
+def euler_exact(pos, vel, dt, eps2, nsteps: int = 1):
+    return get().euler_exact(pos, vel, dt, eps2, nsteps)
+
+
+def energy(pos, vel, eps2):
+    return get().energy(pos, vel, eps2)
+
+
+def energy_exact(pos, vel, eps2):
+    return get().energy_exact(pos, vel, eps2)

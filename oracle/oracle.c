@@ -1,0 +1,174 @@
+/*
+ * fp64 CPU oracle for the direct all-pairs softened-gravity method.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may link, load or call
+ * this code: it is used by tests/, by the smoke check in __graft_entry__.py and
+ * by the cpu_baseline leg of bench.py. It shares no source with the HIP
+ * library.
+ *
+ * The method is an exact direct sum (no approximation), so the oracle is that
+ * sum written out in double precision, one target at a time, sources in
+ * ascending index order, nothing blocked, fused or reordered. OpenMP only
+ * splits the independent targets between threads; each target's sum is
+ * sequential, so results do not depend on the thread count.
+ *
+ * What it computes (G = 1):
+ *   a_i = sum_j m_j (x_j - x_i) / (|x_j - x_i|^2 + eps2)^(3/2)
+ *   p_i = -sum_j m_j / (|x_j - x_i|^2 + eps2)^(1/2)
+ * Sources:
+ *   - Degawa, "N 体問題" (Nagaoka Univ. of Technology lecture), slide 4 for the
+ *     acceleration sum and slide 12 for the softening term that replaces the
+ *     j != i test: with it the j = i term has a zero numerator.
+ *   - Nakasato, "ATI Stream SDK による天文物理計算の高速化" ("スライド 1"), No.4:
+ *     the quantities to compute are the acceleration and the potential.
+ *   - GPU Gems 3 ch. 31 study page (blog.luozichu.ink), section 1: r_ij = x_j - x_i.
+ * Readings where the pages are damaged or silent:
+ *   - the sum runs over ALL j, including j = i, for both a and p (the softened
+ *     sum as written; the Stream SDK IL kernel loops over every particle with no
+ *     branch). So p_i contains the self term -m_i/sqrt(eps2);
+ *   - the sign of p is negative (the minus sign is lost in the slide text);
+ *   - eps2 is the softening squared, added to |r|^2.
+ *
+ * Euler step (Degawa, slides 5-6 and the CPU program's integrate(), slide 15):
+ *   x^{n+1} = x^n + dt v^n,   v^{n+1} = v^n + dt a(x^n)
+ * position first, using the old velocity; a is computed from x^n.
+ *
+ * Per-body error scales reported beside the results (parity bounds):
+ *   B_i = sum_j m_j |r_ij| / (|r_ij|^2 + eps2)^(3/2),  P_i = sum_j m_j / (|r_ij|^2 + eps2)^(1/2)
+ *
+ * Parity pins (tests/test_oracle.py): N = 1 and N = 2 closed forms, a regular
+ * polygon (ring) closed form, zero force at the centre of symmetric sets,
+ * Newton's third law, exact power-of-two scaling, a 50-digit decimal brute
+ * force for small N, and the free-particle Euler step. The multi-step energy
+ * drift (oracle_energy over a trajectory) has no closed form: parity unpinned.
+ *
+ * Layouts: pos is n x 4 doubles (x, y, z, m); vel is n x 4 doubles
+ * (vx, vy, vz, unused). Return value 0 on success, -1 on bad arguments.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* One target against all n sources, j = 0 .. n-1 in order. */
+static void one_target(const double *pos, int64_t n, double eps2, int64_t i,
+                       double a[3], double *p, double *ba, double *bp)
+{
+    const double xi = pos[4 * i + 0], yi = pos[4 * i + 1], zi = pos[4 * i + 2];
+    double ax = 0.0, ay = 0.0, az = 0.0, pp = 0.0, sa = 0.0, sp = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+        const double mj = pos[4 * j + 3];
+        const double dx = pos[4 * j + 0] - xi;          /* r_ij = x_j - x_i */
+        const double dy = pos[4 * j + 1] - yi;
+        const double dz = pos[4 * j + 2] - zi;
+        const double r2 = dx * dx + dy * dy + dz * dz;
+        const double q = r2 + eps2;                     /* |r|^2 + eps^2 */
+        const double q32 = q * sqrt(q);                 /* (|r|^2 + eps^2)^(3/2) */
+        ax += mj * dx / q32;
+        ay += mj * dy / q32;
+        az += mj * dz / q32;
+        pp -= mj / sqrt(q);
+        sa += mj * sqrt(r2) / q32;
+        sp += mj / sqrt(q);
+    }
+    a[0] = ax; a[1] = ay; a[2] = az;
+    *p = pp; *ba = sa; *bp = sp;
+}
+
+/*
+ * Accelerations (and potentials) of the listed targets.
+ * targets: indices into [0, n), or NULL for all n bodies (then nt must equal n).
+ * acc: nt x 3; pot, bound_a, bound_p: nt each; pot/bound_a/bound_p may be NULL.
+ */
+int oracle_accel(const double *pos, int64_t n, double eps2,
+                 const int64_t *targets, int64_t nt,
+                 double *acc, double *pot, double *bound_a, double *bound_p)
+{
+    if (n < 0 || nt < 0 || (n > 0 && !pos) || (nt > 0 && !acc)) return -1;
+    if (!targets && nt != n) return -1;
+    if (targets)
+        for (int64_t k = 0; k < nt; ++k)
+            if (targets[k] < 0 || targets[k] >= n) return -1;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t k = 0; k < nt; ++k) {
+        const int64_t i = targets ? targets[k] : k;
+        double a[3], p, ba, bp;
+        one_target(pos, n, eps2, i, a, &p, &ba, &bp);
+        acc[3 * k + 0] = a[0];
+        acc[3 * k + 1] = a[1];
+        acc[3 * k + 2] = a[2];
+        if (pot) pot[k] = p;
+        if (bound_a) bound_a[k] = ba;
+        if (bound_p) bound_p[k] = bp;
+    }
+    return 0;
+}
+
+/*
+ * nsteps explicit Euler steps in fp64, in place on pos and vel.
+ * Mass (pos[.][3]) and vel[.][3] are never changed.
+ */
+int oracle_euler(double *pos, double *vel, int64_t n, double dt, double eps2, int64_t nsteps)
+{
+    if (n < 0 || nsteps < 0 || (n > 0 && (!pos || !vel))) return -1;
+    if (n == 0 || nsteps == 0) return 0;
+    double *acc = (double *)malloc((size_t)n * 3 * sizeof(double));
+    if (!acc) return -1;
+    for (int64_t s = 0; s < nsteps; ++s) {
+        oracle_accel(pos, n, eps2, NULL, n, acc, NULL, NULL, NULL);  /* a(x^n) */
+        for (int64_t i = 0; i < n; ++i) {
+            for (int c = 0; c < 3; ++c) pos[4 * i + c] += dt * vel[4 * i + c];  /* old v */
+            for (int c = 0; c < 3; ++c) vel[4 * i + c] += dt * acc[3 * i + c];
+        }
+    }
+    free(acc);
+    return 0;
+}
+
+/*
+ * Total energy of the softened system:
+ *   K = sum_i m_i |v_i|^2 / 2
+ *   W = -(1/2) sum_i sum_{j != i} m_i m_j / sqrt(|r_ij|^2 + eps2)   (each pair once)
+ * Returns K + W; kin and pe receive K and W when non-NULL.
+ */
+double oracle_energy(const double *pos, const double *vel, int64_t n, double eps2,
+                     double *kin, double *pe)
+{
+    double k = 0.0, w = 0.0;
+    double *wi = (double *)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+    if (!wi) return NAN;
+    for (int64_t i = 0; i < n; ++i) {
+        const double v2 = vel[4 * i] * vel[4 * i] + vel[4 * i + 1] * vel[4 * i + 1] +
+                          vel[4 * i + 2] * vel[4 * i + 2];
+        k += 0.5 * pos[4 * i + 3] * v2;
+    }
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < n; ++i) {
+        double s = 0.0;
+        for (int64_t j = 0; j < n; ++j) {
+            if (j == i) continue;
+            const double dx = pos[4 * j] - pos[4 * i];
+            const double dy = pos[4 * j + 1] - pos[4 * i + 1];
+            const double dz = pos[4 * j + 2] - pos[4 * i + 2];
+            s -= pos[4 * j + 3] / sqrt(dx * dx + dy * dy + dz * dz + eps2);
+        }
+        wi[i] = 0.5 * pos[4 * i + 3] * s;
+    }
+    for (int64_t i = 0; i < n; ++i) w += wi[i];  /* fixed order: thread-count independent */
+    free(wi);
+    if (kin) *kin = k;
+    if (pe) *pe = w;
+    return k + w;
+}

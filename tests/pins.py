@@ -1,0 +1,305 @@
+"""Pins for the fp64 oracle: checks against facts the pages and the mathematics fix.
+
+Each ``pin_*`` takes a loaded oracle (``oracle.Oracle``) and raises
+AssertionError when the oracle disagrees with a closed form, an invariant, a
+special case or an independent 50-digit brute force. test_oracle.py runs them
+on the real oracle; test_oracle_mutations.py runs them on copies of oracle.c
+with planted mistakes and requires each mistake to trip at least one pin.
+
+Sources for what is pinned:
+- Degawa, "N 体問題", slide 4 (acceleration sum), slide 12 (softening replaces
+  the j != i branch; the self term has a zero numerator), slides 5-6 and 15
+  (explicit Euler, position first with the old velocity).
+- Nakasato, "スライド 1", No.4 (acceleration and potential; minus sign of p).
+- GPU Gems 3 ch. 31 study page, section 1 (r_ij = x_j - x_i).
+"""
+
+from __future__ import annotations
+
+import math
+from decimal import Decimal, getcontext
+
+import numpy as np
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    err = np.abs(a - b)
+    if not np.all(np.isfinite(a)) or np.any(err > tol):
+        raise AssertionError(f"{what}: max err {np.nanmax(err) if err.size else 0:.3e} > tol\n"
+                             f"got {a}\nwant {b}")
+
+
+def _bodies(xyz, m):
+    xyz = np.asarray(xyz, dtype=np.float64).reshape(-1, 3)
+    p = np.zeros((xyz.shape[0], 4))
+    p[:, :3] = xyz
+    p[:, 3] = m
+    return p
+
+
+# ---------------------------------------------------------------- special cases
+
+def pin_single_body(orc):
+    """N = 1: the only term is the self term: a = 0 exactly and p = -m/eps."""
+    for m, e2, x in [(1.0, 1e-6, (0.3, -0.2, 0.9)), (2.5, 0.25, (0, 0, 0)), (1e-3, 4e-4, (7, 1, 2))]:
+        r = orc.accel_exact(_bodies([x], m), e2)
+        if not np.all(r["acc"] == 0.0):
+            raise AssertionError(f"N=1 acceleration not zero: {r['acc']}")
+        _close(r["pot"], [-m / math.sqrt(e2)], 0.0, "N=1 potential")
+        _close(r["bound_p"], [m / math.sqrt(e2)], 0.0, "N=1 P scale")
+        _close(r["bound_a"], [0.0], 0.0, "N=1 B scale")
+
+
+def pin_two_body_345(orc):
+    """Hand-derived worked example: m0 = 1 at the origin, m1 = 2 at (3, 4, 0), eps2 = 11.
+
+    |r|^2 + eps2 = 25 + 11 = 36, so (.)^(3/2) = 216 and (.)^(1/2) = 6:
+      a0 = 2 (3, 4, 0)/216 = (1/36, 1/27, 0)      a1 = 1 (-3, -4, 0)/216 = (-1/72, -1/54, 0)
+      p0 = -2/6 - 1/sqrt(11)                      p1 = -1/6 - 2/sqrt(11)
+      B0 = 2*5/216, B1 = 5/216;  P0 = 2/6 + 1/sqrt(11), P1 = 1/6 + 2/sqrt(11)
+    """
+    pos = _bodies([[0, 0, 0], [3, 4, 0]], [1.0, 2.0])
+    r = orc.accel_exact(pos, 11.0)
+    tol = 4e-16
+    _close(r["acc"], [[1 / 36, 1 / 27, 0], [-1 / 72, -1 / 54, 0]], tol, "3-4-5 accelerations")
+    s11 = math.sqrt(11.0)
+    _close(r["pot"], [-1 / 3 - 1 / s11, -1 / 6 - 2 / s11], 4 * tol, "3-4-5 potentials")
+    _close(r["bound_a"], [10 / 216, 5 / 216], tol, "3-4-5 B scales")
+    _close(r["bound_p"], [1 / 3 + 1 / s11, 1 / 6 + 2 / s11], 4 * tol, "3-4-5 P scales")
+
+
+def pin_two_body_random(orc):
+    """Random pairs: each body is pulled toward the other with m_other |r| / (r^2+eps2)^(3/2)."""
+    rng = np.random.Generator(np.random.PCG64(2))
+    for _ in range(20):
+        x = rng.normal(size=(2, 3))
+        m = rng.uniform(0.1, 3.0, size=2)
+        e2 = 10.0 ** rng.uniform(-6, 0)
+        r = orc.accel_exact(_bodies(x, m), e2)
+        d = x[1] - x[0]
+        dist = float(np.sqrt(d @ d))
+        mag0 = m[1] * dist / (dist * dist + e2) ** 1.5
+        mag1 = m[0] * dist / (dist * dist + e2) ** 1.5
+        unit = d / dist
+        _close(r["acc"][0], mag0 * unit, 1e-14 * mag0, "two-body a0 (toward body 1)")
+        _close(r["acc"][1], -mag1 * unit, 1e-14 * mag1, "two-body a1 (toward body 0)")
+        p0 = -m[1] / math.hypot(dist, math.sqrt(e2)) - m[0] / math.sqrt(e2)
+        _close(r["pot"][0], p0, 1e-14 * abs(p0), "two-body p0")
+
+
+# ------------------------------------------------------------ brute force
+
+def _decimal_sums(pos: np.ndarray, eps2: float):
+    getcontext().prec = 50
+    n = pos.shape[0]
+    P = [[Decimal(float(v)) for v in row] for row in pos]
+    e2 = Decimal(float(eps2))
+    out = []
+    for i in range(n):
+        ax = ay = az = p = B = Pp = Decimal(0)
+        for j in range(n):
+            dx = P[j][0] - P[i][0]
+            dy = P[j][1] - P[i][1]
+            dz = P[j][2] - P[i][2]
+            r2 = dx * dx + dy * dy + dz * dz
+            q = r2 + e2
+            sq = q.sqrt()
+            w = P[j][3] / (q * sq)
+            ax += w * dx
+            ay += w * dy
+            az += w * dz
+            p -= P[j][3] / sq
+            B += w * r2.sqrt()
+            Pp += P[j][3] / sq
+        out.append((float(ax), float(ay), float(az), float(p), float(B), float(Pp)))
+    return np.array(out)
+
+
+def pin_decimal_bruteforce(orc):
+    """Random small systems against 50-digit decimal arithmetic of the same sum."""
+    rng = np.random.Generator(np.random.PCG64(3))
+    for n in (3, 5, 8, 13, 16):
+        x = rng.uniform(-1, 1, size=(n, 3))
+        m = rng.uniform(0.5, 1.5, size=n)
+        e2 = 10.0 ** rng.uniform(-5, -1)
+        pos = _bodies(x, m)
+        r = orc.accel_exact(pos, e2)
+        d = _decimal_sums(pos, e2)
+        B = d[:, 4]
+        Pp = d[:, 5]
+        err_a = np.linalg.norm(r["acc"] - d[:, :3], axis=1)
+        if np.any(err_a > 1e-13 * B):
+            raise AssertionError(f"decimal brute force, accel, N={n}: {err_a / B}")
+        _close(r["pot"], d[:, 3], 1e-13 * Pp, f"decimal brute force, potential, N={n}")
+        _close(r["bound_a"], B, 1e-13 * B, f"decimal brute force, B, N={n}")
+        _close(r["bound_p"], Pp, 1e-13 * Pp, f"decimal brute force, P, N={n}")
+
+
+# ---------------------------------------------------------------- symmetry
+
+def pin_symmetric_centre(orc):
+    """Equal masses on the cube's 8 vertices or the octahedron's 6 vertices plus a central body.
+
+    By symmetry the central body feels no force, and every vertex is pulled
+    straight toward the centre.
+    """
+    cube = np.array([[sx, sy, sz] for sx in (-1, 1) for sy in (-1, 1) for sz in (-1, 1)], float)
+    octa = np.array([[1, 0, 0], [-1, 0, 0], [0, 1, 0], [0, -1, 0], [0, 0, 1], [0, 0, -1]], float)
+    for verts, scale, e2 in [(cube, 0.5, 1e-2), (octa, 1.7, 1e-4), (cube, 3.0, 1.0)]:
+        xyz = np.concatenate([np.zeros((1, 3)), scale * verts])
+        m = np.concatenate([[2.0], np.full(len(verts), 0.75)])
+        r = orc.accel_exact(_bodies(xyz, m), e2)
+        B = r["bound_a"]
+        if np.linalg.norm(r["acc"][0]) > 1e-15 * B[0]:
+            raise AssertionError(f"force at the centre of a symmetric set: {r['acc'][0]}")
+        for k in range(1, len(xyz)):
+            a = r["acc"][k]
+            x = xyz[k]
+            if np.linalg.norm(np.cross(a, x)) > 1e-14 * B[k] * np.linalg.norm(x) or a @ x >= 0:
+                raise AssertionError(f"vertex {k} not pulled toward the centre: a={a}, x={x}")
+        # all vertices are equivalent: same |a| and same p
+        mags = np.linalg.norm(r["acc"][1:], axis=1)
+        _close(mags, np.full_like(mags, mags[0]), 1e-14 * mags[0], "vertex |a| equal")
+        _close(r["pot"][1:], np.full(len(verts), r["pot"][1]), 1e-14 * abs(r["pot"][1]),
+               "vertex p equal")
+
+
+def pin_ring(orc):
+    """n equal masses m on a circle of radius R (a regular polygon), plane z = 0.
+
+    Body i at angle t_i; body j at t_i + 2 pi k/n. The chord has
+    |r|^2 = 4 R^2 sin^2(pi k/n) and its component toward the centre is
+    2 R sin^2(pi k/n); tangential parts cancel between k and n - k. So every
+    body feels an inward pull of
+        A = m sum_{k=1}^{n-1} 2 R sin^2(pi k/n) / (4 R^2 sin^2(pi k/n) + eps2)^(3/2)
+    and has potential
+        p = -m sum_{k=1}^{n-1} (4 R^2 sin^2(pi k/n) + eps2)^(-1/2) - m/sqrt(eps2).
+    """
+    for n, R, e2, m, t0 in [(3, 1.0, 1e-3, 1.0, 0.1), (4, 2.5, 0.3, 0.5, 0.0),
+                            (7, 1.3, 1e-6, 2.0, 1.0), (12, 0.8, 1e-2, 1 / 12, 0.37)]:
+        t = t0 + 2 * np.pi * np.arange(n) / n
+        xyz = np.stack([R * np.cos(t), R * np.sin(t), np.zeros(n)], axis=1)
+        r = orc.accel_exact(_bodies(xyz, m), e2)
+        s2 = np.sin(np.pi * np.arange(1, n) / n) ** 2
+        A = m * np.sum(2 * R * s2 / (4 * R * R * s2 + e2) ** 1.5)
+        p = -m * np.sum(1 / np.sqrt(4 * R * R * s2 + e2)) - m / math.sqrt(e2)
+        want = -A * xyz / R
+        B = r["bound_a"]
+        err = np.linalg.norm(r["acc"] - want, axis=1)
+        if np.any(err > 1e-13 * B):
+            raise AssertionError(f"ring n={n}: accel err/B {err / B}")
+        _close(r["pot"], np.full(n, p), 1e-13 * abs(p), f"ring n={n} potential")
+        if np.any(r["acc"][:, 2] != 0.0):
+            raise AssertionError("ring: out-of-plane acceleration")
+
+
+def pin_third_law(orc):
+    """Newton's third law: pair forces cancel, so sum_i m_i a_i = 0 up to rounding."""
+    rng = np.random.Generator(np.random.PCG64(4))
+    for n, e2 in [(50, 1e-4), (200, 1e-2), (97, 1e-6)]:
+        x = rng.uniform(-1, 1, size=(n, 3))
+        m = rng.uniform(0.1, 2.0, size=n)
+        r = orc.accel_exact(_bodies(x, m), e2)
+        tot = np.linalg.norm((m[:, None] * r["acc"]).sum(axis=0))
+        scale = float((m * r["bound_a"]).sum())
+        if tot > 1e-12 * scale:
+            raise AssertionError(f"third law: |sum m a| = {tot:.3e} vs scale {scale:.3e}")
+
+
+# ---------------------------------------------------------------- exact scaling
+
+def pin_mass_scaling(orc):
+    """Doubling every mass doubles a, p, B and P exactly (power-of-two scaling)."""
+    rng = np.random.Generator(np.random.PCG64(5))
+    x = rng.uniform(-1, 1, size=(40, 3))
+    m = rng.uniform(0.5, 1.5, size=40)
+    r1 = orc.accel_exact(_bodies(x, m), 1e-3)
+    r2 = orc.accel_exact(_bodies(x, 2 * m), 1e-3)
+    for k in ("acc", "pot", "bound_a", "bound_p"):
+        if not np.array_equal(r2[k], 2 * r1[k]):
+            raise AssertionError(f"mass scaling not exact for {k}")
+
+
+def pin_length_scaling(orc):
+    """Positions x 2^k and eps2 x 4^k give a x 2^-2k and p x 2^-k exactly."""
+    rng = np.random.Generator(np.random.PCG64(6))
+    x = rng.uniform(-1, 1, size=(40, 3))
+    m = rng.uniform(0.5, 1.5, size=40)
+    r1 = orc.accel_exact(_bodies(x, m), 1e-3)
+    for k in (-3, 2, 5):
+        s = 2.0 ** k
+        r2 = orc.accel_exact(_bodies(s * x, m), 1e-3 * s * s)
+        if not np.array_equal(r2["acc"], r1["acc"] / (s * s)):
+            raise AssertionError(f"length scaling 2^{k}: acceleration")
+        if not np.array_equal(r2["pot"], r1["pot"] / s):
+            raise AssertionError(f"length scaling 2^{k}: potential")
+
+
+def pin_translation(orc):
+    """On a dyadic grid differences are exact, so a shift changes nothing, bit for bit."""
+    rng = np.random.Generator(np.random.PCG64(7))
+    k = rng.integers(-512, 512, size=(60, 3))
+    x = k * 2.0 ** -10
+    m = rng.integers(2048, 6144, size=60) * 2.0 ** -12
+    r1 = orc.accel_exact(_bodies(x, m), 2.0 ** -10)
+    r2 = orc.accel_exact(_bodies(x + np.array([0.5, -0.25, 0.125]), m), 2.0 ** -10)
+    for key in ("acc", "pot", "bound_a", "bound_p"):
+        if not np.array_equal(r1[key], r2[key]):
+            raise AssertionError(f"translation changed {key}")
+
+
+# ---------------------------------------------------------------- Euler
+
+def pin_euler_free_particle(orc):
+    """A lone body feels no force: x advances by dt v per step, v stays put."""
+    pos = np.array([[0.25, -1.5, 3.0, 2.0]])
+    vel = np.array([[1.0, 0.5, -2.0, 0.0]])
+    dt = 0.125
+    p, v = orc.euler_exact(pos, vel, dt, 1e-4, 3)
+    want = pos[0, :3].copy()
+    for _ in range(3):
+        want = want + dt * vel[0, :3]
+    _close(p[0, :3], want, 0.0, "free particle position")
+    _close(v[0], vel[0], 0.0, "free particle velocity")
+    if p[0, 3] != 2.0:
+        raise AssertionError("mass changed by the step")
+
+
+def pin_euler_two_body(orc):
+    """One step of the 3-4-5 system: x' = x + dt v (old v), v' = v + dt a(x) (old x)."""
+    pos = _bodies([[0, 0, 0], [3, 4, 0]], [1.0, 2.0])
+    vel = np.array([[0.5, 0.0, 0.25, 0.0], [0.0, -1.0, 0.0, 0.0]])
+    dt = 0.0625
+    p, v = orc.euler_exact(pos, vel, dt, 11.0, 1)
+    a = np.array([[1 / 36, 1 / 27, 0], [-1 / 72, -1 / 54, 0]])
+    _close(p[:, :3], pos[:, :3] + dt * vel[:, :3], 0.0, "Euler position uses the old velocity")
+    _close(v[:, :3], vel[:, :3] + dt * a, 1e-17, "Euler velocity uses a(x^n)")
+    _close(p[:, 3], pos[:, 3], 0.0, "mass preserved")
+
+
+def pin_energy_two_body(orc):
+    """E = sum m v^2/2 - m0 m1/sqrt(r^2+eps2) for the 3-4-5 system (pair counted once)."""
+    pos = _bodies([[0, 0, 0], [3, 4, 0]], [1.0, 2.0])
+    vel = np.array([[0.5, 0.0, 0.25, 0.0], [0.0, -1.0, 0.0, 0.0]])
+    E, K, W = orc.energy_exact(pos, vel, 11.0)
+    k_want = 0.5 * 1.0 * (0.25 + 0.0625) + 0.5 * 2.0 * 1.0
+    _close([K, W, E], [k_want, -2.0 / 6.0, k_want - 2.0 / 6.0], 1e-16, "two-body energy")
+
+
+ALL_PINS = [
+    pin_single_body,
+    pin_two_body_345,
+    pin_two_body_random,
+    pin_decimal_bruteforce,
+    pin_symmetric_centre,
+    pin_ring,
+    pin_third_law,
+    pin_mass_scaling,
+    pin_length_scaling,
+    pin_translation,
+    pin_euler_free_particle,
+    pin_euler_two_body,
+    pin_energy_two_body,
+]

@@ -1,0 +1,56 @@
+"""Each plausible mistake planted in a copy of oracle.c must trip at least one pin.
+
+The copies are built in a temporary directory on the CPU; the real oracle is
+never modified. This shows the pins are tight enough to catch a dropped term,
+a wrong sign or index, a transposed operand or a wrong update order.
+"""
+
+import shutil
+
+import pytest
+
+import oracle
+import pins
+
+# (name, text in oracle.c, replacement)
+MUTATIONS = [
+    ("r_ij sign flipped in x", "pos[4 * j + 0] - xi", "xi - pos[4 * j + 0]"),
+    ("eps instead of eps^2", "const double q = r2 + eps2;", "const double q = r2 + eps2 * eps2;"),
+    ("self term skipped", "for (int64_t j = 0; j < n; ++j) {\n        const double mj",
+     "for (int64_t j = 0; j < n; ++j) {\n        if (j == i) continue;\n        const double mj"),
+    ("exponent 1 instead of 3/2", "const double q32 = q * sqrt(q);", "const double q32 = q;"),
+    ("target mass instead of source mass", "const double mj = pos[4 * j + 3];",
+     "const double mj = pos[4 * i + 3];"),
+    ("potential sign", "pp -= mj / sqrt(q);", "pp += mj / sqrt(q);"),
+    ("y component uses dx", "ay += mj * dy / q32;", "ay += mj * dx / q32;"),
+    ("last source dropped", "for (int64_t j = 0; j < n; ++j) {\n        const double mj",
+     "for (int64_t j = 0; j < n - 1; ++j) {\n        const double mj"),
+    ("B scale without |r|", "sa += mj * sqrt(r2) / q32;", "sa += mj / q32;"),
+    ("Euler: velocity first",
+     "for (int c = 0; c < 3; ++c) pos[4 * i + c] += dt * vel[4 * i + c];  /* old v */\n"
+     "            for (int c = 0; c < 3; ++c) vel[4 * i + c] += dt * acc[3 * i + c];",
+     "for (int c = 0; c < 3; ++c) vel[4 * i + c] += dt * acc[3 * i + c];\n"
+     "            for (int c = 0; c < 3; ++c) pos[4 * i + c] += dt * vel[4 * i + c];"),
+    ("energy pairs counted twice", "wi[i] = 0.5 * pos[4 * i + 3] * s;", "wi[i] = pos[4 * i + 3] * s;"),
+    ("z acceleration dropped", "az += mj * dz / q32;", "az += 0.0;"),
+]
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_mutation(tmp_path, name, old, new):
+    src = oracle.SRC.read_text()
+    assert src.count(old) == 1, f"mutation anchor not found exactly once: {name}"
+    mutated = tmp_path / "oracle_mut.c"
+    mutated.write_text(src.replace(old, new))
+    lib = oracle.compile_oracle(mutated, tmp_path / "liboracle_mut.so")
+    orc = oracle.Oracle(lib)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            caught.append(pin.__name__)
+        except (ValueError, FloatingPointError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught the planted mistake: {name}"
