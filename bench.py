@@ -1,0 +1,211 @@
+"""Throughput benchmark of the direct all-pairs softened-gravity path on one MI355X.
+
+Default workload: N = 1,048,576 bodies, uniform cube [-1,1]^3, masses uniform in
+[0.5, 1.5]/N, eps2 = 1e-4, one acceleration + potential evaluation per step
+(nbody_accel through the C ABI), inputs resident in HBM.
+
+Prints one JSON line:
+  value    = whole-job body-body interactions per second, in G/s (N^2 per step)
+  gflops   = 20 flop per interaction (the pair-routine count on the CSDN
+             "Cuda Nbody笔记" page / GPU Gems 3 ch. 31)
+  roofline = the acceleration kernel against the FP32 vector peak (ALU bound)
+  cpu_baseline = the fp64 oracle on the host cores, on a bounded target sample
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+if str(ROOT) not in sys.path:
+    sys.path.insert(0, str(ROOT))
+
+FLOPS_PER_INTERACTION = 20  # 3 (r_ij) + 6 (|r|^2 + eps^2) + 4 (inv^3) + 1 (m inv^3) + 6 (a +=)
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X: 256 CU x 2.4 GHz x 256 FP32 flop/clk/CU (packed FMA)
+PROFILE_TRAFFIC = ROOT / "profiles" / "accel_cube1m_traffic.json"
+KERNEL_SOURCES = [ROOT / "direct_all_pairs_amd" / "csrc" / "kernels.hip",
+                  ROOT / "direct_all_pairs_amd" / "csrc" / "kernels.h"]
+
+
+def interactions(n: int) -> int:
+    """Pair interactions per evaluation: every target against every source, self pairs
+    included (N^2), as the GPU Gems 3 ch. 31 study page's lab counts them."""
+    return n * n
+
+
+def tile_global_loads(n: int, p: int) -> int:
+    """Global body loads per evaluation with p-body shared tiles: N^2 / p."""
+    return n * n // p
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(f.read_bytes())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_hash: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel source; else None."""
+    try:
+        d = json.loads(PROFILE_TRAFFIC.read_text())
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_hash") != kernel_hash:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(pos_h, eps2, budget_s: float):
+    """Time the fp64 oracle (as it stands) on a target sample of the same workload."""
+    import numpy as np
+
+    import oracle
+
+    n = pos_h.shape[0]
+    rng = np.random.default_rng(12345)
+    probe = rng.integers(0, n, 64)
+    t0 = time.perf_counter()
+    oracle.accel(pos_h, eps2, targets=probe)
+    t_probe = time.perf_counter() - t0
+    per_target = t_probe / len(probe)
+    nt = int(max(64, min(n, budget_s / max(per_target, 1e-9))))
+    idx = rng.integers(0, n, nt)
+    t0 = time.perf_counter()
+    oracle.accel(pos_h, eps2, targets=idx)
+    t = time.perf_counter() - t0
+    rate = nt * n / t
+    return {
+        "value": rate / 1e9,
+        "unit": "G interactions/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{nt} random targets x all {n} sources (fp64 accel+pot+bounds), {t:.1f} s",
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--n", type=int, default=None, help="override N (default 1,048,576)")
+    ap.add_argument("--bcast", default=None, help="lds | scalar | readlane (default: auto plan)")
+    ap.add_argument("--tpl", type=int, default=0)
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--no-pot", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for cpu_baseline (0 = skip)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import direct_all_pairs_amd as nb
+    import workloads
+
+    dev = torch.device("cuda:0")
+    w = workloads.make("cube1m", n=args.n)
+    n = w.n
+    want_pot = not args.no_pot
+    pos = torch.from_numpy(w.pos).to(dev)
+    acc = torch.empty_like(pos)
+    pot = torch.empty(n, dtype=torch.float32, device=dev) if want_pot else None
+    plan = None
+    if args.bcast or args.tpl or args.splits:
+        plan = nb.make_plan(bcast=args.bcast or 0, tpl=args.tpl, splits=args.splits)
+    eff = nb.nbody_plan_for(n, want_pot)
+    if plan is not None:
+        eff = nb.make_plan(bcast=plan.bcast or eff.bcast, tpl=plan.tpl or eff.tpl,
+                           splits=plan.splits or eff.splits)
+    stream = torch.cuda.current_stream()
+
+    def one_step():
+        if plan is None:
+            nb.nbody_accel(pos, n, float(w.eps2), acc, pot, stream)
+        else:
+            nb.nbody_accel_plan(pos, n, float(w.eps2), acc, pot, plan, stream)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        starts[k].record(stream)
+        one_step()
+        ends[k].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+
+    n_int = interactions(n)
+    ms_per_step = wall * 1e3 / args.steps
+    value = n_int * args.steps / wall / 1e9
+    launch_s = float(np.mean(ev_ms)) / 1e3
+    achieved_tflops = FLOPS_PER_INTERACTION * n_int / launch_s / 1e12
+    khash = kernel_source_hash()
+    traffic = measured_traffic(khash)
+
+    out = {
+        "metric": "G body-body interactions/s & FP32 GFLOPS (20 flop/int) at N=1M, % of FP32 peak",
+        "value": round(value, 3),
+        "unit": "G interactions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"uniform cube N={n}, masses U[0.5,1.5]/N, eps2=1e-4, "
+                         f"{'acceleration + potential' if want_pot else 'acceleration'}, "
+                         "one evaluation per step"),
+            "N": n,
+            "eps2": float(w.eps2),
+            "potential": want_pot,
+            "plan": eff.as_dict(),
+            "device": torch.cuda.get_device_name(dev),
+        },
+        "gflops_at_20": round(FLOPS_PER_INTERACTION * value, 1),
+        "pct_fp32_peak": round(100 * FLOPS_PER_INTERACTION * value / 1e3 / FP32_VECTOR_PEAK_TFLOPS, 2),
+        "roofline": {
+            "bound": "alu",
+            "achieved": round(achieved_tflops, 3),
+            "peak": FP32_VECTOR_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved_tflops / FP32_VECTOR_PEAK_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel": "accel kernel (nbody_accel), HIP events on its stream",
+            "launch_ms_mean": round(launch_s * 1e3, 4),
+            "kernel_source_hash": khash,
+        },
+    }
+    if args.cpu_budget > 0:
+        out["cpu_baseline"] = cpu_baseline(w.pos, w.eps2, args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

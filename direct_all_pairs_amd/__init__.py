@@ -1,0 +1,176 @@
+"""Python binding of the gfx950 direct all-pairs softened-gravity library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libnbody_amd.so`` (C ABI in include/nbody.h). The functions with
+the C names take raw device pointers or torch tensors (their ``data_ptr()`` is
+passed); ``accel`` and ``step`` are small conveniences on torch tensors that
+allocate outputs with torch and call the same entry points on the current
+torch stream.
+
+Importing this module loads the library and fails loudly if it has not been
+built (``python -m direct_all_pairs_amd.build`` or ``__graft_entry__.build()``).
+There is no CPU fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+_PKG = Path(__file__).resolve().parent
+LIB_PATH = _PKG / "libnbody_amd.so"
+
+NBODY_OK, NBODY_EINVAL, NBODY_EALIGN, NBODY_EHIP, NBODY_ENOMEM = 0, 1, 2, 3, 4
+BCAST_AUTO, BCAST_LDS, BCAST_SCALAR, BCAST_READLANE = 0, 1, 2, 3
+BCAST_NAMES = {BCAST_LDS: "lds", BCAST_SCALAR: "scalar", BCAST_READLANE: "readlane"}
+
+
+class NbodyError(RuntimeError):
+    def __init__(self, code: int, func: str, msg: str):
+        super().__init__(f"{func} returned {code}: {msg}")
+        self.code = code
+
+
+class nbody_plan(ctypes.Structure):
+    _fields_ = [("bcast", ctypes.c_int32), ("tpl", ctypes.c_int32),
+                ("splits", ctypes.c_int32), ("chunk", ctypes.c_int32)]
+
+    def as_dict(self) -> dict:
+        return {"bcast": BCAST_NAMES.get(self.bcast, self.bcast), "tpl": self.tpl,
+                "splits": self.splits, "chunk": self.chunk}
+
+
+# torch (device memory and streams) is imported first: its bundled HIP runtime
+# carries the same soname (libamdhip64.so.7) the library links against, so the
+# loader binds the library to the runtime already in the process instead of
+# starting a second one that would not see the device.
+import torch  # noqa: E402,F401
+
+if not LIB_PATH.exists():
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m direct_all_pairs_amd.build` "
+                      "(hipcc, gfx950) first. There is no CPU fallback.")
+
+_lib = ctypes.CDLL(str(LIB_PATH))
+_vp, _i64, _f32, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+_lib.nbody_accel.argtypes = [_vp, _i64, _f32, _vp, _vp, _vp]
+_lib.nbody_accel_plan.argtypes = [_vp, _i64, _f32, _vp, _vp, ctypes.POINTER(nbody_plan), _vp]
+_lib.nbody_step.argtypes = [_vp, _vp, _i64, _f32, _f32, _i64, _vp]
+_lib.nbody_plan_for.argtypes = [_i64, _int, ctypes.POINTER(nbody_plan)]
+_lib.nbody_last_error.restype = ctypes.c_char_p
+_lib.nbody_release_workspace.argtypes = []
+_lib.nbody_version.restype = ctypes.c_char_p
+for _f in ("nbody_accel", "nbody_accel_plan", "nbody_step", "nbody_plan_for",
+           "nbody_release_workspace"):
+    getattr(_lib, _f).restype = _int
+
+EXPORTS = ("nbody_accel", "nbody_accel_plan", "nbody_step", "nbody_plan_for",
+           "nbody_last_error", "nbody_release_workspace", "nbody_version")
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()  # torch tensor
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream  # torch.cuda.Stream
+
+
+def _check(rc: int, func: str) -> int:
+    if rc != NBODY_OK:
+        raise NbodyError(rc, func, nbody_last_error())
+    return rc
+
+
+def nbody_last_error() -> str:
+    return _lib.nbody_last_error().decode()
+
+
+def nbody_version() -> str:
+    return _lib.nbody_version().decode()
+
+
+def nbody_release_workspace() -> int:
+    return _check(_lib.nbody_release_workspace(), "nbody_release_workspace")
+
+
+def nbody_accel(pos_xyzm, N: int, eps2: float, acc_out, pot_out=None, stream=None,
+                check: bool = True) -> int:
+    rc = _lib.nbody_accel(_ptr(pos_xyzm), int(N), float(eps2), _ptr(acc_out), _ptr(pot_out),
+                          _stream(stream))
+    return _check(rc, "nbody_accel") if check else rc
+
+
+def nbody_accel_plan(pos_xyzm, N: int, eps2: float, acc_out, pot_out=None, plan=None,
+                     stream=None, check: bool = True) -> int:
+    p = None
+    if plan is not None:
+        p = plan if isinstance(plan, nbody_plan) else make_plan(**plan)
+    rc = _lib.nbody_accel_plan(_ptr(pos_xyzm), int(N), float(eps2), _ptr(acc_out),
+                               _ptr(pot_out), ctypes.byref(p) if p is not None else None,
+                               _stream(stream))
+    return _check(rc, "nbody_accel_plan") if check else rc
+
+
+def nbody_step(pos, vel, N: int, dt: float, eps2: float, nsteps: int, stream=None,
+               check: bool = True) -> int:
+    rc = _lib.nbody_step(_ptr(pos), _ptr(vel), int(N), float(dt), float(eps2), int(nsteps),
+                         _stream(stream))
+    return _check(rc, "nbody_step") if check else rc
+
+
+def nbody_plan_for(N: int, want_pot: bool = False) -> nbody_plan:
+    p = nbody_plan()
+    _check(_lib.nbody_plan_for(int(N), int(bool(want_pot)), ctypes.byref(p)), "nbody_plan_for")
+    return p
+
+
+def make_plan(bcast=0, tpl=0, splits=0, chunk=0) -> nbody_plan:
+    if isinstance(bcast, str):
+        bcast = {v: k for k, v in BCAST_NAMES.items()}[bcast]
+    return nbody_plan(int(bcast), int(tpl), int(splits), int(chunk))
+
+
+# ------------------------------------------------------------ torch conveniences
+
+def _bodies(t, name):
+    import torch
+
+    if not (isinstance(t, torch.Tensor) and t.is_cuda and t.dtype == torch.float32
+            and t.dim() == 2 and t.shape[1] == 4 and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous float32 CUDA tensor of shape (N, 4)")
+    return t
+
+
+def accel(pos, eps2: float, pot: bool = True, plan=None):
+    """Accelerations (N, 4) with w = 0 and, if pot, potentials (N,), on the current stream."""
+    import torch
+
+    _bodies(pos, "pos")
+    n = pos.shape[0]
+    acc = torch.empty_like(pos)
+    p = torch.empty(n, dtype=torch.float32, device=pos.device) if pot else None
+    if plan is None:
+        nbody_accel(pos, n, eps2, acc, p)
+    else:
+        nbody_accel_plan(pos, n, eps2, acc, p, plan)
+    return acc, p
+
+
+def step(pos, vel, dt: float, eps2: float, nsteps: int = 1):
+    """nsteps Euler steps in place on pos and vel (N, 4) tensors, on the current stream."""
+    _bodies(pos, "pos")
+    _bodies(vel, "vel")
+    if vel.shape != pos.shape:
+        raise ValueError("pos and vel shapes differ")
+    nbody_step(pos, vel, pos.shape[0], dt, eps2, nsteps)
+    return pos, vel

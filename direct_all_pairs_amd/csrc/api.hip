@@ -1,0 +1,321 @@
+// C ABI of the library (declared in include/nbody.h): argument checks, launch
+// planning, the cached split-j scratch area and the step loop.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cfloat>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "../../include/nbody.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok()
+{
+    g_err.clear();
+    return NBODY_OK;
+}
+
+int hip_fail(hipError_t e, const char *what)
+{
+    return fail(NBODY_EHIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb)
+{
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// eps2 must be a positive, finite, normal float: the softening is what makes
+// the j = i term finite (Degawa, "N 体問題", slide 12), and the rsq of a
+// denormal would not be.
+bool eps2_ok(float e) { return std::isfinite(e) && e >= FLT_MIN; }
+
+// ------------------------------------------------------------ device facts
+
+std::mutex g_mu;
+std::map<int, int> g_cus;  // device -> compute units
+
+int device_cus(int dev, int *cus)
+{
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_cus.find(dev);
+    if (it != g_cus.end()) {
+        *cus = it->second;
+        return NBODY_OK;
+    }
+    int v = 0;
+    hipError_t e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(multiprocessor count)");
+    if (v <= 0) v = 1;
+    g_cus[dev] = v;
+    *cus = v;
+    return NBODY_OK;
+}
+
+// ------------------------------------------------------------ scratch cache
+
+struct Scratch {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
+
+// Returns scratch of at least `bytes` for (device, stream). Growing frees the
+// old block first; hipFree waits for the device, so work still queued on the
+// old block finishes before it is released.
+int scratch_get(int dev, hipStream_t stream, size_t bytes, void **out)
+{
+    std::lock_guard<std::mutex> lk(g_mu);
+    Scratch &s = g_scratch[{dev, stream}];
+    if (s.bytes < bytes) {
+        if (s.ptr) {
+            hipError_t e = hipFree(s.ptr);
+            s.ptr = nullptr;
+            s.bytes = 0;
+            if (e != hipSuccess) return hip_fail(e, "hipFree(scratch)");
+        }
+        size_t want = bytes + bytes / 4;  // some headroom for nearby sizes
+        void *p = nullptr;
+        hipError_t e = hipMalloc(&p, want);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(NBODY_ENOMEM, "hipMalloc(%zu bytes of scratch) failed: %s", want,
+                        hipGetErrorString(e));
+        }
+        s.ptr = p;
+        s.bytes = want;
+    }
+    *out = s.ptr;
+    return NBODY_OK;
+}
+
+// ------------------------------------------------------------ planning
+
+constexpr int kMaxSplits = 4096;
+
+int valid_tpl(int t) { return t == 1 || t == 2 || t == 4 || t == 8; }
+
+// Automatic layout. Targets per lane grow with N; split-j adds source chunks
+// until there are about `waves_per_simd` waves for every SIMD (4 per CU), with
+// chunks of at least kFlush sources.
+void auto_plan(int64_t n, bool pot, int cus, nbody_plan *p)
+{
+    (void)pot;
+    if (p->bcast == NBODY_BCAST_AUTO) p->bcast = NBODY_BCAST_SCALAR;
+    if (p->tpl == 0) p->tpl = n >= (1 << 18) ? 4 : (n >= (1 << 15) ? 2 : 1);
+    if (p->splits == 0) {
+        const int64_t waves_per_simd = 4;
+        const int64_t want = (int64_t)cus * 4 * waves_per_simd;
+        const int64_t tw = (n + 64 * p->tpl - 1) / (64 * p->tpl);  // target waves
+        int64_t s = (want + tw - 1) / tw;
+        const int64_t smax = (n + nbk::kFlush - 1) / nbk::kFlush;
+        if (s > smax) s = smax;
+        if (s < 1) s = 1;
+        if (s > kMaxSplits) s = kMaxSplits;
+        p->splits = (int32_t)s;
+    }
+}
+
+// Final chunking: chunk is a multiple of kFlush and S = ceil(N / chunk).
+void finish_plan(int64_t n, nbody_plan *p)
+{
+    int64_t s = p->splits;
+    int64_t c = (n + s - 1) / s;
+    c = (c + nbk::kFlush - 1) / nbk::kFlush * nbk::kFlush;
+    if (c < nbk::kFlush) c = nbk::kFlush;
+    s = (n + c - 1) / c;
+    if (s < 1) s = 1;
+    if (c > INT32_MAX) c = (int64_t)INT32_MAX / nbk::kFlush * nbk::kFlush;
+    p->splits = (int32_t)s;
+    p->chunk = (int32_t)c;
+}
+
+int make_plan(int64_t n, bool pot, const nbody_plan *user, int *dev_out, nbody_plan *p)
+{
+    *p = user ? *user : nbody_plan{0, 0, 0, 0};
+    if (p->bcast < 0 || p->bcast > NBODY_BCAST_READLANE)
+        return fail(NBODY_EINVAL, "plan.bcast=%d is not a NBODY_BCAST_* value", p->bcast);
+    if (p->tpl != 0 && !valid_tpl(p->tpl))
+        return fail(NBODY_EINVAL, "plan.tpl=%d must be 0, 1, 2, 4 or 8", p->tpl);
+    if (p->splits < 0 || p->splits > kMaxSplits)
+        return fail(NBODY_EINVAL, "plan.splits=%d must be in [0, %d]", p->splits, kMaxSplits);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    int cus = 0;
+    int rc = device_cus(dev, &cus);
+    if (rc != NBODY_OK) return rc;
+    auto_plan(n, pot, cus, p);
+    finish_plan(n, p);
+    *dev_out = dev;
+    return NBODY_OK;
+}
+
+unsigned grid_x(int64_t n, int tpl)
+{
+    const int64_t per = (int64_t)nbk::kWG * tpl;
+    return (unsigned)((n + per - 1) / per);
+}
+
+int check_n(int64_t n)
+{
+    if (n < 0) return fail(NBODY_EINVAL, "N=%lld must be >= 0", (long long)n);
+    if (n > INT32_MAX) return fail(NBODY_EINVAL, "N=%lld exceeds 2^31-1", (long long)n);
+    return NBODY_OK;
+}
+
+// Enqueue one evaluation: accelerations (and potentials) into acc_out/pot_out,
+// or with euler_pos/euler_vel set, one Euler step applied to them instead.
+int enqueue_eval(const float4 *pos, int n, float eps2, float4 *acc_out, float *pot_out,
+                 const nbody_plan &p, int dev, hipStream_t stream, float4 *euler_pos,
+                 float4 *euler_vel, float dt)
+{
+    const bool pot = pot_out != nullptr;
+    const bool step = euler_pos != nullptr;
+    nbk::AccelArgs a{pos, n, eps2, p.chunk, acc_out, pot_out, nullptr};
+    if (p.splits > 1 || step) {
+        void *ws = nullptr;
+        const size_t bytes = (size_t)p.splits * (size_t)n * sizeof(float4);
+        int rc = scratch_get(dev, stream, bytes, &ws);
+        if (rc != NBODY_OK) return rc;
+        a.part = (float4 *)ws;
+    }
+    hipError_t e = nbk::launch_accel(p.bcast, p.tpl, pot, grid_x(n, p.tpl), (unsigned)p.splits, a,
+                                     stream);
+    if (e != hipSuccess) return hip_fail(e, "accel kernel launch");
+    if (step) {
+        e = nbk::launch_euler(a.part, n, p.splits, euler_pos, euler_vel, dt, stream);
+        if (e != hipSuccess) return hip_fail(e, "euler kernel launch");
+    } else if (a.part) {
+        e = nbk::launch_combine(a.part, n, p.splits, acc_out, pot_out, stream);
+        if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+    }
+    return NBODY_OK;
+}
+
+int accel_impl(const nbody_f4 *pos, int64_t N, float eps2, nbody_f4 *acc, float *pot,
+               const nbody_plan *plan, hipStream_t stream)
+{
+    int rc = check_n(N);
+    if (rc != NBODY_OK) return rc;
+    if (N == 0) return ok();
+    if (!pos) return fail(NBODY_EINVAL, "pos_xyzm is NULL");
+    if (!acc) return fail(NBODY_EINVAL, "acc_out is NULL");
+    if (!eps2_ok(eps2))
+        return fail(NBODY_EINVAL, "eps2=%g must be a positive, finite, normal float", (double)eps2);
+    if (!aligned(pos, 16)) return fail(NBODY_EALIGN, "pos_xyzm is not 16-byte aligned");
+    if (!aligned(acc, 16)) return fail(NBODY_EALIGN, "acc_out is not 16-byte aligned");
+    if (pot && !aligned(pot, 4)) return fail(NBODY_EALIGN, "pot_out is not 4-byte aligned");
+    const size_t b16 = (size_t)N * 16, b4 = (size_t)N * 4;
+    if (overlap(pos, b16, acc, b16)) return fail(NBODY_EINVAL, "acc_out overlaps pos_xyzm");
+    if (pot && (overlap(pot, b4, pos, b16) || overlap(pot, b4, acc, b16)))
+        return fail(NBODY_EINVAL, "pot_out overlaps another buffer");
+    nbody_plan p;
+    int dev = 0;
+    rc = make_plan(N, pot != nullptr, plan, &dev, &p);
+    if (rc != NBODY_OK) return rc;
+    rc = enqueue_eval((const float4 *)pos, (int)N, eps2, (float4 *)acc, pot, p, dev, stream,
+                      nullptr, nullptr, 0.0f);
+    return rc == NBODY_OK ? ok() : rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nbody_accel(const nbody_f4 *pos_xyzm, int64_t N, float eps2, nbody_f4 *acc_out,
+                float *pot_out, hipStream_t stream)
+{
+    return accel_impl(pos_xyzm, N, eps2, acc_out, pot_out, nullptr, stream);
+}
+
+int nbody_accel_plan(const nbody_f4 *pos_xyzm, int64_t N, float eps2, nbody_f4 *acc_out,
+                     float *pot_out, const nbody_plan *plan, hipStream_t stream)
+{
+    return accel_impl(pos_xyzm, N, eps2, acc_out, pot_out, plan, stream);
+}
+
+int nbody_step(nbody_f4 *pos, nbody_f4 *vel, int64_t N, float dt, float eps2, int64_t nsteps,
+               hipStream_t stream)
+{
+    int rc = check_n(N);
+    if (rc != NBODY_OK) return rc;
+    if (nsteps < 0) return fail(NBODY_EINVAL, "nsteps=%lld must be >= 0", (long long)nsteps);
+    if (N == 0 || nsteps == 0) return ok();
+    if (!pos) return fail(NBODY_EINVAL, "pos is NULL");
+    if (!vel) return fail(NBODY_EINVAL, "vel is NULL");
+    if (!std::isfinite(dt)) return fail(NBODY_EINVAL, "dt=%g must be finite", (double)dt);
+    if (!eps2_ok(eps2))
+        return fail(NBODY_EINVAL, "eps2=%g must be a positive, finite, normal float", (double)eps2);
+    if (!aligned(pos, 16)) return fail(NBODY_EALIGN, "pos is not 16-byte aligned");
+    if (!aligned(vel, 16)) return fail(NBODY_EALIGN, "vel is not 16-byte aligned");
+    const size_t b16 = (size_t)N * 16;
+    if (overlap(pos, b16, vel, b16)) return fail(NBODY_EINVAL, "vel overlaps pos");
+    nbody_plan p;
+    int dev = 0;
+    rc = make_plan(N, false, nullptr, &dev, &p);
+    if (rc != NBODY_OK) return rc;
+    for (int64_t s = 0; s < nsteps; ++s) {
+        rc = enqueue_eval((const float4 *)pos, (int)N, eps2, nullptr, nullptr, p, dev, stream,
+                          (float4 *)pos, (float4 *)vel, dt);
+        if (rc != NBODY_OK) return rc;
+    }
+    return ok();
+}
+
+int nbody_plan_for(int64_t N, int want_pot, nbody_plan *out)
+{
+    if (!out) return fail(NBODY_EINVAL, "out is NULL");
+    int rc = check_n(N);
+    if (rc != NBODY_OK) return rc;
+    int dev = 0;
+    nbody_plan p;
+    rc = make_plan(N < 1 ? 1 : N, want_pot != 0, nullptr, &dev, &p);
+    if (rc != NBODY_OK) return rc;
+    *out = p;
+    return ok();
+}
+
+const char *nbody_last_error(void) { return g_err.c_str(); }
+
+int nbody_release_workspace(void)
+{
+    std::lock_guard<std::mutex> lk(g_mu);
+    int rc = NBODY_OK;
+    for (auto &kv : g_scratch) {
+        if (kv.second.ptr) {
+            hipError_t e = hipFree(kv.second.ptr);
+            if (e != hipSuccess && rc == NBODY_OK) rc = hip_fail(e, "hipFree(scratch)");
+        }
+    }
+    g_scratch.clear();
+    return rc == NBODY_OK ? ok() : rc;
+}
+
+const char *nbody_version(void) { return "direct_all_pairs_amd 0.1.0 (gfx950)"; }
+
+}  // extern "C"

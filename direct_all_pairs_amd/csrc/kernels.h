@@ -1,0 +1,38 @@
+// Internal interface between the C-ABI layer (api.hip) and the gfx950 kernels
+// (kernels.hip). Not installed; the public interface is include/nbody.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace nbk {
+
+// Threads per workgroup of the acceleration kernels (4 waves of 64).
+constexpr int kWG = 256;
+// Sources summed into a fresh per-target partial before it is added to the
+// running total (two-level accumulation). Also the LDS tile size and the
+// granularity of split-j chunk boundaries.
+constexpr int kFlush = 256;
+
+struct AccelArgs {
+    const float4 *pos;  // N bodies (x, y, z, m)
+    int n;              // N
+    float eps2;         // softening squared (positive normal float)
+    int chunk;          // sources per split-j chunk, multiple of kFlush; chunk s = blockIdx.y
+    float4 *acc_out;    // direct mode: (ax, ay, az, 0) per body
+    float *pot_out;     // direct mode: p_i per body, or nullptr
+    float4 *part;       // split mode (non-null): part[s*N + i] = (ax, ay, az, sum m/r)
+};
+
+// Launch the acceleration kernel: grid (ceil(N / (kWG*tpl)), S), block kWG.
+hipError_t launch_accel(int bcast, int tpl, bool pot, unsigned grid_x, unsigned splits,
+                        const AccelArgs &args, hipStream_t stream);
+
+// acc_out[i] = (sum_s part[s][i].xyz, 0); pot_out[i] = -sum_s part[s][i].w (if non-null).
+hipError_t launch_combine(const float4 *part, int n, int splits, float4 *acc_out, float *pot_out,
+                          hipStream_t stream);
+
+// a = sum_s part[s][i].xyz, then pos.xyz += dt * vel.xyz; vel.xyz += dt * a.
+hipError_t launch_euler(const float4 *part, int n, int splits, float4 *pos, float4 *vel, float dt,
+                        hipStream_t stream);
+
+}  // namespace nbk

@@ -1,0 +1,146 @@
+/*
+ * nbody.h - C ABI of the MI355X (gfx950) direct all-pairs softened-gravity library.
+ *
+ * What the library computes (G = 1, sums over ALL j including j = i):
+ *   a_i = sum_j m_j (x_j - x_i) / (|x_j - x_i|^2 + eps2)^(3/2)
+ *   p_i = -sum_j m_j / (|x_j - x_i|^2 + eps2)^(1/2)
+ * and the explicit Euler update, position first with the old velocity:
+ *   x^{n+1} = x^n + dt v^n,   v^{n+1} = v^n + dt a(x^n).
+ * Sources on the pages:
+ *   - Degawa, "N 体問題" lecture slides: slide 4 (acceleration sum), slide 12
+ *     (softening instead of the j != i test; the self term has a zero
+ *     numerator), slides 5-6 and the CPU program's integrate() on slide 15
+ *     (Euler, always position first).
+ *   - Nakasato, "スライド 1" (ATI Stream SDK): No.4 (acceleration and potential;
+ *     input is position + mass, output is acceleration + potential) and No.5
+ *     (four floats per particle, mass in the fourth slot).
+ *   - GPU Gems 3 ch. 31 as retold on the CSDN page "Cuda Nbody笔记" and the
+ *     blog.luozichu.ink study page: float4 bodies, r_ij = x_j - x_i, the
+ *     float4 acceleration with w = 0.
+ * Readings where the pages are damaged or silent: the potential includes the
+ * j = i term -m_i/sqrt(eps2) and is negative; eps2 is the softening squared,
+ * added to |r|^2 (the lecture's "Soften" constant).
+ *
+ * Conventions for every call:
+ *   - Every pointer is a DEVICE pointer on the current HIP device, owned by the
+ *     caller; the library keeps none of them after the call returns.
+ *   - Work is enqueued on `stream` (0 = the null stream) and the call returns
+ *     without synchronising. The caller keeps buffers alive until the stream has
+ *     run the work. Asynchronous faults surface at the caller's next sync.
+ *   - All arithmetic is IEEE fp32, round-to-nearest-even, with fused multiply-
+ *     add; results are deterministic: the same call on the same device and
+ *     inputs gives the same bits.
+ *   - Argument checks happen before any HIP call; on failure nothing is
+ *     enqueued and nbody_last_error() describes the problem.
+ *   - The library owns a cached scratch area per (device, stream) for split-j
+ *     partial sums and the accelerations inside nbody_step. Calls that overlap
+ *     in time on the SAME stream are ordered by the stream; calls on different
+ *     streams use different scratch areas.
+ */
+#ifndef NBODY_H
+#define NBODY_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* One body: (x, y, z, m) for positions, (vx, vy, vz, unused) for velocities,
+ * (ax, ay, az, 0) for accelerations. 16 bytes, 16-byte aligned. */
+typedef struct nbody_f4 {
+    float x, y, z, w;
+} nbody_f4;
+
+/* Return codes. */
+enum {
+    NBODY_OK = 0,
+    NBODY_EINVAL = 1, /* bad argument: NULL pointer, N out of range, eps2/dt invalid, overlap */
+    NBODY_EALIGN = 2, /* a pointer is not aligned (16 bytes for nbody_f4, 4 for float) */
+    NBODY_EHIP = 3,   /* a HIP runtime call or kernel launch failed */
+    NBODY_ENOMEM = 4  /* the library could not allocate its scratch area */
+};
+
+/* Source-broadcast schemes of the acceleration kernel (nbody_plan.bcast). */
+enum {
+    NBODY_BCAST_AUTO = 0,
+    NBODY_BCAST_LDS = 1,      /* workgroup stages float4 source tiles in LDS; uniform-address LDS reads */
+    NBODY_BCAST_SCALAR = 2,   /* each wave reads sources with scalar (uniform) loads into SGPRs */
+    NBODY_BCAST_READLANE = 3  /* each lane loads one source; v_readlane broadcasts it to the wave */
+};
+
+/* How an evaluation is laid out on the GPU. Zero in a field means "choose
+ * automatically". nbody_plan_for() returns the automatic choice.
+ *   bcast  - source-broadcast scheme (NBODY_BCAST_*).
+ *   tpl    - targets held in registers per lane: 1, 2, 4 or 8.
+ *   splits - split-j source chunks S >= 1. With S > 1 each chunk's partial sums
+ *            go to scratch and a second kernel adds them in ascending chunk
+ *            order (deterministic). S = 1 writes results directly.
+ *   chunk  - (output only) sources per chunk; chunks are [s*chunk, min((s+1)*chunk, N)).
+ * The plan is a pure function of (N, potential wanted, compute-unit count), so
+ * nbody_accel and nbody_step use the same one for the same N. */
+typedef struct nbody_plan {
+    int32_t bcast;
+    int32_t tpl;
+    int32_t splits;
+    int32_t chunk;
+} nbody_plan;
+
+/*
+ * nbody_accel - accelerations, and optionally potentials, of all N bodies.
+ *   pos_xyzm : N bodies (x, y, z, m), read only.
+ *   N        : body count, 0 <= N <= 2^31 - 1. N = 0 enqueues nothing.
+ *   eps2     : softening squared; must be a positive, finite, normal float.
+ *   acc_out  : N records written as (ax, ay, az, 0). Must not overlap pos_xyzm.
+ *   pot_out  : N floats p_i, or NULL to skip the potential. Must not overlap
+ *              the other buffers.
+ * Returns NBODY_OK or an error code.
+ */
+int nbody_accel(const nbody_f4 *pos_xyzm, int64_t N, float eps2, nbody_f4 *acc_out,
+                float *pot_out, hipStream_t stream);
+
+/*
+ * nbody_accel_plan - nbody_accel with an explicit layout (NULL = automatic).
+ * Fields left 0 are chosen automatically. Any accepted plan gives results
+ * within the same error bound; different plans may differ in the last bits.
+ */
+int nbody_accel_plan(const nbody_f4 *pos_xyzm, int64_t N, float eps2, nbody_f4 *acc_out,
+                     float *pot_out, const nbody_plan *plan, hipStream_t stream);
+
+/*
+ * nbody_step - nsteps explicit Euler steps, in place.
+ *   pos : N bodies (x, y, z, m); x, y, z are updated, m is never written.
+ *   vel : N records (vx, vy, vz, w); vx, vy, vz are updated, w is never written.
+ *   dt  : time step, any finite float (0 and negative allowed).
+ *   eps2: as for nbody_accel.
+ *   nsteps >= 0; 0 enqueues nothing.
+ * Each step evaluates a(x^n) with the same plan as nbody_accel(N, no potential),
+ * then x += dt v (old v) and v += dt a, both as single fused multiply-adds.
+ * pos and vel must not overlap.
+ */
+int nbody_step(nbody_f4 *pos, nbody_f4 *vel, int64_t N, float dt, float eps2, int64_t nsteps,
+               hipStream_t stream);
+
+/*
+ * nbody_plan_for - the automatic plan for N bodies (want_pot != 0: with
+ * potential) on the current device. Fills *out. Queries the device's
+ * compute-unit count once per device.
+ */
+int nbody_plan_for(int64_t N, int want_pot, nbody_plan *out);
+
+/* Message describing the last non-OK return on the calling thread ("" if none). */
+const char *nbody_last_error(void);
+
+/* Frees every cached scratch area of the calling process (synchronises the
+ * devices that own them). Later calls allocate again on demand. */
+int nbody_release_workspace(void);
+
+/* Library version string. */
+const char *nbody_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NBODY_H */

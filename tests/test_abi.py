@@ -1,0 +1,112 @@
+"""C-ABI library: loads, exports every declared symbol, rejects bad arguments
+before any HIP call. CPU only (no compute call is made)."""
+
+import ctypes
+import math
+import re
+import subprocess
+from pathlib import Path
+
+import pytest
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "nbody.h"
+
+
+@pytest.fixture(scope="module")
+def nb():
+    lib = ROOT / "direct_all_pairs_amd" / "libnbody_amd.so"
+    if not lib.exists():
+        from direct_all_pairs_amd import build
+
+        build.build()
+    import direct_all_pairs_amd
+
+    return direct_all_pairs_amd
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(nbody_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for f in ("nbody_accel", "nbody_step", "nbody_last_error", "nbody_release_workspace"):
+        assert f in names
+
+
+def test_exports_every_declared_symbol(nb):
+    lib = ctypes.CDLL(str(nb.LIB_PATH))
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", str(nb.LIB_PATH)], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r" T (nbody_\w+)", out))
+    assert set(declared_functions()) <= exported
+    assert set(nb.EXPORTS) == set(declared_functions())
+
+
+def test_library_links_no_oracle_and_no_torch(nb):
+    out = subprocess.run(["ldd", str(nb.LIB_PATH)], capture_output=True, text=True).stdout
+    assert "oracle" not in out and "torch" not in out and "amdhip64" in out
+
+
+def test_product_sources_never_touch_the_oracle():
+    pkg = ROOT / "direct_all_pairs_amd"
+    for f in list(pkg.rglob("*.py")) + list(pkg.rglob("*.hip")) + list(pkg.rglob("*.h")):
+        text = f.read_text()
+        assert "oracle" not in text.lower(), f"{f} mentions the oracle"
+
+
+A = 1 << 20  # a fake, 16-byte aligned address: never dereferenced (checks fail first)
+B = 1 << 28
+
+
+def call_accel(nb, pos=A, n=16, eps2=1e-4, acc=B, pot=None):
+    return nb.nbody_accel(pos, n, eps2, acc, pot, stream=0, check=False)
+
+
+def test_n_zero_is_a_no_op(nb):
+    assert call_accel(nb, pos=None, n=0, acc=None) == nb.NBODY_OK
+    assert nb.nbody_step(None, None, 0, 1e-3, 1e-4, 5, stream=0, check=False) == nb.NBODY_OK
+    assert nb.nbody_step(A, B, 10, 1e-3, 1e-4, 0, stream=0, check=False) == nb.NBODY_OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=-1), 1), (dict(n=2**31), 1), (dict(pos=None), 1), (dict(acc=None), 1),
+    (dict(eps2=0.0), 1), (dict(eps2=-1e-4), 1), (dict(eps2=math.nan), 1),
+    (dict(eps2=math.inf), 1), (dict(eps2=1e-40), 1),
+    (dict(pos=A + 4), 2), (dict(acc=B + 8), 2), (dict(pot=B + 2), 2),
+    (dict(acc=A + 16), 1), (dict(pot=A + 64), 1), (dict(pot=B + 16), 1),
+])
+def test_accel_rejects(nb, kw, code):
+    assert call_accel(nb, **kw) == code
+    assert nb.nbody_last_error() != ""
+
+
+@pytest.mark.parametrize("args,code", [
+    ((A, B, -1, 1e-3, 1e-4, 1), 1), ((A, B, 16, 1e-3, 1e-4, -1), 1),
+    ((None, B, 16, 1e-3, 1e-4, 1), 1), ((A, None, 16, 1e-3, 1e-4, 1), 1),
+    ((A, B, 16, math.nan, 1e-4, 1), 1), ((A, B, 16, math.inf, 1e-4, 1), 1),
+    ((A, B, 16, 1e-3, 0.0, 1), 1), ((A + 4, B, 16, 1e-3, 1e-4, 1), 2),
+    ((A, B + 4, 16, 1e-3, 1e-4, 1), 2), ((A, A + 128, 16, 1e-3, 1e-4, 1), 1),
+])
+def test_step_rejects(nb, args, code):
+    assert nb.nbody_step(*args, stream=0, check=False) == code
+
+
+def test_plan_rejects_bad_fields(nb):
+    for plan in (dict(bcast=7), dict(tpl=3), dict(splits=-1), dict(splits=5000)):
+        rc = nb.nbody_accel_plan(A, 16, 1e-4, B, None, plan=plan, stream=0, check=False)
+        assert rc == nb.NBODY_EINVAL, plan
+
+
+def test_error_raises_in_checked_mode(nb):
+    with pytest.raises(nb.NbodyError) as ei:
+        nb.nbody_accel(A, -5, 1e-4, B, None, stream=0)
+    assert ei.value.code == nb.NBODY_EINVAL and "N=-5" in str(ei.value)
+
+
+def test_version(nb):
+    assert "gfx950" in nb.nbody_version()
