@@ -91,18 +91,76 @@ def cpu_baseline(pos_h, eps2, budget_s: float):
     }
 
 
+def copy_calibration(nbytes: int) -> int:
+    """A plain copy of known size: reads and writes nbytes once per launch."""
+    import torch
+
+    n = nbytes // 16
+    src = torch.ones((n, 4), dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 16, "launches": 2}), flush=True)
+    return 0
+
+
+def sweep(nb, w, pos, acc, pot, args) -> int:
+    """One evaluation (nbody_accel_plan) per layout, HIP-event timed; fastest layout last."""
+    import torch
+
+    n = w.n
+    stream = torch.cuda.current_stream()
+    split_opts = [0, 1, 2, 4, 8, 16, 32, 64]
+    layouts = [("lds", t, wg) for t in (1, 2, 4) for wg in (256, 512)]
+    layouts += [(b, t, 256) for b in ("scalar", "readlane") for t in (1, 2, 4, 8)]
+    results = []
+    for bcast, tpl, wg in layouts:
+        for splits in (split_opts if bcast == "lds" else [0]):
+            plan = nb.make_plan(bcast=bcast, tpl=tpl, splits=splits, wg=wg)
+            if splits and splits * 256 > n:
+                continue
+            for _ in range(max(1, args.warmup)):
+                nb.nbody_accel_plan(pos, n, float(w.eps2), acc, pot, plan, stream)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(args.steps):
+                nb.nbody_accel_plan(pos, n, float(w.eps2), acc, pot, plan, stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / args.steps
+            r = {"workload": args.workload, "N": n, "potential": pot is not None,
+                 "bcast": bcast, "tpl": tpl, "wg": wg, "splits": splits or "auto",
+                 "ms": round(ms, 4), "G_int_per_s": round(interactions(n) / ms / 1e6, 2)}
+            results.append(r)
+            print(json.dumps(r), flush=True)
+    best = max(results, key=lambda r: r["G_int_per_s"])
+    print(json.dumps({"best": best}), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--n", type=int, default=None, help="override N (default 1,048,576)")
+    ap.add_argument("--workload", default="cube1m", choices=sorted(
+        ["cube1m", "plummer65536", "disk4096", "cube2048_steps", "two_plummer300007"]),
+        help="which of the five workloads to time (default: the N=1,048,576 cube)")
+    ap.add_argument("--n", type=int, default=None, help="override N of the workload")
     ap.add_argument("--bcast", default=None, help="lds | scalar | readlane (default: auto plan)")
     ap.add_argument("--tpl", type=int, default=0)
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-pot", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for cpu_baseline (0 = skip)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every (broadcast, targets-per-lane, splits) layout of the workload's "
+                         "evaluation and print one JSON line per layout (no contract line)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES (twice) and exit; "
+                         "used to scale the HBM byte counters of rocprofv3")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -113,14 +171,19 @@ def main(argv=None) -> int:
     import numpy as np
     import torch
 
+    if args.copy_calibration:
+        return copy_calibration(args.copy_calibration)
+
     import direct_all_pairs_amd as nb
     import workloads
 
     dev = torch.device("cuda:0")
-    w = workloads.make("cube1m", n=args.n)
+    w = workloads.make(args.workload, n=args.n)
     n = w.n
-    want_pot = not args.no_pot
+    stepping = w.nsteps > 0 and args.workload != "disk4096"
+    want_pot = (not args.no_pot) and not stepping
     pos = torch.from_numpy(w.pos).to(dev)
+    vel = torch.from_numpy(w.vel).to(dev)
     acc = torch.empty_like(pos)
     pot = torch.empty(n, dtype=torch.float32, device=dev) if want_pot else None
     plan = None
@@ -131,12 +194,18 @@ def main(argv=None) -> int:
         eff = nb.make_plan(bcast=plan.bcast or eff.bcast, tpl=plan.tpl or eff.tpl,
                            splits=plan.splits or eff.splits)
     stream = torch.cuda.current_stream()
+    evals_per_step = w.nsteps if stepping else 1
 
     def one_step():
-        if plan is None:
+        if stepping:
+            nb.nbody_step(pos, vel, n, float(w.dt), float(w.eps2), w.nsteps, stream)
+        elif plan is None:
             nb.nbody_accel(pos, n, float(w.eps2), acc, pot, stream)
         else:
             nb.nbody_accel_plan(pos, n, float(w.eps2), acc, pot, plan, stream)
+
+    if args.sweep:
+        return sweep(nb, w, pos, acc, pot, args)
 
     for _ in range(args.warmup):
         one_step()
@@ -154,13 +223,16 @@ def main(argv=None) -> int:
     wall = time.perf_counter() - t0
     ev_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
 
-    n_int = interactions(n)
+    n_int = interactions(n) * evals_per_step
     ms_per_step = wall * 1e3 / args.steps
     value = n_int * args.steps / wall / 1e9
     launch_s = float(np.mean(ev_ms)) / 1e3
     achieved_tflops = FLOPS_PER_INTERACTION * n_int / launch_s / 1e12
     khash = kernel_source_hash()
-    traffic = measured_traffic(khash)
+    traffic = measured_traffic(khash) if args.workload == "cube1m" and want_pot else None
+    what = (f"{w.nsteps} Euler steps per call (nbody_step)" if stepping else
+            ("acceleration + potential" if want_pot else "acceleration") +
+            ", one evaluation per step (nbody_accel)")
 
     out = {
         "metric": "G body-body interactions/s & FP32 GFLOPS (20 flop/int) at N=1M, % of FP32 peak",
@@ -176,9 +248,7 @@ def main(argv=None) -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": (f"uniform cube N={n}, masses U[0.5,1.5]/N, eps2=1e-4, "
-                         f"{'acceleration + potential' if want_pot else 'acceleration'}, "
-                         "one evaluation per step"),
+            "workload": f"{args.workload}: {workloads.CONFIGS[args.workload]['desc']}; timed: {what}",
             "N": n,
             "eps2": float(w.eps2),
             "potential": want_pot,

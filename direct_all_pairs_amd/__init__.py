@@ -33,11 +33,11 @@ class NbodyError(RuntimeError):
 
 class nbody_plan(ctypes.Structure):
     _fields_ = [("bcast", ctypes.c_int32), ("tpl", ctypes.c_int32),
-                ("splits", ctypes.c_int32), ("chunk", ctypes.c_int32)]
+                ("splits", ctypes.c_int32), ("chunk", ctypes.c_int32), ("wg", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {"bcast": BCAST_NAMES.get(self.bcast, self.bcast), "tpl": self.tpl,
-                "splits": self.splits, "chunk": self.chunk}
+                "splits": self.splits, "chunk": self.chunk, "wg": self.wg}
 
 
 # torch (device memory and streams) is imported first: its bundled HIP runtime
@@ -134,10 +134,10 @@ def nbody_plan_for(N: int, want_pot: bool = False) -> nbody_plan:
     return p
 
 
-def make_plan(bcast=0, tpl=0, splits=0, chunk=0) -> nbody_plan:
+def make_plan(bcast=0, tpl=0, splits=0, chunk=0, wg=0) -> nbody_plan:
     if isinstance(bcast, str):
         bcast = {v: k for k, v in BCAST_NAMES.items()}[bcast]
-    return nbody_plan(int(bcast), int(tpl), int(splits), int(chunk))
+    return nbody_plan(int(bcast), int(tpl), int(splits), int(chunk), int(wg))
 
 
 # ------------------------------------------------------------ torch conveniences

@@ -119,20 +119,28 @@ constexpr int kMaxSplits = 4096;
 
 int valid_tpl(int t) { return t == 1 || t == 2 || t == 4 || t == 8; }
 
-// Automatic layout. Targets per lane grow with N; split-j adds source chunks
-// until there are about `waves_per_simd` waves for every SIMD (4 per CU), with
-// chunks of at least kFlush sources.
-void auto_plan(int64_t n, bool pot, int cus, nbody_plan *p)
+// Automatic layout, chosen by measurement on MI355X (layout sweeps of the
+// five workloads):
+//   - LDS broadcast with one target per lane: every VALU operand of the inner
+//     step is then a VGPR, which issues about twice as fast as an SGPR operand;
+//   - 512-thread workgroups (512-body LDS tiles) from N = 65536 up, 256 below;
+//   - split-j chunks until there are about 128 workgroups per compute unit
+//     over the run (finer load balance; a chunk's sources stay L2-resident),
+//     keeping at least 4 tiles per chunk from N = 65536 up and 1 below.
+void auto_plan(int64_t n, int cus, nbody_plan *p)
 {
-    (void)pot;
-    if (p->bcast == NBODY_BCAST_AUTO) p->bcast = NBODY_BCAST_SCALAR;
-    if (p->tpl == 0) p->tpl = n >= (1 << 18) ? 4 : (n >= (1 << 15) ? 2 : 1);
+    const bool big = n >= 65536;
+    if (p->bcast == NBODY_BCAST_AUTO) p->bcast = NBODY_BCAST_LDS;
+    if (p->tpl == 0) p->tpl = 1;
+    if (p->wg == 0) p->wg = (big && p->bcast == NBODY_BCAST_LDS) ? 512 : 256;
     if (p->splits == 0) {
-        const int64_t waves_per_simd = 4;
-        const int64_t want = (int64_t)cus * 4 * waves_per_simd;
-        const int64_t tw = (n + 64 * p->tpl - 1) / (64 * p->tpl);  // target waves
-        int64_t s = (want + tw - 1) / tw;
-        const int64_t smax = (n + nbk::kFlush - 1) / nbk::kFlush;
+        const int64_t per = (int64_t)p->wg * p->tpl;
+        const int64_t gx = (n + per - 1) / per;  // target workgroups
+        const int64_t want = (int64_t)cus * 128;
+        int64_t s = (want + gx - 1) / gx;
+        const int64_t tile = p->bcast == NBODY_BCAST_LDS ? p->wg : nbk::kFlush;
+        const int64_t min_chunk = tile * (big ? 4 : 1);
+        const int64_t smax = (n + min_chunk - 1) / min_chunk;
         if (s > smax) s = smax;
         if (s < 1) s = 1;
         if (s > kMaxSplits) s = kMaxSplits;
@@ -140,44 +148,50 @@ void auto_plan(int64_t n, bool pot, int cus, nbody_plan *p)
     }
 }
 
-// Final chunking: chunk is a multiple of kFlush and S = ceil(N / chunk).
+// Final chunking: chunk is a whole number of tiles (LDS tile or accumulation
+// block) and S = ceil(N / chunk), so no chunk is empty.
 void finish_plan(int64_t n, nbody_plan *p)
 {
+    const int64_t tile = p->bcast == NBODY_BCAST_LDS ? p->wg : nbk::kFlush;
     int64_t s = p->splits;
     int64_t c = (n + s - 1) / s;
-    c = (c + nbk::kFlush - 1) / nbk::kFlush * nbk::kFlush;
-    if (c < nbk::kFlush) c = nbk::kFlush;
+    c = (c + tile - 1) / tile * tile;
+    if (c < tile) c = tile;
+    if (c > INT32_MAX) c = (int64_t)INT32_MAX / tile * tile;
     s = (n + c - 1) / c;
     if (s < 1) s = 1;
-    if (c > INT32_MAX) c = (int64_t)INT32_MAX / nbk::kFlush * nbk::kFlush;
     p->splits = (int32_t)s;
     p->chunk = (int32_t)c;
 }
 
-int make_plan(int64_t n, bool pot, const nbody_plan *user, int *dev_out, nbody_plan *p)
+int make_plan(int64_t n, const nbody_plan *user, int *dev_out, nbody_plan *p)
 {
-    *p = user ? *user : nbody_plan{0, 0, 0, 0};
+    *p = user ? *user : nbody_plan{0, 0, 0, 0, 0};
+    p->chunk = 0;
     if (p->bcast < 0 || p->bcast > NBODY_BCAST_READLANE)
         return fail(NBODY_EINVAL, "plan.bcast=%d is not a NBODY_BCAST_* value", p->bcast);
     if (p->tpl != 0 && !valid_tpl(p->tpl))
         return fail(NBODY_EINVAL, "plan.tpl=%d must be 0, 1, 2, 4 or 8", p->tpl);
     if (p->splits < 0 || p->splits > kMaxSplits)
         return fail(NBODY_EINVAL, "plan.splits=%d must be in [0, %d]", p->splits, kMaxSplits);
+    if (p->wg != 0 && p->wg != 256 && !(p->wg == 512 && p->bcast == NBODY_BCAST_LDS))
+        return fail(NBODY_EINVAL, "plan.wg=%d must be 0 or 256 (or 512 with the LDS broadcast)",
+                    p->wg);
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     int cus = 0;
     int rc = device_cus(dev, &cus);
     if (rc != NBODY_OK) return rc;
-    auto_plan(n, pot, cus, p);
+    auto_plan(n, cus, p);
     finish_plan(n, p);
     *dev_out = dev;
     return NBODY_OK;
 }
 
-unsigned grid_x(int64_t n, int tpl)
+unsigned grid_x(int64_t n, int tpl, int wg)
 {
-    const int64_t per = (int64_t)nbk::kWG * tpl;
+    const int64_t per = (int64_t)wg * tpl;
     return (unsigned)((n + per - 1) / per);
 }
 
@@ -204,8 +218,8 @@ int enqueue_eval(const float4 *pos, int n, float eps2, float4 *acc_out, float *p
         if (rc != NBODY_OK) return rc;
         a.part = (float4 *)ws;
     }
-    hipError_t e = nbk::launch_accel(p.bcast, p.tpl, pot, grid_x(n, p.tpl), (unsigned)p.splits, a,
-                                     stream);
+    hipError_t e = nbk::launch_accel(p.bcast, p.tpl, p.wg, pot, grid_x(n, p.tpl, p.wg),
+                                     (unsigned)p.splits, a, stream);
     if (e != hipSuccess) return hip_fail(e, "accel kernel launch");
     if (step) {
         e = nbk::launch_euler(a.part, n, p.splits, euler_pos, euler_vel, dt, stream);
@@ -236,7 +250,7 @@ int accel_impl(const nbody_f4 *pos, int64_t N, float eps2, nbody_f4 *acc, float 
         return fail(NBODY_EINVAL, "pot_out overlaps another buffer");
     nbody_plan p;
     int dev = 0;
-    rc = make_plan(N, pot != nullptr, plan, &dev, &p);
+    rc = make_plan(N, plan, &dev, &p);
     if (rc != NBODY_OK) return rc;
     rc = enqueue_eval((const float4 *)pos, (int)N, eps2, (float4 *)acc, pot, p, dev, stream,
                       nullptr, nullptr, 0.0f);
@@ -277,7 +291,7 @@ int nbody_step(nbody_f4 *pos, nbody_f4 *vel, int64_t N, float dt, float eps2, in
     if (overlap(pos, b16, vel, b16)) return fail(NBODY_EINVAL, "vel overlaps pos");
     nbody_plan p;
     int dev = 0;
-    rc = make_plan(N, false, nullptr, &dev, &p);
+    rc = make_plan(N, nullptr, &dev, &p);
     if (rc != NBODY_OK) return rc;
     for (int64_t s = 0; s < nsteps; ++s) {
         rc = enqueue_eval((const float4 *)pos, (int)N, eps2, nullptr, nullptr, p, dev, stream,
@@ -294,7 +308,8 @@ int nbody_plan_for(int64_t N, int want_pot, nbody_plan *out)
     if (rc != NBODY_OK) return rc;
     int dev = 0;
     nbody_plan p;
-    rc = make_plan(N < 1 ? 1 : N, want_pot != 0, nullptr, &dev, &p);
+    (void)want_pot;
+    rc = make_plan(N < 1 ? 1 : N, nullptr, &dev, &p);
     if (rc != NBODY_OK) return rc;
     *out = p;
     return ok();

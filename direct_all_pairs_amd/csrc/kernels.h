@@ -9,8 +9,8 @@ namespace nbk {
 // Threads per workgroup of the acceleration kernels (4 waves of 64).
 constexpr int kWG = 256;
 // Sources summed into a fresh per-target partial before it is added to the
-// running total (two-level accumulation). Also the LDS tile size and the
-// granularity of split-j chunk boundaries.
+// running total (two-level accumulation), and the granularity of split-j chunk
+// boundaries. LDS tiles hold a multiple of it.
 constexpr int kFlush = 256;
 
 struct AccelArgs {
@@ -23,8 +23,9 @@ struct AccelArgs {
     float4 *part;       // split mode (non-null): part[s*N + i] = (ax, ay, az, sum m/r)
 };
 
-// Launch the acceleration kernel: grid (ceil(N / (kWG*tpl)), S), block kWG.
-hipError_t launch_accel(int bcast, int tpl, bool pot, unsigned grid_x, unsigned splits,
+// Launch the acceleration kernel: grid (ceil(N / (wg*tpl)), S), block wg.
+// wg is 256 or 512 for the LDS broadcast and 256 for the others.
+hipError_t launch_accel(int bcast, int tpl, int wg, bool pot, unsigned grid_x, unsigned splits,
                         const AccelArgs &args, hipStream_t stream);
 
 // acc_out[i] = (sum_s part[s][i].xyz, 0); pot_out[i] = -sum_s part[s][i].w (if non-null).

@@ -13,7 +13,7 @@
 //     broadcast source, the idea behind the SoA 4x4 blocking of "スライド 1",
 //     No.13-15).
 //   * Sources reach all 64 lanes of a wave by one of three broadcasts:
-//       LDS      - the workgroup stages 256-body float4 tiles in LDS with
+//       LDS      - the workgroup stages WG-body float4 tiles in LDS with
 //                  coalesced loads (double-buffered, one barrier per tile), and
 //                  each wave reads a source with a uniform-address ds_read_b128;
 //       SCALAR   - each wave reads sources with uniform scalar loads, so the
@@ -106,14 +106,14 @@ __device__ __forceinline__ void interact4(const float4 &b, const Targets<T> &tg,
 
 // Target t of this lane is body base + t*kWG + threadIdx.x: each t is one
 // coalesced 4 KiB segment of the body array.
-template <int T>
+template <int T, int WG = kWG>
 __device__ __forceinline__ Targets<T> load_targets(const float4 *__restrict__ pos, int n,
                                                    unsigned base)
 {
     Targets<T> tg;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-        unsigned i = base + t * kWG + threadIdx.x;
+        unsigned i = base + t * WG + threadIdx.x;
         const float4 b = pos[i < (unsigned)n ? i : (unsigned)(n - 1)];
         tg.x[t] = b.x;
         tg.y[t] = b.y;
@@ -122,12 +122,12 @@ __device__ __forceinline__ Targets<T> load_targets(const float4 *__restrict__ po
     return tg;
 }
 
-template <int T, bool POT>
+template <int T, bool POT, int WG = kWG>
 __device__ __forceinline__ void store(const Sums<T, POT> &a, const AccelArgs &k, unsigned base)
 {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-        const unsigned i = base + t * kWG + threadIdx.x;
+        const unsigned i = base + t * WG + threadIdx.x;
         if (i < (unsigned)k.n) {
             if (k.part) {
                 const size_t o = (size_t)blockIdx.y * (size_t)k.n + i;
@@ -148,6 +148,16 @@ __device__ __forceinline__ float4 load_or_zero(const float4 *__restrict__ pos, i
     const bool in = j < j1;
     const float4 b = pos[in ? j : j1 - 1];
     return make_float4(in ? b.x : 0.0f, in ? b.y : 0.0f, in ? b.z : 0.0f, in ? b.w : 0.0f);
+}
+
+// A uniform value copied into a VGPR. On gfx950 a VALU instruction whose
+// operands are all VGPRs issues about twice as fast as one that reads an SGPR,
+// so loop-invariant scalars used in the inner step are kept in VGPRs.
+__device__ __forceinline__ float in_vgpr(float s)
+{
+    float v;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "s"(s));
+    return v;
 }
 
 // Keeps the compiler's scheduler from moving instructions across this point
@@ -226,59 +236,73 @@ __global__ void __launch_bounds__(kWG) accel_scalar(AccelArgs k)
 }
 
 // ---------------------------------------------------------------- LDS
-// The workgroup stages kFlush = kWG bodies per tile in LDS (each thread loads
-// one float4, coalesced). Two tile buffers: while tile t is read from one,
-// the prefetched tile t+1 is written to the other, so one barrier per tile
-// both publishes the new tile and guards the buffer about to be overwritten.
-template <int T, bool POT>
-__global__ void __launch_bounds__(kWG) accel_lds(AccelArgs k)
+// The workgroup stages WG bodies per tile in LDS (each thread loads one
+// float4, coalesced). Two tile buffers: while tile t is read from one, the
+// prefetched tile t+1 is written to the other, so one barrier per tile both
+// publishes the new tile and guards the buffer about to be overwritten. The
+// prefetch is issued at the top of the tile and only consumed (zero-padded and
+// stored) at its end, so its latency hides behind the tile's arithmetic. Each
+// wave reads sources with uniform-address ds_read_b128 (a broadcast) into
+// VGPRs, in groups of U that are double-buffered across scheduling fences.
+template <int T, bool POT, int WG>
+__global__ void __launch_bounds__(WG) accel_lds(AccelArgs k)
 {
-    static_assert(kFlush == kWG, "LDS tile is one body per thread");
-    constexpr int U = 4;  // bodies per LDS read group; groups are double-buffered in VGPRs
-    __shared__ float4 tile[2][kWG];
-    const unsigned base = blockIdx.x * (unsigned)(kWG * T);
+    static_assert(WG % kFlush == 0, "accumulation blocks must tile the LDS tile");
+    constexpr int U = T <= 2 ? 4 : 2;
+    __shared__ float4 tile[2][WG];
+    const unsigned base = blockIdx.x * (unsigned)(WG * T);
     int j0, j1;
     chunk_range(k, j0, j1);
-    const Targets<T> tg = load_targets<T>(k.pos, k.n, base);
-    const float eps2 = k.eps2;
+    const Targets<T> tg = load_targets<T, WG>(k.pos, k.n, base);
+    const float eps2 = in_vgpr(k.eps2);
 
     Sums<T, POT> tot, blk;
     zero(tot);
+    zero(blk);
 
-    const int ntiles = (j1 - j0 + kWG - 1) / kWG;
+    const int ntiles = (j1 - j0 + WG - 1) / WG;
     int jl = j0 + threadIdx.x;
-    float4 r = load_or_zero(k.pos, jl, j1);
-    tile[0][threadIdx.x] = r;
+    tile[0][threadIdx.x] = load_or_zero(k.pos, jl, j1);
     __syncthreads();
     for (int it = 0; it < ntiles; ++it) {
         const int cur = it & 1;
-        jl += kWG;
-        if (it + 1 < ntiles) r = load_or_zero(k.pos, jl, j1);
-        zero(blk);
+        const bool more = it + 1 < ntiles;
+        jl += WG;
+        // raw prefetch of the next tile (index clamped into the chunk); the
+        // zero-padding select happens at the store below
+        float4 r = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (more) r = k.pos[jl < j1 ? jl : j1 - 1];
         const float4 *tl = tile[cur];
         float4 a[U], b[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) a[u] = tl[u];
-        for (int u0 = 0; u0 < kWG; u0 += 2 * U) {
+        for (int u0 = 0; u0 < WG; u0 += 2 * U) {
 #pragma unroll
             for (int u = 0; u < U; ++u) b[u] = tl[u0 + U + u];
             sched_fence();
 #pragma unroll
             for (int u = 0; u < U; ++u) interact4<T, POT>(a[u], tg, eps2, blk);
             sched_fence();
-            const int un = (u0 + 2 * U < kWG) ? u0 + 2 * U : 0;
+            const int un = (u0 + 2 * U < WG) ? u0 + 2 * U : 0;
 #pragma unroll
             for (int u = 0; u < U; ++u) a[u] = tl[un + u];
             sched_fence();
 #pragma unroll
             for (int u = 0; u < U; ++u) interact4<T, POT>(b[u], tg, eps2, blk);
             sched_fence();
+            if (((u0 + 2 * U) % kFlush) == 0) {
+                add_into(tot, blk);
+                zero(blk);
+            }
         }
-        add_into(tot, blk);
-        if (it + 1 < ntiles) tile[cur ^ 1][threadIdx.x] = r;
+        if (more) {
+            const bool in = jl < j1;
+            tile[cur ^ 1][threadIdx.x] = make_float4(in ? r.x : 0.0f, in ? r.y : 0.0f,
+                                                     in ? r.z : 0.0f, in ? r.w : 0.0f);
+        }
         __syncthreads();
     }
-    store(tot, k, base);
+    store<T, POT, WG>(tot, k, base);
 }
 
 // ---------------------------------------------------------------- READLANE
@@ -377,38 +401,38 @@ __global__ void __launch_bounds__(256) euler_kernel(const float4 *__restrict__ p
 }
 
 template <int T, bool POT>
-const void *accel_fn(int bcast)
+const void *accel_fn(int bcast, int wg)
 {
-    switch (bcast) {
-    case 1: return (const void *)&accel_lds<T, POT>;
-    case 2: return (const void *)&accel_scalar<T, POT>;
-    case 3: return (const void *)&accel_readlane<T, POT>;
-    default: return nullptr;
-    }
+    if (bcast == 1 && wg == 256) return (const void *)&accel_lds<T, POT, 256>;
+    if (bcast == 1 && wg == 512) return (const void *)&accel_lds<T, POT, 512>;
+    if (wg != kWG) return nullptr;
+    if (bcast == 2) return (const void *)&accel_scalar<T, POT>;
+    if (bcast == 3) return (const void *)&accel_readlane<T, POT>;
+    return nullptr;
 }
 
 template <bool POT>
-const void *accel_fn_t(int bcast, int tpl)
+const void *accel_fn_t(int bcast, int tpl, int wg)
 {
     switch (tpl) {
-    case 1: return accel_fn<1, POT>(bcast);
-    case 2: return accel_fn<2, POT>(bcast);
-    case 4: return accel_fn<4, POT>(bcast);
-    case 8: return accel_fn<8, POT>(bcast);
+    case 1: return accel_fn<1, POT>(bcast, wg);
+    case 2: return accel_fn<2, POT>(bcast, wg);
+    case 4: return accel_fn<4, POT>(bcast, wg);
+    case 8: return accel_fn<8, POT>(bcast, wg);
     default: return nullptr;
     }
 }
 
 }  // namespace
 
-hipError_t launch_accel(int bcast, int tpl, bool pot, unsigned grid_x, unsigned splits,
+hipError_t launch_accel(int bcast, int tpl, int wg, bool pot, unsigned grid_x, unsigned splits,
                         const AccelArgs &args, hipStream_t stream)
 {
-    const void *fn = pot ? accel_fn_t<true>(bcast, tpl) : accel_fn_t<false>(bcast, tpl);
+    const void *fn = pot ? accel_fn_t<true>(bcast, tpl, wg) : accel_fn_t<false>(bcast, tpl, wg);
     if (!fn) return hipErrorInvalidValue;
     AccelArgs a = args;
     void *kargs[] = {&a};
-    return hipLaunchKernel(fn, dim3(grid_x, splits, 1), dim3(kWG, 1, 1), kargs, 0, stream);
+    return hipLaunchKernel(fn, dim3(grid_x, splits, 1), dim3(wg, 1, 1), kargs, 0, stream);
 }
 
 hipError_t launch_combine(const float4 *part, int n, int splits, float4 *acc_out, float *pot_out,

@@ -78,13 +78,16 @@ enum {
  *            go to scratch and a second kernel adds them in ascending chunk
  *            order (deterministic). S = 1 writes results directly.
  *   chunk  - (output only) sources per chunk; chunks are [s*chunk, min((s+1)*chunk, N)).
- * The plan is a pure function of (N, potential wanted, compute-unit count), so
- * nbody_accel and nbody_step use the same one for the same N. */
+ *   wg     - threads per workgroup: 256 or 512 for NBODY_BCAST_LDS (also the LDS
+ *            tile, in bodies), 256 for the other schemes.
+ * The plan is a pure function of (N, compute-unit count), so nbody_accel and
+ * nbody_step use the same one for the same N, with or without the potential. */
 typedef struct nbody_plan {
     int32_t bcast;
     int32_t tpl;
     int32_t splits;
     int32_t chunk;
+    int32_t wg;
 } nbody_plan;
 
 /*
@@ -123,9 +126,9 @@ int nbody_step(nbody_f4 *pos, nbody_f4 *vel, int64_t N, float dt, float eps2, in
                hipStream_t stream);
 
 /*
- * nbody_plan_for - the automatic plan for N bodies (want_pot != 0: with
- * potential) on the current device. Fills *out. Queries the device's
- * compute-unit count once per device.
+ * nbody_plan_for - the automatic plan for N bodies on the current device
+ * (want_pot is accepted for symmetry; the plan does not depend on it). Fills
+ * *out. Queries the device's compute-unit count once per device.
  */
 int nbody_plan_for(int64_t N, int want_pot, nbody_plan *out);
 
