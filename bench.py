@@ -116,10 +116,14 @@ def sweep(nb, w, pos, acc, pot, args) -> int:
     split_opts = [0, 1, 2, 4, 8, 16, 32, 64]
     layouts = [("lds", t, wg) for t in (1, 2, 4) for wg in (256, 512)]
     layouts += [(b, t, 256) for b in ("scalar", "readlane") for t in (1, 2, 4, 8)]
+    layouts += [("pairs", 4, band) for band in (512, 1024, 2048)]
     results = []
     for bcast, tpl, wg in layouts:
         for splits in (split_opts if bcast == "lds" else [0]):
-            plan = nb.make_plan(bcast=bcast, tpl=tpl, splits=splits, wg=wg)
+            if bcast == "pairs":
+                plan = nb.make_plan(mode="pairs", band=wg)
+            else:
+                plan = nb.make_plan(mode="tiles", bcast=bcast, tpl=tpl, splits=splits, wg=wg)
             if splits and splits * 256 > n:
                 continue
             for _ in range(max(1, args.warmup)):

@@ -23,6 +23,8 @@ LIB_PATH = _PKG / "libnbody_amd.so"
 NBODY_OK, NBODY_EINVAL, NBODY_EALIGN, NBODY_EHIP, NBODY_ENOMEM = 0, 1, 2, 3, 4
 BCAST_AUTO, BCAST_LDS, BCAST_SCALAR, BCAST_READLANE = 0, 1, 2, 3
 BCAST_NAMES = {BCAST_LDS: "lds", BCAST_SCALAR: "scalar", BCAST_READLANE: "readlane"}
+MODE_AUTO, MODE_TILES, MODE_PAIRS = 0, 1, 2
+MODE_NAMES = {MODE_TILES: "tiles", MODE_PAIRS: "pairs"}
 
 
 class NbodyError(RuntimeError):
@@ -33,11 +35,13 @@ class NbodyError(RuntimeError):
 
 class nbody_plan(ctypes.Structure):
     _fields_ = [("bcast", ctypes.c_int32), ("tpl", ctypes.c_int32),
-                ("splits", ctypes.c_int32), ("chunk", ctypes.c_int32), ("wg", ctypes.c_int32)]
+                ("splits", ctypes.c_int32), ("chunk", ctypes.c_int32), ("wg", ctypes.c_int32),
+                ("mode", ctypes.c_int32), ("band", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
-        return {"bcast": BCAST_NAMES.get(self.bcast, self.bcast), "tpl": self.tpl,
-                "splits": self.splits, "chunk": self.chunk, "wg": self.wg}
+        return {"mode": MODE_NAMES.get(self.mode, self.mode),
+                "bcast": BCAST_NAMES.get(self.bcast, self.bcast), "tpl": self.tpl,
+                "splits": self.splits, "chunk": self.chunk, "wg": self.wg, "band": self.band}
 
 
 # torch (device memory and streams) is imported first: its bundled HIP runtime
@@ -134,10 +138,12 @@ def nbody_plan_for(N: int, want_pot: bool = False) -> nbody_plan:
     return p
 
 
-def make_plan(bcast=0, tpl=0, splits=0, chunk=0, wg=0) -> nbody_plan:
+def make_plan(bcast=0, tpl=0, splits=0, chunk=0, wg=0, mode=0, band=0) -> nbody_plan:
     if isinstance(bcast, str):
         bcast = {v: k for k, v in BCAST_NAMES.items()}[bcast]
-    return nbody_plan(int(bcast), int(tpl), int(splits), int(chunk), int(wg))
+    if isinstance(mode, str):
+        mode = {v: k for k, v in MODE_NAMES.items()}[mode]
+    return nbody_plan(int(bcast), int(tpl), int(splits), int(chunk), int(wg), int(mode), int(band))
 
 
 # ------------------------------------------------------------ torch conveniences

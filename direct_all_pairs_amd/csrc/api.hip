@@ -57,22 +57,31 @@ bool eps2_ok(float e) { return std::isfinite(e) && e >= FLT_MIN; }
 // ------------------------------------------------------------ device facts
 
 std::mutex g_mu;
-std::map<int, int> g_cus;  // device -> compute units
+struct DeviceFacts {
+    int cus = 1;            // compute units
+    size_t mem_bytes = 0;   // device memory
+};
+std::map<int, DeviceFacts> g_dev;
 
-int device_cus(int dev, int *cus)
+int device_facts(int dev, DeviceFacts *out)
 {
     std::lock_guard<std::mutex> lk(g_mu);
-    auto it = g_cus.find(dev);
-    if (it != g_cus.end()) {
-        *cus = it->second;
+    auto it = g_dev.find(dev);
+    if (it != g_dev.end()) {
+        *out = it->second;
         return NBODY_OK;
     }
+    DeviceFacts f;
     int v = 0;
     hipError_t e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(multiprocessor count)");
-    if (v <= 0) v = 1;
-    g_cus[dev] = v;
-    *cus = v;
+    f.cus = v > 0 ? v : 1;
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    f.mem_bytes = prop.totalGlobalMem;
+    g_dev[dev] = f;
+    *out = f;
     return NBODY_OK;
 }
 
@@ -119,24 +128,63 @@ constexpr int kMaxSplits = 4096;
 
 int valid_tpl(int t) { return t == 1 || t == 2 || t == 4 || t == 8; }
 
+// Pair-symmetric bands: partial-sum scratch is (N / band) x N x 16 bytes. The
+// automatic plan uses the mode only while that stays within 1/16 of device
+// memory (about 18 GB on MI355X, enough for N = 2^20 with 2048-body bands).
+constexpr size_t kPairsScratchShare = 16;
+
+int valid_band(int b) { return b == 512 || b == 1024 || b == 2048; }
+
+size_t pairs_scratch(int64_t n, int band)
+{
+    const int64_t nb = (n + band - 1) / band;
+    return (size_t)nb * (size_t)n * sizeof(float4);
+}
+
 // Automatic layout, chosen by measurement on MI355X (layout sweeps of the
 // five workloads):
-//   - LDS broadcast with one target per lane: every VALU operand of the inner
-//     step is then a VGPR, which issues about twice as fast as an SGPR operand;
-//   - 512-thread workgroups (512-body LDS tiles) from N = 65536 up, 256 below;
-//   - split-j chunks until there are about 128 workgroups per compute unit
-//     over the run (finer load balance; a chunk's sources stay L2-resident),
-//     keeping at least 4 tiles per chunk from N = 65536 up and 1 below.
-void auto_plan(int64_t n, int cus, nbody_plan *p)
+//   - from N = 65536 up, pair-symmetric bands when their scratch fits: the
+//     largest band that still yields at least 32 work items per compute unit;
+//   - otherwise one-sided tiles with the LDS broadcast and one target per lane:
+//     every VALU operand of the inner step is then a VGPR, which issues about
+//     twice as fast as an SGPR operand; 512-thread workgroups (512-body LDS
+//     tiles) from N = 65536 up, 256 below; split-j chunks until there are about
+//     128 workgroups per compute unit over the run (finer load balance; a
+//     chunk's sources stay L2-resident), at least 4 tiles per chunk from
+//     N = 65536 up and 1 below.
+void auto_plan(int64_t n, const DeviceFacts &dev, nbody_plan *p)
 {
     const bool big = n >= 65536;
+    if (p->mode == NBODY_MODE_AUTO) {
+        p->mode = NBODY_MODE_TILES;
+        if (big && p->bcast == NBODY_BCAST_AUTO && p->tpl == 0 && p->splits == 0 && p->wg == 0) {
+            for (int band : {2048, 1024, 512}) {
+                if (p->band != 0 && p->band != band) continue;
+                const int64_t nb = (n + band - 1) / band;
+                const int64_t items = nb * (nb / 2 + 1);
+                if (pairs_scratch(n, band) <= dev.mem_bytes / kPairsScratchShare &&
+                    (items >= (int64_t)dev.cus * 32 || band == 512)) {
+                    p->mode = NBODY_MODE_PAIRS;
+                    p->band = band;
+                    break;
+                }
+            }
+        }
+    }
+    if (p->mode == NBODY_MODE_PAIRS) {
+        p->bcast = NBODY_BCAST_LDS;
+        p->tpl = 4;
+        p->wg = 256;
+        if (p->band == 0) p->band = n >= (1 << 19) ? 2048 : (n >= (1 << 17) ? 1024 : 512);
+        return;
+    }
     if (p->bcast == NBODY_BCAST_AUTO) p->bcast = NBODY_BCAST_LDS;
     if (p->tpl == 0) p->tpl = 1;
     if (p->wg == 0) p->wg = (big && p->bcast == NBODY_BCAST_LDS) ? 512 : 256;
     if (p->splits == 0) {
         const int64_t per = (int64_t)p->wg * p->tpl;
         const int64_t gx = (n + per - 1) / per;  // target workgroups
-        const int64_t want = (int64_t)cus * 128;
+        const int64_t want = (int64_t)dev.cus * 128;
         int64_t s = (want + gx - 1) / gx;
         const int64_t tile = p->bcast == NBODY_BCAST_LDS ? p->wg : nbk::kFlush;
         const int64_t min_chunk = tile * (big ? 4 : 1);
@@ -148,10 +196,17 @@ void auto_plan(int64_t n, int cus, nbody_plan *p)
     }
 }
 
-// Final chunking: chunk is a whole number of tiles (LDS tile or accumulation
-// block) and S = ceil(N / chunk), so no chunk is empty.
+// Final chunking. Tiles: chunk is a whole number of tiles (LDS tile or
+// accumulation block) and S = ceil(N / chunk), so no chunk is empty. Pairs:
+// splits = number of bands = number of partial slots, chunk = band.
 void finish_plan(int64_t n, nbody_plan *p)
 {
+    if (p->mode == NBODY_MODE_PAIRS) {
+        p->splits = (int32_t)((n + p->band - 1) / p->band);
+        p->chunk = p->band;
+        return;
+    }
+    p->band = 0;
     const int64_t tile = p->bcast == NBODY_BCAST_LDS ? p->wg : nbk::kFlush;
     int64_t s = p->splits;
     int64_t c = (n + s - 1) / s;
@@ -166,8 +221,10 @@ void finish_plan(int64_t n, nbody_plan *p)
 
 int make_plan(int64_t n, const nbody_plan *user, int *dev_out, nbody_plan *p)
 {
-    *p = user ? *user : nbody_plan{0, 0, 0, 0, 0};
+    *p = user ? *user : nbody_plan{0, 0, 0, 0, 0, 0, 0};
     p->chunk = 0;
+    if (p->mode < 0 || p->mode > NBODY_MODE_PAIRS)
+        return fail(NBODY_EINVAL, "plan.mode=%d is not a NBODY_MODE_* value", p->mode);
     if (p->bcast < 0 || p->bcast > NBODY_BCAST_READLANE)
         return fail(NBODY_EINVAL, "plan.bcast=%d is not a NBODY_BCAST_* value", p->bcast);
     if (p->tpl != 0 && !valid_tpl(p->tpl))
@@ -177,13 +234,20 @@ int make_plan(int64_t n, const nbody_plan *user, int *dev_out, nbody_plan *p)
     if (p->wg != 0 && p->wg != 256 && !(p->wg == 512 && p->bcast == NBODY_BCAST_LDS))
         return fail(NBODY_EINVAL, "plan.wg=%d must be 0 or 256 (or 512 with the LDS broadcast)",
                     p->wg);
+    if (p->band != 0 && !valid_band(p->band))
+        return fail(NBODY_EINVAL, "plan.band=%d must be 0, 512, 1024 or 2048", p->band);
+    if (p->mode == NBODY_MODE_PAIRS &&
+        ((p->bcast != 0 && p->bcast != NBODY_BCAST_LDS) || (p->tpl != 0 && p->tpl != 4) ||
+         p->splits != 0 || (p->wg != 0 && p->wg != 256)))
+        return fail(NBODY_EINVAL, "plan.mode=NBODY_MODE_PAIRS takes only plan.band "
+                                  "(bcast LDS, tpl 4, wg 256 and splits are implied)");
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    int cus = 0;
-    int rc = device_cus(dev, &cus);
+    DeviceFacts facts;
+    int rc = device_facts(dev, &facts);
     if (rc != NBODY_OK) return rc;
-    auto_plan(n, cus, p);
+    auto_plan(n, facts, p);
     finish_plan(n, p);
     *dev_out = dev;
     return NBODY_OK;
@@ -210,16 +274,23 @@ int enqueue_eval(const float4 *pos, int n, float eps2, float4 *acc_out, float *p
 {
     const bool pot = pot_out != nullptr;
     const bool step = euler_pos != nullptr;
+    const bool pairs = p.mode == NBODY_MODE_PAIRS;
     nbk::AccelArgs a{pos, n, eps2, p.chunk, acc_out, pot_out, nullptr};
-    if (p.splits > 1 || step) {
+    if (p.splits > 1 || step || pairs) {
         void *ws = nullptr;
         const size_t bytes = (size_t)p.splits * (size_t)n * sizeof(float4);
         int rc = scratch_get(dev, stream, bytes, &ws);
         if (rc != NBODY_OK) return rc;
         a.part = (float4 *)ws;
     }
-    hipError_t e = nbk::launch_accel(p.bcast, p.tpl, p.wg, pot, grid_x(n, p.tpl, p.wg),
-                                     (unsigned)p.splits, a, stream);
+    hipError_t e;
+    if (pairs) {
+        nbk::PairsArgs pa{pos, n, eps2, p.splits, a.part};
+        e = nbk::launch_pairs(p.band, pot, pa, stream);
+    } else {
+        e = nbk::launch_accel(p.bcast, p.tpl, p.wg, pot, grid_x(n, p.tpl, p.wg),
+                              (unsigned)p.splits, a, stream);
+    }
     if (e != hipSuccess) return hip_fail(e, "accel kernel launch");
     if (step) {
         e = nbk::launch_euler(a.part, n, p.splits, euler_pos, euler_vel, dt, stream);

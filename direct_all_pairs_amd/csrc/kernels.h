@@ -23,6 +23,19 @@ struct AccelArgs {
     float4 *part;       // split mode (non-null): part[s*N + i] = (ax, ay, az, sum m/r)
 };
 
+struct PairsArgs {
+    const float4 *pos;  // N bodies (x, y, z, m)
+    int n;              // N
+    float eps2;         // softening squared (positive normal float)
+    int nbands;         // nb = ceil(N / band)
+    float4 *part;       // part[slot*N + i], slot in [0, nb): every entry written once
+};
+
+// Pair-symmetric evaluation over bands of `band` bodies (512, 1024 or 2048;
+// 4 targets per lane). Writes nb partial slots per body; launch_combine or
+// launch_euler with splits = nb finishes the evaluation.
+hipError_t launch_pairs(int band, bool pot, const PairsArgs &args, hipStream_t stream);
+
 // Launch the acceleration kernel: grid (ceil(N / (wg*tpl)), S), block wg.
 // wg is 256 or 512 for the LDS broadcast and 256 for the others.
 hipError_t launch_accel(int bcast, int tpl, int wg, bool pot, unsigned grid_x, unsigned splits,

@@ -351,6 +351,192 @@ __global__ void __launch_bounds__(kWG) accel_readlane(AccelArgs k)
     store(tot, k, base);
 }
 
+// ---------------------------------------------------------------- PAIRS
+// Pair-symmetric evaluation. r_ji = -r_ij and |r_ji| = |r_ij|, so one pair's
+// q = |r|^2 + eps2 and inv = q^(-1/2) serve both bodies:
+//   a_i += m_j inv^3 r_ij,   a_j -= m_i inv^3 r_ij,   p_i -= m_j inv,   p_j -= m_i inv
+// (19 VALU instructions and one v_rsq_f32 per pair instead of 2 x 13 and two).
+//
+// Work split: bodies are cut into nb bands of BD. Work item (A, d), d in
+// [1, nb/2], is the unordered band pair {A, B = (A + d) mod nb}; for even nb
+// the opposite band d = nb/2 belongs only to the lower-numbered A. Item
+// (A, 0) is the diagonal band, evaluated one-sided (every i of A against every
+// j of A, self pairs included). Item (A, d) writes its A-side sums to partial
+// slot d and its B-side sums to slot nb - d; the diagonal writes slot 0. Each
+// body therefore receives exactly one partial in every slot 0..nb-1, written
+// once, and the combine adds the slots in ascending order (deterministic).
+//
+// Inside an item the 4 waves share one i-set of 64*T bodies of band A (T per
+// lane) and take the 64-body j-blocks of band B round-robin. A j-block pass is
+// 64 steps: at step k lane l pairs its T targets with j-body (l - k) mod 64,
+// read from the wave's own LDS copy of the block with a rotated index; the
+// j-side sums travel with their body by rotating one lane per step (DPP
+// wave_ror:1), so after 64 steps lane l holds the j-side sums of j-body l.
+// A j-block's sums are added into the item's LDS accumulator of band B only by
+// the wave that owns the block, in i-set order. After each i-set the waves'
+// A-side sums are added in wave order through LDS.
+constexpr int kDppWaveRor1 = 0x13C;  // DPP control: rotate the 64 lanes right by one
+
+__device__ __forceinline__ float wave_ror1(float v)
+{
+    // every lane has a source lane under a rotation, so bound_ctrl needs no old value
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                         0, __builtin_bit_cast(int, v), kDppWaveRor1, 0xF, 0xF,
+                                         true));
+}
+
+// Body b (64-bit index) or a zero-mass body at the origin for b >= n.
+__device__ __forceinline__ float4 body_or_zero(const float4 *__restrict__ pos, int n, long long b)
+{
+    const bool in = b < n;
+    const float4 v = pos[in ? b : n - 1];
+    return make_float4(in ? v.x : 0.0f, in ? v.y : 0.0f, in ? v.z : 0.0f, in ? v.w : 0.0f);
+}
+
+template <int T, int BD>
+struct PairsShared {
+    float4 jacc[BD];         // B-side sums of the item, one per body of band B
+    float4 ired[4][64 * T];  // per-wave A-side sums of the current i-set
+    float4 jblk[4][64];      // each wave's copy of its current j-block
+};
+
+template <int T, int BD, bool POT, bool SYM>
+__device__ __forceinline__ void pairs_item(const PairsArgs &k, int A, int B, int slot_i,
+                                           int slot_j, float eps2, PairsShared<T, BD> &sh)
+{
+    constexpr int W = 4;
+    constexpr int NIS = BD / (64 * T);  // i-sets per band
+    constexpr int NJB = BD / 64;        // j-blocks per band
+    static_assert(NIS >= 1 && NJB % W == 0, "band must hold whole i-sets and j-blocks");
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    for (int is = 0; is < NIS; ++is) {
+        float tx[T], ty[T], tz[T], tm[T];
+        float ax[T], ay[T], az[T], ap[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const float4 b = body_or_zero(k.pos, k.n, (long long)A * BD + is * 64 * T + t * 64 + lane);
+            tx[t] = b.x;
+            ty[t] = b.y;
+            tz[t] = b.z;
+            tm[t] = b.w;
+            ax[t] = ay[t] = az[t] = ap[t] = 0.0f;
+        }
+        for (int jb = w; jb < NJB; jb += W) {
+            const float4 jbody = body_or_zero(k.pos, k.n, (long long)B * BD + jb * 64 + lane);
+            // The block copy is written and read only by this wave, whose LDS
+            // accesses execute in program order; the wave barriers keep the
+            // compiler from moving other lanes' reads across the write.
+            __builtin_amdgcn_wave_barrier();
+            sh.jblk[w][lane] = jbody;
+            __builtin_amdgcn_wave_barrier();
+            float jx = jbody.x, jy = jbody.y, jz = jbody.z, jm = jbody.w;
+            float gx = 0.0f, gy = 0.0f, gz = 0.0f, gp = 0.0f;
+            float bx[T], by[T], bz[T], bp[T];
+#pragma unroll
+            for (int t = 0; t < T; ++t) bx[t] = by[t] = bz[t] = bp[t] = 0.0f;
+#pragma unroll 1
+            for (int step = 0; step < 64; ++step) {
+                // partner of the next step, read ahead of this step's arithmetic
+                const float4 nb4 = sh.jblk[w][(lane - step - 1) & 63];
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    const float dx = jx - tx[t], dy = jy - ty[t], dz = jz - tz[t];
+                    float q = __builtin_fmaf(dx, dx, eps2);
+                    q = __builtin_fmaf(dy, dy, q);
+                    q = __builtin_fmaf(dz, dz, q);
+                    const float inv = __builtin_amdgcn_rsqf(q);
+                    const float inv2 = inv * inv;
+                    const float tj = jm * inv;  // m_j / r
+                    const float sj = tj * inv2; // m_j / r^3
+                    bx[t] = __builtin_fmaf(sj, dx, bx[t]);
+                    by[t] = __builtin_fmaf(sj, dy, by[t]);
+                    bz[t] = __builtin_fmaf(sj, dz, bz[t]);
+                    if constexpr (POT) bp[t] = __builtin_fmaf(jm, inv, bp[t]);
+                    if constexpr (SYM) {
+                        const float ti = tm[t] * inv;  // m_i / r
+                        const float si = ti * inv2;    // m_i / r^3
+                        gx = __builtin_fmaf(-si, dx, gx);
+                        gy = __builtin_fmaf(-si, dy, gy);
+                        gz = __builtin_fmaf(-si, dz, gz);
+                        if constexpr (POT) gp = __builtin_fmaf(tm[t], inv, gp);
+                    }
+                }
+                jx = nb4.x;
+                jy = nb4.y;
+                jz = nb4.z;
+                jm = nb4.w;
+                if constexpr (SYM) {
+                    gx = wave_ror1(gx);
+                    gy = wave_ror1(gy);
+                    gz = wave_ror1(gz);
+                    if constexpr (POT) gp = wave_ror1(gp);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                ax[t] += bx[t];
+                ay[t] += by[t];
+                az[t] += bz[t];
+                ap[t] += bp[t];
+            }
+            if constexpr (SYM) {
+                float4 o = sh.jacc[jb * 64 + lane];
+                o.x += gx;
+                o.y += gy;
+                o.z += gz;
+                o.w += gp;
+                sh.jacc[jb * 64 + lane] = o;
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < T; ++t) sh.ired[w][t * 64 + lane] = make_float4(ax[t], ay[t], az[t], ap[t]);
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < 64 * T; idx += 64 * W) {
+            float4 s = sh.ired[0][idx];
+#pragma unroll
+            for (int ww = 1; ww < W; ++ww) {
+                const float4 v = sh.ired[ww][idx];
+                s.x += v.x;
+                s.y += v.y;
+                s.z += v.z;
+                s.w += v.w;
+            }
+            const long long body = (long long)A * BD + is * 64 * T + idx;
+            if (body < k.n) k.part[(size_t)slot_i * (size_t)k.n + body] = s;
+        }
+        __syncthreads();
+    }
+    if constexpr (SYM) {
+        for (int i = threadIdx.x; i < BD; i += 64 * W) {
+            const long long body = (long long)B * BD + i;
+            if (body < k.n) k.part[(size_t)slot_j * (size_t)k.n + body] = sh.jacc[i];
+        }
+    }
+}
+
+// grid (nb, nb/2 + 1), 256 threads. Workgroups whose (A, d) is not an owned
+// item return at once (uniformly, before any barrier).
+template <int T, int BD, bool POT>
+__global__ void __launch_bounds__(256) accel_pairs(PairsArgs k)
+{
+    __shared__ PairsShared<T, BD> sh;
+    const int nb = k.nbands;
+    const int A = blockIdx.x;
+    const int d = blockIdx.y;
+    if (d > nb / 2) return;
+    if (nb % 2 == 0 && d == nb / 2 && A >= nb / 2) return;
+    if (d > 0 && nb == 1) return;
+    const int B = (A + d) % nb;
+    const float eps2 = in_vgpr(k.eps2);
+    if (d == 0) {
+        pairs_item<T, BD, POT, false>(k, A, A, 0, 0, eps2, sh);
+    } else {
+        for (int i = threadIdx.x; i < BD; i += 256) sh.jacc[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        __syncthreads();
+        pairs_item<T, BD, POT, true>(k, A, B, d, nb - d, eps2, sh);
+    }
+}
+
 // ---------------------------------------------------------------- combine / Euler
 // Partial sums are added in ascending chunk order s = 0, 1, ..., S-1.
 __device__ __forceinline__ float4 sum_parts(const float4 *__restrict__ part, int n, int splits,
@@ -433,6 +619,19 @@ hipError_t launch_accel(int bcast, int tpl, int wg, bool pot, unsigned grid_x, u
     AccelArgs a = args;
     void *kargs[] = {&a};
     return hipLaunchKernel(fn, dim3(grid_x, splits, 1), dim3(wg, 1, 1), kargs, 0, stream);
+}
+
+hipError_t launch_pairs(int band, bool pot, const PairsArgs &args, hipStream_t stream)
+{
+    const void *fn = nullptr;
+    if (band == 512) fn = pot ? (const void *)&accel_pairs<4, 512, true> : (const void *)&accel_pairs<4, 512, false>;
+    if (band == 1024) fn = pot ? (const void *)&accel_pairs<4, 1024, true> : (const void *)&accel_pairs<4, 1024, false>;
+    if (band == 2048) fn = pot ? (const void *)&accel_pairs<4, 2048, true> : (const void *)&accel_pairs<4, 2048, false>;
+    if (!fn || args.nbands < 1) return hipErrorInvalidValue;
+    PairsArgs a = args;
+    void *kargs[] = {&a};
+    return hipLaunchKernel(fn, dim3((unsigned)a.nbands, (unsigned)(a.nbands / 2 + 1), 1),
+                           dim3(256, 1, 1), kargs, 0, stream);
 }
 
 hipError_t launch_combine(const float4 *part, int n, int splits, float4 *acc_out, float *pot_out,

@@ -70,6 +70,14 @@ enum {
     NBODY_BCAST_READLANE = 3  /* each lane loads one source; v_readlane broadcasts it to the wave */
 };
 
+/* Evaluation modes (nbody_plan.mode). */
+enum {
+    NBODY_MODE_AUTO = 0,
+    NBODY_MODE_TILES = 1, /* one-sided: every target sums over every source (N^2 pair terms) */
+    NBODY_MODE_PAIRS = 2  /* pair-symmetric: each unordered pair evaluated once, applied to
+                             both bodies (r_ji = -r_ij), over bands of `band` bodies */
+};
+
 /* How an evaluation is laid out on the GPU. Zero in a field means "choose
  * automatically". nbody_plan_for() returns the automatic choice.
  *   bcast  - source-broadcast scheme (NBODY_BCAST_*).
@@ -80,14 +88,25 @@ enum {
  *   chunk  - (output only) sources per chunk; chunks are [s*chunk, min((s+1)*chunk, N)).
  *   wg     - threads per workgroup: 256 or 512 for NBODY_BCAST_LDS (also the LDS
  *            tile, in bodies), 256 for the other schemes.
- * The plan is a pure function of (N, compute-unit count), so nbody_accel and
- * nbody_step use the same one for the same N, with or without the potential. */
+ *   mode   - NBODY_MODE_*. The fields above describe NBODY_MODE_TILES. With
+ *            NBODY_MODE_PAIRS only `band` may be set (512, 1024 or 2048 bodies);
+ *            the output then has splits = number of bands = partial-sum slots
+ *            per body, chunk = band, bcast = LDS, tpl = 4, wg = 256. Its scratch
+ *            is splits x N x 16 bytes (8.6 GB at N = 2^20 with 2048-body bands);
+ *            the automatic plan uses it only when that fits in 1/16 of device
+ *            memory.
+ *   band   - see mode.
+ * The plan is a pure function of (N, device compute units and memory), so
+ * nbody_accel and nbody_step use the same one for the same N, with or without
+ * the potential. */
 typedef struct nbody_plan {
     int32_t bcast;
     int32_t tpl;
     int32_t splits;
     int32_t chunk;
     int32_t wg;
+    int32_t mode;
+    int32_t band;
 } nbody_plan;
 
 /*

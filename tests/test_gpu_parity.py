@@ -87,6 +87,76 @@ def test_single_body(nb):
     assert abs(pot[0] - (-3.0 / 0.5)) <= 4 * 2.0 ** -23 * 6.0
 
 
+# ------------------------------------------------------------------ pair-symmetric bands
+
+BANDS = [512, 1024, 2048]
+
+
+@pytest.mark.parametrize("band", BANDS)
+@pytest.mark.parametrize("n", [1, 2, 3, 65, 257, 1000, 2049, 4097])
+def test_pairs_small_n(nb, n, band):
+    eps2 = np.float32(1e-4)
+    pos, _ = _bodies(n, 100 + n)
+    plan = dict(mode="pairs", band=band)
+    acc, pot = gpu_accel(pos, eps2, pot=True, plan=plan)
+    assert_accel_parity(acc, pot, _ref(n, 100 + n, eps2), what=f"N={n} {plan}")
+
+
+@pytest.mark.parametrize("band", BANDS)
+def test_pairs_mid_n(nb, band):
+    """N = 20011 (prime): odd and even band counts, a ragged last band."""
+    import oracle
+
+    n, eps2 = 20011, np.float32(1e-4)
+    pos, _ = _bodies(n, 7)
+    acc, pot = gpu_accel(pos, eps2, pot=True, plan=dict(mode="pairs", band=band))
+    idx = np.unique(np.concatenate([np.arange(300), np.arange(n - 300, n),
+                                    np.random.default_rng(1).integers(0, n, 1000)]))
+    ref = oracle.accel(pos, eps2, targets=idx)
+    assert_accel_parity(acc, pot, ref, idx=idx, what=f"N={n} pairs band={band}")
+
+
+@pytest.mark.parametrize("n,band", [(4096, 512), (5000, 1024), (6144, 2048), (8192, 1024)])
+def test_pairs_even_and_odd_band_counts(nb, n, band):
+    """Band counts 8, 5, 3 and 8: the opposite band of an even count is owned once."""
+    pos, _ = _bodies(n, 31)
+    acc, pot = gpu_accel(pos, 1e-4, pot=True, plan=dict(mode="pairs", band=band))
+    assert_accel_parity(acc, pot, _ref(n, 31, np.float32(1e-4)), what=f"N={n} band={band}")
+
+
+def test_pairs_invariants(nb):
+    """Determinism, exact mass doubling, potential-independent acceleration, dyadic
+    translation, zero-mass padding (same band count): all bit-exact."""
+    plan = dict(mode="pairs", band=1024)
+    pos, _ = _bodies(6000, 41)
+    a1, p1 = gpu_accel(pos, 1e-4, plan=plan)
+    a2, p2 = gpu_accel(pos, 1e-4, plan=plan)
+    assert np.array_equal(a1, a2) and np.array_equal(p1, p2)
+    a0, _ = gpu_accel(pos, 1e-4, pot=False, plan=plan)
+    assert np.array_equal(a0, a1)
+    pos2 = pos.copy()
+    pos2[:, 3] *= 2
+    a3, p3 = gpu_accel(pos2, 1e-4, plan=plan)
+    assert np.array_equal(a3, 2 * a1) and np.array_equal(p3, 2 * p1)
+    padded = np.concatenate([pos, np.zeros((144, 4), np.float32)])  # 6144: still 6 bands
+    a4, p4 = gpu_accel(padded, 1e-4, plan=plan)
+    assert np.array_equal(a4[:6000], a1) and np.array_equal(p4[:6000], p1)
+    dy, _ = workloads.dyadic_grid_bodies(3000, seed=13)
+    sh = dy.copy()
+    sh[:, :3] += np.array([0.25, -0.125, 0.0625], dtype=np.float32)
+    b1, q1 = gpu_accel(dy, 2.0 ** -10, plan=plan)
+    b2, q2 = gpu_accel(sh, 2.0 ** -10, plan=plan)
+    assert np.array_equal(b1, b2) and np.array_equal(q1, q2)
+
+
+def test_auto_plan_modes(nb):
+    """Pair-symmetric bands from N = 65536 up (scratch permitting), tiles below."""
+    assert nb.nbody_plan_for(4096).mode == nb.MODE_TILES
+    assert nb.nbody_plan_for(65536).mode == nb.MODE_PAIRS
+    p = nb.nbody_plan_for(1 << 20)
+    assert p.mode == nb.MODE_PAIRS and p.band == 2048 and p.splits == 512
+
+
 # ------------------------------------------------------------------ the five workloads
 
 def test_disk4096_accel_and_step(nb):
