@@ -116,12 +116,16 @@ def sweep(nb, w, pos, acc, pot, args) -> int:
     split_opts = [0, 1, 2, 4, 8, 16, 32, 64]
     layouts = [("lds", t, wg) for t in (1, 2, 4) for wg in (256, 512)]
     layouts += [(b, t, 256) for b in ("scalar", "readlane") for t in (1, 2, 4, 8)]
-    layouts += [("pairs", 4, band) for band in (512, 1024, 2048)]
+    layouts += [("pairs", t, band) for t in (4, 8) for band in (512, 1024, 2048)]
+    if args.sweep_only == "pairs":
+        layouts = [lay for lay in layouts if lay[0] == "pairs"]
+    elif args.sweep_only == "tiles":
+        layouts = [lay for lay in layouts if lay[0] != "pairs"]
     results = []
     for bcast, tpl, wg in layouts:
         for splits in (split_opts if bcast == "lds" else [0]):
             if bcast == "pairs":
-                plan = nb.make_plan(mode="pairs", band=wg)
+                plan = nb.make_plan(mode="pairs", band=wg, tpl=tpl)
             else:
                 plan = nb.make_plan(mode="tiles", bcast=bcast, tpl=tpl, splits=splits, wg=wg)
             if splits and splits * 256 > n:
@@ -164,6 +168,8 @@ def main(argv=None) -> int:
     ap.add_argument("--sweep", action="store_true",
                     help="time every (broadcast, targets-per-lane, splits) layout of the workload's "
                          "evaluation and print one JSON line per layout (no contract line)")
+    ap.add_argument("--sweep-only", default="all", choices=["all", "tiles", "pairs"],
+                    help="restrict --sweep to one evaluation mode")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (twice) and exit; "
                          "used to scale the HBM byte counters of rocprofv3")

@@ -144,7 +144,8 @@ size_t pairs_scratch(int64_t n, int band)
 // Automatic layout, chosen by measurement on MI355X (layout sweeps of the
 // five workloads):
 //   - from N = 65536 up, pair-symmetric bands when their scratch fits: the
-//     largest band that still yields at least 32 work items per compute unit;
+//     largest band that still yields at least 64 work items per compute unit,
+//     8 targets per lane;
 //   - otherwise one-sided tiles with the LDS broadcast and one target per lane:
 //     every VALU operand of the inner step is then a VGPR, which issues about
 //     twice as fast as an SGPR operand; 512-thread workgroups (512-body LDS
@@ -163,7 +164,7 @@ void auto_plan(int64_t n, const DeviceFacts &dev, nbody_plan *p)
                 const int64_t nb = (n + band - 1) / band;
                 const int64_t items = nb * (nb / 2 + 1);
                 if (pairs_scratch(n, band) <= dev.mem_bytes / kPairsScratchShare &&
-                    (items >= (int64_t)dev.cus * 32 || band == 512)) {
+                    (items >= (int64_t)dev.cus * 64 || band == 512)) {
                     p->mode = NBODY_MODE_PAIRS;
                     p->band = band;
                     break;
@@ -173,7 +174,7 @@ void auto_plan(int64_t n, const DeviceFacts &dev, nbody_plan *p)
     }
     if (p->mode == NBODY_MODE_PAIRS) {
         p->bcast = NBODY_BCAST_LDS;
-        p->tpl = 4;
+        if (p->tpl == 0) p->tpl = 8;
         p->wg = 256;
         if (p->band == 0) p->band = n >= (1 << 19) ? 2048 : (n >= (1 << 17) ? 1024 : 512);
         return;
@@ -237,10 +238,11 @@ int make_plan(int64_t n, const nbody_plan *user, int *dev_out, nbody_plan *p)
     if (p->band != 0 && !valid_band(p->band))
         return fail(NBODY_EINVAL, "plan.band=%d must be 0, 512, 1024 or 2048", p->band);
     if (p->mode == NBODY_MODE_PAIRS &&
-        ((p->bcast != 0 && p->bcast != NBODY_BCAST_LDS) || (p->tpl != 0 && p->tpl != 4) ||
-         p->splits != 0 || (p->wg != 0 && p->wg != 256)))
-        return fail(NBODY_EINVAL, "plan.mode=NBODY_MODE_PAIRS takes only plan.band "
-                                  "(bcast LDS, tpl 4, wg 256 and splits are implied)");
+        ((p->bcast != 0 && p->bcast != NBODY_BCAST_LDS) ||
+         (p->tpl != 0 && p->tpl != 4 && p->tpl != 8) || p->splits != 0 ||
+         (p->wg != 0 && p->wg != 256)))
+        return fail(NBODY_EINVAL, "plan.mode=NBODY_MODE_PAIRS takes only plan.band and plan.tpl "
+                                  "4 or 8 (bcast LDS, wg 256 and splits are implied)");
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -286,7 +288,7 @@ int enqueue_eval(const float4 *pos, int n, float eps2, float4 *acc_out, float *p
     hipError_t e;
     if (pairs) {
         nbk::PairsArgs pa{pos, n, eps2, p.splits, a.part};
-        e = nbk::launch_pairs(p.band, pot, pa, stream);
+        e = nbk::launch_pairs(p.band, p.tpl, pot, pa, stream);
     } else {
         e = nbk::launch_accel(p.bcast, p.tpl, p.wg, pot, grid_x(n, p.tpl, p.wg),
                               (unsigned)p.splits, a, stream);

@@ -31,10 +31,10 @@ struct PairsArgs {
     float4 *part;       // part[slot*N + i], slot in [0, nb): every entry written once
 };
 
-// Pair-symmetric evaluation over bands of `band` bodies (512, 1024 or 2048;
-// 4 targets per lane). Writes nb partial slots per body; launch_combine or
-// launch_euler with splits = nb finishes the evaluation.
-hipError_t launch_pairs(int band, bool pot, const PairsArgs &args, hipStream_t stream);
+// Pair-symmetric evaluation over bands of `band` bodies (512, 1024 or 2048)
+// with tpl (4 or 8) targets per lane. Writes nb partial slots per body;
+// launch_combine or launch_euler with splits = nb finishes the evaluation.
+hipError_t launch_pairs(int band, int tpl, bool pot, const PairsArgs &args, hipStream_t stream);
 
 // Launch the acceleration kernel: grid (ceil(N / (wg*tpl)), S), block wg.
 // wg is 256 or 512 for the LDS broadcast and 256 for the others.

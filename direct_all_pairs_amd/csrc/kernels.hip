@@ -353,7 +353,7 @@ __global__ void __launch_bounds__(kWG) accel_readlane(AccelArgs k)
 
 // ---------------------------------------------------------------- PAIRS
 // Pair-symmetric evaluation. r_ji = -r_ij and |r_ji| = |r_ij|, so one pair's
-// q = |r|^2 + eps2 and inv = q^(-1/2) serve both bodies:
+// q = |r|^2 + eps2, inv = q^(-1/2) and inv^3 serve both bodies:
 //   a_i += m_j inv^3 r_ij,   a_j -= m_i inv^3 r_ij,   p_i -= m_j inv,   p_j -= m_i inv
 // (19 VALU instructions and one v_rsq_f32 per pair instead of 2 x 13 and two).
 //
@@ -368,22 +368,13 @@ __global__ void __launch_bounds__(kWG) accel_readlane(AccelArgs k)
 //
 // Inside an item the 4 waves share one i-set of 64*T bodies of band A (T per
 // lane) and take the 64-body j-blocks of band B round-robin. A j-block pass is
-// 64 steps: at step k lane l pairs its T targets with j-body (l - k) mod 64,
-// read from the wave's own LDS copy of the block with a rotated index; the
-// j-side sums travel with their body by rotating one lane per step (DPP
-// wave_ror:1), so after 64 steps lane l holds the j-side sums of j-body l.
-// A j-block's sums are added into the item's LDS accumulator of band B only by
-// the wave that owns the block, in i-set order. After each i-set the waves'
-// A-side sums are added in wave order through LDS.
-constexpr int kDppWaveRor1 = 0x13C;  // DPP control: rotate the 64 lanes right by one
-
-__device__ __forceinline__ float wave_ror1(float v)
-{
-    // every lane has a source lane under a rotation, so bound_ctrl needs no old value
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                         0, __builtin_bit_cast(int, v), kDppWaveRor1, 0xF, 0xF,
-                                         true));
-}
+// 64 steps: at step s lane l pairs its T targets with j-body (l - s) mod 64 of
+// the wave's own LDS copy of the block, and adds that body's sums into its LDS
+// slot (same index), which lane l - 1 wrote the step before. After 64 steps
+// every j-body has met every lane's targets once. A j-block's sums are added
+// into the item's LDS accumulator of band B only by the wave that owns the
+// block, in i-set order. After each i-set the waves' A-side sums are added in
+// wave order through LDS.
 
 // Body b (64-bit index) or a zero-mass body at the origin for b >= n.
 __device__ __forceinline__ float4 body_or_zero(const float4 *__restrict__ pos, int n, long long b)
@@ -393,12 +384,75 @@ __device__ __forceinline__ float4 body_or_zero(const float4 *__restrict__ pos, i
     return make_float4(in ? v.x : 0.0f, in ? v.y : 0.0f, in ? v.z : 0.0f, in ? v.w : 0.0f);
 }
 
+// Large i-sets or bands sum an i-set across waves sequentially through the
+// j-block buffer (keeps 2048-body bands at four workgroups per CU at T = 4);
+// small ones, whose occupancy is set by registers, use a one-pass buffer with
+// two barriers.
 template <int T, int BD>
+constexpr bool kSeqReduce = BD >= 2048 || T >= 8;
+
+// Entries per wave row of the j-block and slot arrays: one 64-body block, or,
+// for the sequential i-set sum, the wave's quarter of the 64*T sums. Rows are
+// whole multiples of the 1 KiB block, so a row base ORs onto a block offset.
+template <int T>
+constexpr int kRowLen = 16 * T > 64 ? 16 * T : 64;
+constexpr int kBlkBytes = 64 * (int)sizeof(float4);
+
+template <int T, int BD, bool SEQ = kSeqReduce<T, BD>>
 struct PairsShared {
-    float4 jacc[BD];         // B-side sums of the item, one per body of band B
-    float4 ired[4][64 * T];  // per-wave A-side sums of the current i-set
-    float4 jblk[4][64];      // each wave's copy of its current j-block
+    float4 jacc[BD];             // B-side sums of the item, one per body of band B
+    float4 jblk[4][kRowLen<T>];  // each wave's copy of its current j-block
+    float4 jsum[4][kRowLen<T>];  // each wave's B-side sums of that block, by block index
+    float4 ired[4][64 * T];      // per-wave A-side sums of the current i-set
 };
+
+template <int T, int BD>
+struct PairsShared<T, BD, true> {
+    float4 jacc[BD];             // B-side sums of the item, one per body of band B
+    float4 jblk[4][kRowLen<T>];  // each wave's copy of its current j-block; between
+                                 // i-sets, the running cross-wave sum of the i-set's
+                                 // A-side sums
+    float4 jsum[4][kRowLen<T>];  // each wave's B-side sums of its block, by block index
+};
+
+// One step: partner (jx, jy, jz, jm) against the lane's T targets. b* gather
+// the targets' sums; with SYM, g* gather the partner's.
+template <int T, bool POT, bool SYM>
+__device__ __forceinline__ void pair_step(float jx, float jy, float jz, float jm,
+                                          const float (&tx)[T], const float (&ty)[T],
+                                          const float (&tz)[T], const float (&tm)[T],
+                                          float eps2, float (&bx)[T], float (&by)[T],
+                                          float (&bz)[T], float (&bp)[T], float &gx, float &gy,
+                                          float &gz, float &gp)
+{
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const float dx = jx - tx[t], dy = jy - ty[t], dz = jz - tz[t];
+        float q = __builtin_fmaf(dx, dx, eps2);
+        q = __builtin_fmaf(dy, dy, q);
+        q = __builtin_fmaf(dz, dz, q);
+        const float inv = __builtin_amdgcn_rsqf(q);
+        const float inv3 = (inv * inv) * inv;  // shared by both sides
+        const float sj = jm * inv3;            // m_j / r^3
+        bx[t] = __builtin_fmaf(sj, dx, bx[t]);
+        by[t] = __builtin_fmaf(sj, dy, by[t]);
+        bz[t] = __builtin_fmaf(sj, dz, bz[t]);
+        if constexpr (POT) bp[t] = __builtin_fmaf(jm, inv, bp[t]);
+        if constexpr (SYM) {
+            const float si = tm[t] * inv3;  // m_i / r^3
+            gx = __builtin_fmaf(-si, dx, gx);
+            gy = __builtin_fmaf(-si, dy, gy);
+            gz = __builtin_fmaf(-si, dz, gz);
+            if constexpr (POT) gp = __builtin_fmaf(tm[t], inv, gp);
+        }
+    }
+}
+
+template <typename V>
+__device__ __forceinline__ V &at_byte(void *base, int off)
+{
+    return *reinterpret_cast<V *>(static_cast<char *>(base) + off);
+}
 
 template <int T, int BD, bool POT, bool SYM>
 __device__ __forceinline__ void pairs_item(const PairsArgs &k, int A, int B, int slot_i,
@@ -408,7 +462,10 @@ __device__ __forceinline__ void pairs_item(const PairsArgs &k, int A, int B, int
     constexpr int NIS = BD / (64 * T);  // i-sets per band
     constexpr int NJB = BD / 64;        // j-blocks per band
     static_assert(NIS >= 1 && NJB % W == 0, "band must hold whole i-sets and j-blocks");
+    static_assert(sizeof(sh.jblk[0]) % kBlkBytes == 0 && sizeof(sh.jsum[0]) == sizeof(sh.jblk[0]),
+                  "rows must be whole blocks of equal size");
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int row = w * (int)sizeof(sh.jblk[0]);  // byte offset of the wave's row
     for (int is = 0; is < NIS; ++is) {
         float tx[T], ty[T], tz[T], tm[T];
         float ax[T], ay[T], az[T], ap[T];
@@ -421,56 +478,50 @@ __device__ __forceinline__ void pairs_item(const PairsArgs &k, int A, int B, int
             tm[t] = b.w;
             ax[t] = ay[t] = az[t] = ap[t] = 0.0f;
         }
+        float4 jnext = body_or_zero(k.pos, k.n, (long long)B * BD + w * 64 + lane);
         for (int jb = w; jb < NJB; jb += W) {
-            const float4 jbody = body_or_zero(k.pos, k.n, (long long)B * BD + jb * 64 + lane);
-            // The block copy is written and read only by this wave, whose LDS
-            // accesses execute in program order; the wave barriers keep the
-            // compiler from moving other lanes' reads across the write.
+            const float4 jbody = jnext;
+            // the wave's next j-block, loaded while this one is evaluated
+            if (jb + W < NJB) jnext = body_or_zero(k.pos, k.n, (long long)B * BD + (jb + W) * 64 + lane);
+            // The block copy and the slots are written and read only by this
+            // wave, whose LDS accesses execute in program order; the wave
+            // barriers keep the compiler from moving accesses across.
             __builtin_amdgcn_wave_barrier();
             sh.jblk[w][lane] = jbody;
+            if constexpr (SYM) sh.jsum[w][lane] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             __builtin_amdgcn_wave_barrier();
             float jx = jbody.x, jy = jbody.y, jz = jbody.z, jm = jbody.w;
-            float gx = 0.0f, gy = 0.0f, gz = 0.0f, gp = 0.0f;
             float bx[T], by[T], bz[T], bp[T];
 #pragma unroll
             for (int t = 0; t < T; ++t) bx[t] = by[t] = bz[t] = bp[t] = 0.0f;
-#pragma unroll 1
+            int cur = row | (lane * (int)sizeof(float4));  // byte offset of entry (lane - step) mod 64
+            // two steps per trip (no register copies of the partner) except where
+            // measured slower: 4 targets per lane in 2048-body bands
+            constexpr int U = (T == 4 && BD >= 2048) ? 1 : 2;
+#pragma unroll U
             for (int step = 0; step < 64; ++step) {
+                const int nxt = ((cur - (int)sizeof(float4)) & (kBlkBytes - 1)) | row;
                 // partner of the next step, read ahead of this step's arithmetic
-                const float4 nb4 = sh.jblk[w][(lane - step - 1) & 63];
-#pragma unroll
-                for (int t = 0; t < T; ++t) {
-                    const float dx = jx - tx[t], dy = jy - ty[t], dz = jz - tz[t];
-                    float q = __builtin_fmaf(dx, dx, eps2);
-                    q = __builtin_fmaf(dy, dy, q);
-                    q = __builtin_fmaf(dz, dz, q);
-                    const float inv = __builtin_amdgcn_rsqf(q);
-                    const float inv2 = inv * inv;
-                    const float tj = jm * inv;  // m_j / r
-                    const float sj = tj * inv2; // m_j / r^3
-                    bx[t] = __builtin_fmaf(sj, dx, bx[t]);
-                    by[t] = __builtin_fmaf(sj, dy, by[t]);
-                    bz[t] = __builtin_fmaf(sj, dz, bz[t]);
-                    if constexpr (POT) bp[t] = __builtin_fmaf(jm, inv, bp[t]);
-                    if constexpr (SYM) {
-                        const float ti = tm[t] * inv;  // m_i / r
-                        const float si = ti * inv2;    // m_i / r^3
-                        gx = __builtin_fmaf(-si, dx, gx);
-                        gy = __builtin_fmaf(-si, dy, gy);
-                        gz = __builtin_fmaf(-si, dz, gz);
-                        if constexpr (POT) gp = __builtin_fmaf(tm[t], inv, gp);
-                    }
+                const float4 nb4 = at_byte<const float4>(&sh.jblk[0][0], nxt);
+                float gx = 0.0f, gy = 0.0f, gz = 0.0f, gp = 0.0f;
+                if constexpr (SYM) {
+                    const float4 g = at_byte<const float4>(&sh.jsum[0][0], cur);
+                    gx = g.x;
+                    gy = g.y;
+                    gz = g.z;
+                    gp = g.w;
+                }
+                pair_step<T, POT, SYM>(jx, jy, jz, jm, tx, ty, tz, tm, eps2, bx, by, bz, bp, gx,
+                                       gy, gz, gp);
+                if constexpr (SYM) {
+                    at_byte<float4>(&sh.jsum[0][0], cur) = make_float4(gx, gy, gz, gp);
+                    __builtin_amdgcn_wave_barrier();
                 }
                 jx = nb4.x;
                 jy = nb4.y;
                 jz = nb4.z;
                 jm = nb4.w;
-                if constexpr (SYM) {
-                    gx = wave_ror1(gx);
-                    gy = wave_ror1(gy);
-                    gz = wave_ror1(gz);
-                    if constexpr (POT) gp = wave_ror1(gp);
-                }
+                cur = nxt;
             }
 #pragma unroll
             for (int t = 0; t < T; ++t) {
@@ -480,31 +531,58 @@ __device__ __forceinline__ void pairs_item(const PairsArgs &k, int A, int B, int
                 ap[t] += bp[t];
             }
             if constexpr (SYM) {
+                const float4 g = sh.jsum[w][lane];
                 float4 o = sh.jacc[jb * 64 + lane];
-                o.x += gx;
-                o.y += gy;
-                o.z += gz;
-                o.w += gp;
+                o.x += g.x;
+                o.y += g.y;
+                o.z += g.z;
+                o.w += g.w;
                 sh.jacc[jb * 64 + lane] = o;
             }
         }
+        // Cross-wave sum of the i-set, in wave order ((w0 + w1) + w2) + w3 either way.
+        if constexpr (!kSeqReduce<T, BD>) {
 #pragma unroll
-        for (int t = 0; t < T; ++t) sh.ired[w][t * 64 + lane] = make_float4(ax[t], ay[t], az[t], ap[t]);
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < 64 * T; idx += 64 * W) {
-            float4 s = sh.ired[0][idx];
+            for (int t = 0; t < T; ++t)
+                sh.ired[w][t * 64 + lane] = make_float4(ax[t], ay[t], az[t], ap[t]);
+            __syncthreads();
+            for (int idx = threadIdx.x; idx < 64 * T; idx += 64 * W) {
+                float4 s = sh.ired[0][idx];
 #pragma unroll
-            for (int ww = 1; ww < W; ++ww) {
-                const float4 v = sh.ired[ww][idx];
-                s.x += v.x;
-                s.y += v.y;
-                s.z += v.z;
-                s.w += v.w;
+                for (int ww = 1; ww < W; ++ww) {
+                    const float4 v = sh.ired[ww][idx];
+                    s = make_float4(s.x + v.x, s.y + v.y, s.z + v.z, s.w + v.w);
+                }
+                const long long body = (long long)A * BD + is * 64 * T + idx;
+                if (body < k.n) k.part[(size_t)slot_i * (size_t)k.n + body] = s;
             }
-            const long long body = (long long)A * BD + is * 64 * T + idx;
-            if (body < k.n) k.part[(size_t)slot_i * (size_t)k.n + body] = s;
+            __syncthreads();
+            continue;
         }
+        // Sequential form through the j-block buffer (all waves are past their
+        // j-blocks at the barrier); wave W-1 stores the total.
+        float4 *red = &sh.jblk[0][0];
         __syncthreads();
+        for (int ww = 0; ww < W; ++ww) {
+            if (w == ww) {
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    const int idx = t * 64 + lane;
+                    float4 v = make_float4(ax[t], ay[t], az[t], ap[t]);
+                    if (ww > 0) {
+                        const float4 s = red[idx];
+                        v = make_float4(s.x + v.x, s.y + v.y, s.z + v.z, s.w + v.w);
+                    }
+                    if (ww < W - 1) {
+                        red[idx] = v;
+                    } else {
+                        const long long body = (long long)A * BD + is * 64 * T + idx;
+                        if (body < k.n) k.part[(size_t)slot_i * (size_t)k.n + body] = v;
+                    }
+                }
+            }
+            __syncthreads();
+        }
     }
     if constexpr (SYM) {
         for (int i = threadIdx.x; i < BD; i += 64 * W) {
@@ -621,12 +699,24 @@ hipError_t launch_accel(int bcast, int tpl, int wg, bool pot, unsigned grid_x, u
     return hipLaunchKernel(fn, dim3(grid_x, splits, 1), dim3(wg, 1, 1), kargs, 0, stream);
 }
 
-hipError_t launch_pairs(int band, bool pot, const PairsArgs &args, hipStream_t stream)
+template <int T, int BD>
+const void *pairs_fn(bool pot)
+{
+    return pot ? (const void *)&accel_pairs<T, BD, true> : (const void *)&accel_pairs<T, BD, false>;
+}
+
+hipError_t launch_pairs(int band, int tpl, bool pot, const PairsArgs &args, hipStream_t stream)
 {
     const void *fn = nullptr;
-    if (band == 512) fn = pot ? (const void *)&accel_pairs<4, 512, true> : (const void *)&accel_pairs<4, 512, false>;
-    if (band == 1024) fn = pot ? (const void *)&accel_pairs<4, 1024, true> : (const void *)&accel_pairs<4, 1024, false>;
-    if (band == 2048) fn = pot ? (const void *)&accel_pairs<4, 2048, true> : (const void *)&accel_pairs<4, 2048, false>;
+    if (tpl == 4) {
+        if (band == 512) fn = pairs_fn<4, 512>(pot);
+        if (band == 1024) fn = pairs_fn<4, 1024>(pot);
+        if (band == 2048) fn = pairs_fn<4, 2048>(pot);
+    } else if (tpl == 8) {
+        if (band == 512) fn = pairs_fn<8, 512>(pot);
+        if (band == 1024) fn = pairs_fn<8, 1024>(pot);
+        if (band == 2048) fn = pairs_fn<8, 2048>(pot);
+    }
     if (!fn || args.nbands < 1) return hipErrorInvalidValue;
     PairsArgs a = args;
     void *kargs[] = {&a};

@@ -89,9 +89,10 @@ enum {
  *   wg     - threads per workgroup: 256 or 512 for NBODY_BCAST_LDS (also the LDS
  *            tile, in bodies), 256 for the other schemes.
  *   mode   - NBODY_MODE_*. The fields above describe NBODY_MODE_TILES. With
- *            NBODY_MODE_PAIRS only `band` may be set (512, 1024 or 2048 bodies);
- *            the output then has splits = number of bands = partial-sum slots
- *            per body, chunk = band, bcast = LDS, tpl = 4, wg = 256. Its scratch
+ *            NBODY_MODE_PAIRS only `band` (512, 1024 or 2048 bodies) and `tpl`
+ *            (4 or 8 targets per lane; 0 = 8) may be set; the output then has
+ *            splits = number of bands = partial-sum slots per body, chunk =
+ *            band, bcast = LDS, wg = 256. Its scratch
  *            is splits x N x 16 bytes (8.6 GB at N = 2^20 with 2048-body bands);
  *            the automatic plan uses it only when that fits in 1/16 of device
  *            memory.

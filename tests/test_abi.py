@@ -98,7 +98,7 @@ def test_step_rejects(nb, args, code):
 
 def test_plan_rejects_bad_fields(nb):
     for plan in (dict(bcast=7), dict(tpl=3), dict(splits=-1), dict(splits=5000), dict(mode=3),
-                 dict(band=300), dict(mode=2, splits=4), dict(mode=2, tpl=2),
+                 dict(band=300), dict(mode=2, splits=4), dict(mode=2, tpl=2), dict(mode=2, tpl=1),
                  dict(mode=2, bcast="scalar"), dict(wg=512, bcast="scalar")):
         rc = nb.nbody_accel_plan(A, 16, 1e-4, B, None, plan=plan, stream=0, check=False)
         assert rc == nb.NBODY_EINVAL, plan

@@ -90,44 +90,50 @@ def test_single_body(nb):
 # ------------------------------------------------------------------ pair-symmetric bands
 
 BANDS = [512, 1024, 2048]
+PAIR_TPL = [4, 8]
 
 
+@pytest.mark.parametrize("tpl", PAIR_TPL)
 @pytest.mark.parametrize("band", BANDS)
 @pytest.mark.parametrize("n", [1, 2, 3, 65, 257, 1000, 2049, 4097])
-def test_pairs_small_n(nb, n, band):
+def test_pairs_small_n(nb, n, band, tpl):
     eps2 = np.float32(1e-4)
     pos, _ = _bodies(n, 100 + n)
-    plan = dict(mode="pairs", band=band)
+    plan = dict(mode="pairs", band=band, tpl=tpl)
     acc, pot = gpu_accel(pos, eps2, pot=True, plan=plan)
     assert_accel_parity(acc, pot, _ref(n, 100 + n, eps2), what=f"N={n} {plan}")
 
 
+@pytest.mark.parametrize("tpl", PAIR_TPL)
 @pytest.mark.parametrize("band", BANDS)
-def test_pairs_mid_n(nb, band):
+def test_pairs_mid_n(nb, band, tpl):
     """N = 20011 (prime): odd and even band counts, a ragged last band."""
     import oracle
 
     n, eps2 = 20011, np.float32(1e-4)
     pos, _ = _bodies(n, 7)
-    acc, pot = gpu_accel(pos, eps2, pot=True, plan=dict(mode="pairs", band=band))
+    acc, pot = gpu_accel(pos, eps2, pot=True, plan=dict(mode="pairs", band=band, tpl=tpl))
     idx = np.unique(np.concatenate([np.arange(300), np.arange(n - 300, n),
                                     np.random.default_rng(1).integers(0, n, 1000)]))
     ref = oracle.accel(pos, eps2, targets=idx)
-    assert_accel_parity(acc, pot, ref, idx=idx, what=f"N={n} pairs band={band}")
+    assert_accel_parity(acc, pot, ref, idx=idx, what=f"N={n} pairs band={band} tpl={tpl}")
 
 
+@pytest.mark.parametrize("tpl", PAIR_TPL)
 @pytest.mark.parametrize("n,band", [(4096, 512), (5000, 1024), (6144, 2048), (8192, 1024)])
-def test_pairs_even_and_odd_band_counts(nb, n, band):
+def test_pairs_even_and_odd_band_counts(nb, n, band, tpl):
     """Band counts 8, 5, 3 and 8: the opposite band of an even count is owned once."""
     pos, _ = _bodies(n, 31)
-    acc, pot = gpu_accel(pos, 1e-4, pot=True, plan=dict(mode="pairs", band=band))
-    assert_accel_parity(acc, pot, _ref(n, 31, np.float32(1e-4)), what=f"N={n} band={band}")
+    acc, pot = gpu_accel(pos, 1e-4, pot=True, plan=dict(mode="pairs", band=band, tpl=tpl))
+    assert_accel_parity(acc, pot, _ref(n, 31, np.float32(1e-4)),
+                        what=f"N={n} band={band} tpl={tpl}")
 
 
-def test_pairs_invariants(nb):
+@pytest.mark.parametrize("tpl", PAIR_TPL)
+def test_pairs_invariants(nb, tpl):
     """Determinism, exact mass doubling, potential-independent acceleration, dyadic
     translation, zero-mass padding (same band count): all bit-exact."""
-    plan = dict(mode="pairs", band=1024)
+    plan = dict(mode="pairs", band=1024, tpl=tpl)
     pos, _ = _bodies(6000, 41)
     a1, p1 = gpu_accel(pos, 1e-4, plan=plan)
     a2, p2 = gpu_accel(pos, 1e-4, plan=plan)
@@ -154,7 +160,9 @@ def test_auto_plan_modes(nb):
     assert nb.nbody_plan_for(4096).mode == nb.MODE_TILES
     assert nb.nbody_plan_for(65536).mode == nb.MODE_PAIRS
     p = nb.nbody_plan_for(1 << 20)
-    assert p.mode == nb.MODE_PAIRS and p.band == 2048 and p.splits == 512
+    assert p.mode == nb.MODE_PAIRS and p.band == 2048 and p.splits == 512 and p.tpl == 8
+    p = nb.nbody_plan_for(300007)
+    assert p.mode == nb.MODE_PAIRS and p.band == 1024 and p.splits == 293
 
 
 # ------------------------------------------------------------------ the five workloads
