@@ -107,42 +107,58 @@ def copy_calibration(nbytes: int) -> int:
     return 0
 
 
-def sweep(nb, w, pos, acc, pot, args) -> int:
-    """One evaluation (nbody_accel_plan) per layout, HIP-event timed; fastest layout last."""
+def sweep(nb, w, pos, vel, acc, pot, args) -> int:
+    """One call per layout (nbody_accel_plan, or nbody_step_plan for the stepping workloads),
+    HIP-event timed; fastest layout last."""
     import torch
 
     n = w.n
+    stepping = w.nsteps > 0 and args.workload != "disk4096"
     stream = torch.cuda.current_stream()
-    split_opts = [0, 1, 2, 4, 8, 16, 32, 64]
-    layouts = [("lds", t, wg) for t in (1, 2, 4) for wg in (256, 512)]
+    split_opts = [0, 1, 2, 4, 8, 16, 32, 64, 128]
+    layouts = [("lds", t, wg) for t in (1, 2, 4) for wg in (64, 128, 256, 512)]
     layouts += [(b, t, 256) for b in ("scalar", "readlane") for t in (1, 2, 4, 8)]
     layouts += [("pairs", t, band) for t in (4, 8) for band in (512, 1024, 2048)]
-    if args.sweep_only == "pairs":
-        layouts = [lay for lay in layouts if lay[0] == "pairs"]
-    elif args.sweep_only == "tiles":
-        layouts = [lay for lay in layouts if lay[0] != "pairs"]
+    if n <= 65536:
+        layouts += [("small", tw, 256) for tw in (4, 8, 16, 32)]
+    if args.sweep_only != "all":
+        keep = {"tiles": ("lds", "scalar", "readlane")}.get(args.sweep_only, (args.sweep_only,))
+        layouts = [lay for lay in layouts if lay[0] in keep]
     results = []
     for bcast, tpl, wg in layouts:
         for splits in (split_opts if bcast == "lds" else [0]):
+            if splits and (splits - 1) * wg >= n:  # some chunk would be empty
+                continue
             if bcast == "pairs":
                 plan = nb.make_plan(mode="pairs", band=wg, tpl=tpl)
+            elif bcast == "small":
+                plan = nb.make_plan(mode="small", tpl=tpl)
             else:
                 plan = nb.make_plan(mode="tiles", bcast=bcast, tpl=tpl, splits=splits, wg=wg)
-            if splits and splits * 256 > n:
-                continue
+
+            def call():
+                if stepping:
+                    nb.nbody_step_plan(pos, vel, n, float(w.dt), float(w.eps2), w.nsteps, plan,
+                                       stream)
+                else:
+                    nb.nbody_accel_plan(pos, n, float(w.eps2), acc, pot, plan, stream)
+
             for _ in range(max(1, args.warmup)):
-                nb.nbody_accel_plan(pos, n, float(w.eps2), acc, pot, plan, stream)
+                call()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for _ in range(args.steps):
-                nb.nbody_accel_plan(pos, n, float(w.eps2), acc, pot, plan, stream)
+                call()
             e1.record(stream)
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / args.steps
+            evals = w.nsteps if stepping else 1
             r = {"workload": args.workload, "N": n, "potential": pot is not None,
+                 "call": "nbody_step_plan" if stepping else "nbody_accel_plan",
                  "bcast": bcast, "tpl": tpl, "wg": wg, "splits": splits or "auto",
-                 "ms": round(ms, 4), "G_int_per_s": round(interactions(n) / ms / 1e6, 2)}
+                 "ms": round(ms, 4), "us_per_eval": round(ms * 1e3 / evals, 3),
+                 "G_int_per_s": round(interactions(n) * evals / ms / 1e6, 2)}
             results.append(r)
             print(json.dumps(r), flush=True)
     best = max(results, key=lambda r: r["G_int_per_s"])
@@ -166,9 +182,9 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for cpu_baseline (0 = skip)")
     ap.add_argument("--sweep", action="store_true",
-                    help="time every (broadcast, targets-per-lane, splits) layout of the workload's "
-                         "evaluation and print one JSON line per layout (no contract line)")
-    ap.add_argument("--sweep-only", default="all", choices=["all", "tiles", "pairs"],
+                    help="time every (broadcast, targets-per-lane, tile, splits) layout of the "
+                         "workload's call and print one JSON line per layout (no contract line)")
+    ap.add_argument("--sweep-only", default="all", choices=["all", "tiles", "pairs", "small"],
                     help="restrict --sweep to one evaluation mode")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (twice) and exit; "
@@ -217,7 +233,7 @@ def main(argv=None) -> int:
             nb.nbody_accel_plan(pos, n, float(w.eps2), acc, pot, plan, stream)
 
     if args.sweep:
-        return sweep(nb, w, pos, acc, pot, args)
+        return sweep(nb, w, pos, vel, acc, pot, args)
 
     for _ in range(args.warmup):
         one_step()

@@ -8,7 +8,7 @@ allocate outputs with torch and call the same entry points on the current
 torch stream.
 
 Importing this module loads the library and fails loudly if it has not been
-built (``python -m direct_all_pairs_amd.build`` or ``__graft_entry__.build()``).
+built (``python direct_all_pairs_amd/build.py`` or ``__graft_entry__.build()``).
 There is no CPU fallback.
 """
 
@@ -23,8 +23,8 @@ LIB_PATH = _PKG / "libnbody_amd.so"
 NBODY_OK, NBODY_EINVAL, NBODY_EALIGN, NBODY_EHIP, NBODY_ENOMEM = 0, 1, 2, 3, 4
 BCAST_AUTO, BCAST_LDS, BCAST_SCALAR, BCAST_READLANE = 0, 1, 2, 3
 BCAST_NAMES = {BCAST_LDS: "lds", BCAST_SCALAR: "scalar", BCAST_READLANE: "readlane"}
-MODE_AUTO, MODE_TILES, MODE_PAIRS = 0, 1, 2
-MODE_NAMES = {MODE_TILES: "tiles", MODE_PAIRS: "pairs"}
+MODE_AUTO, MODE_TILES, MODE_PAIRS, MODE_SMALL = 0, 1, 2, 3
+MODE_NAMES = {MODE_TILES: "tiles", MODE_PAIRS: "pairs", MODE_SMALL: "small"}
 
 
 class NbodyError(RuntimeError):
@@ -51,7 +51,7 @@ class nbody_plan(ctypes.Structure):
 import torch  # noqa: E402,F401
 
 if not LIB_PATH.exists():
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m direct_all_pairs_amd.build` "
+    raise ImportError(f"{LIB_PATH} is not built; run `python direct_all_pairs_amd/build.py` "
                       "(hipcc, gfx950) first. There is no CPU fallback.")
 
 _lib = ctypes.CDLL(str(LIB_PATH))
@@ -59,15 +59,17 @@ _vp, _i64, _f32, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.
 _lib.nbody_accel.argtypes = [_vp, _i64, _f32, _vp, _vp, _vp]
 _lib.nbody_accel_plan.argtypes = [_vp, _i64, _f32, _vp, _vp, ctypes.POINTER(nbody_plan), _vp]
 _lib.nbody_step.argtypes = [_vp, _vp, _i64, _f32, _f32, _i64, _vp]
+_lib.nbody_step_plan.argtypes = [_vp, _vp, _i64, _f32, _f32, _i64, ctypes.POINTER(nbody_plan),
+                                 _vp]
 _lib.nbody_plan_for.argtypes = [_i64, _int, ctypes.POINTER(nbody_plan)]
 _lib.nbody_last_error.restype = ctypes.c_char_p
 _lib.nbody_release_workspace.argtypes = []
 _lib.nbody_version.restype = ctypes.c_char_p
-for _f in ("nbody_accel", "nbody_accel_plan", "nbody_step", "nbody_plan_for",
-           "nbody_release_workspace"):
+for _f in ("nbody_accel", "nbody_accel_plan", "nbody_step", "nbody_step_plan",
+           "nbody_plan_for", "nbody_release_workspace"):
     getattr(_lib, _f).restype = _int
 
-EXPORTS = ("nbody_accel", "nbody_accel_plan", "nbody_step", "nbody_plan_for",
+EXPORTS = ("nbody_accel", "nbody_accel_plan", "nbody_step", "nbody_step_plan", "nbody_plan_for",
            "nbody_last_error", "nbody_release_workspace", "nbody_version")
 
 
@@ -132,6 +134,16 @@ def nbody_step(pos, vel, N: int, dt: float, eps2: float, nsteps: int, stream=Non
     return _check(rc, "nbody_step") if check else rc
 
 
+def nbody_step_plan(pos, vel, N: int, dt: float, eps2: float, nsteps: int, plan=None,
+                    stream=None, check: bool = True) -> int:
+    p = None
+    if plan is not None:
+        p = plan if isinstance(plan, nbody_plan) else make_plan(**plan)
+    rc = _lib.nbody_step_plan(_ptr(pos), _ptr(vel), int(N), float(dt), float(eps2), int(nsteps),
+                              ctypes.byref(p) if p is not None else None, _stream(stream))
+    return _check(rc, "nbody_step_plan") if check else rc
+
+
 def nbody_plan_for(N: int, want_pot: bool = False) -> nbody_plan:
     p = nbody_plan()
     _check(_lib.nbody_plan_for(int(N), int(bool(want_pot)), ctypes.byref(p)), "nbody_plan_for")
@@ -172,11 +184,14 @@ def accel(pos, eps2: float, pot: bool = True, plan=None):
     return acc, p
 
 
-def step(pos, vel, dt: float, eps2: float, nsteps: int = 1):
+def step(pos, vel, dt: float, eps2: float, nsteps: int = 1, plan=None):
     """nsteps Euler steps in place on pos and vel (N, 4) tensors, on the current stream."""
     _bodies(pos, "pos")
     _bodies(vel, "vel")
     if vel.shape != pos.shape:
         raise ValueError("pos and vel shapes differ")
-    nbody_step(pos, vel, pos.shape[0], dt, eps2, nsteps)
+    if plan is None:
+        nbody_step(pos, vel, pos.shape[0], dt, eps2, nsteps)
+    else:
+        nbody_step_plan(pos, vel, pos.shape[0], dt, eps2, nsteps, plan)
     return pos, vel

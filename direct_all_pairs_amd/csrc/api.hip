@@ -125,6 +125,10 @@ int scratch_get(int dev, hipStream_t stream, size_t bytes, void **out)
 // ------------------------------------------------------------ planning
 
 constexpr int kMaxSplits = 4096;
+// Largest N the automatic plan gives to NBODY_MODE_SMALL, and the smallest it
+// gives to NBODY_MODE_PAIRS.
+constexpr int64_t kSmallMaxN = 8192;
+constexpr int64_t kPairsMinN = 32768;
 
 int valid_tpl(int t) { return t == 1 || t == 2 || t == 4 || t == 8; }
 
@@ -142,10 +146,12 @@ size_t pairs_scratch(int64_t n, int band)
 }
 
 // Automatic layout, chosen by measurement on MI355X (layout sweeps of the
-// five workloads):
-//   - from N = 65536 up, pair-symmetric bands when their scratch fits: the
+// five workloads and of uniform cubes from N = 8192 to 65536):
+//   - up to N = 8192, the small-N kernel (one kernel per evaluation or step):
+//     4 targets per workgroup to N = 1024, 8 to 4096, 16 above;
+//   - from N = 32768 up, pair-symmetric bands when their scratch fits: the
 //     largest band that still yields at least 64 work items per compute unit,
-//     8 targets per lane;
+//     8 targets per lane from N = 65536 up and 4 below;
 //   - otherwise one-sided tiles with the LDS broadcast and one target per lane:
 //     every VALU operand of the inner step is then a VGPR, which issues about
 //     twice as fast as an SGPR operand; 512-thread workgroups (512-body LDS
@@ -153,12 +159,18 @@ size_t pairs_scratch(int64_t n, int band)
 //     128 workgroups per compute unit over the run (finer load balance; a
 //     chunk's sources stay L2-resident), at least 4 tiles per chunk from
 //     N = 65536 up and 1 below.
+int small_tw(int64_t n) { return n <= 1024 ? 4 : (n <= 4096 ? 8 : 16); }
+
 void auto_plan(int64_t n, const DeviceFacts &dev, nbody_plan *p)
 {
     const bool big = n >= 65536;
     if (p->mode == NBODY_MODE_AUTO) {
         p->mode = NBODY_MODE_TILES;
-        if (big && p->bcast == NBODY_BCAST_AUTO && p->tpl == 0 && p->splits == 0 && p->wg == 0) {
+        if (n <= kSmallMaxN && p->bcast == NBODY_BCAST_AUTO && p->tpl == 0 && p->splits == 0 &&
+            p->wg == 0 && p->band == 0)
+            p->mode = NBODY_MODE_SMALL;
+        if (n >= kPairsMinN && p->bcast == NBODY_BCAST_AUTO && p->tpl == 0 && p->splits == 0 &&
+            p->wg == 0) {
             for (int band : {2048, 1024, 512}) {
                 if (p->band != 0 && p->band != band) continue;
                 const int64_t nb = (n + band - 1) / band;
@@ -172,9 +184,15 @@ void auto_plan(int64_t n, const DeviceFacts &dev, nbody_plan *p)
             }
         }
     }
+    if (p->mode == NBODY_MODE_SMALL) {
+        p->bcast = NBODY_BCAST_LDS;
+        if (p->tpl == 0) p->tpl = small_tw(n);
+        p->wg = 256;
+        return;
+    }
     if (p->mode == NBODY_MODE_PAIRS) {
         p->bcast = NBODY_BCAST_LDS;
-        if (p->tpl == 0) p->tpl = 8;
+        if (p->tpl == 0) p->tpl = big ? 8 : 4;
         p->wg = 256;
         if (p->band == 0) p->band = n >= (1 << 19) ? 2048 : (n >= (1 << 17) ? 1024 : 512);
         return;
@@ -202,6 +220,12 @@ void auto_plan(int64_t n, const DeviceFacts &dev, nbody_plan *p)
 // splits = number of bands = number of partial slots, chunk = band.
 void finish_plan(int64_t n, nbody_plan *p)
 {
+    if (p->mode == NBODY_MODE_SMALL) {
+        p->splits = 1;
+        p->chunk = (int32_t)n;
+        p->band = 0;
+        return;
+    }
     if (p->mode == NBODY_MODE_PAIRS) {
         p->splits = (int32_t)((n + p->band - 1) / p->band);
         p->chunk = p->band;
@@ -224,17 +248,24 @@ int make_plan(int64_t n, const nbody_plan *user, int *dev_out, nbody_plan *p)
 {
     *p = user ? *user : nbody_plan{0, 0, 0, 0, 0, 0, 0};
     p->chunk = 0;
-    if (p->mode < 0 || p->mode > NBODY_MODE_PAIRS)
+    if (p->mode < 0 || p->mode > NBODY_MODE_SMALL)
         return fail(NBODY_EINVAL, "plan.mode=%d is not a NBODY_MODE_* value", p->mode);
+    if (p->mode == NBODY_MODE_SMALL &&
+        ((p->bcast != 0 && p->bcast != NBODY_BCAST_LDS) ||
+         (p->tpl != 0 && p->tpl != 4 && p->tpl != 8 && p->tpl != 16 && p->tpl != 32) ||
+         p->splits != 0 || (p->wg != 0 && p->wg != 256) || p->band != 0))
+        return fail(NBODY_EINVAL, "plan.mode=NBODY_MODE_SMALL takes only plan.tpl 4, 8, 16 or 32 "
+                                  "(targets per workgroup; bcast LDS, wg 256 implied)");
     if (p->bcast < 0 || p->bcast > NBODY_BCAST_READLANE)
         return fail(NBODY_EINVAL, "plan.bcast=%d is not a NBODY_BCAST_* value", p->bcast);
-    if (p->tpl != 0 && !valid_tpl(p->tpl))
+    if (p->tpl != 0 && !valid_tpl(p->tpl) && p->mode != NBODY_MODE_SMALL)
         return fail(NBODY_EINVAL, "plan.tpl=%d must be 0, 1, 2, 4 or 8", p->tpl);
     if (p->splits < 0 || p->splits > kMaxSplits)
         return fail(NBODY_EINVAL, "plan.splits=%d must be in [0, %d]", p->splits, kMaxSplits);
-    if (p->wg != 0 && p->wg != 256 && !(p->wg == 512 && p->bcast == NBODY_BCAST_LDS))
-        return fail(NBODY_EINVAL, "plan.wg=%d must be 0 or 256 (or 512 with the LDS broadcast)",
-                    p->wg);
+    if (p->wg != 0 && p->wg != 256 &&
+        !((p->wg == 64 || p->wg == 128 || p->wg == 512) && p->bcast == NBODY_BCAST_LDS))
+        return fail(NBODY_EINVAL,
+                    "plan.wg=%d must be 0 or 256 (or 64, 128, 512 with the LDS broadcast)", p->wg);
     if (p->band != 0 && !valid_band(p->band))
         return fail(NBODY_EINVAL, "plan.band=%d must be 0, 512, 1024 or 2048", p->band);
     if (p->mode == NBODY_MODE_PAIRS &&
@@ -270,6 +301,8 @@ int check_n(int64_t n)
 
 // Enqueue one evaluation: accelerations (and potentials) into acc_out/pot_out,
 // or with euler_pos/euler_vel set, one Euler step applied to them instead.
+// Enqueue one evaluation: acc/pot into acc_out/pot_out, or with euler_pos and
+// euler_vel set, one Euler step applied to them instead.
 int enqueue_eval(const float4 *pos, int n, float eps2, float4 *acc_out, float *pot_out,
                  const nbody_plan &p, int dev, hipStream_t stream, float4 *euler_pos,
                  float4 *euler_vel, float dt)
@@ -277,6 +310,12 @@ int enqueue_eval(const float4 *pos, int n, float eps2, float4 *acc_out, float *p
     const bool pot = pot_out != nullptr;
     const bool step = euler_pos != nullptr;
     const bool pairs = p.mode == NBODY_MODE_PAIRS;
+    if (p.mode == NBODY_MODE_SMALL) {
+        // steps of this mode go through enqueue_small_step
+        nbk::SmallArgs sa{pos, n, eps2, acc_out, pot_out, nullptr, nullptr, 0.0f};
+        hipError_t e = nbk::launch_small(p.tpl, pot, false, sa, stream);
+        return e == hipSuccess ? NBODY_OK : hip_fail(e, "small kernel launch");
+    }
     nbk::AccelArgs a{pos, n, eps2, p.chunk, acc_out, pot_out, nullptr};
     if (p.splits > 1 || step || pairs) {
         void *ws = nullptr;
@@ -330,6 +369,55 @@ int accel_impl(const nbody_f4 *pos, int64_t N, float eps2, nbody_f4 *acc, float 
     return rc == NBODY_OK ? ok() : rc;
 }
 
+int step_impl(nbody_f4 *pos, nbody_f4 *vel, int64_t N, float dt, float eps2, int64_t nsteps,
+              const nbody_plan *plan, hipStream_t stream)
+{
+    int rc = check_n(N);
+    if (rc != NBODY_OK) return rc;
+    if (nsteps < 0) return fail(NBODY_EINVAL, "nsteps=%lld must be >= 0", (long long)nsteps);
+    if (N == 0 || nsteps == 0) return ok();
+    if (!pos) return fail(NBODY_EINVAL, "pos is NULL");
+    if (!vel) return fail(NBODY_EINVAL, "vel is NULL");
+    if (!std::isfinite(dt)) return fail(NBODY_EINVAL, "dt=%g must be finite", (double)dt);
+    if (!eps2_ok(eps2))
+        return fail(NBODY_EINVAL, "eps2=%g must be a positive, finite, normal float", (double)eps2);
+    if (!aligned(pos, 16)) return fail(NBODY_EALIGN, "pos is not 16-byte aligned");
+    if (!aligned(vel, 16)) return fail(NBODY_EALIGN, "vel is not 16-byte aligned");
+    const size_t b16 = (size_t)N * 16;
+    if (overlap(pos, b16, vel, b16)) return fail(NBODY_EINVAL, "vel overlaps pos");
+    nbody_plan p;
+    int dev = 0;
+    rc = make_plan(N, plan, &dev, &p);
+    if (rc != NBODY_OK) return rc;
+    if (p.mode != NBODY_MODE_SMALL) {
+        for (int64_t s = 0; s < nsteps; ++s) {
+            rc = enqueue_eval((const float4 *)pos, (int)N, eps2, nullptr, nullptr, p, dev, stream,
+                              (float4 *)pos, (float4 *)vel, dt);
+            if (rc != NBODY_OK) return rc;
+        }
+        return ok();
+    }
+    // One kernel per step reads every position while it writes new ones, so the
+    // steps alternate between the caller's array and a scratch copy; after an
+    // odd step count the final positions are copied back on the stream.
+    void *ws = nullptr;
+    rc = scratch_get(dev, stream, b16, &ws);
+    if (rc != NBODY_OK) return rc;
+    float4 *x = (float4 *)pos, *other = (float4 *)ws;
+    for (int64_t s = 0; s < nsteps; ++s) {
+        float4 *src = (s % 2 == 0) ? x : other;
+        float4 *dst = (s % 2 == 0) ? other : x;
+        nbk::SmallArgs sa{src, (int)N, eps2, nullptr, nullptr, dst, (float4 *)vel, dt};
+        hipError_t e = nbk::launch_small(p.tpl, false, true, sa, stream);
+        if (e != hipSuccess) return hip_fail(e, "small kernel launch");
+    }
+    if (nsteps % 2 == 1) {
+        hipError_t e = hipMemcpyAsync(x, other, b16, hipMemcpyDeviceToDevice, stream);
+        if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(positions)");
+    }
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -349,29 +437,13 @@ int nbody_accel_plan(const nbody_f4 *pos_xyzm, int64_t N, float eps2, nbody_f4 *
 int nbody_step(nbody_f4 *pos, nbody_f4 *vel, int64_t N, float dt, float eps2, int64_t nsteps,
                hipStream_t stream)
 {
-    int rc = check_n(N);
-    if (rc != NBODY_OK) return rc;
-    if (nsteps < 0) return fail(NBODY_EINVAL, "nsteps=%lld must be >= 0", (long long)nsteps);
-    if (N == 0 || nsteps == 0) return ok();
-    if (!pos) return fail(NBODY_EINVAL, "pos is NULL");
-    if (!vel) return fail(NBODY_EINVAL, "vel is NULL");
-    if (!std::isfinite(dt)) return fail(NBODY_EINVAL, "dt=%g must be finite", (double)dt);
-    if (!eps2_ok(eps2))
-        return fail(NBODY_EINVAL, "eps2=%g must be a positive, finite, normal float", (double)eps2);
-    if (!aligned(pos, 16)) return fail(NBODY_EALIGN, "pos is not 16-byte aligned");
-    if (!aligned(vel, 16)) return fail(NBODY_EALIGN, "vel is not 16-byte aligned");
-    const size_t b16 = (size_t)N * 16;
-    if (overlap(pos, b16, vel, b16)) return fail(NBODY_EINVAL, "vel overlaps pos");
-    nbody_plan p;
-    int dev = 0;
-    rc = make_plan(N, nullptr, &dev, &p);
-    if (rc != NBODY_OK) return rc;
-    for (int64_t s = 0; s < nsteps; ++s) {
-        rc = enqueue_eval((const float4 *)pos, (int)N, eps2, nullptr, nullptr, p, dev, stream,
-                          (float4 *)pos, (float4 *)vel, dt);
-        if (rc != NBODY_OK) return rc;
-    }
-    return ok();
+    return step_impl(pos, vel, N, dt, eps2, nsteps, nullptr, stream);
+}
+
+int nbody_step_plan(nbody_f4 *pos, nbody_f4 *vel, int64_t N, float dt, float eps2,
+                    int64_t nsteps, const nbody_plan *plan, hipStream_t stream)
+{
+    return step_impl(pos, vel, N, dt, eps2, nsteps, plan, stream);
 }
 
 int nbody_plan_for(int64_t N, int want_pot, nbody_plan *out)

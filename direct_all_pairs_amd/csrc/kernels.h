@@ -17,10 +17,21 @@ struct AccelArgs {
     const float4 *pos;  // N bodies (x, y, z, m)
     int n;              // N
     float eps2;         // softening squared (positive normal float)
-    int chunk;          // sources per split-j chunk, multiple of kFlush; chunk s = blockIdx.y
+    int chunk;          // sources per split-j chunk, a whole number of tiles; chunk s = blockIdx.y
     float4 *acc_out;    // direct mode: (ax, ay, az, 0) per body
     float *pot_out;     // direct mode: p_i per body, or nullptr
     float4 *part;       // split mode (non-null): part[s*N + i] = (ax, ay, az, sum m/r)
+};
+
+struct SmallArgs {
+    const float4 *pos;  // N bodies (x, y, z, m); the positions a step starts from
+    int n;              // N
+    float eps2;         // softening squared (positive normal float)
+    float4 *acc_out;    // evaluation: (ax, ay, az, 0) per body
+    float *pot_out;     // evaluation: p_i per body, or nullptr
+    float4 *pos_next;   // step: x + dt v per body (w copied); must not alias pos
+    float4 *vel;        // step: v += dt a, in place
+    float dt;           // step
 };
 
 struct PairsArgs {
@@ -37,9 +48,14 @@ struct PairsArgs {
 hipError_t launch_pairs(int band, int tpl, bool pot, const PairsArgs &args, hipStream_t stream);
 
 // Launch the acceleration kernel: grid (ceil(N / (wg*tpl)), S), block wg.
-// wg is 256 or 512 for the LDS broadcast and 256 for the others.
+// wg is 64, 128, 256 or 512 for the LDS broadcast and 256 for the others.
 hipError_t launch_accel(int bcast, int tpl, int wg, bool pot, unsigned grid_x, unsigned splits,
                         const AccelArgs &args, hipStream_t stream);
+
+// Small-N evaluation (step = false: acc_out/pot_out) or Euler step (step =
+// true: pos_next/vel) in one kernel without partial sums: tw targets per
+// 256-thread workgroup (4, 8, 16 or 32), grid ceil(N / tw).
+hipError_t launch_small(int tw, bool pot, bool step, const SmallArgs &args, hipStream_t stream);
 
 // acc_out[i] = (sum_s part[s][i].xyz, 0); pot_out[i] = -sum_s part[s][i].w (if non-null).
 hipError_t launch_combine(const float4 *part, int n, int splits, float4 *acc_out, float *pot_out,

@@ -235,6 +235,47 @@ __global__ void __launch_bounds__(kWG) accel_scalar(AccelArgs k)
     store(tot, k, base);
 }
 
+// Partial sums are added in ascending chunk order s = 0, 1, ..., S-1, loading
+// eight slots ahead of the additions (the order of the additions is fixed).
+__device__ __forceinline__ float4 sum_parts(const float4 *part, int n, int splits, unsigned i)
+{
+    float4 a = part[i];
+    int s = 1;
+    for (; s + 8 <= splits; s += 8) {
+        float4 b[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) b[u] = part[(size_t)(s + u) * (size_t)n + i];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            a.x += b[u].x;
+            a.y += b[u].y;
+            a.z += b[u].z;
+            a.w += b[u].w;
+        }
+    }
+    for (; s < splits; ++s) {
+        const float4 b = part[(size_t)s * (size_t)n + i];
+        a.x += b.x;
+        a.y += b.y;
+        a.z += b.z;
+        a.w += b.w;
+    }
+    return a;
+}
+
+// Explicit Euler, position first with the old velocity (Degawa, "N 体問題",
+// slides 5-6 and 15): x' = x + dt v; v' = v + dt a(x). Each update is one FMA;
+// the mass (x.w) and v.w are carried through unchanged.
+__device__ __forceinline__ void euler_update(float4 &x, float4 &v, const float4 &a, float dt)
+{
+    x.x = __builtin_fmaf(dt, v.x, x.x);
+    x.y = __builtin_fmaf(dt, v.y, x.y);
+    x.z = __builtin_fmaf(dt, v.z, x.z);
+    v.x = __builtin_fmaf(dt, a.x, v.x);
+    v.y = __builtin_fmaf(dt, a.y, v.y);
+    v.z = __builtin_fmaf(dt, a.z, v.z);
+}
+
 // ---------------------------------------------------------------- LDS
 // The workgroup stages WG bodies per tile in LDS (each thread loads one
 // float4, coalesced). Two tile buffers: while tile t is read from one, the
@@ -247,7 +288,9 @@ __global__ void __launch_bounds__(kWG) accel_scalar(AccelArgs k)
 template <int T, bool POT, int WG>
 __global__ void __launch_bounds__(WG) accel_lds(AccelArgs k)
 {
-    static_assert(WG % kFlush == 0, "accumulation blocks must tile the LDS tile");
+    // accumulation block: kFlush sources, or the whole tile when it is smaller
+    constexpr int FL = WG < kFlush ? WG : kFlush;
+    static_assert(WG % FL == 0, "accumulation blocks must tile the LDS tile");
     constexpr int U = T <= 2 ? 4 : 2;
     __shared__ float4 tile[2][WG];
     const unsigned base = blockIdx.x * (unsigned)(WG * T);
@@ -276,6 +319,7 @@ __global__ void __launch_bounds__(WG) accel_lds(AccelArgs k)
         float4 a[U], b[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) a[u] = tl[u];
+#pragma unroll 1
         for (int u0 = 0; u0 < WG; u0 += 2 * U) {
 #pragma unroll
             for (int u = 0; u < U; ++u) b[u] = tl[u0 + U + u];
@@ -290,7 +334,7 @@ __global__ void __launch_bounds__(WG) accel_lds(AccelArgs k)
 #pragma unroll
             for (int u = 0; u < U; ++u) interact4<T, POT>(b[u], tg, eps2, blk);
             sched_fence();
-            if (((u0 + 2 * U) % kFlush) == 0) {
+            if (((u0 + 2 * U) % FL) == 0) {
                 add_into(tot, blk);
                 zero(blk);
             }
@@ -303,6 +347,88 @@ __global__ void __launch_bounds__(WG) accel_lds(AccelArgs k)
         __syncthreads();
     }
     store<T, POT, WG>(tot, k, base);
+}
+
+// ---------------------------------------------------------------- SMALL
+// Small N: each 256-thread workgroup owns TW targets and sums over every
+// source, so an evaluation (or an Euler step) is one kernel with no partial
+// sums in memory. Thread (t, g) = (tid mod TW, tid / TW) takes target t and
+// the sources g, g + G, g + 2G, ... (G = 256 / TW groups) of every LDS tile;
+// the G group sums of a target are then added through LDS in ascending g.
+// Tiles of 1024 bodies are double-buffered (the next one is loaded into
+// registers while the current one is evaluated; one barrier per tile). Lanes
+// of one group read the same LDS address (a broadcast) and a wave's groups are
+// consecutive bodies, so the reads are conflict-free.
+template <int TW, bool POT, bool STEP>
+__global__ void __launch_bounds__(256) accel_small(SmallArgs k)
+{
+    constexpr int G = 256 / TW;   // source groups
+    constexpr int TS = 1024;      // bodies per tile
+    constexpr int L = TS / 256;   // tile loads per thread
+    constexpr int PER = TS / G;   // sources per thread per tile
+    __shared__ float4 tile[2][TS];
+    __shared__ float4 red[G][TW];
+    const int t = threadIdx.x % TW, g = threadIdx.x / TW;
+    const int i = blockIdx.x * TW + t;
+    const float4 me = k.pos[i < k.n ? i : k.n - 1];
+    Targets<1> tg;
+    tg.x[0] = me.x;
+    tg.y[0] = me.y;
+    tg.z[0] = me.z;
+    const float eps2 = in_vgpr(k.eps2);
+    Sums<1, POT> tot, blk;
+    zero(tot);
+
+    const int ntiles = (k.n + TS - 1) / TS;
+#pragma unroll
+    for (int l = 0; l < L; ++l) tile[0][l * 256 + threadIdx.x] = load_or_zero(k.pos, l * 256 + threadIdx.x, k.n);
+    __syncthreads();
+    for (int it = 0; it < ntiles; ++it) {
+        const bool more = it + 1 < ntiles;
+        const int nb = (it + 1) * TS + threadIdx.x;  // this thread's first body of the next tile
+        float4 r[L];
+#pragma unroll
+        for (int l = 0; l < L; ++l) {
+            const int j = nb + l * 256;
+            r[l] = more ? k.pos[j < k.n ? j : k.n - 1] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+        const float4 *tl = tile[it & 1];
+        zero(blk);
+#pragma unroll 8
+        for (int u = 0; u < PER; ++u) interact4<1, POT>(tl[g + u * G], tg, eps2, blk);
+        add_into(tot, blk);
+        if (more) {
+#pragma unroll
+            for (int l = 0; l < L; ++l) {
+                const bool in = nb + l * 256 < k.n;
+                tile[(it + 1) & 1][l * 256 + threadIdx.x] =
+                    make_float4(in ? r[l].x : 0.0f, in ? r[l].y : 0.0f, in ? r[l].z : 0.0f,
+                                in ? r[l].w : 0.0f);
+            }
+        }
+        __syncthreads();
+    }
+    red[g][t] = make_float4(tot.ax[0], tot.ay[0], tot.az[0], POT ? tot.p[0] : 0.0f);
+    __syncthreads();
+    if (g != 0 || i >= k.n) return;
+    float4 a = red[0][t];
+    for (int gg = 1; gg < G; ++gg) {
+        const float4 b = red[gg][t];
+        a.x += b.x;
+        a.y += b.y;
+        a.z += b.z;
+        a.w += b.w;
+    }
+    if constexpr (STEP) {
+        float4 x = me;
+        float4 v = k.vel[i];
+        euler_update(x, v, a, k.dt);
+        k.pos_next[i] = x;
+        k.vel[i] = v;
+    } else {
+        k.acc_out[i] = make_float4(a.x, a.y, a.z, 0.0f);
+        if constexpr (POT) k.pot_out[i] = -a.w;
+    }
 }
 
 // ---------------------------------------------------------------- READLANE
@@ -616,21 +742,6 @@ __global__ void __launch_bounds__(256) accel_pairs(PairsArgs k)
 }
 
 // ---------------------------------------------------------------- combine / Euler
-// Partial sums are added in ascending chunk order s = 0, 1, ..., S-1.
-__device__ __forceinline__ float4 sum_parts(const float4 *__restrict__ part, int n, int splits,
-                                            unsigned i)
-{
-    float4 a = part[i];
-    for (int s = 1; s < splits; ++s) {
-        const float4 b = part[(size_t)s * (size_t)n + i];
-        a.x += b.x;
-        a.y += b.y;
-        a.z += b.z;
-        a.w += b.w;
-    }
-    return a;
-}
-
 __global__ void __launch_bounds__(256) combine_kernel(const float4 *__restrict__ part, int n,
                                                       int splits, float4 *__restrict__ acc_out,
                                                       float *__restrict__ pot_out)
@@ -642,9 +753,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const float4 *__restrict__
     if (pot_out) pot_out[i] = -a.w;
 }
 
-// Explicit Euler, position first with the old velocity (Degawa, "N 体問題",
-// slides 5-6 and 15): x += dt v; v += dt a(x^n). Each update is one FMA; the
-// mass (pos.w) and vel.w are carried through unchanged.
+// The ordered sum and Euler step of euler_update, in place.
 __global__ void __launch_bounds__(256) euler_kernel(const float4 *__restrict__ part, int n,
                                                     int splits, float4 *__restrict__ pos,
                                                     float4 *__restrict__ vel, float dt)
@@ -654,12 +763,7 @@ __global__ void __launch_bounds__(256) euler_kernel(const float4 *__restrict__ p
     const float4 a = sum_parts(part, n, splits, i);
     float4 x = pos[i];
     float4 v = vel[i];
-    x.x = __builtin_fmaf(dt, v.x, x.x);
-    x.y = __builtin_fmaf(dt, v.y, x.y);
-    x.z = __builtin_fmaf(dt, v.z, x.z);
-    v.x = __builtin_fmaf(dt, a.x, v.x);
-    v.y = __builtin_fmaf(dt, a.y, v.y);
-    v.z = __builtin_fmaf(dt, a.z, v.z);
+    euler_update(x, v, a, dt);
     pos[i] = x;
     vel[i] = v;
 }
@@ -667,6 +771,8 @@ __global__ void __launch_bounds__(256) euler_kernel(const float4 *__restrict__ p
 template <int T, bool POT>
 const void *accel_fn(int bcast, int wg)
 {
+    if (bcast == 1 && wg == 64) return (const void *)&accel_lds<T, POT, 64>;
+    if (bcast == 1 && wg == 128) return (const void *)&accel_lds<T, POT, 128>;
     if (bcast == 1 && wg == 256) return (const void *)&accel_lds<T, POT, 256>;
     if (bcast == 1 && wg == 512) return (const void *)&accel_lds<T, POT, 512>;
     if (wg != kWG) return nullptr;
@@ -699,6 +805,14 @@ hipError_t launch_accel(int bcast, int tpl, int wg, bool pot, unsigned grid_x, u
     return hipLaunchKernel(fn, dim3(grid_x, splits, 1), dim3(wg, 1, 1), kargs, 0, stream);
 }
 
+template <int TW>
+const void *small_fn(bool pot, bool step)
+{
+    if (step) return (const void *)&accel_small<TW, false, true>;
+    return pot ? (const void *)&accel_small<TW, true, false>
+               : (const void *)&accel_small<TW, false, false>;
+}
+
 template <int T, int BD>
 const void *pairs_fn(bool pot)
 {
@@ -722,6 +836,22 @@ hipError_t launch_pairs(int band, int tpl, bool pot, const PairsArgs &args, hipS
     void *kargs[] = {&a};
     return hipLaunchKernel(fn, dim3((unsigned)a.nbands, (unsigned)(a.nbands / 2 + 1), 1),
                            dim3(256, 1, 1), kargs, 0, stream);
+}
+
+hipError_t launch_small(int tw, bool pot, bool step, const SmallArgs &args, hipStream_t stream)
+{
+    const void *fn = nullptr;
+    if (tw == 4) fn = small_fn<4>(pot, step);
+    if (tw == 8) fn = small_fn<8>(pot, step);
+    if (tw == 16) fn = small_fn<16>(pot, step);
+    if (tw == 32) fn = small_fn<32>(pot, step);
+    if (!fn || args.n < 1) return hipErrorInvalidValue;
+    if (step && (!args.pos_next || !args.vel || args.pos_next == args.pos))
+        return hipErrorInvalidValue;
+    if (!step && !args.acc_out) return hipErrorInvalidValue;
+    SmallArgs a = args;
+    void *kargs[] = {&a};
+    return hipLaunchKernel(fn, dim3((unsigned)((a.n + tw - 1) / tw)), dim3(256), kargs, 0, stream);
 }
 
 hipError_t launch_combine(const float4 *part, int n, int splits, float4 *acc_out, float *pot_out,

@@ -74,8 +74,11 @@ enum {
 enum {
     NBODY_MODE_AUTO = 0,
     NBODY_MODE_TILES = 1, /* one-sided: every target sums over every source (N^2 pair terms) */
-    NBODY_MODE_PAIRS = 2  /* pair-symmetric: each unordered pair evaluated once, applied to
+    NBODY_MODE_PAIRS = 2, /* pair-symmetric: each unordered pair evaluated once, applied to
                              both bodies (r_ji = -r_ij), over bands of `band` bodies */
+    NBODY_MODE_SMALL = 3  /* one-sided, for small N: each 256-thread workgroup owns `tpl`
+                             targets and sums over every source; no partial sums, one kernel
+                             per evaluation and per Euler step */
 };
 
 /* How an evaluation is laid out on the GPU. Zero in a field means "choose
@@ -86,16 +89,20 @@ enum {
  *            go to scratch and a second kernel adds them in ascending chunk
  *            order (deterministic). S = 1 writes results directly.
  *   chunk  - (output only) sources per chunk; chunks are [s*chunk, min((s+1)*chunk, N)).
- *   wg     - threads per workgroup: 256 or 512 for NBODY_BCAST_LDS (also the LDS
- *            tile, in bodies), 256 for the other schemes.
+ *   wg     - threads per workgroup: 64, 128, 256 or 512 for NBODY_BCAST_LDS (also
+ *            the LDS tile, in bodies), 256 for the other schemes.
  *   mode   - NBODY_MODE_*. The fields above describe NBODY_MODE_TILES. With
  *            NBODY_MODE_PAIRS only `band` (512, 1024 or 2048 bodies) and `tpl`
- *            (4 or 8 targets per lane; 0 = 8) may be set; the output then has
+ *            (4 or 8 targets per lane; 0 = automatic) may be set; the output then has
  *            splits = number of bands = partial-sum slots per body, chunk =
  *            band, bcast = LDS, wg = 256. Its scratch
  *            is splits x N x 16 bytes (8.6 GB at N = 2^20 with 2048-body bands);
  *            the automatic plan uses it only when that fits in 1/16 of device
  *            memory.
+ *            With NBODY_MODE_SMALL only `tpl` may be set: targets per workgroup,
+ *            4, 8, 16 or 32 (0 = automatic); the output has splits = 1, chunk =
+ *            N, bcast = LDS, wg = 256. It needs no scratch for an evaluation and
+ *            N x 16 bytes for steps.
  *   band   - see mode.
  * The plan is a pure function of (N, device compute units and memory), so
  * nbody_accel and nbody_step use the same one for the same N, with or without
@@ -144,6 +151,13 @@ int nbody_accel_plan(const nbody_f4 *pos_xyzm, int64_t N, float eps2, nbody_f4 *
  */
 int nbody_step(nbody_f4 *pos, nbody_f4 *vel, int64_t N, float dt, float eps2, int64_t nsteps,
                hipStream_t stream);
+
+/*
+ * nbody_step_plan - nbody_step with an explicit layout (NULL = automatic), as
+ * nbody_accel_plan is to nbody_accel.
+ */
+int nbody_step_plan(nbody_f4 *pos, nbody_f4 *vel, int64_t N, float dt, float eps2,
+                    int64_t nsteps, const nbody_plan *plan, hipStream_t stream);
 
 /*
  * nbody_plan_for - the automatic plan for N bodies on the current device

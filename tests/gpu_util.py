@@ -41,14 +41,14 @@ def gpu_accel(pos_h: np.ndarray, eps2, pot=True, plan=None):
     return acc.cpu().numpy(), (p.cpu().numpy() if p is not None else None)
 
 
-def gpu_step(pos_h, vel_h, dt, eps2, nsteps):
+def gpu_step(pos_h, vel_h, dt, eps2, nsteps, plan=None):
     import torch
 
     import direct_all_pairs_amd as nb
 
     pos = to_dev(pos_h)
     vel = to_dev(vel_h)
-    nb.step(pos, vel, float(dt), float(eps2), nsteps)
+    nb.step(pos, vel, float(dt), float(eps2), nsteps, plan=plan)
     torch.cuda.synchronize()
     return pos.cpu().numpy(), vel.cpu().numpy()
 

@@ -17,9 +17,9 @@ HEADER = ROOT / "include" / "nbody.h"
 def nb():
     lib = ROOT / "direct_all_pairs_amd" / "libnbody_amd.so"
     if not lib.exists():
-        from direct_all_pairs_amd import build
+        import __graft_entry__
 
-        build.build()
+        __graft_entry__._hip_build_module().build()
     import direct_all_pairs_amd
 
     return direct_all_pairs_amd
@@ -97,9 +97,12 @@ def test_step_rejects(nb, args, code):
 
 
 def test_plan_rejects_bad_fields(nb):
-    for plan in (dict(bcast=7), dict(tpl=3), dict(splits=-1), dict(splits=5000), dict(mode=3),
+    for plan in (dict(bcast=7), dict(tpl=3), dict(splits=-1), dict(splits=5000), dict(mode=4),
+                 dict(mode=3, tpl=2), dict(mode=3, tpl=64), dict(mode=3, splits=2),
+                 dict(mode=3, wg=64), dict(mode=3, band=512), dict(mode=3, bcast="scalar"),
                  dict(band=300), dict(mode=2, splits=4), dict(mode=2, tpl=2), dict(mode=2, tpl=1),
-                 dict(mode=2, bcast="scalar"), dict(wg=512, bcast="scalar")):
+                 dict(mode=2, bcast="scalar"), dict(wg=512, bcast="scalar"), dict(wg=96),
+                 dict(wg=64, bcast="readlane")):
         rc = nb.nbody_accel_plan(A, 16, 1e-4, B, None, plan=plan, stream=0, check=False)
         assert rc == nb.NBODY_EINVAL, plan
 

@@ -56,6 +56,113 @@ def test_variants_small_n(nb, n, bcast, tpl, splits):
     assert_accel_parity(acc, pot, _ref(n, 100 + n, eps2), what=f"N={n} {plan}")
 
 
+@pytest.mark.parametrize("splits", [0, 1, 5])
+@pytest.mark.parametrize("tpl", TPLS)
+@pytest.mark.parametrize("wg", [64, 128, 512])
+@pytest.mark.parametrize("n", [1, 65, 257, 1000, 4097])
+def test_lds_tile_sizes(nb, n, wg, tpl, splits):
+    """LDS tiles of 64, 128 and 512 bodies (256 is covered above); tiles shorter than an
+    accumulation block flush once per tile."""
+    eps2 = np.float32(1e-4)
+    pos, _ = _bodies(n, 100 + n)
+    plan = dict(bcast="lds", tpl=tpl, splits=splits, wg=wg)
+    acc, pot = gpu_accel(pos, eps2, pot=True, plan=plan)
+    assert_accel_parity(acc, pot, _ref(n, 100 + n, eps2), what=f"N={n} {plan}")
+
+
+# ------------------------------------------------------------------ small-N kernel
+
+SMALL_TW = [4, 8, 16, 32]
+
+
+@pytest.mark.parametrize("tw", SMALL_TW)
+@pytest.mark.parametrize("n", [1, 2, 3, 65, 257, 1000, 1024, 1025, 2049, 4097, 9000])
+def test_small_mode(nb, n, tw):
+    """One kernel per evaluation: several 1024-body tiles, ragged last tile, targets past N
+    in the last workgroup."""
+    eps2 = np.float32(1e-4)
+    pos, _ = _bodies(n, 500 + n)
+    plan = dict(mode="small", tpl=tw)
+    acc, pot = gpu_accel(pos, eps2, pot=True, plan=plan)
+    assert_accel_parity(acc, pot, oracle_accel_cached(n, 500 + n, eps2), what=f"N={n} {plan}")
+    a0, p0 = gpu_accel(pos, eps2, pot=False, plan=plan)
+    assert p0 is None and np.array_equal(a0, acc)
+
+
+@functools.lru_cache(maxsize=None)
+def oracle_accel_cached(n, seed, eps2):
+    import oracle
+
+    return oracle.accel(_bodies(n, seed)[0], eps2)
+
+
+@pytest.mark.parametrize("tw", [4, 16])
+@pytest.mark.parametrize("n", [1, 700, 2048, 5000])
+def test_small_mode_steps(nb, n, tw):
+    """Steps alternate between the caller's positions and a scratch copy: one step is within
+    the single-step bound, odd and even step counts end in the caller's array and equal
+    repeated single steps bit for bit, masses are untouched."""
+    import oracle
+
+    pos, vel = _bodies(n, 600 + n)
+    plan = dict(mode="small", tpl=tw)
+    x1, v1 = gpu_step(pos, vel, 1e-3, 1e-4, 1, plan=plan)
+    assert_step_parity(pos, vel, x1, v1, 1e-3, oracle.accel(pos, np.float32(1e-4)),
+                       what=f"N={n} small tw={tw}")
+    xs, vs = x1, v1
+    for k in (2, 3):
+        xs, vs = gpu_step(xs, vs, 1e-3, 1e-4, 1, plan=plan)
+        xk, vk = gpu_step(pos, vel, 1e-3, 1e-4, k, plan=plan)
+        assert np.array_equal(xk, xs) and np.array_equal(vk, vs), k
+        assert np.array_equal(xk[:, 3].view(np.uint32), pos[:, 3].view(np.uint32))
+
+
+def test_small_mode_invariants(nb):
+    """Exact mass doubling, dyadic translation and zero-mass padding within the same tiles:
+    bit-exact."""
+    plan = dict(mode="small", tpl=8)
+    pos, _ = _bodies(3000, 43)
+    a1, p1 = gpu_accel(pos, 1e-4, plan=plan)
+    pos2 = pos.copy()
+    pos2[:, 3] *= 2
+    a2, p2 = gpu_accel(pos2, 1e-4, plan=plan)
+    assert np.array_equal(a2, 2 * a1) and np.array_equal(p2, 2 * p1)
+    padded = np.concatenate([pos, np.zeros((72, 4), np.float32)])  # still 3 tiles
+    a3, p3 = gpu_accel(padded, 1e-4, plan=plan)
+    assert np.array_equal(a3[:3000], a1) and np.array_equal(p3[:3000], p1)
+    dy, _ = workloads.dyadic_grid_bodies(3000, seed=14)
+    sh = dy.copy()
+    sh[:, :3] += np.array([0.25, -0.125, 0.0625], dtype=np.float32)
+    b1, q1 = gpu_accel(dy, 2.0 ** -10, plan=plan)
+    b2, q2 = gpu_accel(sh, 2.0 ** -10, plan=plan)
+    assert np.array_equal(b1, b2) and np.array_equal(q1, q2)
+
+
+STEP_PLANS = [dict(bcast="lds", tpl=1, wg=64), dict(bcast="lds", tpl=2, wg=128, splits=3),
+              dict(mode="small", tpl=32),
+              dict(bcast="scalar", tpl=4), dict(mode="pairs", band=512, tpl=8),
+              dict(mode="pairs", band=1024, tpl=4)]
+
+
+@pytest.mark.parametrize("plan", STEP_PLANS, ids=lambda p: "-".join(f"{k}{v}" for k, v in p.items()))
+@pytest.mark.parametrize("n", [1, 700, 3001])
+def test_step_plan(nb, n, plan):
+    """nbody_step_plan: one step within the single-step bound of the oracle for each
+    layout; three steps equal three single steps bit for bit."""
+    import oracle
+
+    pos, vel = _bodies(n, 400 + n)
+    x1, v1 = gpu_step(pos, vel, 1e-3, 1e-4, 1, plan=plan)
+    assert_step_parity(pos, vel, x1, v1, 1e-3, oracle.accel(pos, np.float32(1e-4)),
+                       what=f"N={n} {plan}")
+    assert np.array_equal(x1[:, 3].view(np.uint32), pos[:, 3].view(np.uint32))
+    x3, v3 = gpu_step(pos, vel, 1e-3, 1e-4, 3, plan=plan)
+    xs, vs = x1, v1
+    for _ in range(2):
+        xs, vs = gpu_step(xs, vs, 1e-3, 1e-4, 1, plan=plan)
+    assert np.array_equal(x3, xs) and np.array_equal(v3, vs)
+
+
 @pytest.mark.parametrize("tpl", TPLS)
 @pytest.mark.parametrize("bcast", BCASTS)
 def test_variants_mid_n_auto_splits(nb, bcast, tpl):
@@ -156,9 +263,17 @@ def test_pairs_invariants(nb, tpl):
 
 
 def test_auto_plan_modes(nb):
-    """Pair-symmetric bands from N = 65536 up (scratch permitting), tiles below."""
-    assert nb.nbody_plan_for(4096).mode == nb.MODE_TILES
-    assert nb.nbody_plan_for(65536).mode == nb.MODE_PAIRS
+    """Small-N kernel up to N = 8192, tiles above, pair-symmetric bands from N = 65536 up
+    (scratch permitting)."""
+    for n in (1, 2048, 4096, 8192):
+        p = nb.nbody_plan_for(n)
+        assert p.mode == nb.MODE_SMALL and p.splits == 1 and p.tpl in (4, 8, 16, 32), n
+    assert nb.nbody_plan_for(8193).mode == nb.MODE_TILES
+    assert nb.nbody_plan_for(32767).mode == nb.MODE_TILES
+    p = nb.nbody_plan_for(32768)
+    assert p.mode == nb.MODE_PAIRS and p.band == 512 and p.tpl == 4
+    p = nb.nbody_plan_for(65536)
+    assert p.mode == nb.MODE_PAIRS and p.band == 512 and p.tpl == 8
     p = nb.nbody_plan_for(1 << 20)
     assert p.mode == nb.MODE_PAIRS and p.band == 2048 and p.splits == 512 and p.tpl == 8
     p = nb.nbody_plan_for(300007)
@@ -359,7 +474,11 @@ def test_step_uses_the_accel_path(nb, n):
 
 
 def test_plan_for_is_reported(nb):
-    for n in (1, 2048, 65536, 300007, 1 << 20):
+    for n in (1, 2048, 9000, 65536, 300007, 1 << 20):
         p = nb.nbody_plan_for(n, True)
-        assert p.splits >= 1 and p.chunk % 256 == 0 and p.tpl in (1, 2, 4, 8)
-        assert (p.splits - 1) * p.chunk < n <= p.splits * p.chunk
+        if p.mode == nb.MODE_SMALL:
+            assert p.splits == 1 and p.chunk == n and p.tpl in (4, 8, 16, 32), n
+            continue
+        tile = p.band if p.mode == nb.MODE_PAIRS else p.wg
+        assert p.splits >= 1 and p.chunk % tile == 0 and p.tpl in (1, 2, 4, 8), n
+        assert (p.splits - 1) * p.chunk < n <= p.splits * p.chunk, n
