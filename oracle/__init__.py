@@ -77,6 +77,9 @@ class Oracle:
         lib.oracle_energy.argtypes = [_c_double_p, _c_double_p, ctypes.c_int64, ctypes.c_double,
                                       _c_double_p, _c_double_p]
         lib.oracle_energy.restype = ctypes.c_double
+        lib.oracle_diagnostics.argtypes = [_c_double_p, _c_double_p, _c_double_p, ctypes.c_int64,
+                                           ctypes.c_double, _c_double_p]
+        lib.oracle_diagnostics.restype = ctypes.c_int
         self._lib = lib
 
     def num_threads(self) -> int:
@@ -138,6 +141,34 @@ class Oracle:
     def energy(self, pos, vel, eps2):
         return self.energy_exact(pos, vel, as_f32(eps2))
 
+    def diagnostics_exact(self, pos, vel, eps2: float, pot=None) -> dict:
+        """K, W, E, momentum, angular momentum, mass and centre of mass of a state; W from the
+        given potentials p_i (self term included, as the method returns them) or, if pot is
+        None, from the oracle's own potential sum."""
+        p = _bodies64(pos)
+        v = _bodies64(vel)
+        if p.shape != v.shape:
+            raise ValueError("pos and vel shapes differ")
+        pp = None if pot is None else np.ascontiguousarray(pot, dtype=np.float64)
+        if pp is not None and pp.shape != (p.shape[0],):
+            raise ValueError("pot must hold one value per body")
+        out = np.zeros(13)
+        rc = self._lib.oracle_diagnostics(_ptr(p), _ptr(v), _ptr(pp), p.shape[0], float(eps2),
+                                          _ptr(out))
+        if rc != 0:
+            raise ValueError("oracle_diagnostics rejected its arguments")
+        return unpack_diagnostics(out)
+
+    def diagnostics(self, pos, vel, eps2, pot=None) -> dict:
+        return self.diagnostics_exact(pos, vel, as_f32(eps2), pot)
+
+
+def unpack_diagnostics(out) -> dict:
+    """The 13-value diagnostics record as a dict (same order as oracle_diagnostics)."""
+    out = [float(x) for x in out]
+    return {"kinetic": out[0], "potential": out[1], "total": out[2], "momentum": out[3:6],
+            "angular_momentum": out[6:9], "mass": out[9], "centre_of_mass": out[10:13]}
+
 
 _default: Oracle | None = None
 
@@ -178,3 +209,11 @@ def energy(pos, vel, eps2):
 
 def energy_exact(pos, vel, eps2):
     return get().energy_exact(pos, vel, eps2)
+
+
+def diagnostics(pos, vel, eps2, pot=None) -> dict:
+    return get().diagnostics(pos, vel, eps2, pot)
+
+
+def diagnostics_exact(pos, vel, eps2, pot=None) -> dict:
+    return get().diagnostics_exact(pos, vel, eps2, pot)

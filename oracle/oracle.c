@@ -172,3 +172,67 @@ double oracle_energy(const double *pos, const double *vel, int64_t n, double eps
     if (pe) *pe = w;
     return k + w;
 }
+
+/*
+ * Conserved-quantity diagnostics of a state (the pages give the potential,
+ * Nakasato "スライド 1" No.4; the sums below are the textbook mechanics built
+ * on it and on the velocities of the Euler scheme, Degawa slides 5-6):
+ *   out[0]  K = sum_i m_i |v_i|^2 / 2
+ *   out[1]  W = (1/2) sum_i m_i (p_i + m_i / sqrt(eps2))  (pair energy; each
+ *           pair once, the softened self term of p_i removed)
+ *   out[2]  E = K + W
+ *   out[3..5]  momentum  P = sum_i m_i v_i
+ *   out[6..8]  angular momentum  L = sum_i m_i (x_i x v_i)
+ *   out[9]     M = sum_i m_i
+ *   out[10..12] centre of mass  sum_i m_i x_i / M  (0 when M = 0)
+ * pot: the potentials p_i to use (including the self term, as the method
+ * returns them), or NULL to evaluate them here with the sum of oracle_accel.
+ * Sums run in index order.
+ */
+int oracle_diagnostics(const double *pos, const double *vel, const double *pot, int64_t n,
+                       double eps2, double *out)
+{
+    if (!pos || !vel || !out || n < 0 || !(eps2 > 0.0)) return -1;
+    double *p = NULL;
+    if (!pot) {
+        p = (double *)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+        if (!p) return -1;
+#pragma omp parallel for schedule(dynamic, 16)
+        for (int64_t i = 0; i < n; ++i) {
+            double a[3], ba, bp;
+            one_target(pos, n, eps2, i, a, &p[i], &ba, &bp);
+        }
+        pot = p;
+    }
+    const double inv_eps = 1.0 / sqrt(eps2);
+    double k = 0.0, w = 0.0, mom[3] = {0.0, 0.0, 0.0}, ang[3] = {0.0, 0.0, 0.0};
+    double m_tot = 0.0, mx[3] = {0.0, 0.0, 0.0};
+    for (int64_t i = 0; i < n; ++i) {
+        const double m = pos[4 * i + 3];
+        const double x = pos[4 * i], y = pos[4 * i + 1], z = pos[4 * i + 2];
+        const double vx = vel[4 * i], vy = vel[4 * i + 1], vz = vel[4 * i + 2];
+        k += 0.5 * m * (vx * vx + vy * vy + vz * vz);
+        w += 0.5 * m * (pot[i] + m * inv_eps);
+        mom[0] += m * vx;
+        mom[1] += m * vy;
+        mom[2] += m * vz;
+        ang[0] += m * (y * vz - z * vy);
+        ang[1] += m * (z * vx - x * vz);
+        ang[2] += m * (x * vy - y * vx);
+        m_tot += m;
+        mx[0] += m * x;
+        mx[1] += m * y;
+        mx[2] += m * z;
+    }
+    free(p);
+    out[0] = k;
+    out[1] = w;
+    out[2] = k + w;
+    for (int c = 0; c < 3; ++c) {
+        out[3 + c] = mom[c];
+        out[6 + c] = ang[c];
+        out[10 + c] = m_tot != 0.0 ? mx[c] / m_tot : 0.0;
+    }
+    out[9] = m_tot;
+    return 0;
+}

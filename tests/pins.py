@@ -288,6 +288,78 @@ def pin_energy_two_body(orc):
     _close([K, W, E], [k_want, -2.0 / 6.0, k_want - 2.0 / 6.0], 1e-16, "two-body energy")
 
 
+# ---------------------------------------------------------------- diagnostics
+# Not on the pages: kinetic energy, the pair energy built from the pages' potential
+# (Nakasato No.4), momentum and angular momentum are the textbook definitions.
+
+def pin_diagnostics_two_body(orc):
+    """The 3-4-5 system: every diagnostic by hand. K = 1/2 (0.3125) + 1/2 2 (1) = 1.15625;
+    W = -m0 m1/6 = -1/3 (pair once); P = (0.5, -2, 0.25); L = m1 (3, 4, 0) x (0, -1, 0) =
+    2 (0, 0, -3) = (0, 0, -6) plus m0 0 x v0 = 0; M = 3; centre of mass (2, 8/3, 0)."""
+    pos = _bodies([[0, 0, 0], [3, 4, 0]], [1.0, 2.0])
+    vel = np.array([[0.5, 0.0, 0.25, 0.0], [0.0, -1.0, 0.0, 0.0]])
+    for pot in (None, [-2.0 / 6.0 - 1.0 / math.sqrt(11.0), -1.0 / 6.0 - 2.0 / math.sqrt(11.0)]):
+        d = orc.diagnostics_exact(pos, vel, 11.0, pot=pot)
+        _close([d["kinetic"], d["potential"], d["total"]], [1.15625, -1 / 3, 1.15625 - 1 / 3],
+               1e-15, f"two-body energies (pot given: {pot is not None})")
+        _close(d["momentum"], [0.5, -2.0, 0.25], 0.0, "two-body momentum")
+        _close(d["angular_momentum"], [0.0, 0.0, -6.0], 0.0, "two-body angular momentum")
+        _close([d["mass"]], [3.0], 0.0, "two-body mass")
+        _close(d["centre_of_mass"], [2.0, 8.0 / 3.0, 0.0], 1e-15, "two-body centre of mass")
+
+
+def pin_diagnostics_rotating_ring(orc):
+    """A regular n-gon of masses m at radius R, each moving tangentially at speed u:
+    K = n m u^2/2, W = -(n m^2/2) sum_k (4 R^2 sin^2(pi k/n) + eps2)^(-1/2), P = 0,
+    L = (0, 0, n m R u), centre of mass at the origin."""
+    for n, R, e2, m, u, t0 in [(5, 1.5, 1e-3, 0.2, 0.7, 0.3), (8, 0.5, 0.04, 1.0, -1.25, 0.0)]:
+        t = t0 + 2 * np.pi * np.arange(n) / n
+        xyz = np.stack([R * np.cos(t), R * np.sin(t), np.zeros(n)], axis=1)
+        vel = np.zeros((n, 4))
+        vel[:, 0] = -u * np.sin(t)
+        vel[:, 1] = u * np.cos(t)
+        d = orc.diagnostics_exact(_bodies(xyz, m), vel, e2)
+        s2 = np.sin(np.pi * np.arange(1, n) / n) ** 2
+        w = -(n * m * m / 2) * np.sum(1 / np.sqrt(4 * R * R * s2 + e2))
+        _close([d["kinetic"], d["potential"]], [n * m * u * u / 2, w], 1e-13 * abs(w),
+               f"ring n={n} energies")
+        _close(d["momentum"], [0, 0, 0], 1e-14, f"ring n={n} momentum")
+        _close(d["angular_momentum"], [0, 0, n * m * R * u], 1e-14, f"ring n={n} L")
+        _close(d["centre_of_mass"], [0, 0, 0], 1e-15, f"ring n={n} centre of mass")
+
+
+def pin_diagnostics_pair_sum(orc):
+    """W from the per-body potentials (self term removed analytically) equals the sum over
+    distinct pairs (j != i skipped) of the energy routine, for random bodies."""
+    rng = np.random.Generator(np.random.PCG64(8))
+    x = rng.uniform(-1, 1, size=(60, 3))
+    m = rng.uniform(0.1, 2.0, size=60)
+    v = np.zeros((60, 4))
+    v[:, :3] = rng.uniform(-1, 1, size=(60, 3))
+    d = orc.diagnostics_exact(_bodies(x, m), v, 1e-3)
+    E, K, W = orc.energy_exact(_bodies(x, m), v, 1e-3)
+    _close([d["kinetic"], d["potential"]], [K, W], 1e-12 * abs(W), "pair-sum energy")
+
+
+def pin_diagnostics_euler_momentum(orc):
+    """One Euler step changes momentum by dt sum m a = 0 (third law): conserved to rounding;
+    centre of mass moves by dt P / M exactly in exact arithmetic."""
+    rng = np.random.Generator(np.random.PCG64(9))
+    x = rng.uniform(-1, 1, size=(40, 3))
+    m = rng.uniform(0.5, 1.5, size=40)
+    v = np.zeros((40, 4))
+    v[:, :3] = rng.uniform(-1, 1, size=(40, 3))
+    pos = _bodies(x, m)
+    dt = 1e-2
+    d0 = orc.diagnostics_exact(pos, v, 1e-3)
+    p1, v1 = orc.euler_exact(pos, v, dt, 1e-3, 1)
+    d1 = orc.diagnostics_exact(p1, v1, 1e-3)
+    scale = float(np.sum(m * np.linalg.norm(v[:, :3], axis=1))) + 1.0
+    _close(d1["momentum"], d0["momentum"], 1e-13 * scale, "Euler step momentum")
+    want = np.array(d0["centre_of_mass"]) + dt * np.array(d0["momentum"]) / d0["mass"]
+    _close(d1["centre_of_mass"], want, 1e-14, "Euler step centre of mass")
+
+
 ALL_PINS = [
     pin_single_body,
     pin_two_body_345,
@@ -302,4 +374,8 @@ ALL_PINS = [
     pin_euler_free_particle,
     pin_euler_two_body,
     pin_energy_two_body,
+    pin_diagnostics_two_body,
+    pin_diagnostics_rotating_ring,
+    pin_diagnostics_pair_sum,
+    pin_diagnostics_euler_momentum,
 ]

@@ -33,6 +33,14 @@ MUTATIONS = [
      "            for (int c = 0; c < 3; ++c) pos[4 * i + c] += dt * vel[4 * i + c];"),
     ("energy pairs counted twice", "wi[i] = 0.5 * pos[4 * i + 3] * s;", "wi[i] = pos[4 * i + 3] * s;"),
     ("z acceleration dropped", "az += mj * dz / q32;", "az += 0.0;"),
+    ("kinetic energy without 1/2", "k += 0.5 * m * (vx * vx + vy * vy + vz * vz);",
+     "k += m * (vx * vx + vy * vy + vz * vz);"),
+    ("self term added instead of removed", "w += 0.5 * m * (pot[i] + m * inv_eps);",
+     "w += 0.5 * m * (pot[i] - m * inv_eps);"),
+    ("angular momentum cross product reversed", "ang[2] += m * (x * vy - y * vx);",
+     "ang[2] += m * (y * vx - x * vy);"),
+    ("momentum uses position", "mom[1] += m * vy;", "mom[1] += m * y;"),
+    ("centre of mass unweighted", "mx[0] += m * x;", "mx[0] += x;"),
 ]
 
 
