@@ -235,6 +235,7 @@ def main(argv=None) -> int:
     if args.sweep:
         return sweep(nb, w, pos, vel, acc, pot, args)
 
+    diag0 = nb.diagnostics(pos, vel, float(w.eps2)) if stepping else None
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
@@ -297,6 +298,16 @@ def main(argv=None) -> int:
             "kernel_source_hash": khash,
         },
     }
+    if stepping:
+        # conserved quantities before the warm-up and after the timed steps, on the GPU
+        # (nbody_diagnostics; outside the timed region)
+        diag1 = nb.diagnostics(pos, vel, float(w.eps2))
+        e0, e1 = diag0["total"], diag1["total"]
+        out["config"]["energy_drift"] = {
+            "steps": (args.warmup + args.steps) * w.nsteps,
+            "relative": (e1 - e0) / abs(e0) if e0 else None,
+            "momentum_change": [b - a for a, b in zip(diag0["momentum"], diag1["momentum"])],
+        }
     if args.cpu_budget > 0:
         out["cpu_baseline"] = cpu_baseline(w.pos, w.eps2, args.cpu_budget)
     else:

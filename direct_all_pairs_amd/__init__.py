@@ -62,15 +62,18 @@ _lib.nbody_step.argtypes = [_vp, _vp, _i64, _f32, _f32, _i64, _vp]
 _lib.nbody_step_plan.argtypes = [_vp, _vp, _i64, _f32, _f32, _i64, ctypes.POINTER(nbody_plan),
                                  _vp]
 _lib.nbody_plan_for.argtypes = [_i64, _int, ctypes.POINTER(nbody_plan)]
+_lib.nbody_diagnostics.argtypes = [_vp, _vp, _vp, _i64, _f32, _vp, _vp]
 _lib.nbody_last_error.restype = ctypes.c_char_p
 _lib.nbody_release_workspace.argtypes = []
 _lib.nbody_version.restype = ctypes.c_char_p
 for _f in ("nbody_accel", "nbody_accel_plan", "nbody_step", "nbody_step_plan",
-           "nbody_plan_for", "nbody_release_workspace"):
+           "nbody_diagnostics", "nbody_plan_for", "nbody_release_workspace"):
     getattr(_lib, _f).restype = _int
 
-EXPORTS = ("nbody_accel", "nbody_accel_plan", "nbody_step", "nbody_step_plan", "nbody_plan_for",
-           "nbody_last_error", "nbody_release_workspace", "nbody_version")
+EXPORTS = ("nbody_accel", "nbody_accel_plan", "nbody_step", "nbody_step_plan", "nbody_diagnostics",
+           "nbody_plan_for", "nbody_last_error", "nbody_release_workspace", "nbody_version")
+DIAG_FIELDS = ("kinetic", "potential", "total", "momentum", "angular_momentum", "mass",
+               "centre_of_mass")
 
 
 def _ptr(x):
@@ -144,6 +147,14 @@ def nbody_step_plan(pos, vel, N: int, dt: float, eps2: float, nsteps: int, plan=
     return _check(rc, "nbody_step_plan") if check else rc
 
 
+def nbody_diagnostics(pos, vel, N: int, eps2: float, out, pot=None, stream=None,
+                      check: bool = True) -> int:
+    """out: device buffer of 13 float64 (one nbody_diag); pot: device potentials or None."""
+    rc = _lib.nbody_diagnostics(_ptr(pos), _ptr(vel), _ptr(pot), int(N), float(eps2), _ptr(out),
+                                _stream(stream))
+    return _check(rc, "nbody_diagnostics") if check else rc
+
+
 def nbody_plan_for(N: int, want_pot: bool = False) -> nbody_plan:
     p = nbody_plan()
     _check(_lib.nbody_plan_for(int(N), int(bool(want_pot)), ctypes.byref(p)), "nbody_plan_for")
@@ -195,3 +206,29 @@ def step(pos, vel, dt: float, eps2: float, nsteps: int = 1, plan=None):
     else:
         nbody_step_plan(pos, vel, pos.shape[0], dt, eps2, nsteps, plan)
     return pos, vel
+
+
+def unpack_diag(vals) -> dict:
+    """The 13 float64 of an nbody_diag as a dict."""
+    v = [float(x) for x in vals]
+    return {"kinetic": v[0], "potential": v[1], "total": v[2], "momentum": v[3:6],
+            "angular_momentum": v[6:9], "mass": v[9], "centre_of_mass": v[10:13]}
+
+
+def diagnostics(pos, vel, eps2: float, pot=None) -> dict:
+    """nbody_diagnostics on (N, 4) tensors (pot: (N,) tensor or None), on the current stream;
+    synchronises the stream and returns the values as a dict."""
+    import torch
+
+    _bodies(pos, "pos")
+    _bodies(vel, "vel")
+    if vel.shape != pos.shape:
+        raise ValueError("pos and vel shapes differ")
+    if pot is not None and not (isinstance(pot, torch.Tensor) and pot.is_cuda
+                                and pot.dtype == torch.float32 and pot.shape == (pos.shape[0],)
+                                and pot.is_contiguous()):
+        raise ValueError("pot must be a contiguous float32 CUDA tensor of shape (N,)")
+    out = torch.zeros(13, dtype=torch.float64, device=pos.device)
+    nbody_diagnostics(pos, vel, pos.shape[0], eps2, out, pot)
+    torch.cuda.current_stream().synchronize()
+    return unpack_diag(out.cpu().tolist())

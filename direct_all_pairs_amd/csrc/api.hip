@@ -446,6 +446,61 @@ int nbody_step_plan(nbody_f4 *pos, nbody_f4 *vel, int64_t N, float dt, float eps
     return step_impl(pos, vel, N, dt, eps2, nsteps, plan, stream);
 }
 
+int nbody_diagnostics(const nbody_f4 *pos, const nbody_f4 *vel, const float *pot, int64_t N,
+                      float eps2, nbody_diag *out, hipStream_t stream)
+{
+    int rc = check_n(N);
+    if (rc != NBODY_OK) return rc;
+    if (!out) return fail(NBODY_EINVAL, "out is NULL");
+    if (N > 0 && !pos) return fail(NBODY_EINVAL, "pos is NULL");
+    if (N > 0 && !vel) return fail(NBODY_EINVAL, "vel is NULL");
+    if (!eps2_ok(eps2))
+        return fail(NBODY_EINVAL, "eps2=%g must be a positive, finite, normal float", (double)eps2);
+    if (!aligned(out, 8)) return fail(NBODY_EALIGN, "out is not 8-byte aligned");
+    if (pos && !aligned(pos, 16)) return fail(NBODY_EALIGN, "pos is not 16-byte aligned");
+    if (vel && !aligned(vel, 16)) return fail(NBODY_EALIGN, "vel is not 16-byte aligned");
+    if (pot && !aligned(pot, 4)) return fail(NBODY_EALIGN, "pot is not 4-byte aligned");
+    const size_t b16 = (size_t)N * 16, b4 = (size_t)N * 4, bo = sizeof(nbody_diag);
+    if (N > 0 && (overlap(out, bo, pos, b16) || overlap(out, bo, vel, b16) ||
+                  (pot && overlap(out, bo, pot, b4))))
+        return fail(NBODY_EINVAL, "out overlaps an input");
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    // Scratch: [evaluation partials | acc (N x 16) | pot (N x 4) | workgroup sums]. The
+    // evaluation takes its partials from the start of the same block.
+    nbody_plan p{};
+    size_t part_bytes = 0;
+    if (!pot && N > 0) {
+        rc = make_plan(N, nullptr, &dev, &p);
+        if (rc != NBODY_OK) return rc;
+        if (p.mode == NBODY_MODE_PAIRS || p.splits > 1)
+            part_bytes = (size_t)p.splits * (size_t)N * sizeof(float4);
+    }
+    const size_t eval_bytes = (!pot && N > 0) ? b16 + b4 : 0;
+    const int nb = nbk::diag_blocks((int)N);
+    const size_t sums_off = (part_bytes + eval_bytes + 255) / 256 * 256;
+    const size_t total = sums_off + (size_t)nb * nbk::kDiagSums * sizeof(double);
+    void *ws = nullptr;
+    rc = scratch_get(dev, stream, total, &ws);
+    if (rc != NBODY_OK) return rc;
+    char *base = (char *)ws;
+    const float *use_pot = pot;
+    if (!pot && N > 0) {
+        float4 *acc = (float4 *)(base + part_bytes);
+        float *pp = (float *)(base + part_bytes + b16);
+        rc = enqueue_eval((const float4 *)pos, (int)N, eps2, acc, pp, p, dev, stream, nullptr,
+                          nullptr, 0.0f);
+        if (rc != NBODY_OK) return rc;
+        use_pot = pp;
+    }
+    e = nbk::launch_diagnostics((const float4 *)pos, (const float4 *)vel, use_pot, (int)N,
+                                1.0 / std::sqrt((double)eps2), (double *)(base + sums_off),
+                                (double *)out, stream);
+    if (e != hipSuccess) return hip_fail(e, "diagnostics kernel launch");
+    return ok();
+}
+
 int nbody_plan_for(int64_t N, int want_pot, nbody_plan *out)
 {
     if (!out) return fail(NBODY_EINVAL, "out is NULL");

@@ -57,6 +57,14 @@ hipError_t launch_accel(int bcast, int tpl, int wg, bool pot, unsigned grid_x, u
 // 256-thread workgroup (4, 8, 16 or 32), grid ceil(N / tw).
 hipError_t launch_small(int tw, bool pot, bool step, const SmallArgs &args, hipStream_t stream);
 
+// Diagnostics: fp64 sums over the bodies in a fixed order (independent of
+// timing). diag_blocks(n) workgroups write kDiagSums partial sums each to
+// part; the final kernel adds them and writes the 13 values of nbody_diag.
+constexpr int kDiagSums = 12;  // K, W, P (3), L (3), M, M x (3)
+int diag_blocks(int n);
+hipError_t launch_diagnostics(const float4 *pos, const float4 *vel, const float *pot, int n,
+                              double inv_eps, double *part, double *out, hipStream_t stream);
+
 // acc_out[i] = (sum_s part[s][i].xyz, 0); pot_out[i] = -sum_s part[s][i].w (if non-null).
 hipError_t launch_combine(const float4 *part, int n, int splits, float4 *acc_out, float *pot_out,
                           hipStream_t stream);

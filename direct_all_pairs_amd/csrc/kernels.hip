@@ -768,6 +768,87 @@ __global__ void __launch_bounds__(256) euler_kernel(const float4 *__restrict__ p
     vel[i] = v;
 }
 
+// ---------------------------------------------------------------- diagnostics
+// Conserved quantities of a state, in fp64 (the inputs are fp32, so products
+// and squares are nearly exact): per body
+//   K += m |v|^2 / 2,  W += m (p + m / eps) / 2,  P += m v,  L += m x × v,
+//   M += m,  MX += m x
+// (the pair energy from the method's potential with its softened self term
+// removed; Nakasato, "スライド 1", No.4 for p). Thread t of workgroup b takes
+// bodies b*256 + t + k*(B*256); workgroup sums use a fixed tree, the final sum
+// adds the B workgroup sums in order. Deterministic for a given N.
+constexpr int kDiagMaxBlocks = 1024;
+
+__device__ __forceinline__ void diag_tree(double (&v)[kDiagSums], double (*red)[256])
+{
+#pragma unroll
+    for (int q = 0; q < kDiagSums; ++q) red[q][threadIdx.x] = v[q];
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+        if ((int)threadIdx.x < s) {
+#pragma unroll
+            for (int q = 0; q < kDiagSums; ++q) red[q][threadIdx.x] += red[q][threadIdx.x + s];
+        }
+        __syncthreads();
+    }
+}
+
+__global__ void __launch_bounds__(256) diag_partial_kernel(const float4 *__restrict__ pos,
+                                                           const float4 *__restrict__ vel,
+                                                           const float *__restrict__ pot, int n,
+                                                           double inv_eps, double *part)
+{
+    __shared__ double red[kDiagSums][256];
+    double v[kDiagSums];
+#pragma unroll
+    for (int q = 0; q < kDiagSums; ++q) v[q] = 0.0;
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n;
+         i += (long long)gridDim.x * 256) {
+        const float4 b = pos[i], u = vel[i];
+        const double m = b.w, x = b.x, y = b.y, z = b.z;
+        const double vx = u.x, vy = u.y, vz = u.z;
+        v[0] += 0.5 * m * (vx * vx + vy * vy + vz * vz);
+        v[1] += 0.5 * m * ((double)pot[i] + m * inv_eps);
+        v[2] += m * vx;
+        v[3] += m * vy;
+        v[4] += m * vz;
+        v[5] += m * (y * vz - z * vy);
+        v[6] += m * (z * vx - x * vz);
+        v[7] += m * (x * vy - y * vx);
+        v[8] += m;
+        v[9] += m * x;
+        v[10] += m * y;
+        v[11] += m * z;
+    }
+    diag_tree(v, red);
+    if (threadIdx.x < kDiagSums) part[blockIdx.x * kDiagSums + threadIdx.x] = red[threadIdx.x][0];
+}
+
+__global__ void __launch_bounds__(256) diag_final_kernel(const double *__restrict__ part,
+                                                         int nblocks, double *__restrict__ out)
+{
+    __shared__ double red[kDiagSums][256];
+    double v[kDiagSums];
+#pragma unroll
+    for (int q = 0; q < kDiagSums; ++q) v[q] = 0.0;
+    for (int b = threadIdx.x; b < nblocks; b += 256) {
+#pragma unroll
+        for (int q = 0; q < kDiagSums; ++q) v[q] += part[b * kDiagSums + q];
+    }
+    diag_tree(v, red);
+    if (threadIdx.x != 0) return;
+    const double k = red[0][0], w = red[1][0], m = red[8][0];
+    out[0] = k;
+    out[1] = w;
+    out[2] = k + w;
+    for (int c = 0; c < 3; ++c) {
+        out[3 + c] = red[2 + c][0];
+        out[6 + c] = red[5 + c][0];
+        out[10 + c] = m != 0.0 ? red[9 + c][0] / m : 0.0;
+    }
+    out[9] = m;
+}
+
 template <int T, bool POT>
 const void *accel_fn(int bcast, int wg)
 {
@@ -852,6 +933,26 @@ hipError_t launch_small(int tw, bool pot, bool step, const SmallArgs &args, hipS
     SmallArgs a = args;
     void *kargs[] = {&a};
     return hipLaunchKernel(fn, dim3((unsigned)((a.n + tw - 1) / tw)), dim3(256), kargs, 0, stream);
+}
+
+int diag_blocks(int n)
+{
+    const int b = (n + 255) / 256;
+    return b < 1 ? 1 : (b > kDiagMaxBlocks ? kDiagMaxBlocks : b);
+}
+
+hipError_t launch_diagnostics(const float4 *pos, const float4 *vel, const float *pot, int n,
+                              double inv_eps, double *part, double *out, hipStream_t stream)
+{
+    if (n < 0 || !part || !out || (n > 0 && (!pos || !vel || !pot))) return hipErrorInvalidValue;
+    const int nb = diag_blocks(n);
+    void *k1[] = {&pos, &vel, &pot, &n, &inv_eps, &part};
+    hipError_t e = hipLaunchKernel((const void *)&diag_partial_kernel, dim3(nb), dim3(256), k1, 0,
+                                   stream);
+    if (e != hipSuccess) return e;
+    int nbl = nb;
+    void *k2[] = {&part, &nbl, &out};
+    return hipLaunchKernel((const void *)&diag_final_kernel, dim3(1), dim3(256), k2, 0, stream);
 }
 
 hipError_t launch_combine(const float4 *part, int n, int splits, float4 *acc_out, float *pot_out,

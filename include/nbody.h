@@ -159,6 +159,35 @@ int nbody_step(nbody_f4 *pos, nbody_f4 *vel, int64_t N, float dt, float eps2, in
 int nbody_step_plan(nbody_f4 *pos, nbody_f4 *vel, int64_t N, float dt, float eps2,
                     int64_t nsteps, const nbody_plan *plan, hipStream_t stream);
 
+/* Conserved-quantity diagnostics of a state (nbody_diagnostics), in fp64. */
+typedef struct nbody_diag {
+    double kinetic;             /* K = sum m |v|^2 / 2 */
+    double potential;           /* W = sum m (p + m / sqrt(eps2)) / 2: the pair energy, each
+                                   pair once, the softened self term of p removed */
+    double total;               /* K + W */
+    double momentum[3];         /* sum m v */
+    double angular_momentum[3]; /* sum m (x cross v) */
+    double mass;                /* sum m */
+    double centre_of_mass[3];   /* sum m x / sum m (0 when the mass is 0) */
+} nbody_diag;
+
+/*
+ * nbody_diagnostics - K, W, E, momentum, angular momentum, mass and centre of
+ * mass of the state (pos, vel), written to *out.
+ *   pos, vel : as for nbody_step (read only).
+ *   pot      : the N potentials of pos as nbody_accel returns them (self term
+ *              included), or NULL to have them evaluated here with the
+ *              automatic plan (one more evaluation, into library scratch).
+ *   eps2     : the softening squared the potentials belong to.
+ *   out      : DEVICE pointer to one nbody_diag (8-byte aligned), written
+ *              asynchronously on `stream`; it must not overlap the inputs.
+ * The sums run in fp64 in an order fixed by N alone, so repeated calls on the
+ * same state give identical bits. Not part of the pages' method: the textbook
+ * definitions built on the potential it returns. N = 0 writes zeros.
+ */
+int nbody_diagnostics(const nbody_f4 *pos, const nbody_f4 *vel, const float *pot, int64_t N,
+                      float eps2, nbody_diag *out, hipStream_t stream);
+
 /*
  * nbody_plan_for - the automatic plan for N bodies on the current device
  * (want_pot is accepted for symmetry; the plan does not depend on it). Fills

@@ -96,6 +96,24 @@ def test_step_rejects(nb, args, code):
     assert nb.nbody_step(*args, stream=0, check=False) == code
 
 
+C = 1 << 29
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=-1), 1), (dict(out=None), 1), (dict(pos=None), 1), (dict(vel=None), 1),
+    (dict(eps2=0.0), 1), (dict(eps2=math.nan), 1), (dict(out=C + 4), 2), (dict(pos=A + 8), 2),
+    (dict(vel=B + 4), 2), (dict(pot=C + 4096 + 2), 2), (dict(out=A + 32), 1),
+    (dict(out=B + 16), 1), (dict(pot=C + 4096, out=C + 4096 + 8), 1),
+])
+def test_diagnostics_rejects(nb, kw, code):
+    args = dict(pos=A, vel=B, n=16, eps2=1e-4, out=C, pot=None)
+    args.update(kw)
+    rc = nb.nbody_diagnostics(args["pos"], args["vel"], args["n"], args["eps2"], args["out"],
+                              pot=args["pot"], stream=0, check=False)
+    assert rc == code, kw
+    assert nb.nbody_last_error() != ""
+
+
 def test_plan_rejects_bad_fields(nb):
     for plan in (dict(bcast=7), dict(tpl=3), dict(splits=-1), dict(splits=5000), dict(mode=4),
                  dict(mode=3, tpl=2), dict(mode=3, tpl=64), dict(mode=3, splits=2),

@@ -280,6 +280,81 @@ def test_auto_plan_modes(nb):
     assert p.mode == nb.MODE_PAIRS and p.band == 1024 and p.splits == 293
 
 
+# ------------------------------------------------------------------ diagnostics
+
+def _diag_close(got, want, pos, vel, pot_scale, what):
+    """Component-wise: energies and mass to 1e-12 of their absolute sums, vectors to 1e-12 of
+    sum m |v| (|x| + 1) (the reductions run in fp64 over fp32 inputs; only order differs)."""
+    m = pos[:, 3].astype(np.float64)
+    v = np.linalg.norm(vel[:, :3].astype(np.float64), axis=1)
+    x = np.linalg.norm(pos[:, :3].astype(np.float64), axis=1)
+    sk = float(np.sum(0.5 * m * v * v)) + 1e-300
+    sv = float(np.sum(m * v * (x + 1.0))) + 1e-300
+    sm = float(np.sum(m)) + 1e-300
+    assert abs(got["kinetic"] - want["kinetic"]) <= 1e-12 * sk, what
+    assert abs(got["potential"] - want["potential"]) <= pot_scale, what
+    assert abs(got["total"] - got["kinetic"] - got["potential"]) <= 1e-15 * (sk + pot_scale), what
+    assert np.all(np.abs(np.subtract(got["momentum"], want["momentum"])) <= 1e-12 * sv), what
+    assert np.all(np.abs(np.subtract(got["angular_momentum"],
+                                     want["angular_momentum"])) <= 1e-12 * sv), what
+    assert abs(got["mass"] - want["mass"]) <= 1e-12 * sm, what
+    xm = float(np.sum(m * x)) / sm + 1.0
+    assert np.all(np.abs(np.subtract(got["centre_of_mass"],
+                                     want["centre_of_mass"])) <= 1e-12 * xm), what
+
+
+@pytest.mark.parametrize("n", [1, 100, 1000, 70001, 300007])
+def test_diagnostics_reduction(nb, n):
+    """With the GPU's own potentials as input, the fp64 reductions equal the oracle's sums of
+    the same per-body terms (order aside); repeated calls give identical bits."""
+    import oracle
+    import torch
+
+    pos, vel = _bodies(n, 700 + n)
+    pd, vd = to_dev(pos), to_dev(vel)
+    _, pot = nb.accel(pd, 1e-4, pot=True)
+    got = nb.diagnostics(pd, vd, 1e-4, pot=pot)
+    again = nb.diagnostics(pd, vd, 1e-4, pot=pot)
+    assert got == again
+    pot_h = pot.cpu().numpy()
+    want = oracle.diagnostics(pos, vel, 1e-4, pot=pot_h)
+    scale = 1e-12 * float(np.sum(0.5 * pos[:, 3] * (np.abs(pot_h) + pos[:, 3] / 1e-2)))
+    _diag_close(got, want, pos, vel, scale, f"N={n}")
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name", ["disk4096", "plummer65536", "cube2048_steps"])
+def test_diagnostics_own_potential(nb, name):
+    """With pot = NULL the library evaluates the potential itself (automatic plan): W within
+    the potential bound of the exact pair energy, everything else as the oracle's sums."""
+    import oracle
+
+    w = workloads.make(name)
+    got = nb.diagnostics(to_dev(w.pos), to_dev(w.vel), float(w.eps2))
+    want = oracle.diagnostics(w.pos, w.vel, w.eps2)
+    ref = oracle.accel(w.pos, w.eps2)
+    bound = 0.5 * float(np.sum(w.pos[:, 3].astype(np.float64) * TOL * ref["bound_p"]))
+    _diag_close(got, want, w.pos, w.vel, bound, name)
+    print(f"{name}: K {got['kinetic']:.6e} W {got['potential']:.6e} "
+          f"|dW| {abs(got['potential'] - want['potential']):.2e} (bound {bound:.2e})")
+
+
+def test_diagnostics_empty_and_single(nb):
+    import torch
+
+    out = torch.full((13,), 7.0, dtype=torch.float64, device="cuda")
+    nb.nbody_diagnostics(None, None, 0, 1e-4, out)
+    torch.cuda.synchronize()
+    assert np.all(out.cpu().numpy() == 0.0)
+    pos = np.array([[0.5, -1.0, 2.0, 3.0]], dtype=np.float32)
+    vel = np.array([[1.0, 2.0, -2.0, 0.0]], dtype=np.float32)
+    d = nb.diagnostics(to_dev(pos), to_dev(vel), 0.25)
+    assert d["kinetic"] == 0.5 * 3.0 * 9.0 and d["potential"] == 0.0 and d["mass"] == 3.0
+    assert d["momentum"] == [3.0, 6.0, -6.0] and d["centre_of_mass"] == [0.5, -1.0, 2.0]
+    # x cross v = (-1*-2 - 2*2, 2*1 - 0.5*-2, 0.5*2 - -1*1) = (-2, 3, 2)
+    assert d["angular_momentum"] == [-6.0, 9.0, 6.0]
+
+
 # ------------------------------------------------------------------ the five workloads
 
 def test_disk4096_accel_and_step(nb):
@@ -351,8 +426,12 @@ def test_cube2048_steps_shadow_and_bit_exact(nb):
     e1 = oracle.energy(p_many, v_many, w.eps2)[0]
     rp, rv = oracle.euler(w.pos, w.vel, w.dt, w.eps2, w.nsteps)
     e1_ref = oracle.energy(rp, rv, w.eps2, )[0]
-    print(f"cube2048: energy drift GPU {(e1 - e0) / abs(e0):+.3e}, "
-          f"fp64 trajectory {(e1_ref - e0) / abs(e0):+.3e}")
+    # the same drift measured on the GPU (nbody_diagnostics evaluating its own potential)
+    g0 = nb.diagnostics(to_dev(w.pos), to_dev(w.vel), float(w.eps2))["total"]
+    g1 = nb.diagnostics(to_dev(p_many), to_dev(v_many), float(w.eps2))["total"]
+    print(f"cube2048: energy drift GPU {(e1 - e0) / abs(e0):+.3e} (on the GPU: "
+          f"{(g1 - g0) / abs(g0):+.3e}), fp64 trajectory {(e1_ref - e0) / abs(e0):+.3e}")
+    assert abs((g1 - g0) - (e1 - e0)) <= 1e-4 * abs(e0)
     # multi-step trajectories have no pinned bound (the system is chaotic); report the
     # distance to the independent fp64 trajectory and only reject a gross departure
     dmax = float(np.max(np.abs(p_many[:, :3] - rp[:, :3])))
