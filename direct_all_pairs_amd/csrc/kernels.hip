@@ -60,16 +60,59 @@ __device__ __forceinline__ void zero(Sums<T, POT> &s)
     }
 }
 
+// Running totals of the block sums, compensated: each addition is an exact
+// TwoSum (Knuth: the rounded sum plus its exact rounding error), the errors go
+// into a second sum e, and the total is s + e. The error of the totals then
+// stays at the level of one block sum however many blocks a chunk holds (plain
+// fp32 totals grow with the block count: measured err/B 1.6e-7 at N = 2^20 and
+// 6.3e-7 at 2^22 with one chunk per 2^20 sources). Adding an exact zero leaves
+// (s, e) unchanged, so zero-mass padding stays bit-neutral.
 template <int T, bool POT>
-__device__ __forceinline__ void add_into(Sums<T, POT> &tot, const Sums<T, POT> &blk)
+struct Total {
+    Sums<T, POT> s, e;
+};
+
+template <int T, bool POT>
+__device__ __forceinline__ void zero(Total<T, POT> &tot)
+{
+    zero(tot.s);
+    zero(tot.e);
+}
+
+__device__ __forceinline__ void two_sum_add(float &s, float &e, float x)
+{
+    const float t = s + x;
+    const float xv = t - s;                  // the part of x that reached t
+    const float err = (s - (t - xv)) + (x - xv);
+    s = t;
+    e += err;
+}
+
+template <int T, bool POT>
+__device__ __forceinline__ void add_into(Total<T, POT> &tot, const Sums<T, POT> &blk)
 {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-        tot.ax[t] += blk.ax[t];
-        tot.ay[t] += blk.ay[t];
-        tot.az[t] += blk.az[t];
-        if constexpr (POT) tot.p[t] += blk.p[t];
+        two_sum_add(tot.s.ax[t], tot.e.ax[t], blk.ax[t]);
+        two_sum_add(tot.s.ay[t], tot.e.ay[t], blk.ay[t]);
+        two_sum_add(tot.s.az[t], tot.e.az[t], blk.az[t]);
+        if constexpr (POT) two_sum_add(tot.s.p[t], tot.e.p[t], blk.p[t]);
     }
+}
+
+// s + e of a compensated total.
+template <int T, bool POT>
+__device__ __forceinline__ Sums<T, POT> result(const Total<T, POT> &tot)
+{
+    Sums<T, POT> r;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        r.ax[t] = tot.s.ax[t] + tot.e.ax[t];
+        r.ay[t] = tot.s.ay[t] + tot.e.ay[t];
+        r.az[t] = tot.s.az[t] + tot.e.az[t];
+        r.p[t] = POT ? tot.s.p[t] + tot.e.p[t] : 0.0f;
+    }
+    return r;
 }
 
 // One source (sx, sy, sz, sm) against the lane's T targets. The operation
@@ -189,7 +232,8 @@ __global__ void __launch_bounds__(kWG) accel_scalar(AccelArgs k)
     const float4 *__restrict__ src = k.pos;
     const float eps2 = k.eps2;
 
-    Sums<T, POT> tot, blk;
+    Total<T, POT> tot;
+    Sums<T, POT> blk;
     zero(tot);
     zero(blk);
 
@@ -232,35 +276,34 @@ __global__ void __launch_bounds__(kWG) accel_scalar(AccelArgs k)
     }
     for (; j < j1; ++j) interact4<T, POT>(src[j], tg, eps2, blk);
     add_into(tot, blk);
-    store(tot, k, base);
+    store(result(tot), k, base);
 }
 
-// Partial sums are added in ascending chunk order s = 0, 1, ..., S-1, loading
-// eight slots ahead of the additions (the order of the additions is fixed).
+// Partial sums are added in ascending chunk order s = 0, 1, ..., S-1, each
+// addition a TwoSum whose error goes into a second sum (hundreds of slots in
+// pair mode), loading eight slots ahead of the in-order additions.
+__device__ __forceinline__ void two_sum_add4(float4 &a, float4 &e, const float4 &b)
+{
+    two_sum_add(a.x, e.x, b.x);
+    two_sum_add(a.y, e.y, b.y);
+    two_sum_add(a.z, e.z, b.z);
+    two_sum_add(a.w, e.w, b.w);
+}
+
 __device__ __forceinline__ float4 sum_parts(const float4 *part, int n, int splits, unsigned i)
 {
     float4 a = part[i];
+    float4 e = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     int s = 1;
     for (; s + 8 <= splits; s += 8) {
         float4 b[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) b[u] = part[(size_t)(s + u) * (size_t)n + i];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            a.x += b[u].x;
-            a.y += b[u].y;
-            a.z += b[u].z;
-            a.w += b[u].w;
-        }
+        for (int u = 0; u < 8; ++u) two_sum_add4(a, e, b[u]);
     }
-    for (; s < splits; ++s) {
-        const float4 b = part[(size_t)s * (size_t)n + i];
-        a.x += b.x;
-        a.y += b.y;
-        a.z += b.z;
-        a.w += b.w;
-    }
-    return a;
+    for (; s < splits; ++s) two_sum_add4(a, e, part[(size_t)s * (size_t)n + i]);
+    return make_float4(a.x + e.x, a.y + e.y, a.z + e.z, a.w + e.w);
 }
 
 // Explicit Euler, position first with the old velocity (Degawa, "N 体問題",
@@ -299,7 +342,8 @@ __global__ void __launch_bounds__(WG) accel_lds(AccelArgs k)
     const Targets<T> tg = load_targets<T, WG>(k.pos, k.n, base);
     const float eps2 = in_vgpr(k.eps2);
 
-    Sums<T, POT> tot, blk;
+    Total<T, POT> tot;
+    Sums<T, POT> blk;
     zero(tot);
     zero(blk);
 
@@ -346,7 +390,7 @@ __global__ void __launch_bounds__(WG) accel_lds(AccelArgs k)
         }
         __syncthreads();
     }
-    store<T, POT, WG>(tot, k, base);
+    store<T, POT, WG>(result(tot), k, base);
 }
 
 // ---------------------------------------------------------------- SMALL
@@ -376,7 +420,8 @@ __global__ void __launch_bounds__(256) accel_small(SmallArgs k)
     tg.y[0] = me.y;
     tg.z[0] = me.z;
     const float eps2 = in_vgpr(k.eps2);
-    Sums<1, POT> tot, blk;
+    Total<1, POT> tot;
+    Sums<1, POT> blk;
     zero(tot);
 
     const int ntiles = (k.n + TS - 1) / TS;
@@ -408,7 +453,8 @@ __global__ void __launch_bounds__(256) accel_small(SmallArgs k)
         }
         __syncthreads();
     }
-    red[g][t] = make_float4(tot.ax[0], tot.ay[0], tot.az[0], POT ? tot.p[0] : 0.0f);
+    const Sums<1, POT> r = result(tot);
+    red[g][t] = make_float4(r.ax[0], r.ay[0], r.az[0], POT ? r.p[0] : 0.0f);
     __syncthreads();
     if (g != 0 || i >= k.n) return;
     float4 a = red[0][t];
@@ -446,7 +492,8 @@ __global__ void __launch_bounds__(kWG) accel_readlane(AccelArgs k)
     const float eps2 = k.eps2;
     const int lane = threadIdx.x & 63;
 
-    Sums<T, POT> tot, blk;
+    Total<T, POT> tot;
+    Sums<T, POT> blk;
     zero(tot);
     zero(blk);
 
@@ -474,7 +521,7 @@ __global__ void __launch_bounds__(kWG) accel_readlane(AccelArgs k)
         mine = nxt;
     }
     add_into(tot, blk);
-    store(tot, k, base);
+    store(result(tot), k, base);
 }
 
 // ---------------------------------------------------------------- PAIRS

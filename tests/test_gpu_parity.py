@@ -280,6 +280,26 @@ def test_auto_plan_modes(nb):
     assert p.mode == nb.MODE_PAIRS and p.band == 1024 and p.splits == 293
 
 
+# ------------------------------------------------------------------ long sums
+
+def test_long_chunk_compensated(nb):
+    """N = 2^22 in one split-j chunk: 16,384 blocks of 256 sources add into each target's
+    running totals. With plain fp32 totals the error grows with the block count (at one
+    chunk per 2^20 sources err/B reached 6.3e-7 and pot err/P 1.3e-6 at this N); the Kahan-
+    compensated totals keep it at the level of one block sum."""
+    import oracle
+
+    n = 1 << 22
+    w = workloads.make("cube1m", n=n)
+    acc, pot = gpu_accel(w.pos, w.eps2, pot=True,
+                         plan=dict(mode="tiles", bcast="lds", tpl=1, wg=512, splits=1))
+    idx = np.unique(np.random.default_rng(3).integers(0, n, 256))
+    ref = oracle.accel(w.pos, w.eps2, targets=idx)
+    ea, ep = assert_accel_parity(acc, pot, ref, idx=idx, what="N=2^22 one chunk")
+    print(f"N=2^22 one chunk: max err/B {ea:.3e}, pot err/P {ep:.3e}")
+    assert ea <= 3e-7 and ep <= 5e-7
+
+
 # ------------------------------------------------------------------ diagnostics
 
 def _diag_close(got, want, pos, vel, pot_scale, what):
