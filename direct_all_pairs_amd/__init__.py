@@ -63,15 +63,19 @@ _lib.nbody_step_plan.argtypes = [_vp, _vp, _i64, _f32, _f32, _i64, ctypes.POINTE
                                  _vp]
 _lib.nbody_plan_for.argtypes = [_i64, _int, ctypes.POINTER(nbody_plan)]
 _lib.nbody_diagnostics.argtypes = [_vp, _vp, _vp, _i64, _f32, _vp, _vp]
+_lib.nbody_accel_soa.argtypes = [_vp, _vp, _vp, _vp, _i64, _f32, _vp, _vp, _vp, _vp, _vp]
+_lib.nbody_step_soa.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _f32, _f32, _i64, _vp]
 _lib.nbody_last_error.restype = ctypes.c_char_p
 _lib.nbody_release_workspace.argtypes = []
 _lib.nbody_version.restype = ctypes.c_char_p
 for _f in ("nbody_accel", "nbody_accel_plan", "nbody_step", "nbody_step_plan",
-           "nbody_diagnostics", "nbody_plan_for", "nbody_release_workspace"):
+           "nbody_accel_soa", "nbody_step_soa", "nbody_diagnostics", "nbody_plan_for",
+           "nbody_release_workspace"):
     getattr(_lib, _f).restype = _int
 
-EXPORTS = ("nbody_accel", "nbody_accel_plan", "nbody_step", "nbody_step_plan", "nbody_diagnostics",
-           "nbody_plan_for", "nbody_last_error", "nbody_release_workspace", "nbody_version")
+EXPORTS = ("nbody_accel", "nbody_accel_plan", "nbody_step", "nbody_step_plan", "nbody_accel_soa",
+           "nbody_step_soa", "nbody_diagnostics", "nbody_plan_for", "nbody_last_error",
+           "nbody_release_workspace", "nbody_version")
 DIAG_FIELDS = ("kinetic", "potential", "total", "momentum", "angular_momentum", "mass",
                "centre_of_mass")
 
@@ -145,6 +149,20 @@ def nbody_step_plan(pos, vel, N: int, dt: float, eps2: float, nsteps: int, plan=
     rc = _lib.nbody_step_plan(_ptr(pos), _ptr(vel), int(N), float(dt), float(eps2), int(nsteps),
                               ctypes.byref(p) if p is not None else None, _stream(stream))
     return _check(rc, "nbody_step_plan") if check else rc
+
+
+def nbody_accel_soa(x, y, z, m, N: int, eps2: float, ax, ay, az, pot_out=None, stream=None,
+                    check: bool = True) -> int:
+    rc = _lib.nbody_accel_soa(_ptr(x), _ptr(y), _ptr(z), _ptr(m), int(N), float(eps2), _ptr(ax),
+                              _ptr(ay), _ptr(az), _ptr(pot_out), _stream(stream))
+    return _check(rc, "nbody_accel_soa") if check else rc
+
+
+def nbody_step_soa(x, y, z, m, vx, vy, vz, N: int, dt: float, eps2: float, nsteps: int,
+                   stream=None, check: bool = True) -> int:
+    rc = _lib.nbody_step_soa(_ptr(x), _ptr(y), _ptr(z), _ptr(m), _ptr(vx), _ptr(vy), _ptr(vz),
+                             int(N), float(dt), float(eps2), int(nsteps), _stream(stream))
+    return _check(rc, "nbody_step_soa") if check else rc
 
 
 def nbody_diagnostics(pos, vel, N: int, eps2: float, out, pot=None, stream=None,

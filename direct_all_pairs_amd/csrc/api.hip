@@ -369,6 +369,49 @@ int accel_impl(const nbody_f4 *pos, int64_t N, float eps2, nbody_f4 *acc, float 
     return rc == NBODY_OK ? ok() : rc;
 }
 
+// Scratch bytes an evaluation (or, with step, a step loop) of plan p uses from
+// the start of the (device, stream) block.
+size_t eval_scratch(int64_t n, const nbody_plan &p, bool step)
+{
+    if (p.mode == NBODY_MODE_SMALL) return step ? (size_t)n * sizeof(float4) : 0;
+    if (p.splits > 1 || step || p.mode == NBODY_MODE_PAIRS)
+        return (size_t)p.splits * (size_t)n * sizeof(float4);
+    return 0;
+}
+
+// nsteps Euler steps of (pos, vel) in place with plan p.
+int enqueue_steps(float4 *pos, float4 *vel, int n, float dt, float eps2, int64_t nsteps,
+                  const nbody_plan &p, int dev, hipStream_t stream)
+{
+    if (p.mode != NBODY_MODE_SMALL) {
+        for (int64_t s = 0; s < nsteps; ++s) {
+            int rc = enqueue_eval(pos, n, eps2, nullptr, nullptr, p, dev, stream, pos, vel, dt);
+            if (rc != NBODY_OK) return rc;
+        }
+        return NBODY_OK;
+    }
+    // One kernel per step reads every position while it writes new ones, so the
+    // steps alternate between the caller's array and a scratch copy; after an
+    // odd step count the final positions are copied back on the stream.
+    const size_t b16 = (size_t)n * sizeof(float4);
+    void *ws = nullptr;
+    int rc = scratch_get(dev, stream, b16, &ws);
+    if (rc != NBODY_OK) return rc;
+    float4 *other = (float4 *)ws;
+    for (int64_t s = 0; s < nsteps; ++s) {
+        float4 *src = (s % 2 == 0) ? pos : other;
+        float4 *dst = (s % 2 == 0) ? other : pos;
+        nbk::SmallArgs sa{src, n, eps2, nullptr, nullptr, dst, vel, dt};
+        hipError_t e = nbk::launch_small(p.tpl, false, true, sa, stream);
+        if (e != hipSuccess) return hip_fail(e, "small kernel launch");
+    }
+    if (nsteps % 2 == 1) {
+        hipError_t e = hipMemcpyAsync(pos, other, b16, hipMemcpyDeviceToDevice, stream);
+        if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(positions)");
+    }
+    return NBODY_OK;
+}
+
 int step_impl(nbody_f4 *pos, nbody_f4 *vel, int64_t N, float dt, float eps2, int64_t nsteps,
               const nbody_plan *plan, hipStream_t stream)
 {
@@ -389,32 +432,104 @@ int step_impl(nbody_f4 *pos, nbody_f4 *vel, int64_t N, float dt, float eps2, int
     int dev = 0;
     rc = make_plan(N, plan, &dev, &p);
     if (rc != NBODY_OK) return rc;
-    if (p.mode != NBODY_MODE_SMALL) {
-        for (int64_t s = 0; s < nsteps; ++s) {
-            rc = enqueue_eval((const float4 *)pos, (int)N, eps2, nullptr, nullptr, p, dev, stream,
-                              (float4 *)pos, (float4 *)vel, dt);
-            if (rc != NBODY_OK) return rc;
-        }
-        return ok();
-    }
-    // One kernel per step reads every position while it writes new ones, so the
-    // steps alternate between the caller's array and a scratch copy; after an
-    // odd step count the final positions are copied back on the stream.
-    void *ws = nullptr;
-    rc = scratch_get(dev, stream, b16, &ws);
+    rc = enqueue_steps((float4 *)pos, (float4 *)vel, (int)N, dt, eps2, nsteps, p, dev, stream);
+    return rc == NBODY_OK ? ok() : rc;
+}
+
+// ------------------------------------------------------------ SoA entry points
+
+bool disjoint(const void *const *p, const size_t *bytes, int k)
+{
+    for (int i = 0; i < k; ++i)
+        for (int j = i + 1; j < k; ++j)
+            if (p[i] && p[j] && overlap(p[i], bytes[i], p[j], bytes[j])) return false;
+    return true;
+}
+
+size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+int accel_soa_impl(const float *x, const float *y, const float *z, const float *m, int64_t N,
+                   float eps2, float *ax, float *ay, float *az, float *pot, hipStream_t stream)
+{
+    int rc = check_n(N);
     if (rc != NBODY_OK) return rc;
-    float4 *x = (float4 *)pos, *other = (float4 *)ws;
-    for (int64_t s = 0; s < nsteps; ++s) {
-        float4 *src = (s % 2 == 0) ? x : other;
-        float4 *dst = (s % 2 == 0) ? other : x;
-        nbk::SmallArgs sa{src, (int)N, eps2, nullptr, nullptr, dst, (float4 *)vel, dt};
-        hipError_t e = nbk::launch_small(p.tpl, false, true, sa, stream);
-        if (e != hipSuccess) return hip_fail(e, "small kernel launch");
+    if (N == 0) return ok();
+    const float *in[4] = {x, y, z, m};
+    float *out[3] = {ax, ay, az};
+    const char *in_name[4] = {"x", "y", "z", "m"}, *out_name[3] = {"ax", "ay", "az"};
+    for (int i = 0; i < 4; ++i) {
+        if (!in[i]) return fail(NBODY_EINVAL, "%s is NULL", in_name[i]);
+        if (!aligned(in[i], 4)) return fail(NBODY_EALIGN, "%s is not 4-byte aligned", in_name[i]);
     }
-    if (nsteps % 2 == 1) {
-        hipError_t e = hipMemcpyAsync(x, other, b16, hipMemcpyDeviceToDevice, stream);
-        if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(positions)");
+    for (int i = 0; i < 3; ++i) {
+        if (!out[i]) return fail(NBODY_EINVAL, "%s is NULL", out_name[i]);
+        if (!aligned(out[i], 4)) return fail(NBODY_EALIGN, "%s is not 4-byte aligned", out_name[i]);
     }
+    if (pot && !aligned(pot, 4)) return fail(NBODY_EALIGN, "pot is not 4-byte aligned");
+    if (!eps2_ok(eps2))
+        return fail(NBODY_EINVAL, "eps2=%g must be a positive, finite, normal float", (double)eps2);
+    const size_t b4 = (size_t)N * 4;
+    const void *all[8] = {ax, ay, az, pot, x, y, z, m};
+    const size_t sz[8] = {b4, b4, b4, b4, b4, b4, b4, b4};
+    // outputs must not overlap each other or the inputs (inputs may share storage)
+    for (int o = 0; o < 4; ++o)
+        for (int j = 0; j < 8; ++j)
+            if (j != o && all[o] && all[j] && overlap(all[o], sz[o], all[j], sz[j]))
+                return fail(NBODY_EINVAL, "an output array overlaps another array");
+    nbody_plan p;
+    int dev = 0;
+    rc = make_plan(N, nullptr, &dev, &p);
+    if (rc != NBODY_OK) return rc;
+    const size_t b16 = (size_t)N * 16, base = align256(eval_scratch(N, p, false));
+    void *ws = nullptr;
+    rc = scratch_get(dev, stream, base + 2 * b16, &ws);
+    if (rc != NBODY_OK) return rc;
+    float4 *pos4 = (float4 *)((char *)ws + base), *acc4 = pos4 + N;
+    hipError_t e = nbk::launch_pack(x, y, z, m, (int)N, pos4, stream);
+    if (e != hipSuccess) return hip_fail(e, "pack kernel launch");
+    rc = enqueue_eval(pos4, (int)N, eps2, acc4, pot, p, dev, stream, nullptr, nullptr, 0.0f);
+    if (rc != NBODY_OK) return rc;
+    e = nbk::launch_unpack(acc4, (int)N, ax, ay, az, stream);
+    if (e != hipSuccess) return hip_fail(e, "unpack kernel launch");
+    return ok();
+}
+
+int step_soa_impl(float *x, float *y, float *z, const float *m, float *vx, float *vy, float *vz,
+                  int64_t N, float dt, float eps2, int64_t nsteps, hipStream_t stream)
+{
+    int rc = check_n(N);
+    if (rc != NBODY_OK) return rc;
+    if (nsteps < 0) return fail(NBODY_EINVAL, "nsteps=%lld must be >= 0", (long long)nsteps);
+    if (N == 0 || nsteps == 0) return ok();
+    const void *arr[7] = {x, y, z, m, vx, vy, vz};
+    const char *name[7] = {"x", "y", "z", "m", "vx", "vy", "vz"};
+    for (int i = 0; i < 7; ++i) {
+        if (!arr[i]) return fail(NBODY_EINVAL, "%s is NULL", name[i]);
+        if (!aligned(arr[i], 4)) return fail(NBODY_EALIGN, "%s is not 4-byte aligned", name[i]);
+    }
+    if (!std::isfinite(dt)) return fail(NBODY_EINVAL, "dt=%g must be finite", (double)dt);
+    if (!eps2_ok(eps2))
+        return fail(NBODY_EINVAL, "eps2=%g must be a positive, finite, normal float", (double)eps2);
+    const size_t b4 = (size_t)N * 4;
+    const size_t sz[7] = {b4, b4, b4, b4, b4, b4, b4};
+    if (!disjoint(arr, sz, 7)) return fail(NBODY_EINVAL, "the seven arrays must not overlap");
+    nbody_plan p;
+    int dev = 0;
+    rc = make_plan(N, nullptr, &dev, &p);
+    if (rc != NBODY_OK) return rc;
+    const size_t b16 = (size_t)N * 16, base = align256(eval_scratch(N, p, true));
+    void *ws = nullptr;
+    rc = scratch_get(dev, stream, base + 2 * b16, &ws);
+    if (rc != NBODY_OK) return rc;
+    float4 *pos4 = (float4 *)((char *)ws + base), *vel4 = pos4 + N;
+    hipError_t e = nbk::launch_pack(x, y, z, m, (int)N, pos4, stream);
+    if (e == hipSuccess) e = nbk::launch_pack(vx, vy, vz, nullptr, (int)N, vel4, stream);
+    if (e != hipSuccess) return hip_fail(e, "pack kernel launch");
+    rc = enqueue_steps(pos4, vel4, (int)N, dt, eps2, nsteps, p, dev, stream);
+    if (rc != NBODY_OK) return rc;
+    e = nbk::launch_unpack(pos4, (int)N, x, y, z, stream);
+    if (e == hipSuccess) e = nbk::launch_unpack(vel4, (int)N, vx, vy, vz, stream);
+    if (e != hipSuccess) return hip_fail(e, "unpack kernel launch");
     return ok();
 }
 
@@ -446,6 +561,19 @@ int nbody_step_plan(nbody_f4 *pos, nbody_f4 *vel, int64_t N, float dt, float eps
     return step_impl(pos, vel, N, dt, eps2, nsteps, plan, stream);
 }
 
+int nbody_accel_soa(const float *x, const float *y, const float *z, const float *m, int64_t N,
+                    float eps2, float *ax, float *ay, float *az, float *pot_out,
+                    hipStream_t stream)
+{
+    return accel_soa_impl(x, y, z, m, N, eps2, ax, ay, az, pot_out, stream);
+}
+
+int nbody_step_soa(float *x, float *y, float *z, const float *m, float *vx, float *vy, float *vz,
+                   int64_t N, float dt, float eps2, int64_t nsteps, hipStream_t stream)
+{
+    return step_soa_impl(x, y, z, m, vx, vy, vz, N, dt, eps2, nsteps, stream);
+}
+
 int nbody_diagnostics(const nbody_f4 *pos, const nbody_f4 *vel, const float *pot, int64_t N,
                       float eps2, nbody_diag *out, hipStream_t stream)
 {
@@ -474,8 +602,7 @@ int nbody_diagnostics(const nbody_f4 *pos, const nbody_f4 *vel, const float *pot
     if (!pot && N > 0) {
         rc = make_plan(N, nullptr, &dev, &p);
         if (rc != NBODY_OK) return rc;
-        if (p.mode == NBODY_MODE_PAIRS || p.splits > 1)
-            part_bytes = (size_t)p.splits * (size_t)N * sizeof(float4);
+        part_bytes = align256(eval_scratch(N, p, false));
     }
     const size_t eval_bytes = (!pot && N > 0) ? b16 + b4 : 0;
     const int nb = nbk::diag_blocks((int)N);

@@ -65,6 +65,12 @@ int diag_blocks(int n);
 hipError_t launch_diagnostics(const float4 *pos, const float4 *vel, const float *pot, int n,
                               double inv_eps, double *part, double *out, hipStream_t stream);
 
+// Layout conversion for the SoA entry points: out[i] = (a[i], b[i], c[i], d ? d[i] : 0),
+// and back: a[i], b[i], c[i] = in[i].x, .y, .z.
+hipError_t launch_pack(const float *a, const float *b, const float *c, const float *d, int n,
+                       float4 *out, hipStream_t stream);
+hipError_t launch_unpack(const float4 *in, int n, float *a, float *b, float *c, hipStream_t stream);
+
 // acc_out[i] = (sum_s part[s][i].xyz, 0); pot_out[i] = -sum_s part[s][i].w (if non-null).
 hipError_t launch_combine(const float4 *part, int n, int splits, float4 *acc_out, float *pot_out,
                           hipStream_t stream);

@@ -896,6 +896,33 @@ __global__ void __launch_bounds__(256) diag_final_kernel(const double *__restric
     out[9] = m;
 }
 
+// ---------------------------------------------------------------- SoA layout
+// Separate x, y, z, m arrays (the host layout of the lecture's CPU program,
+// Degawa slide 15) in and out of the 16-byte records the kernels read.
+__global__ void __launch_bounds__(256) pack_kernel(const float *__restrict__ a,
+                                                   const float *__restrict__ b,
+                                                   const float *__restrict__ c,
+                                                   const float *__restrict__ d, int n,
+                                                   float4 *__restrict__ out)
+{
+    const unsigned i = blockIdx.x * 256u + threadIdx.x;
+    if (i >= (unsigned)n) return;
+    out[i] = make_float4(a[i], b[i], c[i], d ? d[i] : 0.0f);
+}
+
+__global__ void __launch_bounds__(256) unpack_kernel(const float4 *__restrict__ in, int n,
+                                                     float *__restrict__ a,
+                                                     float *__restrict__ b,
+                                                     float *__restrict__ c)
+{
+    const unsigned i = blockIdx.x * 256u + threadIdx.x;
+    if (i >= (unsigned)n) return;
+    const float4 v = in[i];
+    a[i] = v.x;
+    b[i] = v.y;
+    c[i] = v.z;
+}
+
 template <int T, bool POT>
 const void *accel_fn(int bcast, int wg)
 {
@@ -980,6 +1007,23 @@ hipError_t launch_small(int tw, bool pot, bool step, const SmallArgs &args, hipS
     SmallArgs a = args;
     void *kargs[] = {&a};
     return hipLaunchKernel(fn, dim3((unsigned)((a.n + tw - 1) / tw)), dim3(256), kargs, 0, stream);
+}
+
+hipError_t launch_pack(const float *a, const float *b, const float *c, const float *d, int n,
+                       float4 *out, hipStream_t stream)
+{
+    if (n <= 0) return n == 0 ? hipSuccess : hipErrorInvalidValue;
+    void *k[] = {&a, &b, &c, &d, &n, &out};
+    return hipLaunchKernel((const void *)&pack_kernel, dim3((unsigned)((n + 255) / 256)),
+                           dim3(256), k, 0, stream);
+}
+
+hipError_t launch_unpack(const float4 *in, int n, float *a, float *b, float *c, hipStream_t stream)
+{
+    if (n <= 0) return n == 0 ? hipSuccess : hipErrorInvalidValue;
+    void *k[] = {&in, &n, &a, &b, &c};
+    return hipLaunchKernel((const void *)&unpack_kernel, dim3((unsigned)((n + 255) / 256)),
+                           dim3(256), k, 0, stream);
 }
 
 int diag_blocks(int n)

@@ -159,6 +159,28 @@ int nbody_step(nbody_f4 *pos, nbody_f4 *vel, int64_t N, float dt, float eps2, in
 int nbody_step_plan(nbody_f4 *pos, nbody_f4 *vel, int64_t N, float dt, float eps2,
                     int64_t nsteps, const nbody_plan *plan, hipStream_t stream);
 
+/*
+ * nbody_accel_soa - nbody_accel for bodies held as separate arrays (the host
+ * layout of the lecture's CPU program): x, y, z, m in; ax, ay, az and, if
+ * pot_out is not NULL, the potentials out. All arrays hold N floats (4-byte
+ * aligned, device memory); the outputs must not overlap any other array. The
+ * library packs the inputs into its own 16-byte records, evaluates them with
+ * the automatic plan and unpacks: the results equal nbody_accel's bit for bit
+ * (cost: 2 x N x 16 bytes of scratch and ~N x 48 bytes of extra HBM traffic).
+ */
+int nbody_accel_soa(const float *x, const float *y, const float *z, const float *m, int64_t N,
+                    float eps2, float *ax, float *ay, float *az, float *pot_out,
+                    hipStream_t stream);
+
+/*
+ * nbody_step_soa - nbody_step for separate arrays: x, y, z and vx, vy, vz are
+ * updated in place, m is read only; the seven arrays must not overlap. Packing
+ * and unpacking happen once per call, not per step; results equal nbody_step's
+ * bit for bit.
+ */
+int nbody_step_soa(float *x, float *y, float *z, const float *m, float *vx, float *vy, float *vz,
+                   int64_t N, float dt, float eps2, int64_t nsteps, hipStream_t stream);
+
 /* Conserved-quantity diagnostics of a state (nbody_diagnostics), in fp64. */
 typedef struct nbody_diag {
     double kinetic;             /* K = sum m |v|^2 / 2 */

@@ -114,6 +114,43 @@ def test_diagnostics_rejects(nb, kw, code):
     assert nb.nbody_last_error() != ""
 
 
+@pytest.mark.parametrize("bad,code", [
+    (dict(n=-1), 1), (dict(x=None), 1), (dict(m=None), 1), (dict(az=None), 1),
+    (dict(eps2=0.0), 1), (dict(y=A + 4096 + 2), 2), (dict(ay=C + 8192 + 1), 2),
+    (dict(pot=C + 3), 2), (dict(ax=A), 1), (dict(ay=C), 1), (dict(pot=C + 8192 + 32), 1),
+])
+def test_accel_soa_rejects(nb, bad, code):
+    a = dict(x=A, y=A + 4096, z=A + 8192, m=A + 12288, n=16, eps2=1e-4, ax=C, ay=C + 8192,
+             az=C + 16384, pot=None)
+    a.update(bad)
+    rc = nb.nbody_accel_soa(a["x"], a["y"], a["z"], a["m"], a["n"], a["eps2"], a["ax"], a["ay"],
+                            a["az"], a["pot"], stream=0, check=False)
+    assert rc == code, bad
+    assert nb.nbody_last_error() != ""
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(n=-1), 1), (dict(nsteps=-1), 1), (dict(vz=None), 1), (dict(m=None), 1),
+    (dict(dt=math.inf), 1), (dict(x=A + 1), 2), (dict(vy=B + 4096 + 2), 2),
+    (dict(vx=A), 1), (dict(m=A + 4096 + 32), 1),
+])
+def test_step_soa_rejects(nb, bad, code):
+    a = dict(x=A, y=A + 4096, z=A + 8192, m=A + 12288, vx=B, vy=B + 4096, vz=B + 8192, n=16,
+             dt=1e-3, eps2=1e-4, nsteps=1)
+    a.update(bad)
+    rc = nb.nbody_step_soa(a["x"], a["y"], a["z"], a["m"], a["vx"], a["vy"], a["vz"], a["n"],
+                           a["dt"], a["eps2"], a["nsteps"], stream=0, check=False)
+    assert rc == code, bad
+    assert nb.nbody_last_error() != ""
+
+
+def test_soa_zero_work_is_a_no_op(nb):
+    assert nb.nbody_accel_soa(None, None, None, None, 0, 1e-4, None, None, None, None,
+                              stream=0, check=False) == nb.NBODY_OK
+    assert nb.nbody_step_soa(A, A + 4096, A + 8192, A + 12288, B, B + 4096, B + 8192, 16, 1e-3,
+                             1e-4, 0, stream=0, check=False) == nb.NBODY_OK
+
+
 def test_plan_rejects_bad_fields(nb):
     for plan in (dict(bcast=7), dict(tpl=3), dict(splits=-1), dict(splits=5000), dict(mode=4),
                  dict(mode=3, tpl=2), dict(mode=3, tpl=64), dict(mode=3, splits=2),

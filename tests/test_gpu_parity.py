@@ -280,6 +280,57 @@ def test_auto_plan_modes(nb):
     assert p.mode == nb.MODE_PAIRS and p.band == 1024 and p.splits == 293
 
 
+# ------------------------------------------------------------------ SoA entry points
+
+def _soa(t):
+    return [t[:, c].contiguous() for c in range(4)]
+
+
+@pytest.mark.parametrize("n", [1, 700, 5000, 20011, 40000])
+def test_accel_soa_equals_aos(nb, n):
+    """Separate x, y, z, m arrays give nbody_accel's results bit for bit (small, tiles and
+    pairs sizes), and within the oracle's bound."""
+    import torch
+
+    pos, _ = _bodies(n, 800 + n)
+    pd = to_dev(pos)
+    acc, pot = nb.accel(pd, 1e-4, pot=True)
+    x, y, z, m = _soa(pd)
+    ax, ay, az, p = (torch.empty(n, device="cuda") for _ in range(4))
+    nb.nbody_accel_soa(x, y, z, m, n, 1e-4, ax, ay, az, p)
+    a0 = torch.empty(n, device="cuda")
+    nb.nbody_accel_soa(x, y, z, m, n, 1e-4, a0, ay, az, None)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.stack([ax, ay, az], 1), acc[:, :3]) and torch.equal(p, pot)
+    assert torch.equal(a0, ax)
+    if n <= 5000:
+        got = np.zeros((n, 4), np.float32)
+        got[:, 0], got[:, 1], got[:, 2] = ax.cpu().numpy(), ay.cpu().numpy(), az.cpu().numpy()
+        assert_accel_parity(got, p.cpu().numpy(), oracle_accel_cached(n, 800 + n, np.float32(1e-4)),
+                            what=f"SoA N={n}")
+
+
+@pytest.mark.parametrize("nsteps", [1, 2, 3])
+@pytest.mark.parametrize("n", [700, 20011, 40000])
+def test_step_soa_equals_aos(nb, n, nsteps):
+    """Pack once, nsteps steps, unpack once: bit-identical to nbody_step on records; the
+    mass array is not written."""
+    import torch
+
+    pos, vel = _bodies(n, 900 + n)
+    x1, v1 = gpu_step(pos, vel, 1e-3, 1e-4, nsteps)
+    pd, vd = to_dev(pos), to_dev(vel)
+    x, y, z, m = _soa(pd)
+    vx, vy, vz, _ = _soa(vd)
+    m_before = m.clone()
+    nb.nbody_step_soa(x, y, z, m, vx, vy, vz, n, 1e-3, 1e-4, nsteps)
+    torch.cuda.synchronize()
+    got_x = torch.stack([x, y, z], 1).cpu().numpy()
+    got_v = torch.stack([vx, vy, vz], 1).cpu().numpy()
+    assert np.array_equal(got_x, x1[:, :3]) and np.array_equal(got_v, v1[:, :3])
+    assert torch.equal(m, m_before)
+
+
 # ------------------------------------------------------------------ long sums
 
 def test_long_chunk_compensated(nb):
