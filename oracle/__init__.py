@@ -80,6 +80,16 @@ class Oracle:
         lib.oracle_diagnostics.argtypes = [_c_double_p, _c_double_p, _c_double_p, ctypes.c_int64,
                                            ctypes.c_double, _c_double_p]
         lib.oracle_diagnostics.restype = ctypes.c_int
+        _i32p = ctypes.POINTER(ctypes.c_int32)
+        lib.oracle_p2p.argtypes = [_c_double_p, ctypes.c_int64, ctypes.c_double, _i32p,
+                                   ctypes.c_int32, _i32p, _i32p, _c_double_p, _c_double_p,
+                                   _c_double_p, _c_double_p]
+        lib.oracle_p2p.restype = ctypes.c_int
+        lib.oracle_near_grid.argtypes = [_c_double_p, ctypes.c_int64, ctypes.c_double,
+                                         _c_double_p, ctypes.c_double, _i32p, _c_int64_p,
+                                         ctypes.c_int64, _c_double_p, _c_double_p, _c_double_p,
+                                         _c_double_p]
+        lib.oracle_near_grid.restype = ctypes.c_int
         self._lib = lib
 
     def num_threads(self) -> int:
@@ -163,6 +173,62 @@ class Oracle:
         return self.diagnostics_exact(pos, vel, as_f32(eps2), pot)
 
 
+    def p2p_exact(self, pos, eps2: float, cell_start, list_off, cells) -> dict:
+        """Near field over cell interaction lists (CSR: cell_start[ncell+1], list_off[ncell+1],
+        cells[list_off[-1]]); float64 bodies and eps2 as given. Arrays as in accel_exact."""
+        p = _bodies64(pos)
+        n = p.shape[0]
+        cs = np.ascontiguousarray(cell_start, dtype=np.int32)
+        lo = np.ascontiguousarray(list_off, dtype=np.int32)
+        li = np.ascontiguousarray(cells, dtype=np.int32)
+        if li.size == 0:
+            li = np.zeros(1, np.int32)
+        ncell = cs.shape[0] - 1
+        if lo.shape[0] != ncell + 1:
+            raise ValueError("list_off must have ncell + 1 entries")
+        acc = np.zeros((n, 3))
+        pot = np.zeros(n)
+        ba = np.zeros(n)
+        bp = np.zeros(n)
+        i32 = ctypes.POINTER(ctypes.c_int32)
+        rc = self._lib.oracle_p2p(_ptr(p), n, float(eps2), _ptr(cs, i32), ncell, _ptr(lo, i32),
+                                  _ptr(li, i32), _ptr(acc), _ptr(pot), _ptr(ba), _ptr(bp))
+        if rc != 0:
+            raise ValueError("oracle_p2p rejected its arguments")
+        return {"acc": acc, "pot": pot, "bound_a": ba, "bound_p": bp}
+
+    def p2p(self, pos, eps2, cell_start, list_off, cells) -> dict:
+        return self.p2p_exact(pos, as_f32(eps2), cell_start, list_off, cells)
+
+    def near_grid_exact(self, pos, eps2: float, lo, h: float, dims, targets=None) -> dict:
+        """Near field on a uniform grid by definition (neighbouring cells by coordinates)."""
+        p = _bodies64(pos)
+        n = p.shape[0]
+        lo64 = np.ascontiguousarray(lo, dtype=np.float64)
+        d32 = np.ascontiguousarray(dims, dtype=np.int32)
+        if targets is None:
+            t, nt = None, n
+        else:
+            t = np.ascontiguousarray(targets, dtype=np.int64)
+            nt = t.shape[0]
+        acc = np.zeros((nt, 3))
+        pot = np.zeros(nt)
+        ba = np.zeros(nt)
+        bp = np.zeros(nt)
+        rc = self._lib.oracle_near_grid(_ptr(p), n, float(eps2), _ptr(lo64), float(h),
+                                        _ptr(d32, ctypes.POINTER(ctypes.c_int32)),
+                                        _ptr(t, _c_int64_p), nt, _ptr(acc), _ptr(pot), _ptr(ba),
+                                        _ptr(bp))
+        if rc != 0:
+            raise ValueError("oracle_near_grid rejected its arguments")
+        return {"acc": acc, "pot": pot, "bound_a": ba, "bound_p": bp}
+
+    def near_grid(self, pos, eps2, lo, h, dims, targets=None) -> dict:
+        """As near_grid_exact with eps2, lo and h rounded to float32 first (the GPU's values)."""
+        lo32 = [as_f32(v) for v in lo]
+        return self.near_grid_exact(pos, as_f32(eps2), lo32, as_f32(h), dims, targets)
+
+
 def unpack_diagnostics(out) -> dict:
     """The 13-value diagnostics record as a dict (same order as oracle_diagnostics)."""
     out = [float(x) for x in out]
@@ -217,3 +283,11 @@ def diagnostics(pos, vel, eps2, pot=None) -> dict:
 
 def diagnostics_exact(pos, vel, eps2, pot=None) -> dict:
     return get().diagnostics_exact(pos, vel, eps2, pot)
+
+
+def p2p(pos, eps2, cell_start, list_off, cells) -> dict:
+    return get().p2p(pos, eps2, cell_start, list_off, cells)
+
+
+def near_grid(pos, eps2, lo, h, dims, targets=None) -> dict:
+    return get().near_grid(pos, eps2, lo, h, dims, targets)

@@ -62,29 +62,38 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* Sums of one target: a (3), -p, B, P. */
+typedef struct {
+    double ax, ay, az, pp, sa, sp;
+} target_sums;
+
+/* Source j acting on target i, added into the target's sums. */
+static inline void add_pair(const double *pos, int64_t i, int64_t j, double eps2, target_sums *s)
+{
+    const double xi = pos[4 * i + 0], yi = pos[4 * i + 1], zi = pos[4 * i + 2];
+    const double mj = pos[4 * j + 3];
+    const double dx = pos[4 * j + 0] - xi;          /* r_ij = x_j - x_i */
+    const double dy = pos[4 * j + 1] - yi;
+    const double dz = pos[4 * j + 2] - zi;
+    const double r2 = dx * dx + dy * dy + dz * dz;
+    const double q = r2 + eps2;                     /* |r|^2 + eps^2 */
+    const double q32 = q * sqrt(q);                 /* (|r|^2 + eps^2)^(3/2) */
+    s->ax += mj * dx / q32;
+    s->ay += mj * dy / q32;
+    s->az += mj * dz / q32;
+    s->pp -= mj / sqrt(q);
+    s->sa += mj * sqrt(r2) / q32;
+    s->sp += mj / sqrt(q);
+}
+
 /* One target against all n sources, j = 0 .. n-1 in order. */
 static void one_target(const double *pos, int64_t n, double eps2, int64_t i,
                        double a[3], double *p, double *ba, double *bp)
 {
-    const double xi = pos[4 * i + 0], yi = pos[4 * i + 1], zi = pos[4 * i + 2];
-    double ax = 0.0, ay = 0.0, az = 0.0, pp = 0.0, sa = 0.0, sp = 0.0;
-    for (int64_t j = 0; j < n; ++j) {
-        const double mj = pos[4 * j + 3];
-        const double dx = pos[4 * j + 0] - xi;          /* r_ij = x_j - x_i */
-        const double dy = pos[4 * j + 1] - yi;
-        const double dz = pos[4 * j + 2] - zi;
-        const double r2 = dx * dx + dy * dy + dz * dz;
-        const double q = r2 + eps2;                     /* |r|^2 + eps^2 */
-        const double q32 = q * sqrt(q);                 /* (|r|^2 + eps^2)^(3/2) */
-        ax += mj * dx / q32;
-        ay += mj * dy / q32;
-        az += mj * dz / q32;
-        pp -= mj / sqrt(q);
-        sa += mj * sqrt(r2) / q32;
-        sp += mj / sqrt(q);
-    }
-    a[0] = ax; a[1] = ay; a[2] = az;
-    *p = pp; *ba = sa; *bp = sp;
+    target_sums s = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    for (int64_t j = 0; j < n; ++j) add_pair(pos, i, j, eps2, &s);
+    a[0] = s.ax; a[1] = s.ay; a[2] = s.az;
+    *p = s.pp; *ba = s.sa; *bp = s.sp;
 }
 
 /*
@@ -234,5 +243,105 @@ int oracle_diagnostics(const double *pos, const double *vel, const double *pot, 
         out[10 + c] = m_tot != 0.0 ? mx[c] / m_tot : 0.0;
     }
     out[9] = m_tot;
+    return 0;
+}
+
+/*
+ * Near field over cell interaction lists (the all-pairs kernel as the near
+ * part of a hierarchical method: GPU Gems 3 ch. 31 study page, section 6;
+ * Nakasato "スライド 1" No.34, neighbour-particle algorithms).
+ * Bodies are grouped by cell: cell c owns bodies [cell_start[c], cell_start[c+1]).
+ * Target cell c interacts with the cells list[list_off[c]] .. list[list_off[c+1]-1],
+ * in list order; every body i of c gets
+ *   a_i = sum over listed cells s, over j in s (ascending) of m_j r_ij / (|r_ij|^2 + eps2)^(3/2)
+ *   p_i = -sum ... m_j / (|r_ij|^2 + eps2)^(1/2)
+ * (j = i included when c lists itself), with the error scales B_i, P_i over the
+ * same terms. List entries outside [0, ncell) are skipped. Bodies not in any
+ * cell range get zeros. Returns -1 on bad arguments.
+ */
+int oracle_p2p(const double *pos, int64_t n, double eps2, const int32_t *cell_start,
+               int32_t ncell, const int32_t *list_off, const int32_t *list, double *acc,
+               double *pot, double *bound_a, double *bound_p)
+{
+    if (!pos || n < 0 || ncell < 0 || !(eps2 > 0.0) || !cell_start || !list_off) return -1;
+    if (cell_start[0] < 0 || cell_start[ncell] > n) return -1;
+    for (int32_t c = 0; c < ncell; ++c)
+        if (cell_start[c + 1] < cell_start[c] || list_off[c + 1] < list_off[c]) return -1;
+    for (int64_t i = 0; i < n; ++i) {
+        acc[3 * i] = acc[3 * i + 1] = acc[3 * i + 2] = 0.0;
+        pot[i] = bound_a[i] = bound_p[i] = 0.0;
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int32_t c = 0; c < ncell; ++c) {
+        for (int64_t i = cell_start[c]; i < cell_start[c + 1]; ++i) {
+            target_sums t = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+            for (int32_t e = list_off[c]; e < list_off[c + 1]; ++e) {
+                const int32_t s = list[e];
+                if (s < 0 || s >= ncell) continue;
+                for (int64_t j = cell_start[s]; j < cell_start[s + 1]; ++j)
+                    add_pair(pos, i, j, eps2, &t);
+            }
+            acc[3 * i] = t.ax;
+            acc[3 * i + 1] = t.ay;
+            acc[3 * i + 2] = t.az;
+            pot[i] = t.pp;
+            bound_a[i] = t.sa;
+            bound_p[i] = t.sp;
+        }
+    }
+    return 0;
+}
+
+/*
+ * Near field on a uniform grid, by definition and without lists: the grid has
+ * dims[0] x dims[1] x dims[2] cubic cells of side h from the corner lo; body i
+ * lies in cell k_d = clamp(floor((x_d - lo_d) * inv_h), 0, dims_d - 1) per
+ * axis, and a_i, p_i sum over every body j (ascending index, j = i included)
+ * whose cell differs from i's by at most one in each axis. Bounds as in
+ * oracle_p2p. targets/nt as in oracle_accel.
+ * The cell index is an integer decided by floating point, so it is decided in
+ * the GPU's precision: x_d - lo_d and the product are float operations with
+ * inv_h = float(1 / h), h and lo given as floats.
+ */
+static int64_t grid_coord(double x, double lo, double h, int32_t dim)
+{
+    const float inv_h = 1.0f / (float)h;
+    const float d = (float)x - (float)lo;
+    float f = floorf(d * inv_h);
+    if (!(f >= 0.0f)) f = 0.0f;
+    if (f > (float)(dim - 1)) f = (float)(dim - 1);
+    return (int64_t)f;
+}
+
+int oracle_near_grid(const double *pos, int64_t n, double eps2, const double *lo, double h,
+                     const int32_t *dims, const int64_t *targets, int64_t nt, double *acc,
+                     double *pot, double *bound_a, double *bound_p)
+{
+    if (!pos || n < 0 || nt < 0 || !(eps2 > 0.0) || !(h > 0.0) || !lo || !dims) return -1;
+    if (dims[0] < 1 || dims[1] < 1 || dims[2] < 1) return -1;
+    int64_t *cell = (int64_t *)malloc((size_t)(n > 0 ? n : 1) * 3 * sizeof(int64_t));
+    if (!cell) return -1;
+    for (int64_t j = 0; j < n; ++j)
+        for (int d = 0; d < 3; ++d) cell[3 * j + d] = grid_coord(pos[4 * j + d], lo[d], h, dims[d]);
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t t = 0; t < nt; ++t) {
+        const int64_t i = targets ? targets[t] : t;
+        target_sums s = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+        for (int64_t j = 0; j < n; ++j) {
+            int near = 1;
+            for (int d = 0; d < 3; ++d) {
+                const int64_t dd = cell[3 * j + d] - cell[3 * i + d];
+                if (dd < -1 || dd > 1) near = 0;
+            }
+            if (near) add_pair(pos, i, j, eps2, &s);
+        }
+        acc[3 * t] = s.ax;
+        acc[3 * t + 1] = s.ay;
+        acc[3 * t + 2] = s.az;
+        pot[t] = s.pp;
+        bound_a[t] = s.sa;
+        bound_p[t] = s.sp;
+    }
+    free(cell);
     return 0;
 }

@@ -360,6 +360,152 @@ def pin_diagnostics_euler_momentum(orc):
     _close(d1["centre_of_mass"], want, 1e-14, "Euler step centre of mass")
 
 
+# ---------------------------------------------------------------- near field
+# The all-pairs sum restricted to listed cells (GPU Gems 3 ch. 31 study page, section 6:
+# near-field leaf cells use all-pairs; Nakasato No.34: neighbour-particle algorithms).
+
+def _csr(lists):
+    off = np.zeros(len(lists) + 1, np.int32)
+    off[1:] = np.cumsum([len(x) for x in lists])
+    flat = np.array([c for x in lists for c in x], np.int32)
+    return off, flat
+
+
+def _random_cells(seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    sizes = [7, 0, 12, 1, 20, 9]  # an empty cell included
+    n = sum(sizes)
+    x = rng.uniform(-1, 1, size=(n, 3))
+    m = rng.uniform(0.1, 2.0, size=n)
+    start = np.zeros(len(sizes) + 1, np.int32)
+    start[1:] = np.cumsum(sizes)
+    return _bodies(x, m), start
+
+
+def pin_p2p_full_lists_equal_direct_sum(orc):
+    """Every cell listing every cell in ascending order sums every j in ascending order: the
+    result equals the direct sum bit for bit."""
+    pos, start = _random_cells(10)
+    nc = len(start) - 1
+    off, flat = _csr([list(range(nc))] * nc)
+    r = orc.p2p_exact(pos, 1e-3, start, off, flat)
+    d = orc.accel_exact(pos, 1e-3)
+    for k in ("acc", "pot", "bound_a", "bound_p"):
+        if not np.array_equal(r[k], d[k]):
+            raise AssertionError(f"p2p with full lists differs from the direct sum in {k}")
+
+
+def pin_p2p_self_lists_equal_subsystems(orc):
+    """Each cell listing only itself gives the direct sum of that cell's bodies alone."""
+    pos, start = _random_cells(11)
+    nc = len(start) - 1
+    off, flat = _csr([[c] for c in range(nc)])
+    r = orc.p2p_exact(pos, 1e-3, start, off, flat)
+    for c in range(nc):
+        a, b = start[c], start[c + 1]
+        if a == b:
+            continue
+        d = orc.accel_exact(pos[a:b], 1e-3)
+        if not (np.array_equal(r["acc"][a:b], d["acc"]) and np.array_equal(r["pot"][a:b], d["pot"])):
+            raise AssertionError(f"cell {c}: self list differs from its subsystem")
+
+
+def pin_p2p_skips_bad_entries_and_empty_lists(orc):
+    """Entries outside [0, ncell) add nothing; an empty list gives exact zeros."""
+    pos, start = _random_cells(12)
+    nc = len(start) - 1
+    good = [[0, 2], [], [5, 4], [1], [3, 3], [2]]
+    bad = [[-1, 0, 2, nc], [nc + 7], [5, -3, 4], [1, 99], [3, 3, -1], [2]]
+    r1 = orc.p2p_exact(pos, 1e-3, start, *_csr(good))
+    r2 = orc.p2p_exact(pos, 1e-3, start, *_csr(bad))
+    for k in ("acc", "pot"):
+        if not np.array_equal(r1[k], r2[k]):
+            raise AssertionError(f"invalid list entries changed {k}")
+    a, b = start[1], start[2]
+    if a != b or not np.all(r1["acc"][start[1]:start[2]] == 0):
+        raise AssertionError("empty cell / empty list not zero")
+    # cell 1 is empty; cell 3 (one body) lists cell 1 only in a variant: exact zeros
+    r3 = orc.p2p_exact(pos, 1e-3, start, *_csr([[0], [], [2], [1], [4], [5]]))
+    i = start[3]
+    if not (np.all(r3["acc"][i] == 0) and r3["pot"][i] == 0):
+        raise AssertionError("a list of only an empty cell must give zeros")
+
+
+def _grid_cells_f32(pos, lo, h, dims):
+    """Cell coordinates decided in float32 as the GPU decides them: floor((x - lo) * (1/h))."""
+    x = pos[:, :3].astype(np.float32)
+    inv = np.float32(1.0) / np.float32(h)
+    f = np.floor((x - np.asarray(lo, np.float32)) * inv)
+    f = np.nan_to_num(f, nan=0.0)
+    return np.clip(f, 0, np.asarray(dims) - 1).astype(np.int64)
+
+
+def pin_near_grid_small_grids_equal_direct_sum(orc):
+    """With at most 2 cells per axis every cell neighbours every other: the near field is the
+    direct sum, bit for bit (both sum every j in ascending order)."""
+    rng = np.random.Generator(np.random.PCG64(13))
+    x = rng.uniform(-1, 1, size=(50, 3)).astype(np.float32).astype(np.float64)
+    m = rng.uniform(0.1, 2.0, size=50)
+    pos = _bodies(x, m)
+    d = orc.accel_exact(pos, 1e-3)
+    for dims, h in (((1, 1, 1), 4.0), ((2, 2, 1), 1.0), ((2, 2, 2), 1.25)):
+        r = orc.near_grid_exact(pos, 1e-3, (-1.0, -1.0, -1.0), h, dims)
+        for k in ("acc", "pot", "bound_a", "bound_p"):
+            if not np.array_equal(r[k], d[k]):
+                raise AssertionError(f"near grid {dims}: differs from the direct sum in {k}")
+
+
+def pin_near_grid_separated_clusters(orc):
+    """Two clusters three cells apart do not see each other: each gets its own direct sum."""
+    rng = np.random.Generator(np.random.PCG64(14))
+    a = rng.uniform(0.0, 1.0, size=(20, 3))
+    b = rng.uniform(0.0, 1.0, size=(15, 3)) + np.array([10.0, 0.0, 0.0])
+    m = rng.uniform(0.5, 1.5, size=35)
+    pos = _bodies(np.concatenate([a, b]), m)
+    r = orc.near_grid_exact(pos, 1e-3, (0.0, 0.0, 0.0), 2.5, (5, 1, 1))
+    da = orc.accel_exact(pos[:20], 1e-3)
+    db = orc.accel_exact(pos[20:], 1e-3)
+    if not (np.array_equal(r["acc"][:20], da["acc"]) and np.array_equal(r["acc"][20:], db["acc"])):
+        raise AssertionError("separated clusters interact in the near field")
+    if not (np.array_equal(r["pot"][:20], da["pot"]) and np.array_equal(r["pot"][20:], db["pot"])):
+        raise AssertionError("separated clusters: potentials")
+
+
+def pin_near_grid_equals_lists(orc):
+    """The grid near field equals the list form built independently here (bodies sorted by
+    cell, 27-neighbour lists): same terms, other order, so to 1e-13 of B and P."""
+    rng = np.random.Generator(np.random.PCG64(15))
+    n = 300
+    x = rng.uniform(-1, 1, size=(n, 3)).astype(np.float32).astype(np.float64)
+    m = rng.uniform(0.1, 2.0, size=n)
+    pos = _bodies(x, m)
+    lo, h, dims = (-1.0, -1.0, -1.0), 0.4, (5, 5, 5)
+    k = _grid_cells_f32(pos, lo, h, dims)
+    cid = (k[:, 2] * dims[1] + k[:, 1]) * dims[0] + k[:, 0]
+    order = np.argsort(cid, kind="stable")
+    nc = dims[0] * dims[1] * dims[2]
+    start = np.searchsorted(cid[order], np.arange(nc + 1)).astype(np.int32)
+    lists = []
+    for c in range(nc):
+        cx, cy, cz = c % dims[0], (c // dims[0]) % dims[1], c // (dims[0] * dims[1])
+        nb = []
+        for dz in (-1, 0, 1):
+            for dy in (-1, 0, 1):
+                for dx in (-1, 0, 1):
+                    X, Y, Z = cx + dx, cy + dy, cz + dz
+                    if 0 <= X < dims[0] and 0 <= Y < dims[1] and 0 <= Z < dims[2]:
+                        nb.append((Z * dims[1] + Y) * dims[0] + X)
+        lists.append(nb)
+    r_list = orc.p2p_exact(pos[order], 1e-3, start, *_csr(lists))
+    r_grid = orc.near_grid_exact(pos, 1e-3, lo, h, dims)
+    back = np.empty(n, np.int64)
+    back[order] = np.arange(n)
+    err = np.linalg.norm(r_list["acc"][back] - r_grid["acc"], axis=1)
+    if np.any(err > 1e-13 * r_grid["bound_a"] + 1e-300):
+        raise AssertionError(f"grid vs lists: max err {np.max(err):.3e}")
+    _close(r_list["pot"][back], r_grid["pot"], 1e-13 * np.max(r_grid["bound_p"]), "grid vs lists p")
+
+
 ALL_PINS = [
     pin_single_body,
     pin_two_body_345,
@@ -378,4 +524,10 @@ ALL_PINS = [
     pin_diagnostics_rotating_ring,
     pin_diagnostics_pair_sum,
     pin_diagnostics_euler_momentum,
+    pin_p2p_full_lists_equal_direct_sum,
+    pin_p2p_self_lists_equal_subsystems,
+    pin_p2p_skips_bad_entries_and_empty_lists,
+    pin_near_grid_small_grids_equal_direct_sum,
+    pin_near_grid_separated_clusters,
+    pin_near_grid_equals_lists,
 ]

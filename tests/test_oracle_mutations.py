@@ -16,23 +16,23 @@ import pins
 MUTATIONS = [
     ("r_ij sign flipped in x", "pos[4 * j + 0] - xi", "xi - pos[4 * j + 0]"),
     ("eps instead of eps^2", "const double q = r2 + eps2;", "const double q = r2 + eps2 * eps2;"),
-    ("self term skipped", "for (int64_t j = 0; j < n; ++j) {\n        const double mj",
-     "for (int64_t j = 0; j < n; ++j) {\n        if (j == i) continue;\n        const double mj"),
+    ("self term skipped", "for (int64_t j = 0; j < n; ++j) add_pair(pos, i, j, eps2, &s);",
+     "for (int64_t j = 0; j < n; ++j) if (j != i) add_pair(pos, i, j, eps2, &s);"),
     ("exponent 1 instead of 3/2", "const double q32 = q * sqrt(q);", "const double q32 = q;"),
     ("target mass instead of source mass", "const double mj = pos[4 * j + 3];",
      "const double mj = pos[4 * i + 3];"),
-    ("potential sign", "pp -= mj / sqrt(q);", "pp += mj / sqrt(q);"),
-    ("y component uses dx", "ay += mj * dy / q32;", "ay += mj * dx / q32;"),
-    ("last source dropped", "for (int64_t j = 0; j < n; ++j) {\n        const double mj",
-     "for (int64_t j = 0; j < n - 1; ++j) {\n        const double mj"),
-    ("B scale without |r|", "sa += mj * sqrt(r2) / q32;", "sa += mj / q32;"),
+    ("potential sign", "s->pp -= mj / sqrt(q);", "s->pp += mj / sqrt(q);"),
+    ("y component uses dx", "s->ay += mj * dy / q32;", "s->ay += mj * dx / q32;"),
+    ("last source dropped", "for (int64_t j = 0; j < n; ++j) add_pair(pos, i, j, eps2, &s);",
+     "for (int64_t j = 0; j < n - 1; ++j) add_pair(pos, i, j, eps2, &s);"),
+    ("B scale without |r|", "s->sa += mj * sqrt(r2) / q32;", "s->sa += mj / q32;"),
     ("Euler: velocity first",
      "for (int c = 0; c < 3; ++c) pos[4 * i + c] += dt * vel[4 * i + c];  /* old v */\n"
      "            for (int c = 0; c < 3; ++c) vel[4 * i + c] += dt * acc[3 * i + c];",
      "for (int c = 0; c < 3; ++c) vel[4 * i + c] += dt * acc[3 * i + c];\n"
      "            for (int c = 0; c < 3; ++c) pos[4 * i + c] += dt * vel[4 * i + c];"),
     ("energy pairs counted twice", "wi[i] = 0.5 * pos[4 * i + 3] * s;", "wi[i] = pos[4 * i + 3] * s;"),
-    ("z acceleration dropped", "az += mj * dz / q32;", "az += 0.0;"),
+    ("z acceleration dropped", "s->az += mj * dz / q32;", "s->az += 0.0;"),
     ("kinetic energy without 1/2", "k += 0.5 * m * (vx * vx + vy * vy + vz * vz);",
      "k += m * (vx * vx + vy * vy + vz * vz);"),
     ("self term added instead of removed", "w += 0.5 * m * (pot[i] + m * inv_eps);",
@@ -41,6 +41,15 @@ MUTATIONS = [
      "ang[2] += m * (y * vx - x * vy);"),
     ("momentum uses position", "mom[1] += m * vy;", "mom[1] += m * y;"),
     ("centre of mass unweighted", "mx[0] += m * x;", "mx[0] += x;"),
+    ("near grid: one-sided neighbourhood", "if (dd < -1 || dd > 1) near = 0;",
+     "if (dd < -1 || dd > 0) near = 0;"),
+    ("near grid: cell by rounding", "float f = floorf(d * inv_h);", "float f = roundf(d * inv_h);"),
+    ("p2p: last body of each source cell dropped",
+     "for (int64_t j = cell_start[s]; j < cell_start[s + 1]; ++j)\n",
+     "for (int64_t j = cell_start[s]; j < cell_start[s + 1] - 1; ++j)\n"),
+    ("p2p: negative list entry read as cell 0",
+     "const int32_t s = list[e];\n                if (s < 0 || s >= ncell) continue;",
+     "const int32_t s = list[e] < 0 ? 0 : list[e];\n                if (s >= ncell) continue;"),
 ]
 
 
