@@ -166,6 +166,52 @@ def sweep(nb, w, pos, vel, acc, pot, args) -> int:
     return 0
 
 
+def near_grid_terms(pos_h, lo, h, dims) -> int:
+    """Pair terms of the grid near field: sum over cells of n_c times the bodies in its 27-cell
+    neighbourhood (cells decided in float32, as the library decides them)."""
+    import numpy as np
+
+    x = pos_h[:, :3].astype(np.float32)
+    inv = np.float32(1.0) / np.float32(h)
+    k = np.floor((x - np.asarray(lo, np.float32)) * inv)
+    k = np.clip(np.nan_to_num(k, nan=0.0), 0, np.asarray(dims) - 1).astype(np.int64)
+    cnt = np.zeros(dims[::-1], np.int64)
+    np.add.at(cnt, (k[:, 2], k[:, 1], k[:, 0]), 1)
+    pad = np.pad(cnt, 1)
+    nbr = sum(pad[1 + dz:1 + dz + dims[2], 1 + dy:1 + dy + dims[1], 1 + dx:1 + dx + dims[0]]
+              for dz in (-1, 0, 1) for dy in (-1, 0, 1) for dx in (-1, 0, 1))
+    return int(np.sum(cnt * nbr))
+
+
+def near_grid_bench(nb, w, pos, args) -> int:
+    """Time nbody_near_grid (binning, sort, near-field kernel, scatter) on a cubic grid of
+    args.near_grid cells per axis over [-1, 1]^3; one JSON line (not the contract line)."""
+    import torch
+
+    d = args.near_grid
+    lo, h, dims = (-1.0, -1.0, -1.0), 2.0 / d, (d, d, d)
+    n = w.n
+    acc = torch.empty_like(pos)
+    pot = torch.empty(n, dtype=torch.float32, device=pos.device)
+    stream = torch.cuda.current_stream()
+    for _ in range(max(1, args.warmup)):
+        nb.nbody_near_grid(pos, n, float(w.eps2), lo, h, dims, acc, pot, stream)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        nb.nbody_near_grid(pos, n, float(w.eps2), lo, h, dims, acc, pot, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    terms = near_grid_terms(w.pos, lo, h, dims)
+    print(json.dumps({"near_grid": {"workload": args.workload, "N": n, "dims": dims, "h": h,
+                                    "bodies_per_cell": n / (d ** 3), "pair_terms": terms,
+                                    "ms": round(ms, 4),
+                                    "G_terms_per_s": round(terms / ms / 1e6, 2)}}), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -186,6 +232,9 @@ def main(argv=None) -> int:
                          "workload's call and print one JSON line per layout (no contract line)")
     ap.add_argument("--sweep-only", default="all", choices=["all", "tiles", "pairs", "small"],
                     help="restrict --sweep to one evaluation mode")
+    ap.add_argument("--near-grid", type=int, default=0, metavar="D",
+                    help="only time nbody_near_grid on a D^3 grid over [-1, 1]^3 (near field; "
+                         "prints its own JSON line, no contract line)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (twice) and exit; "
                          "used to scale the HBM byte counters of rocprofv3")
@@ -234,6 +283,8 @@ def main(argv=None) -> int:
 
     if args.sweep:
         return sweep(nb, w, pos, vel, acc, pot, args)
+    if args.near_grid:
+        return near_grid_bench(nb, w, pos, args)
 
     diag0 = nb.diagnostics(pos, vel, float(w.eps2)) if stepping else None
     for _ in range(args.warmup):

@@ -63,19 +63,22 @@ _lib.nbody_step_plan.argtypes = [_vp, _vp, _i64, _f32, _f32, _i64, ctypes.POINTE
                                  _vp]
 _lib.nbody_plan_for.argtypes = [_i64, _int, ctypes.POINTER(nbody_plan)]
 _lib.nbody_diagnostics.argtypes = [_vp, _vp, _vp, _i64, _f32, _vp, _vp]
+_lib.nbody_p2p.argtypes = [_vp, _i64, _f32, _vp, ctypes.c_int32, _vp, _vp, _i64, _vp, _vp, _vp]
+_lib.nbody_near_grid.argtypes = [_vp, _i64, _f32, ctypes.POINTER(ctypes.c_float), _f32,
+                                 ctypes.POINTER(ctypes.c_int32), _vp, _vp, _vp]
 _lib.nbody_accel_soa.argtypes = [_vp, _vp, _vp, _vp, _i64, _f32, _vp, _vp, _vp, _vp, _vp]
 _lib.nbody_step_soa.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _f32, _f32, _i64, _vp]
 _lib.nbody_last_error.restype = ctypes.c_char_p
 _lib.nbody_release_workspace.argtypes = []
 _lib.nbody_version.restype = ctypes.c_char_p
 for _f in ("nbody_accel", "nbody_accel_plan", "nbody_step", "nbody_step_plan",
-           "nbody_accel_soa", "nbody_step_soa", "nbody_diagnostics", "nbody_plan_for",
-           "nbody_release_workspace"):
+           "nbody_accel_soa", "nbody_step_soa", "nbody_p2p", "nbody_near_grid",
+           "nbody_diagnostics", "nbody_plan_for", "nbody_release_workspace"):
     getattr(_lib, _f).restype = _int
 
 EXPORTS = ("nbody_accel", "nbody_accel_plan", "nbody_step", "nbody_step_plan", "nbody_accel_soa",
-           "nbody_step_soa", "nbody_diagnostics", "nbody_plan_for", "nbody_last_error",
-           "nbody_release_workspace", "nbody_version")
+           "nbody_step_soa", "nbody_p2p", "nbody_near_grid", "nbody_diagnostics",
+           "nbody_plan_for", "nbody_last_error", "nbody_release_workspace", "nbody_version")
 DIAG_FIELDS = ("kinetic", "potential", "total", "momentum", "angular_momentum", "mass",
                "centre_of_mass")
 
@@ -163,6 +166,24 @@ def nbody_step_soa(x, y, z, m, vx, vy, vz, N: int, dt: float, eps2: float, nstep
     rc = _lib.nbody_step_soa(_ptr(x), _ptr(y), _ptr(z), _ptr(m), _ptr(vx), _ptr(vy), _ptr(vz),
                              int(N), float(dt), float(eps2), int(nsteps), _stream(stream))
     return _check(rc, "nbody_step_soa") if check else rc
+
+
+def nbody_p2p(pos, N: int, eps2: float, cell_start, ncell: int, list_off, cells, nlist: int,
+              acc_out, pot_out=None, stream=None, check: bool = True) -> int:
+    rc = _lib.nbody_p2p(_ptr(pos), int(N), float(eps2), _ptr(cell_start), int(ncell),
+                        _ptr(list_off), _ptr(cells), int(nlist), _ptr(acc_out), _ptr(pot_out),
+                        _stream(stream))
+    return _check(rc, "nbody_p2p") if check else rc
+
+
+def nbody_near_grid(pos, N: int, eps2: float, lo, h: float, dims, acc_out, pot_out=None,
+                    stream=None, check: bool = True) -> int:
+    """lo (3 floats) and dims (3 ints) are host values."""
+    lo_c = (ctypes.c_float * 3)(*[float(v) for v in lo]) if lo is not None else None
+    dims_c = (ctypes.c_int32 * 3)(*[int(v) for v in dims]) if dims is not None else None
+    rc = _lib.nbody_near_grid(_ptr(pos), int(N), float(eps2), lo_c, float(h), dims_c,
+                              _ptr(acc_out), _ptr(pot_out), _stream(stream))
+    return _check(rc, "nbody_near_grid") if check else rc
 
 
 def nbody_diagnostics(pos, vel, N: int, eps2: float, out, pot=None, stream=None,

@@ -11,7 +11,7 @@ PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libnbody_amd.so"
-SOURCES = [CSRC / "api.hip", CSRC / "kernels.hip"]
+SOURCES = [CSRC / "api.hip", CSRC / "kernels.hip", CSRC / "sort.hip"]
 
 # -packed-fp32-ops is switched off on purpose: no v_pk_*_f32 is generated.
 HIPCC_FLAGS = [

@@ -125,6 +125,10 @@ int scratch_get(int dev, hipStream_t stream, size_t bytes, void **out)
 // ------------------------------------------------------------ planning
 
 constexpr int kMaxSplits = 4096;
+// Most cells a uniform grid of nbody_near_grid may have (one 32-bit key per body
+// and one start index per cell).
+constexpr int64_t kMaxGridCells = (int64_t)1 << 28;
+
 // Largest N the automatic plan gives to NBODY_MODE_SMALL, and the smallest it
 // gives to NBODY_MODE_PAIRS.
 constexpr int64_t kSmallMaxN = 8192;
@@ -572,6 +576,120 @@ int nbody_step_soa(float *x, float *y, float *z, const float *m, float *vx, floa
                    int64_t N, float dt, float eps2, int64_t nsteps, hipStream_t stream)
 {
     return step_soa_impl(x, y, z, m, vx, vy, vz, N, dt, eps2, nsteps, stream);
+}
+
+int nbody_p2p(const nbody_f4 *pos, int64_t N, float eps2, const int32_t *cell_start,
+              int32_t ncell, const int32_t *list_off, const int32_t *cells, int64_t nlist,
+              nbody_f4 *acc_out, float *pot_out, hipStream_t stream)
+{
+    int rc = check_n(N);
+    if (rc != NBODY_OK) return rc;
+    if (ncell < 0) return fail(NBODY_EINVAL, "ncell=%d must be >= 0", (int)ncell);
+    if (nlist < 0 || nlist > INT32_MAX)
+        return fail(NBODY_EINVAL, "nlist=%lld must be in [0, 2^31 - 1]", (long long)nlist);
+    if (N == 0 || ncell == 0) return ok();
+    if (!pos) return fail(NBODY_EINVAL, "pos_xyzm is NULL");
+    if (!acc_out) return fail(NBODY_EINVAL, "acc_out is NULL");
+    if (!cell_start || !list_off) return fail(NBODY_EINVAL, "cell_start or list_off is NULL");
+    if (nlist > 0 && !cells) return fail(NBODY_EINVAL, "cells is NULL");
+    if (!eps2_ok(eps2))
+        return fail(NBODY_EINVAL, "eps2=%g must be a positive, finite, normal float", (double)eps2);
+    if (!aligned(pos, 16) || !aligned(acc_out, 16))
+        return fail(NBODY_EALIGN, "pos_xyzm and acc_out must be 16-byte aligned");
+    if ((pot_out && !aligned(pot_out, 4)) || !aligned(cell_start, 4) || !aligned(list_off, 4) ||
+        (cells && !aligned(cells, 4)))
+        return fail(NBODY_EALIGN, "pot_out and the index arrays must be 4-byte aligned");
+    const size_t b16 = (size_t)N * 16, b4 = (size_t)N * 4, bc = ((size_t)ncell + 1) * 4;
+    const void *outs[2] = {acc_out, pot_out};
+    const size_t osz[2] = {b16, b4};
+    const void *ins[4] = {pos, cell_start, list_off, cells};
+    const size_t isz[4] = {b16, bc, bc, (size_t)nlist * 4};
+    for (int o = 0; o < 2; ++o) {
+        if (!outs[o]) continue;
+        for (int j = 0; j < 4; ++j)
+            if (ins[j] && isz[j] && overlap(outs[o], osz[o], ins[j], isz[j]))
+                return fail(NBODY_EINVAL, "an output overlaps an input");
+    }
+    if (pot_out && overlap(acc_out, b16, pot_out, b4))
+        return fail(NBODY_EINVAL, "pot_out overlaps acc_out");
+    nbk::P2PArgs a{(const float4 *)pos, (int)N, eps2, cell_start, ncell, list_off, cells,
+                   (long long)nlist, (float4 *)acc_out, pot_out};
+    hipError_t e = nbk::launch_p2p(pot_out != nullptr, a, stream);
+    if (e != hipSuccess) return hip_fail(e, "p2p kernel launch");
+    return ok();
+}
+
+int nbody_near_grid(const nbody_f4 *pos, int64_t N, float eps2, const float lo[3], float h,
+                    const int32_t dims[3], nbody_f4 *acc_out, float *pot_out, hipStream_t stream)
+{
+    int rc = check_n(N);
+    if (rc != NBODY_OK) return rc;
+    if (!lo || !dims) return fail(NBODY_EINVAL, "lo or dims is NULL");
+    int64_t ncell = 1;
+    for (int d = 0; d < 3; ++d) {
+        if (dims[d] < 1) return fail(NBODY_EINVAL, "dims[%d]=%d must be >= 1", d, (int)dims[d]);
+        if (!std::isfinite(lo[d])) return fail(NBODY_EINVAL, "lo[%d] is not finite", d);
+        ncell *= dims[d];
+        if (ncell > kMaxGridCells)
+            return fail(NBODY_EINVAL, "dims hold more than %lld cells", (long long)kMaxGridCells);
+    }
+    const float inv_h = 1.0f / h;
+    if (!(h >= FLT_MIN) || !std::isfinite(h) || !std::isfinite(inv_h))
+        return fail(NBODY_EINVAL, "h=%g must be a positive, finite, normal float with a finite "
+                                  "reciprocal", (double)h);
+    if (N == 0) return ok();
+    if (!pos) return fail(NBODY_EINVAL, "pos_xyzm is NULL");
+    if (!acc_out) return fail(NBODY_EINVAL, "acc_out is NULL");
+    if (!eps2_ok(eps2))
+        return fail(NBODY_EINVAL, "eps2=%g must be a positive, finite, normal float", (double)eps2);
+    if (!aligned(pos, 16) || !aligned(acc_out, 16))
+        return fail(NBODY_EALIGN, "pos_xyzm and acc_out must be 16-byte aligned");
+    if (pot_out && !aligned(pot_out, 4)) return fail(NBODY_EALIGN, "pot_out is not 4-byte aligned");
+    const size_t b16 = (size_t)N * 16, b4 = (size_t)N * 4;
+    if (overlap(pos, b16, acc_out, b16)) return fail(NBODY_EINVAL, "acc_out overlaps pos_xyzm");
+    if (pot_out && (overlap(pot_out, b4, pos, b16) || overlap(pot_out, b4, acc_out, b16)))
+        return fail(NBODY_EINVAL, "pot_out overlaps another buffer");
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    nbk::GridSpec g{{lo[0], lo[1], lo[2]}, inv_h, {dims[0], dims[1], dims[2]}};
+    const int n = (int)N, nc = (int)ncell;
+    int end_bit = 1;
+    while (end_bit < 32 && ((int64_t)1 << end_bit) < ncell) ++end_bit;
+    size_t sort_bytes = 0;
+    e = nbk::sort_pairs(nullptr, sort_bytes, nullptr, nullptr, nullptr, nullptr, n, end_bit, stream);
+    if (e != hipSuccess) return hip_fail(e, "sort temp-size query");
+    // scratch: keys, idx, sorted keys, perm (N x 4 each), sorted pos, acc (N x 16 each),
+    // pot (N x 4), cell starts ((ncell + 1) x 4), sort temp
+    size_t off[10];
+    const size_t sz[9] = {b4, b4, b4, b4, b16, b16, b4, ((size_t)nc + 1) * 4, sort_bytes};
+    off[0] = 0;
+    for (int i = 0; i < 9; ++i) off[i + 1] = align256(off[i] + sz[i]);
+    void *ws = nullptr;
+    rc = scratch_get(dev, stream, off[9], &ws);
+    if (rc != NBODY_OK) return rc;
+    char *b = (char *)ws;
+    unsigned *keys = (unsigned *)(b + off[0]), *skeys = (unsigned *)(b + off[2]);
+    int *idx = (int *)(b + off[1]), *perm = (int *)(b + off[3]);
+    float4 *spos = (float4 *)(b + off[4]), *sacc = (float4 *)(b + off[5]);
+    float *spot = (float *)(b + off[6]);
+    int *start = (int *)(b + off[7]);
+    void *temp = b + off[8];
+    e = nbk::launch_grid_keys((const float4 *)pos, n, g, keys, idx, stream);
+    if (e == hipSuccess)
+        e = nbk::sort_pairs(temp, sort_bytes, keys, skeys, idx, perm, n, end_bit, stream);
+    if (e == hipSuccess) e = nbk::launch_gather((const float4 *)pos, perm, n, spos, stream);
+    if (e == hipSuccess) e = nbk::launch_cell_starts(skeys, n, nc, start, stream);
+    if (e == hipSuccess) {
+        nbk::P2PArgs a{spos, n, eps2, start, nc, nullptr, nullptr, 0, sacc,
+                       pot_out ? spot : nullptr};
+        e = nbk::launch_p2p_grid(pot_out != nullptr, a, g, stream);
+    }
+    if (e == hipSuccess)
+        e = nbk::launch_scatter(sacc, pot_out ? spot : nullptr, perm, n, (float4 *)acc_out,
+                                pot_out, stream);
+    if (e != hipSuccess) return hip_fail(e, "near-grid launch");
+    return ok();
 }
 
 int nbody_diagnostics(const nbody_f4 *pos, const nbody_f4 *vel, const float *pot, int64_t N,

@@ -65,6 +65,50 @@ int diag_blocks(int n);
 hipError_t launch_diagnostics(const float4 *pos, const float4 *vel, const float *pot, int n,
                               double inv_eps, double *part, double *out, hipStream_t stream);
 
+// Near field: target cell c (bodies [cell_start[c], cell_start[c+1])) sums over
+// the bodies of the cells in its interaction list. One wave per target cell.
+struct P2PArgs {
+    const float4 *pos;      // N bodies grouped by cell
+    int n;                  // N
+    float eps2;             // softening squared
+    const int *cell_start;  // ncell + 1 entries (device)
+    int ncell;
+    const int *list_off;    // CSR lists: ncell + 1 entries (device); unused on a grid
+    const int *list;        // nlist cell indices (device); unused on a grid
+    long long nlist;
+    float4 *acc_out;        // (ax, ay, az, 0) per body inside a cell range
+    float *pot_out;         // p per body, or nullptr
+};
+
+// A uniform grid: dims cells per axis, corner lo, cell index per axis
+// clamp(floor((x - lo) * inv_h), 0, dims - 1), linear index (z*dy + y)*dx + x.
+struct GridSpec {
+    float lo[3];
+    float inv_h;
+    int dims[3];
+};
+
+hipError_t launch_p2p(bool pot, const P2PArgs &args, hipStream_t stream);
+// The same kernel with the 27 neighbour cells of the grid as every cell's list.
+hipError_t launch_p2p_grid(bool pot, const P2PArgs &args, const GridSpec &g, hipStream_t stream);
+// keys[i] = linear cell of body i, idx[i] = i.
+hipError_t launch_grid_keys(const float4 *pos, int n, const GridSpec &g, unsigned *keys, int *idx,
+                            hipStream_t stream);
+// out[k] = pos[perm[k]].
+hipError_t launch_gather(const float4 *pos, const int *perm, int n, float4 *out,
+                         hipStream_t stream);
+// cell_start[c] = first k with sorted_keys[k] >= c, for c = 0 .. ncell.
+hipError_t launch_cell_starts(const unsigned *sorted_keys, int n, int ncell, int *cell_start,
+                              hipStream_t stream);
+// acc[perm[k]] = sacc[k]; pot[perm[k]] = spot[k] (if pot).
+hipError_t launch_scatter(const float4 *sacc, const float *spot, const int *perm, int n,
+                          float4 *acc, float *pot, hipStream_t stream);
+// Stable sort of (key, value) pairs on bits [0, end_bit) of the keys (sort.hip).
+// With temp == nullptr only temp_bytes is set.
+hipError_t sort_pairs(void *temp, size_t &temp_bytes, const unsigned *keys_in,
+                      unsigned *keys_out, const int *vals_in, int *vals_out, int n, int end_bit,
+                      hipStream_t stream);
+
 // Layout conversion for the SoA entry points: out[i] = (a[i], b[i], c[i], d ? d[i] : 0),
 // and back: a[i], b[i], c[i] = in[i].x, .y, .z.
 hipError_t launch_pack(const float *a, const float *b, const float *c, const float *d, int n,

@@ -896,6 +896,234 @@ __global__ void __launch_bounds__(256) diag_final_kernel(const double *__restric
     out[9] = m;
 }
 
+// ---------------------------------------------------------------- near field
+// All-pairs as the near part of a hierarchical method (GPU Gems 3 ch. 31 study
+// page, section 6; Nakasato, "スライド 1", No.34): each target cell's bodies
+// sum over the bodies of the cells in its interaction list. One wave (64
+// threads) per target cell: the cell's bodies 64 at a time, one per lane; each
+// listed source cell is staged through the wave's own 64-body LDS row and read
+// back with LDS reads (a broadcast within each source group). Every source
+// tile is one block of the compensated two-level accumulation. Ranges and list entries are
+// checked before use (memory safety for any input): a target cell with an
+// invalid range is skipped, an invalid list range is empty, an out-of-range
+// list entry or a source cell with an invalid range adds nothing.
+struct CsrLists {
+    const int *off;
+    const int *list;
+    long long nlist;
+    int ncell;
+    __device__ void bind(int) {}
+    __device__ void range(int c, int &lo, int &hi) const
+    {
+        long long a = off[c], b = off[c + 1];
+        if (a < 0 || b < a || b > nlist) a = b = 0;
+        lo = (int)a;
+        hi = (int)b;
+    }
+    __device__ int cell(int e, int) const
+    {
+        const int s = list[e];
+        return (s < 0 || s >= ncell) ? -1 : s;
+    }
+};
+
+// The 27 neighbours of the target cell (9 (z + 1) + 3 (y + 1) + (x + 1), -1
+// outside the grid), computed once per workgroup into LDS by lanes 0..26.
+struct GridLists {
+    int dx, dy, dz;
+    int *nbr;  // 27 LDS entries
+    __device__ void bind(int c)
+    {
+        const int lane = threadIdx.x;
+        if (lane < 27) {
+            const int cx = c % dx, cy = (c / dx) % dy, cz = c / (dx * dy);
+            const int x = cx + lane % 3 - 1, y = cy + (lane / 3) % 3 - 1, z = cz + lane / 9 - 1;
+            const bool in = x >= 0 && x < dx && y >= 0 && y < dy && z >= 0 && z < dz;
+            nbr[lane] = in ? (z * dy + y) * dx + x : -1;
+        }
+        __syncthreads();
+    }
+    __device__ void range(int, int &lo, int &hi) const
+    {
+        lo = 0;
+        hi = 27;
+    }
+    __device__ int cell(int e, int) const { return __builtin_amdgcn_readfirstlane(nbr[e]); }
+};
+
+// Walk over the source tiles of a target cell's list: tile = bodies
+// [j0, min(j0 + 64, se)) of listed cell e. Starting from (e, j0, se), moves to
+// the next tile (the rest of the same cell, then the next valid non-empty
+// listed cell); false when the list is exhausted. Uniform across the wave.
+template <typename Lists>
+__device__ __forceinline__ bool next_tile(const P2PArgs &k, const Lists &lists, int c, int hi,
+                                          int &e, int &j0, int &se)
+{
+    if (j0 + 64 < se) {
+        j0 += 64;
+        return true;
+    }
+#pragma unroll 1
+    for (++e; e < hi; ++e) {
+        const int s = lists.cell(e, c);
+        if (s < 0) continue;
+        const int sb = k.cell_start[s], sn = k.cell_start[s + 1];
+        if (sb < 0 || sn <= sb || sn > k.n) continue;  // invalid or empty: no tiles
+        j0 = sb;
+        se = sn;
+        return true;
+    }
+    return false;
+}
+
+// Targets per chunk: a cell's bodies go 64 at a time; a chunk of r < 64 bodies
+// takes tw = the next power of two >= r lanes per source group and G = 64 / tw
+// groups, lane (t, g) = (lane mod tw, lane / tw) summing every G-th source of
+// each tile for target t; the G group sums of a target are added in ascending
+// g through LDS. So a 20-body cell keeps 64 lanes busy instead of 20. The next
+// source tile's global load is issued before the current tile is evaluated.
+template <bool POT, typename Lists>
+__global__ void __launch_bounds__(64) p2p_kernel(P2PArgs k, Lists lists)
+{
+    __shared__ float4 row[64];
+    __shared__ float4 red[64];
+    __shared__ int nbr[27];
+    const int c = blockIdx.x, lane = threadIdx.x;
+    const int tb = k.cell_start[c], te = k.cell_start[c + 1];
+    if (tb < 0 || te < tb || te > k.n) return;
+    if constexpr (__is_same(Lists, GridLists)) lists.nbr = nbr;
+    lists.bind(c);
+    int lo, hi;
+    lists.range(c, lo, hi);
+    const float eps2 = in_vgpr(k.eps2);
+    for (int t0 = tb; t0 < te;) {
+        const int rem = te - t0;
+        int tw = 1, lg = 0;
+        while (tw < rem && tw < 64) {
+            tw <<= 1;
+            ++lg;
+        }
+        const int groups = 64 >> lg;
+        const int t = lane & (tw - 1), g = lane >> lg;
+        const int i = t0 + t;
+        const float4 me = k.pos[i < te ? i : te - 1];
+        Targets<1> tg;
+        tg.x[0] = me.x;
+        tg.y[0] = me.y;
+        tg.z[0] = me.z;
+        Total<1, POT> tot;
+        zero(tot);
+        int e = lo - 1, j0 = 0, se = 0;
+        bool have = next_tile(k, lists, c, hi, e, j0, se);
+        float4 cur = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (have) cur = k.pos[j0 + lane < se ? j0 + lane : se - 1];
+        while (have) {
+            const int cnt = se - j0 < 64 ? se - j0 : 64;
+            const bool in = lane < cnt;
+            // zero-mass padding past the cell end adds exact zeros; the row is
+            // written and read by this wave only (LDS accesses of one wave
+            // execute in order), the wave barriers keep the compiler from moving
+            // them across
+            __builtin_amdgcn_wave_barrier();
+            row[lane] = in ? cur : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            __builtin_amdgcn_wave_barrier();
+            int e2 = e, j2 = j0, se2 = se;
+            const bool have2 = next_tile(k, lists, c, hi, e2, j2, se2);
+            if (have2) cur = k.pos[j2 + lane < se2 ? j2 + lane : se2 - 1];
+            Sums<1, POT> blk;
+            zero(blk);
+            if (groups == 1 && cnt == 64) {
+                // full tile, one target per lane: uniform addresses at constant offsets
+#pragma unroll 16
+                for (int u = 0; u < 64; ++u) interact4<1, POT>(row[u], tg, eps2, blk);
+            } else {
+#pragma unroll 4
+                for (int u0 = 0; u0 < cnt; u0 += groups)
+                    interact4<1, POT>(row[u0 + g], tg, eps2, blk);
+            }
+            add_into(tot, blk);
+            e = e2;
+            j0 = j2;
+            se = se2;
+            have = have2;
+        }
+        const Sums<1, POT> r = result(tot);
+        __builtin_amdgcn_wave_barrier();
+        red[lane] = make_float4(r.ax[0], r.ay[0], r.az[0], POT ? r.p[0] : 0.0f);
+        __builtin_amdgcn_wave_barrier();
+        if (g == 0 && i < te) {
+            float4 a = red[t];
+            for (int gg = 1; gg < groups; ++gg) {
+                const float4 v = red[t + gg * tw];
+                a.x += v.x;
+                a.y += v.y;
+                a.z += v.z;
+                a.w += v.w;
+            }
+            k.acc_out[i] = make_float4(a.x, a.y, a.z, 0.0f);
+            if constexpr (POT) k.pot_out[i] = -a.w;
+        }
+        t0 += tw;
+    }
+}
+
+__device__ __forceinline__ int grid_axis(float x, float lo, float inv_h, int dim)
+{
+    float f = floorf((x - lo) * inv_h);
+    if (!(f >= 0.0f)) f = 0.0f;
+    if (f > (float)(dim - 1)) f = (float)(dim - 1);
+    return (int)f;
+}
+
+__global__ void __launch_bounds__(256) grid_keys_kernel(const float4 *__restrict__ pos, int n,
+                                                        GridSpec g, unsigned *__restrict__ keys,
+                                                        int *__restrict__ idx)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const float4 b = pos[i];
+    const int x = grid_axis(b.x, g.lo[0], g.inv_h, g.dims[0]);
+    const int y = grid_axis(b.y, g.lo[1], g.inv_h, g.dims[1]);
+    const int z = grid_axis(b.z, g.lo[2], g.inv_h, g.dims[2]);
+    keys[i] = (unsigned)((z * g.dims[1] + y) * g.dims[0] + x);
+    idx[i] = i;
+}
+
+__global__ void __launch_bounds__(256) gather_kernel(const float4 *__restrict__ pos,
+                                                     const int *__restrict__ perm, int n,
+                                                     float4 *__restrict__ out)
+{
+    const int k = blockIdx.x * 256 + threadIdx.x;
+    if (k < n) out[k] = pos[perm[k]];
+}
+
+__global__ void __launch_bounds__(256) cell_starts_kernel(const unsigned *__restrict__ keys, int n,
+                                                          int ncell, int *__restrict__ start)
+{
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c > ncell) return;
+    int a = 0, b = n;  // first k in [a, b) with keys[k] >= c
+    while (a < b) {
+        const int m = a + (b - a) / 2;
+        if (keys[m] < (unsigned)c) a = m + 1;
+        else b = m;
+    }
+    start[c] = a;
+}
+
+__global__ void __launch_bounds__(256) scatter_kernel(const float4 *__restrict__ sacc,
+                                                      const float *__restrict__ spot,
+                                                      const int *__restrict__ perm, int n,
+                                                      float4 *__restrict__ acc,
+                                                      float *__restrict__ pot)
+{
+    const int k = blockIdx.x * 256 + threadIdx.x;
+    if (k >= n) return;
+    const int i = perm[k];
+    acc[i] = sacc[k];
+    if (pot) pot[i] = spot[k];
+}
+
 // ---------------------------------------------------------------- SoA layout
 // Separate x, y, z, m arrays (the host layout of the lecture's CPU program,
 // Degawa slide 15) in and out of the 16-byte records the kernels read.
@@ -1007,6 +1235,66 @@ hipError_t launch_small(int tw, bool pot, bool step, const SmallArgs &args, hipS
     SmallArgs a = args;
     void *kargs[] = {&a};
     return hipLaunchKernel(fn, dim3((unsigned)((a.n + tw - 1) / tw)), dim3(256), kargs, 0, stream);
+}
+
+hipError_t launch_p2p(bool pot, const P2PArgs &args, hipStream_t stream)
+{
+    if (args.ncell < 1) return args.ncell == 0 ? hipSuccess : hipErrorInvalidValue;
+    CsrLists l{args.list_off, args.list, args.nlist, args.ncell};
+    P2PArgs a = args;
+    void *k[] = {&a, &l};
+    const void *fn = pot ? (const void *)&p2p_kernel<true, CsrLists>
+                         : (const void *)&p2p_kernel<false, CsrLists>;
+    return hipLaunchKernel(fn, dim3((unsigned)a.ncell), dim3(64), k, 0, stream);
+}
+
+hipError_t launch_p2p_grid(bool pot, const P2PArgs &args, const GridSpec &g, hipStream_t stream)
+{
+    if (args.ncell < 1 || args.ncell != g.dims[0] * g.dims[1] * g.dims[2])
+        return hipErrorInvalidValue;
+    GridLists l{g.dims[0], g.dims[1], g.dims[2], nullptr};
+    P2PArgs a = args;
+    void *k[] = {&a, &l};
+    const void *fn = pot ? (const void *)&p2p_kernel<true, GridLists>
+                         : (const void *)&p2p_kernel<false, GridLists>;
+    return hipLaunchKernel(fn, dim3((unsigned)a.ncell), dim3(64), k, 0, stream);
+}
+
+hipError_t launch_grid_keys(const float4 *pos, int n, const GridSpec &g, unsigned *keys, int *idx,
+                            hipStream_t stream)
+{
+    if (n <= 0) return n == 0 ? hipSuccess : hipErrorInvalidValue;
+    GridSpec gg = g;
+    void *k[] = {&pos, &n, &gg, &keys, &idx};
+    return hipLaunchKernel((const void *)&grid_keys_kernel, dim3((unsigned)((n + 255) / 256)),
+                           dim3(256), k, 0, stream);
+}
+
+hipError_t launch_gather(const float4 *pos, const int *perm, int n, float4 *out,
+                         hipStream_t stream)
+{
+    if (n <= 0) return n == 0 ? hipSuccess : hipErrorInvalidValue;
+    void *k[] = {&pos, &perm, &n, &out};
+    return hipLaunchKernel((const void *)&gather_kernel, dim3((unsigned)((n + 255) / 256)),
+                           dim3(256), k, 0, stream);
+}
+
+hipError_t launch_cell_starts(const unsigned *sorted_keys, int n, int ncell, int *cell_start,
+                              hipStream_t stream)
+{
+    if (ncell < 0 || n < 0) return hipErrorInvalidValue;
+    void *k[] = {&sorted_keys, &n, &ncell, &cell_start};
+    return hipLaunchKernel((const void *)&cell_starts_kernel,
+                           dim3((unsigned)((ncell + 1 + 255) / 256)), dim3(256), k, 0, stream);
+}
+
+hipError_t launch_scatter(const float4 *sacc, const float *spot, const int *perm, int n,
+                          float4 *acc, float *pot, hipStream_t stream)
+{
+    if (n <= 0) return n == 0 ? hipSuccess : hipErrorInvalidValue;
+    void *k[] = {&sacc, &spot, &perm, &n, &acc, &pot};
+    return hipLaunchKernel((const void *)&scatter_kernel, dim3((unsigned)((n + 255) / 256)),
+                           dim3(256), k, 0, stream);
 }
 
 hipError_t launch_pack(const float *a, const float *b, const float *c, const float *d, int n,

@@ -181,6 +181,44 @@ int nbody_accel_soa(const float *x, const float *y, const float *z, const float 
 int nbody_step_soa(float *x, float *y, float *z, const float *m, float *vx, float *vy, float *vz,
                    int64_t N, float dt, float eps2, int64_t nsteps, hipStream_t stream);
 
+/*
+ * nbody_p2p - the all-pairs sum restricted to cell interaction lists: the near
+ * field of a hierarchical method (GPU Gems 3 ch. 31 study page, section 6;
+ * Nakasato "スライド 1", No.34), with the lists a tree or grid code provides.
+ *   pos_xyzm   : N bodies grouped by cell: cell c owns [cell_start[c], cell_start[c+1]).
+ *   cell_start : ncell + 1 device ints, non-decreasing, within [0, N].
+ *   list_off, cells : CSR lists, device ints: target cell c interacts with
+ *                cells[list_off[c]] .. cells[list_off[c+1] - 1] (list_off has
+ *                ncell + 1 non-decreasing entries within [0, nlist]).
+ *   acc_out, pot_out : per body inside a cell range, the sums over the bodies of
+ *                the listed cells (a cell listing itself includes j = i, whose
+ *                term is the softened self term as in nbody_accel); bodies
+ *                outside every cell range are not written.
+ * List entries outside [0, ncell) add nothing. The index arrays are read on the
+ * device, so their contents are not checked on the host; the kernel checks every
+ * range and entry before use (an invalid cell range is skipped, an invalid list
+ * range is empty), so malformed lists cannot make it read or write out of bounds.
+ * Results within the error bound of nbody_accel over the same terms; fixed order.
+ */
+int nbody_p2p(const nbody_f4 *pos_xyzm, int64_t N, float eps2, const int32_t *cell_start,
+              int32_t ncell, const int32_t *list_off, const int32_t *cells, int64_t nlist,
+              nbody_f4 *acc_out, float *pot_out, hipStream_t stream);
+
+/*
+ * nbody_near_grid - near field on a uniform grid: dims[0] x dims[1] x dims[2]
+ * cubic cells of side h from the corner lo (host arrays); body i is in cell
+ * clamp(floor((x_d - lo_d) * (1/h)), 0, dims_d - 1) per axis (float arithmetic,
+ * bodies outside the box join the boundary cells), and gets the sum over every
+ * body in its own and the 26 neighbouring cells (itself included). The library
+ * bins the bodies (stable radix sort of the cell indices, so a cell keeps its
+ * bodies in their input order), runs the nbody_p2p kernel with the 27-cell
+ * neighbourhoods and writes acc_out / pot_out in the caller's body order.
+ * At most 2^28 cells. Scratch: ~N x 56 bytes + 4 bytes per cell + the sort's.
+ */
+int nbody_near_grid(const nbody_f4 *pos_xyzm, int64_t N, float eps2, const float lo[3], float h,
+                    const int32_t dims[3], nbody_f4 *acc_out, float *pot_out,
+                    hipStream_t stream);
+
 /* Conserved-quantity diagnostics of a state (nbody_diagnostics), in fp64. */
 typedef struct nbody_diag {
     double kinetic;             /* K = sum m |v|^2 / 2 */

@@ -151,6 +151,48 @@ def test_soa_zero_work_is_a_no_op(nb):
                              1e-4, 0, stream=0, check=False) == nb.NBODY_OK
 
 
+@pytest.mark.parametrize("bad,code", [
+    (dict(n=-1), 1), (dict(ncell=-1), 1), (dict(nlist=-1), 1), (dict(nlist=2**31), 1),
+    (dict(pos=None), 1), (dict(acc=None), 1), (dict(cs=None), 1), (dict(lo=None), 1),
+    (dict(cells=None), 1), (dict(eps2=0.0), 1), (dict(pos=A + 8), 2), (dict(cs=C + 2), 2),
+    (dict(pot=B + 4096 + 1), 2), (dict(acc=A + 16), 1), (dict(acc=C), 1),
+    (dict(pot=B + 64), 1),
+])
+def test_p2p_rejects(nb, bad, code):
+    a = dict(pos=A, n=16, eps2=1e-4, cs=C, ncell=4, lo=C + 4096, cells=C + 8192, nlist=10, acc=B,
+             pot=None)
+    a.update(bad)
+    rc = nb.nbody_p2p(a["pos"], a["n"], a["eps2"], a["cs"], a["ncell"], a["lo"], a["cells"],
+                      a["nlist"], a["acc"], a["pot"], stream=0, check=False)
+    assert rc == code, bad
+    assert nb.nbody_last_error() != ""
+
+
+def test_p2p_nothing_to_do(nb):
+    assert nb.nbody_p2p(None, 0, 1e-4, None, 0, None, None, 0, None, stream=0,
+                        check=False) == nb.NBODY_OK
+    assert nb.nbody_p2p(A, 16, 1e-4, None, 0, None, None, 0, B, stream=0,
+                        check=False) == nb.NBODY_OK
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(n=-1), 1), (dict(dims=(0, 4, 4)), 1), (dict(dims=(4, -1, 4)), 1),
+    (dict(dims=(1 << 10, 1 << 10, 1 << 9)), 1), (dict(lo=(0.0, math.nan, 0.0)), 1),
+    (dict(lo=(math.inf, 0.0, 0.0)), 1), (dict(h=0.0), 1), (dict(h=-1.0), 1),
+    (dict(h=math.inf), 1), (dict(h=1e-39), 1), (dict(pos=None), 1), (dict(acc=None), 1),
+    (dict(eps2=-1.0), 1), (dict(pos=A + 4), 2), (dict(acc=B + 4), 2), (dict(pot=C + 2), 2),
+    (dict(acc=A + 64), 1), (dict(pot=A), 1), (dict(lo=None), 1), (dict(dims=None), 1),
+])
+def test_near_grid_rejects(nb, bad, code):
+    a = dict(pos=A, n=16, eps2=1e-4, lo=(-1.0, -1.0, -1.0), h=0.5, dims=(4, 4, 4), acc=B,
+             pot=None)
+    a.update(bad)
+    rc = nb.nbody_near_grid(a["pos"], a["n"], a["eps2"], a["lo"], a["h"], a["dims"], a["acc"],
+                            a["pot"], stream=0, check=False)
+    assert rc == code, bad
+    assert nb.nbody_last_error() != ""
+
+
 def test_plan_rejects_bad_fields(nb):
     for plan in (dict(bcast=7), dict(tpl=3), dict(splits=-1), dict(splits=5000), dict(mode=4),
                  dict(mode=3, tpl=2), dict(mode=3, tpl=64), dict(mode=3, splits=2),
