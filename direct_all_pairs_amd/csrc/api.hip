@@ -222,6 +222,9 @@ void auto_plan(int64_t n, const DeviceFacts &dev, nbody_plan *p)
 // Final chunking. Tiles: chunk is a whole number of tiles (LDS tile or
 // accumulation block) and S = ceil(N / chunk), so no chunk is empty. Pairs:
 // splits = number of bands = number of partial slots, chunk = band.
+// Grid limit of the second launch dimension (pair items, split-j chunks).
+constexpr int64_t kMaxGridY = 65535;
+
 void finish_plan(int64_t n, nbody_plan *p)
 {
     if (p->mode == NBODY_MODE_SMALL) {
@@ -286,6 +289,10 @@ int make_plan(int64_t n, const nbody_plan *user, int *dev_out, nbody_plan *p)
     if (rc != NBODY_OK) return rc;
     auto_plan(n, facts, p);
     finish_plan(n, p);
+    if (p->mode == NBODY_MODE_PAIRS && p->splits / 2 + 1 > kMaxGridY)
+        return fail(NBODY_EINVAL, "N=%lld needs %d bands of %d bodies: more than the launch "
+                                  "grid takes (use a larger band or tiles mode)",
+                    (long long)n, (int)p->splits, (int)p->band);
     *dev_out = dev;
     return NBODY_OK;
 }
@@ -303,10 +310,9 @@ int check_n(int64_t n)
     return NBODY_OK;
 }
 
-// Enqueue one evaluation: accelerations (and potentials) into acc_out/pot_out,
-// or with euler_pos/euler_vel set, one Euler step applied to them instead.
 // Enqueue one evaluation: acc/pot into acc_out/pot_out, or with euler_pos and
-// euler_vel set, one Euler step applied to them instead.
+// euler_vel set, one Euler step applied to them in place (tiles and pairs
+// modes; small-mode steps alternate buffers and go through enqueue_steps).
 int enqueue_eval(const float4 *pos, int n, float eps2, float4 *acc_out, float *pot_out,
                  const nbody_plan &p, int dev, hipStream_t stream, float4 *euler_pos,
                  float4 *euler_vel, float dt)
@@ -315,7 +321,7 @@ int enqueue_eval(const float4 *pos, int n, float eps2, float4 *acc_out, float *p
     const bool step = euler_pos != nullptr;
     const bool pairs = p.mode == NBODY_MODE_PAIRS;
     if (p.mode == NBODY_MODE_SMALL) {
-        // steps of this mode go through enqueue_small_step
+        if (step) return fail(NBODY_EINVAL, "internal: small-mode steps go through enqueue_steps");
         nbk::SmallArgs sa{pos, n, eps2, acc_out, pot_out, nullptr, nullptr, 0.0f};
         hipError_t e = nbk::launch_small(p.tpl, pot, false, sa, stream);
         return e == hipSuccess ? NBODY_OK : hip_fail(e, "small kernel launch");

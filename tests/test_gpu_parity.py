@@ -262,6 +262,15 @@ def test_pairs_invariants(nb, tpl):
     assert np.array_equal(b1, b2) and np.array_equal(q1, q2)
 
 
+def test_pairs_plan_beyond_grid_limit_rejected(nb):
+    """A pair plan whose band count exceeds the launch grid is rejected before anything is
+    allocated or launched (fake, aligned pointers: nothing is dereferenced)."""
+    n = 512 * 131072 + 1
+    rc = nb.nbody_accel_plan(1 << 20, n, 1e-4, 1 << 40, None, plan=dict(mode="pairs", band=512),
+                             stream=0, check=False)
+    assert rc == nb.NBODY_EINVAL and "grid" in nb.nbody_last_error()
+
+
 def test_auto_plan_modes(nb):
     """Small-N kernel up to N = 8192, tiles above, pair-symmetric bands from N = 65536 up
     (scratch permitting)."""
