@@ -18,6 +18,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 from pathlib import Path
@@ -44,10 +45,19 @@ def tile_global_loads(n: int, p: int) -> int:
     return n * n // p
 
 
+def code_tokens(text: str) -> str:
+    """C++ source without comments and whitespace runs: what the compiler sees, so that a
+    comment-only edit does not count as a kernel change (string literals hold no comment
+    markers in these files)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        h.update(f.read_bytes())
+        h.update(code_tokens(f.read_text()).encode())
     return h.hexdigest()[:16]
 
 
