@@ -289,6 +289,57 @@ def test_auto_plan_modes(nb):
     assert p.mode == nb.MODE_PAIRS and p.band == 1024 and p.splits == 293
 
 
+# ------------------------------------------------------------------ degenerate inputs
+
+MODE_PLANS = [dict(mode="small", tpl=8), dict(bcast="lds", tpl=1, wg=256, splits=3),
+              dict(mode="pairs", band=512, tpl=8)]
+
+
+@pytest.mark.parametrize("plan", MODE_PLANS, ids=["small", "tiles", "pairs"])
+def test_zero_masses_give_exact_zeros(nb, plan):
+    pos, _ = _bodies(1500, 61)
+    pos = pos.copy()
+    pos[:, 3] = 0.0
+    acc, pot = gpu_accel(pos, 1e-4, plan=plan)
+    assert np.all(acc == 0.0) and np.all(pot == 0.0)
+
+
+@pytest.mark.parametrize("plan", MODE_PLANS, ids=["small", "tiles", "pairs"])
+def test_coincident_bodies(nb, plan):
+    """Every body at one point: every separation is zero, so a = 0 exactly and
+    p_i = -sum_j m_j / eps (to the potential bound)."""
+    n = 1300
+    pos = np.zeros((n, 4), np.float32)
+    pos[:, :3] = np.float32(0.375)
+    pos[:, 3] = (0.5 + np.random.default_rng(3).random(n)).astype(np.float32)
+    acc, pot = gpu_accel(pos, 0.25, plan=plan)
+    assert np.all(acc == 0.0)
+    want = -float(np.sum(pos[:, 3].astype(np.float64))) / 0.5
+    assert np.all(np.abs(pot - want) <= TOL * abs(want))
+
+
+@pytest.mark.parametrize("plan", MODE_PLANS, ids=["small", "tiles", "pairs"])
+def test_nan_input_propagates_without_error(nb, plan):
+    """Inputs are not checked per body: a NaN position reaches every body's sum (it is a
+    source for all of them); the call itself succeeds."""
+    pos, _ = _bodies(1200, 62)
+    pos = pos.copy()
+    pos[17, 0] = np.nan
+    acc, pot = gpu_accel(pos, 1e-4, plan=plan)
+    assert np.all(np.isnan(acc[:, 0])) and np.all(np.isnan(pot))
+
+
+@pytest.mark.parametrize("plan", MODE_PLANS, ids=["small", "tiles", "pairs"])
+def test_negative_dt_step(nb, plan):
+    """dt < 0 is allowed: one step with -dt is the oracle's step with -dt."""
+    import oracle
+
+    pos, vel = _bodies(900, 63)
+    x1, v1 = gpu_step(pos, vel, -1e-3, 1e-4, 1, plan=plan)
+    assert_step_parity(pos, vel, x1, v1, -1e-3, oracle.accel(pos, np.float32(1e-4)),
+                       what=f"negative dt {plan}")
+
+
 # ------------------------------------------------------------------ SoA entry points
 
 def _soa(t):
