@@ -618,10 +618,14 @@ __device__ __forceinline__ void pair_step(float jx, float jy, float jz, float jm
         bz[t] = __builtin_fmaf(sj, dz, bz[t]);
         if constexpr (POT) bp[t] = __builtin_fmaf(jm, inv, bp[t]);
         if constexpr (SYM) {
+            // the partner's sums are kept with the sign of r_ij (a_j = -sum): plain
+            // multiplies and FMAs, no negated operand; the sign is applied once per
+            // j-block when the sums go into the band accumulator (bit-identical,
+            // since fma(-a, b, c) = -fma(a, b, -c) in round-to-nearest)
             const float si = tm[t] * inv3;  // m_i / r^3
-            gx = __builtin_fmaf(-si, dx, gx);
-            gy = __builtin_fmaf(-si, dy, gy);
-            gz = __builtin_fmaf(-si, dz, gz);
+            gx = __builtin_fmaf(si, dx, gx);
+            gy = __builtin_fmaf(si, dy, gy);
+            gz = __builtin_fmaf(si, dz, gz);
             if constexpr (POT) gp = __builtin_fmaf(tm[t], inv, gp);
         }
     }
@@ -712,9 +716,9 @@ __device__ __forceinline__ void pairs_item(const PairsArgs &k, int A, int B, int
             if constexpr (SYM) {
                 const float4 g = sh.jsum[w][lane];
                 float4 o = sh.jacc[jb * 64 + lane];
-                o.x += g.x;
-                o.y += g.y;
-                o.z += g.z;
+                o.x -= g.x;
+                o.y -= g.y;
+                o.z -= g.z;
                 o.w += g.w;
                 sh.jacc[jb * 64 + lane] = o;
             }
