@@ -88,9 +88,12 @@ struct GridSpec {
     int dims[3];
 };
 
-hipError_t launch_p2p(bool pot, const P2PArgs &args, hipStream_t stream);
-// The same kernel with the 27 neighbour cells of the grid as every cell's list.
-hipError_t launch_p2p_grid(bool pot, const P2PArgs &args, const GridSpec &g, hipStream_t stream);
+// wide: one 256-thread workgroup per cell sharing 256-body source tiles (large
+// cells); otherwise one wave per cell (small cells).
+hipError_t launch_p2p(bool pot, bool wide, const P2PArgs &args, hipStream_t stream);
+// The same kernels with the 27 neighbour cells of the grid as every cell's list.
+hipError_t launch_p2p_grid(bool pot, bool wide, const P2PArgs &args, const GridSpec &g,
+                           hipStream_t stream);
 // keys[i] = linear cell of body i, idx[i] = i.
 hipError_t launch_grid_keys(const float4 *pos, int n, const GridSpec &g, unsigned *keys, int *idx,
                             hipStream_t stream);

@@ -1035,7 +1035,8 @@ __global__ void __launch_bounds__(64) p2p_kernel(P2PArgs k, Lists lists)
             // execute in order), the wave barriers keep the compiler from moving
             // them across
             __builtin_amdgcn_wave_barrier();
-            row[lane] = in ? cur : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            row[lane] = make_float4(in ? cur.x : 0.0f, in ? cur.y : 0.0f, in ? cur.z : 0.0f,
+                                    in ? cur.w : 0.0f);
             __builtin_amdgcn_wave_barrier();
             int e2 = e, j2 = j0, se2 = se;
             const bool have2 = next_tile(k, lists, c, hi, e2, j2, se2);
@@ -1074,6 +1075,99 @@ __global__ void __launch_bounds__(64) p2p_kernel(P2PArgs k, Lists lists)
             if constexpr (POT) k.pot_out[i] = -a.w;
         }
         t0 += tw;
+    }
+}
+
+// Large cells: one 256-thread workgroup per target cell, 256 targets per chunk
+// (one per thread), source tiles of 256 bodies staged once for all four waves
+// (double-buffered, one barrier per tile: the barrier after a tile both
+// publishes the next buffer and guards the one about to be overwritten), read
+// with uniform addresses. The cursor over (list entry, tile) is uniform.
+template <typename Lists>
+__device__ __forceinline__ bool next_tile256(const P2PArgs &k, const Lists &lists, int c, int hi,
+                                             int &e, int &j0, int &se)
+{
+    if (j0 + 256 < se) {
+        j0 += 256;
+        return true;
+    }
+#pragma unroll 1
+    for (++e; e < hi; ++e) {
+        const int s = lists.cell(e, c);
+        if (s < 0) continue;
+        const int sb = k.cell_start[s], sn = k.cell_start[s + 1];
+        if (sb < 0 || sn <= sb || sn > k.n) continue;
+        j0 = sb;
+        se = sn;
+        return true;
+    }
+    return false;
+}
+
+template <bool POT, typename Lists>
+__global__ void __launch_bounds__(256) p2p_wg_kernel(P2PArgs k, Lists lists)
+{
+    __shared__ float4 tile[2][256];
+    __shared__ int nbr[27];
+    const int c = blockIdx.x, tid = threadIdx.x;
+    const int tb = k.cell_start[c], te = k.cell_start[c + 1];
+    if (tb < 0 || te < tb || te > k.n) return;
+    if constexpr (__is_same(Lists, GridLists)) lists.nbr = nbr;
+    lists.bind(c);
+    int lo, hi;
+    lists.range(c, lo, hi);
+    const float eps2 = in_vgpr(k.eps2);
+    for (int t0 = tb; t0 < te; t0 += 256) {
+        const int i = t0 + tid;
+        const float4 me = k.pos[i < te ? i : te - 1];
+        Targets<1> tg;
+        tg.x[0] = me.x;
+        tg.y[0] = me.y;
+        tg.z[0] = me.z;
+        Total<1, POT> tot;
+        zero(tot);
+        int e = lo - 1, j0 = 0, se = 0;
+        bool have = next_tile256(k, lists, c, hi, e, j0, se);
+        if (have) tile[0][tid] = load_or_zero(k.pos, j0 + tid, se);
+        __syncthreads();
+        int buf = 0;
+        while (have) {
+            const int cnt = se - j0 < 256 ? se - j0 : 256;
+            int e2 = e, j2 = j0, se2 = se;
+            const bool have2 = next_tile256(k, lists, c, hi, e2, j2, se2);
+            const int jn = j2 + tid;
+            float4 r = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (have2) r = k.pos[jn < se2 ? jn : se2 - 1];  // raw prefetch of the next tile
+            const float4 *tl = tile[buf];
+            Sums<1, POT> blk;
+            zero(blk);
+            if (cnt == 256) {
+                // full tile: uniform addresses at constant offsets
+#pragma unroll 16
+                for (int u = 0; u < 256; ++u) interact4<1, POT>(tl[u], tg, eps2, blk);
+            } else {
+#pragma unroll 8
+                for (int u = 0; u < cnt; ++u) interact4<1, POT>(tl[u], tg, eps2, blk);
+            }
+            add_into(tot, blk);
+            if (have2) {
+                const bool in = jn < se2;  // per-component select: a float4 ternary would
+                                           // go through private memory
+                tile[buf ^ 1][tid] = make_float4(in ? r.x : 0.0f, in ? r.y : 0.0f,
+                                                 in ? r.z : 0.0f, in ? r.w : 0.0f);
+            }
+            __syncthreads();
+            buf ^= 1;
+            e = e2;
+            j0 = j2;
+            se = se2;
+            have = have2;
+        }
+        if (i < te) {
+            const Sums<1, POT> res = result(tot);
+            k.acc_out[i] = make_float4(res.ax[0], res.ay[0], res.az[0], 0.0f);
+            if constexpr (POT) k.pot_out[i] = -res.p[0];
+        }
     }
 }
 
@@ -1247,27 +1341,33 @@ hipError_t launch_small(int tw, bool pot, bool step, const SmallArgs &args, hipS
     return hipLaunchKernel(fn, dim3((unsigned)((a.n + tw - 1) / tw)), dim3(256), kargs, 0, stream);
 }
 
-hipError_t launch_p2p(bool pot, const P2PArgs &args, hipStream_t stream)
+template <typename Lists>
+hipError_t launch_p2p_any(bool pot, bool wide, const P2PArgs &args, Lists l, hipStream_t stream)
 {
-    if (args.ncell < 1) return args.ncell == 0 ? hipSuccess : hipErrorInvalidValue;
-    CsrLists l{args.list_off, args.list, args.nlist, args.ncell};
     P2PArgs a = args;
     void *k[] = {&a, &l};
-    const void *fn = pot ? (const void *)&p2p_kernel<true, CsrLists>
-                         : (const void *)&p2p_kernel<false, CsrLists>;
-    return hipLaunchKernel(fn, dim3((unsigned)a.ncell), dim3(64), k, 0, stream);
+    const void *fn;
+    if (wide)
+        fn = pot ? (const void *)&p2p_wg_kernel<true, Lists> : (const void *)&p2p_wg_kernel<false, Lists>;
+    else
+        fn = pot ? (const void *)&p2p_kernel<true, Lists> : (const void *)&p2p_kernel<false, Lists>;
+    return hipLaunchKernel(fn, dim3((unsigned)a.ncell), dim3(wide ? 256 : 64), k, 0, stream);
 }
 
-hipError_t launch_p2p_grid(bool pot, const P2PArgs &args, const GridSpec &g, hipStream_t stream)
+hipError_t launch_p2p(bool pot, bool wide, const P2PArgs &args, hipStream_t stream)
+{
+    if (args.ncell < 1) return args.ncell == 0 ? hipSuccess : hipErrorInvalidValue;
+    return launch_p2p_any(pot, wide, args, CsrLists{args.list_off, args.list, args.nlist, args.ncell},
+                          stream);
+}
+
+hipError_t launch_p2p_grid(bool pot, bool wide, const P2PArgs &args, const GridSpec &g,
+                           hipStream_t stream)
 {
     if (args.ncell < 1 || args.ncell != g.dims[0] * g.dims[1] * g.dims[2])
         return hipErrorInvalidValue;
-    GridLists l{g.dims[0], g.dims[1], g.dims[2], nullptr};
-    P2PArgs a = args;
-    void *k[] = {&a, &l};
-    const void *fn = pot ? (const void *)&p2p_kernel<true, GridLists>
-                         : (const void *)&p2p_kernel<false, GridLists>;
-    return hipLaunchKernel(fn, dim3((unsigned)a.ncell), dim3(64), k, 0, stream);
+    return launch_p2p_any(pot, wide, args, GridLists{g.dims[0], g.dims[1], g.dims[2], nullptr},
+                          stream);
 }
 
 hipError_t launch_grid_keys(const float4 *pos, int n, const GridSpec &g, unsigned *keys, int *idx,

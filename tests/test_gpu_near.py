@@ -54,9 +54,11 @@ def _cells(n, ncell, seed):
     return np.concatenate([[0], cuts, [n]]).astype(np.int32)
 
 
-@pytest.mark.parametrize("n,ncell", [(1, 1), (70, 3), (1000, 17), (3001, 40)])
+@pytest.mark.parametrize("n,ncell", [(1, 1), (70, 3), (1000, 17), (3001, 40), (3001, 10),
+                                     (5000, 4)])
 def test_p2p_full_lists_equal_direct_sum(nb, n, ncell):
-    """Every cell listing every cell: the near field is the whole direct sum."""
+    """Every cell listing every cell: the near field is the whole direct sum (cells of up to
+    ~75 bodies on average run one wave per cell, larger ones the 256-thread kernel)."""
     import oracle
 
     pos, _ = workloads.random_bodies(n, seed=1000 + n)
@@ -188,3 +190,16 @@ def test_near_grid_deterministic_and_order_free(nb):
     inv = np.empty_like(perm)
     inv[perm] = np.arange(5000)
     assert_accel_parity(a3[inv], p3[inv], ref, what="permuted input")
+
+
+def test_near_grid_few_large_cells(nb):
+    """64 cells of ~780 bodies: the shared-tile 256-thread kernel, several target chunks and
+    source tiles per cell; sampled targets against the grid definition."""
+    import oracle
+
+    pos, _ = workloads.random_bodies(50000, seed=51)
+    args = ((-1.0, -1.0, -1.0), 0.5, (4, 4, 4))
+    acc, pot = gpu_near_grid(nb, pos, 1e-4, *args)
+    idx = np.unique(np.random.default_rng(6).integers(0, 50000, 1500))
+    ref = oracle.near_grid(pos, 1e-4, *args, targets=idx)
+    assert_accel_parity(acc, pot, ref, idx=idx, what="few large cells")
