@@ -564,34 +564,40 @@ __device__ __forceinline__ float4 body_or_zero(const float4 *__restrict__ pos, i
 }
 
 // Large i-sets or bands sum an i-set across waves sequentially through the
-// j-block buffer (keeps 2048-body bands at four workgroups per CU at T = 4);
-// small ones, whose occupancy is set by registers, use a one-pass buffer with
-// two barriers.
+// block and slot rows (keeps 2048-body bands at 40 KiB of LDS, four workgroups
+// per CU); small ones, whose occupancy is set by registers, use a one-pass
+// buffer with two barriers.
 template <int T, int BD>
 constexpr bool kSeqReduce = BD >= 2048 || T >= 8;
 
-// Entries per wave row of the j-block and slot arrays: one 64-body block, or,
-// for the sequential i-set sum, the wave's quarter of the 64*T sums. Rows are
-// whole multiples of the 1 KiB block, so a row base ORs onto a block offset.
-template <int T>
-constexpr int kRowLen = 16 * T > 64 ? 16 * T : 64;
+// Entries per wave row of the j-block and slot arrays: one 64-body block
+// (1 KiB, so a row base ORs onto a block offset). The sequential i-set sum
+// uses both arrays as one buffer of 8 blocks, enough for 64*T sums at T <= 8.
+constexpr int kRowLen = 64;
 constexpr int kBlkBytes = 64 * (int)sizeof(float4);
+
+// With 8 targets per lane the targets' sums run over the wave's whole share of
+// the i-set's j-blocks (no per-j-block partials): 32 fewer registers, which
+// brings the kernel to 128 and four waves per SIMD. The slot combine is
+// compensated, so the longer fp32 sums stay far inside the error bound.
+template <int T>
+constexpr bool kFlatSums = T >= 8;
 
 template <int T, int BD, bool SEQ = kSeqReduce<T, BD>>
 struct PairsShared {
-    float4 jacc[BD];             // B-side sums of the item, one per body of band B
-    float4 jblk[4][kRowLen<T>];  // each wave's copy of its current j-block
-    float4 jsum[4][kRowLen<T>];  // each wave's B-side sums of that block, by block index
-    float4 ired[4][64 * T];      // per-wave A-side sums of the current i-set
+    float4 jacc[BD];          // B-side sums of the item, one per body of band B
+    float4 jblk[4][kRowLen];  // each wave's copy of its current j-block
+    float4 jsum[4][kRowLen];  // each wave's B-side sums of that block, by block index
+    float4 ired[4][64 * T];   // per-wave A-side sums of the current i-set
 };
 
 template <int T, int BD>
 struct PairsShared<T, BD, true> {
-    float4 jacc[BD];             // B-side sums of the item, one per body of band B
-    float4 jblk[4][kRowLen<T>];  // each wave's copy of its current j-block; between
-                                 // i-sets, the running cross-wave sum of the i-set's
-                                 // A-side sums
-    float4 jsum[4][kRowLen<T>];  // each wave's B-side sums of its block, by block index
+    float4 jacc[BD];          // B-side sums of the item, one per body of band B
+    float4 jblk[4][kRowLen];  // each wave's copy of its current j-block; between
+                              // i-sets, with jsum, the running cross-wave sum of
+                              // the i-set's A-side sums
+    float4 jsum[4][kRowLen];  // each wave's B-side sums of its block, by block index
 };
 
 // One step: partner (jx, jy, jz, jm) against the lane's T targets. b* gather
@@ -645,13 +651,18 @@ __device__ __forceinline__ void pairs_item(const PairsArgs &k, int A, int B, int
     constexpr int NIS = BD / (64 * T);  // i-sets per band
     constexpr int NJB = BD / 64;        // j-blocks per band
     static_assert(NIS >= 1 && NJB % W == 0, "band must hold whole i-sets and j-blocks");
-    static_assert(sizeof(sh.jblk[0]) % kBlkBytes == 0 && sizeof(sh.jsum[0]) == sizeof(sh.jblk[0]),
-                  "rows must be whole blocks of equal size");
+    static_assert(sizeof(sh.jblk[0]) == kBlkBytes && sizeof(sh.jsum[0]) == kBlkBytes,
+                  "rows must be one block each");
+    static_assert(!kSeqReduce<T, BD> || 64 * T <= 2 * W * kRowLen,
+                  "the sequential i-set sum must fit the block and slot rows");
+    constexpr bool FLAT = kFlatSums<T>;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int row = w * (int)sizeof(sh.jblk[0]);  // byte offset of the wave's row
     for (int is = 0; is < NIS; ++is) {
         float tx[T], ty[T], tz[T], tm[T];
+        // i-set sums (a*) and, unless FLAT, the current j-block's partials (b*)
         float ax[T], ay[T], az[T], ap[T];
+        float bx[T], by[T], bz[T], bp[T];
 #pragma unroll
         for (int t = 0; t < T; ++t) {
             const float4 b = body_or_zero(k.pos, k.n, (long long)A * BD + is * 64 * T + t * 64 + lane);
@@ -660,6 +671,7 @@ __device__ __forceinline__ void pairs_item(const PairsArgs &k, int A, int B, int
             tz[t] = b.z;
             tm[t] = b.w;
             ax[t] = ay[t] = az[t] = ap[t] = 0.0f;
+            bx[t] = by[t] = bz[t] = bp[t] = 0.0f;
         }
         float4 jnext = body_or_zero(k.pos, k.n, (long long)B * BD + w * 64 + lane);
         for (int jb = w; jb < NJB; jb += W) {
@@ -674,9 +686,10 @@ __device__ __forceinline__ void pairs_item(const PairsArgs &k, int A, int B, int
             if constexpr (SYM) sh.jsum[w][lane] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             __builtin_amdgcn_wave_barrier();
             float jx = jbody.x, jy = jbody.y, jz = jbody.z, jm = jbody.w;
-            float bx[T], by[T], bz[T], bp[T];
+            if constexpr (!FLAT) {
 #pragma unroll
-            for (int t = 0; t < T; ++t) bx[t] = by[t] = bz[t] = bp[t] = 0.0f;
+                for (int t = 0; t < T; ++t) bx[t] = by[t] = bz[t] = bp[t] = 0.0f;
+            }
             int cur = row | (lane * (int)sizeof(float4));  // byte offset of entry (lane - step) mod 64
             // two steps per trip (no register copies of the partner) except where
             // measured slower: 4 targets per lane in 2048-body bands
@@ -706,12 +719,14 @@ __device__ __forceinline__ void pairs_item(const PairsArgs &k, int A, int B, int
                 jm = nb4.w;
                 cur = nxt;
             }
+            if constexpr (!FLAT) {
 #pragma unroll
-            for (int t = 0; t < T; ++t) {
-                ax[t] += bx[t];
-                ay[t] += by[t];
-                az[t] += bz[t];
-                ap[t] += bp[t];
+                for (int t = 0; t < T; ++t) {
+                    ax[t] += bx[t];
+                    ay[t] += by[t];
+                    az[t] += bz[t];
+                    ap[t] += bp[t];
+                }
             }
             if constexpr (SYM) {
                 const float4 g = sh.jsum[w][lane];
@@ -721,6 +736,15 @@ __device__ __forceinline__ void pairs_item(const PairsArgs &k, int A, int B, int
                 o.z -= g.z;
                 o.w += g.w;
                 sh.jacc[jb * 64 + lane] = o;
+            }
+        }
+        if constexpr (FLAT) {
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                ax[t] = bx[t];
+                ay[t] = by[t];
+                az[t] = bz[t];
+                ap[t] = bp[t];
             }
         }
         // Cross-wave sum of the i-set, in wave order ((w0 + w1) + w2) + w3 either way.
@@ -742,8 +766,8 @@ __device__ __forceinline__ void pairs_item(const PairsArgs &k, int A, int B, int
             __syncthreads();
             continue;
         }
-        // Sequential form through the j-block buffer (all waves are past their
-        // j-blocks at the barrier); wave W-1 stores the total.
+        // Sequential form through the block and slot rows (all waves are past
+        // their j-blocks at the barrier); wave W-1 stores the total.
         float4 *red = &sh.jblk[0][0];
         __syncthreads();
         for (int ww = 0; ww < W; ++ww) {
