@@ -103,6 +103,60 @@ def cpu_baseline(pos_h, eps2, budget_s: float):
     }
 
 
+class ClockSampler:
+    """Samples the GPU's shader clocks with `amd-smi metric -c --json` (a child process, one
+    call after another) while the benchmark runs; each sample is the mean of the per-XCD gfx
+    clocks in MHz. Nothing is sampled where amd-smi is missing or prints no clocks."""
+
+    def __init__(self):
+        import threading
+
+        self.samples: list[float] = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _one(self):
+        import subprocess
+
+        r = subprocess.run(["amd-smi", "metric", "-c", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        txt = r.stdout[r.stdout.find("{") if r.stdout.lstrip()[:1] != "[" else 0:]
+        d = json.loads(txt)
+        g = d[0] if isinstance(d, list) else d.get("gpu_data", [d])[0]
+        clk = [v["clk"]["value"] for k, v in g["clock"].items()
+               if k.startswith("gfx") and isinstance(v.get("clk"), dict)
+               and isinstance(v["clk"].get("value"), (int, float))]
+        return sum(clk) / len(clk) if clk else None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                v = self._one()
+            except Exception:
+                return
+            if v is not None and not self._stop.is_set():
+                self.samples.append(float(v))
+            self._stop.wait(0.2)
+
+    def __enter__(self):
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join(timeout=30)
+
+    def summary(self, pct_at_nominal: float):
+        if not self.samples:
+            return None
+        v = sorted(self.samples)
+        med = v[len(v) // 2]
+        return {"median_mhz": round(med), "min_mhz": round(v[0]), "max_mhz": round(v[-1]),
+                "samples": len(v), "source": "amd-smi metric -c, mean of the XCD gfx clocks, "
+                "sampled during warm-up and timed steps",
+                "pct_fp32_peak_at_measured_sclk": round(pct_at_nominal * 2400.0 / med, 2)}
+
+
 def copy_calibration(nbytes: int) -> int:
     """A plain copy of known size: reads and writes nbytes once per launch."""
     import torch
@@ -245,6 +299,8 @@ def main(argv=None) -> int:
     ap.add_argument("--near-grid", type=int, default=0, metavar="D",
                     help="only time nbody_near_grid on a D^3 grid over [-1, 1]^3 (near field; "
                          "prints its own JSON line, no contract line)")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="do not sample the shader clock with amd-smi during the run")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (twice) and exit; "
                          "used to scale the HBM byte counters of rocprofv3")
@@ -297,6 +353,9 @@ def main(argv=None) -> int:
         return near_grid_bench(nb, w, pos, args)
 
     diag0 = nb.diagnostics(pos, vel, float(w.eps2)) if stepping else None
+    clock = ClockSampler()
+    if not args.no_clock:
+        clock.__enter__()
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
@@ -311,6 +370,8 @@ def main(argv=None) -> int:
         ends[k].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if not args.no_clock:
+        clock.__exit__()
     ev_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
 
     n_int = interactions(n) * evals_per_step
@@ -347,6 +408,7 @@ def main(argv=None) -> int:
         },
         "gflops_at_20": round(FLOPS_PER_INTERACTION * value, 1),
         "pct_fp32_peak": round(100 * FLOPS_PER_INTERACTION * value / 1e3 / FP32_VECTOR_PEAK_TFLOPS, 2),
+        "sclk": clock.summary(100 * FLOPS_PER_INTERACTION * value / 1e3 / FP32_VECTOR_PEAK_TFLOPS),
         "roofline": {
             "bound": "alu",
             "achieved": round(achieved_tflops, 3),

@@ -173,7 +173,7 @@ size_t pairs_scratch(int64_t n, int band)
 // Automatic layout, chosen by measurement on MI355X (layout sweeps of the
 // five workloads and of uniform cubes from N = 8192 to 65536):
 //   - up to N = 8192, the small-N kernel (one kernel per evaluation or step):
-//     4 targets per workgroup to N = 1024, 8 to 4096, 16 above;
+//     4 targets per workgroup to N = 2048, 8 to 4096, 16 above;
 //   - from N = 32768 up, pair-symmetric bands when their scratch fits: the
 //     largest band that still yields at least 64 work items per compute unit,
 //     8 targets per lane from N = 65536 up and 4 below;
@@ -184,7 +184,7 @@ size_t pairs_scratch(int64_t n, int band)
 //     128 workgroups per compute unit over the run (finer load balance; a
 //     chunk's sources stay L2-resident), at least 4 tiles per chunk from
 //     N = 65536 up and 1 below.
-int small_tw(int64_t n) { return n <= 1024 ? 4 : (n <= 4096 ? 8 : 16); }
+int small_tw(int64_t n) { return n <= 2048 ? 4 : (n <= 4096 ? 8 : 16); }
 
 void auto_plan(int64_t n, const DeviceFacts &dev, nbody_plan *p)
 {
