@@ -90,6 +90,10 @@ class Oracle:
                                          ctypes.c_int64, _c_double_p, _c_double_p, _c_double_p,
                                          _c_double_p]
         lib.oracle_near_grid.restype = ctypes.c_int
+        lib.oracle_shard.argtypes = [_c_double_p, ctypes.c_int64, ctypes.c_double, ctypes.c_int64,
+                                     ctypes.c_int64, ctypes.c_int64, _c_int64_p, ctypes.c_int64,
+                                     _c_double_p, _c_double_p, _c_double_p, _c_double_p]
+        lib.oracle_shard.restype = ctypes.c_int
         self._lib = lib
 
     def num_threads(self) -> int:
@@ -228,6 +232,32 @@ class Oracle:
         lo32 = [as_f32(v) for v in lo]
         return self.near_grid_exact(pos, as_f32(eps2), lo32, as_f32(h), dims, targets)
 
+    def shard_exact(self, pos, eps2: float, band: int, shard: int, nshards: int,
+                    targets=None) -> dict:
+        """One shard's part of the direct sum (the pairs of the bands it owns, see
+        oracle_shard); float64 bodies and eps2 as given. Arrays as in accel_exact; pot is
+        minus the shard's sum of m_j / r."""
+        p = _bodies64(pos)
+        n = p.shape[0]
+        if targets is None:
+            t, nt = None, n
+        else:
+            t = np.ascontiguousarray(targets, dtype=np.int64)
+            nt = t.shape[0]
+        acc = np.zeros((nt, 3))
+        pot = np.zeros(nt)
+        ba = np.zeros(nt)
+        bp = np.zeros(nt)
+        rc = self._lib.oracle_shard(_ptr(p), n, float(eps2), int(band), int(shard), int(nshards),
+                                    _ptr(t, _c_int64_p), nt, _ptr(acc), _ptr(pot), _ptr(ba),
+                                    _ptr(bp))
+        if rc != 0:
+            raise ValueError("oracle_shard rejected its arguments")
+        return {"acc": acc, "pot": pot, "bound_a": ba, "bound_p": bp}
+
+    def shard(self, pos, eps2, band, shard, nshards, targets=None) -> dict:
+        return self.shard_exact(pos, as_f32(eps2), band, shard, nshards, targets)
+
 
 def unpack_diagnostics(out) -> dict:
     """The 13-value diagnostics record as a dict (same order as oracle_diagnostics)."""
@@ -291,3 +321,7 @@ def p2p(pos, eps2, cell_start, list_off, cells) -> dict:
 
 def near_grid(pos, eps2, lo, h, dims, targets=None) -> dict:
     return get().near_grid(pos, eps2, lo, h, dims, targets)
+
+
+def shard(pos, eps2, band, shard_index, nshards, targets=None) -> dict:
+    return get().shard(pos, eps2, band, shard_index, nshards, targets)

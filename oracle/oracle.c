@@ -293,6 +293,56 @@ int oracle_p2p(const double *pos, int64_t n, double eps2, const int32_t *cell_st
 }
 
 /*
+ * One shard of a split evaluation, by definition: the bodies form nb =
+ * ceil(n / band) bands of `band` consecutive indices; the unordered pair of
+ * bands {bi, bj} belongs to band pair_owner(bi, bj) (below), and shard s of S
+ * owns the bands [floor(s nb / S), floor((s+1) nb / S)). For every target i
+ * (or the listed ones) the sums run over the sources j, ascending, j = i
+ * included, whose pair of bands the shard owns. Summed over all S shards this
+ * is the whole direct sum, every pair once. Outputs as in oracle_accel.
+ * (Splitting a body's sum into parts that are merged afterwards: the
+ * blog.luozichu.ink study page of GPU Gems 3 ch. 31, section 4.)
+ */
+static int64_t pair_owner(int64_t bi, int64_t bj, int64_t nb)
+{
+    if (bi == bj) return bi;
+    const int64_t up = ((bj - bi) % nb + nb) % nb;  /* steps from bi up to bj, mod nb */
+    if (2 * up < nb) return bi;                     /* bj lies in bi's upper half-circle */
+    if (2 * up > nb) return bj;                     /* bi lies in bj's upper half-circle */
+    return bi < bj ? bi : bj;                       /* exactly opposite: the lower band */
+}
+
+int oracle_shard(const double *pos, int64_t n, double eps2, int64_t band, int64_t shard,
+                 int64_t nshards, const int64_t *targets, int64_t nt, double *acc, double *pot,
+                 double *bound_a, double *bound_p)
+{
+    if (!pos || n < 1 || nt < 0 || !(eps2 > 0.0) || band < 1 || nshards < 1 || shard < 0 ||
+        shard >= nshards)
+        return -1;
+    if (!targets && nt != n) return -1;
+    const int64_t nb = (n + band - 1) / band;
+    if (nshards > nb) return -1;
+    const int64_t b0 = shard * nb / nshards, b1 = (shard + 1) * nb / nshards;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t t = 0; t < nt; ++t) {
+        const int64_t i = targets ? targets[t] : t;
+        target_sums s = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+        if (i >= 0 && i < n)
+            for (int64_t j = 0; j < n; ++j) {
+                const int64_t o = pair_owner(i / band, j / band, nb);
+                if (o >= b0 && o < b1) add_pair(pos, i, j, eps2, &s);
+            }
+        acc[3 * t] = s.ax;
+        acc[3 * t + 1] = s.ay;
+        acc[3 * t + 2] = s.az;
+        if (pot) pot[t] = s.pp;
+        if (bound_a) bound_a[t] = s.sa;
+        if (bound_p) bound_p[t] = s.sp;
+    }
+    return 0;
+}
+
+/*
  * Near field on a uniform grid, by definition and without lists: the grid has
  * dims[0] x dims[1] x dims[2] cubic cells of side h from the corner lo; body i
  * lies in cell k_d = clamp(floor((x_d - lo_d) * inv_h), 0, dims_d - 1) per

@@ -506,6 +506,81 @@ def pin_near_grid_equals_lists(orc):
     _close(r_list["pot"][back], r_grid["pot"], 1e-13 * np.max(r_grid["bound_p"]), "grid vs lists p")
 
 
+# ------------------------------------------------------------------ shards of a split evaluation
+
+def _band_items(nb):
+    """The band-pair work items of a split evaluation, enumerated as the library describes
+    them: for every band A the diagonal (A, A) and the pairs (A, (A + d) mod nb) for
+    d = 1 .. nb // 2, where for even nb the opposite pair d = nb / 2 is taken only from the
+    lower band. Yields (owner band, frozenset of the two bands)."""
+    for a in range(nb):
+        yield a, frozenset((a,))
+        for d in range(1, nb // 2 + 1):
+            if 2 * d == nb and a >= nb // 2:
+                continue
+            yield a, frozenset((a, (a + d) % nb))
+
+
+def pin_shard_items_cover_each_pair_once(orc):
+    """One body per band, masses 2^-j, all at the origin, eps2 = 1: a shard's potential at
+    body i is minus the sum of 2^-j over the j it pairs i with, so its bits name the set
+    exactly. With one shard per band that set must be the partners of i in the items the
+    band owns, by an enumeration written independently of the oracle; and the items must
+    cover every unordered pair once (odd and even band counts)."""
+    for n in (11, 12):
+        items = list(_band_items(n))
+        pairs = [p for _, p in items]
+        want = {frozenset((i, j)) for i in range(n) for j in range(n)}
+        if len(pairs) != len(set(pairs)) or set(pairs) != want:
+            raise AssertionError(f"n={n}: items do not cover each unordered band pair once")
+        pos = np.zeros((n, 4))
+        pos[:, 3] = [2.0 ** -j for j in range(n)]
+        for s in range(n):
+            r = orc.shard_exact(pos, 1.0, 1, s, n)
+            if np.any(r["acc"] != 0.0):
+                raise AssertionError("coincident bodies must give zero acceleration")
+            for i in range(n):
+                # partner of i in each item of band s that holds i (itself for the diagonal)
+                expect = sorted(i if len(p) == 1 else min(p - {i})
+                                for a, p in items if a == s and i in p)
+                bits = int(round(-r["pot"][i] * 2.0 ** n))  # sum of 2^(n - j) over the j
+                got = [j for j in range(n) if bits >> (n - j) & 1]
+                if got != expect:
+                    raise AssertionError(f"n={n} shard {s} body {i}: pairs {got} != {expect}")
+
+
+def pin_shard_single_equals_direct_sum(orc):
+    """A single shard owns every band: the result is the direct sum bit for bit."""
+    pos, _ = _random_cells(13)
+    for band in (1, 5, 64):
+        r = orc.shard_exact(pos, 1e-3, band, 0, 1)
+        d = orc.accel_exact(pos, 1e-3)
+        for k in ("acc", "pot", "bound_a", "bound_p"):
+            if not np.array_equal(r[k], d[k]):
+                raise AssertionError(f"band {band}: one shard differs from the direct sum in {k}")
+
+
+def pin_shards_add_up_to_direct_sum(orc):
+    """Over all shards the parts add up to the direct sum (fp64 rounding only), for even and
+    odd band counts and shard counts that do and do not divide them; the error scales add up
+    the same way."""
+    rng = np.random.default_rng(77)
+    for n, band, shards in ((700, 64, (2, 3, 11)), (512, 64, (2, 3, 8)), (97, 8, (5, 13))):
+        pos = _bodies(rng.uniform(-1, 1, (n, 3)), rng.uniform(0.5, 1.5, n) / n)
+        d = orc.accel_exact(pos, 1e-3)
+        for S in shards:
+            parts = [orc.shard_exact(pos, 1e-3, band, s, S) for s in range(S)]
+            for k in ("acc", "pot", "bound_a", "bound_p"):
+                tot = sum(p[k] for p in parts)
+                scale = d["bound_a"] if k == "acc" else d["bound_p"]
+                if k == "acc":
+                    err = np.linalg.norm(tot - d[k], axis=1)
+                else:
+                    err = np.abs(tot - d[k])
+                if np.any(err > 1e-13 * scale):
+                    raise AssertionError(f"n={n} S={S}: shards do not add up in {k}")
+
+
 ALL_PINS = [
     pin_single_body,
     pin_two_body_345,
@@ -530,4 +605,7 @@ ALL_PINS = [
     pin_near_grid_small_grids_equal_direct_sum,
     pin_near_grid_separated_clusters,
     pin_near_grid_equals_lists,
+    pin_shard_items_cover_each_pair_once,
+    pin_shard_single_equals_direct_sum,
+    pin_shards_add_up_to_direct_sum,
 ]

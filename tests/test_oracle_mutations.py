@@ -50,6 +50,12 @@ MUTATIONS = [
     ("p2p: negative list entry read as cell 0",
      "const int32_t s = list[e];\n                if (s < 0 || s >= ncell) continue;",
      "const int32_t s = list[e] < 0 ? 0 : list[e];\n                if (s >= ncell) continue;"),
+    ("shard: opposite bands go to the upper band", "return bi < bj ? bi : bj;",
+     "return bi > bj ? bi : bj;"),
+    ("shard: opposite bands counted from both sides", "if (2 * up < nb) return bi;",
+     "if (2 * up <= nb) return bi;"),
+    ("shard: band ranges overlap", "b1 = (shard + 1) * nb / nshards;",
+     "b1 = (shard + 1) * nb / nshards + 1;"),
 ]
 
 
