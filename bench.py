@@ -280,6 +280,77 @@ def near_grid_bench(nb, w, pos, args) -> int:
     return 0
 
 
+def shard_interactions(n: int, band: int, shard: int, nshards: int) -> int:
+    """Interactions (ordered pairs, N^2 in all) that shard `shard` of `nshards` evaluates:
+    its bands' diagonal items one-sided (self pairs included), the other items for both
+    bodies of each pair."""
+    nb = (n + band - 1) // band
+    size = [min(band, n - b * band) for b in range(nb)]
+    total = 0
+    for a in range(shard * nb // nshards, (shard + 1) * nb // nshards):
+        total += size[a] * size[a]
+        for d in range(1, nb // 2 + 1):
+            if 2 * d == nb and a >= nb // 2:
+                continue
+            total += 2 * size[a] * size[(a + d) % nb]
+    return total
+
+
+def shard_bench(nb, w, pos, args) -> int:
+    """Time nbody_accel_shard for every shard of an evaluation split args.shard ways (one
+    GPU's share of a multi-GPU evaluation, at its real shape) and nbody_shard_finish of one
+    GPU's targets; one JSON line per shard and a summary line (not the contract line)."""
+    import torch
+
+    n, S = w.n, args.shard
+    stream = torch.cuda.current_stream()
+    band = nb.nbody_plan_for(n).band or 512
+    plan = nb.make_plan(mode="pairs", band=band)
+    out = torch.empty((S, n, 4), device=pos.device)
+    acc = torch.empty((n // S + 1, 4), device=pos.device)
+    pot = torch.empty((n // S + 1,), device=pos.device)
+    per = []
+    for s in range(S):
+        def call():
+            nb.nbody_accel_shard(pos, n, float(w.eps2), s, S, out[s], True, plan, stream)
+        for _ in range(max(1, args.warmup)):
+            call()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        it = shard_interactions(n, band, s, S)
+        r = {"workload": args.workload, "N": n, "band": band, "shard": s, "nshards": S,
+             "ms": round(ms, 4), "interactions": it, "G_int_per_s": round(it / ms / 1e6, 1),
+             "pct_fp32_peak": round(100 * FLOPS_PER_INTERACTION * it / ms / 1e9
+                                    / FP32_VECTOR_PEAK_TFLOPS, 2)}
+        per.append(r)
+        print(json.dumps(r), flush=True)
+    t0, t1 = 0, n // S
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    nb.nbody_shard_finish(out, n, S, t0, t1, acc, pot, stream)
+    e0.record(stream)
+    for _ in range(args.steps):
+        nb.nbody_shard_finish(out, n, S, t0, t1, acc, pot, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    fin = e0.elapsed_time(e1) / args.steps
+    worst = max(r["ms"] for r in per)
+    print(json.dumps({"shard_summary": {
+        "nshards": S, "max_shard_ms": worst, "min_shard_ms": min(r["ms"] for r in per),
+        "finish_ms_per_gpu": round(fin, 4),
+        "evaluation_G_int_per_s_if_shards_ran_in_parallel": round(
+            interactions(n) / (worst + fin) / 1e6, 1),
+        "note": "compute only: the exchange of the N-record parts between GPUs is not timed"}}),
+        flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -303,6 +374,10 @@ def main(argv=None) -> int:
     ap.add_argument("--near-grid", type=int, default=0, metavar="D",
                     help="only time nbody_near_grid on a D^3 grid over [-1, 1]^3 (near field; "
                          "prints its own JSON line, no contract line)")
+    ap.add_argument("--shard", type=int, default=0, metavar="S",
+                    help="only time nbody_accel_shard for each of S shards of the workload's "
+                         "evaluation (one GPU's share of an S-GPU split) and the merge of one "
+                         "GPU's targets; prints its own JSON lines, no contract line")
     ap.add_argument("--no-clock", action="store_true",
                     help="do not sample the shader clock with amd-smi during the timed steps "
                          "(sampled only when a step takes 20 ms or more and --warmup >= 2)")
@@ -356,6 +431,8 @@ def main(argv=None) -> int:
         return sweep(nb, w, pos, vel, acc, pot, args)
     if args.near_grid:
         return near_grid_bench(nb, w, pos, args)
+    if args.shard:
+        return shard_bench(nb, w, pos, args)
 
     diag0 = nb.diagnostics(pos, vel, float(w.eps2)) if stepping else None
     # The clock is sampled only when a step is long (>= 20 ms): for microsecond steps the

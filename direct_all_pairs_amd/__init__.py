@@ -68,17 +68,22 @@ _lib.nbody_near_grid.argtypes = [_vp, _i64, _f32, ctypes.POINTER(ctypes.c_float)
                                  ctypes.POINTER(ctypes.c_int32), _vp, _vp, _vp]
 _lib.nbody_accel_soa.argtypes = [_vp, _vp, _vp, _vp, _i64, _f32, _vp, _vp, _vp, _vp, _vp]
 _lib.nbody_step_soa.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _f32, _f32, _i64, _vp]
+_lib.nbody_accel_shard.argtypes = [_vp, _i64, _f32, ctypes.c_int32, ctypes.c_int32, _int,
+                                   ctypes.POINTER(nbody_plan), _vp, _vp]
+_lib.nbody_shard_finish.argtypes = [_vp, _i64, ctypes.c_int32, _i64, _i64, _vp, _vp, _vp]
 _lib.nbody_last_error.restype = ctypes.c_char_p
 _lib.nbody_release_workspace.argtypes = []
 _lib.nbody_version.restype = ctypes.c_char_p
 for _f in ("nbody_accel", "nbody_accel_plan", "nbody_step", "nbody_step_plan",
-           "nbody_accel_soa", "nbody_step_soa", "nbody_p2p", "nbody_near_grid",
-           "nbody_diagnostics", "nbody_plan_for", "nbody_release_workspace"):
+           "nbody_accel_soa", "nbody_step_soa", "nbody_accel_shard", "nbody_shard_finish",
+           "nbody_p2p", "nbody_near_grid", "nbody_diagnostics", "nbody_plan_for",
+           "nbody_release_workspace"):
     getattr(_lib, _f).restype = _int
 
 EXPORTS = ("nbody_accel", "nbody_accel_plan", "nbody_step", "nbody_step_plan", "nbody_accel_soa",
-           "nbody_step_soa", "nbody_p2p", "nbody_near_grid", "nbody_diagnostics",
-           "nbody_plan_for", "nbody_last_error", "nbody_release_workspace", "nbody_version")
+           "nbody_step_soa", "nbody_accel_shard", "nbody_shard_finish", "nbody_p2p",
+           "nbody_near_grid", "nbody_diagnostics", "nbody_plan_for", "nbody_last_error",
+           "nbody_release_workspace", "nbody_version")
 DIAG_FIELDS = ("kinetic", "potential", "total", "momentum", "angular_momentum", "mass",
                "centre_of_mass")
 
@@ -166,6 +171,24 @@ def nbody_step_soa(x, y, z, m, vx, vy, vz, N: int, dt: float, eps2: float, nstep
     rc = _lib.nbody_step_soa(_ptr(x), _ptr(y), _ptr(z), _ptr(m), _ptr(vx), _ptr(vy), _ptr(vz),
                              int(N), float(dt), float(eps2), int(nsteps), _stream(stream))
     return _check(rc, "nbody_step_soa") if check else rc
+
+
+def nbody_accel_shard(pos_xyzm, N: int, eps2: float, shard: int, nshards: int, partial_out,
+                      want_pot: bool = True, plan=None, stream=None, check: bool = True) -> int:
+    p = None
+    if plan is not None:
+        p = plan if isinstance(plan, nbody_plan) else make_plan(**plan)
+    rc = _lib.nbody_accel_shard(_ptr(pos_xyzm), int(N), float(eps2), int(shard), int(nshards),
+                                int(bool(want_pot)), ctypes.byref(p) if p is not None else None,
+                                _ptr(partial_out), _stream(stream))
+    return _check(rc, "nbody_accel_shard") if check else rc
+
+
+def nbody_shard_finish(partials, N: int, nshards: int, t0: int, t1: int, acc_out, pot_out=None,
+                       stream=None, check: bool = True) -> int:
+    rc = _lib.nbody_shard_finish(_ptr(partials), int(N), int(nshards), int(t0), int(t1),
+                                 _ptr(acc_out), _ptr(pot_out), _stream(stream))
+    return _check(rc, "nbody_shard_finish") if check else rc
 
 
 def nbody_p2p(pos, N: int, eps2: float, cell_start, ncell: int, list_off, cells, nlist: int,

@@ -357,7 +357,7 @@ int enqueue_eval(const float4 *pos, int n, float eps2, float4 *acc_out, float *p
     }
     hipError_t e;
     if (pairs) {
-        nbk::PairsArgs pa{pos, n, eps2, p.splits, a.part};
+        nbk::PairsArgs pa{pos, n, eps2, p.splits, a.part, 0, p.splits};
         e = nbk::launch_pairs(p.band, p.tpl, pot, pa, stream);
     } else {
         e = nbk::launch_accel(p.bcast, p.tpl, p.wg, pot, grid_x(n, p.tpl, p.wg),
@@ -566,6 +566,57 @@ int step_soa_impl(float *x, float *y, float *z, const float *m, float *vx, float
 
 }  // namespace
 
+// First band of shard s when nb bands are split into S contiguous ranges.
+int shard_band(int s, int nb, int S) { return (int)((int64_t)s * nb / S); }
+
+int shard_impl(const nbody_f4 *pos, int64_t N, float eps2, int32_t shard, int32_t nshards,
+               int want_pot, const nbody_plan *plan, nbody_f4 *partial_out, hipStream_t stream)
+{
+    int rc = check_n(N);
+    if (rc != NBODY_OK) return rc;
+    if (nshards < 1) return fail(NBODY_EINVAL, "nshards=%d must be >= 1", (int)nshards);
+    if (shard < 0 || shard >= nshards)
+        return fail(NBODY_EINVAL, "shard=%d must be in [0, nshards=%d)", (int)shard, (int)nshards);
+    if (plan && plan->mode != NBODY_MODE_PAIRS)
+        return fail(NBODY_EINVAL, "plan.mode=%d: a shard is a share of the pair-symmetric "
+                                  "evaluation (plan NULL or mode NBODY_MODE_PAIRS)", plan->mode);
+    if (N == 0) return ok();
+    if (!pos) return fail(NBODY_EINVAL, "pos_xyzm is NULL");
+    if (!partial_out) return fail(NBODY_EINVAL, "partial_out is NULL");
+    if (!eps2_ok(eps2))
+        return fail(NBODY_EINVAL, "eps2=%g must be a positive, finite, normal float", (double)eps2);
+    if (!aligned(pos, 16) || !aligned(partial_out, 16))
+        return fail(NBODY_EALIGN, "pos_xyzm and partial_out must be 16-byte aligned");
+    const size_t b16 = (size_t)N * 16;
+    if (overlap(pos, b16, partial_out, b16))
+        return fail(NBODY_EINVAL, "partial_out overlaps pos_xyzm");
+    if (plan && valid_band(plan->band) && nshards > (N + plan->band - 1) / plan->band)
+        return fail(NBODY_EINVAL, "nshards=%d exceeds the %lld bands of %d bodies (each shard "
+                                  "needs at least one band)", (int)nshards,
+                    (long long)((N + plan->band - 1) / plan->band), (int)plan->band);
+    nbody_plan want = plan ? *plan : nbody_plan{0, 0, 0, 0, 0, NBODY_MODE_PAIRS, 0};
+    nbody_plan p;
+    int dev = 0;
+    rc = make_plan(N, &want, &dev, &p);
+    if (rc != NBODY_OK) return rc;
+    const int nb = p.splits;
+    if (nshards > nb)
+        return fail(NBODY_EINVAL, "nshards=%d exceeds the %d bands of %d bodies (each shard "
+                                  "needs at least one band)", (int)nshards, nb, (int)p.band);
+    void *ws = nullptr;
+    rc = scratch_get(dev, stream, eval_scratch(N, p, false), &ws);
+    if (rc != NBODY_OK) return rc;
+    const int n = (int)N;
+    nbk::PairsArgs pa{(const float4 *)pos, n, eps2, nb, (float4 *)ws,
+                      shard_band(shard, nb, nshards), shard_band(shard + 1, nb, nshards)};
+    hipError_t e = nbk::launch_pairs(p.band, p.tpl, want_pot != 0, pa, stream);
+    if (e != hipSuccess) return hip_fail(e, "accel kernel launch");
+    e = nbk::launch_shard_combine(pa.part, n, p.band, nb, pa.band0, pa.band1,
+                                  (float4 *)partial_out, stream);
+    if (e != hipSuccess) return hip_fail(e, "shard combine launch");
+    return ok();
+}
+
 extern "C" {
 
 int nbody_accel(const nbody_f4 *pos_xyzm, int64_t N, float eps2, nbody_f4 *acc_out,
@@ -603,6 +654,41 @@ int nbody_step_soa(float *x, float *y, float *z, const float *m, float *vx, floa
                    int64_t N, float dt, float eps2, int64_t nsteps, hipStream_t stream)
 {
     return step_soa_impl(x, y, z, m, vx, vy, vz, N, dt, eps2, nsteps, stream);
+}
+
+int nbody_accel_shard(const nbody_f4 *pos_xyzm, int64_t N, float eps2, int32_t shard,
+                      int32_t nshards, int want_pot, const nbody_plan *plan,
+                      nbody_f4 *partial_out, hipStream_t stream)
+{
+    return shard_impl(pos_xyzm, N, eps2, shard, nshards, want_pot, plan, partial_out, stream);
+}
+
+int nbody_shard_finish(const nbody_f4 *partials, int64_t N, int32_t nshards, int64_t t0,
+                       int64_t t1, nbody_f4 *acc_out, float *pot_out, hipStream_t stream)
+{
+    int rc = check_n(N);
+    if (rc != NBODY_OK) return rc;
+    if (nshards < 1) return fail(NBODY_EINVAL, "nshards=%d must be >= 1", (int)nshards);
+    if (t0 < 0 || t1 < t0 || t1 > N)
+        return fail(NBODY_EINVAL, "target range [%lld, %lld) must lie in [0, N=%lld]",
+                    (long long)t0, (long long)t1, (long long)N);
+    if ((int64_t)nshards * N > INT64_MAX / 16)
+        return fail(NBODY_EINVAL, "nshards x N records do not fit the address space");
+    if (t0 == t1) return ok();
+    if (!partials) return fail(NBODY_EINVAL, "partials is NULL");
+    if (!acc_out) return fail(NBODY_EINVAL, "acc_out is NULL");
+    if (!aligned(partials, 16) || !aligned(acc_out, 16))
+        return fail(NBODY_EALIGN, "partials and acc_out must be 16-byte aligned");
+    if (pot_out && !aligned(pot_out, 4)) return fail(NBODY_EALIGN, "pot_out is not 4-byte aligned");
+    const size_t bp = (size_t)nshards * (size_t)N * 16, m = (size_t)(t1 - t0);
+    if (overlap(partials, bp, acc_out, m * 16) || (pot_out && overlap(partials, bp, pot_out, m * 4)))
+        return fail(NBODY_EINVAL, "an output overlaps partials");
+    if (pot_out && overlap(acc_out, m * 16, pot_out, m * 4))
+        return fail(NBODY_EINVAL, "pot_out overlaps acc_out");
+    hipError_t e = nbk::launch_shard_finish((const float4 *)partials, (int)N, nshards, (int)t0,
+                                            (int)t1, (float4 *)acc_out, pot_out, stream);
+    if (e != hipSuccess) return hip_fail(e, "shard finish launch");
+    return ok();
 }
 
 int nbody_p2p(const nbody_f4 *pos, int64_t N, float eps2, const int32_t *cell_start,

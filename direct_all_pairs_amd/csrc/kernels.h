@@ -40,12 +40,28 @@ struct PairsArgs {
     float eps2;         // softening squared (positive normal float)
     int nbands;         // nb = ceil(N / band)
     float4 *part;       // part[slot*N + i], slot in [0, nb): every entry written once
+    int band0;          // items (A, d) are evaluated for A in [band0, band1)
+    int band1;          //   (the whole evaluation: 0, nb)
 };
 
 // Pair-symmetric evaluation over bands of `band` bodies (512, 1024 or 2048)
 // with tpl (4 or 8) targets per lane. Writes nb partial slots per body;
 // launch_combine or launch_euler with splits = nb finishes the evaluation.
+// With a band range narrower than [0, nb) only the slots of the items (A, d)
+// with A in the range are written; launch_shard_combine adds exactly those.
 hipError_t launch_pairs(int band, int tpl, bool pot, const PairsArgs &args, hipStream_t stream);
+
+// One shard's contribution to every body: the slots written by the items
+// (A, d) with A in [band0, band1), added in ascending slot order like the
+// combine (compensated), out[i] = (ax, ay, az, sum m/r) partial; N records.
+hipError_t launch_shard_combine(const float4 *part, int n, int band, int nbands, int band0,
+                                int band1, float4 *out, hipStream_t stream);
+
+// Targets [t0, t1): the nshards contributions partials[s*N + i] added in
+// ascending s (compensated); acc_out[i - t0] = (ax, ay, az, 0) and, if
+// pot_out is not null, pot_out[i - t0] = -sum m/r.
+hipError_t launch_shard_finish(const float4 *partials, int n, int nshards, int t0, int t1,
+                               float4 *acc_out, float *pot_out, hipStream_t stream);
 
 // Launch the acceleration kernel: grid (ceil(N / (wg*tpl)), S), block wg.
 // wg is 64, 128, 256 or 512 for the LDS broadcast and 256 for the others.

@@ -815,14 +815,14 @@ __device__ __forceinline__ void pairs_item(const PairsArgs &k, int A, int B, int
     }
 }
 
-// grid (nb, nb/2 + 1), 256 threads. Workgroups whose (A, d) is not an owned
-// item return at once (uniformly, before any barrier).
+// grid (band1 - band0, nb/2 + 1), 256 threads. Workgroups whose (A, d) is not
+// an owned item return at once (uniformly, before any barrier).
 template <int T, int BD, bool POT>
 __global__ void __launch_bounds__(256) accel_pairs(PairsArgs k)
 {
     __shared__ PairsShared<T, BD> sh;
     const int nb = k.nbands;
-    const int A = blockIdx.x;
+    const int A = k.band0 + (int)blockIdx.x;
     const int d = blockIdx.y;
     if (d > nb / 2) return;
     if (nb % 2 == 0 && d == nb / 2 && A >= nb / 2) return;
@@ -863,6 +863,56 @@ __global__ void __launch_bounds__(256) euler_kernel(const float4 *__restrict__ p
     euler_update(x, v, a, dt);
     pos[i] = x;
     vel[i] = v;
+}
+
+// ---------------------------------------------------------------- shards
+// A shard owns the work items (A, d) of the bands A in [band0, band1). The
+// slot k of a body of band x was written by the item of band owner(x, k):
+// slot 0 and slots k < nb/2 by the body's own band (diagonal and A sides),
+// slots k > nb/2 by the B side of item ((x + k) mod nb, nb - k), and for even
+// nb slot nb/2 by the lower band of the opposite pair.
+__device__ __forceinline__ int slot_owner(int x, int k, int nb)
+{
+    if (2 * k < nb) return x;
+    if (2 * k == nb) return x < nb / 2 ? x : x - nb / 2;
+    const int o = x + k;
+    return o >= nb ? o - nb : o;
+}
+
+__global__ void __launch_bounds__(256) shard_combine_kernel(const float4 *__restrict__ part, int n,
+                                                            int band, int nb, int band0,
+                                                            int band1, float4 *__restrict__ out)
+{
+    const unsigned i = blockIdx.x * 256u + threadIdx.x;
+    if (i >= (unsigned)n) return;
+    const int x = (int)(i / (unsigned)band);
+    float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float4 e = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    bool first = true;
+    for (int k = 0; k < nb; ++k) {
+        const int o = slot_owner(x, k, nb);
+        if (o < band0 || o >= band1) continue;
+        const float4 v = part[(size_t)k * (size_t)n + i];
+        if (first) {
+            a = v;  // as in sum_parts: the first slot starts the sum
+            first = false;
+        } else {
+            two_sum_add4(a, e, v);
+        }
+    }
+    out[i] = make_float4(a.x + e.x, a.y + e.y, a.z + e.z, a.w + e.w);
+}
+
+__global__ void __launch_bounds__(256) shard_finish_kernel(const float4 *__restrict__ partials,
+                                                           int n, int nshards, int t0, int t1,
+                                                           float4 *__restrict__ acc_out,
+                                                           float *__restrict__ pot_out)
+{
+    const unsigned i = (unsigned)t0 + blockIdx.x * 256u + threadIdx.x;
+    if (i >= (unsigned)t1) return;
+    const float4 a = sum_parts(partials, n, nshards, i);
+    acc_out[i - t0] = make_float4(a.x, a.y, a.z, 0.0f);
+    if (pot_out) pot_out[i - t0] = -a.w;
 }
 
 // ---------------------------------------------------------------- diagnostics
@@ -1358,11 +1408,35 @@ hipError_t launch_pairs(int band, int tpl, bool pot, const PairsArgs &args, hipS
         if (band == 1024) fn = pairs_fn<8, 1024>(pot);
         if (band == 2048) fn = pairs_fn<8, 2048>(pot);
     }
-    if (!fn || args.nbands < 1) return hipErrorInvalidValue;
+    if (!fn || args.nbands < 1 || args.band0 < 0 || args.band1 > args.nbands ||
+        args.band0 >= args.band1)
+        return hipErrorInvalidValue;
     PairsArgs a = args;
     void *kargs[] = {&a};
-    return hipLaunchKernel(fn, dim3((unsigned)a.nbands, (unsigned)(a.nbands / 2 + 1), 1),
+    return hipLaunchKernel(fn, dim3((unsigned)(a.band1 - a.band0), (unsigned)(a.nbands / 2 + 1), 1),
                            dim3(256, 1, 1), kargs, 0, stream);
+}
+
+hipError_t launch_shard_combine(const float4 *part, int n, int band, int nbands, int band0,
+                                int band1, float4 *out, hipStream_t stream)
+{
+    if (n < 1 || band < 1 || nbands != (n + band - 1) / band || band0 < 0 || band1 > nbands ||
+        band0 >= band1)
+        return hipErrorInvalidValue;
+    void *kargs[] = {&part, &n, &band, &nbands, &band0, &band1, &out};
+    const unsigned g = (unsigned)((n + 255) / 256);
+    return hipLaunchKernel((const void *)&shard_combine_kernel, dim3(g), dim3(256), kargs, 0,
+                           stream);
+}
+
+hipError_t launch_shard_finish(const float4 *partials, int n, int nshards, int t0, int t1,
+                               float4 *acc_out, float *pot_out, hipStream_t stream)
+{
+    if (n < 1 || nshards < 1 || t0 < 0 || t1 > n || t0 >= t1) return hipErrorInvalidValue;
+    void *kargs[] = {&partials, &n, &nshards, &t0, &t1, &acc_out, &pot_out};
+    const unsigned g = (unsigned)((t1 - t0 + 255) / 256);
+    return hipLaunchKernel((const void *)&shard_finish_kernel, dim3(g), dim3(256), kargs, 0,
+                           stream);
 }
 
 hipError_t launch_small(int tw, bool pot, bool step, const SmallArgs &args, hipStream_t stream)

@@ -182,6 +182,47 @@ int nbody_step_soa(float *x, float *y, float *z, const float *m, float *vx, floa
                    int64_t N, float dt, float eps2, int64_t nsteps, hipStream_t stream);
 
 /*
+ * nbody_accel_shard - one shard of a pair-symmetric evaluation: the unit of work
+ * of one GPU when an evaluation is split over nshards GPUs (each holding every
+ * position). The sum is the one above (Degawa slide 4, Nakasato No.4), cut
+ * into partial sums that are merged afterwards, as the blog.luozichu.ink study
+ * page ("GPU Gems 3 · Chapter 31", section 4) splits one body's row over
+ * several threads for small N and merges their accelerations.
+ *   The N bodies form nb bands of plan.band bodies (the plan is the automatic
+ *   NBODY_MODE_PAIRS plan for N when plan is NULL; otherwise plan.mode must be
+ *   NBODY_MODE_PAIRS). Shard s of S owns the bands [floor(s nb / S),
+ *   floor((s+1) nb / S)) and evaluates their band-pair work items: item (A, d)
+ *   covers every pair of a body of band A with a body of band (A + d) mod nb,
+ *   d in [0, nb/2], where for even nb the item d = nb/2 exists only for A < nb/2
+ *   (so every unordered pair of bodies, self pairs included, lies in exactly
+ *   one item, hence in exactly one shard).
+ *   partial_out : N records; record i receives this shard's contribution to
+ *                 body i: (ax, ay, az, sum m_j / r) over the pairs of its items
+ *                 (w = 0 when want_pot is 0), zero-valued terms included.
+ *                 Must not overlap pos_xyzm.
+ *   shard, nshards : 0 <= shard < nshards <= nb.
+ * Scratch: nb x N x 16 bytes, as for nbody_accel in pairs mode. With nshards =
+ * 1 the result, finished by nbody_shard_finish, equals nbody_accel_plan with
+ * the same plan bit for bit.
+ */
+int nbody_accel_shard(const nbody_f4 *pos_xyzm, int64_t N, float eps2, int32_t shard,
+                      int32_t nshards, int want_pot, const nbody_plan *plan,
+                      nbody_f4 *partial_out, hipStream_t stream);
+
+/*
+ * nbody_shard_finish - merges the nshards contributions of nbody_accel_shard for
+ * the targets [t0, t1) (what a GPU owning those bodies does after the
+ * contributions have reached it): partials holds nshards x N records, shard s
+ * at partials[s N .. s N + N); they are added in ascending s (compensated).
+ *   acc_out : t1 - t0 records (ax, ay, az, 0) of bodies t0 .. t1 - 1.
+ *   pot_out : t1 - t0 floats p_i = -sum, or NULL.
+ * 0 <= t0 <= t1 <= N; t0 = t1 enqueues nothing. Outputs must not overlap
+ * partials or each other.
+ */
+int nbody_shard_finish(const nbody_f4 *partials, int64_t N, int32_t nshards, int64_t t0,
+                       int64_t t1, nbody_f4 *acc_out, float *pot_out, hipStream_t stream);
+
+/*
  * nbody_p2p - the all-pairs sum restricted to cell interaction lists: the near
  * field of a hierarchical method (GPU Gems 3 ch. 31 study page, section 6;
  * Nakasato "スライド 1", No.34), with the lists a tree or grid code provides.

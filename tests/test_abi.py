@@ -193,6 +193,46 @@ def test_near_grid_rejects(nb, bad, code):
     assert nb.nbody_last_error() != ""
 
 
+PAIRS512 = dict(mode=2, band=512)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(n=-1), 1), (dict(nshards=0), 1), (dict(shard=-1), 1), (dict(shard=4), 1),
+    (dict(plan=dict(mode=1)), 1), (dict(plan=dict(mode=0)), 1), (dict(nshards=33, shard=0), 1),
+    (dict(pos=None), 1), (dict(out=None), 1), (dict(eps2=0.0), 1), (dict(eps2=math.nan), 1),
+    (dict(pos=A + 4), 2), (dict(out=B + 8), 2), (dict(out=A + 64), 1),
+    (dict(plan=dict(mode=2, band=300)), 1), (dict(plan=dict(mode=2, tpl=2)), 1),
+])
+def test_accel_shard_rejects(nb, bad, code):
+    a = dict(pos=A, n=16384, eps2=1e-4, shard=1, nshards=4, plan=PAIRS512, out=B)
+    a.update(bad)
+    rc = nb.nbody_accel_shard(a["pos"], a["n"], a["eps2"], a["shard"], a["nshards"], a["out"],
+                              plan=a["plan"], stream=0, check=False)
+    assert rc == code, bad
+    assert nb.nbody_last_error() != ""
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(n=-1), 1), (dict(nshards=0), 1), (dict(t0=-1), 1), (dict(t0=9, t1=8), 1),
+    (dict(t1=17), 1), (dict(parts=None), 1), (dict(acc=None), 1), (dict(parts=A + 4), 2),
+    (dict(acc=B + 4), 2), (dict(pot=C + 2), 2), (dict(acc=A + 256), 1), (dict(pot=A), 1),
+    (dict(pot=B), 1),
+])
+def test_shard_finish_rejects(nb, bad, code):
+    a = dict(parts=A, n=16, nshards=3, t0=2, t1=10, acc=B, pot=C)
+    a.update(bad)
+    rc = nb.nbody_shard_finish(a["parts"], a["n"], a["nshards"], a["t0"], a["t1"], a["acc"],
+                               a["pot"], stream=0, check=False)
+    assert rc == code, bad
+    assert nb.nbody_last_error() != ""
+
+
+def test_shard_nothing_to_do(nb):
+    assert nb.nbody_accel_shard(None, 0, 1e-4, 0, 1, None, stream=0, check=False) == nb.NBODY_OK
+    assert nb.nbody_shard_finish(None, 16, 2, 5, 5, None, None, stream=0,
+                                 check=False) == nb.NBODY_OK
+
+
 def test_plan_rejects_bad_fields(nb):
     for plan in (dict(bcast=7), dict(tpl=3), dict(splits=-1), dict(splits=5000), dict(mode=4),
                  dict(mode=3, tpl=2), dict(mode=3, tpl=64), dict(mode=3, splits=2),

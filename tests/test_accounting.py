@@ -3,6 +3,8 @@
 import json
 from pathlib import Path
 
+import pytest
+
 import bench
 
 GOLDEN = Path(__file__).resolve().parent / "golden"
@@ -28,3 +30,11 @@ def test_peak_from_unit_counts():
 def test_multi_gpu_refused(capsys):
     assert bench.main(["--gpus", "2"]) == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+@pytest.mark.parametrize("n,band,nshards", [(1, 512, 1), (1 << 20, 2048, 8), (3000, 512, 3),
+                                            (20011, 512, 40), (5000, 1024, 5), (4096, 512, 8)])
+def test_shard_interactions_add_up_to_n_squared(n, band, nshards):
+    parts = [bench.shard_interactions(n, band, s, nshards) for s in range(nshards)]
+    assert sum(parts) == n * n
+    assert min(parts) > 0
