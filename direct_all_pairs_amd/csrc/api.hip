@@ -152,8 +152,8 @@ int wide_cells(int64_t n, int64_t ncell, bool *wide)
 
 // Largest N the automatic plan gives to NBODY_MODE_SMALL, and the smallest it
 // gives to NBODY_MODE_PAIRS.
-constexpr int64_t kSmallMaxN = 8192;
-constexpr int64_t kPairsMinN = 32768;
+constexpr int64_t kSmallMaxN = 7680;
+constexpr int64_t kPairsMinN = 18432;
 
 int valid_tpl(int t) { return t == 1 || t == 2 || t == 4 || t == 8; }
 
@@ -171,12 +171,14 @@ size_t pairs_scratch(int64_t n, int band)
 }
 
 // Automatic layout, chosen by measurement on MI355X (layout sweeps of the
-// five workloads and of uniform cubes from N = 8192 to 65536):
-//   - up to N = 8192, the small-N kernel (one kernel per evaluation or step):
-//     4 targets per workgroup to N = 2048, 8 to 4096, 16 above;
-//   - from N = 32768 up, pair-symmetric bands when their scratch fits: the
-//     largest band that still yields at least 64 work items per compute unit,
-//     8 targets per lane from N = 65536 up and 4 below;
+// five workloads and of uniform cubes from N = 1024 to 98304):
+//   - up to N = 7680 (small mode measured faster at 7168, tiles at 8192), the
+//     small-N kernel (one kernel per evaluation or step): 4 targets per
+//     workgroup to N = 2048, 8 to 6144, 16 above;
+//   - from N = 18432 up (tiles measured faster at 16384), pair-symmetric bands
+//     when their scratch fits: the largest band that still yields at least 64
+//     work items per compute unit, 4 targets per lane below N = 24576 and 8
+//     from there;
 //   - otherwise one-sided tiles with the LDS broadcast and one target per lane:
 //     every VALU operand of the inner step is then a VGPR, which issues about
 //     twice as fast as an SGPR operand; 512-thread workgroups (512-body LDS
@@ -184,7 +186,7 @@ size_t pairs_scratch(int64_t n, int band)
 //     128 workgroups per compute unit over the run (finer load balance; a
 //     chunk's sources stay L2-resident), at least 4 tiles per chunk from
 //     N = 65536 up and 1 below.
-int small_tw(int64_t n) { return n <= 2048 ? 4 : (n <= 4096 ? 8 : 16); }
+int small_tw(int64_t n) { return n <= 2048 ? 4 : (n <= 6144 ? 8 : 16); }
 
 void auto_plan(int64_t n, const DeviceFacts &dev, nbody_plan *p)
 {
@@ -217,7 +219,7 @@ void auto_plan(int64_t n, const DeviceFacts &dev, nbody_plan *p)
     }
     if (p->mode == NBODY_MODE_PAIRS) {
         p->bcast = NBODY_BCAST_LDS;
-        if (p->tpl == 0) p->tpl = big ? 8 : 4;
+        if (p->tpl == 0) p->tpl = n >= 24576 ? 8 : 4;
         p->wg = 256;
         if (p->band == 0) p->band = n >= (1 << 19) ? 2048 : (n >= (1 << 17) ? 1024 : 512);
         return;

@@ -272,15 +272,17 @@ def test_pairs_plan_beyond_grid_limit_rejected(nb):
 
 
 def test_auto_plan_modes(nb):
-    """Small-N kernel up to N = 8192, tiles above, pair-symmetric bands from N = 65536 up
-    (scratch permitting)."""
-    for n in (1, 2048, 4096, 8192):
+    """Small-N kernel up to N = 7680, tiles above, pair-symmetric bands from N = 18432 up
+    (scratch permitting), with the measured targets per workgroup and per lane."""
+    for n, tw in ((1, 4), (2048, 4), (2049, 8), (6144, 8), (6145, 16), (7680, 16)):
         p = nb.nbody_plan_for(n)
-        assert p.mode == nb.MODE_SMALL and p.splits == 1 and p.tpl in (4, 8, 16, 32), n
-    assert nb.nbody_plan_for(8193).mode == nb.MODE_TILES
-    assert nb.nbody_plan_for(32767).mode == nb.MODE_TILES
-    p = nb.nbody_plan_for(32768)
+        assert p.mode == nb.MODE_SMALL and p.splits == 1 and p.tpl == tw and p.wg == 256, n
+    assert nb.nbody_plan_for(7681).mode == nb.MODE_TILES
+    assert nb.nbody_plan_for(18431).mode == nb.MODE_TILES
+    p = nb.nbody_plan_for(18432)
     assert p.mode == nb.MODE_PAIRS and p.band == 512 and p.tpl == 4
+    p = nb.nbody_plan_for(24576)
+    assert p.mode == nb.MODE_PAIRS and p.band == 512 and p.tpl == 8
     p = nb.nbody_plan_for(65536)
     assert p.mode == nb.MODE_PAIRS and p.band == 512 and p.tpl == 8
     p = nb.nbody_plan_for(1 << 20)
