@@ -22,10 +22,10 @@
 //   * The inner step costs 12 VALU instructions + 1 v_rsq_f32 per interaction
 //     (13 + 1 with the potential): 3 sub, 3 FMA for q, rsq, 3 mul for m inv^3,
 //     3 FMA into a, 1 FMA into p.
-//   * Two-level accumulation: up to 256 sources go into fresh partial sums,
-//     which are then added to compensated running totals (TwoSum with a
-//     separate error sum), so the fp32 summation error stays near the
-//     per-term rounding for any N.
+//   * Two-level accumulation: up to 256 sources (in pair mode, one band-pair
+//     item) go into fresh partial sums, which are then added to compensated
+//     running totals (TwoSum with a separate error sum), so the fp32 summation
+//     error stays near the per-term rounding for any N.
 //   * split-j: blockIdx.y selects a chunk of sources; with more than one chunk
 //     the partial sums go to scratch and a second kernel adds them in ascending
 //     chunk order (the multi-thread-per-row idea for small N of the GPU Gems 3
@@ -36,8 +36,9 @@
 // Sections below: the one-sided tile kernels (SCALAR, LDS, READLANE), the
 // small-N kernel (SMALL: one kernel per evaluation or step), the
 // pair-symmetric kernel (PAIRS: each unordered pair once, applied to both
-// bodies), the near field over cell lists, the ordered combine / Euler
-// kernels, diagnostics and layout conversion.
+// bodies), the ordered combine / Euler kernels, the shards of a split
+// evaluation, diagnostics, the near field over cell lists and layout
+// conversion.
 #include "kernels.h"
 
 namespace nbk {
