@@ -326,10 +326,16 @@ unsigned grid_x(int64_t n, int tpl, int wg)
     return (unsigned)((n + per - 1) / per);
 }
 
+// Largest N any entry point takes: body indices, tile cursors and chunk ends
+// are 32-bit in the kernels and run up to a few tiles past N, so N stays a
+// safe distance below 2^31 (an evaluation at 2^30 bodies is ~10^18
+// interactions, days of work).
+constexpr int64_t kMaxN = int64_t(1) << 30;
+
 int check_n(int64_t n)
 {
     if (n < 0) return fail(NBODY_EINVAL, "N=%lld must be >= 0", (long long)n);
-    if (n > INT32_MAX) return fail(NBODY_EINVAL, "N=%lld exceeds 2^31-1", (long long)n);
+    if (n > kMaxN) return fail(NBODY_EINVAL, "N=%lld exceeds 2^30", (long long)n);
     return NBODY_OK;
 }
 

@@ -120,7 +120,7 @@ typedef struct nbody_plan {
 /*
  * nbody_accel - accelerations, and optionally potentials, of all N bodies.
  *   pos_xyzm : N bodies (x, y, z, m), read only.
- *   N        : body count, 0 <= N <= 2^31 - 1. N = 0 enqueues nothing.
+ *   N        : body count, 0 <= N <= 2^30 (every entry point). N = 0 enqueues nothing.
  *   eps2     : softening squared; must be a positive, finite, normal float.
  *   acc_out  : N records written as (ax, ay, az, 0). Must not overlap pos_xyzm.
  *   pot_out  : N floats p_i, or NULL to skip the potential. Must not overlap

@@ -74,7 +74,8 @@ def test_n_zero_is_a_no_op(nb):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(n=-1), 1), (dict(n=2**31), 1), (dict(pos=None), 1), (dict(acc=None), 1),
+    (dict(n=-1), 1), (dict(n=2**31), 1), (dict(n=2**30 + 1), 1), (dict(pos=None), 1),
+    (dict(acc=None), 1),
     (dict(eps2=0.0), 1), (dict(eps2=-1e-4), 1), (dict(eps2=math.nan), 1),
     (dict(eps2=math.inf), 1), (dict(eps2=1e-40), 1),
     (dict(pos=A + 4), 2), (dict(acc=B + 8), 2), (dict(pot=B + 2), 2),
