@@ -150,10 +150,12 @@ int wide_cells(int64_t n, int64_t ncell, bool *wide)
     return NBODY_OK;
 }
 
-// Largest N the automatic plan gives to NBODY_MODE_SMALL, and the smallest it
-// gives to NBODY_MODE_PAIRS.
-constexpr int64_t kSmallMaxN = 7680;
-constexpr int64_t kPairsMinN = 18432;
+// Largest N the automatic plan gives to NBODY_MODE_SMALL; pair-symmetric bands
+// (scratch permitting) take every N above it.
+constexpr int64_t kSmallMaxN = 6656;
+// Largest N whose automatic band is 256 bodies (4 targets per lane): many
+// small work items fill the GPU there; above it, 512-2048 with 8 per lane.
+constexpr int64_t kBand256MaxN = 49151;
 
 int valid_tpl(int t) { return t == 1 || t == 2 || t == 4 || t == 8; }
 
@@ -162,7 +164,7 @@ int valid_tpl(int t) { return t == 1 || t == 2 || t == 4 || t == 8; }
 // memory (about 18 GB on MI355X, enough for N = 2^20 with 2048-body bands).
 constexpr size_t kPairsScratchShare = 16;
 
-int valid_band(int b) { return b == 512 || b == 1024 || b == 2048; }
+int valid_band(int b) { return b == 256 || b == 512 || b == 1024 || b == 2048; }
 
 size_t pairs_scratch(int64_t n, int band)
 {
@@ -171,14 +173,14 @@ size_t pairs_scratch(int64_t n, int band)
 }
 
 // Automatic layout, chosen by measurement on MI355X (layout sweeps of the
-// five workloads and of uniform cubes from N = 1024 to 98304):
-//   - up to N = 7680 (small mode measured faster at 7168, tiles at 8192), the
-//     small-N kernel (one kernel per evaluation or step): 4 targets per
-//     workgroup to N = 2048, 8 to 6144, 16 above;
-//   - from N = 18432 up (tiles measured faster at 16384), pair-symmetric bands
-//     when their scratch fits: the largest band that still yields at least 64
-//     work items per compute unit, 4 targets per lane below N = 24576 and 8
-//     from there;
+// five workloads and of uniform cubes from N = 1024 to 131072):
+//   - up to N = 6656 (small mode measured fastest at 6144, 256-body pair bands
+//     at 7168), the small-N kernel (one kernel per evaluation or step): 4
+//     targets per workgroup to N = 2048, 8 to 6144, 16 above;
+//   - above it, pair-symmetric bands when their scratch fits: 256 bodies with
+//     4 targets per lane to N = 49151 (even with 512 at 49152, ahead by 18 %
+//     at 20480), then the largest band that still yields at least 64 work
+//     items per compute unit, with 8 targets per lane;
 //   - otherwise one-sided tiles with the LDS broadcast and one target per lane:
 //     every VALU operand of the inner step is then a VGPR, which issues about
 //     twice as fast as an SGPR operand; 512-thread workgroups (512-body LDS
@@ -188,6 +190,21 @@ size_t pairs_scratch(int64_t n, int band)
 //     N = 65536 up and 1 below.
 int small_tw(int64_t n) { return n <= 2048 ? 4 : (n <= 6144 ? 8 : 16); }
 
+// The automatic pair band for N and a requested tpl (0 = any), or 0 when no
+// band's scratch fits.
+int auto_band(int64_t n, int tpl, const DeviceFacts &dev)
+{
+    const size_t cap = dev.mem_bytes / kPairsScratchShare;
+    if (n <= kBand256MaxN && tpl != 8) return pairs_scratch(n, 256) <= cap ? 256 : 0;
+    for (int band : {2048, 1024, 512}) {
+        const int64_t nb = (n + band - 1) / band;
+        const int64_t items = nb * (nb / 2 + 1);
+        if (pairs_scratch(n, band) <= cap && (items >= (int64_t)dev.cus * 64 || band == 512))
+            return band;
+    }
+    return 0;
+}
+
 void auto_plan(int64_t n, const DeviceFacts &dev, nbody_plan *p)
 {
     const bool big = n >= 65536;
@@ -196,18 +213,12 @@ void auto_plan(int64_t n, const DeviceFacts &dev, nbody_plan *p)
         if (n <= kSmallMaxN && p->bcast == NBODY_BCAST_AUTO && p->tpl == 0 && p->splits == 0 &&
             p->wg == 0 && p->band == 0)
             p->mode = NBODY_MODE_SMALL;
-        if (n >= kPairsMinN && p->bcast == NBODY_BCAST_AUTO && p->tpl == 0 && p->splits == 0 &&
+        if (n > kSmallMaxN && p->bcast == NBODY_BCAST_AUTO && p->tpl == 0 && p->splits == 0 &&
             p->wg == 0) {
-            for (int band : {2048, 1024, 512}) {
-                if (p->band != 0 && p->band != band) continue;
-                const int64_t nb = (n + band - 1) / band;
-                const int64_t items = nb * (nb / 2 + 1);
-                if (pairs_scratch(n, band) <= dev.mem_bytes / kPairsScratchShare &&
-                    (items >= (int64_t)dev.cus * 64 || band == 512)) {
-                    p->mode = NBODY_MODE_PAIRS;
-                    p->band = band;
-                    break;
-                }
+            const int band = p->band != 0 ? p->band : auto_band(n, 0, dev);
+            if (band != 0 && pairs_scratch(n, band) <= dev.mem_bytes / kPairsScratchShare) {
+                p->mode = NBODY_MODE_PAIRS;
+                p->band = band;
             }
         }
     }
@@ -219,9 +230,10 @@ void auto_plan(int64_t n, const DeviceFacts &dev, nbody_plan *p)
     }
     if (p->mode == NBODY_MODE_PAIRS) {
         p->bcast = NBODY_BCAST_LDS;
-        if (p->tpl == 0) p->tpl = n >= 24576 ? 8 : 4;
+        if (p->band == 0) p->band = auto_band(n, p->tpl, dev);
+        if (p->band == 0) p->band = (p->tpl == 8 || n > kBand256MaxN) ? 512 : 256;
+        if (p->tpl == 0) p->tpl = (p->band == 256 || n < 24576) ? 4 : 8;
         p->wg = 256;
-        if (p->band == 0) p->band = n >= (1 << 19) ? 2048 : (n >= (1 << 17) ? 1024 : 512);
         return;
     }
     if (p->bcast == NBODY_BCAST_AUTO) p->bcast = NBODY_BCAST_LDS;
@@ -297,7 +309,10 @@ int make_plan(int64_t n, const nbody_plan *user, int *dev_out, nbody_plan *p)
         return fail(NBODY_EINVAL,
                     "plan.wg=%d must be 0 or 256 (or 64, 128, 512 with the LDS broadcast)", p->wg);
     if (p->band != 0 && !valid_band(p->band))
-        return fail(NBODY_EINVAL, "plan.band=%d must be 0, 512, 1024 or 2048", p->band);
+        return fail(NBODY_EINVAL, "plan.band=%d must be 0, 256, 512, 1024 or 2048", p->band);
+    if (p->band == 256 && p->tpl == 8)
+        return fail(NBODY_EINVAL, "plan.band=256 takes plan.tpl 4 (an i-set of 8 targets per "
+                                  "lane is 512 bodies)");
     if (p->mode == NBODY_MODE_PAIRS &&
         ((p->bcast != 0 && p->bcast != NBODY_BCAST_LDS) ||
          (p->tpl != 0 && p->tpl != 4 && p->tpl != 8) || p->splits != 0 ||

@@ -1401,6 +1401,7 @@ hipError_t launch_pairs(int band, int tpl, bool pot, const PairsArgs &args, hipS
 {
     const void *fn = nullptr;
     if (tpl == 4) {
+        if (band == 256) fn = pairs_fn<4, 256>(pot);
         if (band == 512) fn = pairs_fn<4, 512>(pot);
         if (band == 1024) fn = pairs_fn<4, 1024>(pot);
         if (band == 2048) fn = pairs_fn<4, 2048>(pot);

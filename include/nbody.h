@@ -92,8 +92,9 @@ enum {
  *   wg     - threads per workgroup: 64, 128, 256 or 512 for NBODY_BCAST_LDS (also
  *            the LDS tile, in bodies), 256 for the other schemes.
  *   mode   - NBODY_MODE_*. The fields above describe NBODY_MODE_TILES. With
- *            NBODY_MODE_PAIRS only `band` (512, 1024 or 2048 bodies) and `tpl`
- *            (4 or 8 targets per lane; 0 = automatic) may be set; the output then has
+ *            NBODY_MODE_PAIRS only `band` (256, 512, 1024 or 2048 bodies) and
+ *            `tpl` (4 or 8 targets per lane, 4 only with 256-body bands; 0 =
+ *            automatic) may be set; the output then has
  *            splits = number of bands = partial-sum slots per body, chunk =
  *            band, bcast = LDS, wg = 256. Its scratch
  *            is splits x N x 16 bytes (8.6 GB at N = 2^20 with 2048-body bands);

@@ -198,10 +198,11 @@ def test_single_body(nb):
 
 BANDS = [512, 1024, 2048]
 PAIR_TPL = [4, 8]
+# (band, tpl): every instantiated pair kernel (256-body bands take 4 targets per lane only)
+PAIR_LAYOUTS = [(256, 4)] + [(b, t) for b in BANDS for t in PAIR_TPL]
 
 
-@pytest.mark.parametrize("tpl", PAIR_TPL)
-@pytest.mark.parametrize("band", BANDS)
+@pytest.mark.parametrize("band,tpl", PAIR_LAYOUTS)
 @pytest.mark.parametrize("n", [1, 2, 3, 65, 257, 1000, 2049, 4097])
 def test_pairs_small_n(nb, n, band, tpl):
     eps2 = np.float32(1e-4)
@@ -211,8 +212,7 @@ def test_pairs_small_n(nb, n, band, tpl):
     assert_accel_parity(acc, pot, _ref(n, 100 + n, eps2), what=f"N={n} {plan}")
 
 
-@pytest.mark.parametrize("tpl", PAIR_TPL)
-@pytest.mark.parametrize("band", BANDS)
+@pytest.mark.parametrize("band,tpl", PAIR_LAYOUTS)
 def test_pairs_mid_n(nb, band, tpl):
     """N = 20011 (prime): odd and even band counts, a ragged last band."""
     import oracle
@@ -227,20 +227,23 @@ def test_pairs_mid_n(nb, band, tpl):
 
 
 @pytest.mark.parametrize("tpl", PAIR_TPL)
-@pytest.mark.parametrize("n,band", [(4096, 512), (5000, 1024), (6144, 2048), (8192, 1024)])
+@pytest.mark.parametrize("n,band", [(4096, 512), (5000, 1024), (6144, 2048), (8192, 1024),
+                                    (2560, 256), (2300, 256)])
 def test_pairs_even_and_odd_band_counts(nb, n, band, tpl):
-    """Band counts 8, 5, 3 and 8: the opposite band of an even count is owned once."""
+    """Band counts 8, 5, 3, 8, 10 and 9: the opposite band of an even count is owned once."""
+    if band == 256 and tpl == 8:
+        pytest.skip("256-body bands take 4 targets per lane")
     pos, _ = _bodies(n, 31)
     acc, pot = gpu_accel(pos, 1e-4, pot=True, plan=dict(mode="pairs", band=band, tpl=tpl))
     assert_accel_parity(acc, pot, _ref(n, 31, np.float32(1e-4)),
                         what=f"N={n} band={band} tpl={tpl}")
 
 
-@pytest.mark.parametrize("tpl", PAIR_TPL)
-def test_pairs_invariants(nb, tpl):
+@pytest.mark.parametrize("band,tpl", [(1024, 4), (1024, 8), (256, 4)])
+def test_pairs_invariants(nb, band, tpl):
     """Determinism, exact mass doubling, potential-independent acceleration, dyadic
     translation, zero-mass padding (same band count): all bit-exact."""
-    plan = dict(mode="pairs", band=1024, tpl=tpl)
+    plan = dict(mode="pairs", band=band, tpl=tpl)
     pos, _ = _bodies(6000, 41)
     a1, p1 = gpu_accel(pos, 1e-4, plan=plan)
     a2, p2 = gpu_accel(pos, 1e-4, plan=plan)
@@ -272,23 +275,20 @@ def test_pairs_plan_beyond_grid_limit_rejected(nb):
 
 
 def test_auto_plan_modes(nb):
-    """Small-N kernel up to N = 7680, tiles above, pair-symmetric bands from N = 18432 up
-    (scratch permitting), with the measured targets per workgroup and per lane."""
-    for n, tw in ((1, 4), (2048, 4), (2049, 8), (6144, 8), (6145, 16), (7680, 16)):
+    """Small-N kernel up to N = 6656, pair-symmetric bands above (256 bodies and 4 targets per
+    lane to N = 49151, larger bands and 8 per lane from there), with the measured targets per
+    workgroup in small mode."""
+    for n, tw in ((1, 4), (2048, 4), (2049, 8), (6144, 8), (6145, 16), (6656, 16)):
         p = nb.nbody_plan_for(n)
         assert p.mode == nb.MODE_SMALL and p.splits == 1 and p.tpl == tw and p.wg == 256, n
-    assert nb.nbody_plan_for(7681).mode == nb.MODE_TILES
-    assert nb.nbody_plan_for(18431).mode == nb.MODE_TILES
-    p = nb.nbody_plan_for(18432)
-    assert p.mode == nb.MODE_PAIRS and p.band == 512 and p.tpl == 4
-    p = nb.nbody_plan_for(24576)
-    assert p.mode == nb.MODE_PAIRS and p.band == 512 and p.tpl == 8
-    p = nb.nbody_plan_for(65536)
-    assert p.mode == nb.MODE_PAIRS and p.band == 512 and p.tpl == 8
-    p = nb.nbody_plan_for(1 << 20)
-    assert p.mode == nb.MODE_PAIRS and p.band == 2048 and p.splits == 512 and p.tpl == 8
-    p = nb.nbody_plan_for(300007)
-    assert p.mode == nb.MODE_PAIRS and p.band == 1024 and p.splits == 293
+    for n in (6657, 18432, 49151):
+        p = nb.nbody_plan_for(n)
+        assert p.mode == nb.MODE_PAIRS and p.band == 256 and p.tpl == 4, n
+    for n, band in ((49152, 512), (65536, 512), (131072, 512), (300007, 1024), (1 << 20, 2048)):
+        p = nb.nbody_plan_for(n)
+        assert p.mode == nb.MODE_PAIRS and p.band == band and p.tpl == 8, n
+    assert nb.nbody_plan_for(300007).splits == 293
+    assert nb.nbody_plan_for(1 << 20).splits == 512
 
 
 # ------------------------------------------------------------------ degenerate inputs
