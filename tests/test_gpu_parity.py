@@ -226,13 +226,11 @@ def test_pairs_mid_n(nb, band, tpl):
     assert_accel_parity(acc, pot, ref, idx=idx, what=f"N={n} pairs band={band} tpl={tpl}")
 
 
-@pytest.mark.parametrize("tpl", PAIR_TPL)
-@pytest.mark.parametrize("n,band", [(4096, 512), (5000, 1024), (6144, 2048), (8192, 1024),
-                                    (2560, 256), (2300, 256)])
+@pytest.mark.parametrize("n,band,tpl", [(n, b, t) for n, b in ((4096, 512), (5000, 1024),
+                                                                   (6144, 2048), (8192, 1024))
+                                         for t in PAIR_TPL] + [(2560, 256, 4), (2300, 256, 4)])
 def test_pairs_even_and_odd_band_counts(nb, n, band, tpl):
     """Band counts 8, 5, 3, 8, 10 and 9: the opposite band of an even count is owned once."""
-    if band == 256 and tpl == 8:
-        pytest.skip("256-body bands take 4 targets per lane")
     pos, _ = _bodies(n, 31)
     acc, pot = gpu_accel(pos, 1e-4, pot=True, plan=dict(mode="pairs", band=band, tpl=tpl))
     assert_accel_parity(acc, pot, _ref(n, 31, np.float32(1e-4)),
