@@ -21,6 +21,7 @@ HIPCC_FLAGS = [
     "-fPIC",
     "-shared",
     "-ffp-contract=fast",
+    "-fvisibility=hidden",
     "-mcode-object-version=5",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",

@@ -12,7 +12,11 @@
 #include <string>
 #include <utility>
 
+// The library is built with hidden symbol visibility; only the C ABI declared
+// in nbody.h is exported.
+#pragma GCC visibility push(default)
 #include "../../include/nbody.h"
+#pragma GCC visibility pop
 #include "kernels.h"
 
 namespace {
@@ -587,8 +591,6 @@ int step_soa_impl(float *x, float *y, float *z, const float *m, float *vx, float
     return ok();
 }
 
-}  // namespace
-
 // First band of shard s when nb bands are split into S contiguous ranges.
 int shard_band(int s, int nb, int S) { return (int)((int64_t)s * nb / S); }
 
@@ -639,6 +641,8 @@ int shard_impl(const nbody_f4 *pos, int64_t N, float eps2, int32_t shard, int32_
     if (e != hipSuccess) return hip_fail(e, "shard combine launch");
     return ok();
 }
+
+}  // namespace
 
 extern "C" {
 

@@ -45,6 +45,8 @@ def test_exports_every_declared_symbol(nb):
     exported = set(re.findall(r" T (nbody_\w+)", out))
     assert set(declared_functions()) <= exported
     assert set(nb.EXPORTS) == set(declared_functions())
+    # nothing else: the kernels and launchers stay internal (hidden visibility)
+    assert set(re.findall(r" T (\S+)", out)) == set(declared_functions())
 
 
 def test_library_links_no_oracle_and_no_torch(nb):
