@@ -214,6 +214,26 @@ __device__ __forceinline__ float in_vgpr(float s)
 // (used to keep prefetch loads ahead of the arithmetic that hides them).
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// Race probe, compiled in only for the test build of the library
+// (-DNBK_RACE_PROBE): as soon as a barrier hands an LDS slot back for reuse,
+// the thread that will refill it writes NaN there, so a reader that a missing
+// or misplaced barrier left behind reads NaN (or the next data) and the
+// outputs show it. Correct barriers leave every result bit unchanged.
+#ifdef NBK_RACE_PROBE
+constexpr bool kRaceProbe = true;
+#else
+constexpr bool kRaceProbe = false;
+#endif
+
+__device__ __forceinline__ void probe_poison(float4 &slot)
+{
+    if constexpr (kRaceProbe) {
+        const float q = __builtin_nanf("");
+        slot = make_float4(q, q, q, q);
+        asm volatile("" ::: "memory");  // the store must stay although a refill follows
+    }
+}
+
 __device__ __forceinline__ void chunk_range(const AccelArgs &k, int &j0, int &j1)
 {
     const long long a = (long long)blockIdx.y * k.chunk;
@@ -361,6 +381,7 @@ __global__ void __launch_bounds__(WG) accel_lds(AccelArgs k)
     for (int it = 0; it < ntiles; ++it) {
         const int cur = it & 1;
         const bool more = it + 1 < ntiles;
+        if (more) probe_poison(tile[cur ^ 1][threadIdx.x]);
         jl += WG;
         // raw prefetch of the next tile (index clamped into the chunk); the
         // zero-padding select happens at the store below
@@ -444,6 +465,9 @@ __global__ void __launch_bounds__(256) accel_small(SmallArgs k)
     for (int it = 0; it < ntiles; ++it) {
         const bool more = it + 1 < ntiles;
         const int nb = (it + 1) * TS + threadIdx.x;  // this thread's first body of the next tile
+        if (kRaceProbe && more) {
+            for (int l = 0; l < L; ++l) probe_poison(tile[(it + 1) & 1][l * WG + threadIdx.x]);
+        }
         float4 r[L];
 #pragma unroll
         for (int l = 0; l < L; ++l) {
@@ -781,6 +805,9 @@ __device__ __forceinline__ void pairs_item(const PairsArgs &k, int A, int B, int
                 if (body < k.n) k.part[(size_t)slot_i * (size_t)k.n + body] = s;
             }
             __syncthreads();
+            if constexpr (kRaceProbe) {
+                for (int t = 0; t < T; ++t) probe_poison(sh.ired[w][t * 64 + lane]);
+            }
             continue;
         }
         // Sequential form through the block and slot rows (all waves are past
@@ -807,6 +834,8 @@ __device__ __forceinline__ void pairs_item(const PairsArgs &k, int A, int B, int
             }
             __syncthreads();
         }
+        probe_poison(sh.jblk[w][lane]);
+        probe_poison(sh.jsum[w][lane]);
     }
     if constexpr (SYM) {
         for (int i = threadIdx.x; i < BD; i += 64 * W) {
@@ -1226,6 +1255,7 @@ __global__ void __launch_bounds__(256) p2p_wg_kernel(P2PArgs k, Lists lists)
             const int cnt = se - j0 < 256 ? se - j0 : 256;
             int e2 = e, j2 = j0, se2 = se;
             const bool have2 = next_tile256(k, lists, c, hi, e2, j2, se2);
+            if (have2) probe_poison(tile[buf ^ 1][tid]);
             const int jn = j2 + tid;
             float4 r = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             if (have2) r = k.pos[jn < se2 ? jn : se2 - 1];  // raw prefetch of the next tile
@@ -1254,6 +1284,7 @@ __global__ void __launch_bounds__(256) p2p_wg_kernel(P2PArgs k, Lists lists)
             se = se2;
             have = have2;
         }
+        probe_poison(tile[0][tid]);  // the next chunk's first tile goes here
         if (i < te) {
             const Sums<1, POT> res = result(tot);
             k.acc_out[i] = make_float4(res.ax[0], res.ay[0], res.az[0], 0.0f);

@@ -1,0 +1,142 @@
+"""Race probe (GPU): the test build of the library refills every LDS slot that a barrier
+hands back only after first writing NaN into it, so a missing or misplaced barrier shows up
+as NaN or changed outputs. With the barriers in place its results must equal the library's
+bit for bit, with no NaN, for tile counts and sizes at tile boundaries +- 1 in every mode that
+shares LDS between waves (tiles, small N, pair bands, the shared-tile near-field kernel)."""
+
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import pytest
+
+import workloads
+from gpu_util import to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nb():
+    import direct_all_pairs_amd
+
+    return direct_all_pairs_amd
+
+
+@pytest.fixture(scope="module")
+def probe(nb):
+    from direct_all_pairs_amd import build
+
+    if not build.PROBE_LIB.exists():
+        pytest.fail(f"{build.PROBE_LIB} is not built (run __graft_entry__.build())")
+    lib = ctypes.CDLL(str(build.PROBE_LIB))
+    vp, i64, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
+    lib.nbody_accel_plan.argtypes = [vp, i64, f32, vp, vp, ctypes.POINTER(nb.nbody_plan), vp]
+    lib.nbody_step_plan.argtypes = [vp, vp, i64, f32, f32, i64, ctypes.POINTER(nb.nbody_plan), vp]
+    lib.nbody_near_grid.argtypes = [vp, i64, f32, ctypes.POINTER(ctypes.c_float), f32,
+                                    ctypes.POINTER(ctypes.c_int32), vp, vp, vp]
+    lib.nbody_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+def _stream():
+    import torch
+
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _accel_both(nb, probe, pos_h, eps2, plan):
+    import torch
+
+    n = pos_h.shape[0]
+    pd = to_dev(pos_h)
+    outs = []
+    for which in ("library", "probe"):
+        acc = torch.full((n, 4), 7.0, device="cuda")
+        pot = torch.full((n,), 7.0, device="cuda")
+        p = nb.make_plan(**plan)
+        if which == "library":
+            nb.nbody_accel_plan(pd, n, eps2, acc, pot, p)
+        else:
+            rc = probe.nbody_accel_plan(pd.data_ptr(), n, eps2, acc.data_ptr(), pot.data_ptr(),
+                                        ctypes.byref(p), _stream())
+            assert rc == 0, probe.nbody_last_error()
+        torch.cuda.synchronize()
+        outs.append((acc.cpu().numpy(), pot.cpu().numpy()))
+    return outs
+
+
+def _assert_same(outs, what):
+    (a0, p0), (a1, p1) = outs
+    assert not np.isnan(a1).any() and not np.isnan(p1).any(), f"{what}: NaN from the probe build"
+    assert np.array_equal(a0, a1) and np.array_equal(p0, p1), f"{what}: probe build differs"
+
+
+PROBE_CASES = (
+    [dict(bcast="lds", tpl=1, wg=wg, splits=s) for wg in (64, 128, 256, 512) for s in (1, 3)]
+    + [dict(mode="small", tpl=tw) for tw in (4, 8, 16, 32)]
+    + [dict(mode="pairs", band=b, tpl=t)
+       for b, t in ((256, 4), (512, 4), (512, 8), (1024, 4), (1024, 8), (2048, 8))]
+)
+
+
+def _sizes(plan):
+    if plan.get("mode") == "small":
+        return (2047, 2049, 3073)
+    tile = plan.get("band") or plan["wg"]
+    k = 4 if plan.get("mode") == "pairs" else 6
+    return (k * tile - 1, k * tile + 1)
+
+
+@pytest.mark.parametrize("plan", PROBE_CASES, ids=lambda p: "-".join(f"{k}{v}" for k, v in p.items()))
+def test_probe_build_matches_library(nb, probe, plan):
+    for n in _sizes(plan):
+        pos, _ = workloads.random_bodies(n, seed=70 + n)
+        _assert_same(_accel_both(nb, probe, pos, 1e-4, plan), f"N={n} {plan}")
+
+
+def test_probe_build_small_steps(nb, probe):
+    """Small-mode steps (alternating position buffers) agree bit for bit over three steps."""
+    import torch
+
+    n = 3073
+    pos_h, vel_h = workloads.random_bodies(n, seed=9)
+    res = []
+    for which in ("library", "probe"):
+        pos, vel = to_dev(pos_h), to_dev(vel_h)
+        p = nb.make_plan(mode="small", tpl=8)
+        if which == "library":
+            nb.nbody_step_plan(pos, vel, n, 1e-3, 1e-4, 3, p)
+        else:
+            rc = probe.nbody_step_plan(pos.data_ptr(), vel.data_ptr(), n, 1e-3, 1e-4, 3,
+                                       ctypes.byref(p), _stream())
+            assert rc == 0, probe.nbody_last_error()
+        torch.cuda.synchronize()
+        res.append((pos.cpu().numpy(), vel.cpu().numpy()))
+    assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])
+
+
+def test_probe_build_shared_tile_near_field(nb, probe):
+    """Eight large cells (2 x 2 x 2 grid, ~2500 bodies each): the 256-thread shared-tile
+    near-field kernel, several target chunks and source tiles per cell."""
+    import torch
+
+    n = 20000
+    pos_h, _ = workloads.random_bodies(n, seed=12)
+    pd = to_dev(pos_h)
+    lo, h, dims = (-1.0, -1.0, -1.0), 1.0, (2, 2, 2)
+    outs = []
+    for which in ("library", "probe"):
+        acc = torch.full((n, 4), 7.0, device="cuda")
+        pot = torch.full((n,), 7.0, device="cuda")
+        if which == "library":
+            nb.nbody_near_grid(pd, n, 1e-4, lo, h, dims, acc, pot)
+        else:
+            rc = probe.nbody_near_grid(pd.data_ptr(), n, 1e-4, (ctypes.c_float * 3)(*lo), h,
+                                       (ctypes.c_int32 * 3)(*dims), acc.data_ptr(),
+                                       pot.data_ptr(), _stream())
+            assert rc == 0, probe.nbody_last_error()
+        torch.cuda.synchronize()
+        outs.append((acc.cpu().numpy(), pot.cpu().numpy()))
+    _assert_same(outs, "near grid, 8 cells")
