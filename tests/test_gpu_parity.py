@@ -272,6 +272,20 @@ def test_pairs_plan_beyond_grid_limit_rejected(nb):
     assert rc == nb.NBODY_EINVAL and "grid" in nb.nbody_last_error()
 
 
+def test_scratch_allocation_failure_reported_and_recovered(nb):
+    """A layout whose scratch cannot be allocated (4096 split chunks of 2^30 bodies: 70 TB)
+    fails with NBODY_ENOMEM before any launch (fake, aligned pointers: nothing is
+    dereferenced), and the library keeps working: the next evaluation is within the bound."""
+    n = 1 << 30
+    rc = nb.nbody_accel_plan(1 << 20, n, 1e-4, 1 << 46, None,
+                             plan=dict(bcast="lds", tpl=1, wg=256, splits=4096), stream=0,
+                             check=False)
+    assert rc == nb.NBODY_ENOMEM and "hipMalloc" in nb.nbody_last_error()
+    pos, _ = _bodies(3000, 44)
+    acc, pot = gpu_accel(pos, 1e-4)
+    assert_accel_parity(acc, pot, _ref(3000, 44, np.float32(1e-4)), what="after ENOMEM")
+
+
 def test_auto_plan_modes(nb):
     """Small-N kernel up to N = 6656, pair-symmetric bands above (256 bodies and 4 targets per
     lane to N = 49151, larger bands and 8 per lane from there), with the measured targets per
