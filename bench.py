@@ -73,8 +73,10 @@ def measured_traffic(kernel_hash: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(pos_h, eps2, budget_s: float):
-    """Time the fp64 oracle (as it stands) on a target sample of the same workload."""
+def cpu_baseline(pos_h, eps2, budget_s: float, gpu_acc=None, gpu_pot=None):
+    """Time the fp64 oracle (as it stands) on a target sample of the same workload; with the
+    GPU's accelerations (and potentials) of that workload, also report their largest error on
+    the sample in units of the per-body bounds B_i (and P_i)."""
     import numpy as np
 
     import oracle
@@ -91,16 +93,24 @@ def cpu_baseline(pos_h, eps2, budget_s: float):
     nt = int(max(64, min(n, budget_s / max(per_target, 1e-9))))
     idx = rng.integers(0, n, nt)
     t0 = time.perf_counter()
-    oracle.accel(pos_h, eps2, targets=idx)
+    ref = oracle.accel(pos_h, eps2, targets=idx)
     t = time.perf_counter() - t0
     rate = nt * n / t
-    return {
+    out = {
         "value": rate / 1e9,
         "unit": "G interactions/s",
         "cores": threads,
         "kind": "oracle",
         "sample": f"{nt} random targets x all {n} sources (fp64 accel+pot+bounds), {t:.1f} s",
     }
+    if gpu_acc is not None:
+        a = np.asarray(gpu_acc)[idx, :3].astype(np.float64)
+        err = np.linalg.norm(a - ref["acc"], axis=1)
+        out["gpu_max_err_over_B"] = float(np.max(err / ref["bound_a"]))
+        if gpu_pot is not None:
+            e_p = np.abs(np.asarray(gpu_pot)[idx].astype(np.float64) - ref["pot"])
+            out["gpu_max_pot_err_over_P"] = float(np.max(e_p / ref["bound_p"]))
+    return out
 
 
 class ClockSampler:
@@ -522,7 +532,10 @@ def main(argv=None) -> int:
             "momentum_change": [b - a for a, b in zip(diag0["momentum"], diag1["momentum"])],
         }
     if args.cpu_budget > 0:
-        out["cpu_baseline"] = cpu_baseline(w.pos, w.eps2, args.cpu_budget)
+        # the GPU results of the last timed evaluation, checked on the oracle's sample
+        gpu_acc = acc.cpu().numpy() if not stepping else None
+        gpu_pot = pot.cpu().numpy() if (pot is not None and not stepping) else None
+        out["cpu_baseline"] = cpu_baseline(w.pos, w.eps2, args.cpu_budget, gpu_acc, gpu_pot)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
