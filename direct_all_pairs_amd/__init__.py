@@ -36,12 +36,13 @@ class NbodyError(RuntimeError):
 class nbody_plan(ctypes.Structure):
     _fields_ = [("bcast", ctypes.c_int32), ("tpl", ctypes.c_int32),
                 ("splits", ctypes.c_int32), ("chunk", ctypes.c_int32), ("wg", ctypes.c_int32),
-                ("mode", ctypes.c_int32), ("band", ctypes.c_int32)]
+                ("mode", ctypes.c_int32), ("band", ctypes.c_int32), ("passes", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {"mode": MODE_NAMES.get(self.mode, self.mode),
                 "bcast": BCAST_NAMES.get(self.bcast, self.bcast), "tpl": self.tpl,
-                "splits": self.splits, "chunk": self.chunk, "wg": self.wg, "band": self.band}
+                "splits": self.splits, "chunk": self.chunk, "wg": self.wg, "band": self.band,
+                "passes": self.passes}
 
 
 # torch (device memory and streams) is imported first: its bundled HIP runtime
@@ -223,12 +224,13 @@ def nbody_plan_for(N: int, want_pot: bool = False) -> nbody_plan:
     return p
 
 
-def make_plan(bcast=0, tpl=0, splits=0, chunk=0, wg=0, mode=0, band=0) -> nbody_plan:
+def make_plan(bcast=0, tpl=0, splits=0, chunk=0, wg=0, mode=0, band=0, passes=0) -> nbody_plan:
     if isinstance(bcast, str):
         bcast = {v: k for k, v in BCAST_NAMES.items()}[bcast]
     if isinstance(mode, str):
         mode = {v: k for k, v in MODE_NAMES.items()}[mode]
-    return nbody_plan(int(bcast), int(tpl), int(splits), int(chunk), int(wg), int(mode), int(band))
+    return nbody_plan(int(bcast), int(tpl), int(splits), int(chunk), int(wg), int(mode), int(band),
+                      int(passes))
 
 
 # ------------------------------------------------------------ torch conveniences

@@ -176,6 +176,26 @@ size_t pairs_scratch(int64_t n, int band)
     return (size_t)nb * (size_t)n * sizeof(float4);
 }
 
+// Grid limit of the second launch dimension (pair items, split-j chunks).
+constexpr int64_t kMaxGridY = 65535;
+
+// Pair evaluation in `passes` passes over band ranges of at most
+// ceil(nb / passes) bands each: per pass the A sides of the range's own bodies
+// ((nb/2 + 1) slots each), the B sides of every body from the range's bands,
+// and across passes the compensated running totals (two records per body),
+// plus, for a step, the accelerations handed to the Euler kernel.
+size_t pairs_pass_scratch(int64_t n, int band, int64_t passes, bool step)
+{
+    const int64_t nb = (n + band - 1) / band;
+    const int64_t per = (nb + passes - 1) / passes;
+    const int64_t own = per * band < n ? per * band : n;
+    const int64_t recs = (nb / 2 + 1) * own + per * n + 2 * n + (step ? n : 0);
+    return (size_t)recs * sizeof(float4);
+}
+
+// Band range [first, end) of pass q of `passes` over nb bands (balanced).
+int pass_band(int64_t q, int64_t nb, int64_t passes) { return (int)(q * nb / passes); }
+
 // Automatic layout, chosen by measurement on MI355X (layout sweeps of the
 // five workloads and of uniform cubes from N = 1024 to 131072):
 //   - up to N = 6656 (small mode measured fastest at 6144, 256-body pair bands
@@ -194,19 +214,30 @@ size_t pairs_scratch(int64_t n, int band)
 //     N = 65536 up and 1 below.
 int small_tw(int64_t n) { return n <= 2048 ? 4 : (n <= 6144 ? 8 : 16); }
 
-// The automatic pair band for N and a requested tpl (0 = any), or 0 when no
-// band's scratch fits.
+// The automatic pair band for N and a requested tpl (0 = any): 256 bodies to
+// N = 49151, above it the largest band with at least 64 work items per
+// compute unit (512 at least).
 int auto_band(int64_t n, int tpl, const DeviceFacts &dev)
 {
-    const size_t cap = dev.mem_bytes / kPairsScratchShare;
-    if (n <= kBand256MaxN && tpl != 8) return pairs_scratch(n, 256) <= cap ? 256 : 0;
-    for (int band : {2048, 1024, 512}) {
+    if (n <= kBand256MaxN && tpl != 8) return 256;
+    for (int band : {2048, 1024}) {
         const int64_t nb = (n + band - 1) / band;
-        const int64_t items = nb * (nb / 2 + 1);
-        if (pairs_scratch(n, band) <= cap && (items >= (int64_t)dev.cus * 64 || band == 512))
-            return band;
+        if (nb * (nb / 2 + 1) >= (int64_t)dev.cus * 64) return band;
     }
-    return 0;
+    return 512;
+}
+
+// Passes for a pair evaluation: one while all nb slots per body fit the
+// scratch share of device memory, else the fewest that fit (searched in
+// steps of ~25 %); 0 when even one band per pass does not fit.
+int64_t auto_passes(int64_t n, int band, const DeviceFacts &dev, bool step)
+{
+    const size_t cap = dev.mem_bytes / kPairsScratchShare;
+    if (pairs_scratch(n, band) <= cap) return 1;
+    const int64_t nb = (n + band - 1) / band;
+    for (int64_t q = 2; q <= nb; q = q < 8 ? q + 1 : q + q / 4)
+        if (pairs_pass_scratch(n, band, q, step) <= cap) return q;
+    return pairs_pass_scratch(n, band, nb, step) <= cap ? nb : 0;
 }
 
 void auto_plan(int64_t n, const DeviceFacts &dev, nbody_plan *p)
@@ -220,9 +251,11 @@ void auto_plan(int64_t n, const DeviceFacts &dev, nbody_plan *p)
         if (n > kSmallMaxN && p->bcast == NBODY_BCAST_AUTO && p->tpl == 0 && p->splits == 0 &&
             p->wg == 0) {
             const int band = p->band != 0 ? p->band : auto_band(n, 0, dev);
-            if (band != 0 && pairs_scratch(n, band) <= dev.mem_bytes / kPairsScratchShare) {
+            const int64_t q = p->passes != 0 ? p->passes : auto_passes(n, band, dev, true);
+            if (q != 0 && (n + band - 1) / band / 2 + 1 <= kMaxGridY) {
                 p->mode = NBODY_MODE_PAIRS;
                 p->band = band;
+                p->passes = (int32_t)q;
             }
         }
     }
@@ -235,8 +268,13 @@ void auto_plan(int64_t n, const DeviceFacts &dev, nbody_plan *p)
     if (p->mode == NBODY_MODE_PAIRS) {
         p->bcast = NBODY_BCAST_LDS;
         if (p->band == 0) p->band = auto_band(n, p->tpl, dev);
-        if (p->band == 0) p->band = (p->tpl == 8 || n > kBand256MaxN) ? 512 : 256;
         if (p->tpl == 0) p->tpl = (p->band == 256 || n < 24576) ? 4 : 8;
+        if (p->passes == 0) {
+            // explicit pair mode: if nothing fits, the most passes (the scratch
+            // allocation then reports what is missing)
+            const int64_t q = auto_passes(n, p->band, dev, true);
+            p->passes = (int32_t)(q != 0 ? q : (n + p->band - 1) / p->band);
+        }
         p->wg = 256;
         return;
     }
@@ -261,8 +299,6 @@ void auto_plan(int64_t n, const DeviceFacts &dev, nbody_plan *p)
 // Final chunking. Tiles: chunk is a whole number of tiles (LDS tile or
 // accumulation block) and S = ceil(N / chunk), so no chunk is empty. Pairs:
 // splits = number of bands = number of partial slots, chunk = band.
-// Grid limit of the second launch dimension (pair items, split-j chunks).
-constexpr int64_t kMaxGridY = 65535;
 
 void finish_plan(int64_t n, nbody_plan *p)
 {
@@ -270,14 +306,18 @@ void finish_plan(int64_t n, nbody_plan *p)
         p->splits = 1;
         p->chunk = (int32_t)n;
         p->band = 0;
+        p->passes = 0;
         return;
     }
     if (p->mode == NBODY_MODE_PAIRS) {
         p->splits = (int32_t)((n + p->band - 1) / p->band);
         p->chunk = p->band;
+        if (p->passes < 1) p->passes = 1;
+        if (p->passes > p->splits) p->passes = p->splits;
         return;
     }
     p->band = 0;
+    p->passes = 0;
     const int64_t tile = p->bcast == NBODY_BCAST_LDS ? p->wg : nbk::kFlush;
     int64_t s = p->splits;
     int64_t c = (n + s - 1) / s;
@@ -292,8 +332,12 @@ void finish_plan(int64_t n, nbody_plan *p)
 
 int make_plan(int64_t n, const nbody_plan *user, int *dev_out, nbody_plan *p)
 {
-    *p = user ? *user : nbody_plan{0, 0, 0, 0, 0, 0, 0};
+    *p = user ? *user : nbody_plan{0, 0, 0, 0, 0, 0, 0, 0};
     p->chunk = 0;
+    if (p->passes < 0)
+        return fail(NBODY_EINVAL, "plan.passes=%d must be >= 0", p->passes);
+    if (p->passes != 0 && p->mode != NBODY_MODE_AUTO && p->mode != NBODY_MODE_PAIRS)
+        return fail(NBODY_EINVAL, "plan.passes is for pair mode (NBODY_MODE_PAIRS or AUTO)");
     if (p->mode < 0 || p->mode > NBODY_MODE_SMALL)
         return fail(NBODY_EINVAL, "plan.mode=%d is not a NBODY_MODE_* value", p->mode);
     if (p->mode == NBODY_MODE_SMALL &&
@@ -358,6 +402,45 @@ int check_n(int64_t n)
     return NBODY_OK;
 }
 
+// A pair evaluation in p.passes passes over band ranges (compact layout: the
+// scratch holds one pass's sums, reused, and the running totals). The last pass
+// writes acc/pot, or for a step the accelerations that the Euler kernel reads.
+int enqueue_pair_passes(const float4 *pos, int n, float eps2, float4 *acc_out, float *pot_out,
+                        const nbody_plan &p, int dev, hipStream_t stream, float4 *euler_pos,
+                        float4 *euler_vel, float dt)
+{
+    const bool step = euler_pos != nullptr;
+    const int nb = p.splits, band = p.band;
+    const int64_t per = (nb + p.passes - 1) / p.passes;
+    const int64_t own_max = per * band < n ? per * band : n;
+    void *ws = nullptr;
+    int rc = scratch_get(dev, stream, pairs_pass_scratch(n, band, p.passes, step), &ws);
+    if (rc != NBODY_OK) return rc;
+    float4 *partA = (float4 *)ws;
+    float4 *partB = partA + (size_t)(nb / 2 + 1) * (size_t)own_max;
+    float4 *tot_s = partB + (size_t)per * (size_t)n;
+    float4 *tot_e = tot_s + n;
+    float4 *accbuf = step ? tot_e + n : nullptr;
+    for (int64_t q = 0; q < p.passes; ++q) {
+        const int b0 = pass_band(q, nb, p.passes), b1 = pass_band(q + 1, nb, p.passes);
+        const int own0 = b0 * band;
+        const int own_end = (int64_t)b1 * band < n ? b1 * band : n;
+        nbk::PairsArgs pa{pos, n, eps2, nb, partA, b0, b1, own_end - own0, own0, partB, 1};
+        hipError_t e = nbk::launch_pairs(band, p.tpl, pot_out != nullptr, pa, stream);
+        if (e != hipSuccess) return hip_fail(e, "accel kernel launch");
+        nbk::PassArgs ca{partA, partB, n, band, nb, b0, b1, own0, own_end - own0, tot_s, tot_e,
+                         q == 0, q + 1 == p.passes, step ? accbuf : acc_out,
+                         step ? nullptr : pot_out};
+        e = nbk::launch_pass_combine(ca, stream);
+        if (e != hipSuccess) return hip_fail(e, "pass combine launch");
+    }
+    if (step) {
+        hipError_t e = nbk::launch_euler(accbuf, n, 1, euler_pos, euler_vel, dt, stream);
+        if (e != hipSuccess) return hip_fail(e, "euler kernel launch");
+    }
+    return NBODY_OK;
+}
+
 // Enqueue one evaluation: acc/pot into acc_out/pot_out, or with euler_pos and
 // euler_vel set, one Euler step applied to them in place (tiles and pairs
 // modes; small-mode steps alternate buffers and go through enqueue_steps).
@@ -374,6 +457,9 @@ int enqueue_eval(const float4 *pos, int n, float eps2, float4 *acc_out, float *p
         hipError_t e = nbk::launch_small(p.tpl, pot, false, sa, stream);
         return e == hipSuccess ? NBODY_OK : hip_fail(e, "small kernel launch");
     }
+    if (pairs && p.passes > 1)
+        return enqueue_pair_passes(pos, n, eps2, acc_out, pot_out, p, dev, stream, euler_pos,
+                                   euler_vel, dt);
     nbk::AccelArgs a{pos, n, eps2, p.chunk, acc_out, pot_out, nullptr};
     if (p.splits > 1 || step || pairs) {
         void *ws = nullptr;
@@ -384,7 +470,7 @@ int enqueue_eval(const float4 *pos, int n, float eps2, float4 *acc_out, float *p
     }
     hipError_t e;
     if (pairs) {
-        nbk::PairsArgs pa{pos, n, eps2, p.splits, a.part, 0, p.splits};
+        nbk::PairsArgs pa{pos, n, eps2, p.splits, a.part, 0, p.splits, n, 0, a.part, 0};
         e = nbk::launch_pairs(p.band, p.tpl, pot, pa, stream);
     } else {
         e = nbk::launch_accel(p.bcast, p.tpl, p.wg, pot, grid_x(n, p.tpl, p.wg),
@@ -432,6 +518,7 @@ int accel_impl(const nbody_f4 *pos, int64_t N, float eps2, nbody_f4 *acc, float 
 size_t eval_scratch(int64_t n, const nbody_plan &p, bool step)
 {
     if (p.mode == NBODY_MODE_SMALL) return step ? (size_t)n * sizeof(float4) : 0;
+    if (p.mode == NBODY_MODE_PAIRS && p.passes > 1) return pairs_pass_scratch(n, p.band, p.passes, step);
     if (p.splits > 1 || step || p.mode == NBODY_MODE_PAIRS)
         return (size_t)p.splits * (size_t)n * sizeof(float4);
     return 0;
@@ -619,7 +706,7 @@ int shard_impl(const nbody_f4 *pos, int64_t N, float eps2, int32_t shard, int32_
         return fail(NBODY_EINVAL, "nshards=%d exceeds the %lld bands of %d bodies (each shard "
                                   "needs at least one band)", (int)nshards,
                     (long long)((N + plan->band - 1) / plan->band), (int)plan->band);
-    nbody_plan want = plan ? *plan : nbody_plan{0, 0, 0, 0, 0, NBODY_MODE_PAIRS, 0};
+    nbody_plan want = plan ? *plan : nbody_plan{0, 0, 0, 0, 0, NBODY_MODE_PAIRS, 0, 0};
     nbody_plan p;
     int dev = 0;
     rc = make_plan(N, &want, &dev, &p);
@@ -629,11 +716,12 @@ int shard_impl(const nbody_f4 *pos, int64_t N, float eps2, int32_t shard, int32_
         return fail(NBODY_EINVAL, "nshards=%d exceeds the %d bands of %d bodies (each shard "
                                   "needs at least one band)", (int)nshards, nb, (int)p.band);
     void *ws = nullptr;
-    rc = scratch_get(dev, stream, eval_scratch(N, p, false), &ws);
+    rc = scratch_get(dev, stream, pairs_scratch(N, p.band), &ws);  // every slot of every body
     if (rc != NBODY_OK) return rc;
     const int n = (int)N;
     nbk::PairsArgs pa{(const float4 *)pos, n, eps2, nb, (float4 *)ws,
-                      shard_band(shard, nb, nshards), shard_band(shard + 1, nb, nshards)};
+                      shard_band(shard, nb, nshards), shard_band(shard + 1, nb, nshards), n, 0,
+                      (float4 *)ws, 0};
     hipError_t e = nbk::launch_pairs(p.band, p.tpl, want_pot != 0, pa, stream);
     if (e != hipSuccess) return hip_fail(e, "accel kernel launch");
     e = nbk::launch_shard_combine(pa.part, n, p.band, nb, pa.band0, pa.band1,

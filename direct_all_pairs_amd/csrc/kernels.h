@@ -39,9 +39,19 @@ struct PairsArgs {
     int n;              // N
     float eps2;         // softening squared (positive normal float)
     int nbands;         // nb = ceil(N / band)
-    float4 *part;       // part[slot*N + i], slot in [0, nb): every entry written once
+    float4 *part;       // A-side sums: part[slot * stride + i - own0]
     int band0;          // items (A, d) are evaluated for A in [band0, band1)
     int band1;          //   (the whole evaluation: 0, nb)
+    // Layout of the sums. Slots (compact = 0): slot d of a body is the A side of
+    // item (body's band, d), slot nb - d the B side of item (band - d, d); part =
+    // partB, stride N, own0 0, every entry written once. A pass over a band
+    // range (compact = 1): the A sides of the range's own bodies in part
+    // (stride = own body count, own0 = first own body), the B side of item
+    // (A, d) in partB[(A - band0) * N + i].
+    long long stride;
+    int own0;
+    float4 *partB;
+    int compact;
 };
 
 // Pair-symmetric evaluation over bands of `band` bodies (512, 1024 or 2048)
@@ -56,6 +66,23 @@ hipError_t launch_pairs(int band, int tpl, bool pot, const PairsArgs &args, hipS
 // combine (compensated), out[i] = (ax, ay, az, sum m/r) partial; N records.
 hipError_t launch_shard_combine(const float4 *part, int n, int band, int nbands, int band0,
                                 int band1, float4 *out, hipStream_t stream);
+
+// One pass of a multi-pass pair evaluation (compact layout of PairsArgs, band
+// range [band0, band1), own bodies [own0, own0 + own_count)): every body's sums
+// from this pass are added, in a fixed order, into the compensated running
+// totals (tot_s, tot_e) (started fresh when first). On the last pass the
+// result goes to acc_out/pot_out, or to acc_out alone as (ax, ay, az, sum m/r)
+// records when pot_out is null and raw is set (the Euler step's input).
+struct PassArgs {
+    const float4 *partA;
+    const float4 *partB;
+    int n, band, nbands, band0, band1, own0, own_count;
+    float4 *tot_s, *tot_e;
+    int first, last;
+    float4 *acc_out;
+    float *pot_out;
+};
+hipError_t launch_pass_combine(const PassArgs &args, hipStream_t stream);
 
 // Targets [t0, t1): the nshards contributions partials[s*N + i] added in
 // ascending s (compensated); acc_out[i - t0] = (ax, ay, az, 0) and, if

@@ -802,7 +802,7 @@ __device__ __forceinline__ void pairs_item(const PairsArgs &k, int A, int B, int
                     s = make_float4(s.x + v.x, s.y + v.y, s.z + v.z, s.w + v.w);
                 }
                 const long long body = (long long)A * BD + is * 64 * T + idx;
-                if (body < k.n) k.part[(size_t)slot_i * (size_t)k.n + body] = s;
+                if (body < k.n) k.part[(size_t)slot_i * (size_t)k.stride + (body - k.own0)] = s;
             }
             __syncthreads();
             if constexpr (kRaceProbe) {
@@ -828,7 +828,8 @@ __device__ __forceinline__ void pairs_item(const PairsArgs &k, int A, int B, int
                         red[idx] = v;
                     } else {
                         const long long body = (long long)A * BD + is * 64 * T + idx;
-                        if (body < k.n) k.part[(size_t)slot_i * (size_t)k.n + body] = v;
+                        if (body < k.n)
+                            k.part[(size_t)slot_i * (size_t)k.stride + (body - k.own0)] = v;
                     }
                 }
             }
@@ -840,7 +841,7 @@ __device__ __forceinline__ void pairs_item(const PairsArgs &k, int A, int B, int
     if constexpr (SYM) {
         for (int i = threadIdx.x; i < BD; i += 64 * W) {
             const long long body = (long long)B * BD + i;
-            if (body < k.n) k.part[(size_t)slot_j * (size_t)k.n + body] = sh.jacc[i];
+            if (body < k.n) k.partB[(size_t)slot_j * (size_t)k.n + body] = sh.jacc[i];
         }
     }
 }
@@ -864,7 +865,7 @@ __global__ void __launch_bounds__(256) accel_pairs(PairsArgs k)
     } else {
         for (int i = threadIdx.x; i < BD; i += 256) sh.jacc[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         __syncthreads();
-        pairs_item<T, BD, POT, true>(k, A, B, d, nb - d, eps2, sh);
+        pairs_item<T, BD, POT, true>(k, A, B, d, k.compact ? A - k.band0 : nb - d, eps2, sh);
     }
 }
 
@@ -943,6 +944,62 @@ __global__ void __launch_bounds__(256) shard_finish_kernel(const float4 *__restr
     const float4 a = sum_parts(partials, n, nshards, i);
     acc_out[i - t0] = make_float4(a.x, a.y, a.z, 0.0f);
     if (pot_out) pot_out[i - t0] = -a.w;
+}
+
+// ---------------------------------------------------------------- passes
+// Whether item (a, d) exists: the diagonal, d below nb/2, and for even nb the
+// opposite pair d = nb/2 from the lower half only.
+__device__ __forceinline__ bool item_exists(int a, int d, int nb)
+{
+    if (d == 0) return true;
+    if (nb == 1 || 2 * d > nb) return false;
+    return 2 * d < nb || a < nb / 2;
+}
+
+__global__ void __launch_bounds__(256) pass_combine_kernel(PassArgs k)
+{
+    const unsigned i = blockIdx.x * 256u + threadIdx.x;
+    if (i >= (unsigned)k.n) return;
+    const int x = (int)(i / (unsigned)k.band), nb = k.nbands;
+    float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float4 e = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    bool started = !k.first;
+    if (started) {
+        a = k.tot_s[i];
+        e = k.tot_e[i];
+    }
+    auto add = [&](const float4 &v) {
+        if (started) {
+            two_sum_add4(a, e, v);
+        } else {
+            a = v;  // as in sum_parts: the first sum starts the total
+            started = true;
+        }
+    };
+    // this body's A sides (its own band in the range), ascending d
+    if (x >= k.band0 && x < k.band1) {
+        const size_t off = (size_t)((int)i - k.own0);
+        for (int d = 0; d <= nb / 2; ++d)
+            if (item_exists(x, d, nb)) add(k.partA[(size_t)d * (size_t)k.own_count + off]);
+    }
+    // its B sides from the range's bands, ascending band
+    for (int A = k.band0; A < k.band1; ++A) {
+        int d = x - A;
+        if (d < 0) d += nb;
+        if (d >= 1 && item_exists(A, d, nb)) add(k.partB[(size_t)(A - k.band0) * (size_t)k.n + i]);
+    }
+    if (!k.last) {
+        k.tot_s[i] = a;
+        k.tot_e[i] = e;
+        return;
+    }
+    const float4 r = make_float4(a.x + e.x, a.y + e.y, a.z + e.z, a.w + e.w);
+    if (k.pot_out) {
+        k.acc_out[i] = make_float4(r.x, r.y, r.z, 0.0f);
+        k.pot_out[i] = -r.w;
+    } else {
+        k.acc_out[i] = r;
+    }
 }
 
 // ---------------------------------------------------------------- diagnostics
@@ -1448,6 +1505,20 @@ hipError_t launch_pairs(int band, int tpl, bool pot, const PairsArgs &args, hipS
     void *kargs[] = {&a};
     return hipLaunchKernel(fn, dim3((unsigned)(a.band1 - a.band0), (unsigned)(a.nbands / 2 + 1), 1),
                            dim3(256, 1, 1), kargs, 0, stream);
+}
+
+hipError_t launch_pass_combine(const PassArgs &args, hipStream_t stream)
+{
+    const PassArgs &a = args;
+    if (a.n < 1 || a.band < 1 || a.nbands != (a.n + a.band - 1) / a.band || a.band0 < 0 ||
+        a.band1 > a.nbands || a.band0 >= a.band1 || a.own0 != a.band0 * a.band ||
+        a.own_count < 1 || a.own0 + a.own_count > a.n || !a.acc_out ||
+        (!(a.first && a.last) && (!a.tot_s || !a.tot_e)))
+        return hipErrorInvalidValue;
+    PassArgs p = a;
+    void *kargs[] = {&p};
+    const unsigned g = (unsigned)((a.n + 255) / 256);
+    return hipLaunchKernel((const void *)&pass_combine_kernel, dim3(g), dim3(256), kargs, 0, stream);
 }
 
 hipError_t launch_shard_combine(const float4 *part, int n, int band, int nbands, int band0,

@@ -92,14 +92,19 @@ enum {
  *   wg     - threads per workgroup: 64, 128, 256 or 512 for NBODY_BCAST_LDS (also
  *            the LDS tile, in bodies), 256 for the other schemes.
  *   mode   - NBODY_MODE_*. The fields above describe NBODY_MODE_TILES. With
- *            NBODY_MODE_PAIRS only `band` (256, 512, 1024 or 2048 bodies) and
- *            `tpl` (4 or 8 targets per lane, 4 only with 256-body bands; 0 =
- *            automatic) may be set; the output then has
+ *            NBODY_MODE_PAIRS only `band` (256, 512, 1024 or 2048 bodies),
+ *            `tpl` (4 or 8 targets per lane, 4 only with 256-body bands) and
+ *            `passes` may be set (0 = automatic); the output then has
  *            splits = number of bands = partial-sum slots per body, chunk =
- *            band, bcast = LDS, wg = 256. Its scratch
- *            is splits x N x 16 bytes (8.6 GB at N = 2^20 with 2048-body bands);
- *            the automatic plan uses it only when that fits in 1/16 of device
- *            memory.
+ *            band, bcast = LDS, wg = 256. In one pass the scratch is splits x
+ *            N x 16 bytes (8.6 GB at N = 2^20 with 2048-body bands); when that
+ *            would exceed 1/16 of device memory the automatic plan evaluates
+ *            the band-pair items in several passes over band ranges, each
+ *            pass's sums added into running totals, with scratch of about
+ *            (1.5 x splits / passes + 2) x N x 16 bytes.
+ *   passes - pair mode: passes over band ranges, 1 .. splits (0 = automatic:
+ *            one while the full slot scratch fits, else the fewest that fit).
+ *            Results with different pass counts differ in the last bits.
  *            With NBODY_MODE_SMALL only `tpl` may be set: targets per workgroup,
  *            4, 8, 16 or 32 (0 = automatic); the output has splits = 1, chunk =
  *            N, bcast = LDS, wg = 256. It needs no scratch for an evaluation and
@@ -116,6 +121,7 @@ typedef struct nbody_plan {
     int32_t wg;
     int32_t mode;
     int32_t band;
+    int32_t passes;
 } nbody_plan;
 
 /*

@@ -263,6 +263,71 @@ def test_pairs_invariants(nb, band, tpl):
     assert np.array_equal(b1, b2) and np.array_equal(q1, q2)
 
 
+# ------------------------------------------------------------------ pair passes (bounded scratch)
+
+PASS_CASES = [(1000, 256, 4, 2), (1000, 256, 4, 4), (3000, 512, 8, 2), (3000, 512, 8, 6),
+              (5000, 1024, 4, 3), (4097, 2048, 8, 3), (2049, 512, 4, 5)]
+
+
+@pytest.mark.parametrize("n,band,tpl,passes", PASS_CASES)
+def test_pair_passes(nb, n, band, tpl, passes):
+    """Passes over band ranges (compact sums, running totals) against the full oracle, for even
+    and odd band counts, passes that do and do not divide them, one band per pass; the
+    acceleration bits do not depend on the potential, and repeated runs are identical."""
+    eps2 = np.float32(1e-4)
+    pos, _ = _bodies(n, 300 + n)
+    plan = dict(mode="pairs", band=band, tpl=tpl, passes=passes)
+    acc, pot = gpu_accel(pos, eps2, pot=True, plan=plan)
+    assert_accel_parity(acc, pot, _ref(n, 300 + n, eps2), what=f"N={n} {plan}")
+    a0, _ = gpu_accel(pos, eps2, pot=False, plan=plan)
+    a1, p1 = gpu_accel(pos, eps2, pot=True, plan=plan)
+    assert np.array_equal(a0, acc) and np.array_equal(a1, acc) and np.array_equal(p1, pot)
+
+
+def test_pair_passes_mid_n_and_steps(nb):
+    """N = 20011 in 7 passes of 512-body bands (sampled targets), and Euler steps in passes:
+    one step within the single-step bound, three steps equal to three single steps bit for
+    bit."""
+    import oracle
+
+    n, eps2 = 20011, np.float32(1e-4)
+    pos, vel = _bodies(n, 8)
+    plan = dict(mode="pairs", band=512, tpl=8, passes=7)
+    acc, pot = gpu_accel(pos, eps2, pot=True, plan=plan)
+    idx = np.unique(np.concatenate([np.arange(200), np.arange(n - 200, n),
+                                    np.random.default_rng(2).integers(0, n, 600)]))
+    assert_accel_parity(acc, pot, oracle.accel(pos, eps2, targets=idx), idx=idx,
+                        what="N=20011 7 passes")
+    m = 3000
+    p3, v3 = _bodies(m, 9)
+    plan = dict(mode="pairs", band=256, tpl=4, passes=4)
+    x1, v1 = gpu_step(p3, v3, 1e-3, 1e-4, 1, plan=plan)
+    assert_step_parity(p3, v3, x1, v1, 1e-3, oracle.accel(p3, np.float32(1e-4)),
+                       what="step in 4 passes")
+    xs, vs = x1, v1
+    for _ in range(2):
+        xs, vs = gpu_step(xs, vs, 1e-3, 1e-4, 1, plan=plan)
+    xk, vk = gpu_step(p3, v3, 1e-3, 1e-4, 3, plan=plan)
+    assert np.array_equal(xk, xs) and np.array_equal(vk, vs)
+
+
+def test_pair_passes_two_million_sampled(nb):
+    """N = 2^21 uniform cube in the automatic plan: the one-pass slot scratch (34 GB) exceeds
+    the scratch share, so the plan takes several passes; sampled targets against the oracle."""
+    import oracle
+
+    n = 1 << 21
+    p = nb.nbody_plan_for(n)
+    assert p.mode == nb.MODE_PAIRS and p.passes > 1, p.as_dict()
+    w = workloads.make("cube1m", n=n)
+    acc, pot = gpu_accel(w.pos, w.eps2)
+    rng = np.random.default_rng(21)
+    idx = np.unique(np.concatenate([rng.integers(0, n, 40), [0, n - 1]]))
+    assert_accel_parity(acc, pot, oracle.accel(w.pos, w.eps2, targets=idx), idx=idx,
+                        what=f"N=2^21 {p.as_dict()}")
+    nb.nbody_release_workspace()
+
+
 def test_pairs_plan_beyond_grid_limit_rejected(nb):
     """A pair plan whose band count exceeds the launch grid is rejected before anything is
     allocated or launched (fake, aligned pointers: nothing is dereferenced)."""
@@ -301,6 +366,10 @@ def test_auto_plan_modes(nb):
         assert p.mode == nb.MODE_PAIRS and p.band == band and p.tpl == 8, n
     assert nb.nbody_plan_for(300007).splits == 293
     assert nb.nbody_plan_for(1 << 20).splits == 512
+    assert nb.nbody_plan_for(1 << 20).passes == 1
+    p = nb.nbody_plan_for(1 << 22)
+    assert p.mode == nb.MODE_PAIRS and p.band == 2048 and 1 < p.passes <= p.splits
+    assert nb.nbody_plan_for(1 << 30).mode == nb.MODE_TILES  # beyond the pair launch grid
 
 
 # ------------------------------------------------------------------ degenerate inputs
