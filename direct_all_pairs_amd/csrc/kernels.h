@@ -132,7 +132,8 @@ struct GridSpec {
 };
 
 // wide: one 256-thread workgroup per cell sharing 256-body source tiles (large
-// cells); otherwise one wave per cell (small cells).
+// cells); otherwise one wave per cell (small cells), whose chunks of 192 or
+// more targets take four per lane when cells average at least 192 bodies.
 hipError_t launch_p2p(bool pot, bool wide, const P2PArgs &args, hipStream_t stream);
 // The same kernels with the 27 neighbour cells of the grid as every cell's list.
 hipError_t launch_p2p_grid(bool pot, bool wide, const P2PArgs &args, const GridSpec &g,

@@ -1163,13 +1163,23 @@ __device__ __forceinline__ bool next_tile(const P2PArgs &k, const Lists &lists, 
     return false;
 }
 
-// Targets per chunk: a cell's bodies go 64 at a time; a chunk of r < 64 bodies
+// Targets per lane for a cell's large chunks, and the fewest remaining bodies
+// that take one (a chunk of 192-256 targets: at most a quarter of its lanes'
+// targets idle, against three or four separate 64-target passes). The kernel
+// has the four-target path (QUAD) only where cells average at least that many
+// bodies: its registers slow the one-target path for small cells (10 % at 131
+// bodies per cell), and it gains 10 % at 256.
+constexpr int kP2PWideT = 4;
+constexpr int kP2PWideMin = 192;
+
+// Targets per chunk: a cell's bodies go up to 256 at a time (four per lane)
+// while at least 192 remain, then 64 at a time; a chunk of r < 64 bodies
 // takes tw = the next power of two >= r lanes per source group and G = 64 / tw
 // groups, lane (t, g) = (lane mod tw, lane / tw) summing every G-th source of
 // each tile for target t; the G group sums of a target are added in ascending
 // g through LDS. So a 20-body cell keeps 64 lanes busy instead of 20. The next
 // source tile's global load is issued before the current tile is evaluated.
-template <bool POT, typename Lists>
+template <bool POT, typename Lists, bool QUAD>
 __global__ void __launch_bounds__(64) p2p_kernel(P2PArgs k, Lists lists)
 {
     __shared__ float4 row[64];
@@ -1185,6 +1195,57 @@ __global__ void __launch_bounds__(64) p2p_kernel(P2PArgs k, Lists lists)
     const float eps2 = in_vgpr(k.eps2);
     for (int t0 = tb; t0 < te;) {
         const int rem = te - t0;
+        if (QUAD && rem >= kP2PWideMin) {
+            // up to 256 targets, four per lane (target t0 + q * 64 + lane; past the
+            // cell end a lane computes on a clamped body and stores nothing): each
+            // staged source tile and each broadcast read serves four interactions
+            Targets<kP2PWideT> tg;
+#pragma unroll
+            for (int q = 0; q < kP2PWideT; ++q) {
+                const int i = t0 + q * 64 + lane;
+                const float4 me = k.pos[i < te ? i : te - 1];
+                tg.x[q] = me.x;
+                tg.y[q] = me.y;
+                tg.z[q] = me.z;
+            }
+            Total<kP2PWideT, POT> tot;
+            zero(tot);
+            int e = lo - 1, j0 = 0, se = 0;
+            bool have = next_tile(k, lists, c, hi, e, j0, se);
+            float4 cur = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (have) cur = k.pos[j0 + lane < se ? j0 + lane : se - 1];
+            while (have) {
+                const int cnt = se - j0 < 64 ? se - j0 : 64;
+                const bool in = lane < cnt;
+                __builtin_amdgcn_wave_barrier();
+                row[lane] = make_float4(in ? cur.x : 0.0f, in ? cur.y : 0.0f, in ? cur.z : 0.0f,
+                                        in ? cur.w : 0.0f);
+                __builtin_amdgcn_wave_barrier();
+                int e2 = e, j2 = j0, se2 = se;
+                const bool have2 = next_tile(k, lists, c, hi, e2, j2, se2);
+                if (have2) cur = k.pos[j2 + lane < se2 ? j2 + lane : se2 - 1];
+                Sums<kP2PWideT, POT> blk;
+                zero(blk);
+#pragma unroll 8
+                for (int u = 0; u < cnt; ++u) interact4<kP2PWideT, POT>(row[u], tg, eps2, blk);
+                add_into(tot, blk);
+                e = e2;
+                j0 = j2;
+                se = se2;
+                have = have2;
+            }
+            const Sums<kP2PWideT, POT> r = result(tot);
+#pragma unroll
+            for (int q = 0; q < kP2PWideT; ++q) {
+                const int i = t0 + q * 64 + lane;
+                if (i < te) {
+                    k.acc_out[i] = make_float4(r.ax[q], r.ay[q], r.az[q], 0.0f);
+                    if constexpr (POT) k.pot_out[i] = -r.p[q];
+                }
+            }
+            t0 += 64 * kP2PWideT;
+            continue;
+        }
         int tw = 1, lg = 0;
         while (tw < rem && tw < 64) {
             tw <<= 1;
@@ -1565,10 +1626,15 @@ hipError_t launch_p2p_any(bool pot, bool wide, const P2PArgs &args, Lists l, hip
     P2PArgs a = args;
     void *k[] = {&a, &l};
     const void *fn;
+    const bool quad = (long long)a.n >= (long long)kP2PWideMin * a.ncell;
     if (wide)
         fn = pot ? (const void *)&p2p_wg_kernel<true, Lists> : (const void *)&p2p_wg_kernel<false, Lists>;
+    else if (quad)
+        fn = pot ? (const void *)&p2p_kernel<true, Lists, true>
+                 : (const void *)&p2p_kernel<false, Lists, true>;
     else
-        fn = pot ? (const void *)&p2p_kernel<true, Lists> : (const void *)&p2p_kernel<false, Lists>;
+        fn = pot ? (const void *)&p2p_kernel<true, Lists, false>
+                 : (const void *)&p2p_kernel<false, Lists, false>;
     return hipLaunchKernel(fn, dim3((unsigned)a.ncell), dim3(wide ? 256 : 64), k, 0, stream);
 }
 

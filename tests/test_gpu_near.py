@@ -203,3 +203,20 @@ def test_near_grid_few_large_cells(nb):
     idx = np.unique(np.random.default_rng(6).integers(0, 50000, 1500))
     ref = oracle.near_grid(pos, 1e-4, *args, targets=idx)
     assert_accel_parity(acc, pot, ref, idx=idx, what="few large cells")
+
+
+def test_near_grid_many_large_cells_four_targets_per_lane(nb):
+    """N = 2^20 on a 16^3 grid (4096 cells of ~256 bodies: one wave per cell, chunks of 192 or
+    more targets four per lane, the rest one per lane); sampled targets against the grid
+    definition, including cells below and above 256 bodies."""
+    import oracle
+
+    w = workloads.make("cube1m")
+    args = ((-1.0, -1.0, -1.0), 0.125, (16, 16, 16))
+    acc, pot = gpu_near_grid(nb, w.pos, w.eps2, *args)
+    idx = np.unique(np.concatenate([np.random.default_rng(7).integers(0, w.n, 1500),
+                                    [0, w.n - 1]]))
+    ref = oracle.near_grid(w.pos, w.eps2, *args, targets=idx)
+    assert_accel_parity(acc, pot, ref, idx=idx, what="16^3 grid, N = 2^20")
+    a0, p0 = gpu_near_grid(nb, w.pos, w.eps2, *args, pot=False)
+    assert p0 is None and np.array_equal(a0, acc)
