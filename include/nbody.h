@@ -208,9 +208,9 @@ int nbody_step_soa(float *x, float *y, float *z, const float *m, float *vx, floa
  *                 (w = 0 when want_pot is 0), zero-valued terms included.
  *                 Must not overlap pos_xyzm.
  *   shard, nshards : 0 <= shard < nshards <= nb.
- * Scratch: nb x N x 16 bytes, as for nbody_accel in pairs mode. With nshards =
- * 1 the result, finished by nbody_shard_finish, equals nbody_accel_plan with
- * the same plan bit for bit.
+ * Scratch: nb x N x 16 bytes (the full slot array of a one-pass evaluation).
+ * With nshards = 1 the result, finished by nbody_shard_finish, equals
+ * nbody_accel_plan with the same plan in one pass (plan.passes = 1) bit for bit.
  */
 int nbody_accel_shard(const nbody_f4 *pos_xyzm, int64_t N, float eps2, int32_t shard,
                       int32_t nshards, int want_pot, const nbody_plan *plan,
