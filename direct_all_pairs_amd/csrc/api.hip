@@ -97,6 +97,13 @@ struct Scratch {
 };
 std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
 
+// Held by every entry point that uses scratch, from taking the block until its
+// last launch is enqueued, and by nbody_release_workspace: no host thread can
+// grow (free) a block another thread has taken but not yet launched work on.
+// Enqueueing takes microseconds; the GPU work itself runs after the lock.
+std::mutex g_enqueue;
+using EnqueueLock = std::lock_guard<std::mutex>;
+
 // Returns scratch of at least `bytes` for (device, stream). Growing frees the
 // old block first; hipFree waits for the device, so work still queued on the
 // old block finishes before it is released.
@@ -737,24 +744,28 @@ extern "C" {
 int nbody_accel(const nbody_f4 *pos_xyzm, int64_t N, float eps2, nbody_f4 *acc_out,
                 float *pot_out, hipStream_t stream)
 {
+    EnqueueLock lk(g_enqueue);
     return accel_impl(pos_xyzm, N, eps2, acc_out, pot_out, nullptr, stream);
 }
 
 int nbody_accel_plan(const nbody_f4 *pos_xyzm, int64_t N, float eps2, nbody_f4 *acc_out,
                      float *pot_out, const nbody_plan *plan, hipStream_t stream)
 {
+    EnqueueLock lk(g_enqueue);
     return accel_impl(pos_xyzm, N, eps2, acc_out, pot_out, plan, stream);
 }
 
 int nbody_step(nbody_f4 *pos, nbody_f4 *vel, int64_t N, float dt, float eps2, int64_t nsteps,
                hipStream_t stream)
 {
+    EnqueueLock lk(g_enqueue);
     return step_impl(pos, vel, N, dt, eps2, nsteps, nullptr, stream);
 }
 
 int nbody_step_plan(nbody_f4 *pos, nbody_f4 *vel, int64_t N, float dt, float eps2,
                     int64_t nsteps, const nbody_plan *plan, hipStream_t stream)
 {
+    EnqueueLock lk(g_enqueue);
     return step_impl(pos, vel, N, dt, eps2, nsteps, plan, stream);
 }
 
@@ -762,12 +773,14 @@ int nbody_accel_soa(const float *x, const float *y, const float *z, const float 
                     float eps2, float *ax, float *ay, float *az, float *pot_out,
                     hipStream_t stream)
 {
+    EnqueueLock lk(g_enqueue);
     return accel_soa_impl(x, y, z, m, N, eps2, ax, ay, az, pot_out, stream);
 }
 
 int nbody_step_soa(float *x, float *y, float *z, const float *m, float *vx, float *vy, float *vz,
                    int64_t N, float dt, float eps2, int64_t nsteps, hipStream_t stream)
 {
+    EnqueueLock lk(g_enqueue);
     return step_soa_impl(x, y, z, m, vx, vy, vz, N, dt, eps2, nsteps, stream);
 }
 
@@ -775,6 +788,7 @@ int nbody_accel_shard(const nbody_f4 *pos_xyzm, int64_t N, float eps2, int32_t s
                       int32_t nshards, int want_pot, const nbody_plan *plan,
                       nbody_f4 *partial_out, hipStream_t stream)
 {
+    EnqueueLock lk(g_enqueue);
     return shard_impl(pos_xyzm, N, eps2, shard, nshards, want_pot, plan, partial_out, stream);
 }
 
@@ -880,6 +894,7 @@ int nbody_near_grid(const nbody_f4 *pos, int64_t N, float eps2, const float lo[3
     if (overlap(pos, b16, acc_out, b16)) return fail(NBODY_EINVAL, "acc_out overlaps pos_xyzm");
     if (pot_out && (overlap(pot_out, b4, pos, b16) || overlap(pot_out, b4, acc_out, b16)))
         return fail(NBODY_EINVAL, "pot_out overlaps another buffer");
+    EnqueueLock lk(g_enqueue);
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -944,6 +959,7 @@ int nbody_diagnostics(const nbody_f4 *pos, const nbody_f4 *vel, const float *pot
     if (N > 0 && (overlap(out, bo, pos, b16) || overlap(out, bo, vel, b16) ||
                   (pot && overlap(out, bo, pot, b4))))
         return fail(NBODY_EINVAL, "out overlaps an input");
+    EnqueueLock lk(g_enqueue);
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -998,6 +1014,7 @@ const char *nbody_last_error(void) { return g_err.c_str(); }
 
 int nbody_release_workspace(void)
 {
+    EnqueueLock el(g_enqueue);
     std::lock_guard<std::mutex> lk(g_mu);
     int rc = NBODY_OK;
     for (auto &kv : g_scratch) {

@@ -35,7 +35,11 @@
  *   - The library owns a cached scratch area per (device, stream) for split-j
  *     partial sums and the accelerations inside nbody_step. Calls that overlap
  *     in time on the SAME stream are ordered by the stream; calls on different
- *     streams use different scratch areas.
+ *     streams use different scratch areas. The area is keyed by the stream
+ *     handle: destroy a stream only after its work has finished (or call
+ *     nbody_release_workspace) if a new stream may reuse the handle.
+ *   - Any host thread may call the library. Calls that use scratch hold a
+ *     process-wide lock while they enqueue (not while the GPU runs the work).
  */
 #ifndef NBODY_H
 #define NBODY_H
