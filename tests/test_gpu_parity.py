@@ -328,6 +328,28 @@ def test_pair_passes_two_million_sampled(nb):
     nb.nbody_release_workspace()
 
 
+def test_pair_passes_four_million_ragged_sampled(nb):
+    """N = 2^22 + 12345 in the automatic plan: ~2049 bands of 2048 bodies, the last one ragged,
+    in many passes whose band ranges do not divide evenly; sampled targets (both ends, the
+    ragged band, pass boundaries) against the oracle."""
+    import oracle
+
+    n = (1 << 22) + 12345
+    p = nb.nbody_plan_for(n)
+    assert p.mode == nb.MODE_PAIRS and p.passes > 2 and n % p.band != 0, p.as_dict()
+    w = workloads.make("cube1m", n=n)
+    acc, pot = gpu_accel(w.pos, w.eps2)
+    nbands = p.splits
+    edges = [q * nbands // p.passes * p.band for q in range(1, p.passes)]
+    rng = np.random.default_rng(22)
+    idx = np.unique(np.concatenate([rng.integers(0, n, 40), [0, n - 1],
+                                    np.arange(n - 20, n - 1), [e - 1 for e in edges[:6]],
+                                    edges[:6]]))
+    assert_accel_parity(acc, pot, oracle.accel(w.pos, w.eps2, targets=idx), idx=idx,
+                        what=f"N=2^22+12345 {p.as_dict()}")
+    nb.nbody_release_workspace()
+
+
 def test_pairs_plan_beyond_grid_limit_rejected(nb):
     """A pair plan whose band count exceeds the launch grid is rejected before anything is
     allocated or launched (fake, aligned pointers: nothing is dereferenced)."""
