@@ -106,14 +106,14 @@ enum {
  *            the band-pair items in several passes over band ranges, each
  *            pass's sums added into running totals, with scratch of about
  *            (1.5 x splits / passes + 2) x N x 16 bytes.
- *   passes - pair mode: passes over band ranges, 1 .. splits (0 = automatic:
- *            one while the full slot scratch fits, else the fewest that fit).
- *            Results with different pass counts differ in the last bits.
  *            With NBODY_MODE_SMALL only `tpl` may be set: targets per workgroup,
  *            4, 8, 16 or 32 (0 = automatic); the output has splits = 1, chunk =
  *            N, bcast = LDS, wg = 256. It needs no scratch for an evaluation and
  *            N x 16 bytes for steps.
  *   band   - see mode.
+ *   passes - pair mode: passes over band ranges, 1 .. splits (0 = automatic:
+ *            one while the full slot scratch fits, else the fewest that fit).
+ *            Results with different pass counts differ in the last bits.
  * The plan is a pure function of (N, device compute units and memory), so
  * nbody_accel and nbody_step use the same one for the same N, with or without
  * the potential. */
