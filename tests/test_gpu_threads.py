@@ -96,3 +96,37 @@ def test_threads_match_single_thread(nb, shared):
         assert np.array_equal(acc.cpu().numpy(), ra), f"thread {t} N={n} acceleration"
         assert np.array_equal(pot.cpu().numpy(), rp), f"thread {t} N={n} potential"
         assert np.array_equal(po.cpu().numpy(), rpos), f"thread {t} N={n} step positions"
+
+
+def test_scratch_release_and_growth_with_queued_work(nb):
+    """Scratch freed or grown while work that uses it is still queued: nbody_release_workspace
+    and a larger call right behind a smaller one free the old block only after the device has
+    finished with it, so every result equals its one-call-at-a-time reference bit for bit."""
+    import torch
+
+    sizes = [70001, 9000, 200003]
+    data = {n: to_dev(workloads.random_bodies(n, seed=950 + n)[0]) for n in sizes}
+    s = torch.cuda.Stream()
+    ref = {}
+    for n in sizes:
+        nb.nbody_release_workspace()
+        acc = torch.empty((n, 4), device="cuda")
+        pot = torch.empty((n,), device="cuda")
+        nb.nbody_accel(data[n], n, 1e-4, acc, pot, stream=s)
+        torch.cuda.synchronize()
+        ref[n] = (acc.cpu().numpy(), pot.cpu().numpy())
+
+    nb.nbody_release_workspace()
+    out = {n: (torch.full((n, 4), np.nan, device="cuda"), torch.full((n,), np.nan, device="cuda"))
+           for n in sizes}
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        nb.nbody_accel(data[70001], 70001, 1e-4, *out[70001], stream=s)
+        nb.nbody_release_workspace()  # the 70001-body evaluation may still be running
+        nb.nbody_accel(data[9000], 9000, 1e-4, *out[9000], stream=s)
+        nb.nbody_accel(data[200003], 200003, 1e-4, *out[200003], stream=s)  # grows the block
+    torch.cuda.synchronize()
+    for n in sizes:
+        acc, pot = out[n]
+        assert np.array_equal(acc.cpu().numpy(), ref[n][0]), f"N={n} acceleration"
+        assert np.array_equal(pot.cpu().numpy(), ref[n][1]), f"N={n} potential"
