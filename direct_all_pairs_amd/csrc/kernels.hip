@@ -1094,6 +1094,8 @@ __global__ void __launch_bounds__(256) diag_final_kernel(const double *__restric
 // checked before use (memory safety for any input): a target cell with an
 // invalid range is skipped, an invalid list range is empty, an out-of-range
 // list entry or a source cell with an invalid range adds nothing.
+// A list hands out source runs: entry e of [lo, hi) is a range of bodies
+// [sb, sn), or nothing (`source` returns false for an invalid or empty entry).
 struct CsrLists {
     const int *off;
     const int *list;
@@ -1107,44 +1109,63 @@ struct CsrLists {
         lo = (int)a;
         hi = (int)b;
     }
-    __device__ int cell(int e, int) const
+    // entry e: the bodies of listed cell list[e]
+    __device__ bool source(const P2PArgs &k, int e, int &sb, int &sn) const
     {
         const int s = list[e];
-        return (s < 0 || s >= ncell) ? -1 : s;
+        if (s < 0 || s >= ncell) return false;
+        sb = k.cell_start[s];
+        sn = k.cell_start[s + 1];
+        return sb >= 0 && sn > sb && sn <= k.n;
     }
 };
 
-// The 27 neighbours of the target cell (9 (z + 1) + 3 (y + 1) + (x + 1), -1
-// outside the grid), computed once per workgroup into LDS by lanes 0..26.
+// The 27 neighbours of the target cell as 9 runs of consecutive cells: for
+// each (y, z) offset (entry 3 (z + 1) + (y + 1)) the cells x - 1 .. x + 1 that
+// lie in the grid are consecutive in the x-fastest cell order, so their bodies
+// are one contiguous range of the sorted array (the same bodies in the same
+// order as the three cells one after another, in a third of the runs, which
+// leaves fewer part-filled source tiles). Computed once per workgroup into LDS
+// by lanes 0..8.
 struct GridLists {
     int dx, dy, dz;
-    int *nbr;  // 27 LDS entries
+    int *nbr;  // 18 LDS entries: first and last cell of each run, -1 outside the grid
     __device__ void bind(int c)
     {
         const int lane = threadIdx.x;
-        if (lane < 27) {
+        if (lane < 9) {
             const int cx = c % dx, cy = (c / dx) % dy, cz = c / (dx * dy);
-            const int x = cx + lane % 3 - 1, y = cy + (lane / 3) % 3 - 1, z = cz + lane / 9 - 1;
-            const bool in = x >= 0 && x < dx && y >= 0 && y < dy && z >= 0 && z < dz;
-            nbr[lane] = in ? (z * dy + y) * dx + x : -1;
+            const int y = cy + lane % 3 - 1, z = cz + lane / 3 - 1;
+            const bool in = y >= 0 && y < dy && z >= 0 && z < dz;
+            const int row = (z * dy + y) * dx;
+            nbr[2 * lane] = in ? row + (cx > 0 ? cx - 1 : 0) : -1;
+            nbr[2 * lane + 1] = in ? row + (cx + 1 < dx ? cx + 1 : dx - 1) : -1;
         }
         __syncthreads();
     }
     __device__ void range(int, int &lo, int &hi) const
     {
         lo = 0;
-        hi = 27;
+        hi = 9;
     }
-    __device__ int cell(int e, int) const { return __builtin_amdgcn_readfirstlane(nbr[e]); }
+    __device__ bool source(const P2PArgs &k, int e, int &sb, int &sn) const
+    {
+        const int first = __builtin_amdgcn_readfirstlane(nbr[2 * e]);
+        const int last = __builtin_amdgcn_readfirstlane(nbr[2 * e + 1]);
+        if (first < 0) return false;
+        sb = k.cell_start[first];
+        sn = k.cell_start[last + 1];
+        return sb >= 0 && sn > sb && sn <= k.n;
+    }
 };
 
 // Walk over the source tiles of a target cell's list: tile = bodies
-// [j0, min(j0 + 64, se)) of listed cell e. Starting from (e, j0, se), moves to
-// the next tile (the rest of the same cell, then the next valid non-empty
-// listed cell); false when the list is exhausted. Uniform across the wave.
+// [j0, min(j0 + 64, se)) of list entry e. Starting from (e, j0, se), moves to
+// the next tile (the rest of the same run, then the next valid non-empty
+// entry); false when the list is exhausted. Uniform across the wave.
 template <typename Lists>
-__device__ __forceinline__ bool next_tile(const P2PArgs &k, const Lists &lists, int c, int hi,
-                                          int &e, int &j0, int &se)
+__device__ __forceinline__ bool next_tile(const P2PArgs &k, const Lists &lists, int hi, int &e,
+                                          int &j0, int &se)
 {
     if (j0 + 64 < se) {
         j0 += 64;
@@ -1152,10 +1173,8 @@ __device__ __forceinline__ bool next_tile(const P2PArgs &k, const Lists &lists, 
     }
 #pragma unroll 1
     for (++e; e < hi; ++e) {
-        const int s = lists.cell(e, c);
-        if (s < 0) continue;
-        const int sb = k.cell_start[s], sn = k.cell_start[s + 1];
-        if (sb < 0 || sn <= sb || sn > k.n) continue;  // invalid or empty: no tiles
+        int sb, sn;
+        if (!lists.source(k, e, sb, sn)) continue;  // invalid or empty: no tiles
         j0 = sb;
         se = sn;
         return true;
@@ -1184,7 +1203,7 @@ __global__ void __launch_bounds__(64) p2p_kernel(P2PArgs k, Lists lists)
 {
     __shared__ float4 row[64];
     __shared__ float4 red[64];
-    __shared__ int nbr[27];
+    __shared__ int nbr[18];
     const int c = blockIdx.x, lane = threadIdx.x;
     const int tb = k.cell_start[c], te = k.cell_start[c + 1];
     if (tb < 0 || te < tb || te > k.n) return;
@@ -1211,7 +1230,7 @@ __global__ void __launch_bounds__(64) p2p_kernel(P2PArgs k, Lists lists)
             Total<kP2PWideT, POT> tot;
             zero(tot);
             int e = lo - 1, j0 = 0, se = 0;
-            bool have = next_tile(k, lists, c, hi, e, j0, se);
+            bool have = next_tile(k, lists, hi, e, j0, se);
             float4 cur = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             if (have) cur = k.pos[j0 + lane < se ? j0 + lane : se - 1];
             while (have) {
@@ -1222,7 +1241,7 @@ __global__ void __launch_bounds__(64) p2p_kernel(P2PArgs k, Lists lists)
                                         in ? cur.w : 0.0f);
                 __builtin_amdgcn_wave_barrier();
                 int e2 = e, j2 = j0, se2 = se;
-                const bool have2 = next_tile(k, lists, c, hi, e2, j2, se2);
+                const bool have2 = next_tile(k, lists, hi, e2, j2, se2);
                 if (have2) cur = k.pos[j2 + lane < se2 ? j2 + lane : se2 - 1];
                 Sums<kP2PWideT, POT> blk;
                 zero(blk);
@@ -1262,7 +1281,7 @@ __global__ void __launch_bounds__(64) p2p_kernel(P2PArgs k, Lists lists)
         Total<1, POT> tot;
         zero(tot);
         int e = lo - 1, j0 = 0, se = 0;
-        bool have = next_tile(k, lists, c, hi, e, j0, se);
+        bool have = next_tile(k, lists, hi, e, j0, se);
         float4 cur = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         if (have) cur = k.pos[j0 + lane < se ? j0 + lane : se - 1];
         while (have) {
@@ -1277,7 +1296,7 @@ __global__ void __launch_bounds__(64) p2p_kernel(P2PArgs k, Lists lists)
                                     in ? cur.w : 0.0f);
             __builtin_amdgcn_wave_barrier();
             int e2 = e, j2 = j0, se2 = se;
-            const bool have2 = next_tile(k, lists, c, hi, e2, j2, se2);
+            const bool have2 = next_tile(k, lists, hi, e2, j2, se2);
             if (have2) cur = k.pos[j2 + lane < se2 ? j2 + lane : se2 - 1];
             Sums<1, POT> blk;
             zero(blk);
@@ -1322,8 +1341,8 @@ __global__ void __launch_bounds__(64) p2p_kernel(P2PArgs k, Lists lists)
 // publishes the next buffer and guards the one about to be overwritten), read
 // with uniform addresses. The cursor over (list entry, tile) is uniform.
 template <typename Lists>
-__device__ __forceinline__ bool next_tile256(const P2PArgs &k, const Lists &lists, int c, int hi,
-                                             int &e, int &j0, int &se)
+__device__ __forceinline__ bool next_tile256(const P2PArgs &k, const Lists &lists, int hi, int &e,
+                                             int &j0, int &se)
 {
     if (j0 + 256 < se) {
         j0 += 256;
@@ -1331,10 +1350,8 @@ __device__ __forceinline__ bool next_tile256(const P2PArgs &k, const Lists &list
     }
 #pragma unroll 1
     for (++e; e < hi; ++e) {
-        const int s = lists.cell(e, c);
-        if (s < 0) continue;
-        const int sb = k.cell_start[s], sn = k.cell_start[s + 1];
-        if (sb < 0 || sn <= sb || sn > k.n) continue;
+        int sb, sn;
+        if (!lists.source(k, e, sb, sn)) continue;
         j0 = sb;
         se = sn;
         return true;
@@ -1346,7 +1363,7 @@ template <bool POT, typename Lists>
 __global__ void __launch_bounds__(256) p2p_wg_kernel(P2PArgs k, Lists lists)
 {
     __shared__ float4 tile[2][256];
-    __shared__ int nbr[27];
+    __shared__ int nbr[18];
     const int c = blockIdx.x, tid = threadIdx.x;
     const int tb = k.cell_start[c], te = k.cell_start[c + 1];
     if (tb < 0 || te < tb || te > k.n) return;
@@ -1365,14 +1382,14 @@ __global__ void __launch_bounds__(256) p2p_wg_kernel(P2PArgs k, Lists lists)
         Total<1, POT> tot;
         zero(tot);
         int e = lo - 1, j0 = 0, se = 0;
-        bool have = next_tile256(k, lists, c, hi, e, j0, se);
+        bool have = next_tile256(k, lists, hi, e, j0, se);
         if (have) tile[0][tid] = load_or_zero(k.pos, j0 + tid, se);
         __syncthreads();
         int buf = 0;
         while (have) {
             const int cnt = se - j0 < 256 ? se - j0 : 256;
             int e2 = e, j2 = j0, se2 = se;
-            const bool have2 = next_tile256(k, lists, c, hi, e2, j2, se2);
+            const bool have2 = next_tile256(k, lists, hi, e2, j2, se2);
             if (have2) probe_poison(tile[buf ^ 1][tid]);
             const int jn = j2 + tid;
             float4 r = make_float4(0.0f, 0.0f, 0.0f, 0.0f);

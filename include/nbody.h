@@ -263,8 +263,9 @@ int nbody_p2p(const nbody_f4 *pos_xyzm, int64_t N, float eps2, const int32_t *ce
  * bodies outside the box join the boundary cells), and gets the sum over every
  * body in its own and the 26 neighbouring cells (itself included). The library
  * bins the bodies (stable radix sort of the cell indices, so a cell keeps its
- * bodies in their input order), runs the nbody_p2p kernel with the 27-cell
- * neighbourhoods and writes acc_out / pot_out in the caller's body order.
+ * bodies in their input order), runs the nbody_p2p kernel over the 27-cell
+ * neighbourhoods (as 9 runs of 3 consecutive cells) and writes acc_out /
+ * pot_out in the caller's body order.
  * At most 2^28 cells. Scratch: ~N x 56 bytes + 4 bytes per cell + the sort's.
  */
 int nbody_near_grid(const nbody_f4 *pos_xyzm, int64_t N, float eps2, const float lo[3], float h,
