@@ -252,23 +252,27 @@ def accel(pos, eps2: float, pot: bool = True, plan=None):
     n = pos.shape[0]
     acc = torch.empty_like(pos)
     p = torch.empty(n, dtype=torch.float32, device=pos.device) if pot else None
-    if plan is None:
-        nbody_accel(pos, n, eps2, acc, p)
-    else:
-        nbody_accel_plan(pos, n, eps2, acc, p, plan)
+    with torch.cuda.device(pos.device):  # the library works on the current device and stream
+        if plan is None:
+            nbody_accel(pos, n, eps2, acc, p)
+        else:
+            nbody_accel_plan(pos, n, eps2, acc, p, plan)
     return acc, p
 
 
 def step(pos, vel, dt: float, eps2: float, nsteps: int = 1, plan=None):
     """nsteps Euler steps in place on pos and vel (N, 4) tensors, on the current stream."""
+    import torch
+
     _bodies(pos, "pos")
     _bodies(vel, "vel")
-    if vel.shape != pos.shape:
-        raise ValueError("pos and vel shapes differ")
-    if plan is None:
-        nbody_step(pos, vel, pos.shape[0], dt, eps2, nsteps)
-    else:
-        nbody_step_plan(pos, vel, pos.shape[0], dt, eps2, nsteps, plan)
+    if vel.shape != pos.shape or vel.device != pos.device:
+        raise ValueError("pos and vel differ in shape or device")
+    with torch.cuda.device(pos.device):
+        if plan is None:
+            nbody_step(pos, vel, pos.shape[0], dt, eps2, nsteps)
+        else:
+            nbody_step_plan(pos, vel, pos.shape[0], dt, eps2, nsteps, plan)
     return pos, vel
 
 
@@ -286,13 +290,14 @@ def diagnostics(pos, vel, eps2: float, pot=None) -> dict:
 
     _bodies(pos, "pos")
     _bodies(vel, "vel")
-    if vel.shape != pos.shape:
-        raise ValueError("pos and vel shapes differ")
+    if vel.shape != pos.shape or vel.device != pos.device:
+        raise ValueError("pos and vel differ in shape or device")
     if pot is not None and not (isinstance(pot, torch.Tensor) and pot.is_cuda
                                 and pot.dtype == torch.float32 and pot.shape == (pos.shape[0],)
-                                and pot.is_contiguous()):
-        raise ValueError("pot must be a contiguous float32 CUDA tensor of shape (N,)")
-    out = torch.zeros(13, dtype=torch.float64, device=pos.device)
-    nbody_diagnostics(pos, vel, pos.shape[0], eps2, out, pot)
-    torch.cuda.current_stream().synchronize()
-    return unpack_diag(out.cpu().tolist())
+                                and pot.is_contiguous() and pot.device == pos.device):
+        raise ValueError("pot must be a contiguous float32 tensor of shape (N,) on pos's device")
+    with torch.cuda.device(pos.device):
+        out = torch.zeros(13, dtype=torch.float64, device=pos.device)
+        nbody_diagnostics(pos, vel, pos.shape[0], eps2, out, pot)
+        torch.cuda.current_stream().synchronize()
+        return unpack_diag(out.cpu().tolist())
