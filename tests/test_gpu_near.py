@@ -136,10 +136,12 @@ def gpu_near_grid(nb, pos, eps2, lo, h, dims, pot=True):
 
 @pytest.mark.parametrize("n,dims,h", [(1, (1, 1, 1), 4.0), (500, (2, 2, 2), 1.0),
                                       (3000, (5, 5, 5), 0.4), (20000, (8, 8, 8), 0.25),
-                                      (20000, (13, 3, 7), 0.2)])
+                                      (20000, (13, 3, 7), 0.2), (3000, (1, 6, 5), 0.4),
+                                      (3000, (7, 1, 1), 0.3), (3000, (2, 9, 1), 0.25)])
 def test_near_grid_uniform(nb, n, dims, h):
     """Uniform cube [-1, 1]^3 on grids of several shapes (bodies beyond the last cell join
-    the boundary cells) against the grid definition."""
+    the boundary cells; one- and two-cell x extents, where a neighbourhood run holds one or
+    two cells) against the grid definition."""
     import oracle
 
     pos, _ = workloads.random_bodies(n, seed=3000 + n)
