@@ -257,3 +257,19 @@ def test_error_raises_in_checked_mode(nb):
 
 def test_version(nb):
     assert "gfx950" in nb.nbody_version()
+
+
+def test_torch_conveniences_reject_bad_tensors(nb):
+    """accel / step / diagnostics check their tensors before any library call: CPU tensors,
+    wrong dtype or shape, non-contiguous views (no GPU needed)."""
+    import torch
+
+    good_shape = torch.zeros(8, 4)
+    for bad in (good_shape, torch.zeros(8, 4, dtype=torch.float64), torch.zeros(8, 3),
+                torch.zeros(4, 8).t()):
+        with pytest.raises(ValueError):
+            nb.accel(bad, 1e-4)
+        with pytest.raises(ValueError):
+            nb.step(bad, bad, 1e-3, 1e-4)
+        with pytest.raises(ValueError):
+            nb.diagnostics(bad, bad, 1e-4)
