@@ -1191,6 +1191,20 @@ __device__ __forceinline__ bool next_tile(const P2PArgs &k, const Lists &lists, 
 constexpr int kP2PWideT = 4;
 constexpr int kP2PWideMin = 192;
 
+// Whether a cell of r bodies has a chunk q >= 1 (the chunk sequence below:
+// 256 targets while at least kP2PWideMin remain with QUAD, then 64, then the
+// rest). Only q = 1 is asked: the launches use at most two waves per cell.
+template <bool QUAD>
+__device__ __forceinline__ bool cell_has_chunk(int r, int q)
+{
+    int n = 0;
+    while (r > 0 && n <= q) {
+        r -= (QUAD && r >= kP2PWideMin) ? 64 * kP2PWideT : 64;
+        ++n;
+    }
+    return n > q;
+}
+
 // Targets per chunk: a cell's bodies go up to 256 at a time (four per lane)
 // while at least 192 remain, then 64 at a time; a chunk of r < 64 bodies
 // takes tw = the next power of two >= r lanes per source group and G = 64 / tw
@@ -1207,13 +1221,22 @@ __global__ void __launch_bounds__(64) p2p_kernel(P2PArgs k, Lists lists)
     const int c = blockIdx.x, lane = threadIdx.x;
     const int tb = k.cell_start[c], te = k.cell_start[c + 1];
     if (tb < 0 || te < tb || te > k.n) return;
+    // wave blockIdx.y of the cell's gridDim.y waves takes its chunks q with
+    // q mod gridDim.y == blockIdx.y; it exits at once when it has none
+    const int ny = (int)gridDim.y, y = (int)blockIdx.y;
+    if (y > 0 && !cell_has_chunk<QUAD>(te - tb, y)) return;
     if constexpr (__is_same(Lists, GridLists)) lists.nbr = nbr;
     lists.bind(c);
     int lo, hi;
     lists.range(c, lo, hi);
     const float eps2 = in_vgpr(k.eps2);
-    for (int t0 = tb; t0 < te;) {
+    for (int t0 = tb, q = 0; t0 < te; ++q) {
         const int rem = te - t0;
+        const bool mine = q % ny == y;
+        if (QUAD && rem >= kP2PWideMin && !mine) {
+            t0 += 64 * kP2PWideT;
+            continue;
+        }
         if (QUAD && rem >= kP2PWideMin) {
             // up to 256 targets, four per lane (target t0 + q * 64 + lane; past the
             // cell end a lane computes on a clamped body and stores nothing): each
@@ -1269,6 +1292,10 @@ __global__ void __launch_bounds__(64) p2p_kernel(P2PArgs k, Lists lists)
         while (tw < rem && tw < 64) {
             tw <<= 1;
             ++lg;
+        }
+        if (!mine) {
+            t0 += tw;
+            continue;
         }
         const int groups = 64 >> lg;
         const int t = lane & (tw - 1), g = lane >> lg;
@@ -1652,7 +1679,10 @@ hipError_t launch_p2p_any(bool pot, bool wide, const P2PArgs &args, Lists l, hip
     else
         fn = pot ? (const void *)&p2p_kernel<true, Lists, false>
                  : (const void *)&p2p_kernel<false, Lists, false>;
-    return hipLaunchKernel(fn, dim3((unsigned)a.ncell), dim3(wide ? 256 : 64), k, 0, stream);
+    // one-wave kernels: two waves per cell, each taking every other target chunk, so
+    // a cell's large chunk and the chunk of its remaining bodies run side by side
+    return hipLaunchKernel(fn, dim3((unsigned)a.ncell, wide ? 1u : 2u), dim3(wide ? 256 : 64), k, 0,
+                           stream);
 }
 
 hipError_t launch_p2p(bool pot, bool wide, const P2PArgs &args, hipStream_t stream)
