@@ -140,13 +140,15 @@ constexpr int kMaxSplits = 4096;
 // and one start index per cell).
 constexpr int64_t kMaxGridCells = (int64_t)1 << 28;
 
-// Near field: one wave per cell unless the cells are large (at least 96 bodies
-// on average) and too few to give each SIMD several waves (fewer than 16 per
+// Near field: two waves per cell unless the cells are large (at least 96 bodies
+// on average) and too few to give each SIMD several waves (fewer than 10 per
 // CU): then one 256-thread workgroup per cell sharing its source tiles.
-// Measured on N = 2^20 uniform cubes: 512 cells of 2048 bodies 29 vs 103 ms,
-// 1728 of 607: 7.6 vs 10.8 ms; 4096 of 256: 3.8 vs 3.5 ms (one wave better).
+// Measured on N = 2^20 uniform cubes (workgroup vs two waves per cell): 512
+// cells of 2048 bodies 29.2 vs 42.8 ms, 1000 of 1049: 13.8 vs 15.2 ms, 1728 of
+// 607: 7.5 vs 8.1 ms, 2197 of 477: 5.44 vs 5.53 ms; 2744 of 382: 4.44 vs 4.14
+// ms and 3375 of 311: 4.21 vs 3.20 ms (two waves better).
 constexpr int64_t kWideCellBodies = 96;
-constexpr int64_t kWideMaxCellsPerCU = 16;
+constexpr int64_t kWideMaxCellsPerCU = 10;
 int wide_cells(int64_t n, int64_t ncell, bool *wide)
 {
     *wide = false;

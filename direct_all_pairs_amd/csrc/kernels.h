@@ -109,7 +109,8 @@ hipError_t launch_diagnostics(const float4 *pos, const float4 *vel, const float 
                               double inv_eps, double *part, double *out, hipStream_t stream);
 
 // Near field: target cell c (bodies [cell_start[c], cell_start[c+1])) sums over
-// the bodies of the cells in its interaction list. One wave per target cell.
+// the bodies of the cells in its interaction list. Two one-wave workgroups per
+// target cell (alternate target chunks), or one 256-thread workgroup.
 struct P2PArgs {
     const float4 *pos;      // N bodies grouped by cell
     int n;                  // N
@@ -132,8 +133,9 @@ struct GridSpec {
 };
 
 // wide: one 256-thread workgroup per cell sharing 256-body source tiles (large
-// cells); otherwise one wave per cell (small cells), whose chunks of 192 or
-// more targets take four per lane when cells average at least 192 bodies.
+// cells); otherwise two waves per cell (small cells) taking alternate target
+// chunks, where chunks of 192 or more targets take four per lane when cells
+// average at least 192 bodies.
 hipError_t launch_p2p(bool pot, bool wide, const P2PArgs &args, hipStream_t stream);
 // The same kernels with the 27 neighbour cells of the grid as every cell's list.
 hipError_t launch_p2p_grid(bool pot, bool wide, const P2PArgs &args, const GridSpec &g,

@@ -1086,8 +1086,9 @@ __global__ void __launch_bounds__(256) diag_final_kernel(const double *__restric
 // ---------------------------------------------------------------- near field
 // All-pairs as the near part of a hierarchical method (GPU Gems 3 ch. 31 study
 // page, section 6; Nakasato, "スライド 1", No.34): each target cell's bodies
-// sum over the bodies of the cells in its interaction list. One wave (64
-// threads) per target cell: the cell's bodies 64 at a time, one per lane; each
+// sum over the bodies of the cells in its interaction list. Two waves (64
+// threads each) per target cell, taking alternate chunks of the cell's bodies,
+// 64 at a time, one per lane (or 256, four per lane); each
 // listed source cell is staged through the wave's own 64-body LDS row and read
 // back with LDS reads (a broadcast within each source group). Every source
 // tile is one block of the compensated two-level accumulation. Ranges and list entries are
