@@ -141,14 +141,14 @@ constexpr int kMaxSplits = 4096;
 constexpr int64_t kMaxGridCells = (int64_t)1 << 28;
 
 // Near field: two waves per cell unless the cells are large (at least 96 bodies
-// on average) and too few to give each SIMD several waves (fewer than 10 per
-// CU): then one 256-thread workgroup per cell sharing its source tiles.
-// Measured on N = 2^20 uniform cubes (workgroup vs two waves per cell): 512
-// cells of 2048 bodies 29.2 vs 42.8 ms, 1000 of 1049: 13.8 vs 15.2 ms, 1728 of
-// 607: 7.5 vs 8.1 ms, 2197 of 477: 5.44 vs 5.53 ms; 2744 of 382: 4.44 vs 4.14
-// ms and 3375 of 311: 4.21 vs 3.20 ms (two waves better).
+// on average) and few (fewer than 12 per CU): then 256-thread workgroups sharing
+// source tiles, about one per 256-target chunk of a cell. Measured on N = 2^20
+// uniform cubes (workgroups vs two waves per cell): 216 cells of 4855 bodies
+// 34.6 vs 178 ms, 512 of 2048: 18.3 vs 42.9 ms, 1000 of 1049: 9.7 vs 15.3 ms,
+// 2197 of 477: 4.39 vs 5.50 ms, 2744 of 382: 4.14 vs 4.28 ms; 3375 of 311: 4.02
+// vs 3.21 ms and 4096 of 256: 3.17 vs 2.64 ms (two waves better).
 constexpr int64_t kWideCellBodies = 96;
-constexpr int64_t kWideMaxCellsPerCU = 10;
+constexpr int64_t kWideMaxCellsPerCU = 12;
 int wide_cells(int64_t n, int64_t ncell, bool *wide)
 {
     *wide = false;

@@ -110,7 +110,8 @@ hipError_t launch_diagnostics(const float4 *pos, const float4 *vel, const float 
 
 // Near field: target cell c (bodies [cell_start[c], cell_start[c+1])) sums over
 // the bodies of the cells in its interaction list. Two one-wave workgroups per
-// target cell (alternate target chunks), or one 256-thread workgroup.
+// target cell (alternate target chunks), or 256-thread workgroups (one per
+// 256-target chunk, up to 16 per cell).
 struct P2PArgs {
     const float4 *pos;      // N bodies grouped by cell
     int n;                  // N
@@ -132,10 +133,10 @@ struct GridSpec {
     int dims[3];
 };
 
-// wide: one 256-thread workgroup per cell sharing 256-body source tiles (large
-// cells); otherwise two waves per cell (small cells) taking alternate target
-// chunks, where chunks of 192 or more targets take four per lane when cells
-// average at least 192 bodies.
+// wide: 256-thread workgroups sharing 256-body source tiles, about one per
+// 256-target chunk of a cell (large cells); otherwise two waves per cell (small
+// cells) taking alternate target chunks, where chunks of 192 or more targets
+// take four per lane when cells average at least 192 bodies.
 hipError_t launch_p2p(bool pot, bool wide, const P2PArgs &args, hipStream_t stream);
 // The same kernels with the 27 neighbour cells of the grid as every cell's list.
 hipError_t launch_p2p_grid(bool pot, bool wide, const P2PArgs &args, const GridSpec &g,

@@ -41,6 +41,8 @@
 // conversion.
 #include "kernels.h"
 
+#include <cmath>
+
 namespace nbk {
 
 namespace {
@@ -1363,8 +1365,9 @@ __global__ void __launch_bounds__(64) p2p_kernel(P2PArgs k, Lists lists)
     }
 }
 
-// Large cells: one 256-thread workgroup per target cell, 256 targets per chunk
-// (one per thread), source tiles of 256 bodies staged once for all four waves
+// Large cells: gridDim.y 256-thread workgroups per target cell, each taking
+// every gridDim.y-th chunk of 256 targets (one per thread); source tiles of 256
+// bodies are staged once for all four waves
 // (double-buffered, one barrier per tile: the barrier after a tile both
 // publishes the next buffer and guards the one about to be overwritten), read
 // with uniform addresses. The cursor over (list entry, tile) is uniform.
@@ -1395,12 +1398,15 @@ __global__ void __launch_bounds__(256) p2p_wg_kernel(P2PArgs k, Lists lists)
     const int c = blockIdx.x, tid = threadIdx.x;
     const int tb = k.cell_start[c], te = k.cell_start[c + 1];
     if (tb < 0 || te < tb || te > k.n) return;
+    // workgroup blockIdx.y of gridDim.y takes every gridDim.y-th 256-target chunk
+    const int ny = (int)gridDim.y, y = (int)blockIdx.y;
+    if (y > 0 && tb + 256 * y >= te) return;
     if constexpr (__is_same(Lists, GridLists)) lists.nbr = nbr;
     lists.bind(c);
     int lo, hi;
     lists.range(c, lo, hi);
     const float eps2 = in_vgpr(k.eps2);
-    for (int t0 = tb; t0 < te; t0 += 256) {
+    for (int t0 = tb + 256 * y; t0 < te; t0 += 256 * ny) {
         const int i = t0 + tid;
         const float4 me = k.pos[i < te ? i : te - 1];
         Targets<1> tg;
@@ -1681,9 +1687,17 @@ hipError_t launch_p2p_any(bool pot, bool wide, const P2PArgs &args, Lists l, hip
         fn = pot ? (const void *)&p2p_kernel<true, Lists, false>
                  : (const void *)&p2p_kernel<false, Lists, false>;
     // one-wave kernels: two waves per cell, each taking every other target chunk, so
-    // a cell's large chunk and the chunk of its remaining bodies run side by side
-    return hipLaunchKernel(fn, dim3((unsigned)a.ncell, wide ? 1u : 2u), dim3(wide ? 256 : 64), k, 0,
-                           stream);
+    // a cell's large chunk and the chunk of its remaining bodies run side by side;
+    // the workgroup kernel: about one workgroup per 256-target chunk of a cell a
+    // little larger than the mean (at most 16), so large cells spread over the GPU
+    unsigned ny = 2;
+    if (wide) {
+        const double m = (double)a.n / (double)a.ncell;
+        const double chunks = (m + 3.0 * std::sqrt(m)) / 256.0;
+        ny = chunks >= 16.0 ? 16u : (unsigned)std::ceil(chunks);
+        if (ny < 1) ny = 1;
+    }
+    return hipLaunchKernel(fn, dim3((unsigned)a.ncell, ny), dim3(wide ? 256 : 64), k, 0, stream);
 }
 
 hipError_t launch_p2p(bool pot, bool wide, const P2PArgs &args, hipStream_t stream)
