@@ -207,6 +207,22 @@ def test_near_grid_few_large_cells(nb):
     assert_accel_parity(acc, pot, ref, idx=idx, what="few large cells")
 
 
+def test_near_grid_huge_cells_sixteen_workgroups(nb):
+    """Eight cells of ~7500 bodies (2 x 2 x 2: the near field is the whole direct sum): 30
+    target chunks per cell over 16 workgroups per cell, so some take two chunks and some one;
+    sampled targets (both ends of every cell range included) against the direct sum."""
+    import oracle
+
+    n = 60000
+    pos, _ = workloads.random_bodies(n, seed=61)
+    acc, pot = gpu_near_grid(nb, pos, 1e-4, (-1.0, -1.0, -1.0), 1.0, (2, 2, 2))
+    rng = np.random.default_rng(8)
+    idx = np.unique(np.concatenate([rng.integers(0, n, 800), [0, n - 1]]))
+    ref = oracle.accel(pos, np.float32(1e-4), targets=idx)
+    assert_accel_parity(acc, pot, ref, idx=idx, what="2x2x2 grid of 7500-body cells")
+    assert np.all(np.isfinite(acc)) and np.all(np.isfinite(pot))  # every body written
+
+
 def test_near_grid_many_large_cells_four_targets_per_lane(nb):
     """N = 2^20 on a 16^3 grid (4096 cells of ~256 bodies: one wave per cell, chunks of 192 or
     more targets four per lane, the rest one per lane); sampled targets against the grid
