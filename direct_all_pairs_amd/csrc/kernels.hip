@@ -753,8 +753,9 @@ __device__ __forceinline__ void pairs_item(const PairsArgs &k, int A, int B, int
 #pragma unroll U
             for (int step = 0; step < 64; ++step) {
                 const int nxt = ((cur - (int)sizeof(float4)) & (kBlkBytes - 1)) | row;
-                // partner of the next step, read ahead of this step's arithmetic
-                const float4 nb4 = at_byte<const float4>(&sh.jblk[0][0], nxt);
+                // the partner's sums first, then the partner of the next step (read
+                // ahead of this step's arithmetic): LDS reads return in order, so the
+                // first FMA into the sums waits only for the first read
                 float gx = 0.0f, gy = 0.0f, gz = 0.0f, gp = 0.0f;
                 if constexpr (SYM) {
                     const float4 g = at_byte<const float4>(&sh.jsum[0][0], cur);
@@ -763,6 +764,7 @@ __device__ __forceinline__ void pairs_item(const PairsArgs &k, int A, int B, int
                     gz = g.z;
                     gp = g.w;
                 }
+                const float4 nb4 = at_byte<const float4>(&sh.jblk[0][0], nxt);
                 pair_step<T, POT, SYM>(jx, jy, jz, jm, tx, ty, tz, tm, eps2, bx, by, bz, bp, gx,
                                        gy, gz, gp);
                 if constexpr (SYM) {
