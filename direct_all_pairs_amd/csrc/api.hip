@@ -168,7 +168,7 @@ int wide_cells(int64_t n, int64_t ncell, bool *wide)
 constexpr int64_t kSmallMaxN = 6656;
 // Largest N whose automatic band is 256 bodies (4 targets per lane): many
 // small work items fill the GPU there; above it, 512-2048 with 8 per lane.
-constexpr int64_t kBand256MaxN = 49151;
+constexpr int64_t kBand256MaxN = 36863;
 
 int valid_tpl(int t) { return t == 1 || t == 2 || t == 4 || t == 8; }
 
@@ -211,9 +211,10 @@ int pass_band(int64_t q, int64_t nb, int64_t passes) { return (int)(q * nb / pas
 //     at 7168), the small-N kernel (one kernel per evaluation or step): 4
 //     targets per workgroup to N = 2048, 8 to 6144, 16 above;
 //   - above it, pair-symmetric bands when their scratch fits: 256 bodies with
-//     4 targets per lane to N = 49151 (even with 512 at 49152, ahead by 18 %
-//     at 20480), then the largest band that still yields at least 64 work
-//     items per compute unit, with 8 targets per lane;
+//     4 targets per lane to N = 36863 (2 % ahead of 512 with 8 per lane at
+//     32768, 2 % behind at 40960, timed round-robin), then the largest band
+//     that still yields at least 64 work items per compute unit, with 8
+//     targets per lane;
 //   - otherwise one-sided tiles with the LDS broadcast and one target per lane:
 //     every VALU operand of the inner step is then a VGPR, which issues about
 //     twice as fast as an SGPR operand; 512-thread workgroups (512-body LDS
@@ -224,7 +225,7 @@ int pass_band(int64_t q, int64_t nb, int64_t passes) { return (int)(q * nb / pas
 int small_tw(int64_t n) { return n <= 2048 ? 4 : (n <= 6144 ? 8 : 16); }
 
 // The automatic pair band for N and a requested tpl (0 = any): 256 bodies to
-// N = 49151, above it the largest band with at least 64 work items per
+// N = 36863, above it the largest band with at least 64 work items per
 // compute unit (512 at least).
 int auto_band(int64_t n, int tpl, const DeviceFacts &dev)
 {
