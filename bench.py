@@ -6,10 +6,16 @@ Default workload: N = 1,048,576 bodies, uniform cube [-1,1]^3, masses uniform in
 
 Prints one JSON line:
   value    = whole-job body-body interactions per second, in G/s (N^2 per step)
-  gflops   = 20 flop per interaction (the pair-routine count on the CSDN
-             "Cuda Nbody笔记" page / GPU Gems 3 ch. 31)
-  roofline = the acceleration kernel against the FP32 vector peak (ALU bound)
-  cpu_baseline = the fp64 oracle on the host cores, on a bounded target sample
+  gflops_at_20, pct_fp32_peak_at_20 = the metric's convention: 20 flop per
+             interaction (the pair-routine count on the CSDN "Cuda Nbody笔记"
+             page / GPU Gems 3 ch. 31) over the whole call
+  roofline = the pair-term kernel alone (HIP events the library records around
+             its launch, nbody_time_kernel) against the FP32 vector peak, with
+             the FP32 flops its own formulation issues per launch (a symmetric
+             pair 30, a one-sided term 21 with the potential; 26 and 19 without)
+  cpu_baseline = the fp64 oracle on the host cores: every target for N <= 67584,
+             else 65,536 random targets plus the first and last 1024 bodies
+             against all N sources, with the full-N time extrapolated
 """
 
 from __future__ import annotations
@@ -29,6 +35,14 @@ if str(ROOT) not in sys.path:
 
 FLOPS_PER_INTERACTION = 20  # 3 (r_ij) + 6 (|r|^2 + eps^2) + 4 (inv^3) + 1 (m inv^3) + 6 (a +=)
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X: 256 CU x 2.4 GHz x 256 FP32 flop/clk/CU (packed FMA)
+# FP32 flops (FMA = 2, v_rsq_f32 = 1) of one pair term as the kernels write it:
+#  one-sided term (tiles and small-N kernels, the diagonal items of the pair kernel):
+#    3 sub (d), 3 FMA (|d|^2 + eps2), rsq, 3 mul (m / r^3), 3 FMA (a) [+ 1 FMA (p)]
+#  unordered pair of the pair kernel (applied to both bodies):
+#    3 sub, 3 FMA, rsq, 2 mul (inv^3), 2 mul (m_i / r^3, m_j / r^3), 6 FMA (a_i, a_j)
+#    [+ 2 FMA (p_i, p_j)]
+FLOPS_ONE_SIDED = {True: 21, False: 19}   # keyed by "with the potential"
+FLOPS_PAIR = {True: 30, False: 26}
 PROFILE_TRAFFIC = ROOT / "profiles" / "accel_cube1m_traffic.json"
 KERNEL_SOURCES = [ROOT / "direct_all_pairs_amd" / "csrc" / "kernels.hip",
                   ROOT / "direct_all_pairs_amd" / "csrc" / "kernels.h"]
@@ -38,6 +52,49 @@ def interactions(n: int) -> int:
     """Pair interactions per evaluation: every target against every source, self pairs
     included (N^2), as the GPU Gems 3 ch. 31 study page's lab counts them."""
     return n * n
+
+
+def pair_item_terms(n: int, band: int, a0: int, a1: int) -> tuple[int, int]:
+    """(one-sided terms, unordered pairs) of the pair kernel's items (A, d) for bands A in
+    [a0, a1): the diagonal item (A, 0) takes |A|^2 one-sided terms (self pairs included), item
+    (A, d), d = 1 .. nb/2, the |A| |B| pairs with B = (A + d) mod nb, where for even nb the
+    item d = nb/2 exists only for A < nb/2."""
+    import numpy as np
+
+    nb = (n + band - 1) // band
+    size = np.minimum(band, n - band * np.arange(nb, dtype=np.int64))
+    a = np.arange(a0, a1, dtype=np.int64)
+    diag = int(np.sum(size[a] ** 2))
+    off = 0
+    for d in range(1, nb // 2 + 1):
+        own = a if not (2 * d == nb) else a[a < nb // 2]
+        off += int(np.sum(size[own] * size[(own + d) % nb]))
+    return diag, off
+
+
+def first_launch_work(n: int, plan, pot: bool) -> dict:
+    """The pair terms and FP32 flops of the first pair-term kernel launch of one evaluation
+    (the launch nbody_time_kernel brackets): the whole evaluation, or pass 0 of a
+    multi-pass pair plan."""
+    mode = {1: "tiles", 2: "pairs", 3: "small"}[plan.mode]
+    if mode == "pairs":
+        nb = (n + plan.band - 1) // plan.band
+        a1 = nb // max(1, plan.passes)  # pass 0: bands [0, floor(nb / passes))
+        diag, off = pair_item_terms(n, plan.band, 0, a1)
+        flops = FLOPS_ONE_SIDED[pot] * diag + FLOPS_PAIR[pot] * off
+        name = f"accel_pairs<{plan.tpl}, {plan.band}, {str(pot).lower()}>"
+        return {"kernel": name, "interactions": diag + 2 * off, "flops": flops,
+                "units": {"one_sided_terms": diag, "pairs": off},
+                "flops_per_unit": {"one_sided_term": FLOPS_ONE_SIDED[pot],
+                                   "pair": FLOPS_PAIR[pot]}}
+    if mode == "small":
+        name = f"accel_small<{plan.tpl}, ...>"
+    else:
+        bcast = {1: "lds", 2: "scalar", 3: "readlane"}[plan.bcast]
+        name = f"accel_{bcast}<{plan.tpl}, ...>"
+    return {"kernel": name, "interactions": n * n, "flops": FLOPS_ONE_SIDED[pot] * n * n,
+            "units": {"one_sided_terms": n * n},
+            "flops_per_unit": {"one_sided_term": FLOPS_ONE_SIDED[pot]}}
 
 
 def tile_global_loads(n: int, p: int) -> int:
@@ -73,35 +130,47 @@ def measured_traffic(kernel_hash: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(pos_h, eps2, budget_s: float, gpu_acc=None, gpu_pot=None):
-    """Time the fp64 oracle (as it stands) on a target sample of the same workload; with the
-    GPU's accelerations (and potentials) of that workload, also report their largest error on
-    the sample in units of the per-body bounds B_i (and P_i)."""
+def cpu_sample_targets(n: int) -> tuple[object, str]:
+    """The oracle's targets for the CPU baseline: every body for N <= 67,584; above, 65,536
+    distinct random bodies (seed 12345) from [1024, N - 1024) plus [0, 1024) and
+    [N - 1024, N), against all N sources."""
+    import numpy as np
+
+    if n <= 65536 + 2048:
+        return np.arange(n), f"all {n} targets"
+    rng = np.random.default_rng(12345)
+    mid = 1024 + rng.choice(n - 2048, 65536, replace=False)
+    idx = np.concatenate([np.arange(1024), np.sort(mid), np.arange(n - 1024, n)])
+    return idx, "65,536 random targets plus [0, 1024) and [N - 1024, N)"
+
+
+def cpu_baseline(pos_h, eps2, gpu_acc=None, gpu_pot=None):
+    """Time the fp64 oracle (as it stands) on the sample of cpu_sample_targets against all N
+    sources; report its rate, the full-N time extrapolated from it, and, with the GPU's
+    accelerations (and potentials) of the same workload, their largest error on the sample in
+    units of the per-body bounds B_i (and P_i)."""
     import numpy as np
 
     import oracle
 
     n = pos_h.shape[0]
-    rng = np.random.default_rng(12345)
     threads = oracle.num_threads()
-    oracle.accel(pos_h, eps2, targets=rng.integers(0, n, threads))  # start the thread pool
-    probe = rng.integers(0, n, 64 * threads)  # several 16-target chunks per thread
-    t0 = time.perf_counter()
-    oracle.accel(pos_h, eps2, targets=probe)
-    t_probe = time.perf_counter() - t0
-    per_target = t_probe / len(probe)
-    nt = int(max(64, min(n, budget_s / max(per_target, 1e-9))))
-    idx = rng.integers(0, n, nt)
+    idx, what = cpu_sample_targets(n)
+    oracle.accel(pos_h, eps2, targets=np.arange(min(n, threads)))  # start the thread pool
     t0 = time.perf_counter()
     ref = oracle.accel(pos_h, eps2, targets=idx)
     t = time.perf_counter() - t0
-    rate = nt * n / t
+    rate = len(idx) * n / t
     out = {
         "value": rate / 1e9,
         "unit": "G interactions/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{nt} random targets x all {n} sources (fp64 accel+pot+bounds), {t:.1f} s",
+        "sample": f"{what} ({len(idx)} targets) x all {n} sources, fp64 acceleration + "
+                  f"potential + bounds: {t:.1f} s measured",
+        "full_n_seconds": n * t / len(idx),
+        "full_n_seconds_is": "measured" if len(idx) == n else
+                             "extrapolated from the sample's rate (N / sample targets x its time)",
     }
     if gpu_acc is not None:
         a = np.asarray(gpu_acc)[idx, :3].astype(np.float64)
@@ -160,7 +229,7 @@ class ClockSampler:
         self._stop.set()
         self._thread.join(timeout=30)
 
-    def summary(self, pct_at_nominal: float):
+    def summary(self, frac_at_nominal: float):
         if not self.samples:
             return None
         v = sorted(self.samples)
@@ -168,7 +237,7 @@ class ClockSampler:
         return {"median_mhz": round(med), "samples": len(v),
                 "source": "amd-smi metric -c, mean of the XCD gfx clocks, sampled from the end of "
                 "the second warm-up call to the end of the timed steps",
-                "pct_fp32_peak_at_measured_sclk": round(pct_at_nominal * 2400.0 / med, 2)}
+                "roofline_frac_at_measured_sclk": round(frac_at_nominal * 2400.0 / med, 4)}
 
 
 def copy_calibration(nbytes: int) -> int:
@@ -277,17 +346,26 @@ def near_grid_bench(nb, w, pos, args) -> int:
         nb.nbody_near_grid(pos, n, float(w.eps2), lo, h, dims, acc, pot, stream)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    ks = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    for e in ks:
+        e.record(stream)
     e0.record(stream)
-    for _ in range(args.steps):
+    for k in range(args.steps):
+        nb.nbody_time_kernel(ks[2 * k], ks[2 * k + 1])
         nb.nbody_near_grid(pos, n, float(w.eps2), lo, h, dims, acc, pot, stream)
     e1.record(stream)
     torch.cuda.synchronize()
+    nb.nbody_time_kernel(None, None)
     ms = e0.elapsed_time(e1) / args.steps
+    kms = sum(ks[2 * k].elapsed_time(ks[2 * k + 1]) for k in range(args.steps)) / args.steps
     terms = near_grid_terms(w.pos, lo, h, dims)
     print(json.dumps({"near_grid": {"workload": args.workload, "N": n, "dims": dims, "h": h,
                                     "bodies_per_cell": n / (d ** 3), "pair_terms": terms,
                                     "ms": round(ms, 4),
-                                    "G_terms_per_s": round(terms / ms / 1e6, 2)}}), flush=True)
+                                    "G_terms_per_s": round(terms / ms / 1e6, 2),
+                                    "kernel_ms": round(kms, 4),
+                                    "kernel_G_terms_per_s": round(terms / kms / 1e6, 2)}}),
+          flush=True)
     return 0
 
 
@@ -335,10 +413,14 @@ def shard_bench(nb, w, pos, args) -> int:
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / args.steps
         it = shard_interactions(n, band, s, S)
+        nbands = (n + band - 1) // band
+        diag, off = pair_item_terms(n, band, s * nbands // S, (s + 1) * nbands // S)
+        flops = FLOPS_ONE_SIDED[True] * diag + FLOPS_PAIR[True] * off
         r = {"workload": args.workload, "N": n, "band": band, "shard": s, "nshards": S,
              "ms": round(ms, 4), "interactions": it, "G_int_per_s": round(it / ms / 1e6, 1),
-             "pct_fp32_peak": round(100 * FLOPS_PER_INTERACTION * it / ms / 1e9
-                                    / FP32_VECTOR_PEAK_TFLOPS, 2)}
+             "frac_fp32_peak": round(flops / ms / 1e9 / FP32_VECTOR_PEAK_TFLOPS, 4),
+             "pct_fp32_peak_at_20": round(100 * FLOPS_PER_INTERACTION * it / ms / 1e9
+                                          / FP32_VECTOR_PEAK_TFLOPS, 2)}
         per.append(r)
         print(json.dumps(r), flush=True)
     t0, t1 = 0, n // S
@@ -375,8 +457,10 @@ def main(argv=None) -> int:
     ap.add_argument("--tpl", type=int, default=0)
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-pot", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0,
-                    help="seconds of oracle work for cpu_baseline (0 = skip)")
+    ap.add_argument("--cpu-budget", type=float, default=1.0,
+                    help="0 skips cpu_baseline; any other value runs it (its sample is fixed: "
+                         "every target up to N = 67584, else 65,536 random targets plus the "
+                         "first and last 1024)")
     ap.add_argument("--sweep", action="store_true",
                     help="time every (broadcast, targets-per-lane, tile, splits) layout of the "
                          "workload's call and print one JSON line per layout (no contract line)")
@@ -426,7 +510,7 @@ def main(argv=None) -> int:
     eff = nb.nbody_plan_for(n, want_pot)
     if plan is not None:
         eff = nb.make_plan(bcast=plan.bcast or eff.bcast, tpl=plan.tpl or eff.tpl,
-                           splits=plan.splits or eff.splits)
+                           splits=plan.splits or eff.splits, mode=nb.MODE_TILES)
     stream = torch.cuda.current_stream()
     evals_per_step = w.nsteps if stepping else 1
 
@@ -460,25 +544,38 @@ def main(argv=None) -> int:
                 clock.__enter__()
     torch.cuda.synchronize()
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    def events(k):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(k)]
+        for e in ev:
+            e.record(stream)  # torch creates the HIP event at its first record
+        return ev
+
+    # per step: the whole call (torch events around it) and its first pair-term kernel
+    # launch alone (events the library records around that launch on the same stream)
+    starts, ends = events(args.steps), events(args.steps)
+    kstarts, kends = events(args.steps), events(args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
+        nb.nbody_time_kernel(kstarts[k], kends[k])
         starts[k].record(stream)
         one_step()
         ends[k].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    nb.nbody_time_kernel(None, None)
     if not args.no_clock and clock.started:
         clock.__exit__()
     ev_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    kern_ms = [s.elapsed_time(e) for s, e in zip(kstarts, kends)]
 
     n_int = interactions(n) * evals_per_step
     ms_per_step = wall * 1e3 / args.steps
     value = n_int * args.steps / wall / 1e9
-    launch_s = float(np.mean(ev_ms)) / 1e3
-    achieved_tflops = FLOPS_PER_INTERACTION * n_int / launch_s / 1e12
+    launch_s = float(np.mean(kern_ms)) / 1e3
+    work = first_launch_work(n, eff, want_pot)
+    achieved_tflops = work["flops"] / launch_s / 1e12
+    conv_tflops = FLOPS_PER_INTERACTION * work["interactions"] / launch_s / 1e12
     khash = kernel_source_hash()
     traffic = measured_traffic(khash) if args.workload == "cube1m" and want_pot else None
     what = (f"{w.nsteps} Euler steps per call (nbody_step)" if stepping else
@@ -507,8 +604,9 @@ def main(argv=None) -> int:
             "device": torch.cuda.get_device_name(dev),
         },
         "gflops_at_20": round(FLOPS_PER_INTERACTION * value, 1),
-        "pct_fp32_peak": round(100 * FLOPS_PER_INTERACTION * value / 1e3 / FP32_VECTOR_PEAK_TFLOPS, 2),
-        "sclk": clock.summary(100 * FLOPS_PER_INTERACTION * value / 1e3 / FP32_VECTOR_PEAK_TFLOPS),
+        "pct_fp32_peak_at_20": round(100 * FLOPS_PER_INTERACTION * value / 1e3
+                                     / FP32_VECTOR_PEAK_TFLOPS, 2),
+        "sclk": clock.summary(achieved_tflops / FP32_VECTOR_PEAK_TFLOPS),
         "roofline": {
             "bound": "alu",
             "achieved": round(achieved_tflops, 3),
@@ -516,8 +614,16 @@ def main(argv=None) -> int:
             "unit": "TFLOP/s",
             "frac": round(achieved_tflops / FP32_VECTOR_PEAK_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "accel kernel (nbody_accel), HIP events on its stream",
+            "kernel": work["kernel"],
+            "timed": "the first pair-term kernel launch of each call, HIP events recorded by "
+                     "the library on the launch stream (nbody_time_kernel)",
+            "flops_per_launch": work["flops"],
+            "units_per_launch": work["units"],
+            "flops_per_unit": work["flops_per_unit"],
             "launch_ms_mean": round(launch_s * 1e3, 4),
+            "call_ms_mean": round(float(np.mean(ev_ms)), 4),
+            "achieved_at_20_flop_convention": round(conv_tflops, 3),
+            "frac_at_20_flop_convention": round(conv_tflops / FP32_VECTOR_PEAK_TFLOPS, 4),
             "kernel_source_hash": khash,
         },
     }
@@ -535,7 +641,7 @@ def main(argv=None) -> int:
         # the GPU results of the last timed evaluation, checked on the oracle's sample
         gpu_acc = acc.cpu().numpy() if not stepping else None
         gpu_pot = pot.cpu().numpy() if (pot is not None and not stepping) else None
-        out["cpu_baseline"] = cpu_baseline(w.pos, w.eps2, args.cpu_budget, gpu_acc, gpu_pot)
+        out["cpu_baseline"] = cpu_baseline(w.pos, w.eps2, gpu_acc, gpu_pot)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

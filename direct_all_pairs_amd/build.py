@@ -13,7 +13,7 @@ CSRC = PKG / "csrc"
 LIB = PKG / "libnbody_amd.so"
 # Test build with the LDS race probe compiled in (loaded only by the race-probe tests).
 PROBE_LIB = PKG / "libnbody_amd_probe.so"
-SOURCES = [CSRC / "api.hip", CSRC / "kernels.hip", CSRC / "sort.hip"]
+SOURCES = [CSRC / "api.hip", CSRC / "kernels.hip"]
 
 # -packed-fp32-ops is switched off on purpose: no v_pk_*_f32 is generated.
 HIPCC_FLAGS = [

@@ -53,10 +53,18 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb)
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
-// eps2 must be a positive, finite, normal float: the softening is what makes
-// the j = i term finite (Degawa, "N 体問題", slide 12), and the rsq of a
-// denormal would not be.
-bool eps2_ok(float e) { return std::isfinite(e) && e >= FLT_MIN; }
+// eps2 must be finite and at least 2^-84: the softening is what makes the
+// j = i term finite (Degawa, "N 体問題", slide 12), and the largest 1/r^3 a
+// pair term forms, eps2^(-3/2) (the self pair), must be finite in fp32. Below
+// 2^-84 it exceeds 2^126 and overflows once cubed from the rsq (the pair kernel
+// forms (inv * inv) * inv), turning the self term into inf * 0 = NaN.
+constexpr float kEps2Min = 0x1p-84f;
+bool eps2_ok(float e) { return std::isfinite(e) && e >= kEps2Min; }
+int eps2_fail(float e)
+{
+    return fail(NBODY_EINVAL, "eps2=%g must be a finite float >= 2^-84 (%g), so that "
+                              "eps2^(-3/2) is finite in fp32", (double)e, (double)kEps2Min);
+}
 
 // ------------------------------------------------------------ device facts
 
@@ -131,6 +139,32 @@ int scratch_get(int dev, hipStream_t stream, size_t bytes, void **out)
     }
     *out = s.ptr;
     return NBODY_OK;
+}
+
+// ------------------------------------------------------------ kernel timing
+// nbody_time_kernel: events of the calling thread, recorded around the first
+// launch of a pair-term kernel in each later call.
+struct KernelTimer {
+    hipEvent_t start = nullptr, stop = nullptr;
+    bool pending = false;  // the current call has not recorded them yet
+};
+thread_local KernelTimer g_timer;
+
+// At the start of every entry point.
+void timer_arm() { g_timer.pending = g_timer.start != nullptr; }
+
+// fn() launches a pair-term kernel; the call's first such launch is bracketed
+// by the events.
+template <typename F>
+hipError_t timed_launch(hipStream_t stream, F &&fn)
+{
+    if (!g_timer.pending) return fn();
+    g_timer.pending = false;
+    hipError_t e = hipEventRecord(g_timer.start, stream);
+    if (e != hipSuccess) return e;
+    e = fn();
+    if (e != hipSuccess) return e;
+    return hipEventRecord(g_timer.stop, stream);
 }
 
 // ------------------------------------------------------------ planning
@@ -436,7 +470,8 @@ int enqueue_pair_passes(const float4 *pos, int n, float eps2, float4 *acc_out, f
         const int own0 = b0 * band;
         const int own_end = (int64_t)b1 * band < n ? b1 * band : n;
         nbk::PairsArgs pa{pos, n, eps2, nb, partA, b0, b1, own_end - own0, own0, partB, 1};
-        hipError_t e = nbk::launch_pairs(band, p.tpl, pot_out != nullptr, pa, stream);
+        hipError_t e = timed_launch(
+            stream, [&] { return nbk::launch_pairs(band, p.tpl, pot_out != nullptr, pa, stream); });
         if (e != hipSuccess) return hip_fail(e, "accel kernel launch");
         nbk::PassArgs ca{partA, partB, n, band, nb, b0, b1, own0, own_end - own0, tot_s, tot_e,
                          q == 0, q + 1 == p.passes, step ? accbuf : acc_out,
@@ -464,7 +499,8 @@ int enqueue_eval(const float4 *pos, int n, float eps2, float4 *acc_out, float *p
     if (p.mode == NBODY_MODE_SMALL) {
         if (step) return fail(NBODY_EINVAL, "internal: small-mode steps go through enqueue_steps");
         nbk::SmallArgs sa{pos, n, eps2, acc_out, pot_out, nullptr, nullptr, 0.0f};
-        hipError_t e = nbk::launch_small(p.tpl, pot, false, sa, stream);
+        hipError_t e = timed_launch(stream,
+                                    [&] { return nbk::launch_small(p.tpl, pot, false, sa, stream); });
         return e == hipSuccess ? NBODY_OK : hip_fail(e, "small kernel launch");
     }
     if (pairs && p.passes > 1)
@@ -481,10 +517,12 @@ int enqueue_eval(const float4 *pos, int n, float eps2, float4 *acc_out, float *p
     hipError_t e;
     if (pairs) {
         nbk::PairsArgs pa{pos, n, eps2, p.splits, a.part, 0, p.splits, n, 0, a.part, 0};
-        e = nbk::launch_pairs(p.band, p.tpl, pot, pa, stream);
+        e = timed_launch(stream, [&] { return nbk::launch_pairs(p.band, p.tpl, pot, pa, stream); });
     } else {
-        e = nbk::launch_accel(p.bcast, p.tpl, p.wg, pot, grid_x(n, p.tpl, p.wg),
-                              (unsigned)p.splits, a, stream);
+        e = timed_launch(stream, [&] {
+            return nbk::launch_accel(p.bcast, p.tpl, p.wg, pot, grid_x(n, p.tpl, p.wg),
+                                     (unsigned)p.splits, a, stream);
+        });
     }
     if (e != hipSuccess) return hip_fail(e, "accel kernel launch");
     if (step) {
@@ -506,7 +544,7 @@ int accel_impl(const nbody_f4 *pos, int64_t N, float eps2, nbody_f4 *acc, float 
     if (!pos) return fail(NBODY_EINVAL, "pos_xyzm is NULL");
     if (!acc) return fail(NBODY_EINVAL, "acc_out is NULL");
     if (!eps2_ok(eps2))
-        return fail(NBODY_EINVAL, "eps2=%g must be a positive, finite, normal float", (double)eps2);
+        return eps2_fail(eps2);
     if (!aligned(pos, 16)) return fail(NBODY_EALIGN, "pos_xyzm is not 16-byte aligned");
     if (!aligned(acc, 16)) return fail(NBODY_EALIGN, "acc_out is not 16-byte aligned");
     if (pot && !aligned(pot, 4)) return fail(NBODY_EALIGN, "pot_out is not 4-byte aligned");
@@ -557,7 +595,8 @@ int enqueue_steps(float4 *pos, float4 *vel, int n, float dt, float eps2, int64_t
         float4 *src = (s % 2 == 0) ? pos : other;
         float4 *dst = (s % 2 == 0) ? other : pos;
         nbk::SmallArgs sa{src, n, eps2, nullptr, nullptr, dst, vel, dt};
-        hipError_t e = nbk::launch_small(p.tpl, false, true, sa, stream);
+        hipError_t e =
+            timed_launch(stream, [&] { return nbk::launch_small(p.tpl, false, true, sa, stream); });
         if (e != hipSuccess) return hip_fail(e, "small kernel launch");
     }
     if (nsteps % 2 == 1) {
@@ -578,7 +617,7 @@ int step_impl(nbody_f4 *pos, nbody_f4 *vel, int64_t N, float dt, float eps2, int
     if (!vel) return fail(NBODY_EINVAL, "vel is NULL");
     if (!std::isfinite(dt)) return fail(NBODY_EINVAL, "dt=%g must be finite", (double)dt);
     if (!eps2_ok(eps2))
-        return fail(NBODY_EINVAL, "eps2=%g must be a positive, finite, normal float", (double)eps2);
+        return eps2_fail(eps2);
     if (!aligned(pos, 16)) return fail(NBODY_EALIGN, "pos is not 16-byte aligned");
     if (!aligned(vel, 16)) return fail(NBODY_EALIGN, "vel is not 16-byte aligned");
     const size_t b16 = (size_t)N * 16;
@@ -622,7 +661,7 @@ int accel_soa_impl(const float *x, const float *y, const float *z, const float *
     }
     if (pot && !aligned(pot, 4)) return fail(NBODY_EALIGN, "pot is not 4-byte aligned");
     if (!eps2_ok(eps2))
-        return fail(NBODY_EINVAL, "eps2=%g must be a positive, finite, normal float", (double)eps2);
+        return eps2_fail(eps2);
     const size_t b4 = (size_t)N * 4;
     const void *all[8] = {ax, ay, az, pot, x, y, z, m};
     const size_t sz[8] = {b4, b4, b4, b4, b4, b4, b4, b4};
@@ -664,7 +703,7 @@ int step_soa_impl(float *x, float *y, float *z, const float *m, float *vx, float
     }
     if (!std::isfinite(dt)) return fail(NBODY_EINVAL, "dt=%g must be finite", (double)dt);
     if (!eps2_ok(eps2))
-        return fail(NBODY_EINVAL, "eps2=%g must be a positive, finite, normal float", (double)eps2);
+        return eps2_fail(eps2);
     const size_t b4 = (size_t)N * 4;
     const size_t sz[7] = {b4, b4, b4, b4, b4, b4, b4};
     if (!disjoint(arr, sz, 7)) return fail(NBODY_EINVAL, "the seven arrays must not overlap");
@@ -706,7 +745,7 @@ int shard_impl(const nbody_f4 *pos, int64_t N, float eps2, int32_t shard, int32_
     if (!pos) return fail(NBODY_EINVAL, "pos_xyzm is NULL");
     if (!partial_out) return fail(NBODY_EINVAL, "partial_out is NULL");
     if (!eps2_ok(eps2))
-        return fail(NBODY_EINVAL, "eps2=%g must be a positive, finite, normal float", (double)eps2);
+        return eps2_fail(eps2);
     if (!aligned(pos, 16) || !aligned(partial_out, 16))
         return fail(NBODY_EALIGN, "pos_xyzm and partial_out must be 16-byte aligned");
     const size_t b16 = (size_t)N * 16;
@@ -732,7 +771,8 @@ int shard_impl(const nbody_f4 *pos, int64_t N, float eps2, int32_t shard, int32_
     nbk::PairsArgs pa{(const float4 *)pos, n, eps2, nb, (float4 *)ws,
                       shard_band(shard, nb, nshards), shard_band(shard + 1, nb, nshards), n, 0,
                       (float4 *)ws, 0};
-    hipError_t e = nbk::launch_pairs(p.band, p.tpl, want_pot != 0, pa, stream);
+    hipError_t e = timed_launch(
+        stream, [&] { return nbk::launch_pairs(p.band, p.tpl, want_pot != 0, pa, stream); });
     if (e != hipSuccess) return hip_fail(e, "accel kernel launch");
     e = nbk::launch_shard_combine(pa.part, n, p.band, nb, pa.band0, pa.band1,
                                   (float4 *)partial_out, stream);
@@ -748,6 +788,7 @@ int nbody_accel(const nbody_f4 *pos_xyzm, int64_t N, float eps2, nbody_f4 *acc_o
                 float *pot_out, hipStream_t stream)
 {
     EnqueueLock lk(g_enqueue);
+    timer_arm();
     return accel_impl(pos_xyzm, N, eps2, acc_out, pot_out, nullptr, stream);
 }
 
@@ -755,6 +796,7 @@ int nbody_accel_plan(const nbody_f4 *pos_xyzm, int64_t N, float eps2, nbody_f4 *
                      float *pot_out, const nbody_plan *plan, hipStream_t stream)
 {
     EnqueueLock lk(g_enqueue);
+    timer_arm();
     return accel_impl(pos_xyzm, N, eps2, acc_out, pot_out, plan, stream);
 }
 
@@ -762,6 +804,7 @@ int nbody_step(nbody_f4 *pos, nbody_f4 *vel, int64_t N, float dt, float eps2, in
                hipStream_t stream)
 {
     EnqueueLock lk(g_enqueue);
+    timer_arm();
     return step_impl(pos, vel, N, dt, eps2, nsteps, nullptr, stream);
 }
 
@@ -769,7 +812,16 @@ int nbody_step_plan(nbody_f4 *pos, nbody_f4 *vel, int64_t N, float dt, float eps
                     int64_t nsteps, const nbody_plan *plan, hipStream_t stream)
 {
     EnqueueLock lk(g_enqueue);
+    timer_arm();
     return step_impl(pos, vel, N, dt, eps2, nsteps, plan, stream);
+}
+
+int nbody_time_kernel(hipEvent_t start, hipEvent_t stop)
+{
+    if ((start == nullptr) != (stop == nullptr))
+        return fail(NBODY_EINVAL, "start and stop must both be events or both be NULL");
+    g_timer = KernelTimer{start, stop, false};
+    return ok();
 }
 
 int nbody_accel_soa(const float *x, const float *y, const float *z, const float *m, int64_t N,
@@ -777,6 +829,7 @@ int nbody_accel_soa(const float *x, const float *y, const float *z, const float 
                     hipStream_t stream)
 {
     EnqueueLock lk(g_enqueue);
+    timer_arm();
     return accel_soa_impl(x, y, z, m, N, eps2, ax, ay, az, pot_out, stream);
 }
 
@@ -784,6 +837,7 @@ int nbody_step_soa(float *x, float *y, float *z, const float *m, float *vx, floa
                    int64_t N, float dt, float eps2, int64_t nsteps, hipStream_t stream)
 {
     EnqueueLock lk(g_enqueue);
+    timer_arm();
     return step_soa_impl(x, y, z, m, vx, vy, vz, N, dt, eps2, nsteps, stream);
 }
 
@@ -792,6 +846,7 @@ int nbody_accel_shard(const nbody_f4 *pos_xyzm, int64_t N, float eps2, int32_t s
                       nbody_f4 *partial_out, hipStream_t stream)
 {
     EnqueueLock lk(g_enqueue);
+    timer_arm();
     return shard_impl(pos_xyzm, N, eps2, shard, nshards, want_pot, plan, partial_out, stream);
 }
 
@@ -838,7 +893,7 @@ int nbody_p2p(const nbody_f4 *pos, int64_t N, float eps2, const int32_t *cell_st
     if (!cell_start || !list_off) return fail(NBODY_EINVAL, "cell_start or list_off is NULL");
     if (nlist > 0 && !cells) return fail(NBODY_EINVAL, "cells is NULL");
     if (!eps2_ok(eps2))
-        return fail(NBODY_EINVAL, "eps2=%g must be a positive, finite, normal float", (double)eps2);
+        return eps2_fail(eps2);
     if (!aligned(pos, 16) || !aligned(acc_out, 16))
         return fail(NBODY_EALIGN, "pos_xyzm and acc_out must be 16-byte aligned");
     if ((pot_out && !aligned(pot_out, 4)) || !aligned(cell_start, 4) || !aligned(list_off, 4) ||
@@ -857,12 +912,14 @@ int nbody_p2p(const nbody_f4 *pos, int64_t N, float eps2, const int32_t *cell_st
     }
     if (pot_out && overlap(acc_out, b16, pot_out, b4))
         return fail(NBODY_EINVAL, "pot_out overlaps acc_out");
+    timer_arm();
     nbk::P2PArgs a{(const float4 *)pos, (int)N, eps2, cell_start, ncell, list_off, cells,
                    (long long)nlist, (float4 *)acc_out, pot_out};
     bool wide = false;
     rc = wide_cells(N, ncell, &wide);
     if (rc != NBODY_OK) return rc;
-    hipError_t e = nbk::launch_p2p(pot_out != nullptr, wide, a, stream);
+    hipError_t e =
+        timed_launch(stream, [&] { return nbk::launch_p2p(pot_out != nullptr, wide, a, stream); });
     if (e != hipSuccess) return hip_fail(e, "p2p kernel launch");
     return ok();
 }
@@ -889,7 +946,7 @@ int nbody_near_grid(const nbody_f4 *pos, int64_t N, float eps2, const float lo[3
     if (!pos) return fail(NBODY_EINVAL, "pos_xyzm is NULL");
     if (!acc_out) return fail(NBODY_EINVAL, "acc_out is NULL");
     if (!eps2_ok(eps2))
-        return fail(NBODY_EINVAL, "eps2=%g must be a positive, finite, normal float", (double)eps2);
+        return eps2_fail(eps2);
     if (!aligned(pos, 16) || !aligned(acc_out, 16))
         return fail(NBODY_EALIGN, "pos_xyzm and acc_out must be 16-byte aligned");
     if (pot_out && !aligned(pot_out, 4)) return fail(NBODY_EALIGN, "pot_out is not 4-byte aligned");
@@ -898,6 +955,7 @@ int nbody_near_grid(const nbody_f4 *pos, int64_t N, float eps2, const float lo[3
     if (pot_out && (overlap(pot_out, b4, pos, b16) || overlap(pot_out, b4, acc_out, b16)))
         return fail(NBODY_EINVAL, "pot_out overlaps another buffer");
     EnqueueLock lk(g_enqueue);
+    timer_arm();
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -905,9 +963,7 @@ int nbody_near_grid(const nbody_f4 *pos, int64_t N, float eps2, const float lo[3
     const int n = (int)N, nc = (int)ncell;
     int end_bit = 1;
     while (end_bit < 32 && ((int64_t)1 << end_bit) < ncell) ++end_bit;
-    size_t sort_bytes = 0;
-    e = nbk::sort_pairs(nullptr, sort_bytes, nullptr, nullptr, nullptr, nullptr, n, end_bit, stream);
-    if (e != hipSuccess) return hip_fail(e, "sort temp-size query");
+    const size_t sort_bytes = nbk::sort_temp_bytes(n);
     // scratch: keys, idx, sorted keys, perm (N x 4 each), sorted pos, acc (N x 16 each),
     // pot (N x 4), cell starts ((ncell + 1) x 4), sort temp
     size_t off[10];
@@ -926,7 +982,7 @@ int nbody_near_grid(const nbody_f4 *pos, int64_t N, float eps2, const float lo[3
     void *temp = b + off[8];
     e = nbk::launch_grid_keys((const float4 *)pos, n, g, keys, idx, stream);
     if (e == hipSuccess)
-        e = nbk::sort_pairs(temp, sort_bytes, keys, skeys, idx, perm, n, end_bit, stream);
+        e = nbk::sort_pairs(temp, keys, skeys, idx, perm, n, end_bit, stream);
     if (e == hipSuccess) e = nbk::launch_gather((const float4 *)pos, perm, n, spos, stream);
     if (e == hipSuccess) e = nbk::launch_cell_starts(skeys, n, nc, start, stream);
     if (e == hipSuccess) {
@@ -935,7 +991,8 @@ int nbody_near_grid(const nbody_f4 *pos, int64_t N, float eps2, const float lo[3
         bool wide = false;
         rc = wide_cells(N, nc, &wide);
         if (rc != NBODY_OK) return rc;
-        e = nbk::launch_p2p_grid(pot_out != nullptr, wide, a, g, stream);
+        e = timed_launch(
+            stream, [&] { return nbk::launch_p2p_grid(pot_out != nullptr, wide, a, g, stream); });
     }
     if (e == hipSuccess)
         e = nbk::launch_scatter(sacc, pot_out ? spot : nullptr, perm, n, (float4 *)acc_out,
@@ -953,7 +1010,7 @@ int nbody_diagnostics(const nbody_f4 *pos, const nbody_f4 *vel, const float *pot
     if (N > 0 && !pos) return fail(NBODY_EINVAL, "pos is NULL");
     if (N > 0 && !vel) return fail(NBODY_EINVAL, "vel is NULL");
     if (!eps2_ok(eps2))
-        return fail(NBODY_EINVAL, "eps2=%g must be a positive, finite, normal float", (double)eps2);
+        return eps2_fail(eps2);
     if (!aligned(out, 8)) return fail(NBODY_EALIGN, "out is not 8-byte aligned");
     if (pos && !aligned(pos, 16)) return fail(NBODY_EALIGN, "pos is not 16-byte aligned");
     if (vel && !aligned(vel, 16)) return fail(NBODY_EALIGN, "vel is not 16-byte aligned");
@@ -963,6 +1020,7 @@ int nbody_diagnostics(const nbody_f4 *pos, const nbody_f4 *vel, const float *pot
                   (pot && overlap(out, bo, pot, b4))))
         return fail(NBODY_EINVAL, "out overlaps an input");
     EnqueueLock lk(g_enqueue);
+    timer_arm();
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");

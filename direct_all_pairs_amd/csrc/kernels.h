@@ -153,11 +153,12 @@ hipError_t launch_cell_starts(const unsigned *sorted_keys, int n, int ncell, int
 // acc[perm[k]] = sacc[k]; pot[perm[k]] = spot[k] (if pot).
 hipError_t launch_scatter(const float4 *sacc, const float *spot, const int *perm, int n,
                           float4 *acc, float *pot, hipStream_t stream);
-// Stable sort of (key, value) pairs on bits [0, end_bit) of the keys (sort.hip).
-// With temp == nullptr only temp_bytes is set.
-hipError_t sort_pairs(void *temp, size_t &temp_bytes, const unsigned *keys_in,
-                      unsigned *keys_out, const int *vals_in, int *vals_out, int n, int end_bit,
-                      hipStream_t stream);
+// Stable sort of (key, value) pairs on bits [0, end_bit) of the keys (keys below
+// 2^end_bit): LSD radix sort, 8 bits per pass. temp holds sort_temp_bytes(n)
+// bytes; the inputs are read only.
+size_t sort_temp_bytes(int n);
+hipError_t sort_pairs(void *temp, const unsigned *keys_in, unsigned *keys_out, const int *vals_in,
+                      int *vals_out, int n, int end_bit, hipStream_t stream);
 
 // Layout conversion for the SoA entry points: out[i] = (a[i], b[i], c[i], d ? d[i] : 0),
 // and back: a[i], b[i], c[i] = in[i].x, .y, .z.

@@ -1537,6 +1537,142 @@ __global__ void __launch_bounds__(256) scatter_kernel(const float4 *__restrict__
     if (pot) pot[i] = spot[k];
 }
 
+// ---------------------------------------------------------------- binning sort
+// Stable LSD radix sort of the (cell key, body index) pairs of nbody_near_grid,
+// 8 key bits per pass, three kernels per pass:
+//   hist    - workgroup b counts the digits of its contiguous key range
+//             [b per, (b + 1) per) into counts[digit][b] (LDS counters: the
+//             counts do not depend on the order of the additions);
+//   scan    - one workgroup turns counts into exclusive offsets in digit-major
+//             order (digit, then workgroup), so equal digits keep the order of
+//             the workgroups, i.e. of the input;
+//   scatter - workgroup b walks its range 256 keys at a time in input order; a
+//             key's place is its digit's running offset plus the number of keys
+//             with the same digit before it in the sub-tile (earlier waves'
+//             counts, then the lanes below it in its own wave, found from the
+//             eight digit-bit ballots).
+// Every step is integer and in a fixed order: the result is the stable sort,
+// the same bits every time, so a cell keeps its bodies in input order.
+constexpr int kSortBits = 8;
+constexpr int kSortDigits = 1 << kSortBits;  // 256: one counter per thread
+constexpr int kSortMaxBlocks = 2048;         // counts <= 2^19 entries: one-workgroup scan
+constexpr int kSortScanThreads = 1024;
+
+struct SortShape {
+    int nblocks;  // workgroups per pass
+    int per;      // keys per workgroup (a multiple of 256; the last range may be shorter)
+};
+
+SortShape sort_shape(int n)
+{
+    int nb = (n + 4095) / 4096;
+    if (nb > kSortMaxBlocks) nb = kSortMaxBlocks;
+    if (nb < 1) nb = 1;
+    long long per = ((long long)n + nb - 1) / nb;
+    per = (per + 255) / 256 * 256;
+    nb = (int)(((long long)n + per - 1) / per);
+    return {nb < 1 ? 1 : nb, (int)per};
+}
+
+__device__ __forceinline__ void sort_range(int n, int per, int &b0, int &e)
+{
+    const long long a = (long long)blockIdx.x * per;
+    const long long z = a + per;
+    b0 = (int)a;
+    e = (int)(z < n ? z : n);
+}
+
+__global__ void __launch_bounds__(256) sort_hist_kernel(const unsigned *__restrict__ keys, int n,
+                                                        int per, int shift, int nblocks,
+                                                        int *__restrict__ counts)
+{
+    __shared__ int h[kSortDigits];
+    h[threadIdx.x] = 0;
+    __syncthreads();
+    int b0, e;
+    sort_range(n, per, b0, e);
+    for (int i = b0 + (int)threadIdx.x; i < e; i += 256)
+        atomicAdd(&h[(keys[i] >> shift) & (kSortDigits - 1)], 1);
+    __syncthreads();
+    counts[threadIdx.x * nblocks + blockIdx.x] = h[threadIdx.x];
+}
+
+// Exclusive prefix sum of counts[0 .. total) in place: each thread a contiguous run, the
+// run sums scanned across the workgroup, then each run rewritten from its offset.
+__global__ void __launch_bounds__(kSortScanThreads) sort_scan_kernel(int *__restrict__ counts,
+                                                                     int total)
+{
+    __shared__ int part[kSortScanThreads];
+    const int t = threadIdx.x;
+    const int chunk = (total + kSortScanThreads - 1) / kSortScanThreads;
+    const long long a0 = (long long)t * chunk;
+    const int a = (int)(a0 < total ? a0 : total);
+    const int b = a + chunk < total ? a + chunk : total;
+    int sum = 0;
+    for (int i = a; i < b; ++i) sum += counts[i];
+    part[t] = sum;
+    __syncthreads();
+    for (int off = 1; off < kSortScanThreads; off <<= 1) {  // inclusive Hillis-Steele scan
+        const int v = t >= off ? part[t - off] : 0;
+        __syncthreads();
+        part[t] += v;
+        __syncthreads();
+    }
+    int run = part[t] - sum;
+    for (int i = a; i < b; ++i) {
+        const int c = counts[i];
+        counts[i] = run;
+        run += c;
+    }
+}
+
+__global__ void __launch_bounds__(256) sort_scatter_kernel(const unsigned *__restrict__ kin,
+                                                           const int *__restrict__ vin, int n,
+                                                           int per, int shift, int nblocks,
+                                                           const int *__restrict__ offsets,
+                                                           unsigned *__restrict__ kout,
+                                                           int *__restrict__ vout)
+{
+    __shared__ int base[kSortDigits];     // running output position of each digit
+    __shared__ int wcnt[4][kSortDigits];  // per wave: keys of each digit in the sub-tile
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    base[tid] = offsets[tid * nblocks + blockIdx.x];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) wcnt[q][tid] = 0;
+    __syncthreads();
+    int b0, e;
+    sort_range(n, per, b0, e);
+    for (int s0 = b0; s0 < e; s0 += 256) {
+        const int i = s0 + tid;
+        const bool valid = i < e;
+        const unsigned k = valid ? kin[i] : 0u;
+        const int v = valid ? vin[i] : 0;
+        const unsigned d = (k >> shift) & (kSortDigits - 1);
+        // the valid lanes of this wave whose key has digit d
+        unsigned long long same = __ballot(valid);
+#pragma unroll
+        for (int bit = 0; bit < kSortBits; ++bit) {
+            const bool set = (d >> bit) & 1u;
+            const unsigned long long on = __ballot(set);
+            same &= set ? on : ~on;
+        }
+        const unsigned long long below = same & ((1ull << lane) - 1ull);
+        if (valid && below == 0) wcnt[w][d] = __popcll(same);  // the digit's first lane
+        __syncthreads();
+        if (valid) {
+            int at = base[d] + __popcll(below);
+            for (int q = 0; q < w; ++q) at += wcnt[q][d];
+            kout[at] = k;
+            vout[at] = v;
+        }
+        __syncthreads();
+        base[tid] += wcnt[0][tid] + wcnt[1][tid] + wcnt[2][tid] + wcnt[3][tid];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) wcnt[q][tid] = 0;
+        __syncthreads();
+    }
+}
+
 // ---------------------------------------------------------------- SoA layout
 // Separate x, y, z, m arrays (the host layout of the lecture's CPU program,
 // Degawa slide 15) in and out of the 16-byte records the kernels read.
@@ -1769,6 +1905,52 @@ hipError_t launch_scatter(const float4 *sacc, const float *spot, const int *perm
     void *k[] = {&sacc, &spot, &perm, &n, &acc, &pot};
     return hipLaunchKernel((const void *)&scatter_kernel, dim3((unsigned)((n + 255) / 256)),
                            dim3(256), k, 0, stream);
+}
+
+size_t sort_temp_bytes(int n)
+{
+    const SortShape sh = sort_shape(n < 1 ? 1 : n);
+    const size_t keys = ((size_t)(n < 1 ? 1 : n) * 4 + 255) / 256 * 256;
+    return 2 * keys + (size_t)kSortDigits * (size_t)sh.nblocks * sizeof(int);
+}
+
+hipError_t sort_pairs(void *temp, const unsigned *keys_in, unsigned *keys_out, const int *vals_in,
+                      int *vals_out, int n, int end_bit, hipStream_t stream)
+{
+    if (n < 1 || end_bit < 1 || end_bit > 32 || !temp) return hipErrorInvalidValue;
+    const SortShape sh = sort_shape(n);
+    const size_t keys = ((size_t)n * 4 + 255) / 256 * 256;
+    unsigned *k_alt = (unsigned *)temp;
+    int *v_alt = (int *)((char *)temp + keys);
+    int *counts = (int *)((char *)temp + 2 * keys);
+    int total = kSortDigits * sh.nblocks;
+    const int passes = (end_bit + kSortBits - 1) / kSortBits;
+    const unsigned *ks = keys_in;
+    const int *vs = vals_in;
+    int nn = n, per = sh.per, nbl = sh.nblocks;
+    for (int p = 0; p < passes; ++p) {
+        // the last pass writes the outputs; before it, the two buffers alternate so that
+        // no pass reads the array it writes
+        const bool to_out = (passes - 1 - p) % 2 == 0;
+        unsigned *kd = to_out ? keys_out : k_alt;
+        int *vd = to_out ? vals_out : v_alt;
+        int shift = p * kSortBits;
+        void *a1[] = {&ks, &nn, &per, &shift, &nbl, &counts};
+        hipError_t e = hipLaunchKernel((const void *)&sort_hist_kernel, dim3(nbl), dim3(256), a1,
+                                       0, stream);
+        if (e != hipSuccess) return e;
+        void *a2[] = {&counts, &total};
+        e = hipLaunchKernel((const void *)&sort_scan_kernel, dim3(1), dim3(kSortScanThreads), a2,
+                            0, stream);
+        if (e != hipSuccess) return e;
+        void *a3[] = {&ks, &vs, &nn, &per, &shift, &nbl, &counts, &kd, &vd};
+        e = hipLaunchKernel((const void *)&sort_scatter_kernel, dim3(nbl), dim3(256), a3, 0,
+                            stream);
+        if (e != hipSuccess) return e;
+        ks = kd;
+        vs = vd;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_pack(const float *a, const float *b, const float *c, const float *d, int n,

@@ -132,7 +132,9 @@ typedef struct nbody_plan {
  * nbody_accel - accelerations, and optionally potentials, of all N bodies.
  *   pos_xyzm : N bodies (x, y, z, m), read only.
  *   N        : body count, 0 <= N <= 2^30 (every entry point). N = 0 enqueues nothing.
- *   eps2     : softening squared; must be a positive, finite, normal float.
+ *   eps2     : softening squared; a finite float >= 2^-84 (about 5.2e-26), so that
+ *              eps2^(-3/2), the 1/r^3 of the self pair, is finite in fp32 (every
+ *              entry point takes eps2 under this rule; NBODY_EINVAL otherwise).
  *   acc_out  : N records written as (ax, ay, az, 0). Must not overlap pos_xyzm.
  *   pot_out  : N floats p_i, or NULL to skip the potential. Must not overlap
  *              the other buffers.
@@ -307,6 +309,20 @@ int nbody_diagnostics(const nbody_f4 *pos, const nbody_f4 *vel, const float *pot
  * *out. Queries the device's compute-unit count once per device.
  */
 int nbody_plan_for(int64_t N, int want_pot, nbody_plan *out);
+
+/*
+ * nbody_time_kernel - measurement hook (not part of the pages' method). With
+ * start and stop both non-NULL, every later call on the calling host thread
+ * records `start` on its stream immediately before its first launch of a
+ * pair-term kernel (the kernel that evaluates the interactions: the pair,
+ * tile or small-N kernel, or the near-field kernel) and `stop` immediately
+ * after that launch, so hipEventElapsedTime(start, stop) is that one kernel's
+ * duration on the stream. Further launches of the same call (later passes or
+ * steps) are not bracketed. NULL, NULL switches the hook off. The events are
+ * created and owned by the caller (on the device the calls run on); the
+ * library only records them. NBODY_EINVAL if exactly one of them is NULL.
+ */
+int nbody_time_kernel(hipEvent_t start, hipEvent_t stop);
 
 /* Message describing the last non-OK return on the calling thread ("" if none). */
 const char *nbody_last_error(void);

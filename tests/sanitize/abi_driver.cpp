@@ -50,6 +50,8 @@ int main()
     expect("step dt inf", nbody_step(A, B, 16, INFINITY, 1e-4f, 1, nullptr), NBODY_EINVAL);
     expect("step overlap", nbody_step(A, A, 16, 1e-3f, 1e-4f, 1, nullptr), NBODY_EINVAL);
     expect("step plan", nbody_step_plan(A, B, 16, 1e-3f, 1e-4f, 1, &bad, nullptr), NBODY_EINVAL);
+    expect("time_kernel one event", nbody_time_kernel((hipEvent_t)A, nullptr), NBODY_EINVAL);
+    expect("time_kernel off", nbody_time_kernel(nullptr, nullptr), NBODY_OK);
 
     float *f = (float *)A;
     expect("soa x NULL", nbody_accel_soa(nullptr, f, f, f, 16, 1e-4f, C, C + 64, C + 128, nullptr,

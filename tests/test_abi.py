@@ -79,7 +79,10 @@ def test_n_zero_is_a_no_op(nb):
     (dict(n=-1), 1), (dict(n=2**31), 1), (dict(n=2**30 + 1), 1), (dict(pos=None), 1),
     (dict(acc=None), 1),
     (dict(eps2=0.0), 1), (dict(eps2=-1e-4), 1), (dict(eps2=math.nan), 1),
-    (dict(eps2=math.inf), 1), (dict(eps2=1e-40), 1),
+    (dict(eps2=math.inf), 1), (dict(eps2=1e-40), 1), (dict(eps2=1e-30), 1),
+    # the lower bound 2^-84: the float just below it is rejected; 2^-84 itself passes the
+    # eps2 check and the call fails at the next one (a misaligned pointer), before any HIP call
+    (dict(eps2=2.0 ** -84 * (1 - 2.0 ** -24)), 1), (dict(eps2=2.0 ** -84, pos=A + 4), 2),
     (dict(pos=A + 4), 2), (dict(acc=B + 8), 2), (dict(pot=B + 2), 2),
     (dict(acc=A + 16), 1), (dict(pot=A + 64), 1), (dict(pot=B + 16), 1),
 ])
@@ -97,6 +100,13 @@ def test_accel_rejects(nb, kw, code):
 ])
 def test_step_rejects(nb, args, code):
     assert nb.nbody_step(*args, stream=0, check=False) == code
+
+
+def test_time_kernel_takes_both_events_or_none(nb):
+    assert nb.nbody_time_kernel(A, None, check=False) == nb.NBODY_EINVAL
+    assert nb.nbody_time_kernel(None, B, check=False) == nb.NBODY_EINVAL
+    assert "both" in nb.nbody_last_error()
+    assert nb.nbody_time_kernel(None, None, check=False) == nb.NBODY_OK
 
 
 C = 1 << 29

@@ -38,3 +38,48 @@ def test_shard_interactions_add_up_to_n_squared(n, band, nshards):
     parts = [bench.shard_interactions(n, band, s, nshards) for s in range(nshards)]
     assert sum(parts) == n * n
     assert min(parts) > 0
+
+
+@pytest.mark.parametrize("n,band,passes", [(1, 512, 1), (1 << 20, 2048, 1), (1 << 20, 2048, 3),
+                                           (3000, 512, 1), (20011, 256, 1), (5000, 1024, 2)])
+def test_pair_item_terms_cover_every_ordered_pair_once(n, band, passes):
+    """Summed over the band ranges of all passes, the pair kernel's items hold every unordered
+    pair of distinct-band bodies once and every same-band ordered pair once: one-sided terms
+    plus twice the pairs is N^2, and the one-sided terms are the squared band sizes."""
+    nb = (n + band - 1) // band
+    edges = [q * nb // passes for q in range(passes + 1)]
+    parts = [bench.pair_item_terms(n, band, a, b) for a, b in zip(edges, edges[1:])]
+    diag = sum(p[0] for p in parts)
+    off = sum(p[1] for p in parts)
+    assert diag + 2 * off == n * n
+    sizes = [min(band, n - b * band) for b in range(nb)]
+    assert diag == sum(s * s for s in sizes)
+    # the same split by shards (nbody_accel_shard's band ranges) counts the same
+    assert sum(bench.shard_interactions(n, band, q, passes) for q in range(passes)) == n * n
+
+
+def test_first_launch_flops_match_the_formulation():
+    """The pair kernel's FP32 flops per launch: 30 per unordered pair and 21 per one-sided
+    term with the potential (26 and 19 without); one-sided kernels 21 (19) per term."""
+
+    class Plan:
+        mode, band, passes, tpl, bcast = 2, 2048, 1, 8, 1
+
+    n = 1 << 20
+    w = bench.first_launch_work(n, Plan, True)
+    assert w["interactions"] == n * n
+    assert w["units"] == {"one_sided_terms": n * 2048, "pairs": (n * n - n * 2048) // 2}
+    assert w["flops"] == 21 * n * 2048 + 30 * (n * n - n * 2048) // 2
+    assert bench.first_launch_work(n, Plan, False)["flops"] == (19 * n * 2048
+                                                                + 26 * (n * n - n * 2048) // 2)
+    Plan.mode = 3
+    assert bench.first_launch_work(4096, Plan, True)["flops"] == 21 * 4096 * 4096
+
+
+def test_cpu_sample_is_the_protocol_set():
+    idx, _ = bench.cpu_sample_targets(1 << 20)
+    n = 1 << 20
+    assert len(idx) == 65536 + 2048 and len(set(idx.tolist())) == len(idx)
+    assert list(idx[:1024]) == list(range(1024)) and list(idx[-1024:]) == list(range(n - 1024, n))
+    idx2, _ = bench.cpu_sample_targets(65536)
+    assert list(idx2) == list(range(65536))

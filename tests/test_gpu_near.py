@@ -137,7 +137,11 @@ def gpu_near_grid(nb, pos, eps2, lo, h, dims, pot=True):
 @pytest.mark.parametrize("n,dims,h", [(1, (1, 1, 1), 4.0), (500, (2, 2, 2), 1.0),
                                       (3000, (5, 5, 5), 0.4), (20000, (8, 8, 8), 0.25),
                                       (20000, (13, 3, 7), 0.2), (3000, (1, 6, 5), 0.4),
-                                      (3000, (7, 1, 1), 0.3), (3000, (2, 9, 1), 0.25)])
+                                      (3000, (7, 1, 1), 0.3), (3000, (2, 9, 1), 0.25),
+                                      # 256 cells: one sort pass over all 8 digit bits;
+                                      # 64^3 cells: keys of 18 bits, three sort passes
+                                      (20000, (16, 16, 1), 0.125),
+                                      (200000, (64, 64, 64), 2.0 / 64)])
 def test_near_grid_uniform(nb, n, dims, h):
     """Uniform cube [-1, 1]^3 on grids of several shapes (bodies beyond the last cell join
     the boundary cells; one- and two-cell x extents, where a neighbourhood run holds one or

@@ -352,21 +352,35 @@ def test_pair_passes_four_million_ragged_sampled(nb):
 
 def test_pairs_plan_beyond_grid_limit_rejected(nb):
     """A pair plan whose band count exceeds the launch grid is rejected before anything is
-    allocated or launched (fake, aligned pointers: nothing is dereferenced)."""
+    allocated or launched. The buffers are real allocations of the full size (1 GiB each,
+    left uninitialised), so that even a regressed check could not hand a kernel an address
+    outside them; the slot scratch such a plan asks for (10^17 bytes) could not be allocated
+    either."""
+    import torch
+
     n = 512 * 131072 + 1
-    rc = nb.nbody_accel_plan(1 << 20, n, 1e-4, 1 << 40, None, plan=dict(mode="pairs", band=512),
-                             stream=0, check=False)
+    pos = torch.empty((n, 4), dtype=torch.float32, device="cuda:0")
+    acc = torch.empty_like(pos)
+    rc = nb.nbody_accel_plan(pos, n, 1e-4, acc, None, plan=dict(mode="pairs", band=512),
+                             check=False)
     assert rc == nb.NBODY_EINVAL and "grid" in nb.nbody_last_error()
+    del pos, acc
 
 
 def test_scratch_allocation_failure_reported_and_recovered(nb):
-    """A layout whose scratch cannot be allocated (4096 split chunks of 2^30 bodies: 70 TB)
-    fails with NBODY_ENOMEM before any launch (fake, aligned pointers: nothing is
-    dereferenced), and the library keeps working: the next evaluation is within the bound."""
-    n = 1 << 30
-    rc = nb.nbody_accel_plan(1 << 20, n, 1e-4, 1 << 46, None,
-                             plan=dict(bcast="lds", tpl=1, wg=256, splits=4096), stream=0,
-                             check=False)
+    """A layout whose scratch cannot be allocated (4096 split chunks of 2^24 bodies: 1.1 TB,
+    several times the device's memory) fails with NBODY_ENOMEM before any launch, and the
+    library keeps working: the next evaluation is within the bound. The bodies and outputs
+    are real allocations of the full size (256 MiB each, zero masses), so no launch could
+    touch memory outside them."""
+    import torch
+
+    n = 1 << 24
+    pos = torch.zeros((n, 4), dtype=torch.float32, device="cuda:0")
+    acc = torch.empty_like(pos)
+    rc = nb.nbody_accel_plan(pos, n, 1e-4, acc, None,
+                             plan=dict(bcast="lds", tpl=1, wg=256, splits=4096), check=False)
+    del pos, acc
     assert rc == nb.NBODY_ENOMEM and "hipMalloc" in nb.nbody_last_error()
     pos, _ = _bodies(3000, 44)
     acc, pot = gpu_accel(pos, 1e-4)
