@@ -62,6 +62,7 @@ _lib.nbody_accel_plan.argtypes = [_vp, _i64, _f32, _vp, _vp, ctypes.POINTER(nbod
 _lib.nbody_step.argtypes = [_vp, _vp, _i64, _f32, _f32, _i64, _vp]
 _lib.nbody_step_plan.argtypes = [_vp, _vp, _i64, _f32, _f32, _i64, ctypes.POINTER(nbody_plan),
                                  _vp]
+_lib.nbody_step_noalloc.argtypes = [_vp, _vp, _i64, _f32, _f32, _i64, _vp]
 _lib.nbody_time_kernel.argtypes = [_vp, _vp]
 _lib.nbody_plan_for.argtypes = [_i64, _int, ctypes.POINTER(nbody_plan)]
 _lib.nbody_diagnostics.argtypes = [_vp, _vp, _vp, _i64, _f32, _vp, _vp]
@@ -77,13 +78,13 @@ _lib.nbody_last_error.restype = ctypes.c_char_p
 _lib.nbody_release_workspace.argtypes = []
 _lib.nbody_version.restype = ctypes.c_char_p
 for _f in ("nbody_accel", "nbody_accel_plan", "nbody_step", "nbody_step_plan",
-           "nbody_time_kernel", "nbody_accel_soa", "nbody_step_soa", "nbody_accel_shard", "nbody_shard_finish",
+           "nbody_step_noalloc", "nbody_time_kernel", "nbody_accel_soa", "nbody_step_soa", "nbody_accel_shard", "nbody_shard_finish",
            "nbody_p2p", "nbody_near_grid", "nbody_diagnostics", "nbody_plan_for",
            "nbody_release_workspace"):
     getattr(_lib, _f).restype = _int
 
 EXPORTS = ("nbody_accel", "nbody_accel_plan", "nbody_step", "nbody_step_plan",
-           "nbody_time_kernel", "nbody_accel_soa", "nbody_step_soa",
+           "nbody_step_noalloc", "nbody_time_kernel", "nbody_accel_soa", "nbody_step_soa",
            "nbody_accel_shard", "nbody_shard_finish", "nbody_p2p", "nbody_near_grid",
            "nbody_diagnostics", "nbody_plan_for", "nbody_last_error", "nbody_release_workspace",
            "nbody_version")
@@ -160,6 +161,13 @@ def nbody_step_plan(pos, vel, N: int, dt: float, eps2: float, nsteps: int, plan=
     rc = _lib.nbody_step_plan(_ptr(pos), _ptr(vel), int(N), float(dt), float(eps2), int(nsteps),
                               ctypes.byref(p) if p is not None else None, _stream(stream))
     return _check(rc, "nbody_step_plan") if check else rc
+
+
+def nbody_step_noalloc(pos, vel, N: int, dt: float, eps2: float, nsteps: int, stream=None,
+                       check: bool = True) -> int:
+    rc = _lib.nbody_step_noalloc(_ptr(pos), _ptr(vel), int(N), float(dt), float(eps2),
+                                 int(nsteps), _stream(stream))
+    return _check(rc, "nbody_step_noalloc") if check else rc
 
 
 def _event(ev):

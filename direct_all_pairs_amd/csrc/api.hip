@@ -112,11 +112,62 @@ std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
 std::mutex g_enqueue;
 using EnqueueLock = std::lock_guard<std::mutex>;
 
+// ------------------------------------------------------------ static scratch
+// nbody_step_noalloc takes its scratch from this array instead of hipMalloc:
+// every GPU the library runs on holds its own copy (in the library's code
+// object) until the process ends, and every such call on that GPU shares it.
+// In host code `scratch` names only a host-side stand-in: the kernels get the
+// device address that hipGetSymbolAddress returns for the current device.
+constexpr size_t kStaticScratchBytes = size_t(1) << 27;  // 128 MiB
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+std::map<int, void *> g_static_scratch;  // device -> its copy of `scratch` (under g_mu)
+
+// The device address of `scratch` on device dev, which must be current; looked
+// up once per device.
+int static_scratch(int dev, void **out)
+{
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_static_scratch.find(dev);
+    if (it != g_static_scratch.end()) {
+        *out = it->second;
+        return NBODY_OK;
+    }
+    void *p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr || !aligned(p, 256))
+        return fail(NBODY_EHIP, "hipGetSymbolAddress(scratch) returned %p", p);
+    g_static_scratch[dev] = p;
+    *out = p;
+    return NBODY_OK;
+}
+
+// While set (by nbody_step_noalloc, for the length of its enqueueing), scratch_get
+// hands out this block instead of the cached one and never allocates.
+struct FixedScratch {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+thread_local FixedScratch g_fixed;
+
+struct FixedScratchScope {
+    FixedScratchScope(void *p, size_t b) { g_fixed = FixedScratch{p, b}; }
+    ~FixedScratchScope() { g_fixed = FixedScratch{}; }
+};
+
 // Returns scratch of at least `bytes` for (device, stream). Growing frees the
 // old block first; hipFree waits for the device, so work still queued on the
 // old block finishes before it is released.
 int scratch_get(int dev, hipStream_t stream, size_t bytes, void **out)
 {
+    if (g_fixed.ptr) {
+        if (bytes > g_fixed.bytes)
+            return fail(NBODY_EINVAL, "internal: %zu bytes of scratch exceed the static %zu",
+                        bytes, g_fixed.bytes);
+        *out = g_fixed.ptr;
+        return NBODY_OK;
+    }
     std::lock_guard<std::mutex> lk(g_mu);
     Scratch &s = g_scratch[{dev, stream}];
     if (s.bytes < bytes) {
@@ -606,8 +657,10 @@ int enqueue_steps(float4 *pos, float4 *vel, int n, float dt, float eps2, int64_t
     return NBODY_OK;
 }
 
+// noalloc: take the scratch from the static array (nbody_step_noalloc) and
+// reject plans that need more than it holds; nothing is allocated.
 int step_impl(nbody_f4 *pos, nbody_f4 *vel, int64_t N, float dt, float eps2, int64_t nsteps,
-              const nbody_plan *plan, hipStream_t stream)
+              const nbody_plan *plan, hipStream_t stream, bool noalloc = false)
 {
     int rc = check_n(N);
     if (rc != NBODY_OK) return rc;
@@ -626,6 +679,19 @@ int step_impl(nbody_f4 *pos, nbody_f4 *vel, int64_t N, float dt, float eps2, int
     int dev = 0;
     rc = make_plan(N, plan, &dev, &p);
     if (rc != NBODY_OK) return rc;
+    if (!noalloc) {
+        rc = enqueue_steps((float4 *)pos, (float4 *)vel, (int)N, dt, eps2, nsteps, p, dev, stream);
+        return rc == NBODY_OK ? ok() : rc;
+    }
+    const size_t need = eval_scratch(N, p, true);
+    if (need > kStaticScratchBytes)
+        return fail(NBODY_EINVAL, "N=%lld: its step plan needs %zu bytes of scratch, more than the "
+                                  "%zu of nbody_step_noalloc's static array (use nbody_step)",
+                    (long long)N, need, kStaticScratchBytes);
+    void *fixed = nullptr;
+    rc = static_scratch(dev, &fixed);
+    if (rc != NBODY_OK) return rc;
+    FixedScratchScope scope(fixed, kStaticScratchBytes);
     rc = enqueue_steps((float4 *)pos, (float4 *)vel, (int)N, dt, eps2, nsteps, p, dev, stream);
     return rc == NBODY_OK ? ok() : rc;
 }
@@ -814,6 +880,14 @@ int nbody_step_plan(nbody_f4 *pos, nbody_f4 *vel, int64_t N, float dt, float eps
     EnqueueLock lk(g_enqueue);
     timer_arm();
     return step_impl(pos, vel, N, dt, eps2, nsteps, plan, stream);
+}
+
+int nbody_step_noalloc(nbody_f4 *pos, nbody_f4 *vel, int64_t N, float dt, float eps2,
+                       int64_t nsteps, hipStream_t stream)
+{
+    EnqueueLock lk(g_enqueue);
+    timer_arm();
+    return step_impl(pos, vel, N, dt, eps2, nsteps, nullptr, stream, true);
 }
 
 int nbody_time_kernel(hipEvent_t start, hipEvent_t stop)

@@ -173,6 +173,26 @@ int nbody_step_plan(nbody_f4 *pos, nbody_f4 *vel, int64_t N, float dt, float eps
                     int64_t nsteps, const nbody_plan *plan, hipStream_t stream);
 
 /*
+ * nbody_step_noalloc - nbody_step for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving or simulation loops,
+ * harnesses that forbid hipMalloc. Same arguments, plan, kernels and bits as
+ * nbody_step, but no hipMalloc, hipFree or allocating library routine is
+ * called: the scratch (the second position buffer of small-N steps, the pair
+ * or split-j partial sums of larger N) comes from a static 128 MiB array
+ * that each GPU holds, inside the library's code object, until the process
+ * ends (looked up on a device's first call).
+ *   Limit: the step plan's scratch must fit 128 MiB; for uniform bodies that
+ *   is N <= 65536 (NBODY_EINVAL, with the bytes it would need, beyond it).
+ *   The array keeps the last call's contents; nothing in it needs to start at
+ *   zero (every entry is written before it is read within a step). All calls
+ *   on one GPU share it: calls that overlap in time on that GPU (on different
+ *   streams or from different host threads) race; calls on one stream are
+ *   ordered by the stream.
+ */
+int nbody_step_noalloc(nbody_f4 *pos, nbody_f4 *vel, int64_t N, float dt, float eps2,
+                       int64_t nsteps, hipStream_t stream);
+
+/*
  * nbody_accel_soa - nbody_accel for bodies held as separate arrays (the host
  * layout of the lecture's CPU program): x, y, z, m in; ax, ay, az and, if
  * pot_out is not NULL, the potentials out. All arrays hold N floats (4-byte

@@ -50,6 +50,12 @@ int main()
     expect("step dt inf", nbody_step(A, B, 16, INFINITY, 1e-4f, 1, nullptr), NBODY_EINVAL);
     expect("step overlap", nbody_step(A, A, 16, 1e-3f, 1e-4f, 1, nullptr), NBODY_EINVAL);
     expect("step plan", nbody_step_plan(A, B, 16, 1e-3f, 1e-4f, 1, &bad, nullptr), NBODY_EINVAL);
+    expect("step noalloc overlap", nbody_step_noalloc(A, A, 16, 1e-3f, 1e-4f, 1, nullptr),
+           NBODY_EINVAL);
+    expect("step noalloc eps2", nbody_step_noalloc(A, B, 16, 1e-3f, 0x1p-85f, 1, nullptr),
+           NBODY_EINVAL);
+    expect("step noalloc nsteps 0", nbody_step_noalloc(A, B, 16, 1e-3f, 1e-4f, 0, nullptr),
+           NBODY_OK);
     expect("time_kernel one event", nbody_time_kernel((hipEvent_t)A, nullptr), NBODY_EINVAL);
     expect("time_kernel off", nbody_time_kernel(nullptr, nullptr), NBODY_OK);
 

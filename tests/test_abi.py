@@ -100,6 +100,13 @@ def test_accel_rejects(nb, kw, code):
 ])
 def test_step_rejects(nb, args, code):
     assert nb.nbody_step(*args, stream=0, check=False) == code
+    # the static-scratch variant runs the same checks first
+    assert nb.nbody_step_noalloc(*args, stream=0, check=False) == code
+
+
+def test_noalloc_trivial_calls_are_no_ops(nb):
+    assert nb.nbody_step_noalloc(None, None, 0, 1e-3, 1e-4, 5, stream=0, check=False) == 0
+    assert nb.nbody_step_noalloc(A, B, 10, 1e-3, 1e-4, 0, stream=0, check=False) == 0
 
 
 def test_time_kernel_takes_both_events_or_none(nb):
