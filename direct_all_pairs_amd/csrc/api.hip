@@ -988,7 +988,7 @@ int nbody_p2p(const nbody_f4 *pos, int64_t N, float eps2, const int32_t *cell_st
         return fail(NBODY_EINVAL, "pot_out overlaps acc_out");
     timer_arm();
     nbk::P2PArgs a{(const float4 *)pos, (int)N, eps2, cell_start, ncell, list_off, cells,
-                   (long long)nlist, (float4 *)acc_out, pot_out};
+                   (long long)nlist, (float4 *)acc_out, pot_out, nullptr};
     bool wide = false;
     rc = wide_cells(N, ncell, &wide);
     if (rc != NBODY_OK) return rc;
@@ -1038,39 +1038,36 @@ int nbody_near_grid(const nbody_f4 *pos, int64_t N, float eps2, const float lo[3
     int end_bit = 1;
     while (end_bit < 32 && ((int64_t)1 << end_bit) < ncell) ++end_bit;
     const size_t sort_bytes = nbk::sort_temp_bytes(n);
-    // scratch: keys, idx, sorted keys, perm (N x 4 each), sorted pos, acc (N x 16 each),
-    // pot (N x 4), cell starts ((ncell + 1) x 4), sort temp
-    size_t off[10];
-    const size_t sz[9] = {b4, b4, b4, b4, b16, b16, b4, ((size_t)nc + 1) * 4, sort_bytes};
+    // scratch: keys, idx, sorted keys, perm (N x 4 each), sorted pos (N x 16), cell starts
+    // ((ncell + 1) x 4), sort temp. The near-field kernel writes each body's results
+    // straight to its place in the caller's order (perm).
+    size_t off[8];
+    const size_t sz[7] = {b4, b4, b4, b4, b16, ((size_t)nc + 1) * 4, sort_bytes};
     off[0] = 0;
-    for (int i = 0; i < 9; ++i) off[i + 1] = align256(off[i] + sz[i]);
+    for (int i = 0; i < 7; ++i) off[i + 1] = align256(off[i] + sz[i]);
     void *ws = nullptr;
-    rc = scratch_get(dev, stream, off[9], &ws);
+    rc = scratch_get(dev, stream, off[7], &ws);
     if (rc != NBODY_OK) return rc;
     char *b = (char *)ws;
     unsigned *keys = (unsigned *)(b + off[0]), *skeys = (unsigned *)(b + off[2]);
     int *idx = (int *)(b + off[1]), *perm = (int *)(b + off[3]);
-    float4 *spos = (float4 *)(b + off[4]), *sacc = (float4 *)(b + off[5]);
-    float *spot = (float *)(b + off[6]);
-    int *start = (int *)(b + off[7]);
-    void *temp = b + off[8];
+    float4 *spos = (float4 *)(b + off[4]);
+    int *start = (int *)(b + off[5]);
+    void *temp = b + off[6];
     e = nbk::launch_grid_keys((const float4 *)pos, n, g, keys, idx, stream);
     if (e == hipSuccess)
         e = nbk::sort_pairs(temp, keys, skeys, idx, perm, n, end_bit, stream);
     if (e == hipSuccess) e = nbk::launch_gather((const float4 *)pos, perm, n, spos, stream);
     if (e == hipSuccess) e = nbk::launch_cell_starts(skeys, n, nc, start, stream);
     if (e == hipSuccess) {
-        nbk::P2PArgs a{spos, n, eps2, start, nc, nullptr, nullptr, 0, sacc,
-                       pot_out ? spot : nullptr};
+        nbk::P2PArgs a{spos, n, eps2, start, nc, nullptr, nullptr, 0, (float4 *)acc_out, pot_out,
+                       perm};
         bool wide = false;
         rc = wide_cells(N, nc, &wide);
         if (rc != NBODY_OK) return rc;
         e = timed_launch(
             stream, [&] { return nbk::launch_p2p_grid(pot_out != nullptr, wide, a, g, stream); });
     }
-    if (e == hipSuccess)
-        e = nbk::launch_scatter(sacc, pot_out ? spot : nullptr, perm, n, (float4 *)acc_out,
-                                pot_out, stream);
     if (e != hipSuccess) return hip_fail(e, "near-grid launch");
     return ok();
 }

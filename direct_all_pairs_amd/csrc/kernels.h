@@ -109,8 +109,9 @@ hipError_t launch_diagnostics(const float4 *pos, const float4 *vel, const float 
                               double inv_eps, double *part, double *out, hipStream_t stream);
 
 // Near field: target cell c (bodies [cell_start[c], cell_start[c+1])) sums over
-// the bodies of the cells in its interaction list. Two one-wave workgroups per
-// target cell (alternate target chunks), or 256-thread workgroups (one per
+// the bodies of the cells in its interaction list. Two four-wave workgroups per
+// target cell (alternate target chunks; the waves of one share a chunk and split
+// its source tiles), or 256-thread workgroups sharing source tiles (one per
 // 256-target chunk, up to 16 per cell).
 struct P2PArgs {
     const float4 *pos;      // N bodies grouped by cell
@@ -123,6 +124,8 @@ struct P2PArgs {
     long long nlist;
     float4 *acc_out;        // (ax, ay, az, 0) per body inside a cell range
     float *pot_out;         // p per body, or nullptr
+    const int *out_index;   // body i's results go to acc_out/pot_out[out_index[i]]
+                            // (nullptr: to index i)
 };
 
 // A uniform grid: dims cells per axis, corner lo, cell index per axis
@@ -134,9 +137,10 @@ struct GridSpec {
 };
 
 // wide: 256-thread workgroups sharing 256-body source tiles, about one per
-// 256-target chunk of a cell (large cells); otherwise two waves per cell (small
-// cells) taking alternate target chunks, where chunks of 192 or more targets
-// take four per lane when cells average at least 192 bodies.
+// 256-target chunk of a cell (large cells); otherwise two four-wave workgroups
+// per cell (small cells) taking alternate target chunks, whose waves take the
+// chunk's source tiles round-robin, and where chunks of 192 or more targets take
+// four per lane when cells average at least 192 bodies.
 hipError_t launch_p2p(bool pot, bool wide, const P2PArgs &args, hipStream_t stream);
 // The same kernels with the 27 neighbour cells of the grid as every cell's list.
 hipError_t launch_p2p_grid(bool pot, bool wide, const P2PArgs &args, const GridSpec &g,
@@ -150,9 +154,6 @@ hipError_t launch_gather(const float4 *pos, const int *perm, int n, float4 *out,
 // cell_start[c] = first k with sorted_keys[k] >= c, for c = 0 .. ncell.
 hipError_t launch_cell_starts(const unsigned *sorted_keys, int n, int ncell, int *cell_start,
                               hipStream_t stream);
-// acc[perm[k]] = sacc[k]; pot[perm[k]] = spot[k] (if pot).
-hipError_t launch_scatter(const float4 *sacc, const float *spot, const int *perm, int n,
-                          float4 *acc, float *pot, hipStream_t stream);
 // Stable sort of (key, value) pairs on bits [0, end_bit) of the keys (keys below
 // 2^end_bit): LSD radix sort, 8 bits per pass. temp holds sort_temp_bytes(n)
 // bytes; the inputs are read only.

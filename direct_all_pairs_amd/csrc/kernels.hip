@@ -127,7 +127,10 @@ __device__ __forceinline__ Sums<T, POT> result(const Total<T, POT> &tot)
 // One source (sx, sy, sz, sm) against the lane's T targets. The operation
 // order is fixed with explicit FMAs so that the acceleration bits do not
 // depend on whether the potential is also computed.
-template <int T, bool POT>
+// FENCE: a scheduling fence after each term keeps every source's chain whole
+// (the LDS tile kernel at one target per lane: 319.9 -> 314.6 ms at N = 2^20,
+// the same bits).
+template <int T, bool POT, bool FENCE = false>
 __device__ __forceinline__ void interact(float sx, float sy, float sz, float sm,
                                          const Targets<T> &tg, float eps2, Sums<T, POT> &acc)
 {
@@ -146,14 +149,15 @@ __device__ __forceinline__ void interact(float sx, float sy, float sz, float sm,
         acc.ay[t] = __builtin_fmaf(s, dy, acc.ay[t]);
         acc.az[t] = __builtin_fmaf(s, dz, acc.az[t]);
         if constexpr (POT) acc.p[t] = __builtin_fmaf(sm, inv, acc.p[t]);
+        if constexpr (FENCE) __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-template <int T, bool POT>
+template <int T, bool POT, bool FENCE = false>
 __device__ __forceinline__ void interact4(const float4 &b, const Targets<T> &tg, float eps2,
                                           Sums<T, POT> &acc)
 {
-    interact<T, POT>(b.x, b.y, b.z, b.w, tg, eps2, acc);
+    interact<T, POT, FENCE>(b.x, b.y, b.z, b.w, tg, eps2, acc);
 }
 
 // Target t of this lane is body base + t*kWG + threadIdx.x: each t is one
@@ -399,14 +403,14 @@ __global__ void __launch_bounds__(WG) accel_lds(AccelArgs k)
             for (int u = 0; u < U; ++u) b[u] = tl[u0 + U + u];
             sched_fence();
 #pragma unroll
-            for (int u = 0; u < U; ++u) interact4<T, POT>(a[u], tg, eps2, blk);
+            for (int u = 0; u < U; ++u) interact4<T, POT, T == 1>(a[u], tg, eps2, blk);
             sched_fence();
             const int un = (u0 + 2 * U < WG) ? u0 + 2 * U : 0;
 #pragma unroll
             for (int u = 0; u < U; ++u) a[u] = tl[un + u];
             sched_fence();
 #pragma unroll
-            for (int u = 0; u < U; ++u) interact4<T, POT>(b[u], tg, eps2, blk);
+            for (int u = 0; u < U; ++u) interact4<T, POT, T == 1>(b[u], tg, eps2, blk);
             sched_fence();
             if (((u0 + 2 * U) % FL) == 0) {
                 add_into(tot, blk);
@@ -1214,7 +1218,7 @@ constexpr int kP2PWideMin = 192;
 
 // Whether a cell of r bodies has a chunk q >= 1 (the chunk sequence below:
 // 256 targets while at least kP2PWideMin remain with QUAD, then 64, then the
-// rest). Only q = 1 is asked: the launches use at most two waves per cell.
+// rest). Only q = 1 is asked: the launches use at most two chunk workgroups per cell.
 template <bool QUAD>
 __device__ __forceinline__ bool cell_has_chunk(int r, int q)
 {
@@ -1226,23 +1230,60 @@ __device__ __forceinline__ bool cell_has_chunk(int r, int q)
     return n > q;
 }
 
+// Waves per workgroup of the near-field chunk kernel: W waves work on the same
+// target chunk, wave w taking the source tiles w, w + W, w + 2W, ... of the
+// chunk's neighbourhood walk, and their sums are added in wave order at the
+// end. With four waves a cell's work is spread over waves that finish
+// together, instead of one long wave per chunk whose remainder chunk ran after
+// the others (256 bodies per cell at N = 2^20: 2.40 -> 2.11 ms); small cells,
+// whose neighbourhoods are a few tiles, keep one wave (9.5 bodies per cell:
+// 0.23 ms with one wave, 0.49 with four). Four from kP2PWavesMinBodies bodies
+// per cell on average.
+constexpr int kP2PWaves = 4;
+constexpr int kP2PWavesMinBodies = 64;
+
+// Moves the walk `count` tiles on; false if the list ends first.
+template <typename Lists>
+__device__ __forceinline__ bool skip_tiles(const P2PArgs &k, const Lists &lists, int hi, int &e,
+                                           int &j0, int &se, int count)
+{
+    for (int s = 0; s < count; ++s)
+        if (!next_tile(k, lists, hi, e, j0, se)) return false;
+    return true;
+}
+
+// Stages the tile [j0, j0 + cnt) (loaded into cur) in the wave's LDS row, zero-mass
+// padded: the row is written and read by this wave only (LDS accesses of one wave
+// execute in order), the wave barriers keep the compiler from moving them across.
+__device__ __forceinline__ void stage_row(float4 *row, int lane, int cnt, const float4 &cur)
+{
+    const bool in = lane < cnt;
+    __builtin_amdgcn_wave_barrier();
+    row[lane] = make_float4(in ? cur.x : 0.0f, in ? cur.y : 0.0f, in ? cur.z : 0.0f,
+                            in ? cur.w : 0.0f);
+    __builtin_amdgcn_wave_barrier();
+}
+
 // Targets per chunk: a cell's bodies go up to 256 at a time (four per lane)
 // while at least 192 remain, then 64 at a time; a chunk of r < 64 bodies
 // takes tw = the next power of two >= r lanes per source group and G = 64 / tw
 // groups, lane (t, g) = (lane mod tw, lane / tw) summing every G-th source of
-// each tile for target t; the G group sums of a target are added in ascending
-// g through LDS. So a 20-body cell keeps 64 lanes busy instead of 20. The next
-// source tile's global load is issued before the current tile is evaluated.
-template <bool POT, typename Lists, bool QUAD>
-__global__ void __launch_bounds__(64) p2p_kernel(P2PArgs k, Lists lists)
+// each of its tiles for target t; the G group sums of a target are added in
+// ascending g. So a 20-body cell keeps 64 lanes busy instead of 20. Each wave
+// issues the global load of its next source tile before it evaluates the
+// current one.
+template <bool POT, typename Lists, bool QUAD, int W>
+__global__ void __launch_bounds__(64 * W) p2p_kernel(P2PArgs k, Lists lists)
 {
-    __shared__ float4 row[64];
-    __shared__ float4 red[64];
+    static_assert(!QUAD || W == kP2PWideT, "a 256-target chunk is finished by four waves");
+    constexpr int TQ = QUAD ? kP2PWideT : 1;
+    __shared__ float4 rows[W][64];
+    __shared__ float4 red[W][64 * TQ];  // each wave's per-target sums of the chunk
     __shared__ int nbr[18];
-    const int c = blockIdx.x, lane = threadIdx.x;
+    const int c = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int tb = k.cell_start[c], te = k.cell_start[c + 1];
     if (tb < 0 || te < tb || te > k.n) return;
-    // wave blockIdx.y of the cell's gridDim.y waves takes its chunks q with
+    // workgroup blockIdx.y of the cell's gridDim.y takes its chunks q with
     // q mod gridDim.y == blockIdx.y; it exits at once when it has none
     const int ny = (int)gridDim.y, y = (int)blockIdx.y;
     if (y > 0 && !cell_has_chunk<QUAD>(te - tb, y)) return;
@@ -1251,6 +1292,7 @@ __global__ void __launch_bounds__(64) p2p_kernel(P2PArgs k, Lists lists)
     int lo, hi;
     lists.range(c, lo, hi);
     const float eps2 = in_vgpr(k.eps2);
+    float4 *row = rows[w];
     for (int t0 = tb, q = 0; t0 < te; ++q) {
         const int rem = te - t0;
         const bool mine = q % ny == y;
@@ -1274,18 +1316,14 @@ __global__ void __launch_bounds__(64) p2p_kernel(P2PArgs k, Lists lists)
             Total<kP2PWideT, POT> tot;
             zero(tot);
             int e = lo - 1, j0 = 0, se = 0;
-            bool have = next_tile(k, lists, hi, e, j0, se);
+            bool have = skip_tiles(k, lists, hi, e, j0, se, w + 1);
             float4 cur = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             if (have) cur = k.pos[j0 + lane < se ? j0 + lane : se - 1];
             while (have) {
                 const int cnt = se - j0 < 64 ? se - j0 : 64;
-                const bool in = lane < cnt;
-                __builtin_amdgcn_wave_barrier();
-                row[lane] = make_float4(in ? cur.x : 0.0f, in ? cur.y : 0.0f, in ? cur.z : 0.0f,
-                                        in ? cur.w : 0.0f);
-                __builtin_amdgcn_wave_barrier();
+                stage_row(row, lane, cnt, cur);
                 int e2 = e, j2 = j0, se2 = se;
-                const bool have2 = next_tile(k, lists, hi, e2, j2, se2);
+                const bool have2 = skip_tiles(k, lists, hi, e2, j2, se2, W);
                 if (have2) cur = k.pos[j2 + lane < se2 ? j2 + lane : se2 - 1];
                 Sums<kP2PWideT, POT> blk;
                 zero(blk);
@@ -1299,13 +1337,28 @@ __global__ void __launch_bounds__(64) p2p_kernel(P2PArgs k, Lists lists)
             }
             const Sums<kP2PWideT, POT> r = result(tot);
 #pragma unroll
-            for (int q = 0; q < kP2PWideT; ++q) {
-                const int i = t0 + q * 64 + lane;
+            for (int q = 0; q < kP2PWideT; ++q)
+                red[w][q * 64 + lane] = make_float4(r.ax[q], r.ay[q], r.az[q], POT ? r.p[q] : 0.0f);
+            __syncthreads();
+            // thread (w, lane) finishes targets t0 + idx, idx = w * 64 + lane (+ 64 W ...):
+            // the W wave sums in order
+            for (int idx = threadIdx.x; idx < 64 * kP2PWideT; idx += 64 * W) {
+                float4 a = red[0][idx];
+#pragma unroll
+                for (int ww = 1; ww < W; ++ww) {
+                    const float4 v = red[ww][idx];
+                    a = make_float4(a.x + v.x, a.y + v.y, a.z + v.z, a.w + v.w);
+                }
+                const int i = t0 + idx;
                 if (i < te) {
-                    k.acc_out[i] = make_float4(r.ax[q], r.ay[q], r.az[q], 0.0f);
-                    if constexpr (POT) k.pot_out[i] = -r.p[q];
+                    const int o = k.out_index ? k.out_index[i] : i;
+                    k.acc_out[o] = make_float4(a.x, a.y, a.z, 0.0f);
+                    if constexpr (POT) k.pot_out[o] = -a.w;
                 }
             }
+            __syncthreads();  // red is refilled by the next chunk
+#pragma unroll
+            for (int q = 0; q < kP2PWideT; ++q) probe_poison(red[w][q * 64 + lane]);
             t0 += 64 * kP2PWideT;
             continue;
         }
@@ -1329,22 +1382,14 @@ __global__ void __launch_bounds__(64) p2p_kernel(P2PArgs k, Lists lists)
         Total<1, POT> tot;
         zero(tot);
         int e = lo - 1, j0 = 0, se = 0;
-        bool have = next_tile(k, lists, hi, e, j0, se);
+        bool have = skip_tiles(k, lists, hi, e, j0, se, w + 1);
         float4 cur = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         if (have) cur = k.pos[j0 + lane < se ? j0 + lane : se - 1];
         while (have) {
             const int cnt = se - j0 < 64 ? se - j0 : 64;
-            const bool in = lane < cnt;
-            // zero-mass padding past the cell end adds exact zeros; the row is
-            // written and read by this wave only (LDS accesses of one wave
-            // execute in order), the wave barriers keep the compiler from moving
-            // them across
-            __builtin_amdgcn_wave_barrier();
-            row[lane] = make_float4(in ? cur.x : 0.0f, in ? cur.y : 0.0f, in ? cur.z : 0.0f,
-                                    in ? cur.w : 0.0f);
-            __builtin_amdgcn_wave_barrier();
+            stage_row(row, lane, cnt, cur);
             int e2 = e, j2 = j0, se2 = se;
-            const bool have2 = next_tile(k, lists, hi, e2, j2, se2);
+            const bool have2 = skip_tiles(k, lists, hi, e2, j2, se2, W);
             if (have2) cur = k.pos[j2 + lane < se2 ? j2 + lane : se2 - 1];
             Sums<1, POT> blk;
             zero(blk);
@@ -1364,20 +1409,37 @@ __global__ void __launch_bounds__(64) p2p_kernel(P2PArgs k, Lists lists)
             have = have2;
         }
         const Sums<1, POT> r = result(tot);
-        __builtin_amdgcn_wave_barrier();
-        red[lane] = make_float4(r.ax[0], r.ay[0], r.az[0], POT ? r.p[0] : 0.0f);
-        __builtin_amdgcn_wave_barrier();
-        if (g == 0 && i < te) {
-            float4 a = red[t];
-            for (int gg = 1; gg < groups; ++gg) {
-                const float4 v = red[t + gg * tw];
-                a.x += v.x;
-                a.y += v.y;
-                a.z += v.z;
-                a.w += v.w;
+        float4 a = make_float4(r.ax[0], r.ay[0], r.az[0], POT ? r.p[0] : 0.0f);
+        if constexpr (W > 1) {
+            red[w][lane] = a;
+            __syncthreads();
+            // the W wave sums of each (target, group) in wave order
+            a = red[0][lane];
+#pragma unroll
+            for (int ww = 1; ww < W; ++ww) {
+                const float4 v = red[ww][lane];
+                a = make_float4(a.x + v.x, a.y + v.y, a.z + v.z, a.w + v.w);
             }
-            k.acc_out[i] = make_float4(a.x, a.y, a.z, 0.0f);
-            if constexpr (POT) k.pot_out[i] = -a.w;
+        }
+        if (w == 0) {
+            // the groups of each target in ascending g, through wave 0's own row
+            __builtin_amdgcn_wave_barrier();
+            row[lane] = a;
+            __builtin_amdgcn_wave_barrier();
+            if (g == 0 && i < te) {
+                float4 s = row[t];
+                for (int gg = 1; gg < groups; ++gg) {
+                    const float4 v = row[t + gg * tw];
+                    s = make_float4(s.x + v.x, s.y + v.y, s.z + v.z, s.w + v.w);
+                }
+                const int o = k.out_index ? k.out_index[i] : i;
+                k.acc_out[o] = make_float4(s.x, s.y, s.z, 0.0f);
+                if constexpr (POT) k.pot_out[o] = -s.w;
+            }
+        }
+        if constexpr (W > 1) {
+            __syncthreads();  // red is refilled by the next chunk
+            probe_poison(red[w][lane]);
         }
         t0 += tw;
     }
@@ -1474,8 +1536,9 @@ __global__ void __launch_bounds__(256) p2p_wg_kernel(P2PArgs k, Lists lists)
         probe_poison(tile[0][tid]);  // the next chunk's first tile goes here
         if (i < te) {
             const Sums<1, POT> res = result(tot);
-            k.acc_out[i] = make_float4(res.ax[0], res.ay[0], res.az[0], 0.0f);
-            if constexpr (POT) k.pot_out[i] = -res.p[0];
+            const int o = k.out_index ? k.out_index[i] : i;
+            k.acc_out[o] = make_float4(res.ax[0], res.ay[0], res.az[0], 0.0f);
+            if constexpr (POT) k.pot_out[o] = -res.p[0];
         }
     }
 }
@@ -1524,28 +1587,16 @@ __global__ void __launch_bounds__(256) cell_starts_kernel(const unsigned *__rest
     start[c] = a;
 }
 
-__global__ void __launch_bounds__(256) scatter_kernel(const float4 *__restrict__ sacc,
-                                                      const float *__restrict__ spot,
-                                                      const int *__restrict__ perm, int n,
-                                                      float4 *__restrict__ acc,
-                                                      float *__restrict__ pot)
-{
-    const int k = blockIdx.x * 256 + threadIdx.x;
-    if (k >= n) return;
-    const int i = perm[k];
-    acc[i] = sacc[k];
-    if (pot) pot[i] = spot[k];
-}
-
 // ---------------------------------------------------------------- binning sort
 // Stable LSD radix sort of the (cell key, body index) pairs of nbody_near_grid,
 // 8 key bits per pass, three kernels per pass:
 //   hist    - workgroup b counts the digits of its contiguous key range
 //             [b per, (b + 1) per) into counts[digit][b] (LDS counters: the
 //             counts do not depend on the order of the additions);
-//   scan    - one workgroup turns counts into exclusive offsets in digit-major
-//             order (digit, then workgroup), so equal digits keep the order of
-//             the workgroups, i.e. of the input;
+//   scan    - counts become exclusive offsets in digit-major order (digit,
+//             then workgroup), so equal digits keep the order of the
+//             workgroups, i.e. of the input (two kernels: tile sums, then each
+//             tile scanned from the sum of the tiles before it);
 //   scatter - workgroup b walks its range 256 keys at a time in input order; a
 //             key's place is its digit's running offset plus the number of keys
 //             with the same digit before it in the sub-tile (earlier waves'
@@ -1555,7 +1606,7 @@ __global__ void __launch_bounds__(256) scatter_kernel(const float4 *__restrict__
 // the same bits every time, so a cell keeps its bodies in input order.
 constexpr int kSortBits = 8;
 constexpr int kSortDigits = 1 << kSortBits;  // 256: one counter per thread
-constexpr int kSortMaxBlocks = 2048;         // counts <= 2^19 entries: one-workgroup scan
+constexpr int kSortMaxBlocks = 2048;         // counts <= 2^19 entries: <= 128 scan tiles
 constexpr int kSortScanThreads = 1024;
 
 struct SortShape {
@@ -1597,32 +1648,78 @@ __global__ void __launch_bounds__(256) sort_hist_kernel(const unsigned *__restri
     counts[threadIdx.x * nblocks + blockIdx.x] = h[threadIdx.x];
 }
 
-// Exclusive prefix sum of counts[0 .. total) in place: each thread a contiguous run, the
-// run sums scanned across the workgroup, then each run rewritten from its offset.
-__global__ void __launch_bounds__(kSortScanThreads) sort_scan_kernel(int *__restrict__ counts,
-                                                                     int total)
+// Exclusive prefix sum of counts[0 .. total) in place, in tiles of 4096 entries, one
+// workgroup per tile: sort_tile_sums_kernel adds up each tile, then sort_scan_kernel
+// scans its tile from the sum of the tiles before it (a coalesced load of the tile
+// into LDS, each thread the sum of four consecutive entries, an inclusive scan of
+// those over the wave by shuffles, the 16 wave totals added in wave order, the four
+// exclusive prefixes written back through LDS). Integer sums: the result is exact.
+constexpr int kSortScanTile = 4 * kSortScanThreads;
+
+// Sum over the workgroup of v (one value per thread), in a fixed order; every thread
+// gets it. red holds kSortScanThreads / 64 ints.
+__device__ __forceinline__ int sort_block_sum(int v, int *red)
 {
-    __shared__ int part[kSortScanThreads];
-    const int t = threadIdx.x;
-    const int chunk = (total + kSortScanThreads - 1) / kSortScanThreads;
-    const long long a0 = (long long)t * chunk;
-    const int a = (int)(a0 < total ? a0 : total);
-    const int b = a + chunk < total ? a + chunk : total;
-    int sum = 0;
-    for (int i = a; i < b; ++i) sum += counts[i];
-    part[t] = sum;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 0) red[w] = v;
     __syncthreads();
-    for (int off = 1; off < kSortScanThreads; off <<= 1) {  // inclusive Hillis-Steele scan
-        const int v = t >= off ? part[t - off] : 0;
-        __syncthreads();
-        part[t] += v;
-        __syncthreads();
+    int s = 0;
+    for (int q = 0; q < kSortScanThreads / 64; ++q) s += red[q];
+    return s;
+}
+
+__global__ void __launch_bounds__(kSortScanThreads)
+    sort_tile_sums_kernel(const int *__restrict__ counts, int total, int *__restrict__ tile_sums)
+{
+    __shared__ int red[kSortScanThreads / 64];
+    const int base = blockIdx.x * kSortScanTile, t = threadIdx.x;
+    int v = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int i = base + k * kSortScanThreads + t;
+        v += i < total ? counts[i] : 0;
     }
-    int run = part[t] - sum;
-    for (int i = a; i < b; ++i) {
-        const int c = counts[i];
-        counts[i] = run;
-        run += c;
+    const int s = sort_block_sum(v, red);
+    if (t == 0) tile_sums[blockIdx.x] = s;
+}
+
+__global__ void __launch_bounds__(kSortScanThreads)
+    sort_scan_kernel(int *__restrict__ counts, int total, const int *__restrict__ tile_sums)
+{
+    __shared__ int4 buf[kSortScanThreads];  // the tile's kSortScanTile entries
+    __shared__ int wsum[kSortScanThreads / 64];
+    __shared__ int red[kSortScanThreads / 64];
+    int *flat = reinterpret_cast<int *>(buf);
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int base = blockIdx.x * kSortScanTile;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int i = base + k * kSortScanThreads + t;
+        flat[k * kSortScanThreads + t] = i < total ? counts[i] : 0;
+    }
+    // the tiles before this one (at most kSortScanThreads of them)
+    const int carry = sort_block_sum(t < (int)blockIdx.x ? tile_sums[t] : 0, red);
+    const int4 v = buf[t];  // entries 4t .. 4t + 3 of the tile (published by the barrier above)
+    const int sum = v.x + v.y + v.z + v.w;
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+    }
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    int before = carry;
+    for (int q = 0; q < w; ++q) before += wsum[q];
+    const int e = before + incl - sum;
+    buf[t] = make_int4(e, e + v.x, e + v.x + v.y, e + v.x + v.y + v.z);
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int i = base + k * kSortScanThreads + t;
+        if (i < total) counts[i] = flat[k * kSortScanThreads + t];
     }
 }
 
@@ -1642,11 +1739,15 @@ __global__ void __launch_bounds__(256) sort_scatter_kernel(const unsigned *__res
     __syncthreads();
     int b0, e;
     sort_range(n, per, b0, e);
+    bool valid = b0 + tid < e;
+    unsigned k = valid ? kin[b0 + tid] : 0u;
+    int v = valid ? vin[b0 + tid] : 0;
     for (int s0 = b0; s0 < e; s0 += 256) {
-        const int i = s0 + tid;
-        const bool valid = i < e;
-        const unsigned k = valid ? kin[i] : 0u;
-        const int v = valid ? vin[i] : 0;
+        // the next sub-tile's pair, loaded while this one is placed
+        const int ni = s0 + 256 + tid;
+        const bool nvalid = ni < e;
+        const unsigned nk = nvalid ? kin[ni] : 0u;
+        const int nv = nvalid ? vin[ni] : 0;
         const unsigned d = (k >> shift) & (kSortDigits - 1);
         // the valid lanes of this wave whose key has digit d
         unsigned long long same = __ballot(valid);
@@ -1670,6 +1771,9 @@ __global__ void __launch_bounds__(256) sort_scatter_kernel(const unsigned *__res
 #pragma unroll
         for (int q = 0; q < 4; ++q) wcnt[q][tid] = 0;
         __syncthreads();
+        k = nk;
+        v = nv;
+        valid = nvalid;
     }
 }
 
@@ -1831,16 +1935,23 @@ hipError_t launch_p2p_any(bool pot, bool wide, const P2PArgs &args, Lists l, hip
     P2PArgs a = args;
     void *k[] = {&a, &l};
     const void *fn;
+    static_assert(kP2PWideMin >= kP2PWavesMinBodies && kP2PWaves == kP2PWideT,
+                  "chunks of four targets per lane run in four-wave workgroups");
     const bool quad = (long long)a.n >= (long long)kP2PWideMin * a.ncell;
+    const bool four = quad || (long long)a.n >= (long long)kP2PWavesMinBodies * a.ncell;
+    const int waves = four ? kP2PWaves : 1;
     if (wide)
         fn = pot ? (const void *)&p2p_wg_kernel<true, Lists> : (const void *)&p2p_wg_kernel<false, Lists>;
     else if (quad)
-        fn = pot ? (const void *)&p2p_kernel<true, Lists, true>
-                 : (const void *)&p2p_kernel<false, Lists, true>;
+        fn = pot ? (const void *)&p2p_kernel<true, Lists, true, kP2PWaves>
+                 : (const void *)&p2p_kernel<false, Lists, true, kP2PWaves>;
+    else if (four)
+        fn = pot ? (const void *)&p2p_kernel<true, Lists, false, kP2PWaves>
+                 : (const void *)&p2p_kernel<false, Lists, false, kP2PWaves>;
     else
-        fn = pot ? (const void *)&p2p_kernel<true, Lists, false>
-                 : (const void *)&p2p_kernel<false, Lists, false>;
-    // one-wave kernels: two waves per cell, each taking every other target chunk, so
+        fn = pot ? (const void *)&p2p_kernel<true, Lists, false, 1>
+                 : (const void *)&p2p_kernel<false, Lists, false, 1>;
+    // chunk kernel: two workgroups per cell, each taking every other target chunk, so
     // a cell's large chunk and the chunk of its remaining bodies run side by side;
     // the workgroup kernel: about one workgroup per 256-target chunk of a cell a
     // little larger than the mean (at most 16), so large cells spread over the GPU
@@ -1851,7 +1962,8 @@ hipError_t launch_p2p_any(bool pot, bool wide, const P2PArgs &args, Lists l, hip
         ny = chunks >= 16.0 ? 16u : (unsigned)std::ceil(chunks);
         if (ny < 1) ny = 1;
     }
-    return hipLaunchKernel(fn, dim3((unsigned)a.ncell, ny), dim3(wide ? 256 : 64), k, 0, stream);
+    return hipLaunchKernel(fn, dim3((unsigned)a.ncell, ny), dim3(wide ? 256 : 64 * waves), k, 0,
+                           stream);
 }
 
 hipError_t launch_p2p(bool pot, bool wide, const P2PArgs &args, hipStream_t stream)
@@ -1898,20 +2010,12 @@ hipError_t launch_cell_starts(const unsigned *sorted_keys, int n, int ncell, int
                            dim3((unsigned)((ncell + 1 + 255) / 256)), dim3(256), k, 0, stream);
 }
 
-hipError_t launch_scatter(const float4 *sacc, const float *spot, const int *perm, int n,
-                          float4 *acc, float *pot, hipStream_t stream)
-{
-    if (n <= 0) return n == 0 ? hipSuccess : hipErrorInvalidValue;
-    void *k[] = {&sacc, &spot, &perm, &n, &acc, &pot};
-    return hipLaunchKernel((const void *)&scatter_kernel, dim3((unsigned)((n + 255) / 256)),
-                           dim3(256), k, 0, stream);
-}
-
 size_t sort_temp_bytes(int n)
 {
     const SortShape sh = sort_shape(n < 1 ? 1 : n);
     const size_t keys = ((size_t)(n < 1 ? 1 : n) * 4 + 255) / 256 * 256;
-    return 2 * keys + (size_t)kSortDigits * (size_t)sh.nblocks * sizeof(int);
+    const size_t counts = ((size_t)kSortDigits * (size_t)sh.nblocks * sizeof(int) + 255) / 256 * 256;
+    return 2 * keys + counts + (size_t)kSortScanThreads * sizeof(int);
 }
 
 hipError_t sort_pairs(void *temp, const unsigned *keys_in, unsigned *keys_out, const int *vals_in,
@@ -1924,6 +2028,11 @@ hipError_t sort_pairs(void *temp, const unsigned *keys_in, unsigned *keys_out, c
     int *v_alt = (int *)((char *)temp + keys);
     int *counts = (int *)((char *)temp + 2 * keys);
     int total = kSortDigits * sh.nblocks;
+    int *tile_sums = (int *)((char *)counts +
+                             ((size_t)total * sizeof(int) + 255) / 256 * 256);
+    const unsigned ntiles = (unsigned)((total + kSortScanTile - 1) / kSortScanTile);
+    static_assert(kSortDigits * kSortMaxBlocks <= kSortScanTile * kSortScanThreads,
+                  "one scan workgroup adds at most kSortScanThreads tile sums");
     const int passes = (end_bit + kSortBits - 1) / kSortBits;
     const unsigned *ks = keys_in;
     const int *vs = vals_in;
@@ -1939,9 +2048,12 @@ hipError_t sort_pairs(void *temp, const unsigned *keys_in, unsigned *keys_out, c
         hipError_t e = hipLaunchKernel((const void *)&sort_hist_kernel, dim3(nbl), dim3(256), a1,
                                        0, stream);
         if (e != hipSuccess) return e;
-        void *a2[] = {&counts, &total};
-        e = hipLaunchKernel((const void *)&sort_scan_kernel, dim3(1), dim3(kSortScanThreads), a2,
-                            0, stream);
+        void *a2[] = {&counts, &total, &tile_sums};
+        e = hipLaunchKernel((const void *)&sort_tile_sums_kernel, dim3(ntiles),
+                            dim3(kSortScanThreads), a2, 0, stream);
+        if (e != hipSuccess) return e;
+        e = hipLaunchKernel((const void *)&sort_scan_kernel, dim3(ntiles), dim3(kSortScanThreads),
+                            a2, 0, stream);
         if (e != hipSuccess) return e;
         void *a3[] = {&ks, &vs, &nn, &per, &shift, &nbl, &counts, &kd, &vd};
         e = hipLaunchKernel((const void *)&sort_scatter_kernel, dim3(nbl), dim3(256), a3, 0,

@@ -288,7 +288,7 @@ int nbody_p2p(const nbody_f4 *pos_xyzm, int64_t N, float eps2, const int32_t *ce
  * bodies in their input order), runs the nbody_p2p kernel over the 27-cell
  * neighbourhoods (as 9 runs of 3 consecutive cells) and writes acc_out /
  * pot_out in the caller's body order.
- * At most 2^28 cells. Scratch: ~N x 56 bytes + 4 bytes per cell + the sort's.
+ * At most 2^28 cells. Scratch: ~N x 41 bytes + 4 bytes per cell.
  */
 int nbody_near_grid(const nbody_f4 *pos_xyzm, int64_t N, float eps2, const float lo[3], float h,
                     const int32_t dims[3], nbody_f4 *acc_out, float *pot_out,

@@ -117,15 +117,19 @@ def test_probe_build_small_steps(nb, probe):
     assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])
 
 
-def test_probe_build_shared_tile_near_field(nb, probe):
+@pytest.mark.parametrize("n,h,dims", [(20000, 1.0, (2, 2, 2)),
+                                      (800000, 0.125, (16, 16, 16)),
+                                      (100000, 0.125, (16, 16, 16))])
+def test_probe_build_shared_tile_near_field(nb, probe, n, h, dims):
     """Eight large cells (2 x 2 x 2 grid, ~2500 bodies each): the 256-thread shared-tile
-    near-field kernel, several target chunks and source tiles per cell."""
+    near-field kernel, several target chunks and source tiles per cell. 4096 cells of ~195
+    and of ~24 bodies: the chunk kernel, whose four waves add their sums through a shared
+    buffer (four targets per lane, and source groups for small chunks)."""
     import torch
 
-    n = 20000
     pos_h, _ = workloads.random_bodies(n, seed=12)
     pd = to_dev(pos_h)
-    lo, h, dims = (-1.0, -1.0, -1.0), 1.0, (2, 2, 2)
+    lo = (-1.0, -1.0, -1.0)
     outs = []
     for which in ("library", "probe"):
         acc = torch.full((n, 4), 7.0, device="cuda")
@@ -139,4 +143,4 @@ def test_probe_build_shared_tile_near_field(nb, probe):
             assert rc == 0, probe.nbody_last_error()
         torch.cuda.synchronize()
         outs.append((acc.cpu().numpy(), pot.cpu().numpy()))
-    _assert_same(outs, "near grid, 8 cells")
+    _assert_same(outs, f"near grid, {dims} cells")
