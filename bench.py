@@ -255,8 +255,11 @@ def copy_calibration(nbytes: int) -> int:
 
 
 def sweep(nb, w, pos, vel, acc, pot, args) -> int:
-    """One call per layout (nbody_accel_plan, or nbody_step_plan for the stepping workloads),
-    HIP-event timed; fastest layout last."""
+    """Every layout of the workload's call (nbody_accel_plan, or nbody_step_plan for the
+    stepping workloads), HIP-event timed; fastest layout last. Sequentially (args.steps calls
+    per layout after args.warmup), or with args.rounds > 0 round-robin: every layout is timed
+    over args.steps calls once per round, so that clock drift falls on all layouts alike, and
+    the median of the rounds is reported."""
     import torch
 
     n = w.n
@@ -270,9 +273,11 @@ def sweep(nb, w, pos, vel, acc, pot, args) -> int:
     if n <= 65536:
         layouts += [("small", tw, 256) for tw in (4, 8, 16, 32)]
     if args.sweep_only != "all":
-        keep = {"tiles": ("lds", "scalar", "readlane")}.get(args.sweep_only, (args.sweep_only,))
+        keep = set()
+        for m in args.sweep_only.split(","):
+            keep |= set({"tiles": ("lds", "scalar", "readlane")}.get(m, (m,)))
         layouts = [lay for lay in layouts if lay[0] in keep]
-    results = []
+    cases = []
     for bcast, tpl, wg in layouts:
         for splits in (split_opts if bcast == "lds" else [0]):
             if splits and (splits - 1) * wg >= n:  # some chunk would be empty
@@ -283,34 +288,54 @@ def sweep(nb, w, pos, vel, acc, pot, args) -> int:
                 plan = nb.make_plan(mode="small", tpl=tpl)
             else:
                 plan = nb.make_plan(mode="tiles", bcast=bcast, tpl=tpl, splits=splits, wg=wg)
+            cases.append((bcast, tpl, wg, splits, plan))
 
-            def call():
-                if stepping:
-                    nb.nbody_step_plan(pos, vel, n, float(w.dt), float(w.eps2), w.nsteps, plan,
-                                       stream)
-                else:
-                    nb.nbody_accel_plan(pos, n, float(w.eps2), acc, pot, plan, stream)
+    def call(plan):
+        if stepping:
+            nb.nbody_step_plan(pos, vel, n, float(w.dt), float(w.eps2), w.nsteps, plan, stream)
+        else:
+            nb.nbody_accel_plan(pos, n, float(w.eps2), acc, pot, plan, stream)
 
+    def timed(plan):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            call(plan)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    times = [[] for _ in cases]
+    if args.rounds > 0:
+        for c in cases:
             for _ in range(max(1, args.warmup)):
-                call()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(args.steps):
-                call()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / args.steps
-            evals = w.nsteps if stepping else 1
-            r = {"workload": args.workload, "N": n, "potential": pot is not None,
-                 "call": "nbody_step_plan" if stepping else "nbody_accel_plan",
-                 "bcast": bcast, "tpl": tpl, "wg": wg, "splits": splits or "auto",
-                 "ms": round(ms, 4), "us_per_eval": round(ms * 1e3 / evals, 3),
-                 "G_int_per_s": round(interactions(n) * evals / ms / 1e6, 2)}
-            results.append(r)
-            print(json.dumps(r), flush=True)
+                call(c[4])
+        torch.cuda.synchronize()
+        for _ in range(args.rounds):
+            for k, c in enumerate(cases):
+                times[k].append(timed(c[4]))
+    else:
+        for k, c in enumerate(cases):
+            for _ in range(max(1, args.warmup)):
+                call(c[4])
+            times[k].append(timed(c[4]))
+    results = []
+    evals = w.nsteps if stepping else 1
+    for (bcast, tpl, wg, splits, plan), t in zip(cases, times):
+        ms = sorted(t)[len(t) // 2]
+        r = {"workload": args.workload, "N": n, "potential": pot is not None,
+             "call": "nbody_step_plan" if stepping else "nbody_accel_plan",
+             "bcast": bcast, "tpl": tpl, "wg": wg, "splits": splits or "auto",
+             "ms": round(ms, 4), "us_per_eval": round(ms * 1e3 / evals, 3),
+             "G_int_per_s": round(interactions(n) * evals / ms / 1e6, 2),
+             "timing": f"median of {args.rounds} round-robin rounds" if args.rounds > 0
+             else "sequential"}
+        results.append(r)
+        print(json.dumps(r), flush=True)
     best = max(results, key=lambda r: r["G_int_per_s"])
-    print(json.dumps({"best": best}), flush=True)
+    print(json.dumps({"best": best, "auto_plan": nb.nbody_plan_for(n, pot is not None).as_dict()}),
+          flush=True)
     return 0
 
 
@@ -447,8 +472,12 @@ def shard_bench(nb, w, pos, args) -> int:
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 10; 200 for plummer65536, 2000 for disk4096, "
+                         "whose calls take about a millisecond or less)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: 2; 50 for plummer65536 and 200 for "
+                         "disk4096, so that the shader clock has ramped up)")
     ap.add_argument("--workload", default="cube1m", choices=sorted(
         ["cube1m", "plummer65536", "disk4096", "cube2048_steps", "two_plummer300007"]),
         help="which of the five workloads to time (default: the N=1,048,576 cube)")
@@ -464,8 +493,11 @@ def main(argv=None) -> int:
     ap.add_argument("--sweep", action="store_true",
                     help="time every (broadcast, targets-per-lane, tile, splits) layout of the "
                          "workload's call and print one JSON line per layout (no contract line)")
-    ap.add_argument("--sweep-only", default="all", choices=["all", "tiles", "pairs", "small"],
-                    help="restrict --sweep to one evaluation mode")
+    ap.add_argument("--sweep-only", default="all",
+                    help="restrict --sweep to modes: all, or a comma list of tiles, pairs, small")
+    ap.add_argument("--rounds", type=int, default=0,
+                    help="--sweep: time the layouts round-robin over this many rounds (median "
+                         "reported) instead of one after another")
     ap.add_argument("--near-grid", type=int, default=0, metavar="D",
                     help="only time nbody_near_grid on a D^3 grid over [-1, 1]^3 (near field; "
                          "prints its own JSON line, no contract line)")
@@ -480,6 +512,12 @@ def main(argv=None) -> int:
                     help="only run a plain device-to-device copy of BYTES (twice) and exit; "
                          "used to scale the HBM byte counters of rocprofv3")
     args = ap.parse_args(argv)
+    short = {"plummer65536": (200, 50), "disk4096": (2000, 200)}
+    steps0, warm0 = short.get(args.workload, (10, 2)) if args.n is None else (10, 2)
+    if args.steps is None:
+        args.steps = steps0
+    if args.warmup is None:
+        args.warmup = warm0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

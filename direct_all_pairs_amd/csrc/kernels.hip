@@ -1126,7 +1126,7 @@ struct CsrLists {
     const int *list;
     long long nlist;
     int ncell;
-    __device__ void bind(int) {}
+    __device__ void bind(const P2PArgs &, int) {}
     __device__ void range(int c, int &lo, int &hi) const
     {
         long long a = off[c], b = off[c + 1];
@@ -1150,21 +1150,48 @@ struct CsrLists {
 // lie in the grid are consecutive in the x-fastest cell order, so their bodies
 // are one contiguous range of the sorted array (the same bodies in the same
 // order as the three cells one after another, in a third of the runs, which
-// leaves fewer part-filled source tiles). Computed once per workgroup into LDS
-// by lanes 0..8.
+// leaves fewer part-filled source tiles). Lanes 0..8 read the runs' body ranges
+// from cell_start into LDS once per workgroup, so that the tile walk of every
+// wave finds them there instead of waiting on global loads at each run.
+// The chunk kernel walks the 9 runs as one sequence of bodies (run 0, then run 1,
+// ...) cut into 64-body tiles, so that only the last tile of the neighbourhood is
+// part-filled rather than the last tile of every run: position p of the sequence
+// lies in run e with pre[e] <= p < pre[e + 1] and is body p + off[e].
+constexpr int kGridRuns = 9;
+constexpr int kGridLds = 2 * kGridRuns + (kGridRuns + 1) + kGridRuns;  // ints
+
 struct GridLists {
     int dx, dy, dz;
-    int *nbr;  // 18 LDS entries: first and last cell of each run, -1 outside the grid
-    __device__ void bind(int c)
+    // kGridLds LDS ints: the body range [sb, sn) of each run ((-1, -1) outside the grid),
+    // then pre[10] and off[9] of the run sequence
+    int *nbr;
+    __device__ const int *pre() const { return nbr + 2 * kGridRuns; }
+    __device__ const int *off() const { return nbr + 3 * kGridRuns + 1; }
+    __device__ void bind(const P2PArgs &k, int c)
     {
         const int lane = threadIdx.x;
-        if (lane < 9) {
+        if (lane < kGridRuns) {
             const int cx = c % dx, cy = (c / dx) % dy, cz = c / (dx * dy);
             const int y = cy + lane % 3 - 1, z = cz + lane / 3 - 1;
             const bool in = y >= 0 && y < dy && z >= 0 && z < dz;
             const int row = (z * dy + y) * dx;
-            nbr[2 * lane] = in ? row + (cx > 0 ? cx - 1 : 0) : -1;
-            nbr[2 * lane + 1] = in ? row + (cx + 1 < dx ? cx + 1 : dx - 1) : -1;
+            const int first = row + (cx > 0 ? cx - 1 : 0);
+            const int last = row + (cx + 1 < dx ? cx + 1 : dx - 1);
+            nbr[2 * lane] = in ? k.cell_start[first] : -1;
+            nbr[2 * lane + 1] = in ? k.cell_start[last + 1] : -1;
+        }
+        __syncthreads();
+        if (lane == 0) {
+            int *pr = nbr + 2 * kGridRuns, *of = nbr + 3 * kGridRuns + 1;
+            int at = 0;
+            for (int e = 0; e < kGridRuns; ++e) {
+                const int sb = nbr[2 * e], sn = nbr[2 * e + 1];
+                const bool ok = sb >= 0 && sn > sb && sn <= k.n;
+                pr[e] = at;
+                of[e] = ok ? sb - at : 0;
+                at += ok ? sn - sb : 0;
+            }
+            pr[kGridRuns] = at;
         }
         __syncthreads();
     }
@@ -1175,11 +1202,8 @@ struct GridLists {
     }
     __device__ bool source(const P2PArgs &k, int e, int &sb, int &sn) const
     {
-        const int first = __builtin_amdgcn_readfirstlane(nbr[2 * e]);
-        const int last = __builtin_amdgcn_readfirstlane(nbr[2 * e + 1]);
-        if (first < 0) return false;
-        sb = k.cell_start[first];
-        sn = k.cell_start[last + 1];
+        sb = __builtin_amdgcn_readfirstlane(nbr[2 * e]);
+        sn = __builtin_amdgcn_readfirstlane(nbr[2 * e + 1]);
         return sb >= 0 && sn > sb && sn <= k.n;
     }
 };
@@ -1252,6 +1276,79 @@ __device__ __forceinline__ bool skip_tiles(const P2PArgs &k, const Lists &lists,
     return true;
 }
 
+// A wave's walk over the source tiles of a target cell's list: start() puts it on
+// tile w, next() moves it `step` tiles on, count() is the number of bodies in the
+// current tile (at most 64) and load() lane's body of it (an index clamped into
+// the tile; the stage pads the lanes past count() with zero masses). All uniform
+// across the wave.
+//   RunCursor: the listed cells one after another, each cut into tiles (a cell's
+//   last tile may be part-filled): CSR lists.
+template <typename Lists>
+struct RunCursor {
+    int hi, e, j0, se;
+    bool have;
+    __device__ void start(const P2PArgs &k, const Lists &l, int lo, int hi_, int w)
+    {
+        hi = hi_;
+        e = lo - 1;
+        j0 = 0;
+        se = 0;
+        have = skip_tiles(k, l, hi, e, j0, se, w + 1);
+    }
+    __device__ void next(const P2PArgs &k, const Lists &l, int step)
+    {
+        have = skip_tiles(k, l, hi, e, j0, se, step);
+    }
+    __device__ int count() const { return se - j0 < 64 ? se - j0 : 64; }
+    __device__ float4 load(const P2PArgs &k, int lane) const
+    {
+        return k.pos[j0 + lane < se ? j0 + lane : se - 1];
+    }
+};
+
+//   PackedCursor: the 9 grid runs as one sequence of bodies in 64-body tiles
+//   (GridLists), so only the sequence's last tile is part-filled.
+struct PackedCursor {
+    int total, t;
+    int pre[kGridRuns];  // pre[1 .. 8] of the run sequence (uniform)
+    const int *off;      // LDS
+    bool have;
+    __device__ void start(const P2PArgs &, const GridLists &l, int, int, int w)
+    {
+        const int *p = l.pre();
+#pragma unroll
+        for (int e = 1; e < kGridRuns; ++e) pre[e] = __builtin_amdgcn_readfirstlane(p[e]);
+        total = __builtin_amdgcn_readfirstlane(p[kGridRuns]);
+        off = l.off();
+        t = w;
+        have = t * 64 < total;
+    }
+    __device__ void next(const P2PArgs &, const GridLists &, int step)
+    {
+        t += step;
+        have = t * 64 < total;
+    }
+    __device__ int count() const { return total - t * 64 < 64 ? total - t * 64 : 64; }
+    __device__ float4 load(const P2PArgs &k, int lane) const
+    {
+        int p = t * 64 + lane;
+        p = p < total ? p : total - 1;
+        int e = 0;
+#pragma unroll
+        for (int q = 1; q < kGridRuns; ++q) e += p >= pre[q] ? 1 : 0;
+        return k.pos[p + off[e]];
+    }
+};
+
+template <typename Lists>
+struct CursorOf {
+    using type = RunCursor<Lists>;
+};
+template <>
+struct CursorOf<GridLists> {
+    using type = PackedCursor;
+};
+
 // Stages the tile [j0, j0 + cnt) (loaded into cur) in the wave's LDS row, zero-mass
 // padded: the row is written and read by this wave only (LDS accesses of one wave
 // execute in order), the wave barriers keep the compiler from moving them across.
@@ -1277,9 +1374,10 @@ __global__ void __launch_bounds__(64 * W) p2p_kernel(P2PArgs k, Lists lists)
 {
     static_assert(!QUAD || W == kP2PWideT, "a 256-target chunk is finished by four waves");
     constexpr int TQ = QUAD ? kP2PWideT : 1;
+    using Cursor = typename CursorOf<Lists>::type;
     __shared__ float4 rows[W][64];
     __shared__ float4 red[W][64 * TQ];  // each wave's per-target sums of the chunk
-    __shared__ int nbr[18];
+    __shared__ int nbr[kGridLds];
     const int c = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int tb = k.cell_start[c], te = k.cell_start[c + 1];
     if (tb < 0 || te < tb || te > k.n) return;
@@ -1288,7 +1386,7 @@ __global__ void __launch_bounds__(64 * W) p2p_kernel(P2PArgs k, Lists lists)
     const int ny = (int)gridDim.y, y = (int)blockIdx.y;
     if (y > 0 && !cell_has_chunk<QUAD>(te - tb, y)) return;
     if constexpr (__is_same(Lists, GridLists)) lists.nbr = nbr;
-    lists.bind(c);
+    lists.bind(k, c);
     int lo, hi;
     lists.range(c, lo, hi);
     const float eps2 = in_vgpr(k.eps2);
@@ -1315,25 +1413,27 @@ __global__ void __launch_bounds__(64 * W) p2p_kernel(P2PArgs k, Lists lists)
             }
             Total<kP2PWideT, POT> tot;
             zero(tot);
-            int e = lo - 1, j0 = 0, se = 0;
-            bool have = skip_tiles(k, lists, hi, e, j0, se, w + 1);
+            Cursor cs;
+            cs.start(k, lists, lo, hi, w);
             float4 cur = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            if (have) cur = k.pos[j0 + lane < se ? j0 + lane : se - 1];
-            while (have) {
-                const int cnt = se - j0 < 64 ? se - j0 : 64;
+            if (cs.have) cur = cs.load(k, lane);
+            while (cs.have) {
+                const int cnt = cs.count();
                 stage_row(row, lane, cnt, cur);
-                int e2 = e, j2 = j0, se2 = se;
-                const bool have2 = skip_tiles(k, lists, hi, e2, j2, se2, W);
-                if (have2) cur = k.pos[j2 + lane < se2 ? j2 + lane : se2 - 1];
+                Cursor nx = cs;
+                nx.next(k, lists, W);
+                if (nx.have) cur = nx.load(k, lane);
                 Sums<kP2PWideT, POT> blk;
                 zero(blk);
+                if (cnt == 64) {
+#pragma unroll 16
+                    for (int u = 0; u < 64; ++u) interact4<kP2PWideT, POT>(row[u], tg, eps2, blk);
+                } else {
 #pragma unroll 8
-                for (int u = 0; u < cnt; ++u) interact4<kP2PWideT, POT>(row[u], tg, eps2, blk);
+                    for (int u = 0; u < cnt; ++u) interact4<kP2PWideT, POT>(row[u], tg, eps2, blk);
+                }
                 add_into(tot, blk);
-                e = e2;
-                j0 = j2;
-                se = se2;
-                have = have2;
+                cs = nx;
             }
             const Sums<kP2PWideT, POT> r = result(tot);
 #pragma unroll
@@ -1381,16 +1481,16 @@ __global__ void __launch_bounds__(64 * W) p2p_kernel(P2PArgs k, Lists lists)
         tg.z[0] = me.z;
         Total<1, POT> tot;
         zero(tot);
-        int e = lo - 1, j0 = 0, se = 0;
-        bool have = skip_tiles(k, lists, hi, e, j0, se, w + 1);
+        Cursor cs;
+        cs.start(k, lists, lo, hi, w);
         float4 cur = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        if (have) cur = k.pos[j0 + lane < se ? j0 + lane : se - 1];
-        while (have) {
-            const int cnt = se - j0 < 64 ? se - j0 : 64;
+        if (cs.have) cur = cs.load(k, lane);
+        while (cs.have) {
+            const int cnt = cs.count();
             stage_row(row, lane, cnt, cur);
-            int e2 = e, j2 = j0, se2 = se;
-            const bool have2 = skip_tiles(k, lists, hi, e2, j2, se2, W);
-            if (have2) cur = k.pos[j2 + lane < se2 ? j2 + lane : se2 - 1];
+            Cursor nx = cs;
+            nx.next(k, lists, W);
+            if (nx.have) cur = nx.load(k, lane);
             Sums<1, POT> blk;
             zero(blk);
             if (groups == 1 && cnt == 64) {
@@ -1403,10 +1503,7 @@ __global__ void __launch_bounds__(64 * W) p2p_kernel(P2PArgs k, Lists lists)
                     interact4<1, POT>(row[u0 + g], tg, eps2, blk);
             }
             add_into(tot, blk);
-            e = e2;
-            j0 = j2;
-            se = se2;
-            have = have2;
+            cs = nx;
         }
         const Sums<1, POT> r = result(tot);
         float4 a = make_float4(r.ax[0], r.ay[0], r.az[0], POT ? r.p[0] : 0.0f);
@@ -1474,7 +1571,7 @@ template <bool POT, typename Lists>
 __global__ void __launch_bounds__(256) p2p_wg_kernel(P2PArgs k, Lists lists)
 {
     __shared__ float4 tile[2][256];
-    __shared__ int nbr[18];
+    __shared__ int nbr[kGridLds];
     const int c = blockIdx.x, tid = threadIdx.x;
     const int tb = k.cell_start[c], te = k.cell_start[c + 1];
     if (tb < 0 || te < tb || te > k.n) return;
@@ -1482,7 +1579,7 @@ __global__ void __launch_bounds__(256) p2p_wg_kernel(P2PArgs k, Lists lists)
     const int ny = (int)gridDim.y, y = (int)blockIdx.y;
     if (y > 0 && tb + 256 * y >= te) return;
     if constexpr (__is_same(Lists, GridLists)) lists.nbr = nbr;
-    lists.bind(c);
+    lists.bind(k, c);
     int lo, hi;
     lists.range(c, lo, hi);
     const float eps2 = in_vgpr(k.eps2);
