@@ -474,7 +474,7 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
                     help="timed steps (default: 10; 200 for plummer65536, 2000 for disk4096, "
-                         "whose calls take about a millisecond or less)")
+                         "100 for --near-grid, whose calls take milliseconds or less)")
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed warm-up steps (default: 2; 50 for plummer65536 and 200 for "
                          "disk4096, so that the shader clock has ramped up)")
@@ -514,6 +514,8 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
     short = {"plummer65536": (200, 50), "disk4096": (2000, 200)}
     steps0, warm0 = short.get(args.workload, (10, 2)) if args.n is None else (10, 2)
+    if args.near_grid:
+        steps0, warm0 = 100, 20  # a call takes milliseconds: warm the clock up first
     if args.steps is None:
         args.steps = steps0
     if args.warmup is None:

@@ -250,7 +250,7 @@ int wide_cells(int64_t n, int64_t ncell, bool *wide)
 
 // Largest N the automatic plan gives to NBODY_MODE_SMALL; pair-symmetric bands
 // (scratch permitting) take every N above it.
-constexpr int64_t kSmallMaxN = 6656;
+constexpr int64_t kSmallMaxN = 6144;
 // Largest N whose automatic band is 256 bodies (4 targets per lane): many
 // small work items fill the GPU there; above it, 512-2048 with 8 per lane.
 constexpr int64_t kBand256MaxN = 36863;
@@ -292,12 +292,14 @@ int pass_band(int64_t q, int64_t nb, int64_t passes) { return (int)(q * nb / pas
 
 // Automatic layout, chosen by measurement on MI355X (layout sweeps of the
 // five workloads and of uniform cubes from N = 1024 to 131072):
-//   - up to N = 6656 (small mode measured fastest at 6144, 256-body pair bands
-//     at 7168), the small-N kernel (one kernel per evaluation or step): 4
-//     targets per workgroup to N = 2048, 8 to 6144, 16 above;
+//   - up to N = 6144, the small-N kernel (one kernel per evaluation or step;
+//     round-robin on uniform cubes: 20.9 us against 25.3 for 256-body pair
+//     bands at 6144, but 28.2 against 25.4 at 6656, where its last 1024-body
+//     tile is half empty): 4 targets per workgroup to N = 2048, 8 above;
 //   - above it, pair-symmetric bands when their scratch fits: 256 bodies with
-//     4 targets per lane to N = 36863 (2 % ahead of 512 with 8 per lane at
-//     32768, 2 % behind at 40960, timed round-robin), then the largest band
+//     4 targets per lane to N = 36863 (tied with 512 with 8 per lane at 32768;
+//     from 36864 to 49152 within +-3 %, one way on one box and the other way on
+//     another, in round-robin timing), then the largest band
 //     that still yields at least 64 work items per compute unit, with 8
 //     targets per lane;
 //   - otherwise one-sided tiles with the LDS broadcast and one target per lane:

@@ -340,7 +340,9 @@ int nbody_plan_for(int64_t N, int want_pot, nbody_plan *out);
  * duration on the stream. Further launches of the same call (later passes or
  * steps) are not bracketed. NULL, NULL switches the hook off. The events are
  * created and owned by the caller (on the device the calls run on); the
- * library only records them. NBODY_EINVAL if exactly one of them is NULL.
+ * library only records them, so switch the hook off before destroying them
+ * (a call that records a destroyed event fails with NBODY_EHIP). The hook is
+ * per host thread. NBODY_EINVAL if exactly one of them is NULL.
  */
 int nbody_time_kernel(hipEvent_t start, hipEvent_t stop);
 

@@ -388,13 +388,13 @@ def test_scratch_allocation_failure_reported_and_recovered(nb):
 
 
 def test_auto_plan_modes(nb):
-    """Small-N kernel up to N = 6656, pair-symmetric bands above (256 bodies and 4 targets per
+    """Small-N kernel up to N = 6144, pair-symmetric bands above (256 bodies and 4 targets per
     lane to N = 36863, larger bands and 8 per lane from there), with the measured targets per
     workgroup in small mode."""
-    for n, tw in ((1, 4), (2048, 4), (2049, 8), (6144, 8), (6145, 16), (6656, 16)):
+    for n, tw in ((1, 4), (2048, 4), (2049, 8), (6144, 8)):
         p = nb.nbody_plan_for(n)
         assert p.mode == nb.MODE_SMALL and p.splits == 1 and p.tpl == tw and p.wg == 256, n
-    for n in (6657, 18432, 36863):
+    for n in (6145, 6656, 18432, 36863):
         p = nb.nbody_plan_for(n)
         assert p.mode == nb.MODE_PAIRS and p.band == 256 and p.tpl == 4, n
     for n, band in ((36864, 512), (49152, 512), (65536, 512), (131072, 512), (300007, 1024), (1 << 20, 2048)):
