@@ -94,6 +94,10 @@ class Oracle:
                                      ctypes.c_int64, ctypes.c_int64, _c_int64_p, ctypes.c_int64,
                                      _c_double_p, _c_double_p, _c_double_p, _c_double_p]
         lib.oracle_shard.restype = ctypes.c_int
+        lib.oracle_near_tree.argtypes = [_c_double_p, ctypes.c_int64, ctypes.c_double,
+                                         ctypes.c_int64, _c_int64_p, ctypes.c_int64, _c_double_p,
+                                         _c_double_p, _c_double_p, _c_double_p]
+        lib.oracle_near_tree.restype = ctypes.c_int
         self._lib = lib
 
     def num_threads(self) -> int:
@@ -232,6 +236,31 @@ class Oracle:
         lo32 = [as_f32(v) for v in lo]
         return self.near_grid_exact(pos, as_f32(eps2), lo32, as_f32(h), dims, targets)
 
+    def near_tree_exact(self, pos, eps2: float, leaf_size: int, targets=None) -> dict:
+        """Near field over the leaves of the Morton-order octree (leaves of at most leaf_size
+        bodies; leaves near when their closed cubes meet), by definition."""
+        p = _bodies64(pos)
+        n = p.shape[0]
+        if targets is None:
+            t, nt = None, n
+        else:
+            t = np.ascontiguousarray(targets, dtype=np.int64)
+            nt = t.shape[0]
+        acc = np.zeros((nt, 3))
+        pot = np.zeros(nt)
+        ba = np.zeros(nt)
+        bp = np.zeros(nt)
+        rc = self._lib.oracle_near_tree(_ptr(p), n, float(eps2), int(leaf_size),
+                                        _ptr(t, _c_int64_p), nt, _ptr(acc), _ptr(pot), _ptr(ba),
+                                        _ptr(bp))
+        if rc != 0:
+            raise ValueError("oracle_near_tree rejected its arguments")
+        return {"acc": acc, "pot": pot, "bound_a": ba, "bound_p": bp}
+
+    def near_tree(self, pos, eps2, leaf_size, targets=None) -> dict:
+        """As near_tree_exact with eps2 rounded to float32 first (the GPU's value)."""
+        return self.near_tree_exact(pos, as_f32(eps2), leaf_size, targets)
+
     def shard_exact(self, pos, eps2: float, band: int, shard: int, nshards: int,
                     targets=None) -> dict:
         """One shard's part of the direct sum (the pairs of the bands it owns, see
@@ -325,3 +354,7 @@ def near_grid(pos, eps2, lo, h, dims, targets=None) -> dict:
 
 def shard(pos, eps2, band, shard_index, nshards, targets=None) -> dict:
     return get().shard(pos, eps2, band, shard_index, nshards, targets)
+
+
+def near_tree(pos, eps2, leaf_size, targets=None) -> dict:
+    return get().near_tree(pos, eps2, leaf_size, targets)

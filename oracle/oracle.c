@@ -39,8 +39,12 @@
  * Parity pins (tests/test_oracle.py): N = 1 and N = 2 closed forms, a regular
  * polygon (ring) closed form, zero force at the centre of symmetric sets,
  * Newton's third law, exact power-of-two scaling, a 50-digit decimal brute
- * force for small N, and the free-particle Euler step. The multi-step energy
- * drift (oracle_energy over a trajectory) has no closed form: parity unpinned.
+ * force for small N, and the free-particle Euler step. Near fields: lists that
+ * cover every cell give the full sum; the grid neighbourhood equals explicit
+ * lists; the tree with one leaf is the full sum, on a full octree it is the grid
+ * near field of the leaf lattice, and on a two-level tree it equals lists derived
+ * by hand. The multi-step energy drift (oracle_energy over a trajectory) has no
+ * closed form: parity unpinned.
  *
  * Layouts: pos is n x 4 doubles (x, y, z, m); vel is n x 4 doubles
  * (vx, vy, vz, unused). Return value 0 on success, -1 on bad arguments.
@@ -394,4 +398,137 @@ int oracle_near_grid(const double *pos, int64_t n, double eps2, const double *lo
     }
     free(cell);
     return 0;
+}
+
+/*
+ * Near field over the leaves of an octree in Morton order: the all-pairs sum as the
+ * near part of a hierarchical method (GPU Gems 3 ch. 31 study page, section 6; the
+ * tree codes of Nakasato "スライド 1", No.31-38). The tree itself is not on the
+ * pages; it is defined here as follows, every decision taken in float32 (an integer
+ * decided by floating point is decided in the kernel's precision):
+ *   root cube: lo_d = the smallest coordinate d of any body; side = the largest of
+ *     (largest coordinate d - lo_d) over d, or 1 when that is not positive;
+ *   cell of a body per axis at level 10: c_d = floor((x_d - lo_d) * (1024 / side)),
+ *     clamped to [0, 1023] (a NaN goes to 0);
+ *   Morton key: bit 3b + d of the key is bit b of c_d (d = 0, 1, 2 for x, y, z);
+ *   node (L, p), L = 0 .. 10: the bodies whose key shifted right by 3 (10 - L) is p;
+ *   leaf of a body: the node on its path with the smallest L holding at most
+ *     leaf_size bodies, or its level-10 node when there is none;
+ *   cube of node (L, p): per axis the closed interval [o_d, o_d + 2^(10 - L)] in
+ *     level-10 units, where o_d / 2^(10 - L) is made of the bits 3b + d of p;
+ *   near field of body i: the sum over every body j whose leaf's cube meets the cube
+ *     of i's leaf (touching counts; i's own leaf is included, so j = i is).
+ * Sums as oracle_accel, over those j in ascending order, for the listed targets
+ * (NULL: all n). leaf_size >= 1. Returns -1 on bad arguments.
+ */
+static int cmp_u32(const void *a, const void *b)
+{
+    const uint32_t x = *(const uint32_t *)a, y = *(const uint32_t *)b;
+    return x < y ? -1 : (x > y ? 1 : 0);
+}
+
+/* Number of sorted keys in [a, b). */
+static int64_t keys_in(const uint32_t *sorted, int64_t n, uint64_t a, uint64_t b)
+{
+    int64_t l0 = 0, h0 = n, l1 = 0, h1 = n;
+    while (l0 < h0) {
+        const int64_t m = l0 + (h0 - l0) / 2;
+        if ((uint64_t)sorted[m] < a) l0 = m + 1; else h0 = m;
+    }
+    while (l1 < h1) {
+        const int64_t m = l1 + (h1 - l1) / 2;
+        if ((uint64_t)sorted[m] < b) l1 = m + 1; else h1 = m;
+    }
+    return l1 - l0;
+}
+
+int oracle_near_tree(const double *pos, int64_t n, double eps2, int64_t leaf_size,
+                     const int64_t *targets, int64_t nt, double *acc, double *pot,
+                     double *bound_a, double *bound_p)
+{
+    if (!pos || n < 0 || nt < 0 || !(eps2 > 0.0) || leaf_size < 1) return -1;
+    if (nt > 0 && (!acc || !pot || !bound_a || !bound_p)) return -1;
+    const int64_t nn = n > 0 ? n : 1;
+    uint32_t *key = (uint32_t *)malloc((size_t)nn * sizeof(uint32_t));
+    uint32_t *sorted = (uint32_t *)malloc((size_t)nn * sizeof(uint32_t));
+    int64_t *box = (int64_t *)malloc((size_t)nn * 4 * sizeof(int64_t)); /* o_x, o_y, o_z, size */
+    if (!key || !sorted || !box) {
+        free(key); free(sorted); free(box);
+        return -1;
+    }
+    float lo[3] = {0.0f, 0.0f, 0.0f}, hi[3] = {0.0f, 0.0f, 0.0f};
+    for (int d = 0; d < 3; ++d) {
+        for (int64_t j = 0; j < n; ++j) {
+            const float x = (float)pos[4 * j + d];
+            if (j == 0 || x < lo[d]) lo[d] = x;
+            if (j == 0 || x > hi[d]) hi[d] = x;
+        }
+    }
+    float side = 0.0f;
+    for (int d = 0; d < 3; ++d) {
+        const float ext = hi[d] - lo[d];
+        if (ext > side) side = ext;
+    }
+    if (!(side > 0.0f)) side = 1.0f;
+    const float inv = 1024.0f / side;
+    for (int64_t j = 0; j < n; ++j) {
+        uint32_t k = 0;
+        for (int d = 0; d < 3; ++d) {
+            float f = floorf(((float)pos[4 * j + d] - lo[d]) * inv);
+            if (!(f >= 0.0f)) f = 0.0f;
+            if (f > 1023.0f) f = 1023.0f;
+            const uint32_t c = (uint32_t)f;
+            for (int b = 0; b < 10; ++b) k |= ((c >> b) & 1u) << (3 * b + d);
+        }
+        key[j] = k;
+        sorted[j] = k;
+    }
+    qsort(sorted, (size_t)n, sizeof(uint32_t), cmp_u32);
+    for (int64_t j = 0; j < n; ++j) {
+        int level = 10;
+        for (int L = 0; L <= 10; ++L) {
+            const int s = 3 * (10 - L);
+            const uint64_t p = key[j] >> s;
+            if (keys_in(sorted, n, p << s, (p + 1) << s) <= leaf_size) {
+                level = L;
+                break;
+            }
+        }
+        const int s = 3 * (10 - level);
+        const uint32_t p = key[j] >> s;
+        for (int d = 0; d < 3; ++d) {
+            int64_t o = 0;
+            for (int b = 0; b < level; ++b) o |= (int64_t)((p >> (3 * b + d)) & 1u) << b;
+            box[4 * j + d] = o << (10 - level);
+        }
+        box[4 * j + 3] = (int64_t)1 << (10 - level);
+    }
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 16) reduction(| : bad)
+    for (int64_t t = 0; t < nt; ++t) {
+        const int64_t i = targets ? targets[t] : t;
+        if (i < 0 || i >= n) {
+            bad = 1;
+            continue;
+        }
+        target_sums s = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+        const int64_t *bi = box + 4 * i;
+        for (int64_t j = 0; j < n; ++j) {
+            const int64_t *bj = box + 4 * j;
+            int near = 1;
+            for (int d = 0; d < 3; ++d)
+                if (bj[d] > bi[d] + bi[3] || bi[d] > bj[d] + bj[3]) near = 0;
+            if (near) add_pair(pos, i, j, eps2, &s);
+        }
+        acc[3 * t] = s.ax;
+        acc[3 * t + 1] = s.ay;
+        acc[3 * t + 2] = s.az;
+        pot[t] = s.pp;
+        bound_a[t] = s.sa;
+        bound_p[t] = s.sp;
+    }
+    free(key);
+    free(sorted);
+    free(box);
+    return bad ? -1 : 0;
 }

@@ -581,6 +581,139 @@ def pin_shards_add_up_to_direct_sum(orc):
                     raise AssertionError(f"n={n} S={S}: shards do not add up in {k}")
 
 
+# ------------------------------------------------------------------ near field on octree leaves
+
+def pin_near_tree_one_leaf_equals_direct_sum(orc):
+    """With leaf_size >= N the root is the only leaf: the tree near field is the whole direct
+    sum, bit for bit (same terms, same order)."""
+    rng = np.random.Generator(np.random.PCG64(21))
+    for n in (1, 2, 37, 400):
+        x = rng.uniform(-1, 1, size=(n, 3)).astype(np.float32).astype(np.float64)
+        pos = _bodies(x, rng.uniform(0.1, 2.0, size=n))
+        full = orc.accel_exact(pos, 1e-3)
+        for leaf in (n, n + 5):
+            r = orc.near_tree_exact(pos, 1e-3, leaf)
+            for k in ("acc", "pot", "bound_a", "bound_p"):
+                if not np.array_equal(r[k], full[k]):
+                    raise AssertionError(f"one leaf (N={n}, leaf_size={leaf}): {k} differs")
+
+
+def _lattice(cells, k, seed, zcells=None):
+    """k bodies per cell of a lattice of `cells` cubic cells per axis on [0, 1]^3 (zcells along
+    z: a box of height zcells / cells), placed inside their cells away from the faces, plus a
+    body at (0, 0, 0) and one at x = y = 1 inside the top layer of cells, so the tree's root
+    cube is [0, 1]^3 and both corner bodies fall in lattice cells."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    zc = cells if zcells is None else zcells
+    pts = []
+    for c in range(cells):
+        for b in range(cells):
+            for a in range(zc):
+                for _ in range(k):
+                    u = rng.uniform(0.15, 0.85, size=3)
+                    pts.append(((c + u[0]) / cells, (b + u[1]) / cells, (a + u[2]) / cells))
+    pts += [(0.0, 0.0, 0.0), (1.0, 1.0, 1.0 if zc == cells else (zc - 0.5) / cells)]
+    x = np.asarray(pts, dtype=np.float32).astype(np.float64)
+    return _bodies(x, rng.uniform(0.5, 1.5, size=x.shape[0]))
+
+
+def pin_near_tree_full_octree_equals_grid(orc):
+    """k = 2 bodies in every cell of an 8^3 lattice (the two corner cells hold 3): every cell
+    holds at most leaf_size = 3 bodies and every cell of the 4^3 lattice above it 16 or more,
+    so the leaves are exactly the 8^3 cells and the tree near field is the 27-cell grid near
+    field of that lattice (independent definition), bit for bit; with leaf_size = 17 the
+    leaves are the 4^3 cells. On a box half as high (8 x 8 x 4 cells) the cells stay cubic:
+    the root cube's side is the largest extent."""
+    for cells, zc, leaf, dims in ((8, 8, 3, (8, 8, 8)), (8, 8, 17, (4, 4, 4)),
+                                  (8, 4, 3, (8, 8, 4))):
+        pos = _lattice(cells, 2, 30 + leaf + zc, zcells=zc)
+        r = orc.near_tree_exact(pos, 1e-3, leaf)
+        g = orc.near_grid_exact(pos, 1e-3, (0.0, 0.0, 0.0), 1.0 / dims[0], dims)
+        for k in ("acc", "pot", "bound_a", "bound_p"):
+            if not np.array_equal(r[k], g[k]):
+                raise AssertionError(f"full octree (leaf_size={leaf}, {dims}): {k} differs "
+                                     "from the grid")
+
+
+def pin_near_tree_mixed_levels(orc):
+    """Leaves at two levels, neighbour sets derived by hand. The octant [0, 1/2]^3 holds two
+    bodies in each of its eight level-2 cells (16 > leaf_size = 2: it splits; its cells are
+    leaves); each of the other seven octants holds one body (a level-1 leaf). All eight
+    octants meet at the centre, so every octant touches every other; a level-2 cell
+    (a, b, c), a, b, c in {0, 1}, touches the octant (o_x, o_y, o_z) iff a = 1 wherever
+    o_x = 1, and likewise for b and c; the eight level-2 cells all meet at (1/4, 1/4, 1/4).
+    The expected sums come from explicit lists (another summation order: to 1e-13)."""
+    rng = np.random.Generator(np.random.PCG64(41))
+    pts, cell_of = [], []
+    for a in (0, 1):
+        for b in (0, 1):
+            for c in (0, 1):
+                for t in range(2):
+                    if (a, b, c, t) == (0, 0, 0, 0):
+                        pts.append((0.0, 0.0, 0.0))  # the root's lower corner
+                    else:
+                        u = rng.uniform(0.15, 0.85, size=3)
+                        pts.append(((a + u[0]) / 4, (b + u[1]) / 4, (c + u[2]) / 4))
+                    cell_of.append(("d", a, b, c))
+    octants = [(ox, oy, oz) for ox in (0, 1) for oy in (0, 1) for oz in (0, 1)
+               if (ox, oy, oz) != (0, 0, 0)]
+    for o in octants:
+        if o == (1, 1, 1):
+            pts.append((1.0, 1.0, 1.0))  # the root's upper corner
+        else:
+            u = rng.uniform(0.1, 0.9, size=3)
+            pts.append(tuple((o[d] + u[d]) / 2 for d in range(3)))
+        cell_of.append(("s",) + o)
+    x = np.asarray(pts, dtype=np.float32).astype(np.float64)
+    pos = _bodies(x, rng.uniform(0.5, 1.5, size=x.shape[0]))
+    groups = sorted(set(cell_of))
+    members = {g: [i for i, c in enumerate(cell_of) if c == g] for g in groups}
+
+    def touches(g, h):
+        if g[0] == h[0]:
+            return True  # dense cells meet at (1/4, 1/4, 1/4); octants at the centre
+        dense, sparse = (g, h) if g[0] == "d" else (h, g)
+        return all(dense[1 + d] == 1 for d in range(3) if sparse[1 + d] == 1)
+
+    order = [i for g in groups for i in members[g]]
+    start = np.cumsum([0] + [len(members[g]) for g in groups]).astype(np.int32)
+    lists = [[gi2 for gi2, h in enumerate(groups) if touches(g, h)] for g in groups]
+    r_list = orc.p2p_exact(pos[order], 1e-3, start, *_csr(lists))
+    r_tree = orc.near_tree_exact(pos, 1e-3, 2)
+    back = np.empty(len(order), np.int64)
+    back[order] = np.arange(len(order))
+    err = np.linalg.norm(r_list["acc"][back] - r_tree["acc"], axis=1)
+    if np.any(err > 1e-13 * r_tree["bound_a"] + 1e-300):
+        raise AssertionError(f"mixed-level tree vs hand lists: max err {np.max(err):.3e}")
+    _close(r_list["pot"][back], r_tree["pot"], 1e-13 * np.max(r_tree["bound_p"]),
+           "mixed-level tree vs hand lists p")
+
+
+def pin_near_tree_third_law(orc):
+    """Leaf neighbourhood is symmetric (two leaves are near or not, whichever is the
+    target), so the near-field forces cancel in pairs: sum_i m_i a_i = 0 to 1e-12 of
+    sum_i m_i B_i, on clustered bodies whose leaves sit at many levels."""
+    rng = np.random.Generator(np.random.PCG64(51))
+    core = rng.normal(0.0, 0.05, size=(300, 3))
+    halo = rng.uniform(-1.0, 1.0, size=(200, 3))
+    x = np.concatenate([core, halo]).astype(np.float32).astype(np.float64)
+    m = rng.uniform(0.5, 1.5, size=x.shape[0])
+    pos = _bodies(x, m)
+    for leaf in (1, 4, 16):
+        r = orc.near_tree_exact(pos, 1e-4, leaf)
+        tot = np.sum(m[:, None] * r["acc"], axis=0)
+        scale = np.sum(m * r["bound_a"])
+        if np.linalg.norm(tot) > 1e-12 * scale:
+            raise AssertionError(f"tree third law (leaf_size={leaf}): |sum m a| = "
+                                 f"{np.linalg.norm(tot):.3e} against {scale:.3e}")
+        # a finer tree keeps fewer neighbours: the sum of the P scales cannot grow
+        if leaf > 1:
+            r1 = orc.near_tree_exact(pos, 1e-4, 1)
+            if np.sum(r1["bound_p"]) > np.sum(r["bound_p"]) * (1 + 1e-12):
+                raise AssertionError("tree: leaf_size 1 keeps more neighbours than "
+                                     f"leaf_size {leaf}")
+
+
 ALL_PINS = [
     pin_single_body,
     pin_two_body_345,
@@ -608,4 +741,8 @@ ALL_PINS = [
     pin_shard_items_cover_each_pair_once,
     pin_shard_single_equals_direct_sum,
     pin_shards_add_up_to_direct_sum,
+    pin_near_tree_one_leaf_equals_direct_sum,
+    pin_near_tree_full_octree_equals_grid,
+    pin_near_tree_mixed_levels,
+    pin_near_tree_third_law,
 ]

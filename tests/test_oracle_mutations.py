@@ -56,6 +56,20 @@ MUTATIONS = [
      "if (2 * up <= nb) return bi;"),
     ("shard: band ranges overlap", "b1 = (shard + 1) * nb / nshards;",
      "b1 = (shard + 1) * nb / nshards + 1;"),
+    ("near tree: open cubes (face neighbours dropped)",
+     "if (bj[d] > bi[d] + bi[3] || bi[d] > bj[d] + bj[3]) near = 0;",
+     "if (bj[d] >= bi[d] + bi[3] || bi[d] >= bj[d] + bj[3]) near = 0;"),
+    ("near tree: leaf holds fewer than leaf_size",
+     "if (keys_in(sorted, n, p << s, (p + 1) << s) <= leaf_size) {",
+     "if (keys_in(sorted, n, p << s, (p + 1) << s) < leaf_size) {"),
+    ("near tree: deepest level instead of the first",
+     "                level = L;\n                break;", "                level = L;"),
+    ("near tree: root side is the smallest extent", "if (ext > side) side = ext;",
+     "if (side == 0.0f || ext < side) side = ext;"),
+    ("near tree: top face not clamped into the last cell", "if (f > 1023.0f) f = 1023.0f;",
+     "if (f > 1024.0f) f = 1024.0f;"),
+    ("near tree: leaf corner one level off", "box[4 * j + d] = o << (10 - level);",
+     "box[4 * j + d] = o << (9 - level);"),
 ]
 
 
