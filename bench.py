@@ -394,6 +394,48 @@ def near_grid_bench(nb, w, pos, args) -> int:
     return 0
 
 
+def near_tree_bench(nb, w, pos, args) -> int:
+    """Time nbody_near_tree (bounds, keys, sort, leaves, lists, near-field kernel) with leaves
+    of at most args.near_tree bodies; one JSON line (not the contract line). Each call waits
+    once on the stream for the list lengths, so a call's time includes that round trip."""
+    import torch
+
+    leaf = args.near_tree
+    n = w.n
+    acc = torch.empty_like(pos)
+    pot = torch.empty(n, dtype=torch.float32, device=pos.device)
+    stream = torch.cuda.current_stream()
+    st = nb.nbody_tree_stats()
+    for _ in range(max(1, args.warmup)):
+        nb.nbody_near_tree(pos, n, float(w.eps2), leaf, acc, pot, st, stream)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    ks = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    for e in ks:
+        e.record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for k in range(args.steps):
+        nb.nbody_time_kernel(ks[2 * k], ks[2 * k + 1])
+        nb.nbody_near_tree(pos, n, float(w.eps2), leaf, acc, pot, st, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / args.steps
+    nb.nbody_time_kernel(None, None)
+    ms = e0.elapsed_time(e1) / args.steps
+    kms = sum(ks[2 * k].elapsed_time(ks[2 * k + 1]) for k in range(args.steps)) / args.steps
+    terms = st.pair_terms
+    print(json.dumps({"near_tree": {"workload": args.workload, "N": n, "leaf_size": leaf,
+                                    **st.as_dict(), "bodies_per_leaf": round(n / st.leaves, 2),
+                                    "ms": round(ms, 4), "wall_ms": round(wall, 4),
+                                    "G_terms_per_s": round(terms / ms / 1e6, 2),
+                                    "kernel_ms": round(kms, 4),
+                                    "kernel_G_terms_per_s": round(terms / kms / 1e6, 2),
+                                    "build_ms": round(ms - kms, 4)}}), flush=True)
+    return 0
+
+
 def shard_interactions(n: int, band: int, shard: int, nshards: int) -> int:
     """Interactions (ordered pairs, N^2 in all) that shard `shard` of `nshards` evaluates:
     its bands' diagonal items one-sided (self pairs included), the other items for both
@@ -474,7 +516,7 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
                     help="timed steps (default: 10; 200 for plummer65536, 2000 for disk4096, "
-                         "100 for --near-grid, whose calls take milliseconds or less)")
+                         "100 for --near-grid and --near-tree, whose calls take milliseconds)")
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed warm-up steps (default: 2; 50 for plummer65536 and 200 for "
                          "disk4096, so that the shader clock has ramped up)")
@@ -501,6 +543,9 @@ def main(argv=None) -> int:
     ap.add_argument("--near-grid", type=int, default=0, metavar="D",
                     help="only time nbody_near_grid on a D^3 grid over [-1, 1]^3 (near field; "
                          "prints its own JSON line, no contract line)")
+    ap.add_argument("--near-tree", type=int, default=0, metavar="LEAF",
+                    help="only time nbody_near_tree with leaves of at most LEAF bodies (near "
+                         "field over octree leaves; prints its own JSON line, no contract line)")
     ap.add_argument("--shard", type=int, default=0, metavar="S",
                     help="only time nbody_accel_shard for each of S shards of the workload's "
                          "evaluation (one GPU's share of an S-GPU split) and the merge of one "
@@ -514,7 +559,7 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
     short = {"plummer65536": (200, 50), "disk4096": (2000, 200)}
     steps0, warm0 = short.get(args.workload, (10, 2)) if args.n is None else (10, 2)
-    if args.near_grid:
+    if args.near_grid or args.near_tree:
         steps0, warm0 = 100, 20  # a call takes milliseconds: warm the clock up first
     if args.steps is None:
         args.steps = steps0
@@ -566,6 +611,8 @@ def main(argv=None) -> int:
         return sweep(nb, w, pos, vel, acc, pot, args)
     if args.near_grid:
         return near_grid_bench(nb, w, pos, args)
+    if args.near_tree:
+        return near_tree_bench(nb, w, pos, args)
     if args.shard:
         return shard_bench(nb, w, pos, args)
 

@@ -45,6 +45,15 @@ class nbody_plan(ctypes.Structure):
                 "passes": self.passes}
 
 
+class nbody_tree_stats(ctypes.Structure):
+    _fields_ = [("leaves", ctypes.c_int64), ("list_entries", ctypes.c_int64),
+                ("pair_terms", ctypes.c_int64)]
+
+    def as_dict(self) -> dict:
+        return {"leaves": self.leaves, "list_entries": self.list_entries,
+                "pair_terms": self.pair_terms}
+
+
 # torch (device memory and streams) is imported first: its bundled HIP runtime
 # carries the same soname (libamdhip64.so.7) the library links against, so the
 # loader binds the library to the runtime already in the process instead of
@@ -69,6 +78,8 @@ _lib.nbody_diagnostics.argtypes = [_vp, _vp, _vp, _i64, _f32, _vp, _vp]
 _lib.nbody_p2p.argtypes = [_vp, _i64, _f32, _vp, ctypes.c_int32, _vp, _vp, _i64, _vp, _vp, _vp]
 _lib.nbody_near_grid.argtypes = [_vp, _i64, _f32, ctypes.POINTER(ctypes.c_float), _f32,
                                  ctypes.POINTER(ctypes.c_int32), _vp, _vp, _vp]
+_lib.nbody_near_tree.argtypes = [_vp, _i64, _f32, _i64, _vp, _vp, ctypes.POINTER(nbody_tree_stats),
+                                 _vp]
 _lib.nbody_accel_soa.argtypes = [_vp, _vp, _vp, _vp, _i64, _f32, _vp, _vp, _vp, _vp, _vp]
 _lib.nbody_step_soa.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _f32, _f32, _i64, _vp]
 _lib.nbody_accel_shard.argtypes = [_vp, _i64, _f32, ctypes.c_int32, ctypes.c_int32, _int,
@@ -79,14 +90,14 @@ _lib.nbody_release_workspace.argtypes = []
 _lib.nbody_version.restype = ctypes.c_char_p
 for _f in ("nbody_accel", "nbody_accel_plan", "nbody_step", "nbody_step_plan",
            "nbody_step_noalloc", "nbody_time_kernel", "nbody_accel_soa", "nbody_step_soa", "nbody_accel_shard", "nbody_shard_finish",
-           "nbody_p2p", "nbody_near_grid", "nbody_diagnostics", "nbody_plan_for",
-           "nbody_release_workspace"):
+           "nbody_p2p", "nbody_near_grid", "nbody_near_tree", "nbody_diagnostics",
+           "nbody_plan_for", "nbody_release_workspace"):
     getattr(_lib, _f).restype = _int
 
 EXPORTS = ("nbody_accel", "nbody_accel_plan", "nbody_step", "nbody_step_plan",
            "nbody_step_noalloc", "nbody_time_kernel", "nbody_accel_soa", "nbody_step_soa",
            "nbody_accel_shard", "nbody_shard_finish", "nbody_p2p", "nbody_near_grid",
-           "nbody_diagnostics", "nbody_plan_for", "nbody_last_error", "nbody_release_workspace",
+           "nbody_near_tree", "nbody_diagnostics", "nbody_plan_for", "nbody_last_error", "nbody_release_workspace",
            "nbody_version")
 DIAG_FIELDS = ("kinetic", "potential", "total", "momentum", "angular_momentum", "mass",
                "centre_of_mass")
@@ -237,6 +248,15 @@ def nbody_near_grid(pos, N: int, eps2: float, lo, h: float, dims, acc_out, pot_o
     return _check(rc, "nbody_near_grid") if check else rc
 
 
+def nbody_near_tree(pos, N: int, eps2: float, leaf_size: int, acc_out, pot_out=None,
+                    stats: nbody_tree_stats | None = None, stream=None, check: bool = True) -> int:
+    """stats: an nbody_tree_stats to fill (host), or None."""
+    rc = _lib.nbody_near_tree(_ptr(pos), int(N), float(eps2), int(leaf_size), _ptr(acc_out),
+                              _ptr(pot_out), ctypes.byref(stats) if stats is not None else None,
+                              _stream(stream))
+    return _check(rc, "nbody_near_tree") if check else rc
+
+
 def nbody_diagnostics(pos, vel, N: int, eps2: float, out, pot=None, stream=None,
                       check: bool = True) -> int:
     """out: device buffer of 13 float64 (one nbody_diag); pot: device potentials or None."""
@@ -301,6 +321,21 @@ def step(pos, vel, dt: float, eps2: float, nsteps: int = 1, plan=None):
         else:
             nbody_step_plan(pos, vel, pos.shape[0], dt, eps2, nsteps, plan)
     return pos, vel
+
+
+def near_tree(pos, eps2: float, leaf_size: int, pot: bool = True):
+    """Near field over octree leaves of at most leaf_size bodies, on the current stream:
+    (acc (N, 4), pot (N,) or None, stats dict). Waits once on the stream for the build."""
+    import torch
+
+    _bodies(pos, "pos")
+    n = pos.shape[0]
+    acc = torch.empty_like(pos)
+    p = torch.empty(n, dtype=torch.float32, device=pos.device) if pot else None
+    st = nbody_tree_stats()
+    with torch.cuda.device(pos.device):
+        nbody_near_tree(pos, n, eps2, leaf_size, acc, p, st)
+    return acc, p, st.as_dict()
 
 
 def unpack_diag(vals) -> dict:

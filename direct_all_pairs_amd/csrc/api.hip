@@ -7,9 +7,11 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstring>
 #include <map>
 #include <mutex>
 #include <string>
+#include <tuple>
 #include <utility>
 
 // The library is built with hidden symbol visibility; only the C ABI declared
@@ -103,7 +105,9 @@ struct Scratch {
     void *ptr = nullptr;
     size_t bytes = 0;
 };
-std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
+// Keyed by (device, stream, slot); slot 1 holds the interaction lists of
+// nbody_near_tree, whose size is known only after the first part of the build.
+std::map<std::tuple<int, hipStream_t, int>, Scratch> g_scratch;
 
 // Held by every entry point that uses scratch, from taking the block until its
 // last launch is enqueued, and by nbody_release_workspace: no host thread can
@@ -159,7 +163,7 @@ struct FixedScratchScope {
 // Returns scratch of at least `bytes` for (device, stream). Growing frees the
 // old block first; hipFree waits for the device, so work still queued on the
 // old block finishes before it is released.
-int scratch_get(int dev, hipStream_t stream, size_t bytes, void **out)
+int scratch_get(int dev, hipStream_t stream, size_t bytes, void **out, int slot = 0)
 {
     if (g_fixed.ptr) {
         if (bytes > g_fixed.bytes)
@@ -169,7 +173,7 @@ int scratch_get(int dev, hipStream_t stream, size_t bytes, void **out)
         return NBODY_OK;
     }
     std::lock_guard<std::mutex> lk(g_mu);
-    Scratch &s = g_scratch[{dev, stream}];
+    Scratch &s = g_scratch[std::make_tuple(dev, stream, slot)];
     if (s.bytes < bytes) {
         if (s.ptr) {
             hipError_t e = hipFree(s.ptr);
@@ -224,6 +228,8 @@ constexpr int kMaxSplits = 4096;
 // Most cells a uniform grid of nbody_near_grid may have (one 32-bit key per body
 // and one start index per cell).
 constexpr int64_t kMaxGridCells = (int64_t)1 << 28;
+// Most bodies nbody_near_tree takes (its scans run over N + 1 int entries).
+constexpr int64_t kMaxTreeN = (int64_t)1 << 30;
 
 // Near field: two waves per cell unless the cells are large (at least 96 bodies
 // on average) and few (fewer than 12 per CU): then 256-thread workgroups sharing
@@ -1071,6 +1077,107 @@ int nbody_near_grid(const nbody_f4 *pos, int64_t N, float eps2, const float lo[3
             stream, [&] { return nbk::launch_p2p_grid(pot_out != nullptr, wide, a, g, stream); });
     }
     if (e != hipSuccess) return hip_fail(e, "near-grid launch");
+    return ok();
+}
+
+int nbody_near_tree(const nbody_f4 *pos, int64_t N, float eps2, int64_t leaf_size,
+                    nbody_f4 *acc_out, float *pot_out, nbody_tree_stats *stats,
+                    hipStream_t stream)
+{
+    int rc = check_n(N);
+    if (rc != NBODY_OK) return rc;
+    if (N > kMaxTreeN) return fail(NBODY_EINVAL, "N=%lld exceeds 2^30", (long long)N);
+    if (leaf_size < 1) return fail(NBODY_EINVAL, "leaf_size=%lld must be >= 1", (long long)leaf_size);
+    if (stats) *stats = nbody_tree_stats{0, 0, 0};
+    if (N == 0) return ok();
+    if (!pos) return fail(NBODY_EINVAL, "pos_xyzm is NULL");
+    if (!acc_out) return fail(NBODY_EINVAL, "acc_out is NULL");
+    if (!eps2_ok(eps2))
+        return eps2_fail(eps2);
+    if (!aligned(pos, 16) || !aligned(acc_out, 16))
+        return fail(NBODY_EALIGN, "pos_xyzm and acc_out must be 16-byte aligned");
+    if (pot_out && !aligned(pot_out, 4)) return fail(NBODY_EALIGN, "pot_out is not 4-byte aligned");
+    const size_t b16 = (size_t)N * 16, b4 = (size_t)N * 4, b4p = ((size_t)N + 1) * 4;
+    if (overlap(pos, b16, acc_out, b16)) return fail(NBODY_EINVAL, "acc_out overlaps pos_xyzm");
+    if (pot_out && (overlap(pot_out, b4, pos, b16) || overlap(pot_out, b4, acc_out, b16)))
+        return fail(NBODY_EINVAL, "pot_out overlaps another buffer");
+    EnqueueLock lk(g_enqueue);
+    timer_arm();
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    const int n = (int)N;
+    const int S = leaf_size < N ? (int)leaf_size : n;  // a node never holds more than N
+    // scratch: keys, idx, sorted keys, perm, sorted pos, leaf level and leaf number of each
+    // sorted body, cell (leaf) starts, leaf keys and levels, list counts / offsets,
+    // counters, frame, sort temp, scan temp, bounds temp.
+    size_t scan_bytes = nbk::scan_temp_bytes((long long)N + 1);
+    const size_t sz[15] = {b4,  b4,  b4,  b4,  b16, b4,  b4, b4p,
+                           b4,  b4,  b4p, 256, 16,  nbk::sort_temp_bytes(n), scan_bytes};
+    size_t off[17];
+    off[0] = 0;
+    for (int i = 0; i < 15; ++i) off[i + 1] = align256(off[i] + sz[i]);
+    off[16] = align256(off[15] + nbk::tree_frame_temp_bytes(n));
+    void *ws = nullptr;
+    rc = scratch_get(dev, stream, off[16], &ws);
+    if (rc != NBODY_OK) return rc;
+    char *b = (char *)ws;
+    unsigned *keys = (unsigned *)(b + off[0]), *skeys = (unsigned *)(b + off[2]);
+    int *idx = (int *)(b + off[1]), *perm = (int *)(b + off[3]);
+    float4 *spos = (float4 *)(b + off[4]);
+    int *level = (int *)(b + off[5]), *ids = (int *)(b + off[6]), *start = (int *)(b + off[7]);
+    unsigned *leaf_key = (unsigned *)(b + off[8]);
+    int *leaf_level = (int *)(b + off[9]), *list_off = (int *)(b + off[10]);
+    int *counters = (int *)(b + off[11]);
+    float4 *frame = (float4 *)(b + off[12]);
+    void *sort_temp = b + off[13], *scan_temp = b + off[14];
+    float *bounds_temp = (float *)(b + off[15]);
+    e = nbk::launch_tree_frame((const float4 *)pos, n, bounds_temp, frame, counters, stream);
+    if (e == hipSuccess) e = nbk::launch_tree_keys((const float4 *)pos, n, frame, keys, idx, stream);
+    if (e == hipSuccess) e = nbk::sort_pairs(sort_temp, keys, skeys, idx, perm, n, 30, stream);
+    if (e == hipSuccess) e = nbk::launch_gather((const float4 *)pos, perm, n, spos, stream);
+    if (e == hipSuccess) e = nbk::launch_tree_levels(skeys, n, S, level, ids, stream);
+    if (e == hipSuccess) e = nbk::scan_exclusive(ids, n, counters, scan_temp, stream);
+    if (e == hipSuccess)
+        e = nbk::launch_tree_leaves(skeys, level, ids, n, start, leaf_key, leaf_level, stream);
+    if (e == hipSuccess)
+        e = nbk::launch_tree_lists(leaf_key, leaf_level, start, counters, n + 1, list_off, nullptr,
+                                   nullptr, stream);
+    if (e == hipSuccess) e = nbk::scan_exclusive(list_off, (long long)n + 1, counters + 1,
+                                                 scan_temp, stream);
+    int host[nbk::kTreeCounters] = {0, 0, 0, 0, 0, 0};
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(host, counters, sizeof(host), hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "near-tree build");
+    unsigned long long nlist = 0, terms = 0;
+    std::memcpy(&nlist, host + 2, 8);
+    std::memcpy(&terms, host + 4, 8);
+    const int nleaf = host[0];
+    if (nleaf < 1 || nleaf > n)
+        return fail(NBODY_EHIP, "near-tree build: %d leaves for %d bodies", nleaf, n);
+    if (nlist > (unsigned long long)INT32_MAX)
+        return fail(NBODY_EINVAL, "near-tree lists hold %llu entries (at most 2^31 - 1)", nlist);
+    if ((unsigned long long)(unsigned)host[1] != nlist)
+        return fail(NBODY_EHIP, "near-tree build: list offsets end at %d, counted %llu", host[1],
+                    nlist);
+    void *lw = nullptr;
+    rc = scratch_get(dev, stream, ((size_t)nlist + 1) * 4, &lw, 1);
+    if (rc != NBODY_OK) return rc;
+    int *list = (int *)lw;
+    e = nbk::launch_tree_lists(leaf_key, leaf_level, start, counters, nleaf, nullptr, list_off,
+                               list, stream);
+    if (e == hipSuccess) {
+        nbk::P2PArgs a{spos, n, eps2, start, nleaf, list_off, list, (long long)nlist,
+                       (float4 *)acc_out, pot_out, perm};
+        bool wide = false;
+        rc = wide_cells(N, nleaf, &wide);
+        if (rc != NBODY_OK) return rc;
+        e = timed_launch(stream,
+                         [&] { return nbk::launch_p2p(pot_out != nullptr, wide, a, stream); });
+    }
+    if (e != hipSuccess) return hip_fail(e, "near-tree launch");
+    if (stats) *stats = nbody_tree_stats{nleaf, (int64_t)nlist, (int64_t)terms};
     return ok();
 }
 

@@ -42,6 +42,7 @@
 #include "kernels.h"
 
 #include <cmath>
+#include <cstdint>
 
 namespace nbk {
 
@@ -1874,6 +1875,357 @@ __global__ void __launch_bounds__(256) sort_scatter_kernel(const unsigned *__res
     }
 }
 
+// ---------------------------------------------------------------- prefix sums
+// Exclusive prefix sum of any int array in place, tile by tile (4096 entries per
+// workgroup, the layout of sort_scan_kernel), each tile starting from an offset
+// given by the exclusive sums of the tile totals (scanned the same way, so any
+// length below 2^31 works). The last thread of the last tile writes the total.
+__global__ void __launch_bounds__(kSortScanThreads)
+    scan_tiles_kernel(int *__restrict__ data, int total, const int *__restrict__ offsets,
+                      int *__restrict__ total_out)
+{
+    __shared__ int4 buf[kSortScanThreads];
+    __shared__ int wsum[kSortScanThreads / 64];
+    int *flat = reinterpret_cast<int *>(buf);
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int base = blockIdx.x * kSortScanTile;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int i = base + k * kSortScanThreads + t;
+        flat[k * kSortScanThreads + t] = i < total ? data[i] : 0;
+    }
+    __syncthreads();
+    const int carry = offsets ? offsets[blockIdx.x] : 0;
+    const int4 v = buf[t];
+    const int sum = v.x + v.y + v.z + v.w;
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+    }
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    int before = carry;
+    for (int q = 0; q < w; ++q) before += wsum[q];
+    const int e = before + incl - sum;
+    buf[t] = make_int4(e, e + v.x, e + v.x + v.y, e + v.x + v.y + v.z);
+    if (total_out && t == kSortScanThreads - 1 && blockIdx.x == gridDim.x - 1)
+        *total_out = e + sum;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int i = base + k * kSortScanThreads + t;
+        if (i < total) data[i] = flat[k * kSortScanThreads + t];
+    }
+}
+
+// ---------------------------------------------------------------- octree leaves
+// nbody_near_tree builds the leaves of an octree over the bodies and their
+// interaction lists, then runs the near-field kernel over them. The tree is
+// implicit in the Morton order: node (L, p) is the run of sorted keys whose top
+// 3L bits are p. Steps (each a kernel, every decision in float32 or integers):
+//   bounds  - smallest and largest coordinate per axis (exact: min and max);
+//   keys    - the 30-bit key of each body in the root cube, then the stable sort;
+//   levels  - each sorted body's leaf level by bisection over L, with the size of
+//             its node at level L found by two binary searches confined to the
+//             leaf_size bodies on either side of it (a node reaching past them
+//             holds more than leaf_size);
+//   leaves  - the bodies where a leaf begins, scanned into leaf numbers;
+//   lists   - per leaf, the leaves meeting its closed cube: for each of the 27
+//             cells of its own level around it (its own cell included), the leaf
+//             that holds the whole cell (listed once, from the first such cell),
+//             or else the deeper leaves inside the cell whose cubes meet it. Every
+//             leaf meeting the cube lies in or over one of these cells. A count
+//             pass and a fill pass run the same enumeration.
+constexpr int kTreeBits = 10;       // levels below the root
+constexpr int kTreeBoundsBlocks = 512;
+
+__device__ __forceinline__ unsigned tree_spread(unsigned c)  // bit b of c -> bit 3b
+{
+    unsigned r = 0;
+#pragma unroll
+    for (int b = 0; b < kTreeBits; ++b) r |= ((c >> b) & 1u) << (3 * b);
+    return r;
+}
+
+__device__ __forceinline__ int tree_gather(unsigned k, int bits)  // bit 3b of k -> bit b
+{
+    unsigned r = 0;
+    for (int b = 0; b < bits; ++b) r |= ((k >> (3 * b)) & 1u) << b;
+    return (int)r;
+}
+
+__device__ __forceinline__ unsigned tree_cell(float x, float lo, float inv)
+{
+    float f = floorf((x - lo) * inv);
+    if (!(f >= 0.0f)) f = 0.0f;
+    if (f > 1023.0f) f = 1023.0f;
+    return (unsigned)f;
+}
+
+__device__ __forceinline__ int tree_shift(int level) { return 3 * (kTreeBits - level); }
+
+__global__ void __launch_bounds__(256) tree_bounds_kernel(const float4 *__restrict__ pos, int n,
+                                                          float *__restrict__ part)
+{
+    __shared__ float red[4][6];
+    float v[6] = {INFINITY, INFINITY, INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n;
+         i += (long long)gridDim.x * 256) {
+        const float4 b = pos[i];
+        v[0] = fminf(v[0], b.x);
+        v[1] = fminf(v[1], b.y);
+        v[2] = fminf(v[2], b.z);
+        v[3] = fmaxf(v[3], b.x);
+        v[4] = fmaxf(v[4], b.y);
+        v[5] = fmaxf(v[5], b.z);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+#pragma unroll
+        for (int d = 0; d < 3; ++d) {
+            v[d] = fminf(v[d], __shfl_xor(v[d], o));
+            v[3 + d] = fmaxf(v[3 + d], __shfl_xor(v[3 + d], o));
+        }
+    }
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 0)
+        for (int d = 0; d < 6; ++d) red[w][d] = v[d];
+    __syncthreads();
+    if (threadIdx.x < 6) {
+        const int d = threadIdx.x;
+        float r = red[0][d];
+        for (int q = 1; q < 4; ++q) r = d < 3 ? fminf(r, red[q][d]) : fmaxf(r, red[q][d]);
+        part[blockIdx.x * 6 + d] = r;
+    }
+}
+
+__global__ void __launch_bounds__(64) tree_frame_kernel(const float *__restrict__ part, int nparts,
+                                                        float4 *__restrict__ frame,
+                                                        int *__restrict__ counters)
+{
+    float v[6] = {INFINITY, INFINITY, INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    for (int b = threadIdx.x; b < nparts; b += 64)
+        for (int d = 0; d < 6; ++d)
+            v[d] = d < 3 ? fminf(v[d], part[b * 6 + d]) : fmaxf(v[d], part[b * 6 + d]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+#pragma unroll
+        for (int d = 0; d < 3; ++d) {
+            v[d] = fminf(v[d], __shfl_xor(v[d], o));
+            v[3 + d] = fmaxf(v[3 + d], __shfl_xor(v[3 + d], o));
+        }
+    }
+    if (threadIdx.x < kTreeCounters) counters[threadIdx.x] = 0;
+    if (threadIdx.x == 0) {
+        float side = 0.0f;
+        for (int d = 0; d < 3; ++d) {
+            const float ext = v[3 + d] - v[d];
+            if (ext > side) side = ext;
+        }
+        if (!(side > 0.0f)) side = 1.0f;
+        frame[0] = make_float4(v[0], v[1], v[2], 1024.0f / side);
+    }
+}
+
+__global__ void __launch_bounds__(256) tree_keys_kernel(const float4 *__restrict__ pos, int n,
+                                                        const float4 *__restrict__ frame,
+                                                        unsigned *__restrict__ keys,
+                                                        int *__restrict__ idx)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const float4 f = frame[0];
+    const float4 b = pos[i];
+    keys[i] = tree_spread(tree_cell(b.x, f.x, f.w)) | (tree_spread(tree_cell(b.y, f.y, f.w)) << 1) |
+              (tree_spread(tree_cell(b.z, f.z, f.w)) << 2);
+    idx[i] = i;
+}
+
+// Does the node at level L holding sorted body k have at most S bodies? Its first
+// and last bodies are searched for among the S bodies before and after k only: a
+// node reaching past them holds at least S + 1.
+__device__ __forceinline__ bool tree_node_fits(const unsigned *__restrict__ keys, int n, int k,
+                                               unsigned key, int L, int S)
+{
+    const int s = tree_shift(L);
+    const unsigned p = key >> s;
+    int a = k - S > 0 ? k - S : 0, b = k;  // first index in [a, k] with prefix p
+    while (a < b) {
+        const int m = a + (b - a) / 2;
+        if ((keys[m] >> s) < p) a = m + 1;
+        else b = m;
+    }
+    const long long hi = (long long)k + S + 1;
+    int c = k + 1, d = hi < n ? (int)hi : n;  // first index in (k, k + S + 1) past the node
+    while (c < d) {
+        const int m = c + (d - c) / 2;
+        if ((keys[m] >> s) <= p) c = m + 1;
+        else d = m;
+    }
+    return c - a <= S;
+}
+
+// Sorted body k begins its leaf (of level L) when the body before it lies in another
+// node of that level.
+__device__ __forceinline__ bool tree_leaf_begins(const unsigned *__restrict__ keys, int k, int L)
+{
+    const int s = tree_shift(L);
+    return k == 0 || (keys[k - 1] >> s) != (keys[k] >> s);
+}
+
+__global__ void __launch_bounds__(256) tree_levels_kernel(const unsigned *__restrict__ keys, int n,
+                                                          int S, int *__restrict__ level,
+                                                          int *__restrict__ start)
+{
+    const int k = blockIdx.x * 256 + threadIdx.x;
+    if (k >= n) return;
+    const unsigned key = keys[k];
+    int lo = 0, hi = kTreeBits;  // node sizes shrink with L: the first L that fits
+    while (lo < hi) {
+        const int L = (lo + hi) >> 1;
+        if (tree_node_fits(keys, n, k, key, L, S)) hi = L;
+        else lo = L + 1;
+    }
+    level[k] = lo;
+    start[k] = tree_leaf_begins(keys, k, lo) ? 1 : 0;
+}
+
+__global__ void __launch_bounds__(256) tree_leaves_kernel(const unsigned *__restrict__ keys,
+                                                          const int *__restrict__ level,
+                                                          const int *__restrict__ ids, int n,
+                                                          int *__restrict__ cell_start,
+                                                          unsigned *__restrict__ leaf_key,
+                                                          int *__restrict__ leaf_level)
+{
+    const int k = blockIdx.x * 256 + threadIdx.x;
+    if (k >= n) return;
+    const int L = level[k], s = tree_shift(L);
+    const bool first = tree_leaf_begins(keys, k, L);
+    const int a = ids[k];
+    if (first) {
+        cell_start[a] = k;
+        leaf_key[a] = (keys[k] >> s) << s;
+        leaf_level[a] = L;
+    }
+    if (k == n - 1) cell_start[a + (first ? 1 : 0)] = n;
+}
+
+// First leaf whose key is above x (upper) / at least x (lower), over leaf_key[0 .. nleaf).
+__device__ __forceinline__ int tree_upper(const unsigned *__restrict__ leaf_key, int nleaf,
+                                          unsigned x)
+{
+    int a = 0, b = nleaf;
+    while (a < b) {
+        const int m = a + (b - a) / 2;
+        if (leaf_key[m] <= x) a = m + 1;
+        else b = m;
+    }
+    return a;
+}
+
+__device__ __forceinline__ int tree_lower(const unsigned *__restrict__ leaf_key, int nleaf,
+                                          unsigned x)
+{
+    int a = 0, b = nleaf;
+    while (a < b) {
+        const int m = a + (b - a) / 2;
+        if (leaf_key[m] < x) a = m + 1;
+        else b = m;
+    }
+    return a;
+}
+
+__device__ __forceinline__ void tree_coords(unsigned key, int L, int (&c)[3])
+{
+    const unsigned p = key >> tree_shift(L);
+#pragma unroll
+    for (int d = 0; d < 3; ++d) c[d] = tree_gather(p >> d, L);
+}
+
+template <bool FILL>
+__global__ void __launch_bounds__(256) tree_lists_kernel(const unsigned *__restrict__ leaf_key,
+                                                         const int *__restrict__ leaf_level,
+                                                         const int *__restrict__ cell_start,
+                                                         int *__restrict__ counters, int nslots,
+                                                         int *__restrict__ cnt,
+                                                         const int *__restrict__ off,
+                                                         int *__restrict__ list)
+{
+    const int A = blockIdx.x * 256 + threadIdx.x;
+    if (A >= nslots) return;
+    const int nleaf = counters[0];
+    if (A >= nleaf) {
+        if (!FILL) cnt[A] = 0;
+        return;
+    }
+    const int L = leaf_level[A], s = tree_shift(L), lim = 1 << L;
+    int ca[3];
+    tree_coords(leaf_key[A], L, ca);
+    long long at = 0, end = 0;
+    if (FILL) {
+        at = off[A];
+        end = off[A + 1];
+    }
+    int w = 0;
+    long long terms = 0;
+    auto emit = [&](int B) {
+        if (FILL) {
+            if (at + w < end) list[at + w] = B;
+        } else {
+            terms += cell_start[B + 1] - cell_start[B];
+        }
+        ++w;
+    };
+    for (int q = 0; q < 27; ++q) {
+        const int cq[3] = {ca[0] + q % 3 - 1, ca[1] + (q / 3) % 3 - 1, ca[2] + q / 9 - 1};
+        if (cq[0] < 0 || cq[1] < 0 || cq[2] < 0 || cq[0] >= lim || cq[1] >= lim || cq[2] >= lim)
+            continue;
+        const unsigned qk = (tree_spread((unsigned)cq[0]) | (tree_spread((unsigned)cq[1]) << 1) |
+                             (tree_spread((unsigned)cq[2]) << 2)) << s;
+        const unsigned qe = qk + (1u << s);
+        const int b = tree_upper(leaf_key, nleaf, qk) - 1;
+        const int lb = b >= 0 ? leaf_level[b] : kTreeBits + 1;
+        if (lb <= L && qk < leaf_key[b] + (1u << tree_shift(lb))) {
+            // leaf b holds the whole cell: listed from the first in-range cell inside it
+            const int t = L - lb;
+            bool seen = false;
+            for (int r = 0; r < q && !seen; ++r) {
+                const int cr[3] = {ca[0] + r % 3 - 1, ca[1] + (r / 3) % 3 - 1, ca[2] + r / 9 - 1};
+                if (cr[0] < 0 || cr[1] < 0 || cr[2] < 0 || cr[0] >= lim || cr[1] >= lim ||
+                    cr[2] >= lim)
+                    continue;
+                seen = (cr[0] >> t) == (cq[0] >> t) && (cr[1] >> t) == (cq[1] >> t) &&
+                       (cr[2] >> t) == (cq[2] >> t);
+            }
+            if (!seen) emit(b);
+            continue;
+        }
+        // deeper leaves inside the cell: listed when their closed cubes meet A's
+        const int sa = 1 << (kTreeBits - L);
+        for (int B = tree_lower(leaf_key, nleaf, qk); B < nleaf && leaf_key[B] < qe; ++B) {
+            const int LB = leaf_level[B], sb = 1 << (kTreeBits - LB);
+            int cb[3];
+            tree_coords(leaf_key[B], LB, cb);
+            bool meet = true;
+#pragma unroll
+            for (int d = 0; d < 3; ++d) {
+                const int oa = ca[d] * sa, ob = cb[d] * sb;
+                meet = meet && ob <= oa + sa && oa <= ob + sb;
+            }
+            if (meet) emit(B);
+        }
+    }
+    if (!FILL) {
+        cnt[A] = w;
+        atomicAdd(reinterpret_cast<unsigned long long *>(counters + 2), (unsigned long long)w);
+        const long long na = cell_start[A + 1] - cell_start[A];
+        atomicAdd(reinterpret_cast<unsigned long long *>(counters + 4),
+                  (unsigned long long)(na * terms));
+    }
+}
+
 // ---------------------------------------------------------------- SoA layout
 // Separate x, y, z, m arrays (the host layout of the lecture's CPU program,
 // Degawa slide 15) in and out of the 16-byte records the kernels read.
@@ -2160,6 +2512,98 @@ hipError_t sort_pairs(void *temp, const unsigned *keys_in, unsigned *keys_out, c
         vs = vd;
     }
     return hipSuccess;
+}
+
+size_t scan_temp_bytes(long long total)
+{
+    size_t bytes = 256;
+    for (long long t = total; t > kSortScanTile;) {
+        t = (t + kSortScanTile - 1) / kSortScanTile;
+        bytes += ((size_t)t * sizeof(int) + 255) / 256 * 256;
+    }
+    return bytes;
+}
+
+hipError_t scan_exclusive(int *data, long long total, int *total_out, void *temp,
+                          hipStream_t stream)
+{
+    if (total < 0 || total > INT32_MAX || (total > 0 && !data)) return hipErrorInvalidValue;
+    int tot = (int)total;
+    const unsigned ntiles = tot > 0 ? (unsigned)((tot + kSortScanTile - 1) / kSortScanTile) : 1u;
+    int *offsets = nullptr;
+    if (ntiles > 1) {
+        if (!temp) return hipErrorInvalidValue;
+        offsets = (int *)temp;
+        void *a[] = {&data, &tot, &offsets};
+        hipError_t e = hipLaunchKernel((const void *)&sort_tile_sums_kernel, dim3(ntiles),
+                                       dim3(kSortScanThreads), a, 0, stream);
+        if (e != hipSuccess) return e;
+        void *rest = (char *)temp + ((size_t)ntiles * sizeof(int) + 255) / 256 * 256;
+        e = scan_exclusive(offsets, ntiles, nullptr, rest, stream);
+        if (e != hipSuccess) return e;
+    }
+    const int *offs = offsets;
+    void *a[] = {&data, &tot, &offs, &total_out};
+    return hipLaunchKernel((const void *)&scan_tiles_kernel, dim3(ntiles), dim3(kSortScanThreads),
+                           a, 0, stream);
+}
+
+size_t tree_frame_temp_bytes(int) { return (size_t)kTreeBoundsBlocks * 6 * sizeof(float); }
+
+hipError_t launch_tree_frame(const float4 *pos, int n, float *temp, float4 *frame, int *counters,
+                             hipStream_t stream)
+{
+    if (n < 0) return hipErrorInvalidValue;
+    long long nb = ((long long)n + 255) / 256;
+    int nparts = (int)(nb < 1 ? 1 : (nb > kTreeBoundsBlocks ? kTreeBoundsBlocks : nb));
+    void *a[] = {&pos, &n, &temp};
+    hipError_t e = hipLaunchKernel((const void *)&tree_bounds_kernel, dim3(nparts), dim3(256), a, 0,
+                                   stream);
+    if (e != hipSuccess) return e;
+    void *b[] = {&temp, &nparts, &frame, &counters};
+    return hipLaunchKernel((const void *)&tree_frame_kernel, dim3(1), dim3(64), b, 0, stream);
+}
+
+hipError_t launch_tree_keys(const float4 *pos, int n, const float4 *frame, unsigned *keys,
+                            int *idx, hipStream_t stream)
+{
+    if (n <= 0) return n == 0 ? hipSuccess : hipErrorInvalidValue;
+    void *a[] = {&pos, &n, &frame, &keys, &idx};
+    return hipLaunchKernel((const void *)&tree_keys_kernel, dim3((unsigned)((n + 255) / 256)),
+                           dim3(256), a, 0, stream);
+}
+
+hipError_t launch_tree_levels(const unsigned *skeys, int n, int leaf_size, int *level, int *start,
+                              hipStream_t stream)
+{
+    if (n <= 0) return n == 0 ? hipSuccess : hipErrorInvalidValue;
+    if (leaf_size < 1) return hipErrorInvalidValue;
+    void *a[] = {&skeys, &n, &leaf_size, &level, &start};
+    return hipLaunchKernel((const void *)&tree_levels_kernel, dim3((unsigned)((n + 255) / 256)),
+                           dim3(256), a, 0, stream);
+}
+
+hipError_t launch_tree_leaves(const unsigned *skeys, const int *level, const int *ids, int n,
+                              int *cell_start, unsigned *leaf_key, int *leaf_level,
+                              hipStream_t stream)
+{
+    if (n <= 0) return n == 0 ? hipSuccess : hipErrorInvalidValue;
+    void *a[] = {&skeys, &level, &ids, &n, &cell_start, &leaf_key, &leaf_level};
+    return hipLaunchKernel((const void *)&tree_leaves_kernel, dim3((unsigned)((n + 255) / 256)),
+                           dim3(256), a, 0, stream);
+}
+
+hipError_t launch_tree_lists(const unsigned *leaf_key, const int *leaf_level,
+                             const int *cell_start, int *counters, int nslots, int *cnt,
+                             const int *off, int *list, hipStream_t stream)
+{
+    if (nslots <= 0) return nslots == 0 ? hipSuccess : hipErrorInvalidValue;
+    const bool fill = list != nullptr;
+    if (fill ? !off : !cnt) return hipErrorInvalidValue;
+    void *a[] = {&leaf_key, &leaf_level, &cell_start, &counters, &nslots, &cnt, &off, &list};
+    const void *fn = fill ? (const void *)&tree_lists_kernel<true>
+                          : (const void *)&tree_lists_kernel<false>;
+    return hipLaunchKernel(fn, dim3((unsigned)((nslots + 255) / 256)), dim3(256), a, 0, stream);
 }
 
 hipError_t launch_pack(const float *a, const float *b, const float *c, const float *d, int n,

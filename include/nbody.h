@@ -294,6 +294,40 @@ int nbody_near_grid(const nbody_f4 *pos_xyzm, int64_t N, float eps2, const float
                     const int32_t dims[3], nbody_f4 *acc_out, float *pot_out,
                     hipStream_t stream);
 
+/* What nbody_near_tree built (host struct, filled on success). */
+typedef struct nbody_tree_stats {
+    int64_t leaves;        /* leaf cells of the octree */
+    int64_t list_entries;  /* total length of the leaves' interaction lists */
+    int64_t pair_terms;    /* terms summed: sum over leaves A of |A| x sum over listed B of |B| */
+} nbody_tree_stats;
+
+/*
+ * nbody_near_tree - near field over the leaves of an adaptive octree: the all-pairs
+ * sum as the near part of a tree code (GPU Gems 3 ch. 31 study page, section 6;
+ * Nakasato "スライド 1", No.31-38, where the tree code keeps the direct sum for
+ * nearby bodies). The pages do not fix the tree; this one is, in float32:
+ *   root cube: corner lo_d = the smallest coordinate d of any body, side = the
+ *     largest extent over the three axes (1 when all bodies coincide);
+ *   body i's cell at level 10 per axis: clamp(floor((x_d - lo_d) * (1024 / side)),
+ *     0, 1023); its 30-bit Morton key has bit 3b + d equal to bit b of that cell;
+ *   node (L, p), L = 0 .. 10: the bodies whose key shifted right by 3 (10 - L) is p;
+ *   leaf of a body: the node on its path with the smallest L holding at most
+ *     leaf_size bodies (its level-10 node when none does);
+ *   body i gets the sum over every body j whose leaf's closed cube meets the closed
+ *     cube of i's leaf (a shared face, edge or corner counts; j = i included).
+ * The library sorts the bodies by key (stable), finds the leaves and their lists on
+ * the GPU, runs the nbody_p2p kernel over them and writes acc_out / pot_out in the
+ * caller's body order. leaf_size >= 1; N <= 2^30; positions finite (a non-finite
+ * coordinate gives unspecified results for the bodies, never an access out of
+ * bounds). stats (host, may be NULL) receives the leaf and list counts.
+ * The call waits once on the stream, for the list lengths (the host sizes the
+ * lists' scratch from them): it returns after the build, with the near-field
+ * kernel enqueued. Scratch: ~N x 60 bytes + 4 bytes per list entry.
+ */
+int nbody_near_tree(const nbody_f4 *pos_xyzm, int64_t N, float eps2, int64_t leaf_size,
+                    nbody_f4 *acc_out, float *pot_out, nbody_tree_stats *stats,
+                    hipStream_t stream);
+
 /* Conserved-quantity diagnostics of a state (nbody_diagnostics), in fp64. */
 typedef struct nbody_diag {
     double kinetic;             /* K = sum m |v|^2 / 2 */

@@ -78,6 +78,15 @@ int main()
     const int32_t dims0[3] = {0, 4, 4};
     expect("grid dims", nbody_near_grid(A, 16, 1e-4f, lo, 0.5f, dims0, B, nullptr, nullptr),
            NBODY_EINVAL);
+    expect("tree leaf_size 0", nbody_near_tree(A, 16, 1e-4f, 0, B, nullptr, nullptr, nullptr),
+           NBODY_EINVAL);
+    nbody_tree_stats st = {7, 7, 7};
+    expect("tree N=0", nbody_near_tree(nullptr, 0, 1e-4f, 1, nullptr, nullptr, &st, nullptr),
+           NBODY_OK);
+    if (st.leaves != 0 || st.list_entries != 0 || st.pair_terms != 0) {
+        std::printf("FAIL tree N=0 stats not cleared\n");
+        ++failures;
+    }
     expect("diag N<0", nbody_diagnostics(A, B, nullptr, -1, 1e-4f, nullptr, nullptr),
            NBODY_EINVAL);
     expect("plan_for NULL", nbody_plan_for(16, 0, nullptr), NBODY_EINVAL);

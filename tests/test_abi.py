@@ -213,6 +213,31 @@ def test_near_grid_rejects(nb, bad, code):
     assert nb.nbody_last_error() != ""
 
 
+@pytest.mark.parametrize("bad,code", [
+    (dict(n=-1), 1), (dict(n=(1 << 30) + 1), 1), (dict(leaf=0), 1), (dict(leaf=-5), 1),
+    (dict(pos=None), 1), (dict(acc=None), 1), (dict(eps2=0.0), 1), (dict(eps2=math.inf), 1),
+    (dict(eps2=2.0 ** -86), 1), (dict(pos=A + 4), 2), (dict(acc=B + 4), 2),
+    (dict(pot=C + 2), 2), (dict(acc=A + 64), 1), (dict(pot=A), 1), (dict(pot=B + 16), 1),
+])
+def test_near_tree_rejects(nb, bad, code):
+    a = dict(pos=A, n=16, eps2=1e-4, leaf=4, acc=B, pot=None)
+    a.update(bad)
+    st = nb.nbody_tree_stats(7, 7, 7)
+    rc = nb.nbody_near_tree(a["pos"], a["n"], a["eps2"], a["leaf"], a["acc"], a["pot"], st,
+                            stream=0, check=False)
+    assert rc == code, bad
+    assert nb.nbody_last_error() != ""
+
+
+def test_near_tree_nothing_to_do(nb):
+    st = nb.nbody_tree_stats(7, 7, 7)
+    assert nb.nbody_near_tree(None, 0, 1e-4, 1, None, None, st, stream=0,
+                              check=False) == nb.NBODY_OK
+    assert (st.leaves, st.list_entries, st.pair_terms) == (0, 0, 0)
+    assert nb.nbody_near_tree(None, 0, 1e-4, 1, None, None, None, stream=0,
+                              check=False) == nb.NBODY_OK
+
+
 PAIRS512 = dict(mode=2, band=512)
 
 

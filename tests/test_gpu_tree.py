@@ -1,0 +1,175 @@
+"""GPU parity of nbody_near_tree (near field over the leaves of the Morton-order octree)
+against the oracle's definition of the same tree, through the C ABI."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import workloads
+from gpu_util import assert_accel_parity, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nb():
+    import direct_all_pairs_amd
+
+    return direct_all_pairs_amd
+
+
+def gpu_near_tree(nb, pos, eps2, leaf_size, pot=True):
+    import torch
+
+    n = pos.shape[0]
+    print(f"[tree] N={n} leaf_size={leaf_size} pot={pot}", flush=True)
+    pd = to_dev(pos)
+    acc = torch.full((n, 4), np.nan, device="cuda")
+    p = torch.full((n,), np.nan, device="cuda") if pot else None
+    st = nb.nbody_tree_stats()
+    nb.nbody_near_tree(pd, n, float(eps2), int(leaf_size), acc, p, st)
+    torch.cuda.synchronize()
+    return acc.cpu().numpy(), (p.cpu().numpy() if pot else None), st.as_dict()
+
+
+@pytest.mark.parametrize("n,leaf", [(1, 1), (2, 1), (100, 1), (100, 8), (3001, 16), (3001, 64),
+                                    (3001, 300), (5000, 2)])
+def test_near_tree_uniform(nb, n, leaf):
+    """Uniform cube, every target against the tree definition (leaf sizes from one body,
+    where every occupied level-10 cell is a leaf, to a tenth of the bodies)."""
+    import oracle
+
+    pos, _ = workloads.random_bodies(n, seed=4000 + n + leaf)
+    acc, pot, st = gpu_near_tree(nb, pos, 1e-4, leaf)
+    assert_accel_parity(acc, pot, oracle.near_tree(pos, 1e-4, leaf),
+                        what=f"near tree N={n} leaf_size={leaf}")
+    assert 1 <= st["leaves"] <= n and st["list_entries"] >= st["leaves"]
+    assert n <= st["pair_terms"] <= n * n
+
+
+@pytest.mark.parametrize("n,leaf", [(1, 1), (700, 700), (3000, 5000)])
+def test_near_tree_one_leaf_is_the_direct_sum(nb, n, leaf):
+    """leaf_size >= N: the root is the only leaf and the near field is the whole sum."""
+    import oracle
+
+    pos, _ = workloads.random_bodies(n, seed=4100 + n)
+    acc, pot, st = gpu_near_tree(nb, pos, 1e-4, leaf)
+    assert_accel_parity(acc, pot, oracle.accel(pos, np.float32(1e-4)), what=f"one leaf N={n}")
+    assert st == {"leaves": 1, "list_entries": 1, "pair_terms": n * n}
+
+
+def _lattice(cells, k, seed):
+    """k bodies inside each cell of a cells^3 lattice on [0, 1]^3 plus bodies at the two
+    corners, so that the root cube is [0, 1]^3."""
+    rng = np.random.default_rng(seed)
+    c = np.stack(np.meshgrid(*[np.arange(cells)] * 3, indexing="ij"), -1).reshape(-1, 3)
+    c = np.repeat(c, k, axis=0)
+    x = (c + rng.uniform(0.15, 0.85, size=c.shape)) / cells
+    x = np.concatenate([x, [[0.0, 0.0, 0.0], [1.0, 1.0, 1.0]]])
+    pos = np.zeros((x.shape[0], 4), np.float32)
+    pos[:, :3] = x
+    pos[:, 3] = rng.uniform(0.5, 1.5, size=x.shape[0]) / x.shape[0]
+    return pos
+
+
+def test_near_tree_full_octree_counts(nb):
+    """Two bodies in every cell of a 16^3 lattice (three in the corner cells) with
+    leaf_size = 3: the leaves are the lattice cells, each listing its 27-cell neighbourhood
+    (clipped at the faces), so the counts have closed forms; results against the oracle."""
+    import oracle
+
+    cells = 16
+    pos = _lattice(cells, 2, 5)
+    acc, pot, st = gpu_near_tree(nb, pos, 1e-4, 3)
+    per_axis = 2 * 2 + (cells - 2) * 3  # neighbours per axis: 2 at the faces, 3 inside
+    assert st["leaves"] == cells ** 3
+    assert st["list_entries"] == per_axis ** 3
+    # pair terms: sum over cells A of |A| x bodies in A's neighbourhood
+    cnt = np.full((cells,) * 3, 2, np.int64)
+    cnt[0, 0, 0] += 1
+    cnt[-1, -1, -1] += 1
+    pad = np.pad(cnt, 1)
+    hood = sum(pad[1 + dx:1 + dx + cells, 1 + dy:1 + dy + cells, 1 + dz:1 + dz + cells]
+               for dx in (-1, 0, 1) for dy in (-1, 0, 1) for dz in (-1, 0, 1))
+    assert st["pair_terms"] == int(np.sum(cnt * hood))
+    assert_accel_parity(acc, pot, oracle.near_tree(pos, 1e-4, 3), what="16^3 lattice tree")
+
+
+def test_near_tree_clustered_and_duplicates(nb):
+    """A dense core inside a sparse halo (leaves at many levels, big leaves beside deep
+    ones), 40 bodies at one point (a level-10 node holding more than leaf_size) and a plane
+    of bodies (a flat root cube extent), against the definition."""
+    import oracle
+
+    rng = np.random.default_rng(11)
+    core = rng.normal(0.0, 0.01, size=(3000, 3))
+    halo = rng.uniform(-1.0, 1.0, size=(1500, 3))
+    same = np.full((40, 3), 0.3)
+    plane = np.column_stack([rng.uniform(-1, 1, 500), rng.uniform(-1, 1, 500), np.full(500, -0.5)])
+    x = np.concatenate([core, halo, same, plane])
+    pos = np.zeros((x.shape[0], 4), np.float32)
+    pos[:, :3] = x
+    pos[:, 3] = rng.uniform(0.5, 1.5, size=x.shape[0]) / x.shape[0]
+    for leaf in (1, 8, 33):
+        acc, pot, st = gpu_near_tree(nb, pos, 1e-5, leaf)
+        assert_accel_parity(acc, pot, oracle.near_tree(pos, 1e-5, leaf),
+                            what=f"clustered tree leaf_size={leaf}")
+
+
+def test_near_tree_coincident_bodies(nb):
+    """All bodies at one point: one leaf (root cube side 1), the whole direct sum."""
+    import oracle
+
+    pos = np.zeros((37, 4), np.float32)
+    pos[:, :3] = 2.5
+    pos[:, 3] = np.linspace(0.5, 1.5, 37) / 37
+    acc, pot, st = gpu_near_tree(nb, pos, 1e-3, 1)
+    assert st["leaves"] == 1
+    assert_accel_parity(acc, pot, oracle.accel(pos, np.float32(1e-3)), what="coincident")
+
+
+def test_near_tree_plummer_sampled(nb):
+    """Plummer sphere, N = 65536, leaf_size 64: sampled targets (centre, outliers, random)
+    against the definition; repeated calls give the same bits; no potential, same
+    accelerations."""
+    import oracle
+
+    w = workloads.make("plummer65536")
+    acc, pot, st = gpu_near_tree(nb, w.pos, w.eps2, 64)
+    r = np.linalg.norm(w.pos[:, :3], axis=1)
+    idx = np.unique(np.concatenate([np.argsort(r)[:300], np.argsort(r)[-300:],
+                                    np.random.default_rng(9).integers(0, w.n, 1000)]))
+    ref = oracle.near_tree(w.pos, w.eps2, 64, targets=idx)
+    assert_accel_parity(acc, pot, ref, idx=idx, what="plummer tree")
+    a2, p2, st2 = gpu_near_tree(nb, w.pos, w.eps2, 64)
+    assert np.array_equal(acc, a2) and np.array_equal(pot, p2) and st == st2
+    a0, p0, _ = gpu_near_tree(nb, w.pos, w.eps2, 64, pot=False)
+    assert p0 is None and np.array_equal(a0, acc)
+
+
+def test_near_tree_cube1m_sampled(nb):
+    """N = 2^20 uniform cube, leaf_size 64 (the benchmarked configuration): sampled targets,
+    both ends included, against the definition; every body written."""
+    import oracle
+
+    w = workloads.make("cube1m")
+    acc, pot, st = gpu_near_tree(nb, w.pos, w.eps2, 64)
+    idx = np.unique(np.concatenate([np.random.default_rng(10).integers(0, w.n, 1500),
+                                    [0, w.n - 1]]))
+    ref = oracle.near_tree(w.pos, w.eps2, 64, targets=idx)
+    assert_accel_parity(acc, pot, ref, idx=idx, what="cube1m tree")
+    assert np.all(np.isfinite(acc)) and np.all(np.isfinite(pot))
+    print(f"[tree] cube1m stats {st}", flush=True)
+
+
+def test_near_tree_permuted_input(nb):
+    """Permuting the input bodies permutes the rows (up to rounding order)."""
+    import oracle
+
+    pos, _ = workloads.random_bodies(4000, seed=12)
+    perm = np.random.default_rng(13).permutation(4000)
+    acc, pot, _ = gpu_near_tree(nb, pos[perm], 1e-4, 16)
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(4000)
+    assert_accel_parity(acc[inv], pot[inv], oracle.near_tree(pos, 1e-4, 16), what="permuted")
