@@ -299,10 +299,11 @@ _default: Oracle | None = None
 
 
 def get() -> Oracle:
-    """The oracle built from oracle.c (compiled on first use if nothing is built)."""
+    """The oracle built from oracle.c (compiled on first use if nothing is built, or if the
+    source is newer than the library)."""
     global _default
     if _default is None:
-        if not LIB.exists():
+        if not LIB.exists() or LIB.stat().st_mtime < SRC.stat().st_mtime:
             build()
         _default = Oracle(LIB)
     return _default

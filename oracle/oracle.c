@@ -404,40 +404,44 @@ int oracle_near_grid(const double *pos, int64_t n, double eps2, const double *lo
  * Near field over the leaves of an octree in Morton order: the all-pairs sum as the
  * near part of a hierarchical method (GPU Gems 3 ch. 31 study page, section 6; the
  * tree codes of Nakasato "スライド 1", No.31-38). The tree itself is not on the
- * pages; it is defined here as follows, every decision taken in float32 (an integer
- * decided by floating point is decided in the kernel's precision):
+ * pages; it is defined here as follows, with D = TREE_LEVELS = 21 levels below the
+ * root (63-bit keys, so that a centrally concentrated system whose outliers set the
+ * root cube still splits into small leaves), every decision taken in float32 (an
+ * integer decided by floating point is decided in the kernel's precision):
  *   root cube: lo_d = the smallest coordinate d of any body; side = the largest of
  *     (largest coordinate d - lo_d) over d, or 1 when that is not positive;
- *   cell of a body per axis at level 10: c_d = floor((x_d - lo_d) * (1024 / side)),
- *     clamped to [0, 1023] (a NaN goes to 0);
+ *   cell of a body per axis at level D: c_d = floor((x_d - lo_d) * (2^D / side)),
+ *     clamped to [0, 2^D - 1] (a NaN goes to 0);
  *   Morton key: bit 3b + d of the key is bit b of c_d (d = 0, 1, 2 for x, y, z);
- *   node (L, p), L = 0 .. 10: the bodies whose key shifted right by 3 (10 - L) is p;
+ *   node (L, p), L = 0 .. D: the bodies whose key shifted right by 3 (D - L) is p;
  *   leaf of a body: the node on its path with the smallest L holding at most
- *     leaf_size bodies, or its level-10 node when there is none;
- *   cube of node (L, p): per axis the closed interval [o_d, o_d + 2^(10 - L)] in
- *     level-10 units, where o_d / 2^(10 - L) is made of the bits 3b + d of p;
+ *     leaf_size bodies, or its level-D node when there is none;
+ *   cube of node (L, p): per axis the closed interval [o_d, o_d + 2^(D - L)] in
+ *     level-D units, where o_d / 2^(D - L) is made of the bits 3b + d of p;
  *   near field of body i: the sum over every body j whose leaf's cube meets the cube
  *     of i's leaf (touching counts; i's own leaf is included, so j = i is).
  * Sums as oracle_accel, over those j in ascending order, for the listed targets
  * (NULL: all n). leaf_size >= 1. Returns -1 on bad arguments.
  */
-static int cmp_u32(const void *a, const void *b)
+#define TREE_LEVELS 21
+
+static int cmp_u64(const void *a, const void *b)
 {
-    const uint32_t x = *(const uint32_t *)a, y = *(const uint32_t *)b;
+    const uint64_t x = *(const uint64_t *)a, y = *(const uint64_t *)b;
     return x < y ? -1 : (x > y ? 1 : 0);
 }
 
-/* Number of sorted keys in [a, b). */
-static int64_t keys_in(const uint32_t *sorted, int64_t n, uint64_t a, uint64_t b)
+/* Number of sorted keys k with a <= k < b (b = 2^63 + ... is allowed: unsigned). */
+static int64_t keys_in(const uint64_t *sorted, int64_t n, uint64_t a, uint64_t b)
 {
     int64_t l0 = 0, h0 = n, l1 = 0, h1 = n;
     while (l0 < h0) {
         const int64_t m = l0 + (h0 - l0) / 2;
-        if ((uint64_t)sorted[m] < a) l0 = m + 1; else h0 = m;
+        if (sorted[m] < a) l0 = m + 1; else h0 = m;
     }
     while (l1 < h1) {
         const int64_t m = l1 + (h1 - l1) / 2;
-        if ((uint64_t)sorted[m] < b) l1 = m + 1; else h1 = m;
+        if (sorted[m] < b) l1 = m + 1; else h1 = m;
     }
     return l1 - l0;
 }
@@ -449,8 +453,9 @@ int oracle_near_tree(const double *pos, int64_t n, double eps2, int64_t leaf_siz
     if (!pos || n < 0 || nt < 0 || !(eps2 > 0.0) || leaf_size < 1) return -1;
     if (nt > 0 && (!acc || !pot || !bound_a || !bound_p)) return -1;
     const int64_t nn = n > 0 ? n : 1;
-    uint32_t *key = (uint32_t *)malloc((size_t)nn * sizeof(uint32_t));
-    uint32_t *sorted = (uint32_t *)malloc((size_t)nn * sizeof(uint32_t));
+    const int D = TREE_LEVELS;
+    uint64_t *key = (uint64_t *)malloc((size_t)nn * sizeof(uint64_t));
+    uint64_t *sorted = (uint64_t *)malloc((size_t)nn * sizeof(uint64_t));
     int64_t *box = (int64_t *)malloc((size_t)nn * 4 * sizeof(int64_t)); /* o_x, o_y, o_z, size */
     if (!key || !sorted || !box) {
         free(key); free(sorted); free(box);
@@ -470,38 +475,39 @@ int oracle_near_tree(const double *pos, int64_t n, double eps2, int64_t leaf_siz
         if (ext > side) side = ext;
     }
     if (!(side > 0.0f)) side = 1.0f;
-    const float inv = 1024.0f / side;
+    const float cells = (float)(1 << D);  /* 2^D, exact in float32 */
+    const float inv = cells / side;
     for (int64_t j = 0; j < n; ++j) {
-        uint32_t k = 0;
+        uint64_t k = 0;
         for (int d = 0; d < 3; ++d) {
             float f = floorf(((float)pos[4 * j + d] - lo[d]) * inv);
             if (!(f >= 0.0f)) f = 0.0f;
-            if (f > 1023.0f) f = 1023.0f;
-            const uint32_t c = (uint32_t)f;
-            for (int b = 0; b < 10; ++b) k |= ((c >> b) & 1u) << (3 * b + d);
+            if (f > cells - 1.0f) f = cells - 1.0f;
+            const uint64_t c = (uint64_t)f;
+            for (int b = 0; b < D; ++b) k |= ((c >> b) & 1u) << (3 * b + d);
         }
         key[j] = k;
         sorted[j] = k;
     }
-    qsort(sorted, (size_t)n, sizeof(uint32_t), cmp_u32);
+    qsort(sorted, (size_t)n, sizeof(uint64_t), cmp_u64);
     for (int64_t j = 0; j < n; ++j) {
-        int level = 10;
-        for (int L = 0; L <= 10; ++L) {
-            const int s = 3 * (10 - L);
+        int level = D;
+        for (int L = 0; L <= D; ++L) {
+            const int s = 3 * (D - L);
             const uint64_t p = key[j] >> s;
             if (keys_in(sorted, n, p << s, (p + 1) << s) <= leaf_size) {
                 level = L;
                 break;
             }
         }
-        const int s = 3 * (10 - level);
-        const uint32_t p = key[j] >> s;
+        const int s = 3 * (D - level);
+        const uint64_t p = key[j] >> s;
         for (int d = 0; d < 3; ++d) {
             int64_t o = 0;
             for (int b = 0; b < level; ++b) o |= (int64_t)((p >> (3 * b + d)) & 1u) << b;
-            box[4 * j + d] = o << (10 - level);
+            box[4 * j + d] = o << (D - level);
         }
-        box[4 * j + 3] = (int64_t)1 << (10 - level);
+        box[4 * j + 3] = (int64_t)1 << (D - level);
     }
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 16) reduction(| : bad)

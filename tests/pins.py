@@ -635,6 +635,34 @@ def pin_near_tree_full_octree_equals_grid(orc):
                                      "from the grid")
 
 
+def pin_near_tree_deep_lattice(orc):
+    """Leaves deep in the tree: two bodies in each cell of a 4^3 lattice of side 2^-13 at the
+    origin (which fills the level-11 cell there), one more at (0, 0, 0) and one at (1, 1, 1),
+    so the root cube is [0, 1]^3. With leaf_size = 3 the lattice cells are the leaves (level
+    13; every coarser node around them holds 16 or more), so a lattice body's near field is
+    the grid near field of the lattice; the body at (1, 1, 1) is alone in its octant and
+    touches no other leaf, leaving only its self term."""
+    rng = np.random.Generator(np.random.PCG64(45))
+    h = 2.0 ** -13
+    c = np.stack(np.meshgrid(*[np.arange(4)] * 3, indexing="ij"), -1).reshape(-1, 3)
+    c = np.repeat(c, 2, axis=0)
+    x = (c + rng.uniform(0.15, 0.85, size=c.shape)) * h
+    x = np.concatenate([x, [[0.0, 0.0, 0.0], [1.0, 1.0, 1.0]]]).astype(np.float32)
+    pos = _bodies(x.astype(np.float64), rng.uniform(0.5, 1.5, size=x.shape[0]))
+    e2 = 1e-9
+    r = orc.near_tree_exact(pos, e2, 3)
+    lat = pos[:-1]
+    g = orc.near_grid_exact(lat, e2, (0.0, 0.0, 0.0), h, (4, 4, 4))
+    for k in ("acc", "pot", "bound_a", "bound_p"):
+        want = g[k]
+        got = r[k][:-1]
+        if not np.array_equal(got, want):
+            raise AssertionError(f"deep lattice: {k} differs from the grid near field")
+    m = pos[-1, 3]
+    if not (np.all(r["acc"][-1] == 0.0) and r["pot"][-1] == -m / math.sqrt(e2)):
+        raise AssertionError("deep lattice: the lone body's near field is not its self term")
+
+
 def pin_near_tree_mixed_levels(orc):
     """Leaves at two levels, neighbour sets derived by hand. The octant [0, 1/2]^3 holds two
     bodies in each of its eight level-2 cells (16 > leaf_size = 2: it splits; its cells are
@@ -743,6 +771,7 @@ ALL_PINS = [
     pin_shards_add_up_to_direct_sum,
     pin_near_tree_one_leaf_equals_direct_sum,
     pin_near_tree_full_octree_equals_grid,
+    pin_near_tree_deep_lattice,
     pin_near_tree_mixed_levels,
     pin_near_tree_third_law,
 ]

@@ -66,10 +66,11 @@ MUTATIONS = [
      "                level = L;\n                break;", "                level = L;"),
     ("near tree: root side is the smallest extent", "if (ext > side) side = ext;",
      "if (side == 0.0f || ext < side) side = ext;"),
-    ("near tree: top face not clamped into the last cell", "if (f > 1023.0f) f = 1023.0f;",
-     "if (f > 1024.0f) f = 1024.0f;"),
-    ("near tree: leaf corner one level off", "box[4 * j + d] = o << (10 - level);",
-     "box[4 * j + d] = o << (9 - level);"),
+    ("near tree: top face not clamped into the last cell",
+     "if (f > cells - 1.0f) f = cells - 1.0f;", "if (f > cells) f = cells;"),
+    ("near tree: leaf corner one level off", "box[4 * j + d] = o << (D - level);",
+     "box[4 * j + d] = o << (D - 1 - level);"),
+    ("near tree: ten levels instead of 21", "#define TREE_LEVELS 21", "#define TREE_LEVELS 10"),
 ]
 
 
