@@ -105,8 +105,9 @@ struct Scratch {
     void *ptr = nullptr;
     size_t bytes = 0;
 };
-// Keyed by (device, stream, slot); slot 1 holds the interaction lists of
-// nbody_near_tree, whose size is known only after the first part of the build.
+// Keyed by (device, stream, slot); slots 1 and 2 hold the list counts and the
+// interaction lists of nbody_near_tree, whose sizes are known only part-way
+// through its build.
 std::map<std::tuple<int, hipStream_t, int>, Scratch> g_scratch;
 
 // Held by every entry point that uses scratch, from taking the block until its
@@ -1097,7 +1098,7 @@ int nbody_near_tree(const nbody_f4 *pos, int64_t N, float eps2, int64_t leaf_siz
     if (!aligned(pos, 16) || !aligned(acc_out, 16))
         return fail(NBODY_EALIGN, "pos_xyzm and acc_out must be 16-byte aligned");
     if (pot_out && !aligned(pot_out, 4)) return fail(NBODY_EALIGN, "pot_out is not 4-byte aligned");
-    const size_t b16 = (size_t)N * 16, b4 = (size_t)N * 4, b4p = ((size_t)N + 1) * 4;
+    const size_t b16 = (size_t)N * 16, b4 = (size_t)N * 4;
     if (overlap(pos, b16, acc_out, b16)) return fail(NBODY_EINVAL, "acc_out overlaps pos_xyzm");
     if (pot_out && (overlap(pot_out, b4, pos, b16) || overlap(pot_out, b4, acc_out, b16)))
         return fail(NBODY_EINVAL, "pot_out overlaps another buffer");
@@ -1108,65 +1109,88 @@ int nbody_near_tree(const nbody_f4 *pos, int64_t N, float eps2, int64_t leaf_siz
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     const int n = (int)N;
     const int S = leaf_size < N ? (int)leaf_size : n;  // a node never holds more than N
-    // scratch: keys, idx, sorted keys, perm, sorted pos, leaf level and leaf number of each
-    // sorted body, cell (leaf) starts, leaf keys and levels, list counts / offsets,
-    // counters, frame, sort temp, scan temp, bounds temp.
-    size_t scan_bytes = nbk::scan_temp_bytes((long long)N + 1);
-    const size_t sz[15] = {b4,  b4,  b4,  b4,  b16, b4,  b4, b4p,
-                           b4,  b4,  b4p, 256, 16,  nbk::sort_temp_bytes(n), scan_bytes};
+    // Scratch slot 0, sized by N: keys, idx, sorted keys, perm, sorted pos, leaf level and
+    // leaf number of each sorted body, cell (leaf) starts, leaf keys and cubes, list
+    // offsets, counters, frame, sort temp, scan temp, bounds temp.
+    const size_t b8 = (size_t)N * 8, b4p = ((size_t)N + 1) * 4;
+    const size_t sz[16] = {b8,  b4,  b8,  b4,  b16, b4,  b4,  b4p,
+                           b8,  b16, b4p, 256, 16,  nbk::sort_temp_bytes(n, 8),
+                           nbk::scan_temp_bytes(N), nbk::tree_frame_temp_bytes(n)};
     size_t off[17];
     off[0] = 0;
-    for (int i = 0; i < 15; ++i) off[i + 1] = align256(off[i] + sz[i]);
-    off[16] = align256(off[15] + nbk::tree_frame_temp_bytes(n));
+    for (int i = 0; i < 16; ++i) off[i + 1] = align256(off[i] + sz[i]);
     void *ws = nullptr;
     rc = scratch_get(dev, stream, off[16], &ws);
     if (rc != NBODY_OK) return rc;
     char *b = (char *)ws;
-    unsigned *keys = (unsigned *)(b + off[0]), *skeys = (unsigned *)(b + off[2]);
+    auto *keys = (unsigned long long *)(b + off[0]), *skeys = (unsigned long long *)(b + off[2]);
     int *idx = (int *)(b + off[1]), *perm = (int *)(b + off[3]);
     float4 *spos = (float4 *)(b + off[4]);
     int *level = (int *)(b + off[5]), *ids = (int *)(b + off[6]), *start = (int *)(b + off[7]);
-    unsigned *leaf_key = (unsigned *)(b + off[8]);
-    int *leaf_level = (int *)(b + off[9]), *list_off = (int *)(b + off[10]);
-    int *counters = (int *)(b + off[11]);
+    auto *leaf_key = (unsigned long long *)(b + off[8]);
+    int4 *leaf_box = (int4 *)(b + off[9]);
+    int *list_off = (int *)(b + off[10]), *counters = (int *)(b + off[11]);
     float4 *frame = (float4 *)(b + off[12]);
     void *sort_temp = b + off[13], *scan_temp = b + off[14];
     float *bounds_temp = (float *)(b + off[15]);
+    int host[nbk::kTreeCounters] = {0, 0, 0, 0, 0, 0};
     e = nbk::launch_tree_frame((const float4 *)pos, n, bounds_temp, frame, counters, stream);
     if (e == hipSuccess) e = nbk::launch_tree_keys((const float4 *)pos, n, frame, keys, idx, stream);
-    if (e == hipSuccess) e = nbk::sort_pairs(sort_temp, keys, skeys, idx, perm, n, 30, stream);
+    if (e == hipSuccess) e = nbk::sort_pairs64(sort_temp, keys, skeys, idx, perm, n, 63, stream);
     if (e == hipSuccess) e = nbk::launch_gather((const float4 *)pos, perm, n, spos, stream);
     if (e == hipSuccess) e = nbk::launch_tree_levels(skeys, n, S, level, ids, stream);
     if (e == hipSuccess) e = nbk::scan_exclusive(ids, n, counters, scan_temp, stream);
     if (e == hipSuccess)
-        e = nbk::launch_tree_leaves(skeys, level, ids, n, start, leaf_key, leaf_level, stream);
-    if (e == hipSuccess)
-        e = nbk::launch_tree_lists(leaf_key, leaf_level, start, counters, n + 1, list_off, nullptr,
-                                   nullptr, stream);
-    if (e == hipSuccess) e = nbk::scan_exclusive(list_off, (long long)n + 1, counters + 1,
-                                                 scan_temp, stream);
-    int host[nbk::kTreeCounters] = {0, 0, 0, 0, 0, 0};
-    if (e == hipSuccess)
-        e = hipMemcpyAsync(host, counters, sizeof(host), hipMemcpyDeviceToHost, stream);
+        e = nbk::launch_tree_leaves(skeys, level, ids, n, start, leaf_key, leaf_box, stream);
+    // first wait: the number of leaves sizes the list counts
+    if (e == hipSuccess) e = hipMemcpyAsync(host, counters, 4, hipMemcpyDeviceToHost, stream);
     if (e == hipSuccess) e = hipStreamSynchronize(stream);
     if (e != hipSuccess) return hip_fail(e, "near-tree build");
-    unsigned long long nlist = 0, terms = 0;
-    std::memcpy(&nlist, host + 2, 8);
-    std::memcpy(&terms, host + 4, 8);
     const int nleaf = host[0];
     if (nleaf < 1 || nleaf > n)
         return fail(NBODY_EHIP, "near-tree build: %d leaves for %d bodies", nleaf, n);
+    if (nleaf > nbk::kTreeMaxLeaves)
+        return fail(NBODY_EINVAL, "near-tree: %d leaves exceed %d (raise leaf_size)", nleaf,
+                    nbk::kTreeMaxLeaves);
+    // Scratch slot 1, sized by the leaves: coarse table, list part counts, their scan
+    // temp, per-workgroup totals of the count pass.
+    const int lt = nbk::tree_table_level(nleaf);
+    const long long parts = 27ll * nleaf + 1;
+    const size_t s1[4] = {(((size_t)1 << (3 * lt)) + 1) * 4, (size_t)parts * 4,
+                          nbk::scan_temp_bytes(parts), nbk::tree_parts_bytes(nleaf)};
+    size_t o1[5];
+    o1[0] = 0;
+    for (int i = 0; i < 4; ++i) o1[i + 1] = align256(o1[i] + s1[i]);
+    void *ws1 = nullptr;
+    rc = scratch_get(dev, stream, o1[4], &ws1, 1);
+    if (rc != NBODY_OK) return rc;
+    char *b1 = (char *)ws1;
+    int *table = (int *)(b1 + o1[0]), *cnt = (int *)(b1 + o1[1]);
+    void *scan_temp1 = b1 + o1[2], *wg_totals = b1 + o1[3];
+    const nbk::TreeLeaves lv{leaf_key, leaf_box, table, start, nleaf, lt};
+    e = nbk::launch_tree_table(leaf_key, counters, lt, table, stream);
+    if (e == hipSuccess)
+        e = nbk::launch_tree_lists(lv, counters, wg_totals, cnt, nullptr, nullptr, nullptr,
+                                   stream);
+    if (e == hipSuccess) e = nbk::scan_exclusive(cnt, parts, counters + 1, scan_temp1, stream);
+    // second wait: the list total sizes the lists
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(host, counters, sizeof(host), hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "near-tree lists");
+    unsigned long long nlist = 0, terms = 0;
+    std::memcpy(&nlist, host + 2, 8);
+    std::memcpy(&terms, host + 4, 8);
     if (nlist > (unsigned long long)INT32_MAX)
         return fail(NBODY_EINVAL, "near-tree lists hold %llu entries (at most 2^31 - 1)", nlist);
     if ((unsigned long long)(unsigned)host[1] != nlist)
         return fail(NBODY_EHIP, "near-tree build: list offsets end at %d, counted %llu", host[1],
                     nlist);
     void *lw = nullptr;
-    rc = scratch_get(dev, stream, ((size_t)nlist + 1) * 4, &lw, 1);
+    rc = scratch_get(dev, stream, ((size_t)nlist + 1) * 4, &lw, 2);
     if (rc != NBODY_OK) return rc;
     int *list = (int *)lw;
-    e = nbk::launch_tree_lists(leaf_key, leaf_level, start, counters, nleaf, nullptr, list_off,
-                               list, stream);
+    e = nbk::launch_tree_lists(lv, counters, nullptr, nullptr, cnt, list, list_off, stream);
     if (e == hipSuccess) {
         nbk::P2PArgs a{spos, n, eps2, start, nleaf, list_off, list, (long long)nlist,
                        (float4 *)acc_out, pot_out, perm};

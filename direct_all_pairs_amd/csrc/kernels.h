@@ -155,11 +155,14 @@ hipError_t launch_gather(const float4 *pos, const int *perm, int n, float4 *out,
 hipError_t launch_cell_starts(const unsigned *sorted_keys, int n, int ncell, int *cell_start,
                               hipStream_t stream);
 // Stable sort of (key, value) pairs on bits [0, end_bit) of the keys (keys below
-// 2^end_bit): LSD radix sort, 8 bits per pass. temp holds sort_temp_bytes(n)
-// bytes; the inputs are read only.
-size_t sort_temp_bytes(int n);
+// 2^end_bit): LSD radix sort, 8 bits per pass, 32- or 64-bit keys. temp holds
+// sort_temp_bytes(n, key bytes) bytes; the inputs are read only.
+size_t sort_temp_bytes(int n, int key_bytes = 4);
 hipError_t sort_pairs(void *temp, const unsigned *keys_in, unsigned *keys_out, const int *vals_in,
                       int *vals_out, int n, int end_bit, hipStream_t stream);
+hipError_t sort_pairs64(void *temp, const unsigned long long *keys_in,
+                        unsigned long long *keys_out, const int *vals_in, int *vals_out, int n,
+                        int end_bit, hipStream_t stream);
 
 // Exclusive prefix sum of data[0 .. total) in place (int32, exact), in tiles of
 // 4096 entries; *total_out (device, may be null) receives the sum of all entries.
@@ -171,40 +174,57 @@ hipError_t scan_exclusive(int *data, long long total, int *total_out, void *temp
 // ---- Near field over the leaves of an octree in Morton order (nbody_near_tree).
 // Every decision is taken in float32 / integer arithmetic on the device:
 //   root cube: lo_d = smallest coordinate d, side = largest extent (1 if not
-//     positive); frame = (lo_x, lo_y, lo_z, 1024 / side);
-//   level-10 cell per axis: clamp(floor((x_d - lo_d) * (1024 / side)), 0, 1023);
-//   30-bit key: bit 3b + d is bit b of the cell coordinate d;
-//   node (L, p): the bodies whose key >> 3 (10 - L) is p; a body's leaf is the node
-//     on its path with the smallest L holding at most leaf_size bodies (else L = 10);
+//     positive); frame = (lo_x, lo_y, lo_z, 2^21 / side);
+//   level-21 cell per axis: clamp(floor((x_d - lo_d) * (2^21 / side)), 0, 2^21 - 1);
+//   63-bit key: bit 3b + d is bit b of the cell coordinate d;
+//   node (L, p): the bodies whose key >> 3 (21 - L) is p; a body's leaf is the node
+//     on its path with the smallest L holding at most leaf_size bodies (else L = 21);
 //   leaves A and B are near when their closed cubes meet.
 // Counters written by the build: [0] leaves, [1] list entries (the total of the
-// lists, below 2^31 when the build succeeds), [2..3] the list total as 64 bits,
-// [4..5] pair terms sum over leaves of |A| x sum over listed B of |B| (64 bits).
+// lists when below 2^31), [2..3] the list total as 64 bits, [4..5] pair terms: sum
+// over leaves of |A| x sum over listed B of |B| (64 bits).
 constexpr int kTreeCounters = 6;
+constexpr int kTreeTableMaxLevel = 7;                 // coarse table: at most 8^7 + 1 ints
+constexpr int kTreeMaxLeaves = (0x7fffffff - 1) / 27;  // 27 list parts per leaf, int offsets
 size_t tree_frame_temp_bytes(int n);
-// frame[0] = (lo_x, lo_y, lo_z, 1024 / side); zeroes counters[0 .. kTreeCounters).
+// frame[0] = (lo_x, lo_y, lo_z, 2^21 / side); zeroes counters[0 .. kTreeCounters).
 hipError_t launch_tree_frame(const float4 *pos, int n, float *temp, float4 *frame,
                              int *counters, hipStream_t stream);
-// keys[i] = 30-bit key of body i, idx[i] = i.
-hipError_t launch_tree_keys(const float4 *pos, int n, const float4 *frame, unsigned *keys,
-                            int *idx, hipStream_t stream);
+// keys[i] = 63-bit key of body i, idx[i] = i.
+hipError_t launch_tree_keys(const float4 *pos, int n, const float4 *frame,
+                            unsigned long long *keys, int *idx, hipStream_t stream);
 // From the sorted keys: level[k] = level of the leaf of sorted body k; start[k] = 1
 // if k begins its leaf (else 0).
-hipError_t launch_tree_levels(const unsigned *skeys, int n, int leaf_size, int *level,
+hipError_t launch_tree_levels(const unsigned long long *skeys, int n, int leaf_size, int *level,
                               int *start, hipStream_t stream);
 // After start has been scanned into leaf numbers (ids, total in counters[0]): for
 // each leaf A, cell_start[A] = its first sorted body, leaf_key[A] = its first key
-// cleared below its level, leaf_level[A]; cell_start[nleaf] = n.
-hipError_t launch_tree_leaves(const unsigned *skeys, const int *level, const int *ids, int n,
-                              int *cell_start, unsigned *leaf_key, int *leaf_level,
+// cleared below its level, leaf_box[A] = (corner x, y, z in level-21 units, level);
+// cell_start[nleaf] = n.
+hipError_t launch_tree_leaves(const unsigned long long *skeys, const int *level, const int *ids,
+                              int n, int *cell_start, unsigned long long *leaf_key, int4 *leaf_box,
                               hipStream_t stream);
-// Count pass (list == nullptr): cnt[A] = length of leaf A's list for A < nleaf
-// (counters[0]), 0 for nleaf <= A < nslots; adds the list total and the pair terms to
-// the counters. Fill pass: writes leaf A's list at list[off[A] ..] for A < nslots
-// (= nleaf), in the same order as counted.
-hipError_t launch_tree_lists(const unsigned *leaf_key, const int *leaf_level,
-                             const int *cell_start, int *counters, int nslots, int *cnt,
-                             const int *off, int *list, hipStream_t stream);
+// Coarse table level for nleaf leaves (8^lt cells, at least nleaf, at most 8^7), and
+// the table: table[c] = first leaf whose key is at least the start of cell c of level
+// lt, c = 0 .. 8^lt (8^lt + 1 ints; nleaf read from counters[0]).
+int tree_table_level(int nleaf);
+hipError_t launch_tree_table(const unsigned long long *leaf_key, const int *counters, int lt,
+                             int *table, hipStream_t stream);
+struct TreeLeaves {
+    const unsigned long long *leaf_key;
+    const int4 *leaf_box;
+    const int *table;
+    const int *cell_start;
+    int nleaf, lt;
+};
+// Count pass (list == nullptr): cnt[27 A + q] = the length of part q of leaf A's list
+// (27 nleaf + 1 entries, the last 0); the list total and the pair terms go to
+// counters[2..5] through per-workgroup records in parts (tree_parts_bytes). Fill pass
+// (off = the exclusive sums of cnt): part q of leaf A's list written at
+// list[off[27 A + q] ..], list_off[A] = off[27 A], list_off[nleaf] = the total.
+size_t tree_parts_bytes(int nleaf);
+hipError_t launch_tree_lists(const TreeLeaves &leaves, int *counters, void *parts, int *cnt,
+                             const int *off, int *list, int *list_off, hipStream_t stream);
 
 // Layout conversion for the SoA entry points: out[i] = (a[i], b[i], c[i], d ? d[i] : 0),
 // and back: a[i], b[i], c[i] = in[i].x, .y, .z.

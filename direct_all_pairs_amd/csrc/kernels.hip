@@ -1122,12 +1122,23 @@ __global__ void __launch_bounds__(256) diag_final_kernel(const double *__restric
 // list entry or a source cell with an invalid range adds nothing.
 // A list hands out source runs: entry e of [lo, hi) is a range of bodies
 // [sb, sn), or nothing (`source` returns false for an invalid or empty entry).
-struct CsrLists {
+// CSR lists are walked as one sequence of bodies cut into 64-body tiles (the
+// listed cells one after another, so small cells share tiles instead of each
+// filling part of one), kPackEntries entries at a time: for each such segment
+// wave 0 reads the entries' body ranges and writes their exclusive prefix pre[]
+// and offsets off[] (position p of the segment, pre[e] <= p < pre[e + 1], is
+// body p + off[e]) to LDS between two workgroup barriers.
+constexpr int kPackEntries = 64;
+constexpr int kPackLds = 2 * kPackEntries + 1;  // ints: pre[0 .. 64], off[0 .. 63]
+
+struct PackedLists {
     const int *off;
     const int *list;
     long long nlist;
     int ncell;
-    __device__ void bind(const P2PArgs &, int) {}
+    int *tab;         // kPackLds LDS ints (set by the kernel)
+    int bound_seg;    // segment in tab (-1: none), uniform
+    __device__ void bind(const P2PArgs &, int) { bound_seg = -1; }
     __device__ void range(int c, int &lo, int &hi) const
     {
         long long a = off[c], b = off[c + 1];
@@ -1143,6 +1154,28 @@ struct CsrLists {
         sb = k.cell_start[s];
         sn = k.cell_start[s + 1];
         return sb >= 0 && sn > sb && sn <= k.n;
+    }
+    __device__ int segments(int lo, int hi) const
+    {
+        return hi > lo ? (hi - lo + kPackEntries - 1) / kPackEntries : 0;
+    }
+    // wave 0: entries [lo + sg * 64, ...) of the list into tab
+    __device__ void load_segment(const P2PArgs &k, int lo, int hi, int sg, int lane)
+    {
+        const int e = lo + sg * kPackEntries + lane;
+        int sb = 0, sn = 0;
+        const bool ok = e < hi && source(k, e, sb, sn);
+        const int size = ok ? sn - sb : 0;
+        int incl = size;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o);
+            if (lane >= o) incl += y;
+        }
+        const int excl = incl - size;
+        tab[lane] = excl;
+        tab[kPackEntries + 1 + lane] = sb - excl;
+        if (lane == 63) tab[kPackEntries] = incl;
     }
 };
 
@@ -1282,28 +1315,37 @@ __device__ __forceinline__ bool skip_tiles(const P2PArgs &k, const Lists &lists,
 // current tile (at most 64) and load() lane's body of it (an index clamped into
 // the tile; the stage pads the lanes past count() with zero masses). All uniform
 // across the wave.
-//   RunCursor: the listed cells one after another, each cut into tiles (a cell's
-//   last tile may be part-filled): CSR lists.
-template <typename Lists>
-struct RunCursor {
-    int hi, e, j0, se;
+//   PackedListCursor: the current segment of a CSR list (PackedLists, in LDS) as
+//   one sequence of bodies in 64-body tiles; lane's body of tile t is found by a
+//   binary search of its position in the segment's prefix pre[].
+struct PackedListCursor {
+    int total, t;
+    const int *tab;  // LDS: pre[0 .. 64], off[0 .. 63]
     bool have;
-    __device__ void start(const P2PArgs &k, const Lists &l, int lo, int hi_, int w)
+    __device__ void start(const P2PArgs &, const PackedLists &l, int, int, int w)
     {
-        hi = hi_;
-        e = lo - 1;
-        j0 = 0;
-        se = 0;
-        have = skip_tiles(k, l, hi, e, j0, se, w + 1);
+        tab = l.tab;
+        total = __builtin_amdgcn_readfirstlane(tab[kPackEntries]);
+        t = w;
+        have = t * 64 < total;
     }
-    __device__ void next(const P2PArgs &k, const Lists &l, int step)
+    __device__ void next(const P2PArgs &, const PackedLists &, int step)
     {
-        have = skip_tiles(k, l, hi, e, j0, se, step);
+        t += step;
+        have = t * 64 < total;
     }
-    __device__ int count() const { return se - j0 < 64 ? se - j0 : 64; }
+    __device__ int count() const { return total - t * 64 < 64 ? total - t * 64 : 64; }
     __device__ float4 load(const P2PArgs &k, int lane) const
     {
-        return k.pos[j0 + lane < se ? j0 + lane : se - 1];
+        int p = t * 64 + lane;
+        p = p < total ? p : total - 1;
+        int a = 1, b = kPackEntries;  // the last e with pre[e] <= p (pre[0] = 0)
+        while (a < b) {
+            const int m = (a + b) >> 1;
+            if (tab[m] <= p) a = m + 1;
+            else b = m;
+        }
+        return k.pos[p + tab[kPackEntries + 1 + a - 1]];
     }
 };
 
@@ -1342,13 +1384,17 @@ struct PackedCursor {
 };
 
 template <typename Lists>
-struct CursorOf {
-    using type = RunCursor<Lists>;
+struct CursorOf;
+template <>
+struct CursorOf<PackedLists> {
+    using type = PackedListCursor;
 };
 template <>
 struct CursorOf<GridLists> {
     using type = PackedCursor;
 };
+
+
 
 // Stages the tile [j0, j0 + cnt) (loaded into cur) in the wave's LDS row, zero-mass
 // padded: the row is written and read by this wave only (LDS accesses of one wave
@@ -1360,6 +1406,45 @@ __device__ __forceinline__ void stage_row(float4 *row, int lane, int cnt, const 
     row[lane] = make_float4(in ? cur.x : 0.0f, in ? cur.y : 0.0f, in ? cur.z : 0.0f,
                             in ? cur.w : 0.0f);
     __builtin_amdgcn_wave_barrier();
+}
+
+// Runs eval(cnt) for every source tile of the target cell's walk that falls to wave w
+// of W (tiles w, w + W, ...), with the tile's cnt bodies staged in the wave's LDS row
+// (zero-mass padded). Each wave issues the global load of its next tile before it
+// evaluates the current one. CSR lists are walked segment by segment: every wave of
+// the workgroup passes the same barriers (segment count and bound segment are
+// uniform), so wave 0 may rewrite the segment table; a one-segment list stays bound
+// for the cell's later chunks.
+template <int W, typename Lists, typename F>
+__device__ __forceinline__ void walk_tiles(const P2PArgs &k, Lists &lists, int lo, int hi, int w,
+                                           int lane, float4 *row, F &&eval)
+{
+    using Cursor = typename CursorOf<Lists>::type;
+    int nseg = 1;
+    if constexpr (__is_same(Lists, PackedLists)) nseg = lists.segments(lo, hi);
+    for (int sg = 0; sg < nseg; ++sg) {
+        if constexpr (__is_same(Lists, PackedLists)) {
+            if (lists.bound_seg != sg) {
+                __syncthreads();  // every wave is done with the previous table
+                if (w == 0) lists.load_segment(k, lo, hi, sg, lane);
+                __syncthreads();
+                lists.bound_seg = sg;
+            }
+        }
+        Cursor cs;
+        cs.start(k, lists, lo, hi, w);
+        float4 cur = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (cs.have) cur = cs.load(k, lane);
+        while (cs.have) {
+            const int cnt = cs.count();
+            stage_row(row, lane, cnt, cur);
+            Cursor nx = cs;
+            nx.next(k, lists, W);
+            if (nx.have) cur = nx.load(k, lane);
+            eval(cnt);
+            cs = nx;
+        }
+    }
 }
 
 // Targets per chunk: a cell's bodies go up to 256 at a time (four per lane)
@@ -1375,10 +1460,9 @@ __global__ void __launch_bounds__(64 * W) p2p_kernel(P2PArgs k, Lists lists)
 {
     static_assert(!QUAD || W == kP2PWideT, "a 256-target chunk is finished by four waves");
     constexpr int TQ = QUAD ? kP2PWideT : 1;
-    using Cursor = typename CursorOf<Lists>::type;
     __shared__ float4 rows[W][64];
     __shared__ float4 red[W][64 * TQ];  // each wave's per-target sums of the chunk
-    __shared__ int nbr[kGridLds];
+    __shared__ int nbr[kGridLds > kPackLds ? kGridLds : kPackLds];  // the lists' LDS table
     const int c = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int tb = k.cell_start[c], te = k.cell_start[c + 1];
     if (tb < 0 || te < tb || te > k.n) return;
@@ -1387,6 +1471,7 @@ __global__ void __launch_bounds__(64 * W) p2p_kernel(P2PArgs k, Lists lists)
     const int ny = (int)gridDim.y, y = (int)blockIdx.y;
     if (y > 0 && !cell_has_chunk<QUAD>(te - tb, y)) return;
     if constexpr (__is_same(Lists, GridLists)) lists.nbr = nbr;
+    if constexpr (__is_same(Lists, PackedLists)) lists.tab = nbr;
     lists.bind(k, c);
     int lo, hi;
     lists.range(c, lo, hi);
@@ -1414,16 +1499,7 @@ __global__ void __launch_bounds__(64 * W) p2p_kernel(P2PArgs k, Lists lists)
             }
             Total<kP2PWideT, POT> tot;
             zero(tot);
-            Cursor cs;
-            cs.start(k, lists, lo, hi, w);
-            float4 cur = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            if (cs.have) cur = cs.load(k, lane);
-            while (cs.have) {
-                const int cnt = cs.count();
-                stage_row(row, lane, cnt, cur);
-                Cursor nx = cs;
-                nx.next(k, lists, W);
-                if (nx.have) cur = nx.load(k, lane);
+            walk_tiles<W>(k, lists, lo, hi, w, lane, row, [&](int cnt) {
                 Sums<kP2PWideT, POT> blk;
                 zero(blk);
                 if (cnt == 64) {
@@ -1434,8 +1510,7 @@ __global__ void __launch_bounds__(64 * W) p2p_kernel(P2PArgs k, Lists lists)
                     for (int u = 0; u < cnt; ++u) interact4<kP2PWideT, POT>(row[u], tg, eps2, blk);
                 }
                 add_into(tot, blk);
-                cs = nx;
-            }
+            });
             const Sums<kP2PWideT, POT> r = result(tot);
 #pragma unroll
             for (int q = 0; q < kP2PWideT; ++q)
@@ -1482,16 +1557,7 @@ __global__ void __launch_bounds__(64 * W) p2p_kernel(P2PArgs k, Lists lists)
         tg.z[0] = me.z;
         Total<1, POT> tot;
         zero(tot);
-        Cursor cs;
-        cs.start(k, lists, lo, hi, w);
-        float4 cur = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        if (cs.have) cur = cs.load(k, lane);
-        while (cs.have) {
-            const int cnt = cs.count();
-            stage_row(row, lane, cnt, cur);
-            Cursor nx = cs;
-            nx.next(k, lists, W);
-            if (nx.have) cur = nx.load(k, lane);
+        walk_tiles<W>(k, lists, lo, hi, w, lane, row, [&](int cnt) {
             Sums<1, POT> blk;
             zero(blk);
             if (groups == 1 && cnt == 64) {
@@ -1504,8 +1570,7 @@ __global__ void __launch_bounds__(64 * W) p2p_kernel(P2PArgs k, Lists lists)
                     interact4<1, POT>(row[u0 + g], tg, eps2, blk);
             }
             add_into(tot, blk);
-            cs = nx;
-        }
+        });
         const Sums<1, POT> r = result(tot);
         float4 a = make_float4(r.ax[0], r.ay[0], r.az[0], POT ? r.p[0] : 0.0f);
         if constexpr (W > 1) {
@@ -1580,6 +1645,7 @@ __global__ void __launch_bounds__(256) p2p_wg_kernel(P2PArgs k, Lists lists)
     const int ny = (int)gridDim.y, y = (int)blockIdx.y;
     if (y > 0 && tb + 256 * y >= te) return;
     if constexpr (__is_same(Lists, GridLists)) lists.nbr = nbr;
+    if constexpr (__is_same(Lists, PackedLists)) lists.tab = nbr;
     lists.bind(k, c);
     int lo, hi;
     lists.range(c, lo, hi);
@@ -1706,6 +1772,9 @@ constexpr int kSortBits = 8;
 constexpr int kSortDigits = 1 << kSortBits;  // 256: one counter per thread
 constexpr int kSortMaxBlocks = 2048;         // counts <= 2^19 entries: <= 128 scan tiles
 constexpr int kSortScanThreads = 1024;
+constexpr int kSortKeysPerBlock = 4096;      // most keys per workgroup (up to N = 2^23)
+constexpr int kSortMinKeysPerBlock = 1024;   // fewest keys per workgroup
+constexpr int kSortTargetBlocks = 512;
 
 struct SortShape {
     int nblocks;  // workgroups per pass
@@ -1714,7 +1783,12 @@ struct SortShape {
 
 SortShape sort_shape(int n)
 {
-    int nb = (n + 4095) / 4096;
+    // about kSortTargetBlocks workgroups of 1024 to 4096 keys (measured: 1024 keys per
+    // workgroup at N = 2^16 and 300,007 bodies, 2048 at 2^20)
+    long long want = (long long)n / kSortTargetBlocks;
+    want = want < kSortMinKeysPerBlock ? kSortMinKeysPerBlock
+                                       : (want > kSortKeysPerBlock ? kSortKeysPerBlock : want);
+    int nb = (int)(((long long)n + want - 1) / want);
     if (nb > kSortMaxBlocks) nb = kSortMaxBlocks;
     if (nb < 1) nb = 1;
     long long per = ((long long)n + nb - 1) / nb;
@@ -1731,7 +1805,8 @@ __device__ __forceinline__ void sort_range(int n, int per, int &b0, int &e)
     e = (int)(z < n ? z : n);
 }
 
-__global__ void __launch_bounds__(256) sort_hist_kernel(const unsigned *__restrict__ keys, int n,
+template <typename K>
+__global__ void __launch_bounds__(256) sort_hist_kernel(const K *__restrict__ keys, int n,
                                                         int per, int shift, int nblocks,
                                                         int *__restrict__ counts)
 {
@@ -1741,7 +1816,7 @@ __global__ void __launch_bounds__(256) sort_hist_kernel(const unsigned *__restri
     int b0, e;
     sort_range(n, per, b0, e);
     for (int i = b0 + (int)threadIdx.x; i < e; i += 256)
-        atomicAdd(&h[(keys[i] >> shift) & (kSortDigits - 1)], 1);
+        atomicAdd(&h[(unsigned)(keys[i] >> shift) & (kSortDigits - 1)], 1);
     __syncthreads();
     counts[threadIdx.x * nblocks + blockIdx.x] = h[threadIdx.x];
 }
@@ -1821,11 +1896,12 @@ __global__ void __launch_bounds__(kSortScanThreads)
     }
 }
 
-__global__ void __launch_bounds__(256) sort_scatter_kernel(const unsigned *__restrict__ kin,
+template <typename K>
+__global__ void __launch_bounds__(256) sort_scatter_kernel(const K *__restrict__ kin,
                                                            const int *__restrict__ vin, int n,
                                                            int per, int shift, int nblocks,
                                                            const int *__restrict__ offsets,
-                                                           unsigned *__restrict__ kout,
+                                                           K *__restrict__ kout,
                                                            int *__restrict__ vout)
 {
     __shared__ int base[kSortDigits];     // running output position of each digit
@@ -1838,15 +1914,15 @@ __global__ void __launch_bounds__(256) sort_scatter_kernel(const unsigned *__res
     int b0, e;
     sort_range(n, per, b0, e);
     bool valid = b0 + tid < e;
-    unsigned k = valid ? kin[b0 + tid] : 0u;
+    K k = valid ? kin[b0 + tid] : K(0);
     int v = valid ? vin[b0 + tid] : 0;
     for (int s0 = b0; s0 < e; s0 += 256) {
         // the next sub-tile's pair, loaded while this one is placed
         const int ni = s0 + 256 + tid;
         const bool nvalid = ni < e;
-        const unsigned nk = nvalid ? kin[ni] : 0u;
+        const K nk = nvalid ? kin[ni] : K(0);
         const int nv = nvalid ? vin[ni] : 0;
-        const unsigned d = (k >> shift) & (kSortDigits - 1);
+        const unsigned d = (unsigned)(k >> shift) & (kSortDigits - 1);
         // the valid lanes of this wave whose key has digit d
         unsigned long long same = __ballot(valid);
 #pragma unroll
@@ -1924,47 +2000,61 @@ __global__ void __launch_bounds__(kSortScanThreads)
 // nbody_near_tree builds the leaves of an octree over the bodies and their
 // interaction lists, then runs the near-field kernel over them. The tree is
 // implicit in the Morton order: node (L, p) is the run of sorted keys whose top
-// 3L bits are p. Steps (each a kernel, every decision in float32 or integers):
+// 3L bits (of 63) are p. Steps (each a kernel, every decision in float32 or
+// integers):
 //   bounds  - smallest and largest coordinate per axis (exact: min and max);
-//   keys    - the 30-bit key of each body in the root cube, then the stable sort;
+//   keys    - the 63-bit key of each body in the root cube, then the stable sort;
 //   levels  - each sorted body's leaf level by bisection over L, with the size of
 //             its node at level L found by two binary searches confined to the
 //             leaf_size bodies on either side of it (a node reaching past them
 //             holds more than leaf_size);
-//   leaves  - the bodies where a leaf begins, scanned into leaf numbers;
-//   lists   - per leaf, the leaves meeting its closed cube: for each of the 27
-//             cells of its own level around it (its own cell included), the leaf
-//             that holds the whole cell (listed once, from the first such cell),
-//             or else the deeper leaves inside the cell whose cubes meet it. Every
-//             leaf meeting the cube lies in or over one of these cells. A count
-//             pass and a fill pass run the same enumeration.
-constexpr int kTreeBits = 10;       // levels below the root
+//   leaves  - the bodies where a leaf begins, scanned into leaf numbers; each
+//             leaf's key, level and cube;
+//   table   - for the cells of one coarse level, the first leaf at or after each,
+//             so that a search for a key starts inside one cell's leaves;
+//   lists   - one thread per (leaf A, cell q of the 27 of A's level around it): the
+//             leaf that holds the whole cell q (listed once, from the first such
+//             cell), or else the deeper leaves inside q whose cubes meet A's, found
+//             by walking q's leaves in key order and skipping, past a leaf that
+//             misses A, the largest subtree around it that misses A. Every leaf
+//             meeting A's closed cube lies in or over one of the 27 cells. A count
+//             pass and a fill pass run the same enumeration; leaf A's list is the
+//             concatenation of its 27 parts in q order.
+constexpr int kTreeBits = 21;  // levels below the root
 constexpr int kTreeBoundsBlocks = 512;
+using u64 = unsigned long long;
 
-__device__ __forceinline__ unsigned tree_spread(unsigned c)  // bit b of c -> bit 3b
+__device__ __forceinline__ u64 tree_spread(unsigned c)  // bit b of c -> bit 3b
 {
-    unsigned r = 0;
+    u64 r = 0;
 #pragma unroll
-    for (int b = 0; b < kTreeBits; ++b) r |= ((c >> b) & 1u) << (3 * b);
+    for (int b = 0; b < kTreeBits; ++b) r |= (u64)((c >> b) & 1u) << (3 * b);
     return r;
 }
 
-__device__ __forceinline__ int tree_gather(unsigned k, int bits)  // bit 3b of k -> bit b
+__device__ __forceinline__ int tree_gather(u64 k, int bits)  // bit 3b of k -> bit b
 {
     unsigned r = 0;
-    for (int b = 0; b < bits; ++b) r |= ((k >> (3 * b)) & 1u) << b;
+    for (int b = 0; b < bits; ++b) r |= (unsigned)((k >> (3 * b)) & 1u) << b;
     return (int)r;
 }
 
 __device__ __forceinline__ unsigned tree_cell(float x, float lo, float inv)
 {
+    constexpr float top = (float)((1 << kTreeBits) - 1);
     float f = floorf((x - lo) * inv);
     if (!(f >= 0.0f)) f = 0.0f;
-    if (f > 1023.0f) f = 1023.0f;
+    if (f > top) f = top;
     return (unsigned)f;
 }
 
 __device__ __forceinline__ int tree_shift(int level) { return 3 * (kTreeBits - level); }
+
+__device__ __forceinline__ u64 tree_key(int x, int y, int z, int level)  // cell start key
+{
+    return (tree_spread((unsigned)x) | (tree_spread((unsigned)y) << 1) |
+            (tree_spread((unsigned)z) << 2)) << tree_shift(level);
+}
 
 __global__ void __launch_bounds__(256) tree_bounds_kernel(const float4 *__restrict__ pos, int n,
                                                           float *__restrict__ part)
@@ -2025,13 +2115,13 @@ __global__ void __launch_bounds__(64) tree_frame_kernel(const float *__restrict_
             if (ext > side) side = ext;
         }
         if (!(side > 0.0f)) side = 1.0f;
-        frame[0] = make_float4(v[0], v[1], v[2], 1024.0f / side);
+        frame[0] = make_float4(v[0], v[1], v[2], (float)(1 << kTreeBits) / side);
     }
 }
 
 __global__ void __launch_bounds__(256) tree_keys_kernel(const float4 *__restrict__ pos, int n,
                                                         const float4 *__restrict__ frame,
-                                                        unsigned *__restrict__ keys,
+                                                        u64 *__restrict__ keys,
                                                         int *__restrict__ idx)
 {
     const int i = blockIdx.x * 256 + threadIdx.x;
@@ -2046,11 +2136,11 @@ __global__ void __launch_bounds__(256) tree_keys_kernel(const float4 *__restrict
 // Does the node at level L holding sorted body k have at most S bodies? Its first
 // and last bodies are searched for among the S bodies before and after k only: a
 // node reaching past them holds at least S + 1.
-__device__ __forceinline__ bool tree_node_fits(const unsigned *__restrict__ keys, int n, int k,
-                                               unsigned key, int L, int S)
+__device__ __forceinline__ bool tree_node_fits(const u64 *__restrict__ keys, int n, int k,
+                                               u64 key, int L, int S)
 {
     const int s = tree_shift(L);
-    const unsigned p = key >> s;
+    const u64 p = key >> s;
     int a = k - S > 0 ? k - S : 0, b = k;  // first index in [a, k] with prefix p
     while (a < b) {
         const int m = a + (b - a) / 2;
@@ -2069,19 +2159,19 @@ __device__ __forceinline__ bool tree_node_fits(const unsigned *__restrict__ keys
 
 // Sorted body k begins its leaf (of level L) when the body before it lies in another
 // node of that level.
-__device__ __forceinline__ bool tree_leaf_begins(const unsigned *__restrict__ keys, int k, int L)
+__device__ __forceinline__ bool tree_leaf_begins(const u64 *__restrict__ keys, int k, int L)
 {
     const int s = tree_shift(L);
     return k == 0 || (keys[k - 1] >> s) != (keys[k] >> s);
 }
 
-__global__ void __launch_bounds__(256) tree_levels_kernel(const unsigned *__restrict__ keys, int n,
+__global__ void __launch_bounds__(256) tree_levels_kernel(const u64 *__restrict__ keys, int n,
                                                           int S, int *__restrict__ level,
                                                           int *__restrict__ start)
 {
     const int k = blockIdx.x * 256 + threadIdx.x;
     if (k >= n) return;
-    const unsigned key = keys[k];
+    const u64 key = keys[k];
     int lo = 0, hi = kTreeBits;  // node sizes shrink with L: the first L that fits
     while (lo < hi) {
         const int L = (lo + hi) >> 1;
@@ -2092,12 +2182,14 @@ __global__ void __launch_bounds__(256) tree_levels_kernel(const unsigned *__rest
     start[k] = tree_leaf_begins(keys, k, lo) ? 1 : 0;
 }
 
-__global__ void __launch_bounds__(256) tree_leaves_kernel(const unsigned *__restrict__ keys,
+// Leaf A: cell_start[A] = its first sorted body, key (cleared below its level),
+// box = (corner x, y, z in level-21 units, level).
+__global__ void __launch_bounds__(256) tree_leaves_kernel(const u64 *__restrict__ keys,
                                                           const int *__restrict__ level,
                                                           const int *__restrict__ ids, int n,
                                                           int *__restrict__ cell_start,
-                                                          unsigned *__restrict__ leaf_key,
-                                                          int *__restrict__ leaf_level)
+                                                          u64 *__restrict__ leaf_key,
+                                                          int4 *__restrict__ leaf_box)
 {
     const int k = blockIdx.x * 256 + threadIdx.x;
     if (k >= n) return;
@@ -2105,124 +2197,216 @@ __global__ void __launch_bounds__(256) tree_leaves_kernel(const unsigned *__rest
     const bool first = tree_leaf_begins(keys, k, L);
     const int a = ids[k];
     if (first) {
+        const u64 p = keys[k] >> s;
         cell_start[a] = k;
-        leaf_key[a] = (keys[k] >> s) << s;
-        leaf_level[a] = L;
+        leaf_key[a] = p << s;
+        const int sh = kTreeBits - L;
+        leaf_box[a] = make_int4(tree_gather(p, L) << sh, tree_gather(p >> 1, L) << sh,
+                                tree_gather(p >> 2, L) << sh, L);
     }
     if (k == n - 1) cell_start[a + (first ? 1 : 0)] = n;
 }
 
-// First leaf whose key is above x (upper) / at least x (lower), over leaf_key[0 .. nleaf).
-__device__ __forceinline__ int tree_upper(const unsigned *__restrict__ leaf_key, int nleaf,
-                                          unsigned x)
+// Coarse table: table[c] = first leaf whose key is at least the start of cell c of
+// level lt, for c = 0 .. 8^lt (the last: nleaf).
+__global__ void __launch_bounds__(256) tree_table_kernel(const u64 *__restrict__ leaf_key,
+                                                         const int *__restrict__ counters,
+                                                         int lt, int *__restrict__ table)
 {
-    int a = 0, b = nleaf;
-    while (a < b) {
-        const int m = a + (b - a) / 2;
-        if (leaf_key[m] <= x) a = m + 1;
-        else b = m;
+    const long long c = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long cells = 1ll << (3 * lt);
+    if (c > cells) return;
+    const int nleaf = counters[0];
+    if (c == cells) {
+        table[c] = nleaf;
+        return;
     }
-    return a;
-}
-
-__device__ __forceinline__ int tree_lower(const unsigned *__restrict__ leaf_key, int nleaf,
-                                          unsigned x)
-{
+    const u64 x = (u64)c << tree_shift(lt);
     int a = 0, b = nleaf;
     while (a < b) {
         const int m = a + (b - a) / 2;
         if (leaf_key[m] < x) a = m + 1;
         else b = m;
     }
-    return a;
+    table[c] = a;
 }
 
-__device__ __forceinline__ void tree_coords(unsigned key, int L, int (&c)[3])
+struct TreeIndex {
+    const u64 *key;      // leaf keys, ascending
+    const int4 *box;     // leaf cubes
+    const int *table;    // coarse table over level lt
+    int nleaf, lt;
+    // first leaf in [a, b) with key >= x (lower) / > x (upper); b if none
+    __device__ int lower_in(int a, int b, u64 x) const
+    {
+        while (a < b) {
+            const int m = a + (b - a) / 2;
+            if (key[m] < x) a = m + 1;
+            else b = m;
+        }
+        return a;
+    }
+    __device__ int upper_in(int a, int b, u64 x) const
+    {
+        while (a < b) {
+            const int m = a + (b - a) / 2;
+            if (key[m] <= x) a = m + 1;
+            else b = m;
+        }
+        return a;
+    }
+    // the leaves with keys in x's coarse cell are [table[c], table[c + 1])
+    __device__ int lower(u64 x) const
+    {
+        const u64 c = x >> tree_shift(lt);
+        if (c >= (1ull << (3 * lt))) return nleaf;  // x = 2^63: past every key
+        return lower_in(table[c], table[c + 1], x);
+    }
+    __device__ int upper(u64 x) const
+    {
+        const u64 c = x >> tree_shift(lt);
+        return upper_in(table[c], table[c + 1], x);
+    }
+};
+
+// Do the closed cubes (o, level l) and A's (oa, size sa) meet? Coordinates in level-21 units.
+__device__ __forceinline__ bool tree_meet(int ox, int oy, int oz, int l, const int (&oa)[3],
+                                          int sa)
 {
-    const unsigned p = key >> tree_shift(L);
-#pragma unroll
-    for (int d = 0; d < 3; ++d) c[d] = tree_gather(p >> d, L);
+    const int sb = 1 << (kTreeBits - l);
+    return ox <= oa[0] + sa && oa[0] <= ox + sb && oy <= oa[1] + sa && oa[1] <= oy + sb &&
+           oz <= oa[2] + sa && oa[2] <= oz + sb;
 }
 
 template <bool FILL>
-__global__ void __launch_bounds__(256) tree_lists_kernel(const unsigned *__restrict__ leaf_key,
-                                                         const int *__restrict__ leaf_level,
+__global__ void __launch_bounds__(256) tree_lists_kernel(TreeIndex ix,
                                                          const int *__restrict__ cell_start,
-                                                         int *__restrict__ counters, int nslots,
+                                                         longlong2 *__restrict__ part,
                                                          int *__restrict__ cnt,
                                                          const int *__restrict__ off,
-                                                         int *__restrict__ list)
+                                                         int *__restrict__ list,
+                                                         int *__restrict__ list_off)
 {
-    const int A = blockIdx.x * 256 + threadIdx.x;
-    if (A >= nslots) return;
-    const int nleaf = counters[0];
-    if (A >= nleaf) {
-        if (!FILL) cnt[A] = 0;
-        return;
-    }
-    const int L = leaf_level[A], s = tree_shift(L), lim = 1 << L;
-    int ca[3];
-    tree_coords(leaf_key[A], L, ca);
-    long long at = 0, end = 0;
-    if (FILL) {
-        at = off[A];
-        end = off[A + 1];
-    }
+    const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+    const int nleaf = ix.nleaf;
+    const bool live = t < 27ll * nleaf;
+    if (!FILL && t == 27ll * nleaf) cnt[t] = 0;  // the entry past the last part
     int w = 0;
     long long terms = 0;
-    auto emit = [&](int B) {
+    if (live) {
+        const int A = (int)(t / 27), q = (int)(t % 27);
+        const int4 ba = ix.box[A];
+        const int L = ba.w, s = tree_shift(L), lim = 1 << L, sh = kTreeBits - L;
+        const int oa[3] = {ba.x, ba.y, ba.z};
+        const int sa = 1 << sh;
+        const int ca[3] = {ba.x >> sh, ba.y >> sh, ba.z >> sh};
+        long long at = 0, end = 0;
         if (FILL) {
-            if (at + w < end) list[at + w] = B;
-        } else {
-            terms += cell_start[B + 1] - cell_start[B];
+            at = off[t];
+            end = off[t + 1];
+            if (q == 0) list_off[A] = (int)at;
+            if (A == nleaf - 1 && q == 26) list_off[nleaf] = (int)end;
         }
-        ++w;
-    };
-    for (int q = 0; q < 27; ++q) {
+        auto emit = [&](int B) {
+            if (FILL) {
+                if (at + w < end) list[at + w] = B;
+            } else {
+                terms += cell_start[B + 1] - cell_start[B];
+            }
+            ++w;
+        };
         const int cq[3] = {ca[0] + q % 3 - 1, ca[1] + (q / 3) % 3 - 1, ca[2] + q / 9 - 1};
-        if (cq[0] < 0 || cq[1] < 0 || cq[2] < 0 || cq[0] >= lim || cq[1] >= lim || cq[2] >= lim)
-            continue;
-        const unsigned qk = (tree_spread((unsigned)cq[0]) | (tree_spread((unsigned)cq[1]) << 1) |
-                             (tree_spread((unsigned)cq[2]) << 2)) << s;
-        const unsigned qe = qk + (1u << s);
-        const int b = tree_upper(leaf_key, nleaf, qk) - 1;
-        const int lb = b >= 0 ? leaf_level[b] : kTreeBits + 1;
-        if (lb <= L && qk < leaf_key[b] + (1u << tree_shift(lb))) {
-            // leaf b holds the whole cell: listed from the first in-range cell inside it
-            const int t = L - lb;
-            bool seen = false;
-            for (int r = 0; r < q && !seen; ++r) {
-                const int cr[3] = {ca[0] + r % 3 - 1, ca[1] + (r / 3) % 3 - 1, ca[2] + r / 9 - 1};
-                if (cr[0] < 0 || cr[1] < 0 || cr[2] < 0 || cr[0] >= lim || cr[1] >= lim ||
-                    cr[2] >= lim)
-                    continue;
-                seen = (cr[0] >> t) == (cq[0] >> t) && (cr[1] >> t) == (cq[1] >> t) &&
-                       (cr[2] >> t) == (cq[2] >> t);
+        if (cq[0] >= 0 && cq[1] >= 0 && cq[2] >= 0 && cq[0] < lim && cq[1] < lim && cq[2] < lim) {
+            const u64 qk = tree_key(cq[0], cq[1], cq[2], L);
+            const int b = ix.upper(qk) - 1;
+            const int4 bb = b >= 0 ? ix.box[b] : make_int4(0, 0, 0, kTreeBits + 1);
+            if (bb.w <= L && qk < ix.key[b] + (1ull << tree_shift(bb.w))) {
+                // leaf b holds the whole cell: listed from the first in-range cell inside it
+                const int u = L - bb.w;
+                bool seen = false;
+                for (int r = 0; r < q && !seen; ++r) {
+                    const int cr[3] = {ca[0] + r % 3 - 1, ca[1] + (r / 3) % 3 - 1,
+                                       ca[2] + r / 9 - 1};
+                    if (cr[0] < 0 || cr[1] < 0 || cr[2] < 0 || cr[0] >= lim || cr[1] >= lim ||
+                        cr[2] >= lim)
+                        continue;
+                    seen = (cr[0] >> u) == (cq[0] >> u) && (cr[1] >> u) == (cq[1] >> u) &&
+                           (cr[2] >> u) == (cq[2] >> u);
+                }
+                if (!seen) emit(b);
+            } else {
+                // the deeper leaves inside the cell, in key order
+                const u64 qe = qk + (1ull << s);
+                int B = ix.lower(qk);
+                const int E = ix.lower(qe);
+                while (B < E) {
+                    const int4 bx = ix.box[B];
+                    if (tree_meet(bx.x, bx.y, bx.z, bx.w, oa, sa)) {
+                        emit(B);
+                        ++B;
+                        continue;
+                    }
+                    // the coarsest ancestor of B below the cell that misses A: every leaf
+                    // in it misses A too
+                    int l = L + 1;
+                    for (; l < bx.w; ++l) {
+                        const int m = ~((1 << (kTreeBits - l)) - 1);
+                        if (!tree_meet(bx.x & m, bx.y & m, bx.z & m, l, oa, sa)) break;
+                    }
+                    const int sl = tree_shift(l);
+                    const u64 past = ((ix.key[B] >> sl) + 1) << sl;
+                    B = ix.lower_in(B + 1, E, past);
+                }
             }
-            if (!seen) emit(b);
-            continue;
         }
-        // deeper leaves inside the cell: listed when their closed cubes meet A's
-        const int sa = 1 << (kTreeBits - L);
-        for (int B = tree_lower(leaf_key, nleaf, qk); B < nleaf && leaf_key[B] < qe; ++B) {
-            const int LB = leaf_level[B], sb = 1 << (kTreeBits - LB);
-            int cb[3];
-            tree_coords(leaf_key[B], LB, cb);
-            bool meet = true;
-#pragma unroll
-            for (int d = 0; d < 3; ++d) {
-                const int oa = ca[d] * sa, ob = cb[d] * sb;
-                meet = meet && ob <= oa + sa && oa <= ob + sb;
-            }
-            if (meet) emit(B);
-        }
+        if (!FILL) cnt[t] = w;
     }
     if (!FILL) {
-        cnt[A] = w;
-        atomicAdd(reinterpret_cast<unsigned long long *>(counters + 2), (unsigned long long)w);
-        const long long na = cell_start[A + 1] - cell_start[A];
-        atomicAdd(reinterpret_cast<unsigned long long *>(counters + 4),
-                  (unsigned long long)(na * terms));
+        // the workgroup's list entries and pair terms, added later in workgroup order
+        // (integers: exact); one record per workgroup, no contended atomics
+        __shared__ long long red[2][4];
+        long long tw = w, tt = live ? terms * (long long)(cell_start[t / 27 + 1] -
+                                                          cell_start[t / 27]) : 0;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            tw += __shfl_xor(tw, o);
+            tt += __shfl_xor(tt, o);
+        }
+        if ((threadIdx.x & 63) == 0) {
+            red[0][threadIdx.x >> 6] = tw;
+            red[1][threadIdx.x >> 6] = tt;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0)
+            part[blockIdx.x] = make_longlong2(red[0][0] + red[0][1] + red[0][2] + red[0][3],
+                                              red[1][0] + red[1][1] + red[1][2] + red[1][3]);
+    }
+}
+
+// counters[2..3] = sum of part[].x (list entries), counters[4..5] = sum of part[].y
+// (pair terms), as 64-bit integers.
+__global__ void __launch_bounds__(256) tree_totals_kernel(const longlong2 *__restrict__ part,
+                                                          int nparts, int *__restrict__ counters)
+{
+    __shared__ long long red[2][4];
+    long long a = 0, b = 0;
+    for (int i = threadIdx.x; i < nparts; i += 256) {
+        a += part[i].x;
+        b += part[i].y;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        a += __shfl_xor(a, o);
+        b += __shfl_xor(b, o);
+    }
+    if ((threadIdx.x & 63) == 0) {
+        red[0][threadIdx.x >> 6] = a;
+        red[1][threadIdx.x >> 6] = b;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        *reinterpret_cast<u64 *>(counters + 2) = (u64)(red[0][0] + red[0][1] + red[0][2] + red[0][3]);
+        *reinterpret_cast<u64 *>(counters + 4) = (u64)(red[1][0] + red[1][1] + red[1][2] + red[1][3]);
     }
 }
 
@@ -2418,7 +2602,8 @@ hipError_t launch_p2p_any(bool pot, bool wide, const P2PArgs &args, Lists l, hip
 hipError_t launch_p2p(bool pot, bool wide, const P2PArgs &args, hipStream_t stream)
 {
     if (args.ncell < 1) return args.ncell == 0 ? hipSuccess : hipErrorInvalidValue;
-    return launch_p2p_any(pot, wide, args, CsrLists{args.list_off, args.list, args.nlist, args.ncell},
+    return launch_p2p_any(pot, wide, args,
+                          PackedLists{args.list_off, args.list, args.nlist, args.ncell, nullptr, -1},
                           stream);
 }
 
@@ -2459,23 +2644,27 @@ hipError_t launch_cell_starts(const unsigned *sorted_keys, int n, int ncell, int
                            dim3((unsigned)((ncell + 1 + 255) / 256)), dim3(256), k, 0, stream);
 }
 
-size_t sort_temp_bytes(int n)
+size_t sort_temp_bytes(int n, int key_bytes)
 {
     const SortShape sh = sort_shape(n < 1 ? 1 : n);
-    const size_t keys = ((size_t)(n < 1 ? 1 : n) * 4 + 255) / 256 * 256;
+    const size_t keys = ((size_t)(n < 1 ? 1 : n) * (size_t)key_bytes + 255) / 256 * 256;
+    const size_t vals = ((size_t)(n < 1 ? 1 : n) * 4 + 255) / 256 * 256;
     const size_t counts = ((size_t)kSortDigits * (size_t)sh.nblocks * sizeof(int) + 255) / 256 * 256;
-    return 2 * keys + counts + (size_t)kSortScanThreads * sizeof(int);
+    return keys + vals + counts + (size_t)kSortScanThreads * sizeof(int);
 }
 
-hipError_t sort_pairs(void *temp, const unsigned *keys_in, unsigned *keys_out, const int *vals_in,
-                      int *vals_out, int n, int end_bit, hipStream_t stream)
+template <typename K>
+hipError_t sort_pairs_t(void *temp, const K *keys_in, K *keys_out, const int *vals_in,
+                        int *vals_out, int n, int end_bit, hipStream_t stream)
 {
-    if (n < 1 || end_bit < 1 || end_bit > 32 || !temp) return hipErrorInvalidValue;
+    if (n < 1 || end_bit < 1 || end_bit > (int)(8 * sizeof(K)) || !temp)
+        return hipErrorInvalidValue;
     const SortShape sh = sort_shape(n);
-    const size_t keys = ((size_t)n * 4 + 255) / 256 * 256;
-    unsigned *k_alt = (unsigned *)temp;
+    const size_t keys = ((size_t)n * sizeof(K) + 255) / 256 * 256;
+    const size_t vals = ((size_t)n * 4 + 255) / 256 * 256;
+    K *k_alt = (K *)temp;
     int *v_alt = (int *)((char *)temp + keys);
-    int *counts = (int *)((char *)temp + 2 * keys);
+    int *counts = (int *)((char *)temp + keys + vals);
     int total = kSortDigits * sh.nblocks;
     int *tile_sums = (int *)((char *)counts +
                              ((size_t)total * sizeof(int) + 255) / 256 * 256);
@@ -2483,19 +2672,19 @@ hipError_t sort_pairs(void *temp, const unsigned *keys_in, unsigned *keys_out, c
     static_assert(kSortDigits * kSortMaxBlocks <= kSortScanTile * kSortScanThreads,
                   "one scan workgroup adds at most kSortScanThreads tile sums");
     const int passes = (end_bit + kSortBits - 1) / kSortBits;
-    const unsigned *ks = keys_in;
+    const K *ks = keys_in;
     const int *vs = vals_in;
     int nn = n, per = sh.per, nbl = sh.nblocks;
     for (int p = 0; p < passes; ++p) {
         // the last pass writes the outputs; before it, the two buffers alternate so that
         // no pass reads the array it writes
         const bool to_out = (passes - 1 - p) % 2 == 0;
-        unsigned *kd = to_out ? keys_out : k_alt;
+        K *kd = to_out ? keys_out : k_alt;
         int *vd = to_out ? vals_out : v_alt;
         int shift = p * kSortBits;
         void *a1[] = {&ks, &nn, &per, &shift, &nbl, &counts};
-        hipError_t e = hipLaunchKernel((const void *)&sort_hist_kernel, dim3(nbl), dim3(256), a1,
-                                       0, stream);
+        hipError_t e = hipLaunchKernel((const void *)&sort_hist_kernel<K>, dim3(nbl), dim3(256),
+                                       a1, 0, stream);
         if (e != hipSuccess) return e;
         void *a2[] = {&counts, &total, &tile_sums};
         e = hipLaunchKernel((const void *)&sort_tile_sums_kernel, dim3(ntiles),
@@ -2505,13 +2694,27 @@ hipError_t sort_pairs(void *temp, const unsigned *keys_in, unsigned *keys_out, c
                             a2, 0, stream);
         if (e != hipSuccess) return e;
         void *a3[] = {&ks, &vs, &nn, &per, &shift, &nbl, &counts, &kd, &vd};
-        e = hipLaunchKernel((const void *)&sort_scatter_kernel, dim3(nbl), dim3(256), a3, 0,
+        e = hipLaunchKernel((const void *)&sort_scatter_kernel<K>, dim3(nbl), dim3(256), a3, 0,
                             stream);
         if (e != hipSuccess) return e;
         ks = kd;
         vs = vd;
     }
     return hipSuccess;
+}
+
+hipError_t sort_pairs(void *temp, const unsigned *keys_in, unsigned *keys_out, const int *vals_in,
+                      int *vals_out, int n, int end_bit, hipStream_t stream)
+{
+    return sort_pairs_t<unsigned>(temp, keys_in, keys_out, vals_in, vals_out, n, end_bit, stream);
+}
+
+hipError_t sort_pairs64(void *temp, const unsigned long long *keys_in,
+                        unsigned long long *keys_out, const int *vals_in, int *vals_out, int n,
+                        int end_bit, hipStream_t stream)
+{
+    return sort_pairs_t<unsigned long long>(temp, keys_in, keys_out, vals_in, vals_out, n,
+                                            end_bit, stream);
 }
 
 size_t scan_temp_bytes(long long total)
@@ -2564,8 +2767,8 @@ hipError_t launch_tree_frame(const float4 *pos, int n, float *temp, float4 *fram
     return hipLaunchKernel((const void *)&tree_frame_kernel, dim3(1), dim3(64), b, 0, stream);
 }
 
-hipError_t launch_tree_keys(const float4 *pos, int n, const float4 *frame, unsigned *keys,
-                            int *idx, hipStream_t stream)
+hipError_t launch_tree_keys(const float4 *pos, int n, const float4 *frame,
+                            unsigned long long *keys, int *idx, hipStream_t stream)
 {
     if (n <= 0) return n == 0 ? hipSuccess : hipErrorInvalidValue;
     void *a[] = {&pos, &n, &frame, &keys, &idx};
@@ -2573,8 +2776,8 @@ hipError_t launch_tree_keys(const float4 *pos, int n, const float4 *frame, unsig
                            dim3(256), a, 0, stream);
 }
 
-hipError_t launch_tree_levels(const unsigned *skeys, int n, int leaf_size, int *level, int *start,
-                              hipStream_t stream)
+hipError_t launch_tree_levels(const unsigned long long *skeys, int n, int leaf_size, int *level,
+                              int *start, hipStream_t stream)
 {
     if (n <= 0) return n == 0 ? hipSuccess : hipErrorInvalidValue;
     if (leaf_size < 1) return hipErrorInvalidValue;
@@ -2583,27 +2786,56 @@ hipError_t launch_tree_levels(const unsigned *skeys, int n, int leaf_size, int *
                            dim3(256), a, 0, stream);
 }
 
-hipError_t launch_tree_leaves(const unsigned *skeys, const int *level, const int *ids, int n,
-                              int *cell_start, unsigned *leaf_key, int *leaf_level,
+hipError_t launch_tree_leaves(const unsigned long long *skeys, const int *level, const int *ids,
+                              int n, int *cell_start, unsigned long long *leaf_key, int4 *leaf_box,
                               hipStream_t stream)
 {
     if (n <= 0) return n == 0 ? hipSuccess : hipErrorInvalidValue;
-    void *a[] = {&skeys, &level, &ids, &n, &cell_start, &leaf_key, &leaf_level};
+    void *a[] = {&skeys, &level, &ids, &n, &cell_start, &leaf_key, &leaf_box};
     return hipLaunchKernel((const void *)&tree_leaves_kernel, dim3((unsigned)((n + 255) / 256)),
                            dim3(256), a, 0, stream);
 }
 
-hipError_t launch_tree_lists(const unsigned *leaf_key, const int *leaf_level,
-                             const int *cell_start, int *counters, int nslots, int *cnt,
-                             const int *off, int *list, hipStream_t stream)
+int tree_table_level(int nleaf)
 {
-    if (nslots <= 0) return nslots == 0 ? hipSuccess : hipErrorInvalidValue;
+    int lt = 1;
+    while (lt < kTreeTableMaxLevel && (1ll << (3 * lt)) < (long long)nleaf) ++lt;
+    return lt;
+}
+
+hipError_t launch_tree_table(const unsigned long long *leaf_key, const int *counters, int lt,
+                             int *table, hipStream_t stream)
+{
+    if (lt < 1 || lt > kTreeTableMaxLevel) return hipErrorInvalidValue;
+    const long long entries = (1ll << (3 * lt)) + 1;
+    void *a[] = {&leaf_key, &counters, &lt, &table};
+    return hipLaunchKernel((const void *)&tree_table_kernel,
+                           dim3((unsigned)((entries + 255) / 256)), dim3(256), a, 0, stream);
+}
+
+size_t tree_parts_bytes(int nleaf)
+{
+    return (size_t)((27ll * nleaf + 1 + 255) / 256) * sizeof(longlong2);
+}
+
+hipError_t launch_tree_lists(const TreeLeaves &lv, int *counters, void *parts, int *cnt,
+                             const int *off, int *list, int *list_off, hipStream_t stream)
+{
+    if (lv.nleaf <= 0 || lv.nleaf > kTreeMaxLeaves) return hipErrorInvalidValue;
     const bool fill = list != nullptr;
-    if (fill ? !off : !cnt) return hipErrorInvalidValue;
-    void *a[] = {&leaf_key, &leaf_level, &cell_start, &counters, &nslots, &cnt, &off, &list};
+    if (fill ? (!off || !list_off) : (!cnt || !parts || !counters)) return hipErrorInvalidValue;
+    TreeIndex ix{lv.leaf_key, lv.leaf_box, lv.table, lv.nleaf, lv.lt};
+    const int *cs = lv.cell_start;
+    longlong2 *pt = (longlong2 *)parts;
+    void *a[] = {&ix, &cs, &pt, &cnt, &off, &list, &list_off};
     const void *fn = fill ? (const void *)&tree_lists_kernel<true>
                           : (const void *)&tree_lists_kernel<false>;
-    return hipLaunchKernel(fn, dim3((unsigned)((nslots + 255) / 256)), dim3(256), a, 0, stream);
+    const long long threads = 27ll * lv.nleaf + 1;
+    int nblocks = (int)((threads + 255) / 256);
+    hipError_t e = hipLaunchKernel(fn, dim3((unsigned)nblocks), dim3(256), a, 0, stream);
+    if (e != hipSuccess || fill) return e;
+    void *b[] = {&pt, &nblocks, &counters};
+    return hipLaunchKernel((const void *)&tree_totals_kernel, dim3(1), dim3(256), b, 0, stream);
 }
 
 hipError_t launch_pack(const float *a, const float *b, const float *c, const float *d, int n,

@@ -37,7 +37,7 @@ def gpu_near_tree(nb, pos, eps2, leaf_size, pot=True):
                                     (3001, 300), (5000, 2)])
 def test_near_tree_uniform(nb, n, leaf):
     """Uniform cube, every target against the tree definition (leaf sizes from one body,
-    where every occupied level-10 cell is a leaf, to a tenth of the bodies)."""
+    where every body is a leaf, to a tenth of the bodies)."""
     import oracle
 
     pos, _ = workloads.random_bodies(n, seed=4000 + n + leaf)
@@ -98,7 +98,7 @@ def test_near_tree_full_octree_counts(nb):
 
 def test_near_tree_clustered_and_duplicates(nb):
     """A dense core inside a sparse halo (leaves at many levels, big leaves beside deep
-    ones), 40 bodies at one point (a level-10 node holding more than leaf_size) and a plane
+    ones), 40 bodies at one point (a level-21 node holding more than leaf_size) and a plane
     of bodies (a flat root cube extent), against the definition."""
     import oracle
 
@@ -115,6 +115,29 @@ def test_near_tree_clustered_and_duplicates(nb):
         acc, pot, st = gpu_near_tree(nb, pos, 1e-5, leaf)
         assert_accel_parity(acc, pot, oracle.near_tree(pos, 1e-5, leaf),
                             what=f"clustered tree leaf_size={leaf}")
+
+
+def test_near_tree_deep_leaves(nb):
+    """Leaves 13 levels down: a 4^3 lattice of cells of side 2^-13 at the origin, two bodies
+    per cell, and a body at (1, 1, 1) that sets the root cube; with leaf_size 3 the lattice
+    cells are the leaves, so the lattice bodies get the grid near field of the lattice and
+    the lone body only its self term."""
+    import oracle
+
+    rng = np.random.default_rng(14)
+    h = 2.0 ** -13
+    c = np.repeat(np.stack(np.meshgrid(*[np.arange(4)] * 3, indexing="ij"), -1).reshape(-1, 3),
+                  2, axis=0)
+    x = np.concatenate([(c + rng.uniform(0.15, 0.85, size=c.shape)) * h,
+                        [[0.0, 0.0, 0.0], [1.0, 1.0, 1.0]]])
+    pos = np.zeros((x.shape[0], 4), np.float32)
+    pos[:, :3] = x
+    pos[:, 3] = rng.uniform(0.5, 1.5, size=x.shape[0])
+    acc, pot, st = gpu_near_tree(nb, pos, 1e-9, 3)
+    assert st["leaves"] == 64 + 1 and st["list_entries"] == 10 ** 3 + 1  # 2 + 3 + 3 + 2 per axis
+    assert_accel_parity(acc, pot, oracle.near_tree(pos, 1e-9, 3), what="deep leaves")
+    g = oracle.near_grid(pos[:-1], 1e-9, (0.0, 0.0, 0.0), h, (4, 4, 4))
+    assert_accel_parity(acc[:-1], pot[:-1], g, what="deep leaves vs lattice grid")
 
 
 def test_near_tree_coincident_bodies(nb):
@@ -142,6 +165,8 @@ def test_near_tree_plummer_sampled(nb):
                                     np.random.default_rng(9).integers(0, w.n, 1000)]))
     ref = oracle.near_tree(w.pos, w.eps2, 64, targets=idx)
     assert_accel_parity(acc, pot, ref, idx=idx, what="plummer tree")
+    # the core splits into leaves of at most 64 bodies despite outliers at r ~ 500
+    assert st["pair_terms"] < 64 * 27 * w.n
     a2, p2, st2 = gpu_near_tree(nb, w.pos, w.eps2, 64)
     assert np.array_equal(acc, a2) and np.array_equal(pot, p2) and st == st2
     a0, p0, _ = gpu_near_tree(nb, w.pos, w.eps2, 64, pot=False)
