@@ -1170,30 +1170,45 @@ int nbody_near_tree(const nbody_f4 *pos, int64_t N, float eps2, int64_t leaf_siz
     const nbk::TreeLeaves lv{leaf_key, leaf_box, table, start, nleaf, lt};
     e = nbk::launch_tree_table(leaf_key, counters, lt, table, stream);
     if (e == hipSuccess)
-        e = nbk::launch_tree_lists(lv, counters, wg_totals, cnt, nullptr, nullptr, nullptr,
+        e = nbk::launch_tree_lists(lv, counters, wg_totals, cnt, nullptr, nullptr, 0, nullptr,
                                    stream);
     if (e == hipSuccess) e = nbk::scan_exclusive(cnt, parts, counters + 1, scan_temp1, stream);
-    // second wait: the list total sizes the lists
-    if (e == hipSuccess)
-        e = hipMemcpyAsync(host, counters, sizeof(host), hipMemcpyDeviceToHost, stream);
-    if (e == hipSuccess) e = hipStreamSynchronize(stream);
     if (e != hipSuccess) return hip_fail(e, "near-tree lists");
+    // A leaf B meets at most 27 leaves no smaller than itself (each holds a different one
+    // of the 27 cells of B's level around B) and at most 26 smaller ones, so the lists hold
+    // at most 53 entries per leaf: their scratch is sized from the leaf count without a
+    // second wait (which remains for leaf counts whose bound passes 2^31 - 1 entries).
+    const long long bound = (long long)nbk::kTreeListsPerLeaf * nleaf;
     unsigned long long nlist = 0, terms = 0;
-    std::memcpy(&nlist, host + 2, 8);
-    std::memcpy(&terms, host + 4, 8);
-    if (nlist > (unsigned long long)INT32_MAX)
-        return fail(NBODY_EINVAL, "near-tree lists hold %llu entries (at most 2^31 - 1)", nlist);
-    if ((unsigned long long)(unsigned)host[1] != nlist)
-        return fail(NBODY_EHIP, "near-tree build: list offsets end at %d, counted %llu", host[1],
-                    nlist);
+    auto read_totals = [&]() -> int {
+        hipError_t x = hipMemcpyAsync(host, counters, sizeof(host), hipMemcpyDeviceToHost, stream);
+        if (x == hipSuccess) x = hipStreamSynchronize(stream);
+        if (x != hipSuccess) return hip_fail(x, "near-tree lists");
+        std::memcpy(&nlist, host + 2, 8);
+        std::memcpy(&terms, host + 4, 8);
+        if (nlist > (unsigned long long)INT32_MAX)
+            return fail(NBODY_EINVAL, "near-tree lists hold %llu entries (at most 2^31 - 1)",
+                        nlist);
+        if ((unsigned long long)(unsigned)host[1] != nlist)
+            return fail(NBODY_EHIP, "near-tree build: list offsets end at %d, counted %llu",
+                        host[1], nlist);
+        return NBODY_OK;
+    };
+    long long cap = bound;
+    if (bound > INT32_MAX) {
+        rc = read_totals();
+        if (rc != NBODY_OK) return rc;
+        cap = (long long)nlist;
+    }
     void *lw = nullptr;
-    rc = scratch_get(dev, stream, ((size_t)nlist + 1) * 4, &lw, 2);
+    rc = scratch_get(dev, stream, ((size_t)cap + 1) * 4, &lw, 2);
     if (rc != NBODY_OK) return rc;
     int *list = (int *)lw;
-    e = nbk::launch_tree_lists(lv, counters, nullptr, nullptr, cnt, list, list_off, stream);
+    e = nbk::launch_tree_lists(lv, counters, nullptr, nullptr, cnt, list, (int)cap, list_off,
+                               stream);
     if (e == hipSuccess) {
-        nbk::P2PArgs a{spos, n, eps2, start, nleaf, list_off, list, (long long)nlist,
-                       (float4 *)acc_out, pot_out, perm};
+        nbk::P2PArgs a{spos, n, eps2, start, nleaf, list_off, list, cap, (float4 *)acc_out,
+                       pot_out, perm};
         bool wide = false;
         rc = wide_cells(N, nleaf, &wide);
         if (rc != NBODY_OK) return rc;
@@ -1201,7 +1216,17 @@ int nbody_near_tree(const nbody_f4 *pos, int64_t N, float eps2, int64_t leaf_siz
                          [&] { return nbk::launch_p2p(pot_out != nullptr, wide, a, stream); });
     }
     if (e != hipSuccess) return hip_fail(e, "near-tree launch");
-    if (stats) *stats = nbody_tree_stats{nleaf, (int64_t)nlist, (int64_t)terms};
+    if (stats) {
+        // the totals of this call: a wait for the whole call
+        if (bound <= INT32_MAX) {
+            rc = read_totals();
+            if (rc != NBODY_OK) return rc;
+            if ((long long)nlist > bound)
+                return fail(NBODY_EHIP, "near-tree lists: %llu entries exceed the bound %lld",
+                            nlist, bound);
+        }
+        *stats = nbody_tree_stats{nleaf, (int64_t)nlist, (int64_t)terms};
+    }
     return ok();
 }
 

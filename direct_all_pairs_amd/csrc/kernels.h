@@ -221,10 +221,13 @@ struct TreeLeaves {
 // (27 nleaf + 1 entries, the last 0); the list total and the pair terms go to
 // counters[2..5] through per-workgroup records in parts (tree_parts_bytes). Fill pass
 // (off = the exclusive sums of cnt): part q of leaf A's list written at
-// list[off[27 A + q] ..], list_off[A] = off[27 A], list_off[nleaf] = the total.
+// list[off[27 A + q] ..] (never at or past list_cap), list_off[A] = off[27 A],
+// list_off[nleaf] = the total. The lists hold at most kTreeListsPerLeaf entries per leaf.
+constexpr int kTreeListsPerLeaf = 53;
 size_t tree_parts_bytes(int nleaf);
 hipError_t launch_tree_lists(const TreeLeaves &leaves, int *counters, void *parts, int *cnt,
-                             const int *off, int *list, int *list_off, hipStream_t stream);
+                             const int *off, int *list, int list_cap, int *list_off,
+                             hipStream_t stream);
 
 // Layout conversion for the SoA entry points: out[i] = (a[i], b[i], c[i], d ? d[i] : 0),
 // and back: a[i], b[i], c[i] = in[i].x, .y, .z.

@@ -2236,7 +2236,7 @@ struct TreeIndex {
     const int4 *box;     // leaf cubes
     const int *table;    // coarse table over level lt
     int nleaf, lt;
-    // first leaf in [a, b) with key >= x (lower) / > x (upper); b if none
+    // first leaf in [a, b) with key >= x; b if none
     __device__ int lower_in(int a, int b, u64 x) const
     {
         while (a < b) {
@@ -2246,26 +2246,32 @@ struct TreeIndex {
         }
         return a;
     }
-    __device__ int upper_in(int a, int b, u64 x) const
+    // The first leaf with key > x (u) and the first with key >= y (l), as two interleaved
+    // binary searches whose loads overlap; the leaves with keys in x's coarse cell c are
+    // [table[c], table[c + 1]), so each search starts inside one cell.
+    __device__ void upper_lower(u64 x, u64 y, int &u, int &l) const
     {
-        while (a < b) {
-            const int m = a + (b - a) / 2;
-            if (key[m] <= x) a = m + 1;
-            else b = m;
+        const u64 cx = x >> tree_shift(lt), cy = y >> tree_shift(lt);
+        int a0 = table[cx], b0 = table[cx + 1];
+        int a1 = nleaf, b1 = nleaf;  // y = 2^63: past every key
+        if (cy < (1ull << (3 * lt))) {
+            a1 = table[cy];
+            b1 = table[cy + 1];
         }
-        return a;
-    }
-    // the leaves with keys in x's coarse cell are [table[c], table[c + 1])
-    __device__ int lower(u64 x) const
-    {
-        const u64 c = x >> tree_shift(lt);
-        if (c >= (1ull << (3 * lt))) return nleaf;  // x = 2^63: past every key
-        return lower_in(table[c], table[c + 1], x);
-    }
-    __device__ int upper(u64 x) const
-    {
-        const u64 c = x >> tree_shift(lt);
-        return upper_in(table[c], table[c + 1], x);
+        while (a0 < b0 || a1 < b1) {
+            const int m0 = a0 + (b0 - a0) / 2, m1 = a1 + (b1 - a1) / 2;
+            const u64 k0 = a0 < b0 ? key[m0] : 0, k1 = a1 < b1 ? key[m1] : 0;
+            if (a0 < b0) {
+                if (k0 <= x) a0 = m0 + 1;
+                else b0 = m0;
+            }
+            if (a1 < b1) {
+                if (k1 < y) a1 = m1 + 1;
+                else b1 = m1;
+            }
+        }
+        u = a0;
+        l = a1;
     }
 };
 
@@ -2284,7 +2290,7 @@ __global__ void __launch_bounds__(256) tree_lists_kernel(TreeIndex ix,
                                                          longlong2 *__restrict__ part,
                                                          int *__restrict__ cnt,
                                                          const int *__restrict__ off,
-                                                         int *__restrict__ list,
+                                                         int *__restrict__ list, int list_cap,
                                                          int *__restrict__ list_off)
 {
     const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
@@ -2303,7 +2309,7 @@ __global__ void __launch_bounds__(256) tree_lists_kernel(TreeIndex ix,
         long long at = 0, end = 0;
         if (FILL) {
             at = off[t];
-            end = off[t + 1];
+            end = off[t + 1] < list_cap ? off[t + 1] : list_cap;  // never past the buffer
             if (q == 0) list_off[A] = (int)at;
             if (A == nleaf - 1 && q == 26) list_off[nleaf] = (int)end;
         }
@@ -2318,7 +2324,10 @@ __global__ void __launch_bounds__(256) tree_lists_kernel(TreeIndex ix,
         const int cq[3] = {ca[0] + q % 3 - 1, ca[1] + (q / 3) % 3 - 1, ca[2] + q / 9 - 1};
         if (cq[0] >= 0 && cq[1] >= 0 && cq[2] >= 0 && cq[0] < lim && cq[1] < lim && cq[2] < lim) {
             const u64 qk = tree_key(cq[0], cq[1], cq[2], L);
-            const int b = ix.upper(qk) - 1;
+            const u64 qe = qk + (1ull << s);
+            int ub, E;
+            ix.upper_lower(qk, qe, ub, E);
+            const int b = ub - 1;
             const int4 bb = b >= 0 ? ix.box[b] : make_int4(0, 0, 0, kTreeBits + 1);
             if (bb.w <= L && qk < ix.key[b] + (1ull << tree_shift(bb.w))) {
                 // leaf b holds the whole cell: listed from the first in-range cell inside it
@@ -2335,10 +2344,9 @@ __global__ void __launch_bounds__(256) tree_lists_kernel(TreeIndex ix,
                 }
                 if (!seen) emit(b);
             } else {
-                // the deeper leaves inside the cell, in key order
-                const u64 qe = qk + (1ull << s);
-                int B = ix.lower(qk);
-                const int E = ix.lower(qe);
+                // the deeper leaves inside the cell, in key order: from the first key at
+                // or after the cell's start (b itself when it starts there)
+                int B = b >= 0 && ix.key[b] == qk ? b : b + 1;
                 while (B < E) {
                     const int4 bx = ix.box[B];
                     if (tree_meet(bx.x, bx.y, bx.z, bx.w, oa, sa)) {
@@ -2383,14 +2391,19 @@ __global__ void __launch_bounds__(256) tree_lists_kernel(TreeIndex ix,
     }
 }
 
-// counters[2..3] = sum of part[].x (list entries), counters[4..5] = sum of part[].y
-// (pair terms), as 64-bit integers.
+// Sums of the per-workgroup records: workgroup b adds part[b * per .. (b + 1) * per)
+// (integers, fixed order) into out[b]; with counters set (one workgroup), the sums go
+// to counters[2..3] (list entries) and counters[4..5] (pair terms) as 64-bit integers.
 __global__ void __launch_bounds__(256) tree_totals_kernel(const longlong2 *__restrict__ part,
-                                                          int nparts, int *__restrict__ counters)
+                                                          int nparts, int per,
+                                                          longlong2 *__restrict__ out,
+                                                          int *__restrict__ counters)
 {
     __shared__ long long red[2][4];
     long long a = 0, b = 0;
-    for (int i = threadIdx.x; i < nparts; i += 256) {
+    const long long i0 = (long long)blockIdx.x * per;
+    const long long i1 = i0 + per < nparts ? i0 + per : nparts;
+    for (long long i = i0 + threadIdx.x; i < i1; i += 256) {
         a += part[i].x;
         b += part[i].y;
     }
@@ -2405,8 +2418,14 @@ __global__ void __launch_bounds__(256) tree_totals_kernel(const longlong2 *__res
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        *reinterpret_cast<u64 *>(counters + 2) = (u64)(red[0][0] + red[0][1] + red[0][2] + red[0][3]);
-        *reinterpret_cast<u64 *>(counters + 4) = (u64)(red[1][0] + red[1][1] + red[1][2] + red[1][3]);
+        const long long sa = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+        const long long sb = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+        if (counters) {
+            *reinterpret_cast<u64 *>(counters + 2) = (u64)sa;
+            *reinterpret_cast<u64 *>(counters + 4) = (u64)sb;
+        } else {
+            out[blockIdx.x] = make_longlong2(sa, sb);
+        }
     }
 }
 
@@ -2813,13 +2832,17 @@ hipError_t launch_tree_table(const unsigned long long *leaf_key, const int *coun
                            dim3((unsigned)((entries + 255) / 256)), dim3(256), a, 0, stream);
 }
 
+constexpr int kTreeTotalsPer = 1024;  // records per workgroup of the first totals pass
+
 size_t tree_parts_bytes(int nleaf)
 {
-    return (size_t)((27ll * nleaf + 1 + 255) / 256) * sizeof(longlong2);
+    const long long nb = (27ll * nleaf + 1 + 255) / 256;
+    return (size_t)(nb + (nb + kTreeTotalsPer - 1) / kTreeTotalsPer) * sizeof(longlong2);
 }
 
 hipError_t launch_tree_lists(const TreeLeaves &lv, int *counters, void *parts, int *cnt,
-                             const int *off, int *list, int *list_off, hipStream_t stream)
+                             const int *off, int *list, int list_cap, int *list_off,
+                             hipStream_t stream)
 {
     if (lv.nleaf <= 0 || lv.nleaf > kTreeMaxLeaves) return hipErrorInvalidValue;
     const bool fill = list != nullptr;
@@ -2827,15 +2850,23 @@ hipError_t launch_tree_lists(const TreeLeaves &lv, int *counters, void *parts, i
     TreeIndex ix{lv.leaf_key, lv.leaf_box, lv.table, lv.nleaf, lv.lt};
     const int *cs = lv.cell_start;
     longlong2 *pt = (longlong2 *)parts;
-    void *a[] = {&ix, &cs, &pt, &cnt, &off, &list, &list_off};
+    void *a[] = {&ix, &cs, &pt, &cnt, &off, &list, &list_cap, &list_off};
     const void *fn = fill ? (const void *)&tree_lists_kernel<true>
                           : (const void *)&tree_lists_kernel<false>;
     const long long threads = 27ll * lv.nleaf + 1;
     int nblocks = (int)((threads + 255) / 256);
     hipError_t e = hipLaunchKernel(fn, dim3((unsigned)nblocks), dim3(256), a, 0, stream);
     if (e != hipSuccess || fill) return e;
-    void *b[] = {&pt, &nblocks, &counters};
-    return hipLaunchKernel((const void *)&tree_totals_kernel, dim3(1), dim3(256), b, 0, stream);
+    // the workgroup records in two passes: kTreeTotalsPer per workgroup, then one
+    int per = kTreeTotalsPer, ng = (nblocks + per - 1) / per;
+    longlong2 *mid = pt + nblocks;
+    int *none = nullptr;
+    void *b1[] = {&pt, &nblocks, &per, &mid, &none};
+    e = hipLaunchKernel((const void *)&tree_totals_kernel, dim3((unsigned)ng), dim3(256), b1, 0,
+                        stream);
+    if (e != hipSuccess) return e;
+    void *b2[] = {&mid, &ng, &ng, &mid, &counters};
+    return hipLaunchKernel((const void *)&tree_totals_kernel, dim3(1), dim3(256), b2, 0, stream);
 }
 
 hipError_t launch_pack(const float *a, const float *b, const float *c, const float *d, int n,

@@ -320,9 +320,11 @@ typedef struct nbody_tree_stats {
  * caller's body order. leaf_size >= 1; N <= 2^30; positions finite (a non-finite
  * coordinate gives unspecified results for the bodies, never an access out of
  * bounds). stats (host, may be NULL) receives the leaf and list counts.
- * The call waits once on the stream, for the list lengths (the host sizes the
- * lists' scratch from them): it returns after the build, with the near-field
- * kernel enqueued. Scratch: ~N x 60 bytes + 4 bytes per list entry.
+ * The call waits once on the stream, for the number of leaves (the host sizes the
+ * lists' scratch from it: at most 53 list entries per leaf), and returns with the
+ * rest enqueued; with stats it also waits for the end of the call. More than
+ * 2^31 - 1 list entries (possible only with over 40 million leaves) is EINVAL.
+ * Scratch: ~N x 100 bytes + ~300 bytes per leaf.
  */
 int nbody_near_tree(const nbody_f4 *pos_xyzm, int64_t N, float eps2, int64_t leaf_size,
                     nbody_f4 *acc_out, float *pot_out, nbody_tree_stats *stats,
