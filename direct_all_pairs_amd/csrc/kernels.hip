@@ -1426,6 +1426,12 @@ __device__ __forceinline__ void walk_tiles(const P2PArgs &k, Lists &lists, int l
         if constexpr (__is_same(Lists, PackedLists)) {
             if (lists.bound_seg != sg) {
                 __syncthreads();  // every wave is done with the previous table
+                if (kRaceProbe && w == 0) {
+                    // race probe: an empty table first (in-bounds for any reader: every
+                    // position maps to itself, and a reader of the total sees no tiles)
+                    for (int i = lane; i < kPackLds; i += 64) lists.tab[i] = 0;
+                    __builtin_amdgcn_wave_barrier();
+                }
                 if (w == 0) lists.load_segment(k, lo, hi, sg, lane);
                 __syncthreads();
                 lists.bound_seg = sg;
@@ -1752,8 +1758,8 @@ __global__ void __launch_bounds__(256) cell_starts_kernel(const unsigned *__rest
 }
 
 // ---------------------------------------------------------------- binning sort
-// Stable LSD radix sort of the (cell key, body index) pairs of nbody_near_grid,
-// 8 key bits per pass, three kernels per pass:
+// Stable LSD radix sort of (key, body index) pairs (the cell keys of nbody_near_grid,
+// the Morton keys of nbody_near_tree), 8 key bits per pass, three steps per pass:
 //   hist    - workgroup b counts the digits of its contiguous key range
 //             [b per, (b + 1) per) into counts[digit][b] (LDS counters: the
 //             counts do not depend on the order of the additions);
@@ -1761,17 +1767,16 @@ __global__ void __launch_bounds__(256) cell_starts_kernel(const unsigned *__rest
 //             then workgroup), so equal digits keep the order of the
 //             workgroups, i.e. of the input (two kernels: tile sums, then each
 //             tile scanned from the sum of the tiles before it);
-//   scatter - workgroup b walks its range 256 keys at a time in input order; a
-//             key's place is its digit's running offset plus the number of keys
-//             with the same digit before it in the sub-tile (earlier waves'
-//             counts, then the lanes below it in its own wave, found from the
-//             eight digit-bit ballots).
+//   scatter - workgroup b ranks its range in input order, restages each chunk
+//             in LDS in digit order and writes each digit's run from its offset
+//             (below).
 // Every step is integer and in a fixed order: the result is the stable sort,
 // the same bits every time, so a cell keeps its bodies in input order.
 constexpr int kSortBits = 8;
 constexpr int kSortDigits = 1 << kSortBits;  // 256: one counter per thread
 constexpr int kSortMaxBlocks = 2048;         // counts <= 2^19 entries: <= 128 scan tiles
 constexpr int kSortScanThreads = 1024;
+constexpr int kSortScanTile = 4 * kSortScanThreads;  // counts per scan workgroup
 constexpr int kSortKeysPerBlock = 4096;      // most keys per workgroup (up to N = 2^23)
 constexpr int kSortMinKeysPerBlock = 1024;   // fewest keys per workgroup
 constexpr int kSortTargetBlocks = 512;
@@ -1827,8 +1832,6 @@ __global__ void __launch_bounds__(256) sort_hist_kernel(const K *__restrict__ ke
 // into LDS, each thread the sum of four consecutive entries, an inclusive scan of
 // those over the wave by shuffles, the 16 wave totals added in wave order, the four
 // exclusive prefixes written back through LDS). Integer sums: the result is exact.
-constexpr int kSortScanTile = 4 * kSortScanThreads;
-
 // Sum over the workgroup of v (one value per thread), in a fixed order; every thread
 // gets it. red holds kSortScanThreads / 64 ints.
 __device__ __forceinline__ int sort_block_sum(int v, int *red)
@@ -1896,6 +1899,17 @@ __global__ void __launch_bounds__(kSortScanThreads)
     }
 }
 
+// Scatter: workgroup b places its range chunk by chunk (kSortChunk keys, 256 per
+// round). A round ranks its keys in input order (the eight digit-bit ballots give a
+// lane's place among the wave's keys of its digit, the per-wave counts in LDS the
+// place among earlier waves', the running count the place among earlier rounds'),
+// and the chunk is restaged in LDS in digit order; then consecutive threads write
+// consecutive entries of each digit's run, so the global writes come in runs of
+// about chunk / 256 keys instead of one key per address. Stable, integer, fixed
+// order: the same bits every time.
+constexpr int kSortChunk = 2048;
+constexpr int kSortRounds = kSortChunk / 256;
+
 template <typename K>
 __global__ void __launch_bounds__(256) sort_scatter_kernel(const K *__restrict__ kin,
                                                            const int *__restrict__ vin, int n,
@@ -1904,50 +1918,95 @@ __global__ void __launch_bounds__(256) sort_scatter_kernel(const K *__restrict__
                                                            K *__restrict__ kout,
                                                            int *__restrict__ vout)
 {
-    __shared__ int base[kSortDigits];     // running output position of each digit
-    __shared__ int wcnt[4][kSortDigits];  // per wave: keys of each digit in the sub-tile
+    __shared__ int base[kSortDigits];     // global position of each digit's next key
+    __shared__ int run[kSortDigits];      // keys of each digit in the chunk so far
+    __shared__ int lstart[kSortDigits];   // each digit's first slot in the restaged chunk
+    __shared__ int wcnt[4][kSortDigits];  // per wave: keys of each digit in the round
+    __shared__ int wsum[4];
+    __shared__ K skey[kSortChunk];
+    __shared__ int sval[kSortChunk];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     base[tid] = offsets[tid * nblocks + blockIdx.x];
 #pragma unroll
     for (int q = 0; q < 4; ++q) wcnt[q][tid] = 0;
-    __syncthreads();
     int b0, e;
     sort_range(n, per, b0, e);
-    bool valid = b0 + tid < e;
-    K k = valid ? kin[b0 + tid] : K(0);
-    int v = valid ? vin[b0 + tid] : 0;
-    for (int s0 = b0; s0 < e; s0 += 256) {
-        // the next sub-tile's pair, loaded while this one is placed
-        const int ni = s0 + 256 + tid;
-        const bool nvalid = ni < e;
-        const K nk = nvalid ? kin[ni] : K(0);
-        const int nv = nvalid ? vin[ni] : 0;
-        const unsigned d = (unsigned)(k >> shift) & (kSortDigits - 1);
-        // the valid lanes of this wave whose key has digit d
-        unsigned long long same = __ballot(valid);
+    for (int c0 = b0; c0 < e; c0 += kSortChunk) {
+        const int cnt = e - c0 < kSortChunk ? e - c0 : kSortChunk;
+        run[tid] = 0;
+        K key[kSortRounds];
+        int val[kSortRounds], rank[kSortRounds];
+        unsigned dig[kSortRounds];
 #pragma unroll
-        for (int bit = 0; bit < kSortBits; ++bit) {
-            const bool set = (d >> bit) & 1u;
-            const unsigned long long on = __ballot(set);
-            same &= set ? on : ~on;
+        for (int r = 0; r < kSortRounds; ++r) {  // all loads first
+            const int i = c0 + r * 256 + tid;
+            const bool valid = r * 256 + tid < cnt;
+            key[r] = valid ? kin[i] : K(0);
+            val[r] = valid ? vin[i] : 0;
         }
-        const unsigned long long below = same & ((1ull << lane) - 1ull);
-        if (valid && below == 0) wcnt[w][d] = __popcll(same);  // the digit's first lane
         __syncthreads();
-        if (valid) {
-            int at = base[d] + __popcll(below);
+#pragma unroll
+        for (int r = 0; r < kSortRounds; ++r) {
+            if (r * 256 >= cnt) break;  // uniform
+            const bool valid = r * 256 + tid < cnt;
+            const unsigned d = (unsigned)(key[r] >> shift) & (kSortDigits - 1);
+            dig[r] = d;
+            unsigned long long same = __ballot(valid);
+#pragma unroll
+            for (int bit = 0; bit < kSortBits; ++bit) {
+                const bool set = (d >> bit) & 1u;
+                const unsigned long long on = __ballot(set);
+                same &= set ? on : ~on;
+            }
+            const unsigned long long below = same & ((1ull << lane) - 1ull);
+            if (valid && below == 0) wcnt[w][d] = __popcll(same);  // the digit's first lane
+            __syncthreads();
+            int at = run[d] + __popcll(below);
             for (int q = 0; q < w; ++q) at += wcnt[q][d];
-            kout[at] = k;
-            vout[at] = v;
+            rank[r] = at;
+            __syncthreads();
+            run[tid] += wcnt[0][tid] + wcnt[1][tid] + wcnt[2][tid] + wcnt[3][tid];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) wcnt[q][tid] = 0;
+            __syncthreads();
+        }
+        // each digit's first slot in the chunk: exclusive scan of run over the digits
+        const int mine = run[tid];
+        int incl = mine;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o);
+            if (lane >= o) incl += y;
+        }
+        if (lane == 63) wsum[w] = incl;
+        __syncthreads();
+        int before = 0;
+        for (int q = 0; q < w; ++q) before += wsum[q];
+        lstart[tid] = before + incl - mine;
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < kSortRounds; ++r) {
+            if (r * 256 >= cnt) break;
+            if (r * 256 + tid < cnt) {
+                const int slot = lstart[dig[r]] + rank[r];
+                if (slot < cnt) {
+                    skey[slot] = key[r];
+                    sval[slot] = val[r];
+                }
+            }
         }
         __syncthreads();
-        base[tid] += wcnt[0][tid] + wcnt[1][tid] + wcnt[2][tid] + wcnt[3][tid];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) wcnt[q][tid] = 0;
-        __syncthreads();
-        k = nk;
-        v = nv;
-        valid = nvalid;
+        for (int sl = tid; sl < cnt; sl += 256) {
+            const K k = skey[sl];
+            const unsigned d = (unsigned)(k >> shift) & (kSortDigits - 1);
+            const int g = base[d] + sl - lstart[d];
+            if (g >= 0 && g < n) {
+                kout[g] = k;
+                vout[g] = sval[sl];
+            }
+        }
+        __syncthreads();  // base, run and the staging area are rewritten by the next chunk
+        base[tid] += mine;
     }
 }
 

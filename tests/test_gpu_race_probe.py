@@ -36,6 +36,7 @@ def probe(nb):
     lib.nbody_step_plan.argtypes = [vp, vp, i64, f32, f32, i64, ctypes.POINTER(nb.nbody_plan), vp]
     lib.nbody_near_grid.argtypes = [vp, i64, f32, ctypes.POINTER(ctypes.c_float), f32,
                                     ctypes.POINTER(ctypes.c_int32), vp, vp, vp]
+    lib.nbody_p2p.argtypes = [vp, i64, f32, vp, ctypes.c_int32, vp, vp, i64, vp, vp, vp]
     lib.nbody_last_error.restype = ctypes.c_char_p
     return lib
 
@@ -144,3 +145,37 @@ def test_probe_build_shared_tile_near_field(nb, probe, n, h, dims):
         torch.cuda.synchronize()
         outs.append((acc.cpu().numpy(), pot.cpu().numpy()))
     _assert_same(outs, f"near grid, {dims} cells")
+
+
+@pytest.mark.parametrize("n,ncell,per_list", [(3000, 150, 172), (12000, 150, 172),
+                                               (600000, 3100, 70)])
+def test_probe_build_list_segments(nb, probe, n, ncell, per_list):
+    """CSR lists of more than 64 entries: the near-field kernel walks them in segments whose
+    table wave 0 rewrites in LDS between two workgroup barriers: one wave per cell at ~20
+    bodies per cell, four waves at ~80, four waves with four targets per lane at ~190."""
+    import torch
+
+    pos_h, _ = workloads.random_bodies(n, seed=13)
+    rng = np.random.default_rng(ncell)
+    cuts = np.sort(rng.integers(0, n + 1, ncell - 1))
+    start = np.concatenate([[0], cuts, [n]]).astype(np.int32)
+    lists = [list(rng.integers(0, ncell, per_list)) for _ in range(ncell)]
+    off = np.zeros(ncell + 1, np.int32)
+    off[1:] = np.cumsum([len(x) for x in lists])
+    flat = np.array([c for x in lists for c in x], np.int32)
+    pd = to_dev(pos_h)
+    st, of, fl = (torch.from_numpy(a).cuda() for a in (start, off, flat))
+    outs = []
+    for which in ("library", "probe"):
+        acc = torch.full((n, 4), 7.0, device="cuda")
+        pot = torch.full((n,), 7.0, device="cuda")
+        if which == "library":
+            nb.nbody_p2p(pd, n, 1e-4, st, ncell, of, fl, len(flat), acc, pot)
+        else:
+            rc = probe.nbody_p2p(pd.data_ptr(), n, 1e-4, st.data_ptr(), ncell, of.data_ptr(),
+                                 fl.data_ptr(), len(flat), acc.data_ptr(), pot.data_ptr(),
+                                 _stream())
+            assert rc == 0, probe.nbody_last_error()
+        torch.cuda.synchronize()
+        outs.append((acc.cpu().numpy(), pot.cpu().numpy()))
+    _assert_same(outs, f"p2p lists of {per_list} entries, {ncell} cells")
