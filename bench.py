@@ -356,6 +356,50 @@ def near_grid_terms(pos_h, lo, h, dims) -> int:
     return int(np.sum(cnt * nbr))
 
 
+def near_roofline(terms: int, kernel_ms: float, pot: bool, kernel: str) -> dict:
+    """The near-field kernel against the FP32 vector peak: its issued flops per launch (21 per
+    one-sided term with the potential, 19 without, as in the tile kernel) over the
+    event-timed launch."""
+    flops = FLOPS_ONE_SIDED[pot] * terms
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    return {"bound": "alu", "kernel": kernel, "achieved": round(achieved, 2),
+            "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / FP32_VECTOR_PEAK_TFLOPS, 4), "traffic": None,
+            "flops_per_launch": flops, "units_per_launch": {"one_sided_terms": terms},
+            "flops_per_unit": {"one_sided_term": FLOPS_ONE_SIDED[pot]},
+            "launch_ms_mean": round(kernel_ms, 4)}
+
+
+def near_cpu_baseline(ref_fn, n: int, acc, pot) -> dict:
+    """Time the oracle's near field (ref_fn(targets) -> dict) on a fixed sample: 4096 random
+    targets (seed 0) plus the first and last 256 bodies; report targets per second, the
+    full-N time extrapolated from it, and the GPU's largest error on the sample in units of
+    the per-body bounds."""
+    import numpy as np
+
+    import oracle
+
+    rng = np.random.default_rng(0)
+    idx = np.unique(np.concatenate([rng.integers(0, n, 4096), np.arange(min(256, n)),
+                                    np.arange(max(0, n - 256), n)]))
+    t0 = time.perf_counter()
+    ref = ref_fn(idx)
+    t = time.perf_counter() - t0
+    a = np.asarray(acc)[idx, :3].astype(np.float64)
+    out = {"value": round(len(idx) / t, 1), "unit": "targets/s", "cores": oracle.num_threads(),
+           "kind": "oracle",
+           "sample": f"4096 random targets (seed 0) + the first and last 256 ({len(idx)} "
+                     f"targets), fp64 near field + bounds: {t:.2f} s measured",
+           "full_n_seconds": n * t / len(idx),
+           "full_n_seconds_is": "extrapolated from the sample's rate",
+           "gpu_max_err_over_B": float(np.max(np.linalg.norm(a - ref["acc"], axis=1)
+                                              / ref["bound_a"]))}
+    if pot is not None:
+        e_p = np.abs(np.asarray(pot)[idx].astype(np.float64) - ref["pot"])
+        out["gpu_max_pot_err_over_P"] = float(np.max(e_p / ref["bound_p"]))
+    return out
+
+
 def near_grid_bench(nb, w, pos, args) -> int:
     """Time nbody_near_grid (binning, sort, near-field kernel, scatter) on a cubic grid of
     args.near_grid cells per axis over [-1, 1]^3; one JSON line (not the contract line)."""
@@ -384,13 +428,18 @@ def near_grid_bench(nb, w, pos, args) -> int:
     ms = e0.elapsed_time(e1) / args.steps
     kms = sum(ks[2 * k].elapsed_time(ks[2 * k + 1]) for k in range(args.steps)) / args.steps
     terms = near_grid_terms(w.pos, lo, h, dims)
-    print(json.dumps({"near_grid": {"workload": args.workload, "N": n, "dims": dims, "h": h,
-                                    "bodies_per_cell": n / (d ** 3), "pair_terms": terms,
-                                    "ms": round(ms, 4),
-                                    "G_terms_per_s": round(terms / ms / 1e6, 2),
-                                    "kernel_ms": round(kms, 4),
-                                    "kernel_G_terms_per_s": round(terms / kms / 1e6, 2)}}),
-          flush=True)
+    line = {"workload": args.workload, "N": n, "dims": dims, "h": h,
+            "bodies_per_cell": n / (d ** 3), "pair_terms": terms, "ms": round(ms, 4),
+            "G_terms_per_s": round(terms / ms / 1e6, 2), "kernel_ms": round(kms, 4),
+            "kernel_G_terms_per_s": round(terms / kms / 1e6, 2),
+            "roofline": near_roofline(terms, kms, True, "p2p_kernel (grid neighbourhoods)")}
+    if args.cpu_budget > 0:
+        import oracle
+
+        line["cpu_baseline"] = near_cpu_baseline(
+            lambda t: oracle.near_grid(w.pos, w.eps2, lo, h, dims, targets=t), n,
+            acc.cpu().numpy(), pot.cpu().numpy())
+    print(json.dumps({"near_grid": line}), flush=True)
     return 0
 
 
@@ -428,13 +477,19 @@ def near_tree_bench(nb, w, pos, args) -> int:
     ms = e0.elapsed_time(e1) / args.steps
     kms = sum(ks[2 * k].elapsed_time(ks[2 * k + 1]) for k in range(args.steps)) / args.steps
     terms = st.pair_terms
-    print(json.dumps({"near_tree": {"workload": args.workload, "N": n, "leaf_size": leaf,
-                                    **st.as_dict(), "bodies_per_leaf": round(n / st.leaves, 2),
-                                    "ms": round(ms, 4), "wall_ms": round(wall, 4),
-                                    "G_terms_per_s": round(terms / ms / 1e6, 2),
-                                    "kernel_ms": round(kms, 4),
-                                    "kernel_G_terms_per_s": round(terms / kms / 1e6, 2),
-                                    "build_ms": round(ms - kms, 4)}}), flush=True)
+    line = {"workload": args.workload, "N": n, "leaf_size": leaf, **st.as_dict(),
+            "bodies_per_leaf": round(n / st.leaves, 2), "ms": round(ms, 4),
+            "wall_ms": round(wall, 4), "G_terms_per_s": round(terms / ms / 1e6, 2),
+            "kernel_ms": round(kms, 4), "kernel_G_terms_per_s": round(terms / kms / 1e6, 2),
+            "build_ms": round(ms - kms, 4),
+            "roofline": near_roofline(terms, kms, True, "p2p_kernel (octree leaf lists)")}
+    if args.cpu_budget > 0:
+        import oracle
+
+        line["cpu_baseline"] = near_cpu_baseline(
+            lambda t: oracle.near_tree(w.pos, w.eps2, leaf, targets=t), n,
+            acc.cpu().numpy(), pot.cpu().numpy())
+    print(json.dumps({"near_tree": line}), flush=True)
     return 0
 
 

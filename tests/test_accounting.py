@@ -83,3 +83,13 @@ def test_cpu_sample_is_the_protocol_set():
     assert list(idx[:1024]) == list(range(1024)) and list(idx[-1024:]) == list(range(n - 1024, n))
     idx2, _ = bench.cpu_sample_targets(65536)
     assert list(idx2) == list(range(65536))
+
+
+def test_near_roofline_counts_issued_flops():
+    """The near-field line's roofline: 21 issued FP32 flops per one-sided term with the
+    potential (19 without) over the event-timed kernel."""
+    r = bench.near_roofline(10 ** 9, 10.0, True, "p2p")
+    assert r["flops_per_launch"] == 21 * 10 ** 9
+    assert abs(r["achieved"] - 2.1) < 1e-9 and r["unit"] == "TFLOP/s"
+    assert abs(r["frac"] - round(2.1 / bench.FP32_VECTOR_PEAK_TFLOPS, 4)) < 1e-12
+    assert bench.near_roofline(10 ** 9, 10.0, False, "p2p")["flops_per_launch"] == 19 * 10 ** 9
