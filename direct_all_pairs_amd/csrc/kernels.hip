@@ -2663,10 +2663,13 @@ hipError_t launch_p2p_any(bool pot, bool wide, const P2PArgs &args, Lists l, hip
         fn = pot ? (const void *)&p2p_kernel<true, Lists, false, 1>
                  : (const void *)&p2p_kernel<false, Lists, false, 1>;
     // chunk kernel: two workgroups per cell, each taking every other target chunk, so
-    // a cell's large chunk and the chunk of its remaining bodies run side by side;
-    // the workgroup kernel: about one workgroup per 256-target chunk of a cell a
-    // little larger than the mean (at most 16), so large cells spread over the GPU
-    unsigned ny = 2;
+    // a cell's large chunk and the chunk of its remaining bodies run side by side; one
+    // when cells average fewer than 64 bodies (most are one chunk: the second workgroup
+    // would only exit; N = 2^20 on a 64^3 grid 0.268 -> 0.220 ms, leaves of ~4 bodies
+    // 0.375 -> 0.326 ms); the workgroup kernel: about one workgroup per 256-target chunk
+    // of a cell a little larger than the mean (at most 16), so large cells spread over
+    // the GPU
+    unsigned ny = (long long)a.n >= 64ll * a.ncell ? 2u : 1u;
     if (wide) {
         const double m = (double)a.n / (double)a.ncell;
         const double chunks = (m + 3.0 * std::sqrt(m)) / 256.0;
