@@ -1274,15 +1274,41 @@ __device__ __forceinline__ bool next_tile(const P2PArgs &k, const Lists &lists, 
 constexpr int kP2PWideT = 4;
 constexpr int kP2PWideMin = 192;
 
-// Whether a cell of r bodies has a chunk q >= 1 (the chunk sequence below:
-// 256 targets while at least kP2PWideMin remain with QUAD, then 64, then the
-// rest). Only q = 1 is asked: the launches use at most two chunk workgroups per cell.
+// The chunk that starts where rem targets of a cell are left: four targets per lane
+// (quad: 256 targets) while at least kP2PWideMin remain with QUAD; else one per lane
+// on 2^lg lanes per source group: 64 when more than 48 remain, 32 when 33-48 remain
+// (the rest, at most 16, then takes a chunk of its own with four or more source
+// groups, instead of leaving up to half of a 64-lane chunk idle: a chunk costs a
+// walk over the neighbourhood, so a rest of 17 or more keeps the 64-lane chunk),
+// else the next power of two >= rem. Returns the targets the chunk takes.
+template <bool QUAD>
+__device__ __forceinline__ int chunk_span(int rem, int &lg, bool &quad)
+{
+    quad = QUAD && rem >= kP2PWideMin;
+    if (quad) {
+        lg = 6;
+        return 64 * kP2PWideT;
+    }
+    const int want = rem > 48 ? 64 : (rem > 32 ? 32 : rem);
+    int tw = 1;
+    lg = 0;
+    while (tw < want) {
+        tw <<= 1;
+        ++lg;
+    }
+    return tw;
+}
+
+// Whether a cell of r bodies has a chunk q >= 1 (the chunk sequence of chunk_span).
+// Only q = 1 is asked: the launches use at most two chunk workgroups per cell.
 template <bool QUAD>
 __device__ __forceinline__ bool cell_has_chunk(int r, int q)
 {
     int n = 0;
     while (r > 0 && n <= q) {
-        r -= (QUAD && r >= kP2PWideMin) ? 64 * kP2PWideT : 64;
+        int lg;
+        bool quad;
+        r -= chunk_span<QUAD>(r, lg, quad);
         ++n;
     }
     return n > q;
@@ -1453,14 +1479,15 @@ __device__ __forceinline__ void walk_tiles(const P2PArgs &k, Lists &lists, int l
     }
 }
 
-// Targets per chunk: a cell's bodies go up to 256 at a time (four per lane)
-// while at least 192 remain, then 64 at a time; a chunk of r < 64 bodies
-// takes tw = the next power of two >= r lanes per source group and G = 64 / tw
-// groups, lane (t, g) = (lane mod tw, lane / tw) summing every G-th source of
-// each of its tiles for target t; the G group sums of a target are added in
-// ascending g. So a 20-body cell keeps 64 lanes busy instead of 20. Each wave
-// issues the global load of its next source tile before it evaluates the
-// current one.
+// Targets per chunk (chunk_span): a cell's bodies go up to 256 at a time (four per
+// lane) while at least 192 remain, then 64 at a time; a chunk of tw < 64 targets
+// has tw lanes per source group and G = 64 / tw groups, lane (t, g) = (lane mod tw,
+// lane / tw) summing every G-th source of each of its tiles for target t; the G
+// group sums of a target are added in ascending g. So a 20-body cell keeps 64 lanes
+// busy instead of 20. A lane's terms go into an fp32 partial of at most kFlush
+// sources, then into the compensated totals (after every tile this cost a 4-body
+// cell's lanes more than their four terms per tile). Each wave issues the global
+// load of its next source tile before it evaluates the current one.
 template <bool POT, typename Lists, bool QUAD, int W>
 __global__ void __launch_bounds__(64 * W) p2p_kernel(P2PArgs k, Lists lists)
 {
@@ -1486,11 +1513,14 @@ __global__ void __launch_bounds__(64 * W) p2p_kernel(P2PArgs k, Lists lists)
     for (int t0 = tb, q = 0; t0 < te; ++q) {
         const int rem = te - t0;
         const bool mine = q % ny == y;
-        if (QUAD && rem >= kP2PWideMin && !mine) {
-            t0 += 64 * kP2PWideT;
+        int lg;
+        bool quad;
+        const int span = chunk_span<QUAD>(rem, lg, quad);
+        if (!mine) {
+            t0 += span;
             continue;
         }
-        if (QUAD && rem >= kP2PWideMin) {
+        if (quad) {
             // up to 256 targets, four per lane (target t0 + q * 64 + lane; past the
             // cell end a lane computes on a clamped body and stores nothing): each
             // staged source tile and each broadcast read serves four interactions
@@ -1505,9 +1535,10 @@ __global__ void __launch_bounds__(64 * W) p2p_kernel(P2PArgs k, Lists lists)
             }
             Total<kP2PWideT, POT> tot;
             zero(tot);
+            Sums<kP2PWideT, POT> blk;  // at most kFlush sources per target, then into tot
+            zero(blk);
+            int held = 0;
             walk_tiles<W>(k, lists, lo, hi, w, lane, row, [&](int cnt) {
-                Sums<kP2PWideT, POT> blk;
-                zero(blk);
                 if (cnt == 64) {
 #pragma unroll 16
                     for (int u = 0; u < 64; ++u) interact4<kP2PWideT, POT>(row[u], tg, eps2, blk);
@@ -1515,8 +1546,14 @@ __global__ void __launch_bounds__(64 * W) p2p_kernel(P2PArgs k, Lists lists)
 #pragma unroll 8
                     for (int u = 0; u < cnt; ++u) interact4<kP2PWideT, POT>(row[u], tg, eps2, blk);
                 }
-                add_into(tot, blk);
+                held += cnt;
+                if (held > kFlush - 64) {
+                    add_into(tot, blk);
+                    zero(blk);
+                    held = 0;
+                }
             });
+            add_into(tot, blk);
             const Sums<kP2PWideT, POT> r = result(tot);
 #pragma unroll
             for (int q = 0; q < kP2PWideT; ++q)
@@ -1541,18 +1578,10 @@ __global__ void __launch_bounds__(64 * W) p2p_kernel(P2PArgs k, Lists lists)
             __syncthreads();  // red is refilled by the next chunk
 #pragma unroll
             for (int q = 0; q < kP2PWideT; ++q) probe_poison(red[w][q * 64 + lane]);
-            t0 += 64 * kP2PWideT;
+            t0 += span;
             continue;
         }
-        int tw = 1, lg = 0;
-        while (tw < rem && tw < 64) {
-            tw <<= 1;
-            ++lg;
-        }
-        if (!mine) {
-            t0 += tw;
-            continue;
-        }
+        const int tw = span;
         const int groups = 64 >> lg;
         const int t = lane & (tw - 1), g = lane >> lg;
         const int i = t0 + t;
@@ -1563,9 +1592,13 @@ __global__ void __launch_bounds__(64 * W) p2p_kernel(P2PArgs k, Lists lists)
         tg.z[0] = me.z;
         Total<1, POT> tot;
         zero(tot);
+        // a lane's sources go into blk, at most kFlush of them, then into tot: a tile
+        // gives a lane cnt / groups of them
+        Sums<1, POT> blk;
+        zero(blk);
+        int held = 0;
+        const int per_tile = tw;  // at most 64 / groups = tw sources per tile
         walk_tiles<W>(k, lists, lo, hi, w, lane, row, [&](int cnt) {
-            Sums<1, POT> blk;
-            zero(blk);
             if (groups == 1 && cnt == 64) {
                 // full tile, one target per lane: uniform addresses at constant offsets
 #pragma unroll 16
@@ -1575,8 +1608,14 @@ __global__ void __launch_bounds__(64 * W) p2p_kernel(P2PArgs k, Lists lists)
                 for (int u0 = 0; u0 < cnt; u0 += groups)
                     interact4<1, POT>(row[u0 + g], tg, eps2, blk);
             }
-            add_into(tot, blk);
+            held += per_tile;
+            if (held > kFlush - per_tile) {
+                add_into(tot, blk);
+                zero(blk);
+                held = 0;
+            }
         });
+        add_into(tot, blk);
         const Sums<1, POT> r = result(tot);
         float4 a = make_float4(r.ax[0], r.ay[0], r.az[0], POT ? r.p[0] : 0.0f);
         if constexpr (W > 1) {
