@@ -1488,8 +1488,12 @@ __device__ __forceinline__ void walk_tiles(const P2PArgs &k, Lists &lists, int l
 // sources, then into the compensated totals (after every tile this cost a 4-body
 // cell's lanes more than their four terms per tile). Each wave issues the global
 // load of its next source tile before it evaluates the current one.
+// Occupancy: the one-target kernels ask for eight waves per SIMD (at most 64 VGPRs).
+// Left alone, the compiler gave the CSR-list variants 116-122 VGPRs (four waves per
+// SIMD), loading a whole 16-source unroll of LDS reads ahead of the arithmetic; capped
+// they take 59-64 and no scratch (octree leaves of 32 bodies: 0.31 -> 0.24 ms).
 template <bool POT, typename Lists, bool QUAD, int W>
-__global__ void __launch_bounds__(64 * W) p2p_kernel(P2PArgs k, Lists lists)
+__global__ void __launch_bounds__(64 * W, QUAD ? 4 : 8) p2p_kernel(P2PArgs k, Lists lists)
 {
     static_assert(!QUAD || W == kP2PWideT, "a 256-target chunk is finished by four waves");
     constexpr int TQ = QUAD ? kP2PWideT : 1;
