@@ -55,10 +55,12 @@ def _cells(n, ncell, seed):
 
 
 @pytest.mark.parametrize("n,ncell", [(1, 1), (70, 3), (1000, 17), (3001, 40), (3001, 10),
-                                     (5000, 4)])
+                                     (5000, 4), (3001, 150), (12000, 150), (40000, 200)])
 def test_p2p_full_lists_equal_direct_sum(nb, n, ncell):
     """Every cell listing every cell: the near field is the whole direct sum (cells of up to
-    ~75 bodies on average run one wave per cell, larger ones the 256-thread kernel)."""
+    ~75 bodies on average run one wave per cell, larger ones the 256-thread kernel; lists of
+    150 and 200 entries are walked in segments of 64 entries: one wave per cell at ~20
+    bodies, four waves at ~80 and four targets per lane at ~200)."""
     import oracle
 
     pos, _ = workloads.random_bodies(n, seed=1000 + n)

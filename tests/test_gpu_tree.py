@@ -188,6 +188,24 @@ def test_near_tree_cube1m_sampled(nb):
     print(f"[tree] cube1m stats {st}", flush=True)
 
 
+@pytest.mark.parametrize("n,leaf", [(60000, 200), (60000, 1000), (1 << 20, 1024)])
+def test_near_tree_large_leaves(nb, n, leaf):
+    """Large leaves, uniform cubes: 512 leaves of ~117 bodies (the four-wave kernel), 64 of
+    ~940 (the 256-thread shared-tile kernel) and 4096 of ~256 at N = 2^20 (four targets per
+    lane) over the packed leaf lists; sampled targets, both ends included, against the
+    definition."""
+    import oracle
+
+    pos, _ = workloads.random_bodies(n, seed=15 + leaf)
+    acc, pot, st = gpu_near_tree(nb, pos, 1e-4, leaf)
+    idx = np.unique(np.concatenate([np.random.default_rng(leaf).integers(0, n, 1500),
+                                    [0, n - 1]]))
+    assert_accel_parity(acc, pot, oracle.near_tree(pos, 1e-4, leaf, targets=idx), idx=idx,
+                        what=f"large leaves leaf_size={leaf}")
+    assert np.all(np.isfinite(acc)) and np.all(np.isfinite(pot))
+    print(f"[tree] leaf_size={leaf}: {st}, {n / st['leaves']:.1f} bodies per leaf", flush=True)
+
+
 def test_near_tree_permuted_input(nb):
     """Permuting the input bodies permutes the rows (up to rounding order)."""
     import oracle
