@@ -1479,6 +1479,17 @@ __device__ __forceinline__ void walk_tiles(const P2PArgs &k, Lists &lists, int l
     }
 }
 
+// One lane's share of a full 64-body tile in one-target chunks of G source groups: the
+// sources r[0], r[G], r[2G], ... (r = the row plus the lane's group), 64 / G of them; a
+// compile-time G puts every LDS read at an immediate offset.
+template <int G, bool POT>
+__device__ __forceinline__ void full_tile_sources(const float4 *r, const Targets<1> &tg,
+                                                  float eps2, Sums<1, POT> &blk)
+{
+#pragma unroll 16
+    for (int u = 0; u < 64 / G; ++u) interact4<1, POT>(r[u * G], tg, eps2, blk);
+}
+
 // Targets per chunk (chunk_span): a cell's bodies go up to 256 at a time (four per
 // lane) while at least 192 remain, then 64 at a time; a chunk of tw < 64 targets
 // has tw lanes per source group and G = 64 / tw groups, lane (t, g) = (lane mod tw,
@@ -1603,10 +1614,17 @@ __global__ void __launch_bounds__(64 * W, QUAD ? 4 : 8) p2p_kernel(P2PArgs k, Li
         int held = 0;
         const int per_tile = tw;  // at most 64 / groups = tw sources per tile
         walk_tiles<W>(k, lists, lo, hi, w, lane, row, [&](int cnt) {
-            if (groups == 1 && cnt == 64) {
-                // full tile, one target per lane: uniform addresses at constant offsets
-#pragma unroll 16
-                for (int u = 0; u < 64; ++u) interact4<1, POT>(row[u], tg, eps2, blk);
+            if (cnt == 64) {
+                // full tile: the lane's sources at constant offsets from row + g
+                switch (groups) {
+                case 1: full_tile_sources<1, POT>(row, tg, eps2, blk); break;
+                case 2: full_tile_sources<2, POT>(row + g, tg, eps2, blk); break;
+                case 4: full_tile_sources<4, POT>(row + g, tg, eps2, blk); break;
+                case 8: full_tile_sources<8, POT>(row + g, tg, eps2, blk); break;
+                case 16: full_tile_sources<16, POT>(row + g, tg, eps2, blk); break;
+                case 32: full_tile_sources<32, POT>(row + g, tg, eps2, blk); break;
+                default: full_tile_sources<64, POT>(row + g, tg, eps2, blk); break;
+                }
             } else {
 #pragma unroll 4
                 for (int u0 = 0; u0 < cnt; u0 += groups)
