@@ -130,3 +130,57 @@ def test_scratch_release_and_growth_with_queued_work(nb):
         acc, pot = out[n]
         assert np.array_equal(acc.cpu().numpy(), ref[n][0]), f"N={n} acceleration"
         assert np.array_equal(pot.cpu().numpy(), ref[n][1]), f"N={n} potential"
+
+
+@pytest.mark.parametrize("shared", [True, False], ids=["one_stream", "stream_each"])
+def test_near_field_threads_match_single_thread(nb, shared):
+    """nbody_near_tree (which waits on its stream part-way and keeps three scratch areas per
+    stream) and nbody_near_grid from several threads at once, sizes in a different order per
+    thread: every result equals the one-thread result bit for bit."""
+    import torch
+
+    sizes = [(5000, 16), (40000, 64), (150001, 32)]
+    data = {n: to_dev(workloads.random_bodies(n, seed=970 + n)[0]) for n, _ in sizes}
+    grid = ((-1.0, -1.0, -1.0), 0.25, (8, 8, 8))
+
+    def run(n, leaf, stream, acc_t, pot_t, acc_g, pot_g):
+        with torch.cuda.stream(stream):
+            nb.nbody_near_tree(data[n], n, 1e-4, leaf, acc_t, pot_t, None, stream=stream)
+            nb.nbody_near_grid(data[n], n, 1e-4, *grid, acc_g, pot_g, stream=stream)
+
+    def bufs(n):
+        return tuple(torch.full(shape, np.nan, device="cuda")
+                     for shape in ((n, 4), (n,), (n, 4), (n,)))
+
+    s0 = torch.cuda.Stream()
+    ref = {}
+    for n, leaf in sizes:
+        nb.nbody_release_workspace()
+        b = bufs(n)
+        run(n, leaf, s0, *b)
+        torch.cuda.synchronize()
+        ref[n] = [x.cpu().numpy() for x in b]
+    nb.nbody_release_workspace()
+    streams = [torch.cuda.Stream()] * THREADS if shared else [torch.cuda.Stream() for _ in range(THREADS)]
+    outs = {(t, n): bufs(n) for t in range(THREADS) for n, _ in sizes}
+    torch.cuda.synchronize()
+    errors = []
+
+    def work(t):
+        try:
+            order = sizes[t % len(sizes):] + sizes[:t % len(sizes)]
+            for n, leaf in order:
+                run(n, leaf, streams[t], *outs[t, n])
+        except Exception as e:  # reported after the join
+            errors.append(f"thread {t}: {e!r}")
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(THREADS)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for (t, n), b in outs.items():
+        for what, x, r in zip(("tree acc", "tree pot", "grid acc", "grid pot"), b, ref[n]):
+            assert np.array_equal(x.cpu().numpy(), r), f"thread {t} N={n} {what}"
