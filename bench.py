@@ -270,6 +270,7 @@ def sweep(nb, w, pos, vel, acc, pot, args) -> int:
     layouts += [(b, t, 256) for b in ("scalar", "readlane") for t in (1, 2, 4, 8)]
     layouts += [("pairs", 4, 256)]
     layouts += [("pairs", t, band) for t in (4, 8) for band in (512, 1024, 2048)]
+    layouts += [("pairs", 8, 4096)]
     if n <= 65536:
         layouts += [("small", tw, 256) for tw in (4, 8, 16, 32)]
     if args.sweep_only != "all":

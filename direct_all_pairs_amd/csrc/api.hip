@@ -269,7 +269,7 @@ int valid_tpl(int t) { return t == 1 || t == 2 || t == 4 || t == 8; }
 // memory (about 18 GB on MI355X, enough for N = 2^20 with 2048-body bands).
 constexpr size_t kPairsScratchShare = 16;
 
-int valid_band(int b) { return b == 256 || b == 512 || b == 1024 || b == 2048; }
+int valid_band(int b) { return b == 256 || b == 512 || b == 1024 || b == 2048 || b == 4096; }
 
 size_t pairs_scratch(int64_t n, int band)
 {
@@ -320,7 +320,10 @@ int small_tw(int64_t n) { return n <= 2048 ? 4 : (n <= 6144 ? 8 : 16); }
 
 // The automatic pair band for N and a requested tpl (0 = any): 256 bodies to
 // N = 36863, above it the largest band with at least 64 work items per
-// compute unit (512 at least).
+// compute unit (512 at least). 4096-body bands (half the slots of 2048, on
+// request) measured 0.3-0.7 % slower at N = 2^20, 0.25 % slower at 1.5 M
+// (one pass against two of 2048), 0.25 % faster at 2^21 and 1 % slower at
+// 2^22 (round-robin), so they are not chosen automatically.
 int auto_band(int64_t n, int tpl, const DeviceFacts &dev)
 {
     if (n <= kBand256MaxN && tpl != 8) return 256;
@@ -372,7 +375,7 @@ void auto_plan(int64_t n, const DeviceFacts &dev, nbody_plan *p)
     if (p->mode == NBODY_MODE_PAIRS) {
         p->bcast = NBODY_BCAST_LDS;
         if (p->band == 0) p->band = auto_band(n, p->tpl, dev);
-        if (p->tpl == 0) p->tpl = (p->band == 256 || n < 24576) ? 4 : 8;
+        if (p->tpl == 0) p->tpl = (p->band == 256 || (n < 24576 && p->band != 4096)) ? 4 : 8;
         if (p->passes == 0) {
             // explicit pair mode: if nothing fits, the most passes (the scratch
             // allocation then reports what is missing)
@@ -461,10 +464,13 @@ int make_plan(int64_t n, const nbody_plan *user, int *dev_out, nbody_plan *p)
         return fail(NBODY_EINVAL,
                     "plan.wg=%d must be 0 or 256 (or 64, 128, 512 with the LDS broadcast)", p->wg);
     if (p->band != 0 && !valid_band(p->band))
-        return fail(NBODY_EINVAL, "plan.band=%d must be 0, 256, 512, 1024 or 2048", p->band);
+        return fail(NBODY_EINVAL, "plan.band=%d must be 0, 256, 512, 1024, 2048 or 4096",
+                    p->band);
     if (p->band == 256 && p->tpl == 8)
         return fail(NBODY_EINVAL, "plan.band=256 takes plan.tpl 4 (an i-set of 8 targets per "
                                   "lane is 512 bodies)");
+    if (p->band == 4096 && p->tpl != 0 && p->tpl != 8)
+        return fail(NBODY_EINVAL, "plan.band=4096 takes plan.tpl 8");
     if (p->mode == NBODY_MODE_PAIRS &&
         ((p->bcast != 0 && p->bcast != NBODY_BCAST_LDS) ||
          (p->tpl != 0 && p->tpl != 4 && p->tpl != 8) || p->splits != 0 ||

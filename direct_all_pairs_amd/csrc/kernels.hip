@@ -631,7 +631,15 @@ constexpr int kBlkBytes = 64 * (int)sizeof(float4);
 template <int T>
 constexpr bool kFlatSums = T >= 8;
 
-template <int T, int BD, bool SEQ = kSeqReduce<T, BD>>
+// Bands above 2048 bodies keep an item's B-side sums in the item's own B-side
+// slot in global memory instead of LDS (64 KiB would not fit four workgroups per
+// CU): the thread that owns a j-body reads, updates and writes its slot entry
+// once per i-set, in i-set order, so the sums and their bits are those of the
+// LDS accumulator and no other thread touches the entry.
+template <int BD>
+constexpr bool kGlobalJacc = BD > 2048;
+
+template <int T, int BD, bool SEQ = kSeqReduce<T, BD>, bool GJ = kGlobalJacc<BD>>
 struct PairsShared {
     float4 jacc[BD];          // B-side sums of the item, one per body of band B
     float4 jblk[4][kRowLen];  // each wave's copy of its current j-block
@@ -640,7 +648,13 @@ struct PairsShared {
 };
 
 template <int T, int BD>
-struct PairsShared<T, BD, true> {
+struct PairsShared<T, BD, true, true> {
+    float4 jblk[4][kRowLen];  // as below, without the LDS accumulator of band B
+    float4 jsum[4][kRowLen];
+};
+
+template <int T, int BD>
+struct PairsShared<T, BD, true, false> {
     float4 jacc[BD];          // B-side sums of the item, one per body of band B
     float4 jblk[4][kRowLen];  // each wave's copy of its current j-block; between
                               // i-sets, with jsum, the running cross-wave sum of
@@ -794,7 +808,19 @@ __device__ __forceinline__ void pairs_item(const PairsArgs &k, int A, int B, int
                     ap[t] += bp[t];
                 }
             }
-            if constexpr (SYM) {
+            if constexpr (SYM && kGlobalJacc<BD>) {
+                const float4 g = sh.jsum[w][lane];
+                const long long body = (long long)B * BD + jb * 64 + lane;
+                if (body < k.n) {
+                    float4 *dst = k.partB + (size_t)slot_j * (size_t)k.n + body;
+                    float4 o = is == 0 ? make_float4(0.0f, 0.0f, 0.0f, 0.0f) : *dst;
+                    o.x -= g.x;
+                    o.y -= g.y;
+                    o.z -= g.z;
+                    o.w += g.w;
+                    *dst = o;
+                }
+            } else if constexpr (SYM) {
                 const float4 g = sh.jsum[w][lane];
                 float4 o = sh.jacc[jb * 64 + lane];
                 o.x -= g.x;
@@ -863,7 +889,7 @@ __device__ __forceinline__ void pairs_item(const PairsArgs &k, int A, int B, int
         probe_poison(sh.jblk[w][lane]);
         probe_poison(sh.jsum[w][lane]);
     }
-    if constexpr (SYM) {
+    if constexpr (SYM && !kGlobalJacc<BD>) {
         for (int i = threadIdx.x; i < BD; i += 64 * W) {
             const long long body = (long long)B * BD + i;
             if (body < k.n) k.partB[(size_t)slot_j * (size_t)k.n + body] = sh.jacc[i];
@@ -888,8 +914,10 @@ __global__ void __launch_bounds__(256) accel_pairs(PairsArgs k)
     if (d == 0) {
         pairs_item<T, BD, POT, false>(k, A, A, 0, 0, eps2, sh);
     } else {
-        for (int i = threadIdx.x; i < BD; i += 256) sh.jacc[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        __syncthreads();
+        if constexpr (!kGlobalJacc<BD>) {
+            for (int i = threadIdx.x; i < BD; i += 256) sh.jacc[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            __syncthreads();
+        }
         pairs_item<T, BD, POT, true>(k, A, B, d, k.compact ? A - k.band0 : nb - d, eps2, sh);
     }
 }
@@ -2659,6 +2687,7 @@ hipError_t launch_pairs(int band, int tpl, bool pot, const PairsArgs &args, hipS
         if (band == 512) fn = pairs_fn<8, 512>(pot);
         if (band == 1024) fn = pairs_fn<8, 1024>(pot);
         if (band == 2048) fn = pairs_fn<8, 2048>(pot);
+        if (band == 4096) fn = pairs_fn<8, 4096>(pot);
     }
     if (!fn || args.nbands < 1 || args.band0 < 0 || args.band1 > args.nbands ||
         args.band0 >= args.band1)

@@ -96,15 +96,16 @@ enum {
  *   wg     - threads per workgroup: 64, 128, 256 or 512 for NBODY_BCAST_LDS (also
  *            the LDS tile, in bodies), 256 for the other schemes.
  *   mode   - NBODY_MODE_*. The fields above describe NBODY_MODE_TILES. With
- *            NBODY_MODE_PAIRS only `band` (256, 512, 1024 or 2048 bodies),
- *            `tpl` (4 or 8 targets per lane, 4 only with 256-body bands) and
- *            `passes` may be set (0 = automatic); the output then has
- *            splits = number of bands = partial-sum slots per body, chunk =
- *            band, bcast = LDS, wg = 256. In one pass the scratch is splits x
- *            N x 16 bytes (8.6 GB at N = 2^20 with 2048-body bands); when that
- *            would exceed 1/16 of device memory the automatic plan evaluates
- *            the band-pair items in several passes over band ranges, each
- *            pass's sums added into running totals, with scratch of about
+ *            NBODY_MODE_PAIRS only `band` (256, 512, 1024, 2048 or 4096 bodies),
+ *            `tpl` (4 or 8 targets per lane, 4 only with 256-body bands, 8 only
+ *            with 4096-body bands) and `passes` may be set (0 = automatic); the
+ *            output then has splits = number of bands = partial-sum slots per
+ *            body, chunk = band, bcast = LDS, wg = 256. In one pass the scratch
+ *            is splits x N x 16 bytes (8.6 GB at N = 2^20 with 2048-body bands,
+ *            4.3 GB with 4096-body bands, which take 0.3-0.7 % longer there);
+ *            when that would exceed 1/16 of device memory the automatic plan
+ *            evaluates the band-pair items in several passes over band ranges,
+ *            each pass's sums added into running totals, with scratch of about
  *            (1.5 x splits / passes + 2) x N x 16 bytes.
  *            With NBODY_MODE_SMALL only `tpl` may be set: targets per workgroup,
  *            4, 8, 16 or 32 (0 = automatic); the output has splits = 1, chunk =

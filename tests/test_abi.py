@@ -284,6 +284,7 @@ def test_plan_rejects_bad_fields(nb):
                  dict(mode=3, wg=64), dict(mode=3, band=512), dict(mode=3, bcast="scalar"),
                  dict(band=300), dict(mode=2, splits=4), dict(mode=2, tpl=2), dict(mode=2, tpl=1),
                  dict(mode=2, band=256, tpl=8), dict(mode=2, band=128), dict(mode=2, passes=-1),
+                 dict(mode=2, band=4096, tpl=4), dict(mode=2, band=8192),
                  dict(mode=1, passes=2), dict(mode=3, passes=2),
                  dict(mode=2, bcast="scalar"), dict(wg=512, bcast="scalar"), dict(wg=96),
                  dict(wg=64, bcast="readlane")):

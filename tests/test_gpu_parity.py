@@ -199,7 +199,7 @@ def test_single_body(nb):
 BANDS = [512, 1024, 2048]
 PAIR_TPL = [4, 8]
 # (band, tpl): every instantiated pair kernel (256-body bands take 4 targets per lane only)
-PAIR_LAYOUTS = [(256, 4)] + [(b, t) for b in BANDS for t in PAIR_TPL]
+PAIR_LAYOUTS = [(256, 4)] + [(b, t) for b in BANDS for t in PAIR_TPL] + [(4096, 8)]
 
 
 @pytest.mark.parametrize("band,tpl", PAIR_LAYOUTS)
@@ -228,16 +228,18 @@ def test_pairs_mid_n(nb, band, tpl):
 
 @pytest.mark.parametrize("n,band,tpl", [(n, b, t) for n, b in ((4096, 512), (5000, 1024),
                                                                    (6144, 2048), (8192, 1024))
-                                         for t in PAIR_TPL] + [(2560, 256, 4), (2300, 256, 4)])
+                                         for t in PAIR_TPL] + [(2560, 256, 4), (2300, 256, 4)]
+                         + [(8192, 4096, 8), (12290, 4096, 8), (20000, 4096, 8)])
 def test_pairs_even_and_odd_band_counts(nb, n, band, tpl):
-    """Band counts 8, 5, 3, 8, 10 and 9: the opposite band of an even count is owned once."""
+    """Band counts 8, 5, 3, 8, 10, 9, 2, 4 and 5: the opposite band of an even count is owned
+    once (4096-body bands keep their B-side sums in the global slot)."""
     pos, _ = _bodies(n, 31)
     acc, pot = gpu_accel(pos, 1e-4, pot=True, plan=dict(mode="pairs", band=band, tpl=tpl))
     assert_accel_parity(acc, pot, _ref(n, 31, np.float32(1e-4)),
                         what=f"N={n} band={band} tpl={tpl}")
 
 
-@pytest.mark.parametrize("band,tpl", [(1024, 4), (1024, 8), (256, 4)])
+@pytest.mark.parametrize("band,tpl", [(1024, 4), (1024, 8), (256, 4), (4096, 8)])
 def test_pairs_invariants(nb, band, tpl):
     """Determinism, exact mass doubling, potential-independent acceleration, dyadic
     translation, zero-mass padding (same band count): all bit-exact."""
@@ -266,7 +268,8 @@ def test_pairs_invariants(nb, band, tpl):
 # ------------------------------------------------------------------ pair passes (bounded scratch)
 
 PASS_CASES = [(1000, 256, 4, 2), (1000, 256, 4, 4), (3000, 512, 8, 2), (3000, 512, 8, 6),
-              (5000, 1024, 4, 3), (4097, 2048, 8, 3), (2049, 512, 4, 5)]
+              (5000, 1024, 4, 3), (4097, 2048, 8, 3), (2049, 512, 4, 5), (9000, 4096, 8, 2),
+              (13000, 4096, 8, 4)]
 
 
 @pytest.mark.parametrize("n,band,tpl,passes", PASS_CASES)
@@ -311,20 +314,27 @@ def test_pair_passes_mid_n_and_steps(nb):
     assert np.array_equal(xk, xs) and np.array_equal(vk, vs)
 
 
-def test_pair_passes_two_million_sampled(nb):
-    """N = 2^21 uniform cube in the automatic plan: the one-pass slot scratch (34 GB) exceeds
-    the scratch share, so the plan takes several passes; sampled targets against the oracle."""
+@pytest.mark.parametrize("band", [0, 4096])
+def test_pair_passes_two_million_sampled(nb, band):
+    """N = 2^21 uniform cube: the automatic plan (2048-body bands, 34 GB of slots in one pass,
+    beyond the scratch share) takes several passes; 4096-body bands take one (16 GiB); sampled
+    targets against the oracle."""
     import oracle
 
     n = 1 << 21
-    p = nb.nbody_plan_for(n)
-    assert p.mode == nb.MODE_PAIRS and p.passes > 1, p.as_dict()
+    plan = None if band == 0 else dict(mode="pairs", band=band, tpl=8)
+    if band == 0:
+        p = nb.nbody_plan_for(n)
+        assert p.mode == nb.MODE_PAIRS and p.band == 2048 and p.passes > 1, p.as_dict()
+        band = p.band
     w = workloads.make("cube1m", n=n)
-    acc, pot = gpu_accel(w.pos, w.eps2)
+    acc, pot = gpu_accel(w.pos, w.eps2, plan=plan)
     rng = np.random.default_rng(21)
-    idx = np.unique(np.concatenate([rng.integers(0, n, 40), [0, n - 1]]))
+    idx = np.unique(np.concatenate([rng.integers(0, n, 40), [0, n - 1],
+                                    [k * band - 1 for k in (1, 255, 256, 511)],
+                                    [k * band for k in (1, 255, 256, 511)]]))
     assert_accel_parity(acc, pot, oracle.accel(w.pos, w.eps2, targets=idx), idx=idx,
-                        what=f"N=2^21 {p.as_dict()}")
+                        what=f"N=2^21 band={band}")
     nb.nbody_release_workspace()
 
 
@@ -405,6 +415,7 @@ def test_auto_plan_modes(nb):
     assert nb.nbody_plan_for(1 << 20).passes == 1
     p = nb.nbody_plan_for(1 << 22)
     assert p.mode == nb.MODE_PAIRS and p.band == 2048 and 1 < p.passes <= p.splits
+    assert nb.nbody_plan_for(1 << 27).mode == nb.MODE_PAIRS
     assert nb.nbody_plan_for(1 << 30).mode == nb.MODE_TILES  # beyond the pair launch grid
 
 

@@ -78,7 +78,7 @@ PROBE_CASES = (
     [dict(bcast="lds", tpl=1, wg=wg, splits=s) for wg in (64, 128, 256, 512) for s in (1, 3)]
     + [dict(mode="small", tpl=tw) for tw in (4, 8, 16, 32)]
     + [dict(mode="pairs", band=b, tpl=t)
-       for b, t in ((256, 4), (512, 4), (512, 8), (1024, 4), (1024, 8), (2048, 8))]
+       for b, t in ((256, 4), (512, 4), (512, 8), (1024, 4), (1024, 8), (2048, 8), (4096, 8))]
 )
 
 

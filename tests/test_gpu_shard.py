@@ -87,7 +87,7 @@ def test_shard_parts_and_merge(nb, n, band, shards, tpl):
         assert p3 is None and np.array_equal(a3, a2)
 
 
-@pytest.mark.parametrize("n,band", [(3000, 512), (70000, 2048)])
+@pytest.mark.parametrize("n,band", [(3000, 512), (70000, 2048), (70000, 4096)])
 def test_one_shard_equals_accel(nb, n, band):
     """A single shard finished is nbody_accel_plan with the same pairs plan, bit for bit."""
     import torch
