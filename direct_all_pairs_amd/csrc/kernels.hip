@@ -1167,6 +1167,7 @@ struct PackedLists {
     int *tab;         // kPackLds LDS ints (set by the kernel)
     int bound_seg;    // segment in tab (-1: none), uniform
     __device__ void bind(const P2PArgs &, int) { bound_seg = -1; }
+    __device__ int cell(int b) const { return b; }  // workgroups in cell order
     __device__ void range(int c, int &lo, int &hi) const
     {
         long long a = off[c], b = off[c + 1];
@@ -1227,6 +1228,49 @@ struct GridLists {
     // kGridLds LDS ints: the body range [sb, sn) of each run ((-1, -1) outside the grid),
     // then pre[10] and off[9] of the run sequence
     int *nbr;
+    int heavy_first;  // launch order of cells: see cell()
+    // The cell of launch index b. With heavy_first, heaviest neighbourhoods first: the
+    // interior cells (27 neighbours), then the six faces (18), the twelve edges (12)
+    // and the eight corners (8), each in natural order. Workgroups start roughly in
+    // launch order, so the cheapest cells are the ones left for the end of the launch,
+    // where they fill the CUs that free up (at 256 bodies per cell and N = 2^20, 4096
+    // cells run as about four rounds of workgroups: 4.3 % faster, same bits). A
+    // bijection of [0, dx*dy*dz); the identity without heavy_first or when a dimension
+    // is below 3.
+    __device__ int at(int x, int y, int z) const { return (z * dy + y) * dx + x; }
+    __device__ int cell(int b) const
+    {
+        const int ix = dx - 2, iy = dy - 2, iz = dz - 2;
+        if (!heavy_first || ix < 1 || iy < 1 || iz < 1) return b;
+        const int ni = ix * iy * iz;
+        if (b < ni) return at(1 + b % ix, 1 + (b / ix) % iy, 1 + b / (ix * iy));
+        b -= ni;
+#pragma unroll 1
+        for (int f = 0; f < 6; ++f) {  // z faces, y faces, x faces; low side first
+            const int axis = f >> 1, hi = f & 1;
+            const int a = axis == 2 ? iy : ix, sz = (axis == 0 ? iy : iz) * a;
+            if (b < sz) {
+                const int u = 1 + b % a, v = 1 + b / a;
+                if (axis == 0) return at(u, v, hi ? dz - 1 : 0);
+                if (axis == 1) return at(u, hi ? dy - 1 : 0, v);
+                return at(hi ? dx - 1 : 0, u, v);
+            }
+            b -= sz;
+        }
+#pragma unroll 1
+        for (int e = 0; e < 12; ++e) {  // four edges along x, four along y, four along z
+            const int axis = e >> 2, p = e & 1, q = (e >> 1) & 1;
+            const int len = axis == 0 ? ix : (axis == 1 ? iy : iz);
+            if (b < len) {
+                const int t = 1 + b;
+                if (axis == 0) return at(t, p ? dy - 1 : 0, q ? dz - 1 : 0);
+                if (axis == 1) return at(p ? dx - 1 : 0, t, q ? dz - 1 : 0);
+                return at(p ? dx - 1 : 0, q ? dy - 1 : 0, t);
+            }
+            b -= len;
+        }
+        return at(b & 1 ? dx - 1 : 0, b & 2 ? dy - 1 : 0, b & 4 ? dz - 1 : 0);
+    }
     __device__ const int *pre() const { return nbr + 2 * kGridRuns; }
     __device__ const int *off() const { return nbr + 3 * kGridRuns + 1; }
     __device__ void bind(const P2PArgs &k, int c)
@@ -1539,7 +1583,7 @@ __global__ void __launch_bounds__(64 * W, QUAD ? 4 : 8) p2p_kernel(P2PArgs k, Li
     __shared__ float4 rows[W][64];
     __shared__ float4 red[W][64 * TQ];  // each wave's per-target sums of the chunk
     __shared__ int nbr[kGridLds > kPackLds ? kGridLds : kPackLds];  // the lists' LDS table
-    const int c = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int c = lists.cell((int)blockIdx.x), lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int tb = k.cell_start[c], te = k.cell_start[c + 1];
     if (tb < 0 || te < tb || te > k.n) return;
     // workgroup blockIdx.y of the cell's gridDim.y takes its chunks q with
@@ -1733,7 +1777,7 @@ __global__ void __launch_bounds__(256) p2p_wg_kernel(P2PArgs k, Lists lists)
 {
     __shared__ float4 tile[2][256];
     __shared__ int nbr[kGridLds];
-    const int c = blockIdx.x, tid = threadIdx.x;
+    const int c = lists.cell((int)blockIdx.x), tid = threadIdx.x;
     const int tb = k.cell_start[c], te = k.cell_start[c + 1];
     if (tb < 0 || te < tb || te > k.n) return;
     // workgroup blockIdx.y of gridDim.y takes every gridDim.y-th 256-target chunk
@@ -2803,8 +2847,12 @@ hipError_t launch_p2p_grid(bool pot, bool wide, const P2PArgs &args, const GridS
 {
     if (args.ncell < 1 || args.ncell != g.dims[0] * g.dims[1] * g.dims[2])
         return hipErrorInvalidValue;
-    return launch_p2p_any(pot, wide, args, GridLists{g.dims[0], g.dims[1], g.dims[2], nullptr},
-                          stream);
+    // heavy cells first from 16 bodies per cell on average (measured: 0.9 % faster at
+    // 16, 2.4 % slower at 9.5 and 11 % at 4 bodies per cell, where the launch has many
+    // rounds and the natural order reads neighbouring cells together)
+    const int heavy_first = (long long)args.n >= 16ll * args.ncell ? 1 : 0;
+    return launch_p2p_any(pot, wide, args,
+                          GridLists{g.dims[0], g.dims[1], g.dims[2], nullptr, heavy_first}, stream);
 }
 
 hipError_t launch_grid_keys(const float4 *pos, int n, const GridSpec &g, unsigned *keys, int *idx,
