@@ -1337,30 +1337,18 @@ __device__ __forceinline__ bool next_tile(const P2PArgs &k, const Lists &lists, 
     return false;
 }
 
-// Targets per lane for a cell's large chunks, and the fewest remaining bodies
-// that take one (a chunk of 192-256 targets: at most a quarter of its lanes'
-// targets idle, against three or four separate 64-target passes). The kernel
-// has the four-target path (QUAD) only where cells average at least that many
-// bodies: its registers slow the one-target path for small cells (10 % at 131
-// bodies per cell), and it gains 10 % at 256.
-constexpr int kP2PWideT = 4;
-constexpr int kP2PWideMin = 192;
-
-// The chunk that starts where rem targets of a cell are left: four targets per lane
-// (quad: 256 targets) while at least kP2PWideMin remain with QUAD; else one per lane
+// The chunk that starts where rem targets of a cell are left: one target per lane
 // on 2^lg lanes per source group: 64 when more than 48 remain, 32 when 33-48 remain
 // (the rest, at most 16, then takes a chunk of its own with four or more source
 // groups, instead of leaving up to half of a 64-lane chunk idle: a chunk costs a
 // walk over the neighbourhood, so a rest of 17 or more keeps the 64-lane chunk),
-// else the next power of two >= rem. Returns the targets the chunk takes.
-template <bool QUAD>
-__device__ __forceinline__ int chunk_span(int rem, int &lg, bool &quad)
+// else the next power of two >= rem. Returns the targets the chunk takes. (Four
+// targets per lane in 256-target chunks, each staged source serving four terms,
+// needed 124 VGPRs and four waves per SIMD; at eight waves the one-target chunks
+// measured 4-5 % faster on 16^3 and 15^3 grids of N = 2^20 and on octree leaves of
+// ~256 bodies, the only places the automatic choice had used them.)
+__device__ __forceinline__ int chunk_span(int rem, int &lg)
 {
-    quad = QUAD && rem >= kP2PWideMin;
-    if (quad) {
-        lg = 6;
-        return 64 * kP2PWideT;
-    }
     const int want = rem > 48 ? 64 : (rem > 32 ? 32 : rem);
     int tw = 1;
     lg = 0;
@@ -1371,16 +1359,14 @@ __device__ __forceinline__ int chunk_span(int rem, int &lg, bool &quad)
     return tw;
 }
 
-// Whether a cell of r bodies has a chunk q >= 1 (the chunk sequence of chunk_span).
-// Only q = 1 is asked: the launches use at most two chunk workgroups per cell.
-template <bool QUAD>
+// Whether a cell of r bodies has a chunk q >= 1 (the chunk sequence of chunk_span);
+// the launches ask for q < 4 (at most four chunk workgroups per cell).
 __device__ __forceinline__ bool cell_has_chunk(int r, int q)
 {
     int n = 0;
     while (r > 0 && n <= q) {
         int lg;
-        bool quad;
-        r -= chunk_span<QUAD>(r, lg, quad);
+        r -= chunk_span(r, lg);
         ++n;
     }
     return n > q;
@@ -1562,8 +1548,7 @@ __device__ __forceinline__ void full_tile_sources(const float4 *r, const Targets
     for (int u = 0; u < 64 / G; ++u) interact4<1, POT>(r[u * G], tg, eps2, blk);
 }
 
-// Targets per chunk (chunk_span): a cell's bodies go up to 256 at a time (four per
-// lane) while at least 192 remain, then 64 at a time; a chunk of tw < 64 targets
+// Targets per chunk (chunk_span): a cell's bodies go 64 at a time; a chunk of tw < 64 targets
 // has tw lanes per source group and G = 64 / tw groups, lane (t, g) = (lane mod tw,
 // lane / tw) summing every G-th source of each of its tiles for target t; the G
 // group sums of a target are added in ascending g. So a 20-body cell keeps 64 lanes
@@ -1575,13 +1560,11 @@ __device__ __forceinline__ void full_tile_sources(const float4 *r, const Targets
 // Left alone, the compiler gave the CSR-list variants 116-122 VGPRs (four waves per
 // SIMD), loading a whole 16-source unroll of LDS reads ahead of the arithmetic; capped
 // they take 59-64 and no scratch (octree leaves of 32 bodies: 0.31 -> 0.24 ms).
-template <bool POT, typename Lists, bool QUAD, int W>
-__global__ void __launch_bounds__(64 * W, QUAD ? 4 : 8) p2p_kernel(P2PArgs k, Lists lists)
+template <bool POT, typename Lists, int W>
+__global__ void __launch_bounds__(64 * W, 8) p2p_kernel(P2PArgs k, Lists lists)
 {
-    static_assert(!QUAD || W == kP2PWideT, "a 256-target chunk is finished by four waves");
-    constexpr int TQ = QUAD ? kP2PWideT : 1;
     __shared__ float4 rows[W][64];
-    __shared__ float4 red[W][64 * TQ];  // each wave's per-target sums of the chunk
+    __shared__ float4 red[W][64];  // each wave's per-(target, group) sums of the chunk
     __shared__ int nbr[kGridLds > kPackLds ? kGridLds : kPackLds];  // the lists' LDS table
     const int c = lists.cell((int)blockIdx.x), lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int tb = k.cell_start[c], te = k.cell_start[c + 1];
@@ -1589,7 +1572,7 @@ __global__ void __launch_bounds__(64 * W, QUAD ? 4 : 8) p2p_kernel(P2PArgs k, Li
     // workgroup blockIdx.y of the cell's gridDim.y takes its chunks q with
     // q mod gridDim.y == blockIdx.y; it exits at once when it has none
     const int ny = (int)gridDim.y, y = (int)blockIdx.y;
-    if (y > 0 && !cell_has_chunk<QUAD>(te - tb, y)) return;
+    if (y > 0 && !cell_has_chunk(te - tb, y)) return;
     if constexpr (__is_same(Lists, GridLists)) lists.nbr = nbr;
     if constexpr (__is_same(Lists, PackedLists)) lists.tab = nbr;
     lists.bind(k, c);
@@ -1601,70 +1584,8 @@ __global__ void __launch_bounds__(64 * W, QUAD ? 4 : 8) p2p_kernel(P2PArgs k, Li
         const int rem = te - t0;
         const bool mine = q % ny == y;
         int lg;
-        bool quad;
-        const int span = chunk_span<QUAD>(rem, lg, quad);
+        const int span = chunk_span(rem, lg);
         if (!mine) {
-            t0 += span;
-            continue;
-        }
-        if (quad) {
-            // up to 256 targets, four per lane (target t0 + q * 64 + lane; past the
-            // cell end a lane computes on a clamped body and stores nothing): each
-            // staged source tile and each broadcast read serves four interactions
-            Targets<kP2PWideT> tg;
-#pragma unroll
-            for (int q = 0; q < kP2PWideT; ++q) {
-                const int i = t0 + q * 64 + lane;
-                const float4 me = k.pos[i < te ? i : te - 1];
-                tg.x[q] = me.x;
-                tg.y[q] = me.y;
-                tg.z[q] = me.z;
-            }
-            Total<kP2PWideT, POT> tot;
-            zero(tot);
-            Sums<kP2PWideT, POT> blk;  // at most kFlush sources per target, then into tot
-            zero(blk);
-            int held = 0;
-            walk_tiles<W>(k, lists, lo, hi, w, lane, row, [&](int cnt) {
-                if (cnt == 64) {
-#pragma unroll 16
-                    for (int u = 0; u < 64; ++u) interact4<kP2PWideT, POT>(row[u], tg, eps2, blk);
-                } else {
-#pragma unroll 8
-                    for (int u = 0; u < cnt; ++u) interact4<kP2PWideT, POT>(row[u], tg, eps2, blk);
-                }
-                held += cnt;
-                if (held > kFlush - 64) {
-                    add_into(tot, blk);
-                    zero(blk);
-                    held = 0;
-                }
-            });
-            add_into(tot, blk);
-            const Sums<kP2PWideT, POT> r = result(tot);
-#pragma unroll
-            for (int q = 0; q < kP2PWideT; ++q)
-                red[w][q * 64 + lane] = make_float4(r.ax[q], r.ay[q], r.az[q], POT ? r.p[q] : 0.0f);
-            __syncthreads();
-            // thread (w, lane) finishes targets t0 + idx, idx = w * 64 + lane (+ 64 W ...):
-            // the W wave sums in order
-            for (int idx = threadIdx.x; idx < 64 * kP2PWideT; idx += 64 * W) {
-                float4 a = red[0][idx];
-#pragma unroll
-                for (int ww = 1; ww < W; ++ww) {
-                    const float4 v = red[ww][idx];
-                    a = make_float4(a.x + v.x, a.y + v.y, a.z + v.z, a.w + v.w);
-                }
-                const int i = t0 + idx;
-                if (i < te) {
-                    const int o = k.out_index ? k.out_index[i] : i;
-                    k.acc_out[o] = make_float4(a.x, a.y, a.z, 0.0f);
-                    if constexpr (POT) k.pot_out[o] = -a.w;
-                }
-            }
-            __syncthreads();  // red is refilled by the next chunk
-#pragma unroll
-            for (int q = 0; q < kP2PWideT; ++q) probe_poison(red[w][q * 64 + lane]);
             t0 += span;
             continue;
         }
@@ -2800,30 +2721,25 @@ hipError_t launch_p2p_any(bool pot, bool wide, const P2PArgs &args, Lists l, hip
     P2PArgs a = args;
     void *k[] = {&a, &l};
     const void *fn;
-    static_assert(kP2PWideMin >= kP2PWavesMinBodies && kP2PWaves == kP2PWideT,
-                  "chunks of four targets per lane run in four-wave workgroups");
-    const bool quad = (long long)a.n >= (long long)kP2PWideMin * a.ncell;
-    const bool four = quad || (long long)a.n >= (long long)kP2PWavesMinBodies * a.ncell;
+    const bool four = (long long)a.n >= (long long)kP2PWavesMinBodies * a.ncell;
     const int waves = four ? kP2PWaves : 1;
     if (wide)
         fn = pot ? (const void *)&p2p_wg_kernel<true, Lists> : (const void *)&p2p_wg_kernel<false, Lists>;
-    else if (quad)
-        fn = pot ? (const void *)&p2p_kernel<true, Lists, true, kP2PWaves>
-                 : (const void *)&p2p_kernel<false, Lists, true, kP2PWaves>;
     else if (four)
-        fn = pot ? (const void *)&p2p_kernel<true, Lists, false, kP2PWaves>
-                 : (const void *)&p2p_kernel<false, Lists, false, kP2PWaves>;
+        fn = pot ? (const void *)&p2p_kernel<true, Lists, kP2PWaves>
+                 : (const void *)&p2p_kernel<false, Lists, kP2PWaves>;
     else
-        fn = pot ? (const void *)&p2p_kernel<true, Lists, false, 1>
-                 : (const void *)&p2p_kernel<false, Lists, false, 1>;
-    // chunk kernel: two workgroups per cell, each taking every other target chunk, so
-    // a cell's large chunk and the chunk of its remaining bodies run side by side; one
-    // when cells average fewer than 64 bodies (most are one chunk: the second workgroup
+        fn = pot ? (const void *)&p2p_kernel<true, Lists, 1>
+                 : (const void *)&p2p_kernel<false, Lists, 1>;
+    // chunk kernel: ny workgroups per cell, workgroup y taking the target chunks
+    // q = y, y + ny, ...: four from 192 bodies per cell on average (against two: 16^3
+    // and 15^3 grids of N = 2^20 0.9 and 2.2 % faster, octree leaves of ~256 bodies
+    // 4 %), two from 64, one below (most cells are one chunk: a second workgroup
     // would only exit; N = 2^20 on a 64^3 grid 0.268 -> 0.220 ms, leaves of ~4 bodies
-    // 0.375 -> 0.326 ms); the workgroup kernel: about one workgroup per 256-target chunk
-    // of a cell a little larger than the mean (at most 16), so large cells spread over
-    // the GPU
-    unsigned ny = (long long)a.n >= 64ll * a.ncell ? 2u : 1u;
+    // 0.375 -> 0.326 ms); the workgroup kernel: about one workgroup per 256-target
+    // chunk of a cell a little larger than the mean (at most 16), so large cells
+    // spread over the GPU
+    unsigned ny = (long long)a.n >= 192ll * a.ncell ? 4u : ((long long)a.n >= 64ll * a.ncell ? 2u : 1u);
     if (wide) {
         const double m = (double)a.n / (double)a.ncell;
         const double chunks = (m + 3.0 * std::sqrt(m)) / 256.0;

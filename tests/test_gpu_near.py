@@ -60,7 +60,7 @@ def test_p2p_full_lists_equal_direct_sum(nb, n, ncell):
     """Every cell listing every cell: the near field is the whole direct sum (cells of up to
     ~75 bodies on average run one wave per cell, larger ones the 256-thread kernel; lists of
     150 and 200 entries are walked in segments of 64 entries: one wave per cell at ~20
-    bodies, four waves at ~80 and four targets per lane at ~200)."""
+    bodies, four waves at ~80, four workgroups of four waves per cell at ~200)."""
     import oracle
 
     pos, _ = workloads.random_bodies(n, seed=1000 + n)
@@ -229,10 +229,10 @@ def test_near_grid_huge_cells_sixteen_workgroups(nb):
     assert np.all(np.isfinite(acc)) and np.all(np.isfinite(pot))  # every body written
 
 
-def test_near_grid_many_large_cells_four_targets_per_lane(nb):
-    """N = 2^20 on a 16^3 grid (4096 cells of ~256 bodies: one wave per cell, chunks of 192 or
-    more targets four per lane, the rest one per lane); sampled targets against the grid
-    definition, including cells below and above 256 bodies."""
+def test_near_grid_many_large_cells(nb):
+    """N = 2^20 on a 16^3 grid (4096 cells of ~256 bodies: four workgroups of four waves per
+    cell, 64-target chunks and a smaller rest, interior cells launched first); sampled targets
+    against the grid definition, including cells below and above 256 bodies."""
     import oracle
 
     w = workloads.make("cube1m")

@@ -125,7 +125,7 @@ def test_probe_build_shared_tile_near_field(nb, probe, n, h, dims):
     """Eight large cells (2 x 2 x 2 grid, ~2500 bodies each): the 256-thread shared-tile
     near-field kernel, several target chunks and source tiles per cell. 4096 cells of ~195
     and of ~24 bodies: the chunk kernel, whose four waves add their sums through a shared
-    buffer (four targets per lane, and source groups for small chunks)."""
+    buffer (64-target chunks, and source groups for small chunks)."""
     import torch
 
     pos_h, _ = workloads.random_bodies(n, seed=12)
@@ -152,7 +152,7 @@ def test_probe_build_shared_tile_near_field(nb, probe, n, h, dims):
 def test_probe_build_list_segments(nb, probe, n, ncell, per_list):
     """CSR lists of more than 64 entries: the near-field kernel walks them in segments whose
     table wave 0 rewrites in LDS between two workgroup barriers: one wave per cell at ~20
-    bodies per cell, four waves at ~80, four waves with four targets per lane at ~190."""
+    bodies per cell, four waves at ~80, four workgroups of four waves per cell at ~190."""
     import torch
 
     pos_h, _ = workloads.random_bodies(n, seed=13)
