@@ -321,7 +321,7 @@ int small_tw(int64_t n) { return n <= 2048 ? 4 : (n <= 6144 ? 8 : 16); }
 // The automatic pair band for N and a requested tpl (0 = any): 256 bodies to
 // N = 36863, above it the largest band with at least 64 work items per
 // compute unit (512 at least). 4096-body bands (half the slots of 2048, on
-// request) measured 0.3-0.7 % slower at N = 2^20, 0.25 % slower at 1.5 M
+// request) measured 0.3-1.3 % slower at N = 2^20, 0.25 % slower at 1.5 M
 // (one pass against two of 2048), 0.25 % faster at 2^21 and 1 % slower at
 // 2^22 (round-robin), so they are not chosen automatically.
 int auto_band(int64_t n, int tpl, const DeviceFacts &dev)

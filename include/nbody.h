@@ -102,7 +102,7 @@ enum {
  *            output then has splits = number of bands = partial-sum slots per
  *            body, chunk = band, bcast = LDS, wg = 256. In one pass the scratch
  *            is splits x N x 16 bytes (8.6 GB at N = 2^20 with 2048-body bands,
- *            4.3 GB with 4096-body bands, which take 0.3-0.7 % longer there);
+ *            4.3 GB with 4096-body bands, which take 0.3-1.3 % longer there);
  *            when that would exceed 1/16 of device memory the automatic plan
  *            evaluates the band-pair items in several passes over band ranges,
  *            each pass's sums added into running totals, with scratch of about
