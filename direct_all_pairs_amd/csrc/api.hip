@@ -1180,10 +1180,12 @@ int nbody_near_tree(const nbody_f4 *pos, int64_t N, float eps2, int64_t leaf_siz
                                    stream);
     if (e == hipSuccess) e = nbk::scan_exclusive(cnt, parts, counters + 1, scan_temp1, stream);
     if (e != hipSuccess) return hip_fail(e, "near-tree lists");
-    // A leaf B meets at most 27 leaves no smaller than itself (each holds a different one
-    // of the 27 cells of B's level around B) and at most 26 smaller ones, so the lists hold
-    // at most 53 entries per leaf: their scratch is sized from the leaf count without a
-    // second wait (which remains for leaf counts whose bound passes 2^31 - 1 entries).
+    // A leaf meets at most 27 leaves no smaller than itself (each holds a different one of
+    // the 27 cells of its level around it). A leaf may meet any number of smaller ones, but
+    // each such pair is also a pair of the smaller leaf with a larger one, of which that
+    // leaf has at most 26; so all lists together hold at most 27 + 26 = 53 entries per
+    // leaf. Their scratch is sized from the leaf count without a second wait (which
+    // remains for leaf counts whose bound passes 2^31 - 1 entries).
     const long long bound = (long long)nbk::kTreeListsPerLeaf * nleaf;
     unsigned long long nlist = 0, terms = 0;
     auto read_totals = [&]() -> int {

@@ -222,7 +222,8 @@ struct TreeLeaves {
 // counters[2..5] through per-workgroup records in parts (tree_parts_bytes). Fill pass
 // (off = the exclusive sums of cnt): part q of leaf A's list written at
 // list[off[27 A + q] ..] (never at or past list_cap), list_off[A] = off[27 A],
-// list_off[nleaf] = the total. The lists hold at most kTreeListsPerLeaf entries per leaf.
+// list_off[nleaf] = the total. All lists together hold at most kTreeListsPerLeaf entries
+// per leaf (one leaf's list may hold more).
 constexpr int kTreeListsPerLeaf = 53;
 size_t tree_parts_bytes(int nleaf);
 hipError_t launch_tree_lists(const TreeLeaves &leaves, int *counters, void *parts, int *cnt,

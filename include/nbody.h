@@ -322,7 +322,7 @@ typedef struct nbody_tree_stats {
  * coordinate gives unspecified results for the bodies, never an access out of
  * bounds). stats (host, may be NULL) receives the leaf and list counts.
  * The call waits once on the stream, for the number of leaves (the host sizes the
- * lists' scratch from it: at most 53 list entries per leaf), and returns with the
+ * lists' scratch from it: at most 53 list entries per leaf in total), and returns with the
  * rest enqueued; with stats it also waits for the end of the call. More than
  * 2^31 - 1 list entries (possible only with over 40 million leaves) is EINVAL.
  * Scratch: ~N x 100 bytes + ~300 bytes per leaf.

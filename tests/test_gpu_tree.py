@@ -140,6 +140,43 @@ def test_near_tree_deep_leaves(nb):
     assert_accel_parity(acc[:-1], pot[:-1], g, what="deep leaves vs lattice grid")
 
 
+def test_near_tree_big_leaf_beside_fine_leaves(nb):
+    """One leaf may list many smaller ones; only the total is bounded (53 per leaf). The octant
+    [0, 1/2]^3 holds two bodies (one leaf at level 1); the octant beside it along x holds two
+    bodies in each of its 8^3 cells of side 1/16 (512 leaves at level 4), and a body at (1, 1, 1)
+    sets the root cube [0, 1]^3 (one more leaf). The big leaf's closed cube meets the 64 fine
+    leaves on the shared face and the corner leaf: 66 entries with itself. Leaf, list-entry and
+    pair-term counts against a brute-force count over the known leaf cubes; results against the
+    oracle."""
+    import oracle
+
+    rng = np.random.default_rng(21)
+    fine = np.stack(np.meshgrid(*[np.arange(8)] * 3, indexing="ij"), -1).reshape(-1, 3)
+    fine = np.repeat(fine, 2, axis=0)
+    xf = (fine + rng.uniform(0.15, 0.85, size=fine.shape)) / 16.0
+    xf[:, 0] += 0.5
+    x = np.concatenate([[[0.0, 0.0, 0.0], [0.25, 0.25, 0.25]], xf, [[1.0, 1.0, 1.0]]])
+    pos = np.zeros((x.shape[0], 4), np.float32)
+    pos[:, :3] = x
+    pos[:, 3] = rng.uniform(0.5, 1.5, size=x.shape[0]) / x.shape[0]
+    # leaves as (lo corner, side, bodies)
+    leaves = [((0.0, 0.0, 0.0), 0.5, 2), ((0.5, 0.5, 0.5), 0.5, 1)]
+    leaves += [((0.5 + i / 16, j / 16, k / 16), 1 / 16, 2)
+               for i in range(8) for j in range(8) for k in range(8)]
+    lo = np.array([l[0] for l in leaves])
+    side = np.array([l[1] for l in leaves])
+    cnt = np.array([l[2] for l in leaves], np.int64)
+    hi = lo + side[:, None]
+    meet = np.all((np.maximum(lo[:, None, :], lo[None, :, :])
+                   <= np.minimum(hi[:, None, :], hi[None, :, :])), axis=2)
+    assert meet[0].sum() == 66  # the big leaf's list
+    acc, pot, st = gpu_near_tree(nb, pos, 1e-6, 2)
+    assert st["leaves"] == len(leaves)
+    assert st["list_entries"] == int(meet.sum()) <= 53 * len(leaves)
+    assert st["pair_terms"] == int((meet * np.outer(cnt, cnt)).sum())
+    assert_accel_parity(acc, pot, oracle.near_tree(pos, 1e-6, 2), what="big leaf beside fine leaves")
+
+
 def test_near_tree_coincident_bodies(nb):
     """All bodies at one point: one leaf (root cube side 1), the whole direct sum."""
     import oracle
