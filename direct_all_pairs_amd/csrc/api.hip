@@ -232,29 +232,6 @@ constexpr int64_t kMaxGridCells = (int64_t)1 << 28;
 // Most bodies nbody_near_tree takes (its scans run over N + 1 int entries).
 constexpr int64_t kMaxTreeN = (int64_t)1 << 30;
 
-// Near field: two waves per cell unless the cells are large (at least 96 bodies
-// on average) and few (fewer than 12 per CU): then 256-thread workgroups sharing
-// source tiles, about one per 256-target chunk of a cell. Measured on N = 2^20
-// uniform cubes (workgroups vs two waves per cell): 216 cells of 4855 bodies
-// 34.6 vs 178 ms, 512 of 2048: 18.3 vs 42.9 ms, 1000 of 1049: 9.7 vs 15.3 ms,
-// 2197 of 477: 4.39 vs 5.50 ms, 2744 of 382: 4.14 vs 4.28 ms; 3375 of 311: 4.02
-// vs 3.21 ms and 4096 of 256: 3.17 vs 2.64 ms (two waves better).
-constexpr int64_t kWideCellBodies = 96;
-constexpr int64_t kWideMaxCellsPerCU = 12;
-int wide_cells(int64_t n, int64_t ncell, bool *wide)
-{
-    *wide = false;
-    if (ncell <= 0 || n < kWideCellBodies * ncell) return NBODY_OK;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    DeviceFacts f;
-    int rc = device_facts(dev, &f);
-    if (rc != NBODY_OK) return rc;
-    *wide = ncell < kWideMaxCellsPerCU * (int64_t)f.cus;
-    return NBODY_OK;
-}
-
 // Largest N the automatic plan gives to NBODY_MODE_SMALL; pair-symmetric bands
 // (scratch permitting) take every N above it.
 constexpr int64_t kSmallMaxN = 6144;
@@ -1004,11 +981,8 @@ int nbody_p2p(const nbody_f4 *pos, int64_t N, float eps2, const int32_t *cell_st
     timer_arm();
     nbk::P2PArgs a{(const float4 *)pos, (int)N, eps2, cell_start, ncell, list_off, cells,
                    (long long)nlist, (float4 *)acc_out, pot_out, nullptr};
-    bool wide = false;
-    rc = wide_cells(N, ncell, &wide);
-    if (rc != NBODY_OK) return rc;
     hipError_t e =
-        timed_launch(stream, [&] { return nbk::launch_p2p(pot_out != nullptr, wide, a, stream); });
+        timed_launch(stream, [&] { return nbk::launch_p2p(pot_out != nullptr, a, stream); });
     if (e != hipSuccess) return hip_fail(e, "p2p kernel launch");
     return ok();
 }
@@ -1077,11 +1051,8 @@ int nbody_near_grid(const nbody_f4 *pos, int64_t N, float eps2, const float lo[3
     if (e == hipSuccess) {
         nbk::P2PArgs a{spos, n, eps2, start, nc, nullptr, nullptr, 0, (float4 *)acc_out, pot_out,
                        perm};
-        bool wide = false;
-        rc = wide_cells(N, nc, &wide);
-        if (rc != NBODY_OK) return rc;
-        e = timed_launch(
-            stream, [&] { return nbk::launch_p2p_grid(pot_out != nullptr, wide, a, g, stream); });
+        e = timed_launch(stream,
+                         [&] { return nbk::launch_p2p_grid(pot_out != nullptr, a, g, stream); });
     }
     if (e != hipSuccess) return hip_fail(e, "near-grid launch");
     return ok();
@@ -1217,11 +1188,7 @@ int nbody_near_tree(const nbody_f4 *pos, int64_t N, float eps2, int64_t leaf_siz
     if (e == hipSuccess) {
         nbk::P2PArgs a{spos, n, eps2, start, nleaf, list_off, list, cap, (float4 *)acc_out,
                        pot_out, perm};
-        bool wide = false;
-        rc = wide_cells(N, nleaf, &wide);
-        if (rc != NBODY_OK) return rc;
-        e = timed_launch(stream,
-                         [&] { return nbk::launch_p2p(pot_out != nullptr, wide, a, stream); });
+        e = timed_launch(stream, [&] { return nbk::launch_p2p(pot_out != nullptr, a, stream); });
     }
     if (e != hipSuccess) return hip_fail(e, "near-tree launch");
     if (stats) {

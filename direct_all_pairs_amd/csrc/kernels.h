@@ -136,15 +136,13 @@ struct GridSpec {
     int dims[3];
 };
 
-// wide: 256-thread workgroups sharing 256-body source tiles, about one per
-// 256-target chunk of a cell (large cells); otherwise two four-wave workgroups
-// per cell (small cells) taking alternate target chunks, whose waves take the
-// chunk's source tiles round-robin, and where chunks of 192 or more targets take
-// four per lane when cells average at least 192 bodies.
-hipError_t launch_p2p(bool pot, bool wide, const P2PArgs &args, hipStream_t stream);
-// The same kernels with the 27 neighbour cells of the grid as every cell's list.
-hipError_t launch_p2p_grid(bool pot, bool wide, const P2PArgs &args, const GridSpec &g,
-                           hipStream_t stream);
+// One to 1024 workgroups per cell (by the mean cell size) taking the cell's target
+// chunks in turn (64 targets, one per lane, or a smaller rest with source groups);
+// four waves per workgroup from 64 bodies per cell on average, which take the
+// chunk's source tiles round-robin.
+hipError_t launch_p2p(bool pot, const P2PArgs &args, hipStream_t stream);
+// The same kernel with the 27 neighbour cells of the grid as every cell's list.
+hipError_t launch_p2p_grid(bool pot, const P2PArgs &args, const GridSpec &g, hipStream_t stream);
 // keys[i] = linear cell of body i, idx[i] = i.
 hipError_t launch_grid_keys(const float4 *pos, int n, const GridSpec &g, unsigned *keys, int *idx,
                             hipStream_t stream);

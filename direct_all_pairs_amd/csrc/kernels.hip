@@ -1668,105 +1668,6 @@ __global__ void __launch_bounds__(64 * W, 8) p2p_kernel(P2PArgs k, Lists lists)
     }
 }
 
-// Large cells: gridDim.y 256-thread workgroups per target cell, each taking
-// every gridDim.y-th chunk of 256 targets (one per thread); source tiles of 256
-// bodies are staged once for all four waves
-// (double-buffered, one barrier per tile: the barrier after a tile both
-// publishes the next buffer and guards the one about to be overwritten), read
-// with uniform addresses. The cursor over (list entry, tile) is uniform.
-template <typename Lists>
-__device__ __forceinline__ bool next_tile256(const P2PArgs &k, const Lists &lists, int hi, int &e,
-                                             int &j0, int &se)
-{
-    if (j0 + 256 < se) {
-        j0 += 256;
-        return true;
-    }
-#pragma unroll 1
-    for (++e; e < hi; ++e) {
-        int sb, sn;
-        if (!lists.source(k, e, sb, sn)) continue;
-        j0 = sb;
-        se = sn;
-        return true;
-    }
-    return false;
-}
-
-template <bool POT, typename Lists>
-__global__ void __launch_bounds__(256) p2p_wg_kernel(P2PArgs k, Lists lists)
-{
-    __shared__ float4 tile[2][256];
-    __shared__ int nbr[kGridLds];
-    const int c = lists.cell((int)blockIdx.x), tid = threadIdx.x;
-    const int tb = k.cell_start[c], te = k.cell_start[c + 1];
-    if (tb < 0 || te < tb || te > k.n) return;
-    // workgroup blockIdx.y of gridDim.y takes every gridDim.y-th 256-target chunk
-    const int ny = (int)gridDim.y, y = (int)blockIdx.y;
-    if (y > 0 && tb + 256 * y >= te) return;
-    if constexpr (__is_same(Lists, GridLists)) lists.nbr = nbr;
-    if constexpr (__is_same(Lists, PackedLists)) lists.tab = nbr;
-    lists.bind(k, c);
-    int lo, hi;
-    lists.range(c, lo, hi);
-    const float eps2 = in_vgpr(k.eps2);
-    for (int t0 = tb + 256 * y; t0 < te; t0 += 256 * ny) {
-        const int i = t0 + tid;
-        const float4 me = k.pos[i < te ? i : te - 1];
-        Targets<1> tg;
-        tg.x[0] = me.x;
-        tg.y[0] = me.y;
-        tg.z[0] = me.z;
-        Total<1, POT> tot;
-        zero(tot);
-        int e = lo - 1, j0 = 0, se = 0;
-        bool have = next_tile256(k, lists, hi, e, j0, se);
-        if (have) tile[0][tid] = load_or_zero(k.pos, j0 + tid, se);
-        __syncthreads();
-        int buf = 0;
-        while (have) {
-            const int cnt = se - j0 < 256 ? se - j0 : 256;
-            int e2 = e, j2 = j0, se2 = se;
-            const bool have2 = next_tile256(k, lists, hi, e2, j2, se2);
-            if (have2) probe_poison(tile[buf ^ 1][tid]);
-            const int jn = j2 + tid;
-            float4 r = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            if (have2) r = k.pos[jn < se2 ? jn : se2 - 1];  // raw prefetch of the next tile
-            const float4 *tl = tile[buf];
-            Sums<1, POT> blk;
-            zero(blk);
-            if (cnt == 256) {
-                // full tile: uniform addresses at constant offsets
-#pragma unroll 16
-                for (int u = 0; u < 256; ++u) interact4<1, POT>(tl[u], tg, eps2, blk);
-            } else {
-#pragma unroll 8
-                for (int u = 0; u < cnt; ++u) interact4<1, POT>(tl[u], tg, eps2, blk);
-            }
-            add_into(tot, blk);
-            if (have2) {
-                const bool in = jn < se2;  // per-component select: a float4 ternary would
-                                           // go through private memory
-                tile[buf ^ 1][tid] = make_float4(in ? r.x : 0.0f, in ? r.y : 0.0f,
-                                                 in ? r.z : 0.0f, in ? r.w : 0.0f);
-            }
-            __syncthreads();
-            buf ^= 1;
-            e = e2;
-            j0 = j2;
-            se = se2;
-            have = have2;
-        }
-        probe_poison(tile[0][tid]);  // the next chunk's first tile goes here
-        if (i < te) {
-            const Sums<1, POT> res = result(tot);
-            const int o = k.out_index ? k.out_index[i] : i;
-            k.acc_out[o] = make_float4(res.ax[0], res.ay[0], res.az[0], 0.0f);
-            if constexpr (POT) k.pot_out[o] = -res.p[0];
-        }
-    }
-}
-
 __device__ __forceinline__ int grid_axis(float x, float lo, float inv_h, int dim)
 {
     float f = floorf((x - lo) * inv_h);
@@ -2716,50 +2617,49 @@ hipError_t launch_small(int tw, bool pot, bool step, const SmallArgs &args, hipS
 }
 
 template <typename Lists>
-hipError_t launch_p2p_any(bool pot, bool wide, const P2PArgs &args, Lists l, hipStream_t stream)
+hipError_t launch_p2p_any(bool pot, const P2PArgs &args, Lists l, hipStream_t stream)
 {
     P2PArgs a = args;
     void *k[] = {&a, &l};
     const void *fn;
     const bool four = (long long)a.n >= (long long)kP2PWavesMinBodies * a.ncell;
     const int waves = four ? kP2PWaves : 1;
-    if (wide)
-        fn = pot ? (const void *)&p2p_wg_kernel<true, Lists> : (const void *)&p2p_wg_kernel<false, Lists>;
-    else if (four)
+    if (four)
         fn = pot ? (const void *)&p2p_kernel<true, Lists, kP2PWaves>
                  : (const void *)&p2p_kernel<false, Lists, kP2PWaves>;
     else
         fn = pot ? (const void *)&p2p_kernel<true, Lists, 1>
                  : (const void *)&p2p_kernel<false, Lists, 1>;
-    // chunk kernel: ny workgroups per cell, workgroup y taking the target chunks
-    // q = y, y + ny, ...: four from 192 bodies per cell on average (against two: 16^3
-    // and 15^3 grids of N = 2^20 0.9 and 2.2 % faster, octree leaves of ~256 bodies
-    // 4 %), two from 64, one below (most cells are one chunk: a second workgroup
-    // would only exit; N = 2^20 on a 64^3 grid 0.268 -> 0.220 ms, leaves of ~4 bodies
-    // 0.375 -> 0.326 ms); the workgroup kernel: about one workgroup per 256-target
-    // chunk of a cell a little larger than the mean (at most 16), so large cells
-    // spread over the GPU
+    // ny workgroups per cell, workgroup y taking the target chunks q = y, y + ny, ...:
+    // one below 64 bodies per cell on average (most cells are one chunk: a second
+    // workgroup would only exit; N = 2^20 on a 64^3 grid 0.268 -> 0.220 ms, leaves of
+    // ~4 bodies 0.375 -> 0.326 ms), two from 64, four from 192 (against two: 16^3 and
+    // 15^3 grids of N = 2^20 0.9 and 2.2 % faster, octree leaves of ~256 bodies 4 %),
+    // and from 384 about one per 64-target chunk of a cell a little larger than the
+    // mean, ceil((m + 3 sqrt(m)) / 64) for mean cell size m, at most 1024 (so that a
+    // few very large cells still fill the GPU). This replaced a kernel of 256-thread
+    // workgroups sharing 256-body source tiles for large cells: against it, N = 2^20
+    // on grids of 14^3 to 4^3 cells (382 to 16384 bodies each) 3.58 -> 2.80, 5.31 ->
+    // 4.47, 8.73 -> 7.51, 15.6 -> 14.7, 33.0 -> 31.1 and 162 -> 99 ms; octree leaves of
+    // ~1000 bodies 14.6 -> 9.2 ms.
     unsigned ny = (long long)a.n >= 192ll * a.ncell ? 4u : ((long long)a.n >= 64ll * a.ncell ? 2u : 1u);
-    if (wide) {
+    if ((long long)a.n >= 384ll * a.ncell) {
         const double m = (double)a.n / (double)a.ncell;
-        const double chunks = (m + 3.0 * std::sqrt(m)) / 256.0;
-        ny = chunks >= 16.0 ? 16u : (unsigned)std::ceil(chunks);
-        if (ny < 1) ny = 1;
+        const double want = std::ceil((m + 3.0 * std::sqrt(m)) / 64.0);
+        ny = want >= 1024.0 ? 1024u : (unsigned)want;
     }
-    return hipLaunchKernel(fn, dim3((unsigned)a.ncell, ny), dim3(wide ? 256 : 64 * waves), k, 0,
-                           stream);
+    return hipLaunchKernel(fn, dim3((unsigned)a.ncell, ny), dim3(64 * waves), k, 0, stream);
 }
 
-hipError_t launch_p2p(bool pot, bool wide, const P2PArgs &args, hipStream_t stream)
+hipError_t launch_p2p(bool pot, const P2PArgs &args, hipStream_t stream)
 {
     if (args.ncell < 1) return args.ncell == 0 ? hipSuccess : hipErrorInvalidValue;
-    return launch_p2p_any(pot, wide, args,
+    return launch_p2p_any(pot, args,
                           PackedLists{args.list_off, args.list, args.nlist, args.ncell, nullptr, -1},
                           stream);
 }
 
-hipError_t launch_p2p_grid(bool pot, bool wide, const P2PArgs &args, const GridSpec &g,
-                           hipStream_t stream)
+hipError_t launch_p2p_grid(bool pot, const P2PArgs &args, const GridSpec &g, hipStream_t stream)
 {
     if (args.ncell < 1 || args.ncell != g.dims[0] * g.dims[1] * g.dims[2])
         return hipErrorInvalidValue;
@@ -2767,8 +2667,8 @@ hipError_t launch_p2p_grid(bool pot, bool wide, const P2PArgs &args, const GridS
     // 16, 2.4 % slower at 9.5 and 11 % at 4 bodies per cell, where the launch has many
     // rounds and the natural order reads neighbouring cells together)
     const int heavy_first = (long long)args.n >= 16ll * args.ncell ? 1 : 0;
-    return launch_p2p_any(pot, wide, args,
-                          GridLists{g.dims[0], g.dims[1], g.dims[2], nullptr, heavy_first}, stream);
+    return launch_p2p_any(pot, args, GridLists{g.dims[0], g.dims[1], g.dims[2], nullptr, heavy_first},
+                          stream);
 }
 
 hipError_t launch_grid_keys(const float4 *pos, int n, const GridSpec &g, unsigned *keys, int *idx,

@@ -57,10 +57,10 @@ def _cells(n, ncell, seed):
 @pytest.mark.parametrize("n,ncell", [(1, 1), (70, 3), (1000, 17), (3001, 40), (3001, 10),
                                      (5000, 4), (3001, 150), (12000, 150), (40000, 200)])
 def test_p2p_full_lists_equal_direct_sum(nb, n, ncell):
-    """Every cell listing every cell: the near field is the whole direct sum (cells of up to
-    ~75 bodies on average run one wave per cell, larger ones the 256-thread kernel; lists of
-    150 and 200 entries are walked in segments of 64 entries: one wave per cell at ~20
-    bodies, four waves at ~80, four workgroups of four waves per cell at ~200)."""
+    """Every cell listing every cell: the near field is the whole direct sum (one wave per
+    cell below 64 bodies per cell on average, four-wave workgroups above, up to 22 of them per
+    cell at ~1250 bodies; lists of 150 and 200 entries are walked in segments of 64 entries:
+    one wave per cell at ~20 bodies, four waves at ~80, four workgroups per cell at ~200)."""
     import oracle
 
     pos, _ = workloads.random_bodies(n, seed=1000 + n)
@@ -201,8 +201,9 @@ def test_near_grid_deterministic_and_order_free(nb):
 
 
 def test_near_grid_few_large_cells(nb):
-    """64 cells of ~780 bodies: the shared-tile 256-thread kernel, several target chunks and
-    source tiles per cell; sampled targets against the grid definition."""
+    """64 cells of ~780 bodies: 15 four-wave workgroups per cell, each taking every 15th
+    64-target chunk, many source tiles per chunk; sampled targets against the grid
+    definition."""
     import oracle
 
     pos, _ = workloads.random_bodies(50000, seed=51)

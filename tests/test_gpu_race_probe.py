@@ -2,7 +2,7 @@
 hands back only after first writing NaN into it, so a missing or misplaced barrier shows up
 as NaN or changed outputs. With the barriers in place its results must equal the library's
 bit for bit, with no NaN, for tile counts and sizes at tile boundaries +- 1 in every mode that
-shares LDS between waves (tiles, small N, pair bands, the shared-tile near-field kernel)."""
+shares LDS between waves (tiles, small N, pair bands, the near-field chunk kernel)."""
 
 from __future__ import annotations
 
@@ -121,11 +121,11 @@ def test_probe_build_small_steps(nb, probe):
 @pytest.mark.parametrize("n,h,dims", [(20000, 1.0, (2, 2, 2)),
                                       (800000, 0.125, (16, 16, 16)),
                                       (100000, 0.125, (16, 16, 16))])
-def test_probe_build_shared_tile_near_field(nb, probe, n, h, dims):
-    """Eight large cells (2 x 2 x 2 grid, ~2500 bodies each): the 256-thread shared-tile
-    near-field kernel, several target chunks and source tiles per cell. 4096 cells of ~195
-    and of ~24 bodies: the chunk kernel, whose four waves add their sums through a shared
-    buffer (64-target chunks, and source groups for small chunks)."""
+def test_probe_build_chunk_near_field(nb, probe, n, h, dims):
+    """The near-field chunk kernel, whose four waves add their sums through a shared buffer:
+    eight large cells (2 x 2 x 2 grid, ~2500 bodies each: 42 workgroups per cell, each with
+    one or two 64-target chunks and many source tiles), 4096 cells of ~195 and of ~24 bodies
+    (64-target chunks, and source groups for small chunks)."""
     import torch
 
     pos_h, _ = workloads.random_bodies(n, seed=12)

@@ -227,10 +227,9 @@ def test_near_tree_cube1m_sampled(nb):
 
 @pytest.mark.parametrize("n,leaf", [(60000, 200), (60000, 1000), (1 << 20, 1024)])
 def test_near_tree_large_leaves(nb, n, leaf):
-    """Large leaves, uniform cubes: 512 leaves of ~117 bodies (the four-wave kernel), 64 of
-    ~940 (the 256-thread shared-tile kernel) and 4096 of ~256 at N = 2^20 (four targets per
-    lane) over the packed leaf lists; sampled targets, both ends included, against the
-    definition."""
+    """Large leaves, uniform cubes: 512 leaves of ~117 bodies (two four-wave workgroups per
+    leaf), 64 of ~940 (16 per leaf) and 4096 of ~256 at N = 2^20 (four per leaf) over the
+    packed leaf lists; sampled targets, both ends included, against the definition."""
     import oracle
 
     pos, _ = workloads.random_bodies(n, seed=15 + leaf)
