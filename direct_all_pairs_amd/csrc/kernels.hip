@@ -2280,6 +2280,22 @@ struct TreeIndex {
         }
         return a;
     }
+    // lower_in(a, b, x) found from a outwards: a, then a + 1, a + 2, a + 4, ... until a key
+    // at or past x, then a binary search inside that step. A skipped subtree mostly ends
+    // at the next leaf (94 % of the skips of a 65,536-body Plummer sphere at leaf size 64),
+    // which this finds with one load instead of a search over the cell's whole key range
+    // (the walk's chains of dependent loads were up to ~600 long there).
+    __device__ int gallop(int a, int b, u64 x) const
+    {
+        if (a >= b || key[a] >= x) return a;
+        int lo = a + 1, step = 1;
+        while (lo < b && key[lo] < x) {
+            a = lo;
+            step <<= 1;
+            lo = a + step < b ? a + step : b;
+        }
+        return lower_in(a + 1, lo, x);
+    }
     // The first leaf with key > x (u) and the first with key >= y (l), as two interleaved
     // binary searches whose loads overlap; the leaves with keys in x's coarse cell c are
     // [table[c], table[c + 1]), so each search starts inside one cell.
@@ -2397,7 +2413,7 @@ __global__ void __launch_bounds__(256) tree_lists_kernel(TreeIndex ix,
                     }
                     const int sl = tree_shift(l);
                     const u64 past = ((ix.key[B] >> sl) + 1) << sl;
-                    B = ix.lower_in(B + 1, E, past);
+                    B = ix.gallop(B + 1, E, past);
                 }
             }
         }
