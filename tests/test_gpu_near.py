@@ -214,10 +214,11 @@ def test_near_grid_few_large_cells(nb):
     assert_accel_parity(acc, pot, ref, idx=idx, what="few large cells")
 
 
-def test_near_grid_huge_cells_sixteen_workgroups(nb):
-    """Eight cells of ~7500 bodies (2 x 2 x 2: the near field is the whole direct sum): 30
-    target chunks per cell over 16 workgroups per cell, so some take two chunks and some one;
-    sampled targets (both ends of every cell range included) against the direct sum."""
+def test_near_grid_huge_cells(nb):
+    """Eight cells of ~7500 bodies (2 x 2 x 2: the near field is the whole direct sum): ~118
+    64-target chunks per cell over 122 workgroups per cell, so the larger cells' chunks fill
+    them all and the others leave some workgroups without a chunk; sampled targets (both ends
+    of the body range included) against the direct sum."""
     import oracle
 
     n = 60000
@@ -227,6 +228,23 @@ def test_near_grid_huge_cells_sixteen_workgroups(nb):
     idx = np.unique(np.concatenate([rng.integers(0, n, 800), [0, n - 1]]))
     ref = oracle.accel(pos, np.float32(1e-4), targets=idx)
     assert_accel_parity(acc, pot, ref, idx=idx, what="2x2x2 grid of 7500-body cells")
+    assert np.all(np.isfinite(acc)) and np.all(np.isfinite(pot))  # every body written
+
+
+def test_near_grid_one_cell_workgroup_cap(nb):
+    """All 70,000 bodies in one cell (a 1 x 1 x 1 grid: the near field is the direct sum):
+    1095 target chunks (1093 of 64 targets, then 32 and 16) over the most workgroups a cell
+    gets (1024, below the 1107 its size asks for), so 71 of them take two chunks; sampled
+    targets, both ends included, against the direct sum."""
+    import oracle
+
+    n = 70000
+    pos, _ = workloads.random_bodies(n, seed=71)
+    acc, pot = gpu_near_grid(nb, pos, 1e-4, (-1.0, -1.0, -1.0), 2.0, (1, 1, 1))
+    rng = np.random.default_rng(9)
+    idx = np.unique(np.concatenate([rng.integers(0, n, 600), [0, 63, 64, n - 1]]))
+    ref = oracle.accel(pos, np.float32(1e-4), targets=idx)
+    assert_accel_parity(acc, pot, ref, idx=idx, what="one cell of 70000 bodies")
     assert np.all(np.isfinite(acc)) and np.all(np.isfinite(pot))  # every body written
 
 
