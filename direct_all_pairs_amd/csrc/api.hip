@@ -1130,25 +1130,31 @@ int nbody_near_tree(const nbody_f4 *pos, int64_t N, float eps2, int64_t leaf_siz
         return fail(NBODY_EINVAL, "near-tree: %d leaves exceed %d (raise leaf_size)", nleaf,
                     nbk::kTreeMaxLeaves);
     // Scratch slot 1, sized by the leaves: coarse table, list part counts, their scan
-    // temp, per-workgroup totals of the count pass.
+    // temp, per-workgroup totals of the count pass, and the parts' first entries kept by
+    // the count pass for the fill pass (up to kTreeKeepMax per part and kTreeKeepBytes in
+    // all; Plummer 65,536, leaf_size 64: the fill pass 62 -> ~10 us).
     const int lt = nbk::tree_table_level(nleaf);
     const long long parts = 27ll * nleaf + 1;
-    const size_t s1[4] = {(((size_t)1 << (3 * lt)) + 1) * 4, (size_t)parts * 4,
-                          nbk::scan_temp_bytes(parts), nbk::tree_parts_bytes(nleaf)};
-    size_t o1[5];
+    const long long keep_fit = (long long)(nbk::kTreeKeepBytes / ((size_t)27 * nleaf * 4));
+    const int keep_cap = keep_fit < nbk::kTreeKeepMax ? (int)keep_fit : nbk::kTreeKeepMax;
+    const size_t s1[5] = {(((size_t)1 << (3 * lt)) + 1) * 4, (size_t)parts * 4,
+                          nbk::scan_temp_bytes(parts), nbk::tree_parts_bytes(nleaf),
+                          (size_t)27 * nleaf * keep_cap * 4};
+    size_t o1[6];
     o1[0] = 0;
-    for (int i = 0; i < 4; ++i) o1[i + 1] = align256(o1[i] + s1[i]);
+    for (int i = 0; i < 5; ++i) o1[i + 1] = align256(o1[i] + s1[i]);
     void *ws1 = nullptr;
-    rc = scratch_get(dev, stream, o1[4], &ws1, 1);
+    rc = scratch_get(dev, stream, o1[5], &ws1, 1);
     if (rc != NBODY_OK) return rc;
     char *b1 = (char *)ws1;
     int *table = (int *)(b1 + o1[0]), *cnt = (int *)(b1 + o1[1]);
     void *scan_temp1 = b1 + o1[2], *wg_totals = b1 + o1[3];
+    int *keep = keep_cap > 0 ? (int *)(b1 + o1[4]) : nullptr;
     const nbk::TreeLeaves lv{leaf_key, leaf_box, table, start, nleaf, lt};
     e = nbk::launch_tree_table(leaf_key, counters, lt, table, stream);
     if (e == hipSuccess)
         e = nbk::launch_tree_lists(lv, counters, wg_totals, cnt, nullptr, nullptr, 0, nullptr,
-                                   stream);
+                                   keep, keep_cap, stream);
     if (e == hipSuccess) e = nbk::scan_exclusive(cnt, parts, counters + 1, scan_temp1, stream);
     if (e != hipSuccess) return hip_fail(e, "near-tree lists");
     // A leaf meets at most 27 leaves no smaller than itself (each holds a different one of
@@ -1184,7 +1190,7 @@ int nbody_near_tree(const nbody_f4 *pos, int64_t N, float eps2, int64_t leaf_siz
     if (rc != NBODY_OK) return rc;
     int *list = (int *)lw;
     e = nbk::launch_tree_lists(lv, counters, nullptr, nullptr, cnt, list, (int)cap, list_off,
-                               stream);
+                               keep, keep_cap, stream);
     if (e == hipSuccess) {
         nbk::P2PArgs a{spos, n, eps2, start, nleaf, list_off, list, cap, (float4 *)acc_out,
                        pot_out, perm};

@@ -221,12 +221,17 @@ struct TreeLeaves {
 // (off = the exclusive sums of cnt): part q of leaf A's list written at
 // list[off[27 A + q] ..] (never at or past list_cap), list_off[A] = off[27 A],
 // list_off[nleaf] = the total. All lists together hold at most kTreeListsPerLeaf entries
-// per leaf (one leaf's list may hold more).
+// per leaf (one leaf's list may hold more). keep (27 nleaf x keep_cap ints, keep_cap >= 0,
+// the same for both passes): the count pass stores each part's first keep_cap entries
+// there, and the fill pass copies a part of at most keep_cap entries instead of walking
+// its cell again.
 constexpr int kTreeListsPerLeaf = 53;
+constexpr int kTreeKeepMax = 32;                        // most entries kept per part
+constexpr size_t kTreeKeepBytes = (size_t)256 << 20;    // most bytes the kept entries take
 size_t tree_parts_bytes(int nleaf);
 hipError_t launch_tree_lists(const TreeLeaves &leaves, int *counters, void *parts, int *cnt,
-                             const int *off, int *list, int list_cap, int *list_off,
-                             hipStream_t stream);
+                             const int *off, int *list, int list_cap, int *list_off, int *keep,
+                             int keep_cap, hipStream_t stream);
 
 // Layout conversion for the SoA entry points: out[i] = (a[i], b[i], c[i], d ? d[i] : 0),
 // and back: a[i], b[i], c[i] = in[i].x, .y, .z.

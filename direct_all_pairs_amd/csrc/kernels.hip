@@ -2334,6 +2334,8 @@ __device__ __forceinline__ bool tree_meet(int ox, int oy, int oz, int l, const i
            oz <= oa[2] + sa && oa[2] <= oz + sb;
 }
 
+// The count pass also keeps each part's first keep_cap entries in keep[t * keep_cap ..];
+// the fill pass copies a part that fits from there and walks again only for longer ones.
 template <bool FILL>
 __global__ void __launch_bounds__(256) tree_lists_kernel(TreeIndex ix,
                                                          const int *__restrict__ cell_start,
@@ -2341,7 +2343,8 @@ __global__ void __launch_bounds__(256) tree_lists_kernel(TreeIndex ix,
                                                          int *__restrict__ cnt,
                                                          const int *__restrict__ off,
                                                          int *__restrict__ list, int list_cap,
-                                                         int *__restrict__ list_off)
+                                                         int *__restrict__ list_off,
+                                                         int *__restrict__ keep, int keep_cap)
 {
     const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
     const int nleaf = ix.nleaf;
@@ -2368,11 +2371,22 @@ __global__ void __launch_bounds__(256) tree_lists_kernel(TreeIndex ix,
                 if (at + w < end) list[at + w] = B;
             } else {
                 terms += cell_start[B + 1] - cell_start[B];
+                if (w < keep_cap) keep[(size_t)t * keep_cap + w] = B;
             }
             ++w;
         };
+        bool kept = false;
+        if (FILL && keep_cap > 0) {
+            const long long c = off[t + 1] - off[t];
+            if (c <= keep_cap) {  // the count pass kept the whole part
+                for (int i = 0; i < (int)c; ++i)
+                    if (at + i < end) list[at + i] = keep[(size_t)t * keep_cap + i];
+                kept = true;
+            }
+        }
         const int cq[3] = {ca[0] + q % 3 - 1, ca[1] + (q / 3) % 3 - 1, ca[2] + q / 9 - 1};
-        if (cq[0] >= 0 && cq[1] >= 0 && cq[2] >= 0 && cq[0] < lim && cq[1] < lim && cq[2] < lim) {
+        if (!kept && cq[0] >= 0 && cq[1] >= 0 && cq[2] >= 0 && cq[0] < lim && cq[1] < lim &&
+            cq[2] < lim) {
             const u64 qk = tree_key(cq[0], cq[1], cq[2], L);
             const u64 qe = qk + (1ull << s);
             int ub, E;
@@ -2894,16 +2908,17 @@ size_t tree_parts_bytes(int nleaf)
 }
 
 hipError_t launch_tree_lists(const TreeLeaves &lv, int *counters, void *parts, int *cnt,
-                             const int *off, int *list, int list_cap, int *list_off,
-                             hipStream_t stream)
+                             const int *off, int *list, int list_cap, int *list_off, int *keep,
+                             int keep_cap, hipStream_t stream)
 {
     if (lv.nleaf <= 0 || lv.nleaf > kTreeMaxLeaves) return hipErrorInvalidValue;
     const bool fill = list != nullptr;
     if (fill ? (!off || !list_off) : (!cnt || !parts || !counters)) return hipErrorInvalidValue;
+    if (keep_cap < 0 || (keep_cap > 0 && !keep)) return hipErrorInvalidValue;
     TreeIndex ix{lv.leaf_key, lv.leaf_box, lv.table, lv.nleaf, lv.lt};
     const int *cs = lv.cell_start;
     longlong2 *pt = (longlong2 *)parts;
-    void *a[] = {&ix, &cs, &pt, &cnt, &off, &list, &list_cap, &list_off};
+    void *a[] = {&ix, &cs, &pt, &cnt, &off, &list, &list_cap, &list_off, &keep, &keep_cap};
     const void *fn = fill ? (const void *)&tree_lists_kernel<true>
                           : (const void *)&tree_lists_kernel<false>;
     const long long threads = 27ll * lv.nleaf + 1;

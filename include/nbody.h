@@ -325,7 +325,8 @@ typedef struct nbody_tree_stats {
  * lists' scratch from it: at most 53 list entries per leaf in total), and returns with the
  * rest enqueued; with stats it also waits for the end of the call. More than
  * 2^31 - 1 list entries (possible only with over 40 million leaves) is EINVAL.
- * Scratch: ~N x 100 bytes + ~300 bytes per leaf.
+ * Scratch: ~N x 100 bytes + ~300 bytes per leaf, plus the lists' first entries kept
+ * between the two list passes (up to 3.5 KB per leaf, at most 256 MiB).
  */
 int nbody_near_tree(const nbody_f4 *pos_xyzm, int64_t N, float eps2, int64_t leaf_size,
                     nbody_f4 *acc_out, float *pot_out, nbody_tree_stats *stats,
