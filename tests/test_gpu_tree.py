@@ -177,6 +177,38 @@ def test_near_tree_big_leaf_beside_fine_leaves(nb):
     assert_accel_parity(acc, pot, oracle.near_tree(pos, 1e-6, 2), what="big leaf beside fine leaves")
 
 
+@pytest.mark.parametrize("bad", ["nan", "inf"])
+def test_near_tree_non_finite_body(nb, bad):
+    """A non-finite coordinate gives unspecified values but a normal call: a NaN coordinate is
+    left out of the bounding cube and binned to the cube's low face on its axis; an infinite
+    one makes the cube infinite, so every body lands in one cell. The call succeeds and
+    writes every row (w = 0); with a NaN body the rows of bodies far from that face stay
+    finite; the next call on finite bodies is unaffected. The same for the grid near field."""
+    import oracle
+
+    pos, _ = workloads.random_bodies(3000, seed=17)
+    bad_pos = pos.copy()
+    bad_pos[5, 0] = np.nan if bad == "nan" else np.inf
+    acc, pot, st = gpu_near_tree(nb, bad_pos, 1e-4, 16)
+    assert st["leaves"] >= 1 and np.all(acc[:, 3] == 0.0)
+    if bad == "nan":
+        far = np.all(bad_pos[:, :3] > 0.0, axis=1)  # the octant away from the corner cell
+        assert far.sum() > 100 and np.all(np.isfinite(acc[far])) and np.all(np.isfinite(pot[far]))
+    acc2, pot2, _ = gpu_near_tree(nb, pos, 1e-4, 16)
+    assert_accel_parity(acc2, pot2, oracle.near_tree(pos, 1e-4, 16), what="after a non-finite call")
+    import torch
+
+    pd = to_dev(bad_pos)
+    acc_g = torch.full((3000, 4), 7.0, device="cuda")
+    pot_g = torch.full((3000,), 7.0, device="cuda")
+    nb.nbody_near_grid(pd, 3000, 1e-4, (-1.0, -1.0, -1.0), 0.25, (8, 8, 8), acc_g, pot_g)
+    torch.cuda.synchronize()
+    ag = acc_g.cpu().numpy()
+    assert np.all(ag[:, 3] == 0.0)
+    if bad == "nan":
+        assert np.all(np.isfinite(ag[far]))
+
+
 def test_near_tree_coincident_bodies(nb):
     """All bodies at one point: one leaf (root cube side 1), the whole direct sum."""
     import oracle
