@@ -109,10 +109,11 @@ hipError_t launch_diagnostics(const float4 *pos, const float4 *vel, const float 
                               double inv_eps, double *part, double *out, hipStream_t stream);
 
 // Near field: target cell c (bodies [cell_start[c], cell_start[c+1])) sums over
-// the bodies of the cells in its interaction list. Two four-wave workgroups per
-// target cell (alternate target chunks; the waves of one share a chunk and split
-// its source tiles), or 256-thread workgroups sharing source tiles (one per
-// 256-target chunk, up to 16 per cell).
+// the bodies of the cells in its interaction list. One to 1024 workgroups per
+// target cell by the mean cell size, each taking every ny-th target chunk (64
+// targets, one per lane, or a smaller rest with source groups); four waves per
+// workgroup from 64 bodies per cell on average, sharing a chunk and splitting its
+// source tiles.
 struct P2PArgs {
     const float4 *pos;      // N bodies grouped by cell
     int n;                  // N
