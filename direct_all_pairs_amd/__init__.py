@@ -36,13 +36,14 @@ class NbodyError(RuntimeError):
 class nbody_plan(ctypes.Structure):
     _fields_ = [("bcast", ctypes.c_int32), ("tpl", ctypes.c_int32),
                 ("splits", ctypes.c_int32), ("chunk", ctypes.c_int32), ("wg", ctypes.c_int32),
-                ("mode", ctypes.c_int32), ("band", ctypes.c_int32), ("passes", ctypes.c_int32)]
+                ("mode", ctypes.c_int32), ("band", ctypes.c_int32), ("passes", ctypes.c_int32),
+                ("run", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {"mode": MODE_NAMES.get(self.mode, self.mode),
                 "bcast": BCAST_NAMES.get(self.bcast, self.bcast), "tpl": self.tpl,
                 "splits": self.splits, "chunk": self.chunk, "wg": self.wg, "band": self.band,
-                "passes": self.passes}
+                "passes": self.passes, "run": self.run}
 
 
 class nbody_tree_stats(ctypes.Structure):
@@ -271,13 +272,14 @@ def nbody_plan_for(N: int, want_pot: bool = False) -> nbody_plan:
     return p
 
 
-def make_plan(bcast=0, tpl=0, splits=0, chunk=0, wg=0, mode=0, band=0, passes=0) -> nbody_plan:
+def make_plan(bcast=0, tpl=0, splits=0, chunk=0, wg=0, mode=0, band=0, passes=0,
+              run=0) -> nbody_plan:
     if isinstance(bcast, str):
         bcast = {v: k for k, v in BCAST_NAMES.items()}[bcast]
     if isinstance(mode, str):
         mode = {v: k for k, v in MODE_NAMES.items()}[mode]
     return nbody_plan(int(bcast), int(tpl), int(splits), int(chunk), int(wg), int(mode), int(band),
-                      int(passes))
+                      int(passes), int(run))
 
 
 # ------------------------------------------------------------ torch conveniences

@@ -248,26 +248,30 @@ constexpr size_t kPairsScratchShare = 16;
 
 int valid_band(int b) { return b == 256 || b == 512 || b == 1024 || b == 2048 || b == 4096; }
 
-size_t pairs_scratch(int64_t n, int band)
+// Largest run length a plan may ask for (items per pair workgroup).
+constexpr int kMaxRun = 1 << 16;
+
+size_t pairs_scratch(int64_t n, int band, int run)
 {
     const int64_t nb = (n + band - 1) / band;
-    return (size_t)nb * (size_t)n * sizeof(float4);
+    return (size_t)nbk::pair_slots((int)nb, run) * (size_t)n * sizeof(float4);
 }
 
 // Grid limit of the second launch dimension (pair items, split-j chunks).
 constexpr int64_t kMaxGridY = 65535;
 
-// Pair evaluation in `passes` passes over band ranges of at most
-// ceil(nb / passes) bands each: per pass the A sides of the range's own bodies
-// ((nb/2 + 1) slots each), the B sides of every body from the range's bands,
-// and across passes the compensated running totals (two records per body),
-// plus, for a step, the accelerations handed to the Euler kernel.
-size_t pairs_pass_scratch(int64_t n, int band, int64_t passes, bool step)
+// Pair evaluation in `passes` passes over owner-band ranges of at most
+// ceil(nb / passes) bands each: per pass the own slots of the range's bodies
+// (1 + R each), the partner sides of every body from the range's owners (one
+// record per owner and body), and across passes the compensated running totals
+// (two records per body), plus, for a step, the accelerations handed to the
+// Euler kernel.
+size_t pairs_pass_scratch(int64_t n, int band, int run, int64_t passes, bool step)
 {
     const int64_t nb = (n + band - 1) / band;
     const int64_t per = (nb + passes - 1) / passes;
     const int64_t own = per * band < n ? per * band : n;
-    const int64_t recs = (nb / 2 + 1) * own + per * n + 2 * n + (step ? n : 0);
+    const int64_t recs = (1 + nbk::pair_runs((int)nb, run)) * own + per * n + 2 * n + (step ? n : 0);
     return (size_t)recs * sizeof(float4);
 }
 
@@ -314,14 +318,34 @@ int auto_band(int64_t n, int tpl, const DeviceFacts &dev)
 // Passes for a pair evaluation: one while all nb slots per body fit the
 // scratch share of device memory, else the fewest that fit (searched in
 // steps of ~25 %); 0 when even one band per pass does not fit.
-int64_t auto_passes(int64_t n, int band, const DeviceFacts &dev, bool step)
+int64_t auto_passes(int64_t n, int band, int run, const DeviceFacts &dev, bool step)
 {
     const size_t cap = dev.mem_bytes / kPairsScratchShare;
-    if (pairs_scratch(n, band) <= cap) return 1;
+    if (pairs_scratch(n, band, run) <= cap) return 1;
     const int64_t nb = (n + band - 1) / band;
     for (int64_t q = 2; q <= nb; q = q < 8 ? q + 1 : q + q / 4)
-        if (pairs_pass_scratch(n, band, q, step) <= cap) return q;
-    return pairs_pass_scratch(n, band, nb, step) <= cap ? nb : 0;
+        if (pairs_pass_scratch(n, band, run, q, step) <= cap) return q;
+    return pairs_pass_scratch(n, band, run, nb, step) <= cap ? nb : 0;
+}
+
+// Items per pair workgroup (run length K): the longest power of two, up to
+// kMaxAutoRun, that still leaves at least kRunWorkgroupsPerCU workgroups per
+// compute unit. Measured round-robin on MI355X (whole calls): N = 2^20 in
+// 2048-body bands 203.1 ms at K = 1 and 8, 204.9 at 16, 207.9 at 32 (34 and 17
+// workgroups per CU); two Plummer spheres of 300,007 in 1024-body bands 17.24
+// ms at K = 1, 17.34 at 4, 17.57 at 8; 65,536 in 512-body bands 0.839 ms at
+// K = 1, 0.848 at 2. Coarser work per workgroup leaves the last ones unevenly
+// spread over the CUs.
+constexpr int kMaxAutoRun = 32;
+constexpr int64_t kRunWorkgroupsPerCU = 64;
+int auto_run(int64_t n, int band, const DeviceFacts &dev)
+{
+    const int64_t nb = (n + band - 1) / band;
+    int run = 1;
+    while (run < kMaxAutoRun &&
+           nb * (1 + nbk::pair_runs((int)nb, 2 * run)) >= kRunWorkgroupsPerCU * dev.cus)
+        run *= 2;
+    return run;
 }
 
 void auto_plan(int64_t n, const DeviceFacts &dev, nbody_plan *p)
@@ -335,10 +359,12 @@ void auto_plan(int64_t n, const DeviceFacts &dev, nbody_plan *p)
         if (n > kSmallMaxN && p->bcast == NBODY_BCAST_AUTO && p->tpl == 0 && p->splits == 0 &&
             p->wg == 0) {
             const int band = p->band != 0 ? p->band : auto_band(n, 0, dev);
-            const int64_t q = p->passes != 0 ? p->passes : auto_passes(n, band, dev, true);
+            const int run = p->run != 0 ? p->run : auto_run(n, band, dev);
+            const int64_t q = p->passes != 0 ? p->passes : auto_passes(n, band, run, dev, true);
             if (q != 0 && (n + band - 1) / band / 2 + 1 <= kMaxGridY) {
                 p->mode = NBODY_MODE_PAIRS;
                 p->band = band;
+                p->run = run;
                 p->passes = (int32_t)q;
             }
         }
@@ -353,10 +379,11 @@ void auto_plan(int64_t n, const DeviceFacts &dev, nbody_plan *p)
         p->bcast = NBODY_BCAST_LDS;
         if (p->band == 0) p->band = auto_band(n, p->tpl, dev);
         if (p->tpl == 0) p->tpl = (p->band == 256 || (n < 24576 && p->band != 4096)) ? 4 : 8;
+        if (p->run == 0) p->run = auto_run(n, p->band, dev);
         if (p->passes == 0) {
             // explicit pair mode: if nothing fits, the most passes (the scratch
             // allocation then reports what is missing)
-            const int64_t q = auto_passes(n, p->band, dev, true);
+            const int64_t q = auto_passes(n, p->band, p->run, dev, true);
             p->passes = (int32_t)(q != 0 ? q : (n + p->band - 1) / p->band);
         }
         p->wg = 256;
@@ -391,6 +418,7 @@ void finish_plan(int64_t n, nbody_plan *p)
         p->chunk = (int32_t)n;
         p->band = 0;
         p->passes = 0;
+        p->run = 0;
         return;
     }
     if (p->mode == NBODY_MODE_PAIRS) {
@@ -402,6 +430,7 @@ void finish_plan(int64_t n, nbody_plan *p)
     }
     p->band = 0;
     p->passes = 0;
+    p->run = 0;
     const int64_t tile = p->bcast == NBODY_BCAST_LDS ? p->wg : nbk::kFlush;
     int64_t s = p->splits;
     int64_t c = (n + s - 1) / s;
@@ -416,10 +445,14 @@ void finish_plan(int64_t n, nbody_plan *p)
 
 int make_plan(int64_t n, const nbody_plan *user, int *dev_out, nbody_plan *p)
 {
-    *p = user ? *user : nbody_plan{0, 0, 0, 0, 0, 0, 0, 0};
+    *p = user ? *user : nbody_plan{0, 0, 0, 0, 0, 0, 0, 0, 0};
     p->chunk = 0;
     if (p->passes < 0)
         return fail(NBODY_EINVAL, "plan.passes=%d must be >= 0", p->passes);
+    if (p->run < 0 || p->run > kMaxRun)
+        return fail(NBODY_EINVAL, "plan.run=%d must be in [0, %d]", p->run, kMaxRun);
+    if (p->run != 0 && p->mode != NBODY_MODE_AUTO && p->mode != NBODY_MODE_PAIRS)
+        return fail(NBODY_EINVAL, "plan.run is for pair mode (NBODY_MODE_PAIRS or AUTO)");
     if (p->passes != 0 && p->mode != NBODY_MODE_AUTO && p->mode != NBODY_MODE_PAIRS)
         return fail(NBODY_EINVAL, "plan.passes is for pair mode (NBODY_MODE_PAIRS or AUTO)");
     if (p->mode < 0 || p->mode > NBODY_MODE_SMALL)
@@ -452,8 +485,9 @@ int make_plan(int64_t n, const nbody_plan *user, int *dev_out, nbody_plan *p)
         ((p->bcast != 0 && p->bcast != NBODY_BCAST_LDS) ||
          (p->tpl != 0 && p->tpl != 4 && p->tpl != 8) || p->splits != 0 ||
          (p->wg != 0 && p->wg != 256)))
-        return fail(NBODY_EINVAL, "plan.mode=NBODY_MODE_PAIRS takes only plan.band and plan.tpl "
-                                  "4 or 8 (bcast LDS, wg 256 and splits are implied)");
+        return fail(NBODY_EINVAL, "plan.mode=NBODY_MODE_PAIRS takes only plan.band, plan.run, "
+                                  "plan.passes and plan.tpl 4 or 8 (bcast LDS, wg 256 and splits "
+                                  "are implied)");
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -497,26 +531,27 @@ int enqueue_pair_passes(const float4 *pos, int n, float eps2, float4 *acc_out, f
                         float4 *euler_vel, float dt)
 {
     const bool step = euler_pos != nullptr;
-    const int nb = p.splits, band = p.band;
+    const int nb = p.splits, band = p.band, nruns = nbk::pair_runs(nb, p.run);
     const int64_t per = (nb + p.passes - 1) / p.passes;
     const int64_t own_max = per * band < n ? per * band : n;
     void *ws = nullptr;
-    int rc = scratch_get(dev, stream, pairs_pass_scratch(n, band, p.passes, step), &ws);
+    int rc = scratch_get(dev, stream, pairs_pass_scratch(n, band, p.run, p.passes, step), &ws);
     if (rc != NBODY_OK) return rc;
-    float4 *partA = (float4 *)ws;
-    float4 *partB = partA + (size_t)(nb / 2 + 1) * (size_t)own_max;
-    float4 *tot_s = partB + (size_t)per * (size_t)n;
+    float4 *own = (float4 *)ws;
+    float4 *partner = own + (size_t)(1 + nruns) * (size_t)own_max;
+    float4 *tot_s = partner + (size_t)per * (size_t)n;
     float4 *tot_e = tot_s + n;
     float4 *accbuf = step ? tot_e + n : nullptr;
     for (int64_t q = 0; q < p.passes; ++q) {
         const int b0 = pass_band(q, nb, p.passes), b1 = pass_band(q + 1, nb, p.passes);
         const int own0 = b0 * band;
         const int own_end = (int64_t)b1 * band < n ? b1 * band : n;
-        nbk::PairsArgs pa{pos, n, eps2, nb, partA, b0, b1, own_end - own0, own0, partB, 1};
+        nbk::PairsArgs pa{pos, n, eps2, nb, b0, b1, p.run, nruns, own, own_end - own0, own0,
+                          partner, n, 1};
         hipError_t e = timed_launch(
             stream, [&] { return nbk::launch_pairs(band, p.tpl, pot_out != nullptr, pa, stream); });
         if (e != hipSuccess) return hip_fail(e, "accel kernel launch");
-        nbk::PassArgs ca{partA, partB, n, band, nb, b0, b1, own0, own_end - own0, tot_s, tot_e,
+        nbk::PassArgs ca{own, partner, n, band, nb, p.run, b0, b1, own0, own_end - own0, tot_s, tot_e,
                          q == 0, q + 1 == p.passes, step ? accbuf : acc_out,
                          step ? nullptr : pot_out};
         e = nbk::launch_pass_combine(ca, stream);
@@ -549,24 +584,32 @@ int enqueue_eval(const float4 *pos, int n, float eps2, float4 *acc_out, float *p
     if (pairs && p.passes > 1)
         return enqueue_pair_passes(pos, n, eps2, acc_out, pot_out, p, dev, stream, euler_pos,
                                    euler_vel, dt);
+    if (pairs) {
+        void *ws = nullptr;
+        int rc = scratch_get(dev, stream, pairs_scratch(n, p.band, p.run), &ws);
+        if (rc != NBODY_OK) return rc;
+        float4 *part = (float4 *)ws;
+        const int nb = p.splits, nruns = nbk::pair_runs(nb, p.run);
+        nbk::PairsArgs pa{pos, n, eps2, nb, 0, nb, p.run, nruns, part, n, 0,
+                          part + (size_t)(1 + nruns) * (size_t)n, n, 0};
+        hipError_t e = timed_launch(stream, [&] { return nbk::launch_pairs(p.band, p.tpl, pot, pa, stream); });
+        if (e != hipSuccess) return hip_fail(e, "accel kernel launch");
+        nbk::PairsFinishArgs fa{part, n, p.band, nb, p.run, acc_out, pot_out, euler_pos, euler_vel, dt};
+        e = nbk::launch_pairs_finish(fa, stream);
+        return e == hipSuccess ? NBODY_OK : hip_fail(e, "pair finish launch");
+    }
     nbk::AccelArgs a{pos, n, eps2, p.chunk, acc_out, pot_out, nullptr};
-    if (p.splits > 1 || step || pairs) {
+    if (p.splits > 1 || step) {
         void *ws = nullptr;
         const size_t bytes = (size_t)p.splits * (size_t)n * sizeof(float4);
         int rc = scratch_get(dev, stream, bytes, &ws);
         if (rc != NBODY_OK) return rc;
         a.part = (float4 *)ws;
     }
-    hipError_t e;
-    if (pairs) {
-        nbk::PairsArgs pa{pos, n, eps2, p.splits, a.part, 0, p.splits, n, 0, a.part, 0};
-        e = timed_launch(stream, [&] { return nbk::launch_pairs(p.band, p.tpl, pot, pa, stream); });
-    } else {
-        e = timed_launch(stream, [&] {
-            return nbk::launch_accel(p.bcast, p.tpl, p.wg, pot, grid_x(n, p.tpl, p.wg),
-                                     (unsigned)p.splits, a, stream);
-        });
-    }
+    hipError_t e = timed_launch(stream, [&] {
+        return nbk::launch_accel(p.bcast, p.tpl, p.wg, pot, grid_x(n, p.tpl, p.wg),
+                                 (unsigned)p.splits, a, stream);
+    });
     if (e != hipSuccess) return hip_fail(e, "accel kernel launch");
     if (step) {
         e = nbk::launch_euler(a.part, n, p.splits, euler_pos, euler_vel, dt, stream);
@@ -609,9 +652,10 @@ int accel_impl(const nbody_f4 *pos, int64_t N, float eps2, nbody_f4 *acc, float 
 size_t eval_scratch(int64_t n, const nbody_plan &p, bool step)
 {
     if (p.mode == NBODY_MODE_SMALL) return step ? (size_t)n * sizeof(float4) : 0;
-    if (p.mode == NBODY_MODE_PAIRS && p.passes > 1) return pairs_pass_scratch(n, p.band, p.passes, step);
-    if (p.splits > 1 || step || p.mode == NBODY_MODE_PAIRS)
-        return (size_t)p.splits * (size_t)n * sizeof(float4);
+    if (p.mode == NBODY_MODE_PAIRS && p.passes > 1)
+        return pairs_pass_scratch(n, p.band, p.run, p.passes, step);
+    if (p.mode == NBODY_MODE_PAIRS) return pairs_scratch(n, p.band, p.run);
+    if (p.splits > 1 || step) return (size_t)p.splits * (size_t)n * sizeof(float4);
     return 0;
 }
 
@@ -813,7 +857,7 @@ int shard_impl(const nbody_f4 *pos, int64_t N, float eps2, int32_t shard, int32_
         return fail(NBODY_EINVAL, "nshards=%d exceeds the %lld bands of %d bodies (each shard "
                                   "needs at least one band)", (int)nshards,
                     (long long)((N + plan->band - 1) / plan->band), (int)plan->band);
-    nbody_plan want = plan ? *plan : nbody_plan{0, 0, 0, 0, 0, NBODY_MODE_PAIRS, 0, 0};
+    nbody_plan want = plan ? *plan : nbody_plan{0, 0, 0, 0, 0, NBODY_MODE_PAIRS, 0, 0, 0};
     nbody_plan p;
     int dev = 0;
     rc = make_plan(N, &want, &dev, &p);
@@ -823,16 +867,17 @@ int shard_impl(const nbody_f4 *pos, int64_t N, float eps2, int32_t shard, int32_
         return fail(NBODY_EINVAL, "nshards=%d exceeds the %d bands of %d bodies (each shard "
                                   "needs at least one band)", (int)nshards, nb, (int)p.band);
     void *ws = nullptr;
-    rc = scratch_get(dev, stream, pairs_scratch(N, p.band), &ws);  // every slot of every body
+    rc = scratch_get(dev, stream, pairs_scratch(N, p.band, p.run), &ws);  // the one-pass layout
     if (rc != NBODY_OK) return rc;
-    const int n = (int)N;
-    nbk::PairsArgs pa{(const float4 *)pos, n, eps2, nb, (float4 *)ws,
-                      shard_band(shard, nb, nshards), shard_band(shard + 1, nb, nshards), n, 0,
-                      (float4 *)ws, 0};
+    const int n = (int)N, nruns = nbk::pair_runs(nb, p.run);
+    float4 *part = (float4 *)ws;
+    nbk::PairsArgs pa{(const float4 *)pos, n, eps2, nb, shard_band(shard, nb, nshards),
+                      shard_band(shard + 1, nb, nshards), p.run, nruns, part, n, 0,
+                      part + (size_t)(1 + nruns) * (size_t)n, n, 0};
     hipError_t e = timed_launch(
         stream, [&] { return nbk::launch_pairs(p.band, p.tpl, want_pot != 0, pa, stream); });
     if (e != hipSuccess) return hip_fail(e, "accel kernel launch");
-    e = nbk::launch_shard_combine(pa.part, n, p.band, nb, pa.band0, pa.band1,
+    e = nbk::launch_shard_combine(part, n, p.band, nb, p.run, pa.band0, pa.band1,
                                   (float4 *)partial_out, stream);
     if (e != hipSuccess) return hip_fail(e, "shard combine launch");
     return ok();

@@ -34,49 +34,78 @@ struct SmallArgs {
     float dt;           // step
 };
 
+// Pair-symmetric evaluation over nb = ceil(N / band) bands. The unordered band
+// pair {X, X + d mod nb}, d in [1, nb/2], is item (X, d) of its owner band X
+// (for even nb the opposite pair d = nb/2 belongs only to the lower X); item
+// (X, 0) is band X against itself, one-sided. With D = nb/2 and run length K,
+// owner X's items d >= 1 form R = ceil(D / K) runs of K consecutive d, one
+// workgroup each. Sums of a body of band x:
+//   own slots     k = 0 (its diagonal item), k = 1 + r (run r of owner x: its
+//                 band's sums over the run's items), at own[k * own_stride + i - own0];
+//   partner slots the targets' side of item (x - d mod nb, d), d = 1..D, at
+//                 partner[p * partner_stride + i] with p = d - 1, or in a pass
+//                 over an owner range p = owner - band0.
+// The one-pass layout is one array of 1 + R + D slots of N records (own slots
+// first, stride N, own0 0), every existing entry written once.
 struct PairsArgs {
-    const float4 *pos;  // N bodies (x, y, z, m)
-    int n;              // N
-    float eps2;         // softening squared (positive normal float)
-    int nbands;         // nb = ceil(N / band)
-    float4 *part;       // A-side sums: part[slot * stride + i - own0]
-    int band0;          // items (A, d) are evaluated for A in [band0, band1)
-    int band1;          //   (the whole evaluation: 0, nb)
-    // Layout of the sums. Slots (compact = 0): slot d of a body is the A side of
-    // item (body's band, d), slot nb - d the B side of item (band - d, d); part =
-    // partB, stride N, own0 0, every entry written once. A pass over a band
-    // range (compact = 1): the A sides of the range's own bodies in part
-    // (stride = own body count, own0 = first own body), the B side of item
-    // (A, d) in partB[(A - band0) * N + i].
-    long long stride;
+    const float4 *pos;        // N bodies (x, y, z, m)
+    int n;                    // N
+    float eps2;               // softening squared (positive normal float)
+    int nbands;               // nb
+    int band0, band1;         // owner bands evaluated: [band0, band1) (all: 0, nb)
+    int run;                  // K >= 1
+    int nruns;                // R = ceil(D / K) (0 when nb = 1)
+    float4 *own;
+    long long own_stride;
     int own0;
-    float4 *partB;
-    int compact;
+    float4 *partner;
+    long long partner_stride;
+    int partner_by_owner;     // 0: p = d - 1; 1: p = owner - band0
 };
 
-// Pair-symmetric evaluation over bands of `band` bodies (512, 1024 or 2048)
-// with tpl (4 or 8) targets per lane. Writes nb partial slots per body;
-// launch_combine or launch_euler with splits = nb finishes the evaluation.
-// With a band range narrower than [0, nb) only the slots of the items (A, d)
-// with A in the range are written; launch_shard_combine adds exactly those.
+// Runs per owner band: R = ceil(floor(nb / 2) / K).
+__host__ __device__ inline int pair_runs(int nb, int run) { return (nb / 2 + run - 1) / run; }
+
+// Slots per body of the one-pass layout: 1 + R + floor(nb / 2).
+__host__ __device__ inline long long pair_slots(int nb, int run) { return 1 + pair_runs(nb, run) + nb / 2; }
+
+// Pair-symmetric evaluation over bands of `band` bodies (256 to 4096) with tpl
+// (4 or 8) targets per lane, grid (band1 - band0, 1 + R). launch_pairs_finish
+// finishes a one-pass evaluation; with an owner range narrower than [0, nb)
+// only the items of those owners are evaluated, and launch_shard_combine adds
+// exactly their slots.
 hipError_t launch_pairs(int band, int tpl, bool pot, const PairsArgs &args, hipStream_t stream);
 
-// One shard's contribution to every body: the slots written by the items
-// (A, d) with A in [band0, band1), added in ascending slot order like the
-// combine (compensated), out[i] = (ax, ay, az, sum m/r) partial; N records.
-hipError_t launch_shard_combine(const float4 *part, int n, int band, int nbands, int band0,
-                                int band1, float4 *out, hipStream_t stream);
+// One-pass finish: every body's own slots (ascending k), then its partner slots
+// (ascending d), in compensated sums; then acc_out = (ax, ay, az, 0) and pot_out
+// = -sum m/r (if not null), or with pos/vel set one Euler step in place.
+struct PairsFinishArgs {
+    const float4 *part;       // the one-pass slot array
+    int n, band, nbands, run;
+    float4 *acc_out;
+    float *pot_out;
+    float4 *pos, *vel;
+    float dt;
+};
+hipError_t launch_pairs_finish(const PairsFinishArgs &args, hipStream_t stream);
 
-// One pass of a multi-pass pair evaluation (compact layout of PairsArgs, band
-// range [band0, band1), own bodies [own0, own0 + own_count)): every body's sums
-// from this pass are added, in a fixed order, into the compensated running
-// totals (tot_s, tot_e) (started fresh when first). On the last pass the
-// result goes to acc_out/pot_out, or to acc_out alone as (ax, ay, az, sum m/r)
-// records when pot_out is null and raw is set (the Euler step's input).
+// One shard's contribution to every body from a one-pass slot array written by
+// the owners [band0, band1): the slots of their items, in the finish's order
+// (compensated), out[i] = (ax, ay, az, sum m/r) partial; N records.
+hipError_t launch_shard_combine(const float4 *part, int n, int band, int nbands, int run,
+                                int band0, int band1, float4 *out, hipStream_t stream);
+
+// One pass of a multi-pass pair evaluation over owners [band0, band1) (own
+// bodies [own0, own0 + own_count) with 1 + R own slots each in `own`, partner
+// slots partner[(owner - band0) * N + i]): every body's sums from this pass are
+// added, own slots first, then partners by ascending owner, into the
+// compensated running totals (tot_s, tot_e) (started fresh when first). On the
+// last pass the result goes to acc_out/pot_out, or to acc_out alone as (ax, ay,
+// az, sum m/r) records when pot_out is null (the Euler step's input).
 struct PassArgs {
-    const float4 *partA;
-    const float4 *partB;
-    int n, band, nbands, band0, band1, own0, own_count;
+    const float4 *own;
+    const float4 *partner;
+    int n, band, nbands, run, band0, band1, own0, own_count;
     float4 *tot_s, *tot_e;
     int first, last;
     float4 *acc_out;

@@ -721,9 +721,15 @@ __device__ __forceinline__ V &at_byte(void *base, int off)
     return *reinterpret_cast<V *>(static_cast<char *>(base) + off);
 }
 
+// Item {A, B}: band A's targets held in registers (their sums written to
+// outA[body - offA] after each i-set), band B walked in j-blocks. With SYM the
+// B side is added into the LDS accumulator jacc (kept across the items of a
+// run; the caller zeroes and stores it), or with a global accumulator into
+// outB[body - offB], which the first item of a run starts afresh.
 template <int T, int BD, bool POT, bool SYM>
-__device__ __forceinline__ void pairs_item(const PairsArgs &k, int A, int B, int slot_i,
-                                           int slot_j, float eps2, PairsShared<T, BD> &sh)
+__device__ __forceinline__ void pairs_item(const PairsArgs &k, int A, int B, float4 *outA,
+                                           long long offA, float4 *outB, long long offB,
+                                           bool first_of_run, float eps2, PairsShared<T, BD> &sh)
 {
     constexpr int W = 4;
     constexpr int NIS = BD / (64 * T);  // i-sets per band
@@ -812,8 +818,8 @@ __device__ __forceinline__ void pairs_item(const PairsArgs &k, int A, int B, int
                 const float4 g = sh.jsum[w][lane];
                 const long long body = (long long)B * BD + jb * 64 + lane;
                 if (body < k.n) {
-                    float4 *dst = k.partB + (size_t)slot_j * (size_t)k.n + body;
-                    float4 o = is == 0 ? make_float4(0.0f, 0.0f, 0.0f, 0.0f) : *dst;
+                    float4 *dst = outB + (body - offB);
+                    float4 o = (is == 0 && first_of_run) ? make_float4(0.0f, 0.0f, 0.0f, 0.0f) : *dst;
                     o.x -= g.x;
                     o.y -= g.y;
                     o.z -= g.z;
@@ -853,7 +859,7 @@ __device__ __forceinline__ void pairs_item(const PairsArgs &k, int A, int B, int
                     s = make_float4(s.x + v.x, s.y + v.y, s.z + v.z, s.w + v.w);
                 }
                 const long long body = (long long)A * BD + is * 64 * T + idx;
-                if (body < k.n) k.part[(size_t)slot_i * (size_t)k.stride + (body - k.own0)] = s;
+                if (body < k.n) outA[body - offA] = s;
             }
             __syncthreads();
             if constexpr (kRaceProbe) {
@@ -879,8 +885,7 @@ __device__ __forceinline__ void pairs_item(const PairsArgs &k, int A, int B, int
                         red[idx] = v;
                     } else {
                         const long long body = (long long)A * BD + is * 64 * T + idx;
-                        if (body < k.n)
-                            k.part[(size_t)slot_i * (size_t)k.stride + (body - k.own0)] = v;
+                        if (body < k.n) outA[body - offA] = v;
                     }
                 }
             }
@@ -889,36 +894,59 @@ __device__ __forceinline__ void pairs_item(const PairsArgs &k, int A, int B, int
         probe_poison(sh.jblk[w][lane]);
         probe_poison(sh.jsum[w][lane]);
     }
-    if constexpr (SYM && !kGlobalJacc<BD>) {
-        for (int i = threadIdx.x; i < BD; i += 64 * W) {
-            const long long body = (long long)B * BD + i;
-            if (body < k.n) k.partB[(size_t)slot_j * (size_t)k.n + body] = sh.jacc[i];
-        }
-    }
 }
 
-// grid (band1 - band0, nb/2 + 1), 256 threads. Workgroups whose (A, d) is not
-// an owned item return at once (uniformly, before any barrier).
+// Whether item (x, d) exists: the diagonal, d below nb/2, and for even nb the
+// opposite pair d = nb/2 from the lower half only.
+__device__ __forceinline__ bool item_exists(int x, int d, int nb)
+{
+    if (d == 0) return true;
+    if (nb == 1 || 2 * d > nb) return false;
+    return 2 * d < nb || x < nb / 2;
+}
+
+// grid (band1 - band0, 1 + R), 256 threads. Row 0: the diagonal item of
+// owner X = band0 + blockIdx.x. Row 1 + r: run r of X, the items (X, d) for d
+// in [1 + r K, min((r + 1) K, nb/2)] in ascending d; band X is the walked band
+// of each, so its sums stay in the LDS accumulator for the whole run and are
+// stored once, into own slot 1 + r, and each partner band Y = X + d holds its
+// targets in registers and writes them to partner slot d. A run whose first
+// item does not exist (only d = nb/2 for X >= nb/2, even nb) returns at once,
+// uniformly, before any barrier.
 template <int T, int BD, bool POT>
 __global__ void __launch_bounds__(256) accel_pairs(PairsArgs k)
 {
     __shared__ PairsShared<T, BD> sh;
     const int nb = k.nbands;
-    const int A = k.band0 + (int)blockIdx.x;
-    const int d = blockIdx.y;
-    if (d > nb / 2) return;
-    if (nb % 2 == 0 && d == nb / 2 && A >= nb / 2) return;
-    if (d > 0 && nb == 1) return;
-    const int B = (A + d) % nb;
+    const int X = k.band0 + (int)blockIdx.x;
     const float eps2 = in_vgpr(k.eps2);
-    if (d == 0) {
-        pairs_item<T, BD, POT, false>(k, A, A, 0, 0, eps2, sh);
-    } else {
-        if constexpr (!kGlobalJacc<BD>) {
-            for (int i = threadIdx.x; i < BD; i += 256) sh.jacc[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            __syncthreads();
+    if (blockIdx.y == 0) {
+        pairs_item<T, BD, POT, false>(k, X, X, k.own, k.own0, nullptr, 0, true, eps2, sh);
+        return;
+    }
+    const int r = (int)blockIdx.y - 1;
+    const int d0 = 1 + r * k.run;
+    const int d1 = min(nb / 2, d0 + k.run - 1);
+    if (!item_exists(X, d0, nb)) return;
+    float4 *runslot = k.own + (size_t)(1 + r) * (size_t)k.own_stride;
+    if constexpr (!kGlobalJacc<BD>) {
+        for (int i = threadIdx.x; i < BD; i += 256) sh.jacc[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        __syncthreads();
+    }
+    for (int d = d0; d <= d1; ++d) {
+        if (!item_exists(X, d, nb)) break;  // only d = nb/2 can be missing: the run's last
+        const int Y = X + d < nb ? X + d : X + d - nb;
+        const int p = k.partner_by_owner ? X - k.band0 : d - 1;
+        float4 *tgt = k.partner + (size_t)p * (size_t)k.partner_stride;
+        pairs_item<T, BD, POT, true>(k, Y, X, tgt, 0, runslot, k.own0, d == d0, eps2, sh);
+    }
+    if constexpr (!kGlobalJacc<BD>) {
+        // entry i was accumulated by this same thread (block i / 64 belongs to
+        // wave (i / 64) mod 4), so no barrier is needed before the store
+        for (int i = threadIdx.x; i < BD; i += 256) {
+            const long long body = (long long)X * BD + i;
+            if (body < k.n) runslot[body - k.own0] = sh.jacc[i];
         }
-        pairs_item<T, BD, POT, true>(k, A, B, d, k.compact ? A - k.band0 : nb - d, eps2, sh);
     }
 }
 
@@ -949,40 +977,102 @@ __global__ void __launch_bounds__(256) euler_kernel(const float4 *__restrict__ p
     vel[i] = v;
 }
 
-// ---------------------------------------------------------------- shards
-// A shard owns the work items (A, d) of the bands A in [band0, band1). The
-// slot k of a body of band x was written by the item of band owner(x, k):
-// slot 0 and slots k < nb/2 by the body's own band (diagonal and A sides),
-// slots k > nb/2 by the B side of item ((x + k) mod nb, nb - k), and for even
-// nb slot nb/2 by the lower band of the opposite pair.
-__device__ __forceinline__ int slot_owner(int x, int k, int nb)
+// ---------------------------------------------------------------- pair finish
+// Adds base[s * stride], s = 0 .. count-1, in order into the compensated sum
+// (a, e); a body's first addend starts the sum (as in sum_parts). Loads run
+// eight slots ahead of the in-order additions.
+__device__ __forceinline__ void add_slots(float4 &a, float4 &e, bool &started,
+                                          const float4 *base, size_t stride, int count)
 {
-    if (2 * k < nb) return x;
-    if (2 * k == nb) return x < nb / 2 ? x : x - nb / 2;
-    const int o = x + k;
-    return o >= nb ? o - nb : o;
+    int s = 0;
+    if (!started && count > 0) {
+        a = base[0];
+        started = true;
+        s = 1;
+    }
+    for (; s + 8 <= count; s += 8) {
+        float4 b[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) b[u] = base[(size_t)(s + u) * stride];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) two_sum_add4(a, e, b[u]);
+    }
+    for (; s < count; ++s) two_sum_add4(a, e, base[(size_t)s * stride]);
 }
 
+__device__ __forceinline__ void add_one(float4 &a, float4 &e, bool &started, const float4 &v)
+{
+    if (started) {
+        two_sum_add4(a, e, v);
+    } else {
+        a = v;
+        started = true;
+    }
+}
+
+// Own slots that band x's bodies hold: the diagonal and every run whose first
+// item exists (only the last run, when it is d = nb/2 alone for x >= nb/2,
+// can be empty).
+__device__ __forceinline__ int own_slots(int x, int nb, int run, int nruns)
+{
+    return 1 + nruns - ((nruns > 0 && !item_exists(x, 1 + (nruns - 1) * run, nb)) ? 1 : 0);
+}
+
+// Partner slots d = 1 .. that band x's bodies hold: all D = nb/2 except, for
+// even nb, d = nb/2 when its owner x - nb/2 (mod nb) is in the upper half.
+__device__ __forceinline__ int partner_slots(int x, int nb)
+{
+    const int D = nb / 2;
+    if (D == 0) return 0;
+    const int o = x >= D ? x - D : x - D + nb;
+    return item_exists(o, D, nb) ? D : D - 1;
+}
+
+__global__ void __launch_bounds__(256) pairs_finish_kernel(PairsFinishArgs k)
+{
+    const unsigned i = blockIdx.x * 256u + threadIdx.x;
+    if (i >= (unsigned)k.n) return;
+    const int x = (int)(i / (unsigned)k.band), nb = k.nbands;
+    const int nruns = pair_runs(nb, k.run);
+    const size_t n = (size_t)k.n;
+    float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f), e = a;
+    bool started = false;
+    add_slots(a, e, started, k.part + i, n, own_slots(x, nb, k.run, nruns));
+    add_slots(a, e, started, k.part + (size_t)(1 + nruns) * n + i, n, partner_slots(x, nb));
+    const float4 r = make_float4(a.x + e.x, a.y + e.y, a.z + e.z, a.w + e.w);
+    if (k.pos) {
+        float4 xp = k.pos[i];
+        float4 v = k.vel[i];
+        euler_update(xp, v, r, k.dt);
+        k.pos[i] = xp;
+        k.vel[i] = v;
+        return;
+    }
+    k.acc_out[i] = make_float4(r.x, r.y, r.z, 0.0f);
+    if (k.pot_out) k.pot_out[i] = -r.w;
+}
+
+// ---------------------------------------------------------------- shards
+// A shard owns the items of the owner bands [band0, band1): the own slots of
+// its bands' bodies and the partner slot d of a body of band x when x - d
+// (mod nb) is one of them. Added in the finish's order, so one shard of one is
+// the one-pass finish bit for bit.
 __global__ void __launch_bounds__(256) shard_combine_kernel(const float4 *__restrict__ part, int n,
-                                                            int band, int nb, int band0,
+                                                            int band, int nb, int run, int band0,
                                                             int band1, float4 *__restrict__ out)
 {
     const unsigned i = blockIdx.x * 256u + threadIdx.x;
     if (i >= (unsigned)n) return;
     const int x = (int)(i / (unsigned)band);
-    float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    float4 e = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    bool first = true;
-    for (int k = 0; k < nb; ++k) {
-        const int o = slot_owner(x, k, nb);
-        if (o < band0 || o >= band1) continue;
-        const float4 v = part[(size_t)k * (size_t)n + i];
-        if (first) {
-            a = v;  // as in sum_parts: the first slot starts the sum
-            first = false;
-        } else {
-            two_sum_add4(a, e, v);
-        }
+    const int nruns = pair_runs(nb, run);
+    float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f), e = a;
+    bool started = false;
+    if (x >= band0 && x < band1) add_slots(a, e, started, part + i, (size_t)n, own_slots(x, nb, run, nruns));
+    const int np = partner_slots(x, nb);
+    const float4 *pb = part + (size_t)(1 + nruns) * (size_t)n + i;
+    for (int d = 1; d <= np; ++d) {
+        const int o = x >= d ? x - d : x - d + nb;
+        if (o >= band0 && o < band1) add_one(a, e, started, pb[(size_t)(d - 1) * (size_t)n]);
     }
     out[i] = make_float4(a.x + e.x, a.y + e.y, a.z + e.z, a.w + e.w);
 }
@@ -1000,46 +1090,27 @@ __global__ void __launch_bounds__(256) shard_finish_kernel(const float4 *__restr
 }
 
 // ---------------------------------------------------------------- passes
-// Whether item (a, d) exists: the diagonal, d below nb/2, and for even nb the
-// opposite pair d = nb/2 from the lower half only.
-__device__ __forceinline__ bool item_exists(int a, int d, int nb)
-{
-    if (d == 0) return true;
-    if (nb == 1 || 2 * d > nb) return false;
-    return 2 * d < nb || a < nb / 2;
-}
-
 __global__ void __launch_bounds__(256) pass_combine_kernel(PassArgs k)
 {
     const unsigned i = blockIdx.x * 256u + threadIdx.x;
     if (i >= (unsigned)k.n) return;
     const int x = (int)(i / (unsigned)k.band), nb = k.nbands;
-    float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    float4 e = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f), e = a;
     bool started = !k.first;
     if (started) {
         a = k.tot_s[i];
         e = k.tot_e[i];
     }
-    auto add = [&](const float4 &v) {
-        if (started) {
-            two_sum_add4(a, e, v);
-        } else {
-            a = v;  // as in sum_parts: the first sum starts the total
-            started = true;
-        }
-    };
-    // this body's A sides (its own band in the range), ascending d
-    if (x >= k.band0 && x < k.band1) {
-        const size_t off = (size_t)((int)i - k.own0);
-        for (int d = 0; d <= nb / 2; ++d)
-            if (item_exists(x, d, nb)) add(k.partA[(size_t)d * (size_t)k.own_count + off]);
-    }
-    // its B sides from the range's bands, ascending band
-    for (int A = k.band0; A < k.band1; ++A) {
-        int d = x - A;
+    // this body's own slots (its band is one of the pass's owners)
+    if (x >= k.band0 && x < k.band1)
+        add_slots(a, e, started, k.own + ((int)i - k.own0), (size_t)k.own_count,
+                  own_slots(x, nb, k.run, pair_runs(nb, k.run)));
+    // its partner sides from the pass's owners, ascending owner
+    for (int o = k.band0; o < k.band1; ++o) {
+        int d = x - o;
         if (d < 0) d += nb;
-        if (d >= 1 && item_exists(A, d, nb)) add(k.partB[(size_t)(A - k.band0) * (size_t)k.n + i]);
+        if (d >= 1 && item_exists(o, d, nb))
+            add_one(a, e, started, k.partner[(size_t)(o - k.band0) * (size_t)k.n + i]);
     }
     if (!k.last) {
         k.tot_s[i] = a;
@@ -2585,13 +2656,29 @@ hipError_t launch_pairs(int band, int tpl, bool pot, const PairsArgs &args, hipS
         if (band == 2048) fn = pairs_fn<8, 2048>(pot);
         if (band == 4096) fn = pairs_fn<8, 4096>(pot);
     }
-    if (!fn || args.nbands < 1 || args.band0 < 0 || args.band1 > args.nbands ||
-        args.band0 >= args.band1)
+    const PairsArgs &a = args;
+    if (!fn || a.n < 1 || a.nbands != (a.n + band - 1) / band || a.band0 < 0 ||
+        a.band1 > a.nbands || a.band0 >= a.band1 || a.run < 1 ||
+        a.nruns != pair_runs(a.nbands, a.run) || !a.own || !a.partner || a.own0 < 0 ||
+        1 + a.nruns > 65535)
         return hipErrorInvalidValue;
-    PairsArgs a = args;
-    void *kargs[] = {&a};
-    return hipLaunchKernel(fn, dim3((unsigned)(a.band1 - a.band0), (unsigned)(a.nbands / 2 + 1), 1),
+    PairsArgs c = a;
+    void *kargs[] = {&c};
+    return hipLaunchKernel(fn, dim3((unsigned)(a.band1 - a.band0), (unsigned)(1 + a.nruns), 1),
                            dim3(256, 1, 1), kargs, 0, stream);
+}
+
+hipError_t launch_pairs_finish(const PairsFinishArgs &args, hipStream_t stream)
+{
+    const PairsFinishArgs &a = args;
+    if (a.n < 1 || a.band < 1 || a.nbands != (a.n + a.band - 1) / a.band || a.run < 1 ||
+        !a.part || (a.pos == nullptr) != (a.vel == nullptr) || (!a.pos && !a.acc_out))
+        return hipErrorInvalidValue;
+    PairsFinishArgs c = a;
+    void *kargs[] = {&c};
+    const unsigned g = (unsigned)((a.n + 255) / 256);
+    return hipLaunchKernel((const void *)&pairs_finish_kernel, dim3(g), dim3(256), kargs, 0,
+                           stream);
 }
 
 hipError_t launch_pass_combine(const PassArgs &args, hipStream_t stream)
@@ -2599,7 +2686,8 @@ hipError_t launch_pass_combine(const PassArgs &args, hipStream_t stream)
     const PassArgs &a = args;
     if (a.n < 1 || a.band < 1 || a.nbands != (a.n + a.band - 1) / a.band || a.band0 < 0 ||
         a.band1 > a.nbands || a.band0 >= a.band1 || a.own0 != a.band0 * a.band ||
-        a.own_count < 1 || a.own0 + a.own_count > a.n || !a.acc_out ||
+        a.own_count < 1 || a.own0 + a.own_count > a.n || !a.acc_out || a.run < 1 ||
+        !a.own || !a.partner ||
         (!(a.first && a.last) && (!a.tot_s || !a.tot_e)))
         return hipErrorInvalidValue;
     PassArgs p = a;
@@ -2608,13 +2696,13 @@ hipError_t launch_pass_combine(const PassArgs &args, hipStream_t stream)
     return hipLaunchKernel((const void *)&pass_combine_kernel, dim3(g), dim3(256), kargs, 0, stream);
 }
 
-hipError_t launch_shard_combine(const float4 *part, int n, int band, int nbands, int band0,
-                                int band1, float4 *out, hipStream_t stream)
+hipError_t launch_shard_combine(const float4 *part, int n, int band, int nbands, int run,
+                                int band0, int band1, float4 *out, hipStream_t stream)
 {
     if (n < 1 || band < 1 || nbands != (n + band - 1) / band || band0 < 0 || band1 > nbands ||
-        band0 >= band1)
+        band0 >= band1 || run < 1 || !part || !out)
         return hipErrorInvalidValue;
-    void *kargs[] = {&part, &n, &band, &nbands, &band0, &band1, &out};
+    void *kargs[] = {&part, &n, &band, &nbands, &run, &band0, &band1, &out};
     const unsigned g = (unsigned)((n + 255) / 256);
     return hipLaunchKernel((const void *)&shard_combine_kernel, dim3(g), dim3(256), kargs, 0,
                            stream);

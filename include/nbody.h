@@ -98,15 +98,17 @@ enum {
  *   mode   - NBODY_MODE_*. The fields above describe NBODY_MODE_TILES. With
  *            NBODY_MODE_PAIRS only `band` (256, 512, 1024, 2048 or 4096 bodies),
  *            `tpl` (4 or 8 targets per lane, 4 only with 256-body bands, 8 only
- *            with 4096-body bands) and `passes` may be set (0 = automatic); the
- *            output then has splits = number of bands = partial-sum slots per
- *            body, chunk = band, bcast = LDS, wg = 256. In one pass the scratch
- *            is splits x N x 16 bytes (8.6 GB at N = 2^20 with 2048-body bands,
- *            4.3 GB with 4096-body bands, which take 0.3-1.3 % longer there);
- *            when that would exceed 1/16 of device memory the automatic plan
- *            evaluates the band-pair items in several passes over band ranges,
- *            each pass's sums added into running totals, with scratch of about
- *            (1.5 x splits / passes + 2) x N x 16 bytes.
+ *            with 4096-body bands), `run` and `passes` may be set (0 =
+ *            automatic); the output then has splits = nb = number of bands,
+ *            chunk = band, bcast = LDS, wg = 256. Each workgroup evaluates `run`
+ *            band pairs that share one band, whose sums it keeps on chip across
+ *            them, so a body receives 1 + R + floor(nb / 2) partial sums with
+ *            R = ceil(floor(nb / 2) / run). In one pass the scratch is that
+ *            many records of N x 16 bytes (4.85 GB at N = 2^20 with 2048-body
+ *            bands and run 8); when that would exceed 1/16 of device memory the
+ *            automatic plan evaluates the band pairs in several passes over
+ *            band ranges, each pass's sums added into running totals, with
+ *            scratch of about (splits / passes + 3) x N x 16 bytes.
  *            With NBODY_MODE_SMALL only `tpl` may be set: targets per workgroup,
  *            4, 8, 16 or 32 (0 = automatic); the output has splits = 1, chunk =
  *            N, bcast = LDS, wg = 256. It needs no scratch for an evaluation and
@@ -115,6 +117,10 @@ enum {
  *   passes - pair mode: passes over band ranges, 1 .. splits (0 = automatic:
  *            one while the full slot scratch fits, else the fewest that fit).
  *            Results with different pass counts differ in the last bits.
+ *   run    - pair mode: band pairs per workgroup, 1 .. 65536 (0 = automatic:
+ *            the longest power of two up to 32 that leaves at least 64
+ *            workgroups per compute unit). Results with different run lengths
+ *            differ in the last bits.
  * The plan is a pure function of (N, device compute units and memory), so
  * nbody_accel and nbody_step use the same one for the same N, with or without
  * the potential. */
@@ -127,6 +133,7 @@ typedef struct nbody_plan {
     int32_t mode;
     int32_t band;
     int32_t passes;
+    int32_t run;
 } nbody_plan;
 
 /*

@@ -286,6 +286,8 @@ def test_plan_rejects_bad_fields(nb):
                  dict(mode=2, band=256, tpl=8), dict(mode=2, band=128), dict(mode=2, passes=-1),
                  dict(mode=2, band=4096, tpl=4), dict(mode=2, band=8192),
                  dict(mode=1, passes=2), dict(mode=3, passes=2),
+                 dict(mode=2, run=-1), dict(mode=2, run=(1 << 16) + 1), dict(mode=1, run=2),
+                 dict(mode=3, run=2), dict(run=-3),
                  dict(mode=2, bcast="scalar"), dict(wg=512, bcast="scalar"), dict(wg=96),
                  dict(wg=64, bcast="readlane")):
         rc = nb.nbody_accel_plan(A, 16, 1e-4, B, None, plan=plan, stream=0, check=False)

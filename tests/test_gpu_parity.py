@@ -265,6 +265,78 @@ def test_pairs_invariants(nb, band, tpl):
     assert np.array_equal(b1, b2) and np.array_equal(q1, q2)
 
 
+# ------------------------------------------------------------------ pair runs
+# (n, band, tpl, run): band counts nb and run lengths K chosen so that runs are whole, ragged
+# (a shorter last run), or hold only the opposite band d = nb/2 of an even count (then empty for
+# the upper half of the owners); 4096-body bands keep the walked band's sums in the global slot
+# across a run.
+RUN_CASES = [(4096, 512, 8, 1), (4096, 512, 8, 3), (4096, 512, 8, 4), (5000, 1024, 4, 2),
+             (4615, 512, 8, 5), (4615, 512, 4, 2), (6144, 256, 4, 7), (6144, 256, 4, 11),
+             (20000, 1024, 8, 64), (8192, 4096, 8, 2), (12290, 4096, 8, 1), (20000, 4096, 8, 3),
+             (3000, 2048, 8, 1), (2047, 256, 4, 1)]
+
+
+@pytest.mark.parametrize("n,band,tpl,run", RUN_CASES)
+def test_pair_runs(nb, n, band, tpl, run):
+    """Runs of K band pairs per workgroup against the full oracle; repeated runs are identical and
+    the acceleration bits do not depend on the potential."""
+    eps2 = np.float32(1e-4)
+    pos, _ = _bodies(n, 500 + run)
+    plan = dict(mode="pairs", band=band, tpl=tpl, run=run)
+    acc, pot = gpu_accel(pos, eps2, pot=True, plan=plan)
+    assert_accel_parity(acc, pot, _ref(n, 500 + run, eps2), what=f"N={n} {plan}")
+    a0, _ = gpu_accel(pos, eps2, pot=False, plan=plan)
+    a1, p1 = gpu_accel(pos, eps2, pot=True, plan=plan)
+    assert np.array_equal(a0, acc) and np.array_equal(a1, acc) and np.array_equal(p1, pot)
+
+
+@pytest.mark.parametrize("n,band,tpl,run,passes", [(3000, 512, 8, 2, 2), (4615, 512, 8, 3, 4),
+                                                     (9000, 4096, 8, 1, 2), (6144, 256, 4, 5, 7)])
+def test_pair_runs_in_passes_and_steps(nb, n, band, tpl, run, passes):
+    """Runs inside passes over owner ranges, against the full oracle; Euler steps with runs in
+    one pass and in passes: three steps equal three single steps bit for bit."""
+    import oracle
+
+    eps2 = np.float32(1e-4)
+    pos, vel = _bodies(n, 600 + run)
+    plan = dict(mode="pairs", band=band, tpl=tpl, run=run, passes=passes)
+    acc, pot = gpu_accel(pos, eps2, pot=True, plan=plan)
+    assert_accel_parity(acc, pot, _ref(n, 600 + run, eps2), what=f"N={n} {plan}")
+    for q in (1, passes):
+        sp = dict(plan, passes=q)
+        x1, v1 = gpu_step(pos, vel, 1e-3, eps2, 1, plan=sp)
+        assert_step_parity(pos, vel, x1, v1, 1e-3, oracle.accel(pos, eps2), what=f"step {sp}")
+        xs, vs = x1, v1
+        for _ in range(2):
+            xs, vs = gpu_step(xs, vs, 1e-3, eps2, 1, plan=sp)
+        xk, vk = gpu_step(pos, vel, 1e-3, eps2, 3, plan=sp)
+        assert np.array_equal(xk, xs) and np.array_equal(vk, vs), sp
+
+
+def test_auto_run_lengths(nb):
+    """The automatic run length: the longest power of two up to 32 that leaves 64 workgroups
+    per compute unit (the MI355X has 256): one pair per workgroup while items are few, 8 at
+    N = 2^20 (289 slots of 16 bytes per body: 4.85 GB), 32 at 2^21 (529 slots, one pass)."""
+    import torch
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for n in (8192, 65536, 300007, 1 << 20, 1 << 21, (1 << 22) + 12345):
+        p = nb.nbody_plan_for(n)
+        nbands = p.splits
+        wgs = lambda k: nbands * (1 + (nbands // 2 + k - 1) // k)  # noqa: E731
+        want = 1
+        while want < 32 and wgs(2 * want) >= 64 * cus:
+            want *= 2
+        assert p.run == want, (n, p.as_dict())
+    if cus == 256:
+        assert nb.nbody_plan_for(65536).run == 1 and nb.nbody_plan_for(300007).run == 2
+        p = nb.nbody_plan_for(1 << 20)
+        assert p.run == 8 and p.passes == 1 and p.band == 2048, p.as_dict()
+        assert 1 + (256 + p.run - 1) // p.run + 256 == 289
+        p = nb.nbody_plan_for(1 << 21)
+        assert p.run == 32 and p.passes == 1, p.as_dict()
+
+
 # ------------------------------------------------------------------ pair passes (bounded scratch)
 
 PASS_CASES = [(1000, 256, 4, 2), (1000, 256, 4, 4), (3000, 512, 8, 2), (3000, 512, 8, 6),
@@ -314,18 +386,18 @@ def test_pair_passes_mid_n_and_steps(nb):
     assert np.array_equal(xk, xs) and np.array_equal(vk, vs)
 
 
-@pytest.mark.parametrize("band", [0, 4096])
-def test_pair_passes_two_million_sampled(nb, band):
-    """N = 2^21 uniform cube: the automatic plan (2048-body bands, 34 GB of slots in one pass,
-    beyond the scratch share) takes several passes; 4096-body bands take one (16 GiB); sampled
-    targets against the oracle."""
+@pytest.mark.parametrize("band,passes", [(0, 0), (2048, 3), (4096, 0)])
+def test_pair_passes_two_million_sampled(nb, band, passes):
+    """N = 2^21 uniform cube: the automatic plan (2048-body bands in runs of 32, 529 slots per
+    body, 17.7 GB, within the scratch share) takes one pass; the same bands in three passes, and
+    4096-body bands in one; sampled targets against the oracle."""
     import oracle
 
     n = 1 << 21
-    plan = None if band == 0 else dict(mode="pairs", band=band, tpl=8)
+    plan = None if band == 0 else dict(mode="pairs", band=band, tpl=8, passes=passes)
     if band == 0:
         p = nb.nbody_plan_for(n)
-        assert p.mode == nb.MODE_PAIRS and p.band == 2048 and p.passes > 1, p.as_dict()
+        assert p.mode == nb.MODE_PAIRS and p.band == 2048 and p.run == 32, p.as_dict()
         band = p.band
     w = workloads.make("cube1m", n=n)
     acc, pot = gpu_accel(w.pos, w.eps2, plan=plan)

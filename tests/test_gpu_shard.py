@@ -20,12 +20,12 @@ def nb():
     return direct_all_pairs_amd
 
 
-def run_shard(nb, pd, n, eps2, s, S, band, tpl=0, want_pot=True):
+def run_shard(nb, pd, n, eps2, s, S, band, tpl=0, want_pot=True, run=0):
     import torch
 
     out = torch.full((n, 4), float("nan"), device="cuda")
     nb.nbody_accel_shard(pd, n, float(eps2), s, S, out, want_pot=want_pot,
-                         plan=dict(mode="pairs", band=band, tpl=tpl))
+                         plan=dict(mode="pairs", band=band, tpl=tpl, run=run))
     torch.cuda.synchronize()
     return out
 
@@ -55,8 +55,8 @@ SHARD_CASES = [(1, 512, (1,)), (2049, 512, (1, 2, 5)), (3000, 512, (2, 3, 6)),
 
 
 @pytest.mark.parametrize("n,band,shards", SHARD_CASES)
-@pytest.mark.parametrize("tpl", [4, 8])
-def test_shard_parts_and_merge(nb, n, band, shards, tpl):
+@pytest.mark.parametrize("tpl,run", [(4, 0), (8, 0), (8, 3)])
+def test_shard_parts_and_merge(nb, n, band, shards, tpl, run):
     import torch
 
     import oracle
@@ -71,11 +71,11 @@ def test_shard_parts_and_merge(nb, n, band, shards, tpl):
     for S in shards:
         parts = []
         for s in range(S):
-            out = run_shard(nb, pd, n, eps2, s, S, band, tpl)
+            out = run_shard(nb, pd, n, eps2, s, S, band, tpl, run=run)
             part = out.cpu().numpy()
             ref = oracle.shard(pos, eps2, band, s, S, targets=idx)
             assert_part_parity(part if idx is None else part[idx], ref,
-                               f"N={n} band={band} tpl={tpl} shard {s}/{S}")
+                               f"N={n} band={band} tpl={tpl} run={run} shard {s}/{S}")
             parts.append(out)
         stacked = torch.stack(parts).contiguous()
         acc, pot = finish(nb, stacked, n, S, 0, n)
@@ -87,15 +87,16 @@ def test_shard_parts_and_merge(nb, n, band, shards, tpl):
         assert p3 is None and np.array_equal(a3, a2)
 
 
-@pytest.mark.parametrize("n,band", [(3000, 512), (70000, 2048), (70000, 4096)])
-def test_one_shard_equals_accel(nb, n, band):
+@pytest.mark.parametrize("n,band,run", [(3000, 512, 0), (3000, 512, 2), (70000, 2048, 0),
+                                        (70000, 2048, 5), (70000, 4096, 0), (70000, 4096, 4)])
+def test_one_shard_equals_accel(nb, n, band, run):
     """A single shard finished is nbody_accel_plan with the same pairs plan, bit for bit."""
     import torch
 
     pos, _ = workloads.random_bodies(n, seed=31)
     pd = to_dev(pos)
-    plan = dict(mode="pairs", band=band, tpl=8)
-    out = run_shard(nb, pd, n, 1e-4, 0, 1, band, 8)
+    plan = dict(mode="pairs", band=band, tpl=8, run=run)
+    out = run_shard(nb, pd, n, 1e-4, 0, 1, band, 8, run=run)
     acc, pot = finish(nb, out.unsqueeze(0).contiguous(), n, 1, 0, n)
     a_ref = torch.empty((n, 4), device="cuda")
     p_ref = torch.empty((n,), device="cuda")
