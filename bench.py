@@ -340,9 +340,9 @@ def sweep(nb, w, pos, vel, acc, pot, args) -> int:
     return 0
 
 
-def near_grid_terms(pos_h, lo, h, dims) -> int:
-    """Pair terms of the grid near field: sum over cells of n_c times the bodies in its 27-cell
-    neighbourhood (cells decided in float32, as the library decides them)."""
+def near_grid_counts(pos_h, lo, h, dims):
+    """Bodies per cell, as an array indexed (z, y, x) (cells decided in float32, as the library
+    decides them)."""
     import numpy as np
 
     x = pos_h[:, :3].astype(np.float32)
@@ -351,16 +351,49 @@ def near_grid_terms(pos_h, lo, h, dims) -> int:
     k = np.clip(np.nan_to_num(k, nan=0.0), 0, np.asarray(dims) - 1).astype(np.int64)
     cnt = np.zeros(dims[::-1], np.int64)
     np.add.at(cnt, (k[:, 2], k[:, 1], k[:, 0]), 1)
+    return cnt
+
+
+def near_grid_terms(pos_h, lo, h, dims) -> int:
+    """Pair terms of the grid near field: sum over cells of n_c times the bodies in its 27-cell
+    neighbourhood."""
+    import numpy as np
+
+    cnt = near_grid_counts(pos_h, lo, h, dims)
     pad = np.pad(cnt, 1)
     nbr = sum(pad[1 + dz:1 + dz + dims[2], 1 + dy:1 + dy + dims[1], 1 + dx:1 + dx + dims[0]]
               for dz in (-1, 0, 1) for dy in (-1, 0, 1) for dx in (-1, 0, 1))
     return int(np.sum(cnt * nbr))
 
 
-def near_roofline(terms: int, kernel_ms: float, pot: bool, kernel: str) -> dict:
-    """The near-field kernel against the FP32 vector peak: its issued flops per launch (21 per
-    one-sided term with the potential, 19 without, as in the tile kernel) over the
-    event-timed launch."""
+def near_grid_pair_units(pos_h, lo, h, dims) -> tuple[int, int]:
+    """The pair-symmetric near-grid kernel's units: (unordered pairs of bodies in neighbouring
+    cells, each evaluated once; one-sided terms of the cells with themselves, sum of n_c^2).
+    Twice the pairs plus the self terms are the near field's pair terms."""
+    import numpy as np
+
+    cnt = near_grid_counts(pos_h, lo, h, dims)
+    self_terms = int(np.sum(cnt * cnt))
+    return (near_grid_terms(pos_h, lo, h, dims) - self_terms) // 2, self_terms
+
+
+def near_roofline(terms: int, kernel_ms: float, pot: bool, kernel: str,
+                  pairs: tuple[int, int] | None = None) -> dict:
+    """The near-field kernel against the FP32 vector peak: its own flops per launch over the
+    event-timed launch. One-sided: 21 per term with the potential, 19 without, as in the tile
+    kernel. Pair-symmetric (pairs = (unordered pairs, self terms)): 30 (26) per pair and 21
+    (19) per self term, as in the all-pairs pair kernel; padding lanes are not counted."""
+    if pairs is not None:
+        npair, nself = pairs
+        flops = FLOPS_PAIR[pot] * npair + FLOPS_ONE_SIDED[pot] * nself
+        achieved = flops / (kernel_ms * 1e-3) / 1e12
+        return {"bound": "alu", "kernel": kernel, "achieved": round(achieved, 2),
+                "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / FP32_VECTOR_PEAK_TFLOPS, 4), "traffic": None,
+                "flops_per_launch": flops,
+                "units_per_launch": {"pairs": npair, "one_sided_terms": nself},
+                "flops_per_unit": {"pair": FLOPS_PAIR[pot], "one_sided_term": FLOPS_ONE_SIDED[pot]},
+                "launch_ms_mean": round(kernel_ms, 4)}
     flops = FLOPS_ONE_SIDED[pot] * terms
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     return {"bound": "alu", "kernel": kernel, "achieved": round(achieved, 2),
@@ -409,11 +442,17 @@ def near_grid_bench(nb, w, pos, args) -> int:
     d = args.near_grid
     lo, h, dims = (-1.0, -1.0, -1.0), 2.0 / d, (d, d, d)
     n = w.n
+    kernel = {"auto": nb.NEAR_AUTO, "one-sided": nb.NEAR_ONE_SIDED,
+              "pairs": nb.NEAR_PAIRS}[args.near_kernel]
+    if kernel == nb.NEAR_AUTO:  # the library's rule: pairs from 96 to 2048 bodies per cell
+        cus = torch.cuda.get_device_properties(pos.device).multi_processor_count
+        kernel = (nb.NEAR_PAIRS if 96 * d ** 3 <= n <= 2048 * d ** 3 and d ** 3 >= 2 * cus
+                  else nb.NEAR_ONE_SIDED)
     acc = torch.empty_like(pos)
     pot = torch.empty(n, dtype=torch.float32, device=pos.device)
     stream = torch.cuda.current_stream()
     for _ in range(max(1, args.warmup)):
-        nb.nbody_near_grid(pos, n, float(w.eps2), lo, h, dims, acc, pot, stream)
+        nb.nbody_near_grid_kernel(pos, n, float(w.eps2), lo, h, dims, kernel, acc, pot, stream)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     ks = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
@@ -422,7 +461,7 @@ def near_grid_bench(nb, w, pos, args) -> int:
     e0.record(stream)
     for k in range(args.steps):
         nb.nbody_time_kernel(ks[2 * k], ks[2 * k + 1])
-        nb.nbody_near_grid(pos, n, float(w.eps2), lo, h, dims, acc, pot, stream)
+        nb.nbody_near_grid_kernel(pos, n, float(w.eps2), lo, h, dims, kernel, acc, pot, stream)
     e1.record(stream)
     torch.cuda.synchronize()
     nb.nbody_time_kernel(None, None)
@@ -433,7 +472,11 @@ def near_grid_bench(nb, w, pos, args) -> int:
             "bodies_per_cell": n / (d ** 3), "pair_terms": terms, "ms": round(ms, 4),
             "G_terms_per_s": round(terms / ms / 1e6, 2), "kernel_ms": round(kms, 4),
             "kernel_G_terms_per_s": round(terms / kms / 1e6, 2),
-            "roofline": near_roofline(terms, kms, True, "p2p_kernel (grid neighbourhoods)")}
+            "kernel": "pairs" if kernel == nb.NEAR_PAIRS else "one-sided",
+            "roofline": (near_roofline(terms, kms, True, "p2p_sym_kernel (forward neighbour cells)",
+                                       near_grid_pair_units(w.pos, lo, h, dims))
+                         if kernel == nb.NEAR_PAIRS else
+                         near_roofline(terms, kms, True, "p2p_kernel (grid neighbourhoods)"))}
     if args.cpu_budget > 0:
         import oracle
 
@@ -601,6 +644,8 @@ def main(argv=None) -> int:
     ap.add_argument("--near-grid", type=int, default=0, metavar="D",
                     help="only time nbody_near_grid on a D^3 grid over [-1, 1]^3 (near field; "
                          "prints its own JSON line, no contract line)")
+    ap.add_argument("--near-kernel", default="auto", choices=["auto", "one-sided", "pairs"],
+                    help="--near-grid: the near-field kernel (default: the library's choice)")
     ap.add_argument("--near-tree", type=int, default=0, metavar="LEAF",
                     help="only time nbody_near_tree with leaves of at most LEAF bodies (near "
                          "field over octree leaves; prints its own JSON line, no contract line)")

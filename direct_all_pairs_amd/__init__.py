@@ -25,6 +25,7 @@ BCAST_AUTO, BCAST_LDS, BCAST_SCALAR, BCAST_READLANE = 0, 1, 2, 3
 BCAST_NAMES = {BCAST_LDS: "lds", BCAST_SCALAR: "scalar", BCAST_READLANE: "readlane"}
 MODE_AUTO, MODE_TILES, MODE_PAIRS, MODE_SMALL = 0, 1, 2, 3
 MODE_NAMES = {MODE_TILES: "tiles", MODE_PAIRS: "pairs", MODE_SMALL: "small"}
+NEAR_AUTO, NEAR_ONE_SIDED, NEAR_PAIRS = 0, 1, 2
 
 
 class NbodyError(RuntimeError):
@@ -79,6 +80,9 @@ _lib.nbody_diagnostics.argtypes = [_vp, _vp, _vp, _i64, _f32, _vp, _vp]
 _lib.nbody_p2p.argtypes = [_vp, _i64, _f32, _vp, ctypes.c_int32, _vp, _vp, _i64, _vp, _vp, _vp]
 _lib.nbody_near_grid.argtypes = [_vp, _i64, _f32, ctypes.POINTER(ctypes.c_float), _f32,
                                  ctypes.POINTER(ctypes.c_int32), _vp, _vp, _vp]
+_lib.nbody_near_grid_kernel.argtypes = [_vp, _i64, _f32, ctypes.POINTER(ctypes.c_float), _f32,
+                                        ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, _vp, _vp,
+                                        _vp]
 _lib.nbody_near_tree.argtypes = [_vp, _i64, _f32, _i64, _vp, _vp, ctypes.POINTER(nbody_tree_stats),
                                  _vp]
 _lib.nbody_accel_soa.argtypes = [_vp, _vp, _vp, _vp, _i64, _f32, _vp, _vp, _vp, _vp, _vp]
@@ -91,14 +95,14 @@ _lib.nbody_release_workspace.argtypes = []
 _lib.nbody_version.restype = ctypes.c_char_p
 for _f in ("nbody_accel", "nbody_accel_plan", "nbody_step", "nbody_step_plan",
            "nbody_step_noalloc", "nbody_time_kernel", "nbody_accel_soa", "nbody_step_soa", "nbody_accel_shard", "nbody_shard_finish",
-           "nbody_p2p", "nbody_near_grid", "nbody_near_tree", "nbody_diagnostics",
-           "nbody_plan_for", "nbody_release_workspace"):
+           "nbody_p2p", "nbody_near_grid", "nbody_near_grid_kernel", "nbody_near_tree",
+           "nbody_diagnostics", "nbody_plan_for", "nbody_release_workspace"):
     getattr(_lib, _f).restype = _int
 
 EXPORTS = ("nbody_accel", "nbody_accel_plan", "nbody_step", "nbody_step_plan",
            "nbody_step_noalloc", "nbody_time_kernel", "nbody_accel_soa", "nbody_step_soa",
            "nbody_accel_shard", "nbody_shard_finish", "nbody_p2p", "nbody_near_grid",
-           "nbody_near_tree", "nbody_diagnostics", "nbody_plan_for", "nbody_last_error", "nbody_release_workspace",
+           "nbody_near_grid_kernel", "nbody_near_tree", "nbody_diagnostics", "nbody_plan_for", "nbody_last_error", "nbody_release_workspace",
            "nbody_version")
 DIAG_FIELDS = ("kinetic", "potential", "total", "momentum", "angular_momentum", "mass",
                "centre_of_mass")
@@ -247,6 +251,17 @@ def nbody_near_grid(pos, N: int, eps2: float, lo, h: float, dims, acc_out, pot_o
     rc = _lib.nbody_near_grid(_ptr(pos), int(N), float(eps2), lo_c, float(h), dims_c,
                               _ptr(acc_out), _ptr(pot_out), _stream(stream))
     return _check(rc, "nbody_near_grid") if check else rc
+
+
+def nbody_near_grid_kernel(pos, N: int, eps2: float, lo, h: float, dims, kernel: int, acc_out,
+                           pot_out=None, stream=None, check: bool = True) -> int:
+    """nbody_near_grid with the near-field kernel chosen (NEAR_AUTO, NEAR_ONE_SIDED,
+    NEAR_PAIRS)."""
+    lo_c = (ctypes.c_float * 3)(*[float(v) for v in lo]) if lo is not None else None
+    dims_c = (ctypes.c_int32 * 3)(*[int(v) for v in dims]) if dims is not None else None
+    rc = _lib.nbody_near_grid_kernel(_ptr(pos), int(N), float(eps2), lo_c, float(h), dims_c,
+                                     int(kernel), _ptr(acc_out), _ptr(pot_out), _stream(stream))
+    return _check(rc, "nbody_near_grid_kernel") if check else rc
 
 
 def nbody_near_tree(pos, N: int, eps2: float, leaf_size: int, acc_out, pot_out=None,

@@ -226,6 +226,16 @@ hipError_t timed_launch(hipStream_t stream, F &&fn)
 // ------------------------------------------------------------ planning
 
 constexpr int kMaxSplits = 4096;
+// nbody_near_grid chooses the pair-symmetric kernel for 96 to 2048 bodies per cell on
+// average and at least two cells per compute unit (it runs one workgroup per cell).
+// Measured at N = 2^20 on D^3 grids (kernel time, one-sided -> pairs): D = 23 (86
+// per cell) 0.80 -> 0.84 ms, D = 22 (98) 0.86 -> 0.78, D = 16 (256) 2.0 -> 1.6, D = 12
+// (607) 4.4 -> 3.8, D = 8 (2048, 512 cells) 14.6 -> 12.6, D = 7 (3057, 343 cells)
+// 20.5 -> 25.6.
+constexpr int64_t kSymMinMean = 96;
+constexpr int64_t kSymMaxMean = 2048;
+constexpr int64_t kSymMinCellsPerCU = 2;
+
 // Most cells a uniform grid of nbody_near_grid may have (one 32-bit key per body
 // and one start index per cell).
 constexpr int64_t kMaxGridCells = (int64_t)1 << 28;
@@ -1035,6 +1045,16 @@ int nbody_p2p(const nbody_f4 *pos, int64_t N, float eps2, const int32_t *cell_st
 int nbody_near_grid(const nbody_f4 *pos, int64_t N, float eps2, const float lo[3], float h,
                     const int32_t dims[3], nbody_f4 *acc_out, float *pot_out, hipStream_t stream)
 {
+    return nbody_near_grid_kernel(pos, N, eps2, lo, h, dims, NBODY_NEAR_AUTO, acc_out, pot_out,
+                                  stream);
+}
+
+int nbody_near_grid_kernel(const nbody_f4 *pos, int64_t N, float eps2, const float lo[3], float h,
+                           const int32_t dims[3], int32_t kernel, nbody_f4 *acc_out,
+                           float *pot_out, hipStream_t stream)
+{
+    if (kernel < NBODY_NEAR_AUTO || kernel > NBODY_NEAR_PAIRS)
+        return fail(NBODY_EINVAL, "kernel=%d is not a NBODY_NEAR_* value", (int)kernel);
     int rc = check_n(N);
     if (rc != NBODY_OK) return rc;
     if (!lo || !dims) return fail(NBODY_EINVAL, "lo or dims is NULL");
@@ -1069,18 +1089,27 @@ int nbody_near_grid(const nbody_f4 *pos, int64_t N, float eps2, const float lo[3
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     nbk::GridSpec g{{lo[0], lo[1], lo[2]}, inv_h, {dims[0], dims[1], dims[2]}};
     const int n = (int)N, nc = (int)ncell;
+    bool pairs = kernel == NBODY_NEAR_PAIRS;
+    if (kernel == NBODY_NEAR_AUTO && N >= kSymMinMean * ncell && N <= kSymMaxMean * ncell) {
+        DeviceFacts facts;
+        rc = device_facts(dev, &facts);
+        if (rc != NBODY_OK) return rc;
+        pairs = ncell >= kSymMinCellsPerCU * facts.cus;
+    }
     int end_bit = 1;
     while (end_bit < 32 && ((int64_t)1 << end_bit) < ncell) ++end_bit;
     const size_t sort_bytes = nbk::sort_temp_bytes(n);
     // scratch: keys, idx, sorted keys, perm (N x 4 each), sorted pos (N x 16), cell starts
-    // ((ncell + 1) x 4), sort temp. The near-field kernel writes each body's results
-    // straight to its place in the caller's order (perm).
-    size_t off[8];
-    const size_t sz[7] = {b4, b4, b4, b4, b16, ((size_t)nc + 1) * 4, sort_bytes};
+    // ((ncell + 1) x 4), sort temp, and for the pair-symmetric kernel its slots. The
+    // one-sided kernel, or the pair finish, writes each body's results straight to its
+    // place in the caller's order (perm).
+    size_t off[9];
+    const size_t sz[8] = {b4, b4, b4, b4, b16, ((size_t)nc + 1) * 4, sort_bytes,
+                          pairs ? (size_t)nbk::kSymSlots * b16 : 0};
     off[0] = 0;
-    for (int i = 0; i < 7; ++i) off[i + 1] = align256(off[i] + sz[i]);
+    for (int i = 0; i < 8; ++i) off[i + 1] = align256(off[i] + sz[i]);
     void *ws = nullptr;
-    rc = scratch_get(dev, stream, off[7], &ws);
+    rc = scratch_get(dev, stream, off[8], &ws);
     if (rc != NBODY_OK) return rc;
     char *b = (char *)ws;
     unsigned *keys = (unsigned *)(b + off[0]), *skeys = (unsigned *)(b + off[2]);
@@ -1093,7 +1122,15 @@ int nbody_near_grid(const nbody_f4 *pos, int64_t N, float eps2, const float lo[3
         e = nbk::sort_pairs(temp, keys, skeys, idx, perm, n, end_bit, stream);
     if (e == hipSuccess) e = nbk::launch_gather((const float4 *)pos, perm, n, spos, stream);
     if (e == hipSuccess) e = nbk::launch_cell_starts(skeys, n, nc, start, stream);
-    if (e == hipSuccess) {
+    if (e == hipSuccess && pairs) {
+        float4 *part = (float4 *)(b + off[7]);
+        e = timed_launch(stream, [&] {
+            return nbk::launch_p2p_sym(pot_out != nullptr, spos, n, eps2, start, g, part, stream);
+        });
+        if (e == hipSuccess)
+            e = nbk::launch_sym_finish(part, n, skeys, start, g, perm, (float4 *)acc_out, pot_out,
+                                       stream);
+    } else if (e == hipSuccess) {
         nbk::P2PArgs a{spos, n, eps2, start, nc, nullptr, nullptr, 0, (float4 *)acc_out, pot_out,
                        perm};
         e = timed_launch(stream,

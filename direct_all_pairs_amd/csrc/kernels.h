@@ -173,6 +173,19 @@ struct GridSpec {
 hipError_t launch_p2p(bool pot, const P2PArgs &args, hipStream_t stream);
 // The same kernel with the 27 neighbour cells of the grid as every cell's list.
 hipError_t launch_p2p_grid(bool pot, const P2PArgs &args, const GridSpec &g, hipStream_t stream);
+// The same near field with each unordered pair of neighbouring cells evaluated
+// once, by the cell with the lower linear index, and applied to both cells'
+// bodies (a cell's own pairs one-sided): one workgroup per cell holding up to 512
+// of its bodies in registers at a time, the 13 forward neighbour cells walked as
+// one sequence of 64-body blocks. part holds kSymSlots slots of N records (every
+// slot a body has is written once); launch_sym_finish adds them in a fixed order
+// and writes row out_index[i] (cell_of[i]: the cell of sorted body i).
+constexpr int kSymSlots = 14;
+hipError_t launch_p2p_sym(bool pot, const float4 *pos, int n, float eps2, const int *cell_start,
+                          const GridSpec &g, float4 *part, hipStream_t stream);
+hipError_t launch_sym_finish(const float4 *part, int n, const unsigned *cell_of,
+                             const int *cell_start, const GridSpec &g, const int *out_index,
+                             float4 *acc_out, float *pot_out, hipStream_t stream);
 // keys[i] = linear cell of body i, idx[i] = i.
 hipError_t launch_grid_keys(const float4 *pos, int n, const GridSpec &g, unsigned *keys, int *idx,
                             hipStream_t stream);

@@ -41,6 +41,7 @@
 // conversion.
 #include "kernels.h"
 
+#include <climits>
 #include <cmath>
 #include <cstdint>
 
@@ -726,6 +727,49 @@ __device__ __forceinline__ V &at_byte(void *base, int off)
 // B side is added into the LDS accumulator jacc (kept across the items of a
 // run; the caller zeroes and stores it), or with a global accumulator into
 // outB[body - offB], which the first item of a run starts afresh.
+// One j-block pass of 64 steps: at step s lane l pairs its T targets with body
+// (l - s) mod 64 of the wave's block copy (byte row `row` of blk; jbody is the
+// lane's own body, the partner of step 0), and with SYM adds that body's sums
+// into its entry of the wave's sum row, which lane l - 1 wrote the step before.
+// U steps per loop trip.
+template <int T, bool POT, bool SYM, int U>
+__device__ __forceinline__ void block_pass(void *blk, void *sum, int row, int lane, float4 jbody,
+                                           const float (&tx)[T], const float (&ty)[T],
+                                           const float (&tz)[T], const float (&tm)[T],
+                                           float eps2, float (&bx)[T], float (&by)[T],
+                                           float (&bz)[T], float (&bp)[T])
+{
+    float jx = jbody.x, jy = jbody.y, jz = jbody.z, jm = jbody.w;
+    int cur = row | (lane * (int)sizeof(float4));  // byte offset of entry (lane - step) mod 64
+#pragma unroll U
+    for (int step = 0; step < 64; ++step) {
+        const int nxt = ((cur - (int)sizeof(float4)) & (kBlkBytes - 1)) | row;
+        // the partner's sums first, then the partner of the next step (read
+        // ahead of this step's arithmetic): LDS reads return in order, so the
+        // first FMA into the sums waits only for the first read
+        float gx = 0.0f, gy = 0.0f, gz = 0.0f, gp = 0.0f;
+        if constexpr (SYM) {
+            const float4 g = at_byte<const float4>(sum, cur);
+            gx = g.x;
+            gy = g.y;
+            gz = g.z;
+            gp = g.w;
+        }
+        const float4 nb4 = at_byte<const float4>(blk, nxt);
+        pair_step<T, POT, SYM>(jx, jy, jz, jm, tx, ty, tz, tm, eps2, bx, by, bz, bp, gx, gy, gz,
+                               gp);
+        if constexpr (SYM) {
+            at_byte<float4>(sum, cur) = make_float4(gx, gy, gz, gp);
+            __builtin_amdgcn_wave_barrier();
+        }
+        jx = nb4.x;
+        jy = nb4.y;
+        jz = nb4.z;
+        jm = nb4.w;
+        cur = nxt;
+    }
+}
+
 template <int T, int BD, bool POT, bool SYM>
 __device__ __forceinline__ void pairs_item(const PairsArgs &k, int A, int B, float4 *outA,
                                            long long offA, float4 *outB, long long offB,
@@ -769,42 +813,15 @@ __device__ __forceinline__ void pairs_item(const PairsArgs &k, int A, int B, flo
             sh.jblk[w][lane] = jbody;
             if constexpr (SYM) sh.jsum[w][lane] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             __builtin_amdgcn_wave_barrier();
-            float jx = jbody.x, jy = jbody.y, jz = jbody.z, jm = jbody.w;
             if constexpr (!FLAT) {
 #pragma unroll
                 for (int t = 0; t < T; ++t) bx[t] = by[t] = bz[t] = bp[t] = 0.0f;
             }
-            int cur = row | (lane * (int)sizeof(float4));  // byte offset of entry (lane - step) mod 64
             // two steps per trip (no register copies of the partner) except where
             // measured slower: 4 targets per lane in 2048-body bands
             constexpr int U = (T == 4 && BD >= 2048) ? 1 : 2;
-#pragma unroll U
-            for (int step = 0; step < 64; ++step) {
-                const int nxt = ((cur - (int)sizeof(float4)) & (kBlkBytes - 1)) | row;
-                // the partner's sums first, then the partner of the next step (read
-                // ahead of this step's arithmetic): LDS reads return in order, so the
-                // first FMA into the sums waits only for the first read
-                float gx = 0.0f, gy = 0.0f, gz = 0.0f, gp = 0.0f;
-                if constexpr (SYM) {
-                    const float4 g = at_byte<const float4>(&sh.jsum[0][0], cur);
-                    gx = g.x;
-                    gy = g.y;
-                    gz = g.z;
-                    gp = g.w;
-                }
-                const float4 nb4 = at_byte<const float4>(&sh.jblk[0][0], nxt);
-                pair_step<T, POT, SYM>(jx, jy, jz, jm, tx, ty, tz, tm, eps2, bx, by, bz, bp, gx,
-                                       gy, gz, gp);
-                if constexpr (SYM) {
-                    at_byte<float4>(&sh.jsum[0][0], cur) = make_float4(gx, gy, gz, gp);
-                    __builtin_amdgcn_wave_barrier();
-                }
-                jx = nb4.x;
-                jy = nb4.y;
-                jz = nb4.z;
-                jm = nb4.w;
-                cur = nxt;
-            }
+            block_pass<T, POT, SYM, U>(&sh.jblk[0][0], &sh.jsum[0][0], row, lane, jbody, tx, ty,
+                                       tz, tm, eps2, bx, by, bz, bp);
             if constexpr (!FLAT) {
 #pragma unroll
                 for (int t = 0; t < T; ++t) {
@@ -1745,6 +1762,274 @@ __device__ __forceinline__ int grid_axis(float x, float lo, float inv_h, int dim
     if (!(f >= 0.0f)) f = 0.0f;
     if (f > (float)(dim - 1)) f = (float)(dim - 1);
     return (int)f;
+}
+
+// ---------------------------------------------------------------- near grid, pair-symmetric
+// Each unordered pair of neighbouring cells {c, c + dir} is evaluated once, by the
+// cell with the lower linear index (its owner), and applied to both cells'
+// bodies, as the band pairs of the all-pairs kernel are; a cell's own pairs are
+// evaluated one-sided. The 13 forward directions (dx, dy, dz), those with dz > 0,
+// or dz = 0 and dy > 0, or dz = dy = 0 and dx > 0, are numbered
+//   k = 0: (+1, 0, 0);  k = 1..3: (k - 2, +1, 0);  k = 4..12: ((k-4) % 3 - 1, (k-4) / 3 - 1, +1)
+// and form five runs of consecutive cells (x fastest in the linear index): run 0
+// = direction 0, run 1 = directions 1..3, run 2 + r = directions 4 + 3r .. 6 + 3r,
+// each clipped to the grid. A body of cell c holds 14 partial sums: slot 0 from
+// its own cell's workgroup (its cell one-sided and its side of the cell's forward
+// pairs), slot 1 + k from the workgroup of the cell c - dir_k (its side of that
+// pair), written once each; the finish adds the slots that exist in that order.
+constexpr int kSymRuns = 5;
+constexpr int kSymDirs = 13;
+
+__host__ __device__ constexpr int sym_dir_dx(int k) { return k == 0 ? 1 : (k < 4 ? k - 2 : (k - 4) % 3 - 1); }
+__host__ __device__ constexpr int sym_dir_dy(int k) { return k == 0 ? 0 : (k < 4 ? 1 : (k - 4) / 3 - 1); }
+__host__ __device__ constexpr int sym_dir_dz(int k) { return k < 4 ? 0 : 1; }
+
+// Launch index b -> owner cell: with heavy, first the cells whose forward
+// neighbourhood is whole (1 <= x <= dx-2, 1 <= y <= dy-2, z <= dz-2: 13
+// neighbour cells), then the others in natural order, so that the smaller
+// neighbourhoods fill the CUs at the end of the launch. A bijection of
+// [0, dx*dy*dz); the identity without heavy or below 3 x 3 x 2 cells.
+__host__ __device__ inline int sym_cell(int b, int dx, int dy, int dz, bool heavy)
+{
+    const int ix = dx - 2, iy = dy - 2, iz = dz - 1;
+    if (!heavy || ix < 1 || iy < 1 || iz < 1) return b;
+    const int ni = ix * iy * iz;
+    if (b < ni) return ((b / (ix * iy)) * dy + 1 + (b / ix) % iy) * dx + 1 + b % ix;
+    int k = b - ni;
+    const int per = 2 * dx + 2 * iy;  // other cells of a plane z <= dz-2: rows y = 0, dy-1, ends x = 0, dx-1
+    if (k < per * iz) {
+        const int z = k / per;
+        int r = k % per, y, x;
+        if (r < dx) {
+            y = 0;
+            x = r;
+        } else if ((r -= dx) < 2 * iy) {
+            y = 1 + r / 2;
+            x = (r & 1) ? dx - 1 : 0;
+        } else {
+            y = dy - 1;
+            x = r - 2 * iy;
+        }
+        return (z * dy + y) * dx + x;
+    }
+    k -= per * iz;  // the last plane, whole
+    return ((dz - 1) * dy + k / dx) * dx + k % dx;
+}
+
+// Run t (0..4) of owner cell (cx, cy, cz) on a dx x dy x dz grid: the row (y, z)
+// of its cells, their x range [xf, xl] and the direction k0 of cell xf; false when
+// the run holds no cell of the grid.
+__host__ __device__ inline bool sym_run(int t, int cx, int cy, int cz, int dx, int dy, int dz,
+                                        int &y, int &z, int &xf, int &xl, int &k0)
+{
+    y = cy;
+    z = cz;
+    xf = cx + 1;
+    xl = cx + 1;
+    k0 = 0;
+    if (t == 1) {
+        y = cy + 1;
+        xf = cx - 1;
+        k0 = 1;
+    } else if (t >= 2) {
+        y = cy + (t - 2) - 1;
+        z = cz + 1;
+        xf = cx - 1;
+        k0 = 4 + 3 * (t - 2);
+    }
+    if (xf < 0) {
+        k0 -= xf;
+        xf = 0;
+    }
+    if (xl > dx - 1) xl = dx - 1;
+    return y >= 0 && y < dy && z < dz && xf <= xl;
+}
+
+struct SymShared {
+    float4 jblk[4][kRowLen];  // each wave's copy of its current block; with jsum,
+                              // between i-sets, the running cross-wave sum
+    float4 jsum[4][kRowLen];  // each wave's partner sums of that block
+    int sb[kSymRuns];         // body range [sb, sb + len) of each run (len 0 outside the grid)
+    int pre[kSymRuns + 1];    // prefix of the run lengths
+    int b1[kSymRuns], b2[kSymRuns];  // first body of the run's second and third cell (INT_MAX: none)
+    int k0[kSymRuns];         // direction of the run's first cell
+};
+
+static_assert(kSymSlots == 1 + kSymDirs, "one own slot and one per forward direction");
+
+struct SymArgs {
+    const float4 *pos;      // N bodies grouped by cell (cell order)
+    int n;
+    float eps2;
+    const int *cell_start;  // ncell + 1 entries
+    int dims[3];
+    int heavy_first;
+    float4 *part;           // 14 slots of N records: part[slot * N + i]
+};
+
+// One i-set of R rows of 64 owner targets [i0, i0 + 64 R) (past o1: zero mass):
+// the owner cell one-sided, then the forward sequence in pairs; the targets'
+// sums go to own slot 0, the forward bodies' sums to their direction slots
+// (stored on the first i-set, added to on later ones by the same thread).
+template <int R, bool POT>
+__device__ __forceinline__ void sym_iset(const SymArgs &k, SymShared &sh, int i0, int o0, int o1,
+                                         bool first, float eps2)
+{
+    constexpr int W = 4;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int row = w * (int)sizeof(sh.jblk[0]);
+    float tx[R], ty[R], tz[R], tm[R], ax[R], ay[R], az[R], ap[R];
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+        const int b = i0 + t * 64 + lane;
+        const float4 v = k.pos[b < o1 ? b : o1 - 1];
+        const bool in = b < o1;
+        tx[t] = in ? v.x : 0.0f;
+        ty[t] = in ? v.y : 0.0f;
+        tz[t] = in ? v.z : 0.0f;
+        tm[t] = in ? v.w : 0.0f;
+        ax[t] = ay[t] = az[t] = ap[t] = 0.0f;
+    }
+    // the owner cell against itself, one-sided (self pairs included)
+    const int no = o1 - o0;
+    for (int jb = w; jb * 64 < no; jb += W) {
+        const int b = o0 + jb * 64 + lane;
+        const float4 v = k.pos[b < o1 ? b : o1 - 1];
+        const float4 jbody = b < o1 ? v : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        __builtin_amdgcn_wave_barrier();
+        sh.jblk[w][lane] = jbody;
+        __builtin_amdgcn_wave_barrier();
+        block_pass<R, POT, false, 2>(&sh.jblk[0][0], &sh.jsum[0][0], row, lane, jbody, tx, ty, tz,
+                                     tm, eps2, ax, ay, az, ap);
+    }
+    // the forward sequence, pair-symmetric
+    const int total = sh.pre[kSymRuns];
+    for (int jb = w; jb * 64 < total; jb += W) {
+        const int p = jb * 64 + lane;
+        int e = 0;
+#pragma unroll
+        for (int r = 1; r < kSymRuns; ++r) e += p >= sh.pre[r] ? 1 : 0;
+        const int b = sh.sb[e] + (p - sh.pre[e]);
+        const bool in = p < total;
+        const float4 v = k.pos[in ? b : 0];
+        const float4 jbody = in ? v : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        __builtin_amdgcn_wave_barrier();
+        sh.jblk[w][lane] = jbody;
+        sh.jsum[w][lane] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        __builtin_amdgcn_wave_barrier();
+        block_pass<R, POT, true, 2>(&sh.jblk[0][0], &sh.jsum[0][0], row, lane, jbody, tx, ty, tz,
+                                    tm, eps2, ax, ay, az, ap);
+        const float4 g = sh.jsum[w][lane];
+        if (in) {
+            const int dir = sh.k0[e] + (b >= sh.b1[e] ? 1 : 0) + (b >= sh.b2[e] ? 1 : 0);
+            float4 *dst = k.part + (size_t)(1 + dir) * (size_t)k.n + b;
+            float4 o = first ? make_float4(0.0f, 0.0f, 0.0f, 0.0f) : *dst;
+            o.x -= g.x;
+            o.y -= g.y;
+            o.z -= g.z;
+            o.w += g.w;
+            *dst = o;
+        }
+    }
+    // the targets' sums across the waves, in wave order, through the block and sum rows
+    float4 *red = &sh.jblk[0][0];
+    __syncthreads();
+    for (int ww = 0; ww < W; ++ww) {
+        if (w == ww) {
+#pragma unroll
+            for (int t = 0; t < R; ++t) {
+                const int idx = t * 64 + lane;
+                float4 v = make_float4(ax[t], ay[t], az[t], ap[t]);
+                if (ww > 0) {
+                    const float4 q = red[idx];
+                    v = make_float4(q.x + v.x, q.y + v.y, q.z + v.z, q.w + v.w);
+                }
+                if (ww < W - 1) {
+                    red[idx] = v;
+                } else if (i0 + idx < o1) {
+                    k.part[i0 + idx] = v;
+                }
+            }
+        }
+        __syncthreads();
+    }
+    probe_poison(sh.jblk[w][lane]);
+    probe_poison(sh.jsum[w][lane]);
+}
+
+// One workgroup per owner cell (launch order: sym_cell), 256 threads.
+template <bool POT>
+__global__ void __launch_bounds__(256) p2p_sym_kernel(SymArgs k)
+{
+    __shared__ SymShared sh;
+    const int dx = k.dims[0], dy = k.dims[1], dz = k.dims[2];
+    const int c = sym_cell((int)blockIdx.x, dx, dy, dz, k.heavy_first != 0);
+    const int o0 = k.cell_start[c], o1 = k.cell_start[c + 1];
+    if (o1 <= o0) return;  // an empty cell owns no pairs (uniform, before any barrier)
+    const int cx = c % dx, cy = (c / dx) % dy, cz = c / (dx * dy);
+    const int t = threadIdx.x;
+    if (t < kSymRuns) {
+        int y, z, xf, xl, k0;
+        const bool in = sym_run(t, cx, cy, cz, dx, dy, dz, y, z, xf, xl, k0);
+        const int rowc = (z * dy + y) * dx;
+        const int sb = in ? k.cell_start[rowc + xf] : 0;
+        const int se = in ? k.cell_start[rowc + xl + 1] : 0;
+        sh.sb[t] = sb;
+        sh.pre[t + 1] = se - sb;  // lengths; prefix below
+        sh.b1[t] = in && xf + 1 <= xl ? k.cell_start[rowc + xf + 1] : INT_MAX;
+        sh.b2[t] = in && xf + 2 <= xl ? k.cell_start[rowc + xf + 2] : INT_MAX;
+        sh.k0[t] = k0;
+    }
+    __syncthreads();
+    if (t == 0) {
+        sh.pre[0] = 0;
+        for (int r = 0; r < kSymRuns; ++r) sh.pre[r + 1] += sh.pre[r];
+    }
+    __syncthreads();
+    const float eps2 = in_vgpr(k.eps2);
+    for (int i0 = o0; i0 < o1; i0 += 512) {
+        const int rows = min(8, (o1 - i0 + 63) / 64);
+        const bool first = i0 == o0;
+        switch (rows) {
+        case 1: sym_iset<1, POT>(k, sh, i0, o0, o1, first, eps2); break;
+        case 2: sym_iset<2, POT>(k, sh, i0, o0, o1, first, eps2); break;
+        case 3: sym_iset<3, POT>(k, sh, i0, o0, o1, first, eps2); break;
+        case 4: sym_iset<4, POT>(k, sh, i0, o0, o1, first, eps2); break;
+        case 5: sym_iset<5, POT>(k, sh, i0, o0, o1, first, eps2); break;
+        case 6: sym_iset<6, POT>(k, sh, i0, o0, o1, first, eps2); break;
+        case 7: sym_iset<7, POT>(k, sh, i0, o0, o1, first, eps2); break;
+        default: sym_iset<8, POT>(k, sh, i0, o0, o1, first, eps2); break;
+        }
+    }
+}
+
+// Body i (cell order, cell from its sorted key): slot 0, then slot 1 + k for each
+// direction k whose owner cell (its cell - dir_k) lies in the grid and holds
+// bodies, in compensated sums; the results go to row out_index[i].
+__global__ void __launch_bounds__(256) sym_finish_kernel(const float4 *__restrict__ part, int n,
+                                                         const unsigned *__restrict__ cell_of,
+                                                         const int *__restrict__ cell_start,
+                                                         int dx, int dy, int dz,
+                                                         const int *__restrict__ out_index,
+                                                         float4 *__restrict__ acc_out,
+                                                         float *__restrict__ pot_out)
+{
+    const unsigned i = blockIdx.x * 256u + threadIdx.x;
+    if (i >= (unsigned)n) return;
+    const int c = (int)cell_of[i];
+    const int cx = c % dx, cy = (c / dx) % dy, cz = c / (dx * dy);
+    float4 a = part[i], e = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll 1
+    for (int q = 0; q < kSymDirs; ++q) {
+        const int ox = cx - sym_dir_dx(q), oy = cy - sym_dir_dy(q), oz = cz - sym_dir_dz(q);
+        if (ox < 0 || ox >= dx || oy < 0 || oy >= dy || oz < 0) continue;
+        const int o = (oz * dy + oy) * dx + ox;
+        if (cell_start[o + 1] <= cell_start[o]) continue;
+        two_sum_add4(a, e, part[(size_t)(1 + q) * (size_t)n + i]);
+    }
+    const int r = out_index ? out_index[i] : (int)i;
+    acc_out[r] = make_float4(a.x + e.x, a.y + e.y, a.z + e.z, 0.0f);
+    if (pot_out) pot_out[r] = -(a.w + e.w);
 }
 
 __global__ void __launch_bounds__(256) grid_keys_kernel(const float4 *__restrict__ pos, int n,
@@ -2787,6 +3072,30 @@ hipError_t launch_p2p_grid(bool pot, const P2PArgs &args, const GridSpec &g, hip
     const int heavy_first = (long long)args.n >= 16ll * args.ncell ? 1 : 0;
     return launch_p2p_any(pot, args, GridLists{g.dims[0], g.dims[1], g.dims[2], nullptr, heavy_first},
                           stream);
+}
+
+hipError_t launch_p2p_sym(bool pot, const float4 *pos, int n, float eps2, const int *cell_start,
+                          const GridSpec &g, float4 *part, hipStream_t stream)
+{
+    const long long ncell = (long long)g.dims[0] * g.dims[1] * g.dims[2];
+    if (n < 1 || !pos || !cell_start || !part || g.dims[0] < 1 || g.dims[1] < 1 ||
+        g.dims[2] < 1 || ncell > INT_MAX)
+        return hipErrorInvalidValue;
+    SymArgs a{pos, n, eps2, cell_start, {g.dims[0], g.dims[1], g.dims[2]}, 1, part};
+    void *kargs[] = {&a};
+    const void *fn = pot ? (const void *)&p2p_sym_kernel<true> : (const void *)&p2p_sym_kernel<false>;
+    return hipLaunchKernel(fn, dim3((unsigned)ncell), dim3(256), kargs, 0, stream);
+}
+
+hipError_t launch_sym_finish(const float4 *part, int n, const unsigned *cell_of,
+                             const int *cell_start, const GridSpec &g, const int *out_index,
+                             float4 *acc_out, float *pot_out, hipStream_t stream)
+{
+    if (n < 1 || !part || !cell_of || !cell_start || !acc_out) return hipErrorInvalidValue;
+    int dx = g.dims[0], dy = g.dims[1], dz = g.dims[2];
+    void *kargs[] = {&part, &n, &cell_of, &cell_start, &dx, &dy, &dz, &out_index, &acc_out, &pot_out};
+    return hipLaunchKernel((const void *)&sym_finish_kernel, dim3((unsigned)((n + 255) / 256)),
+                           dim3(256), kargs, 0, stream);
 }
 
 hipError_t launch_grid_keys(const float4 *pos, int n, const GridSpec &g, unsigned *keys, int *idx,

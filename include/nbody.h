@@ -293,14 +293,38 @@ int nbody_p2p(const nbody_f4 *pos_xyzm, int64_t N, float eps2, const int32_t *ce
  * bodies outside the box join the boundary cells), and gets the sum over every
  * body in its own and the 26 neighbouring cells (itself included). The library
  * bins the bodies (stable radix sort of the cell indices, so a cell keeps its
- * bodies in their input order), runs the nbody_p2p kernel over the 27-cell
- * neighbourhoods (as 9 runs of 3 consecutive cells) and writes acc_out /
- * pot_out in the caller's body order.
- * At most 2^28 cells. Scratch: ~N x 41 bytes + 4 bytes per cell.
+ * bodies in their input order), runs a near-field kernel and writes acc_out /
+ * pot_out in the caller's body order. The kernel is the automatic choice of
+ * nbody_near_grid_kernel.
+ * At most 2^28 cells. Scratch: ~N x 41 bytes + 4 bytes per cell, plus N x 224
+ * bytes for the pair-symmetric kernel.
  */
 int nbody_near_grid(const nbody_f4 *pos_xyzm, int64_t N, float eps2, const float lo[3], float h,
                     const int32_t dims[3], nbody_f4 *acc_out, float *pot_out,
                     hipStream_t stream);
+
+/* Near-field kernels of nbody_near_grid_kernel. */
+enum {
+    NBODY_NEAR_AUTO = 0,
+    NBODY_NEAR_ONE_SIDED = 1, /* every cell sums over its 27-cell neighbourhood (the nbody_p2p
+                                 kernel, the neighbourhood as 9 runs of 3 consecutive cells) */
+    NBODY_NEAR_PAIRS = 2      /* each unordered pair of neighbouring cells evaluated once by the
+                                 cell with the lower linear index and applied to both cells'
+                                 bodies (one distance, one rsq per two interactions, as in
+                                 NBODY_MODE_PAIRS); a cell's own pairs one-sided; every body's
+                                 14 partial sums (its cell's, and one per forward direction of
+                                 the cells below it) added in a fixed order */
+};
+
+/*
+ * nbody_near_grid_kernel - nbody_near_grid with the near-field kernel chosen by
+ * `kernel` (NBODY_NEAR_*; AUTO: pairs when the cells hold 96 to 2048 bodies on
+ * average and there are at least two cells per compute unit, else one-sided). Same definition and error bound; results of the two
+ * kernels differ in the last bits. NBODY_EINVAL for another value.
+ */
+int nbody_near_grid_kernel(const nbody_f4 *pos_xyzm, int64_t N, float eps2, const float lo[3],
+                           float h, const int32_t dims[3], int32_t kernel, nbody_f4 *acc_out,
+                           float *pot_out, hipStream_t stream);
 
 /* What nbody_near_tree built (host struct, filled on success). */
 typedef struct nbody_tree_stats {

@@ -318,3 +318,10 @@ def test_torch_conveniences_reject_bad_tensors(nb):
             nb.step(bad, bad, 1e-3, 1e-4)
         with pytest.raises(ValueError):
             nb.diagnostics(bad, bad, 1e-4)
+
+
+@pytest.mark.parametrize("kernel", [-1, 3, 100])
+def test_near_grid_kernel_rejects_unknown_kernel(nb, kernel):
+    rc = nb.nbody_near_grid_kernel(A, 16, 1e-4, (0.0, 0.0, 0.0), 1.0, (1, 1, 1), kernel, B, None,
+                                   stream=0, check=False)
+    assert rc == nb.NBODY_EINVAL and "kernel" in nb.nbody_last_error()

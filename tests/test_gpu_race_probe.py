@@ -36,6 +36,9 @@ def probe(nb):
     lib.nbody_step_plan.argtypes = [vp, vp, i64, f32, f32, i64, ctypes.POINTER(nb.nbody_plan), vp]
     lib.nbody_near_grid.argtypes = [vp, i64, f32, ctypes.POINTER(ctypes.c_float), f32,
                                     ctypes.POINTER(ctypes.c_int32), vp, vp, vp]
+    lib.nbody_near_grid_kernel.argtypes = [vp, i64, f32, ctypes.POINTER(ctypes.c_float), f32,
+                                           ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, vp,
+                                           vp, vp]
     lib.nbody_p2p.argtypes = [vp, i64, f32, vp, ctypes.c_int32, vp, vp, i64, vp, vp, vp]
     lib.nbody_last_error.restype = ctypes.c_char_p
     return lib
@@ -118,14 +121,17 @@ def test_probe_build_small_steps(nb, probe):
     assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])
 
 
+@pytest.mark.parametrize("kernel", [1, 2])
 @pytest.mark.parametrize("n,h,dims", [(20000, 1.0, (2, 2, 2)),
                                       (800000, 0.125, (16, 16, 16)),
                                       (100000, 0.125, (16, 16, 16))])
-def test_probe_build_chunk_near_field(nb, probe, n, h, dims):
-    """The near-field chunk kernel, whose four waves add their sums through a shared buffer:
-    eight large cells (2 x 2 x 2 grid, ~2500 bodies each: 42 workgroups per cell, each with
-    one or two 64-target chunks and many source tiles), 4096 cells of ~195 and of ~24 bodies
-    (64-target chunks, and source groups for small chunks)."""
+def test_probe_build_chunk_near_field(nb, probe, n, h, dims, kernel):
+    """The near-field kernels whose four waves add their sums through a shared buffer. The
+    one-sided chunk kernel (kernel 1): eight large cells (2 x 2 x 2 grid, ~2500 bodies each:
+    42 workgroups per cell, each with one or two 64-target chunks and many source tiles), 4096
+    cells of ~195 and of ~24 bodies (64-target chunks, and source groups for small chunks). The
+    pair-symmetric kernel (kernel 2): the same grids, i.e. five 512-body i-sets per large cell
+    with the block and sum rows reused between them, and one i-set of 1 to 5 rows per cell."""
     import torch
 
     pos_h, _ = workloads.random_bodies(n, seed=12)
@@ -136,15 +142,15 @@ def test_probe_build_chunk_near_field(nb, probe, n, h, dims):
         acc = torch.full((n, 4), 7.0, device="cuda")
         pot = torch.full((n,), 7.0, device="cuda")
         if which == "library":
-            nb.nbody_near_grid(pd, n, 1e-4, lo, h, dims, acc, pot)
+            nb.nbody_near_grid_kernel(pd, n, 1e-4, lo, h, dims, kernel, acc, pot)
         else:
-            rc = probe.nbody_near_grid(pd.data_ptr(), n, 1e-4, (ctypes.c_float * 3)(*lo), h,
-                                       (ctypes.c_int32 * 3)(*dims), acc.data_ptr(),
-                                       pot.data_ptr(), _stream())
+            rc = probe.nbody_near_grid_kernel(pd.data_ptr(), n, 1e-4, (ctypes.c_float * 3)(*lo),
+                                              h, (ctypes.c_int32 * 3)(*dims), kernel,
+                                              acc.data_ptr(), pot.data_ptr(), _stream())
             assert rc == 0, probe.nbody_last_error()
         torch.cuda.synchronize()
         outs.append((acc.cpu().numpy(), pot.cpu().numpy()))
-    _assert_same(outs, f"near grid, {dims} cells")
+    _assert_same(outs, f"near grid kernel {kernel}, {dims} cells")
 
 
 @pytest.mark.parametrize("n,ncell,per_list", [(3000, 150, 172), (12000, 150, 172),
