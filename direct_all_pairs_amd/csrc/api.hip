@@ -338,23 +338,28 @@ int64_t auto_passes(int64_t n, int band, int run, const DeviceFacts &dev, bool s
     return pairs_pass_scratch(n, band, run, nb, step) <= cap ? nb : 0;
 }
 
-// Items per pair workgroup (run length K): the longest power of two, up to
-// kMaxAutoRun, that still leaves at least kRunWorkgroupsPerCU workgroups per
-// compute unit. Measured round-robin on MI355X (whole calls): N = 2^20 in
-// 2048-body bands 203.1 ms at K = 1 and 8, 204.9 at 16, 207.9 at 32 (34 and 17
-// workgroups per CU); two Plummer spheres of 300,007 in 1024-body bands 17.24
-// ms at K = 1, 17.34 at 4, 17.57 at 8; 65,536 in 512-body bands 0.839 ms at
-// K = 1, 0.848 at 2. Coarser work per workgroup leaves the last ones unevenly
-// spread over the CUs.
+// Items per pair workgroup (run length K): the longest power of two up to
+// kMaxAutoRun whose shortest runs (K, or K / 4 where the last K band pairs of an
+// owner are split) hold at most 1/kRunTailShare of the items each resident
+// workgroup slot (four per CU) takes on average, so that the launch ends on
+// short workgroups. Measured round-robin on MI355X (whole calls): N = 2^20 in
+// 2048-body bands (128 items per slot) 208.4, 207.8, 208.3 and 209.7 ms at K = 8,
+// 16, 32 and 64 with the split tail (without it 32 had cost 2.4 %); N = 2^21 827.1,
+// 830.4 and 832.7 ms at K = 16, 32, 64; two Plummer spheres of 300,007 in 1024-body
+// bands (42 items per slot) 17.99, 18.09 and 18.83 ms at K = 1, 2 and 16 (17.34 ms
+// at 4 and 17.57 at 8 against 17.24 at 1 on another box); 65,536 in 512-body bands
+// (8 items per slot) 0.839 ms at K = 1, 0.848 at 2.
 constexpr int kMaxAutoRun = 32;
-constexpr int64_t kRunWorkgroupsPerCU = 64;
+constexpr int64_t kRunTailShare = 16;
 int auto_run(int64_t n, int band, const DeviceFacts &dev)
 {
     const int64_t nb = (n + band - 1) / band;
+    const int64_t per_slot = nb * (nb / 2 + 1) / (4 * (int64_t)dev.cus);
     int run = 1;
-    while (run < kMaxAutoRun &&
-           nb * (1 + nbk::pair_runs((int)nb, 2 * run)) >= kRunWorkgroupsPerCU * dev.cus)
-        run *= 2;
+    for (int k = 2; k <= kMaxAutoRun; k *= 2) {
+        const int64_t tail = nbk::run_split((int)nb, k) ? k / nbk::kRunSplit : k;
+        if (tail * kRunTailShare <= per_slot) run = k;
+    }
     return run;
 }
 

@@ -38,7 +38,7 @@ struct SmallArgs {
 // pair {X, X + d mod nb}, d in [1, nb/2], is item (X, d) of its owner band X
 // (for even nb the opposite pair d = nb/2 belongs only to the lower X); item
 // (X, 0) is band X against itself, one-sided. With D = nb/2 and run length K,
-// owner X's items d >= 1 form R = ceil(D / K) runs of K consecutive d, one
+// owner X's items d >= 1 form R runs of consecutive d (run_start below), one
 // workgroup each. Sums of a body of band x:
 //   own slots     k = 0 (its diagonal item), k = 1 + r (run r of owner x: its
 //                 band's sums over the run's items), at own[k * own_stride + i - own0];
@@ -54,7 +54,7 @@ struct PairsArgs {
     int nbands;               // nb
     int band0, band1;         // owner bands evaluated: [band0, band1) (all: 0, nb)
     int run;                  // K >= 1
-    int nruns;                // R = ceil(D / K) (0 when nb = 1)
+    int nruns;                // R = pair_runs(nb, K) (0 when nb = 1)
     float4 *own;
     long long own_stride;
     int own0;
@@ -63,8 +63,31 @@ struct PairsArgs {
     int partner_by_owner;     // 0: p = d - 1; 1: p = owner - band0
 };
 
-// Runs per owner band: R = ceil(floor(nb / 2) / K).
-__host__ __device__ inline int pair_runs(int nb, int run) { return (nb / 2 + run - 1) / run; }
+// Runs of an owner band's items d = 1 .. D (D = floor(nb / 2)): consecutive d in
+// runs of K, except that for K >= kRunSplitMin and D > K the last K values of d
+// form kRunSplit runs of K / kRunSplit, so that a launch ends on short
+// workgroups. Run r covers d in [1 + run_start(r), run_start(r + 1)].
+constexpr int kRunSplitMin = 16;
+constexpr int kRunSplit = 4;
+__host__ __device__ inline bool run_split(int nb, int run)
+{
+    return run >= kRunSplitMin && nb / 2 > run;
+}
+__host__ __device__ inline int pair_runs(int nb, int run)
+{
+    const int D = nb / 2;
+    if (!run_split(nb, run)) return (D + run - 1) / run;
+    return (D - run + run - 1) / run + kRunSplit;
+}
+__host__ __device__ inline int run_start(int r, int nb, int run)
+{
+    const int D = nb / 2;
+    if (!run_split(nb, run)) return r * run < D ? r * run : D;
+    const int head = (D - run + run - 1) / run;  // runs of K over d = 1 .. D - K
+    if (r <= head) return r * run < D - run ? r * run : D - run;
+    if (r >= head + kRunSplit) return D;  // the last run takes any remainder of K / kRunSplit
+    return D - run + (r - head) * (run / kRunSplit);
+}
 
 // Slots per body of the one-pass layout: 1 + R + floor(nb / 2).
 __host__ __device__ inline long long pair_slots(int nb, int run) { return 1 + pair_runs(nb, run) + nb / 2; }

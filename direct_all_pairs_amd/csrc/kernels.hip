@@ -722,11 +722,6 @@ __device__ __forceinline__ V &at_byte(void *base, int off)
     return *reinterpret_cast<V *>(static_cast<char *>(base) + off);
 }
 
-// Item {A, B}: band A's targets held in registers (their sums written to
-// outA[body - offA] after each i-set), band B walked in j-blocks. With SYM the
-// B side is added into the LDS accumulator jacc (kept across the items of a
-// run; the caller zeroes and stores it), or with a global accumulator into
-// outB[body - offB], which the first item of a run starts afresh.
 // One j-block pass of 64 steps: at step s lane l pairs its T targets with body
 // (l - s) mod 64 of the wave's block copy (byte row `row` of blk; jbody is the
 // lane's own body, the partner of step 0), and with SYM adds that body's sums
@@ -770,6 +765,11 @@ __device__ __forceinline__ void block_pass(void *blk, void *sum, int row, int la
     }
 }
 
+// Item {A, B}: band A's targets held in registers (their sums written to
+// outA[body - offA] after each i-set), band B walked in j-blocks. With SYM the
+// B side is added into the LDS accumulator jacc (kept across the items of a
+// run; the caller zeroes and stores it), or with a global accumulator into
+// outB[body - offB], which the first item of a run starts afresh.
 template <int T, int BD, bool POT, bool SYM>
 __device__ __forceinline__ void pairs_item(const PairsArgs &k, int A, int B, float4 *outA,
                                            long long offA, float4 *outB, long long offB,
@@ -942,8 +942,8 @@ __global__ void __launch_bounds__(256) accel_pairs(PairsArgs k)
         return;
     }
     const int r = (int)blockIdx.y - 1;
-    const int d0 = 1 + r * k.run;
-    const int d1 = min(nb / 2, d0 + k.run - 1);
+    const int d0 = 1 + run_start(r, nb, k.run);
+    const int d1 = run_start(r + 1, nb, k.run);
     if (!item_exists(X, d0, nb)) return;
     float4 *runslot = k.own + (size_t)(1 + r) * (size_t)k.own_stride;
     if constexpr (!kGlobalJacc<BD>) {
@@ -1032,7 +1032,7 @@ __device__ __forceinline__ void add_one(float4 &a, float4 &e, bool &started, con
 // can be empty).
 __device__ __forceinline__ int own_slots(int x, int nb, int run, int nruns)
 {
-    return 1 + nruns - ((nruns > 0 && !item_exists(x, 1 + (nruns - 1) * run, nb)) ? 1 : 0);
+    return 1 + nruns - ((nruns > 0 && !item_exists(x, 1 + run_start(nruns - 1, nb, run), nb)) ? 1 : 0);
 }
 
 // Partner slots d = 1 .. that band x's bodies hold: all D = nb/2 except, for

@@ -103,9 +103,9 @@ enum {
  *            chunk = band, bcast = LDS, wg = 256. Each workgroup evaluates `run`
  *            band pairs that share one band, whose sums it keeps on chip across
  *            them, so a body receives 1 + R + floor(nb / 2) partial sums with
- *            R = ceil(floor(nb / 2) / run). In one pass the scratch is that
- *            many records of N x 16 bytes (4.85 GB at N = 2^20 with 2048-body
- *            bands and run 8); when that would exceed 1/16 of device memory the
+ *            R the number of runs. In one pass the scratch is that
+ *            many records of N x 16 bytes (4.50 GB at N = 2^20 with 2048-body
+ *            bands and run 32); when that would exceed 1/16 of device memory the
  *            automatic plan evaluates the band pairs in several passes over
  *            band ranges, each pass's sums added into running totals, with
  *            scratch of about (splits / passes + 3) x N x 16 bytes.
@@ -118,9 +118,10 @@ enum {
  *            one while the full slot scratch fits, else the fewest that fit).
  *            Results with different pass counts differ in the last bits.
  *   run    - pair mode: band pairs per workgroup, 1 .. 65536 (0 = automatic:
- *            the longest power of two up to 32 that leaves at least 64
- *            workgroups per compute unit). Results with different run lengths
- *            differ in the last bits.
+ *            the longest power of two up to 32 that keeps the last workgroups of
+ *            the launch short; 32 at N = 2^20). From 16 on, the last `run` band
+ *            pairs of each band are split into four shorter runs. Results with
+ *            different run lengths differ in the last bits.
  * The plan is a pure function of (N, device compute units and memory), so
  * nbody_accel and nbody_step use the same one for the same N, with or without
  * the potential. */

@@ -273,7 +273,10 @@ def test_pairs_invariants(nb, band, tpl):
 RUN_CASES = [(4096, 512, 8, 1), (4096, 512, 8, 3), (4096, 512, 8, 4), (5000, 1024, 4, 2),
              (4615, 512, 8, 5), (4615, 512, 4, 2), (6144, 256, 4, 7), (6144, 256, 4, 11),
              (20000, 1024, 8, 64), (8192, 4096, 8, 2), (12290, 4096, 8, 1), (20000, 4096, 8, 3),
-             (3000, 2048, 8, 1), (2047, 256, 4, 1)]
+             (3000, 2048, 8, 1), (2047, 256, 4, 1),
+             # from K = 16 the last K band pairs of an owner run as four runs of K / 4 (K = 18:
+             # 4, 4, 4 and 6)
+             (40000, 512, 8, 16), (40000, 512, 8, 18), (70000, 1024, 8, 32), (20000, 256, 4, 17)]
 
 
 @pytest.mark.parametrize("n,band,tpl,run", RUN_CASES)
@@ -314,25 +317,28 @@ def test_pair_runs_in_passes_and_steps(nb, n, band, tpl, run, passes):
 
 
 def test_auto_run_lengths(nb):
-    """The automatic run length: the longest power of two up to 32 that leaves 64 workgroups
-    per compute unit (the MI355X has 256): one pair per workgroup while items are few, 8 at
-    N = 2^20 (289 slots of 16 bytes per body: 4.85 GB), 32 at 2^21 (529 slots, one pass)."""
+    """The automatic run length: the longest power of two up to 32 whose shortest runs (K, or
+    K / 4 with the split tail from K = 16) hold at most 1/16 of the items per resident
+    workgroup slot (four per compute unit): 32 at N = 2^20 (268 slots of 16 bytes per body:
+    4.50 GB) and 2^21 (one pass), 2 for two Plummer spheres of 300,007, 1 at 65,536."""
     import torch
 
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     for n in (8192, 65536, 300007, 1 << 20, 1 << 21, (1 << 22) + 12345):
         p = nb.nbody_plan_for(n)
         nbands = p.splits
-        wgs = lambda k: nbands * (1 + (nbands // 2 + k - 1) // k)  # noqa: E731
+        per_slot = nbands * (nbands // 2 + 1) // (4 * cus)
         want = 1
-        while want < 32 and wgs(2 * want) >= 64 * cus:
-            want *= 2
+        for k in (2, 4, 8, 16, 32):
+            tail = k // 4 if (k >= 16 and nbands // 2 > k) else k
+            if tail * 16 <= per_slot:
+                want = k
         assert p.run == want, (n, p.as_dict())
     if cus == 256:
         assert nb.nbody_plan_for(65536).run == 1 and nb.nbody_plan_for(300007).run == 2
         p = nb.nbody_plan_for(1 << 20)
-        assert p.run == 8 and p.passes == 1 and p.band == 2048, p.as_dict()
-        assert 1 + (256 + p.run - 1) // p.run + 256 == 289
+        assert p.run == 32 and p.passes == 1 and p.band == 2048, p.as_dict()
+        assert 1 + (7 + 4) + 256 == 268  # runs: seven of 32, then four of 8
         p = nb.nbody_plan_for(1 << 21)
         assert p.run == 32 and p.passes == 1, p.as_dict()
 
