@@ -227,7 +227,8 @@ hipError_t timed_launch(hipStream_t stream, F &&fn)
 
 constexpr int kMaxSplits = 4096;
 // nbody_near_grid chooses the pair-symmetric kernel for 96 to 2048 bodies per cell on
-// average and at least two cells per compute unit (it runs one workgroup per cell).
+// average and at least two cells per compute unit (it runs one workgroup per cell), while
+// its slots fit 1/16 of device memory (N up to ~86 million on MI355X).
 // Measured at N = 2^20 on D^3 grids (kernel time, one-sided -> pairs): D = 23 (86
 // per cell) 0.80 -> 0.84 ms, D = 22 (98) 0.86 -> 0.78, D = 16 (256) 2.0 -> 1.6, D = 12
 // (607) 4.4 -> 3.8, D = 8 (2048, 512 cells) 14.6 -> 12.6, D = 7 (3057, 343 cells)
@@ -1099,7 +1100,10 @@ int nbody_near_grid_kernel(const nbody_f4 *pos, int64_t N, float eps2, const flo
         DeviceFacts facts;
         rc = device_facts(dev, &facts);
         if (rc != NBODY_OK) return rc;
-        pairs = ncell >= kSymMinCellsPerCU * facts.cus;
+        // and while its slots (kSymSlots records per body) fit the pair mode's share of
+        // device memory; beyond that the one-sided kernel needs none
+        pairs = ncell >= kSymMinCellsPerCU * facts.cus &&
+                (size_t)nbk::kSymSlots * b16 <= facts.mem_bytes / kPairsScratchShare;
     }
     int end_bit = 1;
     while (end_bit < 32 && ((int64_t)1 << end_bit) < ncell) ++end_bit;

@@ -190,8 +190,9 @@ int nbody_step_plan(nbody_f4 *pos, nbody_f4 *vel, int64_t N, float dt, float eps
  * or split-j partial sums of larger N) comes from a static 128 MiB array
  * that each GPU holds, inside the library's code object, until the process
  * ends (looked up on a device's first call).
- *   Limit: the step plan's scratch must fit 128 MiB; for uniform bodies that
- *   is N <= 65536 (NBODY_EINVAL, with the bytes it would need, beyond it).
+ *   Limit: the step plan's scratch must fit 128 MiB; with the automatic plan
+ *   (a function of N) that is N <= 65027: at N = 65536 the pair slots take
+ *   129 x N x 16 bytes (NBODY_EINVAL, with the bytes it would need, beyond it).
  *   The array keeps the last call's contents; nothing in it needs to start at
  *   zero (every entry is written before it is read within a step). All calls
  *   on one GPU share it: calls that overlap in time on that GPU (on different
@@ -320,7 +321,8 @@ enum {
 /*
  * nbody_near_grid_kernel - nbody_near_grid with the near-field kernel chosen by
  * `kernel` (NBODY_NEAR_*; AUTO: pairs when the cells hold 96 to 2048 bodies on
- * average and there are at least two cells per compute unit, else one-sided). Same definition and error bound; results of the two
+ * average, there are at least two cells per compute unit and its N x 224 bytes of
+ * scratch fit 1/16 of device memory, else one-sided). Same definition and error bound; results of the two
  * kernels differ in the last bits. NBODY_EINVAL for another value.
  */
 int nbody_near_grid_kernel(const nbody_f4 *pos_xyzm, int64_t N, float eps2, const float lo[3],

@@ -77,6 +77,42 @@ def test_noalloc_rejects_beyond_static_scratch(nb):
     assert np.array_equal(pos.cpu().numpy(), pos_h) and np.array_equal(vel.cpu().numpy(), vel_h)
 
 
+def _pair_step_bytes(nb, n):
+    """Scratch of the automatic plan's pair step: 1 + R + D slots of N records (D = nb/2, R runs
+    of the plan's length, the last run of 16 or more split into four)."""
+    p = nb.nbody_plan_for(n)
+    assert p.mode == nb.MODE_PAIRS and p.passes == 1, p.as_dict()
+    d, k = p.splits // 2, p.run
+    r = (-(-(d - k) // k) + 4) if (k >= 16 and d > k) else -(-d // k)
+    return (1 + r + d) * n * 16
+
+
+@pytest.mark.parametrize("n", [65027, 65028])
+def test_noalloc_limit_at_the_boundary(nb, n):
+    """Just below and just above the 128 MiB array (N = 65027: 129 slots of N records take
+    134,215,728 of its 134,217,728 bytes; N = 65028 needs 64 bytes more): the first runs a step
+    equal to nbody_step bit for bit, the second is rejected before anything is enqueued."""
+    import torch
+
+    need = _pair_step_bytes(nb, n)
+    fits = need <= 128 * 1024 * 1024
+    assert fits == (n == 65027), need
+    pos_h, vel_h = workloads.random_bodies(n, seed=13)
+    pos, vel = to_dev(pos_h), to_dev(vel_h)
+    rc = nb.nbody_step_noalloc(pos, vel, n, float(DT), float(EPS2), 1, check=False)
+    torch.cuda.synchronize()
+    if not fits:
+        assert rc == nb.NBODY_EINVAL and "static" in nb.nbody_last_error()
+        assert np.array_equal(pos.cpu().numpy(), pos_h) and np.array_equal(vel.cpu().numpy(), vel_h)
+        return
+    assert rc == 0, nb.nbody_last_error()
+    p2, v2 = to_dev(pos_h), to_dev(vel_h)
+    nb.nbody_step(p2, v2, n, float(DT), float(EPS2), 1)
+    torch.cuda.synchronize()
+    assert np.array_equal(pos.cpu().numpy(), p2.cpu().numpy())
+    assert np.array_equal(vel.cpu().numpy(), v2.cpu().numpy())
+
+
 def test_noalloc_takes_no_device_memory(nb):
     """After the library's cached scratch is released, a noalloc call leaves the device's
     free memory where it was, while nbody_step of the same size takes its slot array."""
