@@ -128,3 +128,34 @@ def test_pairs_and_one_sided_agree_and_auto(nb):
     assert_accel_parity(a1, p1, ref, idx=idx, what="one-sided 16^3")
     a3, p3 = near(nb, w.pos, w.eps2, *args, nb.NEAR_PAIRS)
     assert np.array_equal(a3, a2) and np.array_equal(p3, p2)
+
+
+@pytest.mark.parametrize("bad", ["nan", "inf"])
+def test_pairs_non_finite_body(nb, bad):
+    """A non-finite coordinate gives unspecified values but a normal call through the pair
+    kernel: every row is written (w = 0, no canary left); with a NaN coordinate (binned to the
+    grid's low face on its axis) the bodies in the octant away from that corner stay finite; the
+    next call on finite bodies is unaffected."""
+    import torch
+
+    import oracle
+
+    n = 8000
+    pos, _ = workloads.random_bodies(n, seed=19)
+    bad_pos = pos.copy()
+    bad_pos[5, 0] = np.nan if bad == "nan" else np.inf
+    args = ((-1.0, -1.0, -1.0), 0.25, (8, 8, 8))
+    print(f"[near pairs] non-finite {bad}", flush=True)
+    pd = to_dev(bad_pos)
+    acc = torch.full((n, 4), 7.0, device="cuda")
+    pot = torch.full((n,), 7.0, device="cuda")
+    nb.nbody_near_grid_kernel(pd, n, 1e-4, *args, nb.NEAR_PAIRS, acc, pot)
+    torch.cuda.synchronize()
+    a, p = acc.cpu().numpy(), pot.cpu().numpy()
+    assert np.all(a[:, 3] == 0.0) and not np.any(p == 7.0)
+    if bad == "nan":
+        far = np.all(bad_pos[:, :3] > 0.0, axis=1)
+        assert far.sum() > 500 and np.all(np.isfinite(a[far])) and np.all(np.isfinite(p[far]))
+    a2, p2 = near(nb, pos, 1e-4, *args, nb.NEAR_PAIRS)
+    assert_accel_parity(a2, p2, oracle.near_grid(pos, np.float32(1e-4), *args),
+                        what="pairs after a non-finite call")
