@@ -2,7 +2,8 @@
 hands back only after first writing NaN into it, so a missing or misplaced barrier shows up
 as NaN or changed outputs. With the barriers in place its results must equal the library's
 bit for bit, with no NaN, for tile counts and sizes at tile boundaries +- 1 in every mode that
-shares LDS between waves (tiles, small N, pair bands, the near-field chunk kernel)."""
+shares LDS between waves (tiles, small N, pair bands and runs of band pairs, the near-field
+kernels)."""
 
 from __future__ import annotations
 
@@ -82,6 +83,10 @@ PROBE_CASES = (
     + [dict(mode="small", tpl=tw) for tw in (4, 8, 16, 32)]
     + [dict(mode="pairs", band=b, tpl=t)
        for b, t in ((256, 4), (512, 4), (512, 8), (1024, 4), (1024, 8), (2048, 8), (4096, 8))]
+    # runs of several band pairs that keep the walked band's sums in LDS (or, with 4096-body
+    # bands, in its global slot) across their items; run 16 with a split tail on 40 bands
+    + [dict(mode="pairs", band=b, tpl=t, run=r)
+       for b, t, r in ((256, 4, 2), (512, 8, 2), (2048, 8, 2), (4096, 8, 2), (256, 4, 16))]
 )
 
 
@@ -90,6 +95,8 @@ def _sizes(plan):
         return (2047, 2049, 3073)
     tile = plan.get("band") or plan["wg"]
     k = 4 if plan.get("mode") == "pairs" else 6
+    if plan.get("run", 0) >= 16:
+        k = 40  # 20 band pairs per owner band: one run of 4, then the last 16 split into four
     return (k * tile - 1, k * tile + 1)
 
 
