@@ -2018,15 +2018,23 @@ __global__ void __launch_bounds__(256) sym_finish_kernel(const float4 *__restric
     if (i >= (unsigned)n) return;
     const int c = (int)cell_of[i];
     const int cx = c % dx, cy = (c / dx) % dy, cz = c / (dx * dy);
-    float4 a = part[i], e = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-#pragma unroll 1
+    // which slots exist, then all their loads, then the additions in slot order
+    bool has[kSymDirs];
+#pragma unroll
     for (int q = 0; q < kSymDirs; ++q) {
         const int ox = cx - sym_dir_dx(q), oy = cy - sym_dir_dy(q), oz = cz - sym_dir_dz(q);
-        if (ox < 0 || ox >= dx || oy < 0 || oy >= dy || oz < 0) continue;
-        const int o = (oz * dy + oy) * dx + ox;
-        if (cell_start[o + 1] <= cell_start[o]) continue;
-        two_sum_add4(a, e, part[(size_t)(1 + q) * (size_t)n + i]);
+        const bool in = ox >= 0 && ox < dx && oy >= 0 && oy < dy && oz >= 0;
+        const int o = in ? (oz * dy + oy) * dx + ox : 0;
+        has[q] = in && cell_start[o + 1] > cell_start[o];
     }
+    float4 v[kSymDirs];
+#pragma unroll
+    for (int q = 0; q < kSymDirs; ++q)
+        v[q] = has[q] ? part[(size_t)(1 + q) * (size_t)n + i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float4 a = part[i], e = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+    for (int q = 0; q < kSymDirs; ++q)
+        if (has[q]) two_sum_add4(a, e, v[q]);
     const int r = out_index ? out_index[i] : (int)i;
     acc_out[r] = make_float4(a.x + e.x, a.y + e.y, a.z + e.z, 0.0f);
     if (pot_out) pot_out[r] = -(a.w + e.w);
