@@ -93,3 +93,42 @@ def test_near_roofline_counts_issued_flops():
     assert abs(r["achieved"] - 2.1) < 1e-9 and r["unit"] == "TFLOP/s"
     assert abs(r["frac"] - round(2.1 / bench.FP32_VECTOR_PEAK_TFLOPS, 4)) < 1e-12
     assert bench.near_roofline(10 ** 9, 10.0, False, "p2p")["flops_per_launch"] == 19 * 10 ** 9
+
+
+@pytest.mark.parametrize("dims,n,seed", [((3, 4, 5), 700, 1), ((1, 1, 1), 50, 2), ((6, 2, 1), 300, 3)])
+def test_near_grid_pair_units_count_each_neighbour_pair_once(dims, n, seed):
+    """The pair-symmetric near grid's units against brute force over the bodies: unordered
+    pairs {i, j}, i != j, in neighbouring cells (cells differing by at most one per axis, same
+    cell excluded), and one-sided self terms (ordered pairs in one cell, i = j included); twice
+    the first plus the second is the one-sided near field's term count."""
+    import numpy as np
+
+    rng = np.random.default_rng(seed)
+    lo, h = (-1.0, -1.0, -1.0), 0.4
+    pos = np.zeros((n, 4), np.float32)
+    pos[:, :3] = rng.uniform(-1.2, -1.0 + h * max(dims) + 0.2, size=(n, 3))
+    pos[:, 3] = 1.0
+    x = pos[:, :3].astype(np.float32)
+    k = np.floor((x - np.asarray(lo, np.float32)) * (np.float32(1.0) / np.float32(h)))
+    k = np.clip(k, 0, np.asarray(dims) - 1).astype(np.int64)
+    cell = (k[:, 2] * dims[1] + k[:, 1]) * dims[0] + k[:, 0]
+    pairs = self_terms = 0
+    for i in range(n):
+        for j in range(n):
+            if cell[i] == cell[j]:
+                self_terms += 1
+            elif i < j and np.all(np.abs(k[i] - k[j]) <= 1):
+                pairs += 1
+    got = bench.near_grid_pair_units(pos, lo, h, dims)
+    assert got == (pairs, self_terms)
+    assert bench.near_grid_terms(pos, lo, h, dims) == 2 * pairs + self_terms
+
+
+def test_near_roofline_pair_units():
+    """The pair kernel's near-field roofline: 30 flops per unordered pair and 21 per self
+    term with the potential (26 and 19 without)."""
+    r = bench.near_roofline(0, 10.0, True, "p2p_sym", (10 ** 9, 10 ** 8))
+    assert r["flops_per_launch"] == 30 * 10 ** 9 + 21 * 10 ** 8
+    assert r["units_per_launch"] == {"pairs": 10 ** 9, "one_sided_terms": 10 ** 8}
+    r0 = bench.near_roofline(0, 10.0, False, "p2p_sym", (10 ** 9, 10 ** 8))
+    assert r0["flops_per_launch"] == 26 * 10 ** 9 + 19 * 10 ** 8
