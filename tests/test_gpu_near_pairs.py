@@ -159,3 +159,21 @@ def test_pairs_non_finite_body(nb, bad):
     a2, p2 = near(nb, pos, 1e-4, *args, nb.NEAR_PAIRS)
     assert_accel_parity(a2, p2, oracle.near_grid(pos, np.float32(1e-4), *args),
                         what="pairs after a non-finite call")
+
+
+def test_pairs_plummer_dense_core(nb):
+    """The Plummer sphere of 65,536 bodies on a 16^3 grid of side 0.25 (outliers clamped into
+    the boundary cells): the core cells hold thousands of bodies (several 512-body i-sets whose
+    forward bodies' sums are added to in place), most outer cells a few; sampled targets in the
+    core, the outliers and at random against the grid definition."""
+    import oracle
+
+    w = workloads.make("plummer65536")
+    args = ((-2.0, -2.0, -2.0), 0.25, (16, 16, 16))
+    print("[near pairs] plummer65536 16^3", flush=True)
+    acc, pot = near(nb, w.pos, w.eps2, *args, nb.NEAR_PAIRS)
+    r = np.linalg.norm(w.pos[:, :3], axis=1)
+    idx = np.unique(np.concatenate([np.argsort(r)[:300], np.argsort(r)[-200:],
+                                    np.random.default_rng(5).integers(0, w.n, 600)]))
+    ref = oracle.near_grid(w.pos, w.eps2, *args, targets=idx)
+    assert_accel_parity(acc, pot, ref, idx=idx, what="pairs plummer near grid")

@@ -316,6 +316,26 @@ def test_pair_runs_in_passes_and_steps(nb, n, band, tpl, run, passes):
         assert np.array_equal(xk, xs) and np.array_equal(vk, vs), sp
 
 
+def test_pair_runs_two_spheres_full_size(nb):
+    """The two-sphere workload (N = 300,007, 293 bands of 1024) with runs of 16 band pairs, the
+    last 16 of each band split into four runs of 4: one evaluation against the oracle on
+    sampled targets (both ends, band edges, random), and one Euler step in the same plan within
+    the single-step bound."""
+    import oracle
+
+    w = workloads.make("two_plummer300007")
+    n = w.n
+    plan = dict(mode="pairs", band=1024, tpl=8, run=16)
+    acc, pot = gpu_accel(w.pos, w.eps2, pot=True, plan=plan)
+    rng = np.random.default_rng(16)
+    idx = np.unique(np.concatenate([rng.integers(0, n, 300), [0, n - 1], np.arange(1023, n, 1024 * 37),
+                                    np.arange(1024, n, 1024 * 41)]))
+    ref = oracle.accel(w.pos, w.eps2, targets=idx)
+    assert_accel_parity(acc, pot, ref, idx=idx, what="two spheres, runs of 16")
+    x1, v1 = gpu_step(w.pos, w.vel, w.dt, w.eps2, 1, plan=plan)
+    assert_step_parity(w.pos, w.vel, x1, v1, w.dt, ref, idx=idx, what="two spheres step, runs of 16")
+
+
 def test_auto_run_lengths(nb):
     """The automatic run length: the longest power of two up to 32 whose shortest runs (K, or
     K / 4 with the split tail from K = 16) hold at most 1/16 of the items per resident
