@@ -444,10 +444,13 @@ def near_grid_bench(nb, w, pos, args) -> int:
     n = w.n
     kernel = {"auto": nb.NEAR_AUTO, "one-sided": nb.NEAR_ONE_SIDED,
               "pairs": nb.NEAR_PAIRS}[args.near_kernel]
-    if kernel == nb.NEAR_AUTO:  # the library's rule: pairs from 96 to 2048 bodies per cell
-        cus = torch.cuda.get_device_properties(pos.device).multi_processor_count
-        kernel = (nb.NEAR_PAIRS if 96 * d ** 3 <= n <= 2048 * d ** 3 and d ** 3 >= 2 * cus
-                  else nb.NEAR_ONE_SIDED)
+    if kernel == nb.NEAR_AUTO:
+        # the library's rule: pairs from 96 to 2048 bodies per cell, at least two cells per
+        # compute unit, and its 14 slots of N records within 1/16 of device memory
+        props = torch.cuda.get_device_properties(pos.device)
+        kernel = (nb.NEAR_PAIRS if 96 * d ** 3 <= n <= 2048 * d ** 3
+                  and d ** 3 >= 2 * props.multi_processor_count
+                  and 14 * 16 * n <= props.total_memory // 16 else nb.NEAR_ONE_SIDED)
     acc = torch.empty_like(pos)
     pot = torch.empty(n, dtype=torch.float32, device=pos.device)
     stream = torch.cuda.current_stream()
