@@ -2,6 +2,7 @@
 // planning, the cached split-j scratch area and the step loop.
 #include <hip/hip_runtime.h>
 
+#include <array>
 #include <cmath>
 #include <cfloat>
 #include <cstdarg>
@@ -11,6 +12,7 @@
 #include <map>
 #include <mutex>
 #include <string>
+#include <tuple>
 #include <tuple>
 #include <utility>
 
@@ -146,6 +148,75 @@ int static_scratch(int dev, void **out)
     g_static_scratch[dev] = p;
     *out = p;
     return NBODY_OK;
+}
+
+// ------------------------------------------------------------ near-tree graphs
+// A near-tree call launches about fifty kernels of a few microseconds each, so past
+// the first sort passes the GPU waits on the host's launches (~160 us of a 950 us
+// call at N = 2^20). The kernels and arguments of its build up to the leaf-count wait
+// are fixed by (N, node size, positions, scratch block), those of the list passes
+// after it by (leaf count, table level, kept entries, list capacity, scratch blocks).
+// The second call with the same key captures that sequence into a graph on a library
+// stream and later ones replay it on the caller's stream; a first call launches the
+// kernels directly, so one-off calls pay no capture and the replays can be checked
+// against it. Under g_enqueue. Every entry's last replay has finished when the next
+// call takes the lock for the build phase (the call waits for it); list-phase
+// entries may still run, so replacing any entry first waits for the device.
+struct TreeGraphKey {
+    int dev, phase;
+    hipStream_t stream;
+    std::array<int64_t, 6> v;
+    std::array<const void *, 6> p;
+    bool operator<(const TreeGraphKey &o) const
+    {
+        return std::tie(dev, phase, stream, v, p) < std::tie(o.dev, o.phase, o.stream, o.v, o.p);
+    }
+};
+struct TreeGraph {
+    int seen = 0;
+    hipGraphExec_t exec = nullptr;
+};
+std::map<TreeGraphKey, TreeGraph> g_tree_graphs;
+std::map<int, hipStream_t> g_capture_stream;  // per device, default priority
+constexpr size_t kTreeGraphMax = 16;
+
+int drop_tree_graphs()
+{
+    if (g_tree_graphs.empty()) return NBODY_OK;
+    hipError_t e = hipDeviceSynchronize();
+    for (auto &kv : g_tree_graphs)
+        if (kv.second.exec) hipGraphExecDestroy(kv.second.exec);
+    g_tree_graphs.clear();
+    return e == hipSuccess ? NBODY_OK : hip_fail(e, "hipDeviceSynchronize (tree graphs)");
+}
+
+template <typename F>
+hipError_t run_graphed(const TreeGraphKey &key, hipStream_t stream, F &&enqueue)
+{
+    if (g_tree_graphs.size() >= kTreeGraphMax && g_tree_graphs.find(key) == g_tree_graphs.end())
+        if (drop_tree_graphs() != NBODY_OK) return hipErrorUnknown;
+    TreeGraph &g = g_tree_graphs[key];
+    if (g.exec) return hipGraphLaunch(g.exec, stream);
+    if (g.seen++ == 0) return enqueue(stream);
+    hipStream_t &cs = g_capture_stream[key.dev];
+    hipError_t e = hipSuccess;
+    if (!cs) e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) return e;
+    const hipError_t le = enqueue(cs);
+    hipGraph_t graph = nullptr;
+    e = hipStreamEndCapture(cs, &graph);
+    if (le != hipSuccess || e != hipSuccess) {
+        if (graph) hipGraphDestroy(graph);
+        return le != hipSuccess ? le : e;
+    }
+    e = hipGraphInstantiate(&g.exec, graph, nullptr, nullptr, 0);
+    hipGraphDestroy(graph);
+    if (e != hipSuccess) {
+        g.exec = nullptr;
+        return e;
+    }
+    return hipGraphLaunch(g.exec, stream);
 }
 
 // While set (by nbody_step_noalloc, for the length of its enqueueing), scratch_get
@@ -1202,14 +1273,19 @@ int nbody_near_tree(const nbody_f4 *pos, int64_t N, float eps2, int64_t leaf_siz
     void *sort_temp = b + off[13], *scan_temp = b + off[14];
     float *bounds_temp = (float *)(b + off[15]);
     int host[nbk::kTreeCounters] = {0, 0, 0, 0, 0, 0};
-    e = nbk::launch_tree_frame((const float4 *)pos, n, bounds_temp, frame, counters, stream);
-    if (e == hipSuccess) e = nbk::launch_tree_keys((const float4 *)pos, n, frame, keys, idx, stream);
-    if (e == hipSuccess) e = nbk::sort_pairs64(sort_temp, keys, skeys, idx, perm, n, 63, stream);
-    if (e == hipSuccess) e = nbk::launch_gather((const float4 *)pos, perm, n, spos, stream);
-    if (e == hipSuccess) e = nbk::launch_tree_levels(skeys, n, S, level, ids, stream);
-    if (e == hipSuccess) e = nbk::scan_exclusive(ids, n, counters, scan_temp, stream);
-    if (e == hipSuccess)
-        e = nbk::launch_tree_leaves(skeys, level, ids, n, start, leaf_key, leaf_box, stream);
+    auto build = [&](hipStream_t s) {
+        hipError_t x = nbk::launch_tree_frame((const float4 *)pos, n, bounds_temp, frame, counters, s);
+        if (x == hipSuccess) x = nbk::launch_tree_keys((const float4 *)pos, n, frame, keys, idx, s);
+        if (x == hipSuccess) x = nbk::sort_pairs64(sort_temp, keys, skeys, idx, perm, n, 63, s);
+        if (x == hipSuccess) x = nbk::launch_gather((const float4 *)pos, perm, n, spos, s);
+        if (x == hipSuccess) x = nbk::launch_tree_levels(skeys, n, S, level, ids, s);
+        if (x == hipSuccess) x = nbk::scan_exclusive(ids, n, counters, scan_temp, s);
+        if (x == hipSuccess)
+            x = nbk::launch_tree_leaves(skeys, level, ids, n, start, leaf_key, leaf_box, s);
+        return x;
+    };
+    e = run_graphed(TreeGraphKey{dev, 0, stream, {n, S, 0, 0, 0, 0}, {pos, ws, nullptr, nullptr, nullptr, nullptr}},
+                    stream, build);
     // first wait: the number of leaves sizes the list counts
     if (e == hipSuccess) e = hipMemcpyAsync(host, counters, 4, hipMemcpyDeviceToHost, stream);
     if (e == hipSuccess) e = hipStreamSynchronize(stream);
@@ -1242,12 +1318,14 @@ int nbody_near_tree(const nbody_f4 *pos, int64_t N, float eps2, int64_t leaf_siz
     void *scan_temp1 = b1 + o1[2], *wg_totals = b1 + o1[3];
     int *keep = keep_cap > 0 ? (int *)(b1 + o1[4]) : nullptr;
     const nbk::TreeLeaves lv{leaf_key, leaf_box, table, start, nleaf, lt};
-    e = nbk::launch_tree_table(leaf_key, counters, lt, table, stream);
-    if (e == hipSuccess)
-        e = nbk::launch_tree_lists(lv, counters, wg_totals, cnt, nullptr, nullptr, 0, nullptr,
-                                   keep, keep_cap, stream);
-    if (e == hipSuccess) e = nbk::scan_exclusive(cnt, parts, counters + 1, scan_temp1, stream);
-    if (e != hipSuccess) return hip_fail(e, "near-tree lists");
+    auto count_lists = [&](hipStream_t s) {
+        hipError_t x = nbk::launch_tree_table(leaf_key, counters, lt, table, s);
+        if (x == hipSuccess)
+            x = nbk::launch_tree_lists(lv, counters, wg_totals, cnt, nullptr, nullptr, 0, nullptr,
+                                       keep, keep_cap, s);
+        if (x == hipSuccess) x = nbk::scan_exclusive(cnt, parts, counters + 1, scan_temp1, s);
+        return x;
+    };
     // A leaf meets at most 27 leaves no smaller than itself (each holds a different one of
     // the 27 cells of its level around it). A leaf may meet any number of smaller ones, but
     // each such pair is also a pair of the smaller leaf with a larger one, of which that
@@ -1271,17 +1349,34 @@ int nbody_near_tree(const nbody_f4 *pos, int64_t N, float eps2, int64_t leaf_siz
         return NBODY_OK;
     };
     long long cap = bound;
+    void *lw = nullptr;
+    int *list = nullptr;
+    auto fill_lists = [&](hipStream_t s) {
+        return nbk::launch_tree_lists(lv, counters, nullptr, nullptr, cnt, list, (int)cap, list_off,
+                                      keep, keep_cap, s);
+    };
     if (bound > INT32_MAX) {
+        // the lists' true length sizes their scratch: a second wait, no graph
+        e = count_lists(stream);
+        if (e != hipSuccess) return hip_fail(e, "near-tree lists");
         rc = read_totals();
         if (rc != NBODY_OK) return rc;
         cap = (long long)nlist;
+        rc = scratch_get(dev, stream, ((size_t)cap + 1) * 4, &lw, 2);
+        if (rc != NBODY_OK) return rc;
+        list = (int *)lw;
+        e = fill_lists(stream);
+    } else {
+        rc = scratch_get(dev, stream, ((size_t)cap + 1) * 4, &lw, 2);
+        if (rc != NBODY_OK) return rc;
+        list = (int *)lw;
+        e = run_graphed(TreeGraphKey{dev, 1, stream, {n, nleaf, lt, keep_cap, cap, S},
+                                     {ws, ws1, lw, nullptr, nullptr, nullptr}},
+                        stream, [&](hipStream_t s) {
+                            hipError_t x = count_lists(s);
+                            return x == hipSuccess ? fill_lists(s) : x;
+                        });
     }
-    void *lw = nullptr;
-    rc = scratch_get(dev, stream, ((size_t)cap + 1) * 4, &lw, 2);
-    if (rc != NBODY_OK) return rc;
-    int *list = (int *)lw;
-    e = nbk::launch_tree_lists(lv, counters, nullptr, nullptr, cnt, list, (int)cap, list_off,
-                               keep, keep_cap, stream);
     if (e == hipSuccess) {
         nbk::P2PArgs a{spos, n, eps2, start, nleaf, list_off, list, cap, (float4 *)acc_out,
                        pot_out, perm};
@@ -1377,8 +1472,8 @@ const char *nbody_last_error(void) { return g_err.c_str(); }
 int nbody_release_workspace(void)
 {
     EnqueueLock el(g_enqueue);
+    int rc = drop_tree_graphs();  // they hold scratch addresses
     std::lock_guard<std::mutex> lk(g_mu);
-    int rc = NBODY_OK;
     for (auto &kv : g_scratch) {
         if (kv.second.ptr) {
             hipError_t e = hipFree(kv.second.ptr);

@@ -284,3 +284,59 @@ def test_near_tree_permuted_input(nb):
     inv = np.empty_like(perm)
     inv[perm] = np.arange(4000)
     assert_accel_parity(acc[inv], pot[inv], oracle.near_tree(pos, 1e-4, 16), what="permuted")
+
+
+@pytest.mark.parametrize("with_stats", [False, True])
+def test_near_tree_graph_replays_equal_the_first_call(nb, with_stats):
+    """Repeated calls with the same buffers: the first launches the build and list passes
+    directly, the second captures them into graphs, later ones replay them. Five calls, with
+    other library work (a grid near field, an all-pairs evaluation) and a synchronization
+    between them, all equal the first bit for bit, and it agrees with the oracle; new positions
+    written into the same buffer replay to the same bits as a first call on another buffer
+    (the graphs read the buffers' current contents)."""
+    import torch
+
+    import oracle
+
+    n, leaf, eps2 = 20000, 32, np.float32(1e-4)
+    pos, _ = workloads.random_bodies(n, seed=77)
+    other, _ = workloads.random_bodies(4000, seed=78)
+    pd, od = to_dev(pos), to_dev(other)
+    acc = torch.empty((n, 4), device="cuda")
+    pot = torch.empty((n,), device="cuda")
+    oa = torch.empty((4000, 4), device="cuda")
+    op = torch.empty((4000,), device="cuda")
+    nb.nbody_release_workspace()
+    print(f"[tree] graph replays, stats={with_stats}", flush=True)
+    runs = []
+    for k in range(5):
+        acc.fill_(np.nan)
+        pot.fill_(np.nan)
+        st = nb.nbody_tree_stats() if with_stats else None
+        nb.nbody_near_tree(pd, n, float(eps2), leaf, acc, pot, st)
+        torch.cuda.synchronize()
+        runs.append((acc.cpu().numpy().copy(), pot.cpu().numpy().copy(),
+                     st.as_dict() if st is not None else None))
+        nb.nbody_near_grid(od, 4000, float(eps2), (-1.0, -1.0, -1.0), 0.5, (4, 4, 4), oa, op)
+        nb.nbody_accel(od, 4000, float(eps2), oa, op)
+        torch.cuda.synchronize()
+    for a, p, st in runs[1:]:
+        assert np.array_equal(a, runs[0][0]) and np.array_equal(p, runs[0][1])
+        assert st == runs[0][2]
+    idx = np.unique(np.random.default_rng(9).integers(0, n, 500))
+    assert_accel_parity(runs[0][0], runs[0][1], oracle.near_tree(pos, eps2, leaf, targets=idx),
+                        idx=idx, what="tree, first call")
+    # new contents, same buffer (a replay) against a first call on a fresh buffer
+    pos2, _ = workloads.random_bodies(n, seed=79)
+    pd.copy_(torch.from_numpy(pos2).cuda())
+    nb.nbody_near_tree(pd, n, float(eps2), leaf, acc, pot, None)
+    fresh = to_dev(pos2)
+    acc2 = torch.empty((n, 4), device="cuda")
+    pot2 = torch.empty((n,), device="cuda")
+    nb.nbody_near_tree(fresh, n, float(eps2), leaf, acc2, pot2, None)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), acc2.cpu().numpy())
+    assert np.array_equal(pot.cpu().numpy(), pot2.cpu().numpy())
+    assert_accel_parity(acc.cpu().numpy(), pot.cpu().numpy(),
+                        oracle.near_tree(pos2, eps2, leaf, targets=idx), idx=idx,
+                        what="tree, replay on new positions")
