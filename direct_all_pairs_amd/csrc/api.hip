@@ -180,10 +180,23 @@ std::map<TreeGraphKey, TreeGraph> g_tree_graphs;
 std::map<int, hipStream_t> g_capture_stream;  // per device, default priority
 constexpr size_t kTreeGraphMax = 16;
 
+// Waits for every device that holds a cached graph (a replay may still run there), then
+// destroys them all; the caller's current device is restored.
 int drop_tree_graphs()
 {
     if (g_tree_graphs.empty()) return NBODY_OK;
-    hipError_t e = hipDeviceSynchronize();
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    int last = -1;
+    for (auto &kv : g_tree_graphs) {  // ordered by device first
+        if (kv.first.dev == last) continue;
+        last = kv.first.dev;
+        hipError_t x = hipSetDevice(last);
+        if (x == hipSuccess) x = hipDeviceSynchronize();
+        if (e == hipSuccess) e = x;
+    }
+    const hipError_t r = hipSetDevice(cur);
+    if (e == hipSuccess) e = r;
     for (auto &kv : g_tree_graphs)
         if (kv.second.exec) hipGraphExecDestroy(kv.second.exec);
     g_tree_graphs.clear();
