@@ -343,11 +343,11 @@ typedef struct nbody_tree_stats {
  * nearby bodies). The pages do not fix the tree; this one is, in float32:
  *   root cube: corner lo_d = the smallest coordinate d of any body, side = the
  *     largest extent over the three axes (1 when all bodies coincide);
- *   body i's cell at level 10 per axis: clamp(floor((x_d - lo_d) * (1024 / side)),
- *     0, 1023); its 30-bit Morton key has bit 3b + d equal to bit b of that cell;
- *   node (L, p), L = 0 .. 10: the bodies whose key shifted right by 3 (10 - L) is p;
+ *   body i's cell at level 21 per axis: clamp(floor((x_d - lo_d) * (2^21 / side)),
+ *     0, 2^21 - 1); its 63-bit Morton key has bit 3b + d equal to bit b of that cell;
+ *   node (L, p), L = 0 .. 21: the bodies whose key shifted right by 3 (21 - L) is p;
  *   leaf of a body: the node on its path with the smallest L holding at most
- *     leaf_size bodies (its level-10 node when none does);
+ *     leaf_size bodies (its level-21 node when none does);
  *   body i gets the sum over every body j whose leaf's closed cube meets the closed
  *     cube of i's leaf (a shared face, edge or corner counts; j = i included).
  * The library sorts the bodies by key (stable), finds the leaves and their lists on
@@ -361,6 +361,9 @@ typedef struct nbody_tree_stats {
  * 2^31 - 1 list entries (possible only with over 40 million leaves) is EINVAL.
  * Scratch: ~N x 100 bytes + ~300 bytes per leaf, plus the lists' first entries kept
  * between the two list passes (up to 3.5 KB per leaf, at most 256 MiB).
+ * From the second call with the same N, leaf_size, positions pointer and stream, the
+ * build and the list passes are replayed from cached HIP graphs (same results);
+ * nbody_release_workspace destroys them.
  */
 int nbody_near_tree(const nbody_f4 *pos_xyzm, int64_t N, float eps2, int64_t leaf_size,
                     nbody_f4 *acc_out, float *pot_out, nbody_tree_stats *stats,
@@ -421,8 +424,9 @@ int nbody_time_kernel(hipEvent_t start, hipEvent_t stop);
 /* Message describing the last non-OK return on the calling thread ("" if none). */
 const char *nbody_last_error(void);
 
-/* Frees every cached scratch area of the calling process (synchronises the
- * devices that own them). Later calls allocate again on demand. */
+/* Frees every cached scratch area of the calling process and destroys the cached
+ * near-tree graphs (synchronises the devices that own them). Later calls allocate
+ * again on demand. */
 int nbody_release_workspace(void);
 
 /* Library version string. */
